@@ -1,0 +1,341 @@
+"""Plain, slow CPU oracle of the Parallel Box Decoding (PBD) window step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  It shares no code with
+the HIP path and imports nothing from it.
+
+What it computes, step by step, in float64 numpy (``dtype`` can lower it to
+float32), with every stored input decoded exactly:
+
+* The window is the last accepted token followed by mask tokens; it sits at
+  positions P..P+W-1 right after the cached prefix, and its rows attend to the
+  whole cached prefix and to every row of the window (bidirectional inside the
+  window).  Source: "LocateAnything-3B for RK3588 (RKLLM + RKNN)", section
+  "How it differs from the original", item 1; "LocateAnything-3B on Jetson Orin
+  Nano", Part 1 section 1.3 (a block mask instead of a strictly causal one).
+* The decoder is a plain Qwen2 causal LM (Jetson page, Part 1 section 1.2):
+  pre-RMSNorm, GQA attention with half-rotation RoPE and q/k/v biases, a
+  SiLU-gated MLP, a final RMSNorm, and an lm_head tied to the input embedding
+  ("LocateAnything-3B — ONNX WebGPU (INT4 + 4-bit embeddings)", section "Why
+  this repo exists").  GQA K/V have 2 heads of 128 (same page, section
+  "KV-cache graph for in-browser use").
+* Group-wise symmetric INT4: element j of a row is (q_j - 8) * scale[j // g],
+  q_j from the low nibble for even j and the high nibble for odd j (WebGPU
+  page, section "Embedding gather / dequant (JS reference)"; g = 32 for the
+  embedding; g = 128 along the input dim for the linears, section "Files").
+* Greedy selection: the per-position argmax of the logits (Jetson page, Part 1
+  section 1.4: temperature 0, no sampling), lowest index on exact ties.
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes): one key bound P+W shared by every window row; the window's
+K/V rounded to bf16 (round-to-nearest-even from the fp32 value) before
+attention, as they are read back from a bf16 cache; RoPE inv_freq =
+theta^(-2i/D) pairing dims i and i+D/2; attention scale 1/sqrt(D); SiLU(z) =
+z / (1 + exp(-z)).
+
+Pins (tests/test_oracle_pins.py): INT4 decode against hand-built rows in
+tests/golden; window attention against a dense brute-force masked softmax and
+torch SDPA; W=1 against textbook causal decode; bidirectionality; paging and
+NaN-poisoned-slot invariance; RoPE, RMSNorm, SiLU closed forms; argmax ties
+and gaps; structural special cases of the layer and of the whole step.
+Whole-step agreement with the trained model: parity unpinned (no trained
+weights exist here).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_float", "fp16_to_float", "round_to_bf16_bits", "int4_dequant", "decode_weight",
+    "embed_rows", "rmsnorm", "silu", "rope_angles", "rope_apply", "window_attention",
+    "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "pbd_emission_loop",
+]
+
+
+def _dim(d, name):
+    return d[name] if isinstance(d, dict) else getattr(d, name)
+
+
+# ---------------------------------------------------------------------------
+# Storage decoding (exact)
+# ---------------------------------------------------------------------------
+
+def bf16_to_float(bits, dtype=np.float64):
+    """bf16 bit patterns (uint16/int16) -> float (exact: bf16 is the top half of fp32)."""
+    u = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(dtype)
+
+
+def fp16_to_float(bits, dtype=np.float64):
+    """IEEE fp16 bit patterns (uint16/int16) -> float (exact)."""
+    return np.asarray(bits).view(np.uint16).view(np.float16).astype(dtype)
+
+
+def round_to_bf16_bits(x):
+    """Round values to bf16 bit patterns the way the fp32 kernel does.
+
+    The value is first rounded to fp32, then to bf16 with round-to-nearest-even
+    (the decision is taken in the kernel's precision, fp32).
+    """
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def int4_dequant(packed, scales, group, dtype=np.float64):
+    """Group-wise symmetric INT4 -> float.
+
+    packed: uint8 [..., k/2]; element 2i is the low nibble of byte i, element
+    2i+1 its high nibble.  scales: fp16 bits [..., k/group].  Element j decodes
+    to (q_j - 8) * scale[j // group] (WebGPU page, embedding gather/dequant).
+    """
+    packed = np.asarray(packed).view(np.uint8)
+    low = (packed & 0x0F).astype(np.int64)
+    high = (packed >> 4).astype(np.int64)
+    k = 2 * packed.shape[-1]
+    q = np.empty(packed.shape[:-1] + (k,), dtype=np.int64)
+    q[..., 0::2] = low
+    q[..., 1::2] = high
+    s = fp16_to_float(scales, dtype)
+    j = np.arange(k)
+    return (q - 8).astype(dtype) * s[..., j // group]
+
+
+def decode_weight(w, rows=None, dtype=np.float64):
+    """Decode a weight descriptor (bf16 or INT4) to a float matrix [n, k]."""
+    data = w["data"] if rows is None else w["data"][rows]
+    if w["fmt"] == "bf16":
+        return bf16_to_float(data, dtype)
+    scales = w["scales"] if rows is None else w["scales"][rows]
+    return int4_dequant(data, scales, int(w["group"]), dtype)
+
+
+def embed_rows(ids, emb, dtype=np.float64):
+    """x[t] = E[ids[t]] (bf16 row, or INT4 group-32 row dequantized)."""
+    ids = np.asarray(ids).reshape(-1).astype(np.int64)
+    return decode_weight(emb, rows=ids, dtype=dtype)
+
+
+# ---------------------------------------------------------------------------
+# Elementwise pieces
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x, gain, eps):
+    """x / sqrt(mean(x^2) + eps) * gain, over the last axis."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gain
+
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def rope_angles(pos, head_dim, theta, dtype=np.float64):
+    """Angles [len(pos), D/2]: pos * theta^(-2i/D), computed in float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    return (np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]).astype(dtype)
+
+
+def rope_apply(x, ang):
+    """Half-rotation RoPE on x [T, heads, D] with angles [T, D/2].
+
+    (x_i, x_{i+D/2}) -> (x_i cos a_i - x_{i+D/2} sin a_i, x_{i+D/2} cos a_i + x_i sin a_i).
+    """
+    h = x.shape[-1] // 2
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Attention over the paged cache
+# ---------------------------------------------------------------------------
+
+def cache_read(cache, layer, b, n, dtype=np.float64):
+    """Token slots 0..n-1 of sequence b from the paged cache -> (K, V) [n, Hkv, D].
+
+    K pages are [blocks, Hkv, block, D]; V pages are [blocks, Hkv, D, block].
+    Slot t lives in block block_table[b, t // block] at offset t % block.
+    """
+    bs = int(cache["block"])
+    t = np.arange(n)
+    blk = np.asarray(cache["block_table"])[b, t // bs].astype(np.int64)
+    off = t % bs
+    kl = cache["k"][layer]
+    vl = cache["v"][layer]
+    k = kl[blk, :, off, :]            # [n, Hkv, D]
+    v = vl[blk, :, :, off]            # [n, Hkv, D]
+    return bf16_to_float(k, dtype), bf16_to_float(v, dtype)
+
+
+def window_attention(q, k, v, dtype=np.float64):
+    """Attention of the W window rows over n keys (prefix + window).
+
+    q: [W, Hq, D]; k, v: [n, Hkv, D].  Every window row sees all n keys: the
+    prefix is before it (causal) and the window is bidirectional.  Query head h
+    reads KV head h // (Hq / Hkv).  softmax(q.k / sqrt(D)) . v.
+    """
+    W, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((W, Hq, D), dtype=dtype)
+    scale = 1.0 / np.sqrt(D)
+    for h in range(Hq):
+        kv = h // G
+        s = (q[:, h, :] @ k[:, kv, :].T) * scale        # [W, n]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, kv, :]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Decoder layer, lm_head, step
+# ---------------------------------------------------------------------------
+
+def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float64, parts=None):
+    """One decoder layer on the window rows of every sequence.
+
+    h: [B*W, H] hidden states (row b*W + j is window position j of sequence b).
+    Returns (h_out, k_bits, v_bits) where k_bits/v_bits [B*W, Hkv, D] are the
+    bf16 K/V the step stores at slots P_b + j.  ``parts`` (a dict) receives
+    intermediate values when given.
+    """
+    H = _dim(dims, "hidden")
+    Hq = _dim(dims, "n_heads")
+    Hkv = _dim(dims, "n_kv_heads")
+    D = _dim(dims, "head_dim")
+    F = _dim(dims, "inter")
+    eps = float(_dim(dims, "rms_eps"))
+    theta = float(_dim(dims, "rope_theta"))
+    P = np.asarray(prefix_len).astype(np.int64)
+    B = len(P)
+    W = int(window)
+    T = B * W
+    assert h.shape == (T, H)
+
+    a = rmsnorm(h, bf16_to_float(lay["in_norm"], dtype), eps)
+    qkv = a @ decode_weight(lay["qkv"], dtype=dtype).T
+    if lay.get("qkv_bias") is not None:
+        qkv = qkv + bf16_to_float(lay["qkv_bias"], dtype)
+    q = qkv[:, :Hq * D].reshape(T, Hq, D)
+    k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
+    v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
+
+    pos = (P[:, None] + np.arange(W)[None, :]).reshape(-1)
+    ang = rope_angles(pos, D, theta, dtype)
+    q = rope_apply(q, ang)
+    k = rope_apply(k, ang)
+    k_bits = round_to_bf16_bits(k)
+    v_bits = round_to_bf16_bits(v)
+    kw = bf16_to_float(k_bits, dtype)
+    vw = bf16_to_float(v_bits, dtype)
+
+    o = np.zeros((T, Hq, D), dtype=dtype)
+    for b in range(B):
+        rows = slice(b * W, (b + 1) * W)
+        kp, vp = cache_read(cache, layer, b, int(P[b]), dtype)
+        kk = np.concatenate([kp, kw[rows]], axis=0)
+        vv = np.concatenate([vp, vw[rows]], axis=0)
+        o[rows] = window_attention(q[rows], kk, vv, dtype)
+
+    h1 = h + o.reshape(T, Hq * D) @ decode_weight(lay["o"], dtype=dtype).T
+    a2 = rmsnorm(h1, bf16_to_float(lay["post_norm"], dtype), eps)
+    gu = a2 @ decode_weight(lay["gate_up"], dtype=dtype).T
+    m = silu(gu[:, :F]) * gu[:, F:]
+    h2 = h1 + m @ decode_weight(lay["down"], dtype=dtype).T
+    if parts is not None:
+        parts.update(q=q, k=k, v=v, attn=o.reshape(T, Hq * D), h_mid=h1, mlp=m, qkv=qkv)
+    return h2, k_bits, v_bits
+
+
+def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64):
+    """Per-row argmax of f . E^T over the vocabulary, with top-1 and top-2 gap.
+
+    Lowest index wins an exact tie.  gap = logit[id] - max_{v != id} logit[v].
+    The vocabulary is processed in chunks only to bound memory.
+    """
+    f = np.asarray(f, dtype=dtype)
+    T = f.shape[0]
+    V = int(lm["n"]) if "n" in lm else lm["data"].shape[0]
+    best = np.full(T, -np.inf)
+    best_id = np.full(T, -1, dtype=np.int64)
+    second = np.full(T, -np.inf)
+    for v0 in range(0, V, chunk):
+        v1 = min(V, v0 + chunk)
+        E = decode_weight(lm, rows=np.arange(v0, v1), dtype=dtype)
+        logits = f @ E.T                               # [T, v1-v0]
+        for t in range(T):
+            row = logits[t]
+            i = int(np.argmax(row))                    # first (lowest) index of the max
+            top = row[i]
+            rest = np.delete(row, i)
+            sec = rest.max() if rest.size else -np.inf
+            if top > best[t]:
+                second[t] = max(best[t], sec)
+                best[t] = top
+                best_id[t] = v0 + i
+            else:
+                second[t] = max(second[t], top)
+    return best_id, best, best - second
+
+
+def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidden=False,
+             layers=None):
+    """One PBD window step for every sequence.
+
+    window_ids [B, W] -> per-position argmax ids [B, W] and top-2 gaps [B, W].
+    The step writes nothing into ``cache``; it returns the bf16 K/V it would
+    store at slots P_b .. P_b+W-1 of each layer.
+    """
+    dims = model["dims"]
+    ids = np.asarray(window_ids)
+    B, W = ids.shape
+    h = embed_rows(ids.reshape(-1), model["embed"], dtype)
+    kv = []
+    n_layers = len(model["layers"]) if layers is None else layers
+    for l in range(n_layers):
+        h, kb, vb = decoder_layer(h, model["layers"][l], dims, cache, l, prefix_len, W, dtype)
+        kv.append((kb, vb))
+    f = rmsnorm(h, bf16_to_float(model["final_norm"], dtype), float(_dim(dims, "rms_eps")))
+    lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
+    out_ids, top1, gap = lm_head_argmax(f, lm, dtype=dtype)
+    res = {"ids": out_ids.reshape(B, W), "top1": top1.reshape(B, W), "gap": gap.reshape(B, W),
+           "kv": kv}
+    if return_hidden:
+        res["hidden"] = h
+        res["final"] = f
+    return res
+
+
+def pbd_emission_loop(model, cache, window_ids, prefix_len, steps, mask_id, dtype=np.float64):
+    """Consecutive window steps with every window accepted.
+
+    After each step the window's K/V are stored at slots P_b..P_b+W-1, the
+    prefix grows by W, and the next window is [last output id, mask x (W-1)].
+    ``cache`` is copied, never modified.
+    """
+    c = {k: (np.array(v, copy=True) if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+    ids = np.array(window_ids, copy=True)
+    P = np.array(prefix_len, dtype=np.int64, copy=True)
+    B, W = ids.shape
+    bs = int(c["block"])
+    outs = []
+    for _ in range(steps):
+        r = pbd_step(model, c, ids, P, dtype)
+        outs.append(r["ids"])
+        for l, (kb, vb) in enumerate(r["kv"]):
+            for b in range(B):
+                for j in range(W):
+                    t = int(P[b]) + j
+                    blk = int(c["block_table"][b, t // bs])
+                    c["k"][l, blk, :, t % bs, :] = kb[b * W + j].view(np.int16)
+                    c["v"][l, blk, :, :, t % bs] = vb[b * W + j].view(np.int16)
+        P = P + W
+        ids = np.full((B, W), mask_id, dtype=np.int32)
+        ids[:, 0] = r["ids"][:, W - 1]
+    return outs, P, c

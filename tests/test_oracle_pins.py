@@ -1,0 +1,461 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a worked example from the pages
+(tests/golden), a closed form, a textbook/library routine, an invariant of the
+method, or brute force on a tiny input.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import oracle as O
+from box_decoding_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+TINY = synth.ModelDims(hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, inter=96, n_layers=2,
+                       vocab=300, rms_eps=1e-6, rope_theta=1e6, block=4)
+
+
+def _np(x):
+    return synth.to_numpy_tree(x)
+
+
+# ---------------------------------------------------------------- INT4 / bf16 decode
+
+def test_int4_golden_rows():
+    g = json.load(open(os.path.join(GOLDEN, "int4_rows.json")))
+    for row in g["rows"]:
+        packed = np.array([int(b, 16) for b in row["bytes_hex"]], dtype=np.uint8)[None, :]
+        scales = np.array([int(s, 16) for s in row["scales_fp16_hex"]], dtype=np.uint16)[None, :]
+        assert np.array_equal(O.fp16_to_float(scales)[0], np.array(row["scales_value"]))
+        got = O.int4_dequant(packed, scales, g["group"])[0]
+        if "all" in row:
+            exp = np.array(row["all"])
+        else:
+            exp = np.zeros(64)
+            for j, val in row["nonzero"].items():
+                exp[int(j)] = val
+        assert np.array_equal(got, exp)
+
+
+def test_int4_storage_sizes_match_page():
+    # WebGPU page, "Files": packed table [152681, 1024] uint8 (~156 MB) and fp16
+    # scales [152681, 64] (~19.5 MB) for a 2048-wide, group-32 embedding.
+    V, H = 152681, 2048
+    assert V * (H // 2) == 156_345_344
+    assert V * (H // 32) * 2 == 19_543_168
+    # Tied embedding: vocab x hidden in fp32 is ~1.25 GB ("Why this repo exists").
+    assert V * H * 4 == 1_250_762_752
+    d = synth.QWEN25_3B
+    assert (d.vocab, d.hidden) == (V, H)
+    # KV graph: 36 layers x (K, V) x [2 heads, 128] bf16 per token.
+    assert d.n_layers * 2 * d.n_kv_heads * d.head_dim * 2 == 36_864
+
+
+def test_int4_dequant_matches_synth_packing_roundtrip():
+    # The decoder must invert the packer for every code: pack codes 0..15 in all
+    # even/odd positions and read them back with unit scales (value q - 8).
+    q = np.array([[a, b] for a in range(16) for b in range(16)], dtype=np.uint8).reshape(1, -1)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    ones = np.full((1, q.shape[1] // 32), 0x3C00, dtype=np.uint16)
+    assert np.array_equal(O.int4_dequant(packed, ones, 32), q.astype(np.float64) - 8)
+
+
+def test_bf16_rounding_textbook():
+    for line in open(os.path.join(GOLDEN, "bf16_rne.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        _, f32hex, bfhex = line.split()
+        f = np.array([int(f32hex, 16)], dtype=np.uint32).view(np.float32)
+        assert int(O.round_to_bf16_bits(f)[0]) == int(bfhex, 16), line
+    # library routine: torch's fp32 -> bf16 conversion is round-to-nearest-even
+    x = torch.randn(100000, generator=torch.Generator().manual_seed(3)) * 10
+    ref = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.round_to_bf16_bits(x.numpy()), ref)
+    # decode is exact
+    assert np.array_equal(O.bf16_to_float(ref), x.to(torch.bfloat16).double().numpy())
+
+
+# ---------------------------------------------------------------- attention
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _dense_bruteforce(q, k, v, mask, G):
+    """Plain loops: masked softmax attention of every row over every allowed key."""
+    N, Hq, D = q.shape
+    out = np.zeros_like(q)
+    for i in range(N):
+        for h in range(Hq):
+            kv = h // G
+            scores = []
+            for t in range(N):
+                if mask[i, t]:
+                    scores.append(sum(q[i, h, d] * k[t, kv, d] for d in range(D)) / math.sqrt(D))
+                else:
+                    scores.append(-math.inf)
+            mx = max(scores)
+            w = [math.exp(s - mx) if s != -math.inf else 0.0 for s in scores]
+            z = sum(w)
+            for d in range(D):
+                out[i, h, d] = sum(w[t] * v[t, kv, d] for t in range(N)) / z
+    return out
+
+
+def _pbd_mask(P, W):
+    """Dense mask of a prefix of P tokens followed by a W-token window.
+
+    Prefix rows are causal; every window row sees the prefix and the whole window.
+    """
+    N = P + W
+    m = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        for t in range(N):
+            m[i, t] = (t <= i) if i < P else True
+    return m
+
+
+@pytest.mark.parametrize("P,W", [(0, 6), (5, 6), (13, 6), (9, 1), (7, 4)])
+def test_window_attention_equals_dense_masked_bruteforce(P, W):
+    Hq, Hkv, D = 4, 2, 8
+    N = P + W
+    q = _rand((N, Hq, D), 1)
+    k = _rand((N, Hkv, D), 2)
+    v = _rand((N, Hkv, D), 3)
+    mask = _pbd_mask(P, W)
+    ref = _dense_bruteforce(q, k, v, mask, Hq // Hkv)
+    got = O.window_attention(q[P:], k, v)
+    np.testing.assert_allclose(got, ref[P:], rtol=1e-12, atol=1e-12)
+    # library routine: torch SDPA in float64 with the explicit boolean mask
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1)).permute(1, 0, 2)[None]
+    sd = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask))
+    np.testing.assert_allclose(got, sd[0].permute(1, 0, 2).numpy()[P:], rtol=1e-12, atol=1e-12)
+
+
+def test_w1_is_textbook_causal_decode():
+    Hq, Hkv, D, P = 4, 2, 16, 37
+    N = P + 1
+    q = _rand((N, Hq, D), 11)
+    k = _rand((N, Hkv, D), 12)
+    v = _rand((N, Hkv, D), 13)
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(np.repeat(k, 2, axis=1)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.repeat(v, 2, axis=1)).permute(1, 0, 2)[None]
+    sd = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    got = O.window_attention(q[P:], k, v)
+    np.testing.assert_allclose(got[0], sd[0, :, -1, :].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_window_is_bidirectional():
+    Hq, Hkv, D, P, W = 4, 2, 8, 10, 6
+    N = P + W
+    q = _rand((W, Hq, D), 21)
+    k = _rand((N, Hkv, D), 22)
+    v = _rand((N, Hkv, D), 23)
+    base = O.window_attention(q, k, v)
+    for j in range(W):
+        k2, v2 = k.copy(), v.copy()
+        k2[P + j] += 0.5
+        v2[P + j] += 0.5
+        pert = O.window_attention(q, k2, v2)
+        # every window row, including rows before j, sees the changed key
+        for r in range(W):
+            assert np.abs(pert[r] - base[r]).max() > 1e-6
+        # under a causal mask rows before j would not change (control)
+        causal = np.tril(np.ones((N, N), dtype=bool))
+        a = _dense_bruteforce(np.concatenate([np.zeros((P, Hq, D)), q]), k, v, causal, 2)
+        b = _dense_bruteforce(np.concatenate([np.zeros((P, Hq, D)), q]), k2, v2, causal, 2)
+        if j > 0:
+            assert np.abs(a[P:P + j] - b[P:P + j]).max() == 0.0
+
+
+def test_equal_scores_give_mean_of_values():
+    Hq, Hkv, D, n = 4, 2, 8, 9
+    q = np.zeros((3, Hq, D))
+    k = _rand((n, Hkv, D), 31)
+    v = _rand((n, Hkv, D), 32)
+    got = O.window_attention(q, k, v)
+    for h in range(Hq):
+        np.testing.assert_allclose(got[:, h, :], np.broadcast_to(v[:, h // 2, :].mean(0), (3, D)),
+                                   rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- elementwise closed forms
+
+def test_rope_closed_forms():
+    D, theta = 16, 1e6
+    x = _rand((1, 3, D), 41)
+    # position 0 is the identity
+    np.testing.assert_array_equal(O.rope_apply(x, O.rope_angles([0], D, theta)), x)
+    # each (i, i + D/2) pair keeps its norm
+    ang = O.rope_angles([12345], D, theta)
+    y = O.rope_apply(x, ang)
+    n0 = x[..., :D // 2] ** 2 + x[..., D // 2:] ** 2
+    n1 = y[..., :D // 2] ** 2 + y[..., D // 2:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-12)
+    # the dot product depends only on the position difference
+    q = _rand((1, 1, D), 42)
+    k = _rand((1, 1, D), 43)
+
+    def dot(p, pk):
+        return float((O.rope_apply(q, O.rope_angles([p], D, theta)) *
+                      O.rope_apply(k, O.rope_angles([pk], D, theta))).sum())
+    assert abs(dot(100, 37) - dot(1100, 1037)) < 1e-10
+    assert abs(dot(100, 37) - dot(37, 100)) > 1e-6
+    # textbook RoPE frequencies (RoFormer): pair i turns by theta^(-2i/D) rad per
+    # position; the pairing is (i, i + D/2)
+    for i in (0, 1, D // 2 - 1):
+        e = np.zeros((1, 1, D))
+        e[0, 0, i] = 1.0
+        w = theta ** (-2.0 * i / D)
+        r = O.rope_apply(e, O.rope_angles([3], D, theta))
+        assert abs(r[0, 0, i] - math.cos(3 * w)) < 1e-15
+        assert abs(r[0, 0, i + D // 2] - math.sin(3 * w)) < 1e-15
+
+
+def test_rmsnorm_constant_vector():
+    g = 1.0 + _rand(32, 51, 0.02)
+    for c in (3.0, -0.25, 1e-4):
+        eps = 1e-6
+        got = O.rmsnorm(np.full((1, 32), c), g, eps)
+        np.testing.assert_allclose(got[0], np.sign(c) * g / np.sqrt(1.0 + eps / c ** 2), rtol=1e-14)
+
+
+def test_silu_library_and_limits():
+    z = np.linspace(-30, 30, 2001)
+    np.testing.assert_allclose(O.silu(z), z * expit(z), rtol=1e-13, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(-z), O.silu(z) - z, atol=1e-12)
+
+
+# ---------------------------------------------------------------- argmax / gap
+
+def test_lm_head_argmax_planted_max_tie_and_gap():
+    rng = np.random.default_rng(61)
+    V, H = 20000, 8
+    E = rng.standard_normal((V, H)) * 0.02
+    E[:, 0] = 0.0
+    E[777, 0] = 5.0          # planted maximum for row 0
+    E[123, 1] = 9.0          # planted tie for row 1 ...
+    E[18001, 1] = 9.0        # ... across two vocab chunks: lowest index wins
+    E[4100, 2] = 7.0         # planted tie inside one vocab chunk
+    E[4200, 2] = 7.0
+    bits = O.round_to_bf16_bits(E)
+    lm = {"fmt": "bf16", "n": V, "data": bits}
+    f = np.zeros((3, H))
+    f[0, 0] = 1.0
+    f[1, 1] = 1.0
+    f[2, 2] = 1.0
+    f2 = np.zeros((1, H))
+    f2[0] = rng.standard_normal(H)
+    f = np.concatenate([f, f2])
+    ids, top1, gap = O.lm_head_argmax(f, lm, chunk=8192)
+    assert ids[0] == 777 and ids[1] == 123 and ids[2] == 4100
+    assert gap[1] == 0.0 and gap[2] == 0.0
+    logits = f @ O.bf16_to_float(bits).T
+    for t in range(4):
+        s = np.sort(logits[t])[::-1]
+        assert top1[t] == s[0]
+        assert gap[t] == s[0] - s[1]
+        assert ids[t] == int(np.flatnonzero(logits[t] == s[0])[0])
+
+
+# ---------------------------------------------------------------- layer structure
+
+def _tiny_setup(P_list=(5, 9), W=3, seed=0, dims=TINY):
+    model = _np(synth.make_model(dims, "bf16", seed))
+    model["dims"] = dims
+    cache = _np(synth.make_cache(dims, torch.tensor(P_list), W, seed=seed + 1))
+    h = np.random.default_rng(seed).standard_normal((len(P_list) * W, dims.hidden))
+    return model, cache, h
+
+
+def _zero_like_weight(w):
+    if w["fmt"] == "int4":  # code 8 decodes to zero
+        return {**w, "data": np.full_like(w["data"], 0x88)}
+    return {**w, "data": np.zeros_like(w["data"])}
+
+
+def test_layer_with_zero_weights_is_identity():
+    model, cache, h = _tiny_setup()
+    lay = dict(model["layers"][0])
+    for name in ("qkv", "o", "gate_up", "down"):
+        lay[name] = _zero_like_weight(lay[name])
+    out, _, _ = O.decoder_layer(h, lay, TINY, cache, 0, [5, 9], 3)
+    np.testing.assert_array_equal(out, h)
+
+
+def test_layer_gqa_head_mapping_and_value_slice():
+    # q = k = 0 (uniform attention); every cached and window value of kv head 0 is
+    # c0 and of kv head 1 is c1; with W_o = I the attention output of query head h
+    # is c_{h // 2} on all its dims, and the MLP is off.
+    d = TINY
+    model, cache, h = _tiny_setup()
+    lay = dict(model["layers"][0])
+    c0, c1 = 0.5, -1.25
+    lay["qkv"] = _zero_like_weight(lay["qkv"])
+    bias = np.zeros(d.qkv_out)
+    bias[(d.n_heads + d.n_kv_heads) * d.head_dim:][:d.head_dim] = c0
+    bias[(d.n_heads + d.n_kv_heads) * d.head_dim:][d.head_dim:] = c1
+    lay["qkv_bias"] = O.round_to_bf16_bits(bias)
+    lay["o"] = {"fmt": "bf16", "data": O.round_to_bf16_bits(np.eye(d.hidden))}
+    lay["down"] = _zero_like_weight(lay["down"])
+    cache = dict(cache)
+    v = np.array(cache["v"])
+    v[0, :, 0] = O.round_to_bf16_bits(np.full(v[0, :, 0].shape, c0)).view(np.int16)
+    v[0, :, 1] = O.round_to_bf16_bits(np.full(v[0, :, 1].shape, c1)).view(np.int16)
+    cache["v"] = v
+    out, _, vb = O.decoder_layer(h, lay, d, cache, 0, [5, 9], 3)
+    expect = np.concatenate([np.full(d.head_dim * 2, c0), np.full(d.head_dim * 2, c1)])
+    np.testing.assert_allclose(out - h, np.broadcast_to(expect, h.shape), rtol=0, atol=1e-14)
+    assert np.all(O.bf16_to_float(vb)[:, 0] == c0) and np.all(O.bf16_to_float(vb)[:, 1] == c1)
+
+
+def test_layer_single_key_attention_returns_value():
+    # P = 0 and W = 1: the only key is the token itself, softmax is 1, so the
+    # attention output of head h is the bf16-rounded value of kv head h // G, and
+    # RoPE at position 0 leaves q, k unchanged.
+    d = TINY
+    model, cache, h = _tiny_setup(P_list=(0,), W=1, seed=3)
+    lay = model["layers"][0]
+    parts = {}
+    O.decoder_layer(h, lay, d, cache, 0, [0], 1, parts=parts)
+    a = O.rmsnorm(h, O.bf16_to_float(lay["in_norm"]), d.rms_eps)
+    Wqkv = O.bf16_to_float(lay["qkv"]["data"])
+    bq = O.bf16_to_float(lay["qkv_bias"])
+    HqD, HkvD = d.n_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    v = a @ Wqkv[HqD + HkvD:].T + bq[HqD + HkvD:]
+    q = a @ Wqkv[:HqD].T + bq[:HqD]
+    vr = O.bf16_to_float(O.round_to_bf16_bits(v)).reshape(1, d.n_kv_heads, d.head_dim)
+    np.testing.assert_allclose(parts["attn"].reshape(1, d.n_heads, d.head_dim),
+                               np.repeat(vr, d.n_heads // d.n_kv_heads, axis=1), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(parts["q"].reshape(1, -1), q, rtol=1e-13, atol=1e-14)
+
+
+def test_mlp_gate_up_order_and_down_mapping():
+    # Attention branch off (W_o = 0) and h constant c, so the post-norm input is
+    # a = g / sqrt(1 + eps/c^2) exactly.  With W_gate = diag(alpha), W_up =
+    # diag(beta) and W_down = I, the layer adds silu(alpha*a) * (beta*a); swapping
+    # gate and up, or misplacing the down columns, changes it.
+    d = synth.ModelDims(hidden=16, n_heads=2, n_kv_heads=1, head_dim=8, inter=16, n_layers=1,
+                        vocab=40, block=4)
+    model, cache, _ = _tiny_setup(P_list=(3,), W=2, seed=5, dims=d)
+    lay = dict(model["layers"][0])
+    lay["o"] = _zero_like_weight(lay["o"])
+    c = 2.0
+    h = np.full((2, d.hidden), c)
+    g = O.bf16_to_float(lay["post_norm"])
+    s = 1.0 / math.sqrt(1.0 + d.rms_eps / c ** 2)
+    alpha = np.linspace(-3, 3, d.inter)
+    beta = np.linspace(0.5, 2.0, d.inter)
+    Wg = np.zeros((d.inter, d.hidden))
+    Wu = np.zeros((d.inter, d.hidden))
+    for i in range(d.inter):
+        Wg[i, i] = 1.0
+        Wu[i, i] = 1.0
+    lay["gate_up"] = {"fmt": "bf16", "data": O.round_to_bf16_bits(np.concatenate([Wg, Wu]))}
+    lay["down"] = {"fmt": "bf16", "data": O.round_to_bf16_bits(np.eye(d.hidden, d.inter))}
+    out, _, _ = O.decoder_layer(h, lay, d, cache, 0, [3], 2)
+    a = g * s
+    np.testing.assert_allclose(out - h, np.broadcast_to(a * expit(a) * a, out.shape), rtol=1e-12)
+    # swap gate and up rows: the result must differ (order matters)
+    Wg2 = Wg * alpha[:, None]
+    Wu2 = Wu * beta[:, None]
+    lay["gate_up"] = {"fmt": "bf16", "data": O.round_to_bf16_bits(np.concatenate([Wg2, Wu2]))}
+    out2, _, _ = O.decoder_layer(h, lay, d, cache, 0, [3], 2)
+    ag = O.bf16_to_float(O.round_to_bf16_bits(alpha)) * a
+    bu = O.bf16_to_float(O.round_to_bf16_bits(beta)) * a
+    np.testing.assert_allclose(out2 - h, np.broadcast_to(ag * expit(ag) * bu, out.shape), rtol=1e-12)
+
+
+def test_paging_and_poisoned_slots_do_not_change_layer():
+    d = TINY
+    model, cache, h = _tiny_setup(P_list=(6, 11), W=3, seed=7)
+    ref, kb, vb = O.decoder_layer(h, model["layers"][1], d, cache, 1, [6, 11], 3)
+    # the same logical tokens under another block permutation, with every slot
+    # at or beyond P_b (and all spare blocks) poisoned with NaN
+    bs = cache["block"]
+    L, nb = cache["k"].shape[:2]
+    nb2 = nb + 5
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(nb2)
+    nan16 = np.uint16(0x7FC0).view(np.int16)
+    k2 = np.full((L, nb2) + cache["k"].shape[2:], nan16, dtype=np.int16)
+    v2 = np.full((L, nb2) + cache["v"].shape[2:], nan16, dtype=np.int16)
+    table2 = np.full_like(cache["block_table"], -1)
+    for b, P in enumerate((6, 11)):
+        for t in range(P):
+            ob = cache["block_table"][b, t // bs]
+            nbk = perm[b * 5 + t // bs]
+            table2[b, t // bs] = nbk
+            k2[:, nbk, :, t % bs, :] = cache["k"][:, ob, :, t % bs, :]
+            v2[:, nbk, :, :, t % bs] = cache["v"][:, ob, :, :, t % bs]
+    cache2 = {**cache, "k": k2, "v": v2, "block_table": table2}
+    out, kb2, vb2 = O.decoder_layer(h, model["layers"][1], d, cache2, 1, [6, 11], 3)
+    np.testing.assert_array_equal(out, ref)
+    np.testing.assert_array_equal(kb2, kb)
+
+
+# ---------------------------------------------------------------- whole step
+
+@pytest.mark.parametrize("wfmt", ["bf16", "int4"])
+def test_step_with_identity_layers_returns_input_ids(wfmt):
+    # With every layer's weights zero the layers are the identity, so the final
+    # hidden state of a position is its own (dequantized) embedding row, and the
+    # tied lm_head scores that row highest: the step returns the window ids.
+    d = synth.ModelDims(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, inter=128, n_layers=2,
+                        vocab=700, block=16)
+    model = _np(synth.make_model(d, wfmt, 11))
+    model["dims"] = d
+    for lay in model["layers"]:
+        for name in ("qkv", "o", "gate_up", "down"):
+            lay[name] = _zero_like_weight(lay[name])
+    cache = _np(synth.make_cache(d, torch.tensor([20, 33]), 6, seed=12))
+    ids = synth.draw_window_ids(2, 6, d.vocab, 13, mask_id=-1).numpy()
+    r = O.pbd_step(model, cache, ids, [20, 33])
+    np.testing.assert_array_equal(r["ids"], ids)
+    assert np.all(r["gap"] > 0)
+
+
+def test_oracle_float32_tracks_float64():
+    # Self-consistency of the precision switch (not a pin): the float32 run of a
+    # tiny 2-layer step stays close to the float64 run.
+    model, cache, _ = _tiny_setup(P_list=(5, 9), W=3, seed=17)
+    ids = synth.draw_window_ids(2, 3, TINY.vocab, 19, mask_id=-1).numpy()
+    r64 = O.pbd_step(model, cache, ids, [5, 9], return_hidden=True)
+    r32 = O.pbd_step(model, cache, ids, [5, 9], dtype=np.float32, return_hidden=True)
+    rel = np.linalg.norm(r32["hidden"] - r64["hidden"]) / np.linalg.norm(r64["hidden"])
+    assert rel < 1e-5
+
+
+def test_emission_loop_commits_window_kv():
+    model, cache, _ = _tiny_setup(P_list=(5, 9), W=3, seed=23)
+    # room for two windows per sequence
+    cache = _np(synth.make_cache(TINY, torch.tensor([5, 9]), 3, extra_tokens=3, seed=24))
+    ids = synth.draw_window_ids(2, 3, TINY.vocab, 25).numpy()
+    outs, P, c2 = O.pbd_emission_loop(model, cache, ids, [5, 9], 2, mask_id=int(ids[0, 1]))
+    assert list(P) == [11, 15]
+    r0 = O.pbd_step(model, cache, ids, [5, 9])
+    np.testing.assert_array_equal(outs[0], r0["ids"])
+    bs = cache["block"]
+    for l, (kb, vb) in enumerate(r0["kv"]):
+        for b, p in enumerate((5, 9)):
+            for j in range(3):
+                t = p + j
+                blk = cache["block_table"][b, t // bs]
+                assert np.array_equal(c2["k"][l, blk, :, t % bs, :].view(np.uint16), kb[b * 3 + j])
+                assert np.array_equal(c2["v"][l, blk, :, :, t % bs].view(np.uint16), vb[b * 3 + j])
+    # the second step reads the committed window as prefix
+    nxt = np.full((2, 3), int(ids[0, 1]), dtype=np.int32)
+    nxt[:, 0] = r0["ids"][:, 2]
+    r1 = O.pbd_step(model, c2, nxt, [8, 12])
+    np.testing.assert_array_equal(outs[1], r1["ids"])
