@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""PBD window-step benchmark on one MI355X.
+
+Times K consecutive calls of la_pbd_step on the full 36-layer, 152,681-token
+decoder at batch 1, prefix 1280 (synthetic, random-init weights, inputs resident
+in HBM before the timed region), and prints one JSON line with the window steps
+per second, the roofline figures of the dominant kernel and the CPU oracle timed
+on the host as a reference.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "PBD window steps/sec (≈boxes/sec) at batch 1 and 32; achieved HBM GB/s vs peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def weight_bytes(w):
+    n = w["data"].numel() * w["data"].element_size()
+    if w.get("scales") is not None:
+        n += w["scales"].numel() * w["scales"].element_size()
+    return n
+
+
+def step_bytes(model, dims, prefix_len, W):
+    """Algorithmic HBM bytes of one step: every weight once, the KV read once,
+    the window's K/V written once, the gathered embedding rows."""
+    total = 0
+    for lay in model["layers"]:
+        for k in ("qkv", "o", "gate_up", "down"):
+            total += weight_bytes(lay[k])
+        total += (lay["in_norm"].numel() + lay["post_norm"].numel()) * 2
+        if lay.get("qkv_bias") is not None:
+            total += lay["qkv_bias"].numel() * 2
+    lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
+    total += weight_bytes(lm) + model["final_norm"].numel() * 2
+    per_tok = dims.n_layers * 2 * dims.n_kv_heads * dims.head_dim * 2
+    keys = int(sum(int(p) + W for p in prefix_len.tolist()))
+    total += keys * per_tok + len(prefix_len) * W * per_tok
+    total += len(prefix_len) * W * dims.hidden * 2
+    return total
+
+
+def cpu_baseline(workload_name, sample_layers):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from box_decoding_amd import synth
+
+    w = synth.WORKLOADS[workload_name]
+    d = w.dims
+    import dataclasses
+    ds = dataclasses.replace(d, n_layers=sample_layers)
+    log(f"cpu_baseline: generating a {sample_layers}-layer sample on the host")
+    model = synth.to_numpy_tree(synth.make_model(ds, w.wfmt, w.model_seed, "cpu"))
+    model["dims"] = ds
+    P = synth.draw_prefix_lens(w)
+    cache = synth.to_numpy_tree(synth.make_cache(ds, P, w.window, seed=w.input_seed, device="cpu"))
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed).numpy()
+    h = O.embed_rows(ids.reshape(-1), model["embed"])
+    t0 = time.perf_counter()
+    for l in range(sample_layers):
+        h, _, _ = O.decoder_layer(h, model["layers"][l], ds, cache, l, P.numpy(), w.window)
+    t_layers = time.perf_counter() - t0
+    f = O.rmsnorm(h, O.bf16_to_float(model["final_norm"]), d.rms_eps)
+    lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
+    t0 = time.perf_counter()
+    O.lm_head_argmax(f, lm)
+    t_lm = time.perf_counter() - t0
+    t_step = t_layers / sample_layers * d.n_layers + t_lm
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{workload_name}: {sample_layers} of {d.n_layers} decoder layers "
+                      f"({t_layers:.1f} s) + the full lm_head argmax ({t_lm:.1f} s), float64 numpy, "
+                      f"extrapolated to one {d.n_layers}-layer step ({t_step:.1f} s)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="step_b1_p1280")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=3)
+    ap.add_argument("--kernel-reps", type=int, default=72)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the PBD step here is a single-GPU path "
+              "(data-parallel serving would run one independent copy per GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from box_decoding_amd import binding as B
+    from box_decoding_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    B.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    d = w.dims
+    log(f"bench: building {args.workload} on the GPU")
+    model = synth.make_model(d, w.wfmt, w.model_seed, dev)
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    max_len = int(P.max()) + w.window
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, (time.perf_counter() - t0) / n * 1e3
+
+    def eager():
+        B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, out_gap=out_gap)
+
+    for _ in range(args.warmup):
+        eager()
+    torch.cuda.synchronize()
+    eager_ms, _ = timed(eager, max(3, args.steps // 5))
+    # the serving loop replays the step as one captured graph
+    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
+    for _ in range(args.warmup):
+        graph.replay()
+    log(f"bench: warmup done (eager {eager_ms:.3f} ms/step), timing {args.steps} graph replays")
+    ms_step, wall_ms = timed(graph.replay, args.steps)
+    steps_per_s = 1000.0 / ms_step
+    sbytes = step_bytes(model, d, P, w.window)
+    log(f"bench: {ms_step:.3f} ms/step (wall {wall_ms:.3f} ms), "
+        f"{steps_per_s:.1f} steps/s, {sbytes / ms_step / 1e6:.0f} GB/s algorithmic")
+
+    # Dominant kernel: the gate/up projection with the SiLU epilogue (58% of a
+    # layer's weight bytes).  Timed with HIP events on the launch stream, cycling
+    # through the 36 layers' weights so that they stream from HBM.
+    F, H = d.inter, d.hidden
+    T = w.batch * w.window
+    xin = torch.randn((T, H), device=dev, generator=torch.Generator(device=dev).manual_seed(1))
+    gain = model["layers"][0]["post_norm"]
+    yout = torch.empty((T, F), dtype=torch.float32, device=dev)
+    kws = B.Workspace(dev)
+    for l in range(4):
+        B.wgemm(xin, model["layers"][l]["gate_up"], norm_gain=gain, silu_gate=True, out=yout, ws=kws)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for r in range(args.kernel_reps):
+        B.wgemm(xin, model["layers"][r % d.n_layers]["gate_up"], norm_gain=gain, silu_gate=True,
+                out=yout, ws=kws)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    k_ms = k0.elapsed_time(k1) / args.kernel_reps
+    gu_bytes = weight_bytes(model["layers"][0]["gate_up"]) + T * H * 4 + T * F * 4
+    k_gbps = gu_bytes / (k_ms * 1e-3) / 1e9
+    log(f"bench: gate_up call {k_ms * 1e3:.1f} us, {k_gbps:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and KV cache, uniform token ids)",
+        "config": {"workload": args.workload, "batch": w.batch, "window": w.window,
+                   "prefix": int(P.max()), "layers": d.n_layers, "vocab": d.vocab,
+                   "weights": w.wfmt},
+        "tokens_per_s": round(steps_per_s * T, 2),
+        "windows_per_s": round(steps_per_s * w.batch, 3),
+        "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
+        "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
+        "step_bytes": sbytes,
+        "roofline": {"bound": "hbm", "kernel": "gate_up GEMM + SiLU (la_wgemm call)",
+                     "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

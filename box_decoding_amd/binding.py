@@ -1,0 +1,328 @@
+"""ctypes binding of libla_pbd.so (include/la_pbd.h).
+
+Argument marshalling only: every step of the PBD window step runs in the HIP
+library.  torch supplies device memory and the current stream.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
+from typing import Optional
+
+import torch
+
+from . import synth
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_pbd.so")
+
+LA_W_BF16, LA_W_INT4 = 0, 1
+LA_EPI_NONE, LA_EPI_SILU_GATE = 0, 1
+LA_DERR_TOKEN_ID, LA_DERR_CAPACITY, LA_DERR_BLOCK_ID = 1, 2, 4
+
+EXPORTED = [
+    "la_int4_embed_gather", "la_wgemm_workspace", "la_wgemm", "la_pbd_attention_workspace",
+    "la_pbd_attention", "la_lm_head_argmax_workspace", "la_lm_head_argmax", "la_pbd_layer",
+    "la_pbd_step_workspace", "la_pbd_step", "la_status_str",
+]
+
+
+class LaWeight(ctypes.Structure):
+    _fields_ = [("fmt", c_int32), ("n", c_int32), ("k", c_int32), ("group", c_int32),
+                ("data", c_void_p), ("scales", c_void_p)]
+
+
+class LaLayer(ctypes.Structure):
+    _fields_ = [("in_norm", c_void_p), ("post_norm", c_void_p), ("qkv", LaWeight),
+                ("qkv_bias", c_void_p), ("o", LaWeight), ("gate_up", LaWeight),
+                ("down", LaWeight)]
+
+
+class LaModel(ctypes.Structure):
+    _fields_ = [("hidden", c_int32), ("n_heads", c_int32), ("n_kv_heads", c_int32),
+                ("head_dim", c_int32), ("inter", c_int32), ("n_layers", c_int32),
+                ("vocab", c_int32), ("rms_eps", c_float), ("rope_theta", c_float),
+                ("layers", POINTER(LaLayer)), ("embed", LaWeight), ("lm_head", LaWeight),
+                ("final_norm", c_void_p)]
+
+
+class LaKvCache(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("block_table", c_void_p),
+                ("num_blocks", c_int32), ("max_blocks", c_int32), ("block_size", c_int32),
+                ("n_layers", c_int32)]
+
+
+class LaError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libla_pbd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise LaError(f"{_LIB_PATH} is missing: build it with box_decoding_amd.build.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    W = POINTER(LaWeight)
+    sig = {
+        "la_int4_embed_gather": (c_int32, [c_void_p, c_int32, W, c_void_p, c_void_p, c_void_p]),
+        "la_wgemm_workspace": (c_size_t, [c_int32, W, c_int32]),
+        "la_wgemm": (c_int32, [c_void_p, c_int32, W, c_void_p, c_float, c_void_p, c_void_p, c_int32,
+                               c_void_p, c_void_p, c_size_t, c_void_p]),
+        "la_pbd_attention_workspace": (c_size_t, [c_int32] * 6),
+        "la_pbd_attention": (c_int32, [c_void_p, POINTER(LaKvCache), c_int32, c_int32, c_int32,
+                                       c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
+        "la_lm_head_argmax_workspace": (c_size_t, [c_int32, W]),
+        "la_lm_head_argmax": (c_int32, [c_void_p, c_int32, W, c_void_p, c_float, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "la_pbd_layer": (c_int32, [POINTER(LaModel), c_int32, POINTER(LaKvCache), c_void_p,
+                                   c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                   c_void_p, c_size_t, c_void_p]),
+        "la_pbd_step_workspace": (c_size_t, [POINTER(LaModel), c_int32, c_int32, c_int32]),
+        "la_pbd_step": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
+                                  c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_size_t, c_void_p, c_void_p]),
+        "la_status_str": (ctypes.c_char_p, [c_int32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().la_status_str(status).decode()
+        raise LaError(f"{what} failed: {msg} ({status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream():
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise LaError("every tensor handed to the library must live on the GPU")
+
+
+def weight_desc(w: dict) -> LaWeight:
+    if w is None:
+        return LaWeight(LA_W_BF16, 0, 0, 0, None, None)
+    fmt = LA_W_BF16 if w["fmt"] == "bf16" else LA_W_INT4
+    _require_cuda(w["data"], w.get("scales"))
+    return LaWeight(fmt, int(w["n"]), int(w["k"]), int(w.get("group") or 0), _ptr(w["data"]),
+                    _ptr(w.get("scales")))
+
+
+class Workspace:
+    """Grow-only device workspace."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _ws(ws: Optional[Workspace]) -> Workspace:
+    if ws is not None:
+        return ws
+    dev = torch.cuda.current_device()
+    if dev not in _default_ws:
+        _default_ws[dev] = Workspace(f"cuda:{dev}")
+    return _default_ws[dev]
+
+
+class DeviceModel:
+    """A model dict (from synth.make_model, tensors on the GPU) plus its ABI struct."""
+
+    def __init__(self, model: dict):
+        d: synth.ModelDims = model["dims"]
+        self.model = model
+        self.dims = d
+        self.layers = (LaLayer * d.n_layers)()
+        for i, lay in enumerate(model["layers"]):
+            _require_cuda(lay["in_norm"], lay["post_norm"], lay.get("qkv_bias"))
+            self.layers[i] = LaLayer(_ptr(lay["in_norm"]), _ptr(lay["post_norm"]),
+                                     weight_desc(lay["qkv"]), _ptr(lay.get("qkv_bias")),
+                                     weight_desc(lay["o"]), weight_desc(lay["gate_up"]),
+                                     weight_desc(lay["down"]))
+        self.struct = LaModel(d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.inter, d.n_layers,
+                              d.vocab, d.rms_eps, d.rope_theta,
+                              ctypes.cast(self.layers, POINTER(LaLayer)),
+                              weight_desc(model["embed"]), weight_desc(model.get("lm_head")),
+                              _ptr(model["final_norm"]))
+
+
+class DeviceCache:
+    """A paged cache dict (from synth.make_cache, tensors on the GPU) plus its ABI struct."""
+
+    def __init__(self, cache: dict, n_layers: int):
+        _require_cuda(cache["k"], cache["v"], cache["block_table"])
+        self.cache = cache
+        self.struct = LaKvCache(_ptr(cache["k"]), _ptr(cache["v"]), _ptr(cache["block_table"]),
+                                int(cache["num_blocks"]), int(cache["max_blocks"]),
+                                int(cache["block"]), int(n_layers))
+
+
+# ---------------------------------------------------------------- entry points
+
+def embed_gather(ids: torch.Tensor, emb: dict, err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load()
+    _require_cuda(ids, err)
+    ids = ids.to(torch.int32).contiguous().view(-1)
+    out = torch.empty((ids.numel(), int(emb["k"])), dtype=torch.float32, device=ids.device)
+    wd = weight_desc(emb)
+    _check(lib.la_int4_embed_gather(_ptr(ids), ids.numel(), ctypes.byref(wd), _ptr(out), _ptr(err),
+                                    _stream()), "la_int4_embed_gather")
+    return out
+
+
+def wgemm(x: torch.Tensor, w: dict, norm_gain=None, eps: float = 1e-6, bias=None, residual=None,
+          silu_gate: bool = False, out: Optional[torch.Tensor] = None,
+          ws: Optional[Workspace] = None) -> torch.Tensor:
+    lib = load()
+    _require_cuda(x, norm_gain, bias, residual)
+    M = x.shape[0]
+    wd = weight_desc(w)
+    epi = LA_EPI_SILU_GATE if silu_gate else LA_EPI_NONE
+    n_out = int(w["n"]) // 2 if silu_gate else int(w["n"])
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.float32, device=x.device)
+    need = lib.la_wgemm_workspace(M, ctypes.byref(wd), epi)
+    buf = _ws(ws).get(need)
+    _check(lib.la_wgemm(_ptr(x), M, ctypes.byref(wd), _ptr(norm_gain), eps, _ptr(bias),
+                        _ptr(residual), epi, _ptr(y), _ptr(buf), buf.numel(), _stream()),
+           "la_wgemm")
+    return y
+
+
+def pbd_attention(q: torch.Tensor, cache: DeviceCache, layer: int, n_heads: int, n_kv_heads: int,
+                  prefix_len: torch.Tensor, B: int, W: int, max_len: int,
+                  ws: Optional[Workspace] = None) -> torch.Tensor:
+    lib = load()
+    _require_cuda(q, prefix_len)
+    out = torch.empty_like(q)
+    need = lib.la_pbd_attention_workspace(B, W, n_heads, n_kv_heads, 128, max_len)
+    buf = _ws(ws).get(need)
+    _check(lib.la_pbd_attention(_ptr(q), ctypes.byref(cache.struct), layer, n_heads, n_kv_heads, 128,
+                                _ptr(prefix_len), B, W, max_len, _ptr(out), _ptr(buf), buf.numel(),
+                                _stream()), "la_pbd_attention")
+    return out
+
+
+def lm_head_argmax(h: torch.Tensor, lm: dict, norm_gain=None, eps: float = 1e-6,
+                   ws: Optional[Workspace] = None):
+    lib = load()
+    _require_cuda(h, norm_gain)
+    M = h.shape[0]
+    wd = weight_desc(lm)
+    ids = torch.empty(M, dtype=torch.int32, device=h.device)
+    top1 = torch.empty(M, dtype=torch.float32, device=h.device)
+    gap = torch.empty(M, dtype=torch.float32, device=h.device)
+    need = lib.la_lm_head_argmax_workspace(M, ctypes.byref(wd))
+    buf = _ws(ws).get(need)
+    _check(lib.la_lm_head_argmax(_ptr(h), M, ctypes.byref(wd), _ptr(norm_gain), eps, _ptr(ids),
+                                 _ptr(top1), _ptr(gap), _ptr(buf), buf.numel(), _stream()),
+           "la_lm_head_argmax")
+    return ids, top1, gap
+
+
+def pbd_layer(model: DeviceModel, layer: int, cache: DeviceCache, x: torch.Tensor,
+              prefix_len: torch.Tensor, B: int, W: int, max_len: int, want_attn: bool = False,
+              ws: Optional[Workspace] = None):
+    lib = load()
+    _require_cuda(x, prefix_len)
+    d = model.dims
+    y = torch.empty_like(x)
+    attn = (torch.empty((B * W, d.n_heads * d.head_dim), dtype=torch.float32, device=x.device)
+            if want_attn else None)
+    need = lib.la_pbd_step_workspace(ctypes.byref(model.struct), B, W, max_len)
+    if need == 0:
+        raise LaError("la_pbd_step_workspace rejected the model or shape")
+    buf = _ws(ws).get(need)
+    _check(lib.la_pbd_layer(ctypes.byref(model.struct), layer, ctypes.byref(cache.struct), _ptr(x),
+                            _ptr(prefix_len), B, W, max_len, _ptr(y), _ptr(attn), _ptr(buf),
+                            buf.numel(), _stream()), "la_pbd_layer")
+    return (y, attn) if want_attn else y
+
+
+def step_workspace_bytes(model: DeviceModel, B: int, W: int, max_len: int) -> int:
+    return int(load().la_pbd_step_workspace(ctypes.byref(model.struct), B, W, max_len))
+
+
+def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
+             prefix_len: torch.Tensor, max_len: int, want_gap: bool = True,
+             want_hidden: bool = False, ws: Optional[Workspace] = None, out_ids=None, out_gap=None,
+             err: Optional[torch.Tensor] = None):
+    """One PBD window step; returns (ids [B,W], gap [B,W] or None, hidden or None)."""
+    lib = load()
+    _require_cuda(window_ids, prefix_len, err)
+    B, W = window_ids.shape
+    dev = window_ids.device
+    ids = out_ids if out_ids is not None else torch.empty((B, W), dtype=torch.int32, device=dev)
+    gap = out_gap if out_gap is not None else (
+        torch.empty((B, W), dtype=torch.float32, device=dev) if want_gap else None)
+    hid = (torch.empty((B * W, model.dims.hidden), dtype=torch.float32, device=dev)
+           if want_hidden else None)
+    need = lib.la_pbd_step_workspace(ctypes.byref(model.struct), B, W, max_len)
+    if need == 0:
+        raise LaError("la_pbd_step_workspace rejected the model or shape")
+    buf = _ws(ws).get(need)
+    _check(lib.la_pbd_step(ctypes.byref(model.struct), ctypes.byref(cache.struct), _ptr(window_ids),
+                           _ptr(prefix_len), B, W, max_len, _ptr(ids), _ptr(gap), _ptr(hid),
+                           _ptr(buf), buf.numel(), _ptr(err), _stream()), "la_pbd_step")
+    return ids, gap, hid
+
+
+class StepGraph:
+    """One la_pbd_step call captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed; inputs and outputs are the tensors given at capture time."""
+
+    def __init__(self, model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
+                 prefix_len: torch.Tensor, max_len: int, out_ids: torch.Tensor,
+                 out_gap: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None,
+                 err: Optional[torch.Tensor] = None):
+        self.args = (model, cache, window_ids, prefix_len, max_len)
+        self.ws = ws or Workspace(window_ids.device)
+        self.out_ids, self.out_gap, self.err = out_ids, out_gap, err
+        side = torch.cuda.Stream(device=window_ids.device)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self._call()  # sizes the workspace before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._call()
+
+    def _call(self):
+        m, c, ids, P, ml = self.args
+        pbd_step(m, c, ids, P, ml, want_gap=self.out_gap is not None, ws=self.ws,
+                 out_ids=self.out_ids, out_gap=self.out_gap, err=self.err)
+
+    def replay(self):
+        self.graph.replay()

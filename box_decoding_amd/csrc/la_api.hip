@@ -1,0 +1,529 @@
+// C ABI of the PBD window step: host-side validation, workspace carving and the
+// launch sequence of every entry point declared in include/la_pbd.h.
+#include <string.h>
+
+#include <algorithm>
+
+#include "la_internal.hpp"
+
+using namespace la;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base((char*)p) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += al(count * sizeof(T));
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int int4_group) {
+  if (!w || !w->data) return LA_ERR_ARG;
+  if (w->n != n || w->k != k) return LA_ERR_SHAPE;
+  if (!aligned16(w->data)) return LA_ERR_ARG;
+  if (w->fmt == LA_W_BF16) return LA_OK;
+  if (w->fmt != LA_W_INT4) return LA_ERR_ARG;
+  if (!allow_int4) return LA_ERR_UNSUPPORTED;
+  if (!w->scales || w->group != int4_group || k % int4_group) return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
+la_status check_gemm_weight(const la_weight* w) {
+  if (!w || !w->data) return LA_ERR_ARG;
+  if (w->n < 1 || w->k < 256 || w->k % 256) return LA_ERR_SHAPE;
+  return check_weight(w, w->n, w->k, true, 128);
+}
+
+// ---------------------------------------------------------------- workspace plans
+
+int gemm_parts(int M, const la_weight* w, int epi) {
+  return plan_gemm(M, w->n, w->k, w->fmt == LA_W_INT4, epi, true).grid;
+}
+
+struct StepWs {
+  float* h;
+  float* q;
+  float* o;
+  float* mlp;
+  uint16_t* apack;    // packed operand with K <= max(hidden, heads * head_dim)
+  float* asum;
+  uint16_t* apack_m;  // packed MLP activations (K = inter)
+  float* asum_m;
+  float2* rope;
+  int32_t* flags;
+  float* part_o;
+  float* part_ml;
+  float* amax;
+  int pps, max_splits, nqp, vocab_parts;
+  size_t bytes;
+};
+
+StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool lm_head) {
+  StepWs s;
+  Carver c(ws);
+  const int T = B * W;
+  const int H = m->hidden, HQ = m->n_heads * m->head_dim, F = m->inter;
+  const int Kx = H > HQ ? H : HQ;
+  s.h = c.take<float>((size_t)T * H);
+  s.q = c.take<float>((size_t)T * HQ);
+  s.o = c.take<float>((size_t)T * HQ);
+  s.mlp = c.take<float>((size_t)T * F);
+  s.apack = c.take<uint16_t>(apack_elems(T, Kx));
+  s.asum = c.take<float>((size_t)((T + 7) / 8) * (Kx / 128) * 16);
+  s.apack_m = c.take<uint16_t>(apack_elems(T, F));
+  s.asum_m = c.take<float>((size_t)((T + 7) / 8) * (F / 128) * 16);
+  s.rope = c.take<float2>((size_t)T * 64);
+  s.flags = c.take<int32_t>(T);
+  plan_attention(B, m->n_kv_heads, max_len, &s.pps, &s.max_splits);
+  s.nqp = attn_nqp(W, m->n_heads / m->n_kv_heads);
+  const size_t units = (size_t)B * m->n_kv_heads * s.max_splits * s.nqp;
+  s.part_o = c.take<float>(units * kHeadDim);
+  s.part_ml = c.take<float>(units * 2);
+  const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
+  s.vocab_parts = gemm_parts(T, lm, EPI_ARGMAX);
+  s.amax = lm_head ? c.take<float>((size_t)T * s.vocab_parts * 3) : nullptr;
+  s.bytes = c.off;
+  return s;
+}
+
+la_status check_model(const la_model* m) {
+  if (!m || !m->layers) return LA_ERR_ARG;
+  if (m->head_dim != kHeadDim || m->n_kv_heads < 1 || m->n_heads < m->n_kv_heads ||
+      m->n_heads % m->n_kv_heads || m->hidden < 256 || m->hidden % 256 ||
+      (m->n_heads * m->head_dim) % 256 || m->inter < 256 || m->inter % 256 || m->n_layers < 1 ||
+      m->vocab < 1 || !(m->rms_eps > 0.f) || !(m->rope_theta > 1.f))
+    return LA_ERR_SHAPE;
+  const int H = m->hidden, HQ = m->n_heads * m->head_dim;
+  const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+  const int fmt = m->layers[0].qkv.fmt;
+  if (fmt != LA_W_BF16 && fmt != LA_W_INT4) return LA_ERR_ARG;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const la_layer& L = m->layers[l];
+    if (!L.in_norm || !L.post_norm) return LA_ERR_ARG;
+    if (!aligned16(L.in_norm) || !aligned16(L.post_norm)) return LA_ERR_ARG;
+    la_status st;
+    if ((st = check_weight(&L.qkv, NQKV, H, true, 128)) != LA_OK) return st;
+    if ((st = check_weight(&L.o, H, HQ, true, 128)) != LA_OK) return st;
+    if ((st = check_weight(&L.gate_up, 2 * m->inter, H, true, 128)) != LA_OK) return st;
+    if ((st = check_weight(&L.down, H, m->inter, true, 128)) != LA_OK) return st;
+    if (L.qkv.fmt != fmt || L.o.fmt != fmt || L.gate_up.fmt != fmt || L.down.fmt != fmt)
+      return LA_ERR_UNSUPPORTED;
+  }
+  if (!m->final_norm || !aligned16(m->final_norm)) return LA_ERR_ARG;
+  if (fmt == LA_W_BF16) {
+    la_status st = check_weight(&m->embed, m->vocab, H, false, 0);
+    if (st != LA_OK) return st;
+    if (m->lm_head.data) {
+      if ((st = check_weight(&m->lm_head, m->vocab, H, false, 0)) != LA_OK) return st;
+    }
+  } else {
+    la_status st = check_weight(&m->embed, m->vocab, H, true, 32);
+    if (st != LA_OK) return st;
+    if (!m->lm_head.data) return LA_ERR_ARG;
+    if ((st = check_weight(&m->lm_head, m->vocab, H, true, 128)) != LA_OK) return st;
+  }
+  return LA_OK;
+}
+
+la_status check_cache(const la_kv_cache* kv, const la_model* m, int B) {
+  if (!kv || !kv->k || !kv->v || !kv->block_table) return LA_ERR_ARG;
+  if (kv->block_size != kBlock || kv->num_blocks < 1 || kv->max_blocks < 1) return LA_ERR_SHAPE;
+  if (m && kv->n_layers < m->n_layers) return LA_ERR_SHAPE;
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return LA_ERR_ARG;
+  (void)B;
+  return LA_OK;
+}
+
+la_status check_step_shape(const la_model* m, int B, int W, int max_len) {
+  if (B < 1 || B > 64 || W < 1 || W > 8 || max_len < W) return LA_ERR_SHAPE;
+  if (W * (m->n_heads / m->n_kv_heads) > 64) return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
+la_status hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+#define LA_TRY(expr)                          \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return LA_ERR_HIP;  \
+  } while (0)
+
+size_t kv_layer_elems(const la_kv_cache* kv, const la_model* m) {
+  return (size_t)kv->num_blocks * m->n_kv_heads * kBlock * kHeadDim;
+}
+
+GemmArgs base_gemm(const la_weight* w, int M) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.w = w->data;
+  g.wscale = (const uint16_t*)w->scales;
+  g.M = M;
+  g.N = w->n;
+  g.K = w->k;
+  return g;
+}
+
+// GEMM whose activations are fp32 rows x (RMSNorm'd when gain != NULL): packed
+// by the GEMM's own workgroups when M is small, else by one packing launch.
+la_status gemm_from_rows(GemmArgs g, const float* x, int ldx, const uint16_t* gain, float eps,
+                         uint16_t* apack, float* asum, int epi, bool int4, hipStream_t st) {
+  const GemmPlan p = plan_gemm(g.M, g.N, g.K, int4, epi, true);
+  if (p.lds) {
+    g.x = x;
+    g.ldx = ldx;
+    g.gain = gain;
+    g.eps = eps;
+  } else {
+    LA_TRY(launch_pack({x, ldx, g.M, g.K, gain, eps, apack, asum, int4}, st));
+    g.apack = apack;
+    g.asum = asum;
+  }
+  LA_TRY(launch_gemm(g, epi, int4, st));
+  return LA_OK;
+}
+
+// One decoder layer on the rows in s.h (in place).
+la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
+                    int B, int W, int max_len, const StepWs& s, float* attn_out,
+                    hipStream_t st) {
+  const la_layer& L = m->layers[l];
+  const int T = B * W;
+  const int H = m->hidden, HQ = m->n_heads * m->head_dim, F = m->inter;
+  const bool int4 = L.qkv.fmt == LA_W_INT4;
+  const size_t le = kv_layer_elems(kv, m);
+  la_status rs;
+
+  // RMSNorm + QKV + bias + RoPE + K/V write
+  GemmArgs g = base_gemm(&L.qkv, T);
+  g.bias = L.qkv_bias;
+  g.y = s.q;
+  g.ldy = HQ;
+  g.rope = s.rope;
+  g.prefix_len = prefix_len;
+  g.flags = s.flags;
+  g.W = W;
+  g.n_heads = m->n_heads;
+  g.n_kv_heads = m->n_kv_heads;
+  g.block_table = kv->block_table;
+  g.max_blocks = kv->max_blocks;
+  g.num_blocks = kv->num_blocks;
+  g.kc = (uint16_t*)kv->k + (size_t)l * le;
+  g.vc = (uint16_t*)kv->v + (size_t)l * le;
+  if ((rs = gemm_from_rows(g, s.h, H, L.in_norm, m->rms_eps, s.apack, s.asum, EPI_QKV, int4, st)) != LA_OK)
+    return rs;
+
+  // window attention -> packed O-projection operand
+  AttnArgs at;
+  memset(&at, 0, sizeof(at));
+  at.q = s.q;
+  at.kc = g.kc;
+  at.vc = g.vc;
+  at.block_table = kv->block_table;
+  at.prefix_len = prefix_len;
+  at.B = B;
+  at.W = W;
+  at.Hq = m->n_heads;
+  at.Hkv = m->n_kv_heads;
+  at.num_blocks = kv->num_blocks;
+  at.max_blocks = kv->max_blocks;
+  at.cap = std::min(max_len, kv->max_blocks * kBlock);
+  at.pages_per_split = s.pps;
+  at.max_splits = s.max_splits;
+  at.part_o = s.part_o;
+  at.part_ml = s.part_ml;
+  at.nqp = s.nqp;
+  at.out = (int4 || attn_out) ? (attn_out ? attn_out : s.o) : nullptr;
+  at.out_apack = int4 ? nullptr : s.apack;
+  at.out_int4 = false;
+  LA_TRY(launch_attention(at, st));
+  if (int4) LA_TRY(launch_pack({at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true}, st));
+
+  // O projection + residual
+  g = base_gemm(&L.o, T);
+  g.apack = s.apack;
+  g.asum = s.asum;
+  g.residual = s.h;
+  g.y = s.h;
+  g.ldy = H;
+  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
+
+  // RMSNorm + gate/up + SiLU (bf16: packed straight into the down operand)
+  g = base_gemm(&L.gate_up, T);
+  if (int4) {
+    g.y = s.mlp;
+    g.ldy = F;
+  } else {
+    g.y_apack = s.apack_m;
+  }
+  if ((rs = gemm_from_rows(g, s.h, H, L.post_norm, m->rms_eps, s.apack, s.asum, EPI_SILU, int4, st)) != LA_OK)
+    return rs;
+  if (int4) LA_TRY(launch_pack({s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true}, st));
+
+  // down + residual
+  g = base_gemm(&L.down, T);
+  g.apack = s.apack_m;
+  g.asum = s.asum_m;
+  g.residual = s.h;
+  g.y = s.h;
+  g.ldy = H;
+  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
+  return LA_OK;
+}
+
+PrologueArgs base_prologue(const la_model* m, const la_kv_cache* kv, const int32_t* prefix_len,
+                           int B, int W, int max_len, const StepWs& s) {
+  PrologueArgs p;
+  memset(&p, 0, sizeof(p));
+  p.T = B * W;
+  p.prefix_len = prefix_len;
+  p.W = W;
+  p.rope = s.rope;
+  p.rope_theta = m->rope_theta;
+  p.flags = s.flags;
+  p.block_table = kv->block_table;
+  p.max_blocks = kv->max_blocks;
+  p.num_blocks = kv->num_blocks;
+  p.cap = std::min(max_len, kv->max_blocks * kBlock);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_str(int32_t status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_ERR_ARG: return "invalid argument";
+    case LA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_UNSUPPORTED: return "unsupported request";
+    case LA_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+la_status la_int4_embed_gather(const int32_t* ids, int32_t T, const la_weight* emb, float* out,
+                               int32_t* err, hipStream_t stream) {
+  if (!ids || !emb || !out || !emb->data || T < 0) return LA_ERR_ARG;
+  if (emb->k < 8 || emb->k % 8 || emb->n < 1) return LA_ERR_SHAPE;
+  if (emb->fmt == LA_W_INT4) {
+    if (!emb->scales || emb->group < 8 || emb->group % 8 || emb->k % emb->group) return LA_ERR_SHAPE;
+  } else if (emb->fmt != LA_W_BF16) {
+    return LA_ERR_ARG;
+  }
+  if (!aligned16(out) || !aligned16(emb->data)) return LA_ERR_ARG;
+  if (T == 0) return LA_OK;
+  PrologueArgs p;
+  memset(&p, 0, sizeof(p));
+  p.ids = ids;
+  p.T = T;
+  p.emb = *emb;
+  p.out = out;
+  p.err = err;
+  return hip_status(launch_prologue(p, stream));
+}
+
+size_t la_wgemm_workspace(int32_t M, const la_weight* w, int32_t epilogue) {
+  if (!w || M < 1 || w->k < 256) return 0;
+  Carver c(nullptr);
+  c.take<uint16_t>(apack_elems(M, w->k));
+  c.take<float>((size_t)((M + 7) / 8) * (w->k / 128) * 16);
+  (void)epilogue;
+  return c.off;
+}
+
+la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t* norm_gain,
+                   float rms_eps, const uint16_t* bias, const float* residual, int32_t epilogue,
+                   float* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !y || !w) return LA_ERR_ARG;
+  if (epilogue != LA_EPI_NONE && epilogue != LA_EPI_SILU_GATE) return LA_ERR_ARG;
+  if (M < 1 || M > 512) return LA_ERR_SHAPE;
+  la_status st = check_gemm_weight(w);
+  if (st != LA_OK) return st;
+  const int epi = epilogue == LA_EPI_SILU_GATE ? EPI_SILU : EPI_STORE;
+  if (epi == EPI_SILU && (w->n % 16 || bias || residual)) return LA_ERR_SHAPE;
+  if (!aligned16(x) || (norm_gain && !aligned16(norm_gain))) return LA_ERR_ARG;
+  if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
+  const size_t need = la_wgemm_workspace(M, w, epilogue);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  const bool int4 = w->fmt == LA_W_INT4;
+  Carver c(workspace);
+  uint16_t* apack = c.take<uint16_t>(apack_elems(M, w->k));
+  float* asum = c.take<float>((size_t)((M + 7) / 8) * (w->k / 128) * 16);
+  GemmArgs g = base_gemm(w, M);
+  g.bias = bias;
+  g.residual = residual;
+  g.y = y;
+  g.ldy = epi == EPI_SILU ? w->n / 2 : w->n;
+  return gemm_from_rows(g, x, w->k, norm_gain, rms_eps, apack, asum, epi, int4, stream);
+}
+
+size_t la_pbd_attention_workspace(int32_t B, int32_t W, int32_t n_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t max_len) {
+  if (B < 1 || W < 1 || n_kv_heads < 1 || n_heads < n_kv_heads || head_dim != kHeadDim ||
+      max_len < 1)
+    return 0;
+  int pps, ms;
+  plan_attention(B, n_kv_heads, max_len, &pps, &ms);
+  const size_t units = (size_t)B * n_kv_heads * ms * attn_nqp(W, n_heads / n_kv_heads);
+  Carver c(nullptr);
+  c.take<float>(units * kHeadDim);
+  c.take<float>(units * 2);
+  return c.off;
+}
+
+la_status la_pbd_attention(const float* q, const la_kv_cache* kv, int32_t layer, int32_t n_heads,
+                           int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
+                           int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !out || !prefix_len) return LA_ERR_ARG;
+  la_status st = check_cache(kv, nullptr, B);
+  if (st != LA_OK) return st;
+  if (head_dim != kHeadDim || n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads)
+    return LA_ERR_SHAPE;
+  if (B < 1 || B > 64 || W < 1 || W > 8 || W * (n_heads / n_kv_heads) > 64 || max_len < 1)
+    return LA_ERR_SHAPE;
+  if (layer < 0 || layer >= kv->n_layers) return LA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out)) return LA_ERR_ARG;
+  const size_t need = la_pbd_attention_workspace(B, W, n_heads, n_kv_heads, head_dim, max_len);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  AttnArgs at;
+  memset(&at, 0, sizeof(at));
+  const size_t le = (size_t)kv->num_blocks * n_kv_heads * kBlock * kHeadDim;
+  at.q = q;
+  at.kc = (const uint16_t*)kv->k + (size_t)layer * le;
+  at.vc = (const uint16_t*)kv->v + (size_t)layer * le;
+  at.block_table = kv->block_table;
+  at.prefix_len = prefix_len;
+  at.B = B;
+  at.W = W;
+  at.Hq = n_heads;
+  at.Hkv = n_kv_heads;
+  at.num_blocks = kv->num_blocks;
+  at.max_blocks = kv->max_blocks;
+  at.cap = std::min(max_len, kv->max_blocks * kBlock);
+  plan_attention(B, n_kv_heads, max_len, &at.pages_per_split, &at.max_splits);
+  at.nqp = attn_nqp(W, n_heads / n_kv_heads);
+  Carver c(workspace);
+  const size_t units = (size_t)B * n_kv_heads * at.max_splits * at.nqp;
+  at.part_o = c.take<float>(units * kHeadDim);
+  at.part_ml = c.take<float>(units * 2);
+  at.out = out;
+  return hip_status(launch_attention(at, stream));
+}
+
+size_t la_lm_head_argmax_workspace(int32_t M, const la_weight* lm) {
+  if (!lm || M < 1 || lm->k < 256) return 0;
+  Carver c(nullptr);
+  c.take<uint16_t>(apack_elems(M, lm->k));
+  c.take<float>((size_t)((M + 7) / 8) * (lm->k / 128) * 16);
+  c.take<float>((size_t)M * gemm_parts(M, lm, EPI_ARGMAX) * 3);
+  return c.off;
+}
+
+la_status la_lm_head_argmax(const float* h, int32_t M, const la_weight* lm,
+                            const uint16_t* norm_gain, float rms_eps, int32_t* ids, float* top1,
+                            float* gap, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (!h || !ids || !lm) return LA_ERR_ARG;
+  if (M < 1 || M > 512) return LA_ERR_SHAPE;
+  la_status st = check_gemm_weight(lm);
+  if (st != LA_OK) return st;
+  if (!aligned16(h) || (norm_gain && !aligned16(norm_gain))) return LA_ERR_ARG;
+  if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
+  const size_t need = la_lm_head_argmax_workspace(M, lm);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  const bool int4 = lm->fmt == LA_W_INT4;
+  Carver c(workspace);
+  uint16_t* apack = c.take<uint16_t>(apack_elems(M, lm->k));
+  float* asum = c.take<float>((size_t)((M + 7) / 8) * (lm->k / 128) * 16);
+  const int parts = gemm_parts(M, lm, EPI_ARGMAX);
+  float* amax = c.take<float>((size_t)M * parts * 3);
+  GemmArgs g = base_gemm(lm, M);
+  g.amax = amax;
+  if ((st = gemm_from_rows(g, h, lm->k, norm_gain, rms_eps, apack, asum, EPI_ARGMAX, int4, stream)) != LA_OK)
+    return st;
+  return hip_status(launch_argmax_reduce(amax, M, parts, nullptr, ids, top1, gap, nullptr, stream));
+}
+
+la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, const float* x,
+                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len, float* y,
+                       float* attn_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  la_status st = check_model(m);
+  if (st != LA_OK) return st;
+  if ((st = check_cache(kv, m, B)) != LA_OK) return st;
+  if ((st = check_step_shape(m, B, W, max_len)) != LA_OK) return st;
+  if (!x || !y || !prefix_len) return LA_ERR_ARG;
+  if (layer < 0 || layer >= m->n_layers) return LA_ERR_ARG;
+  if (!aligned16(x) || !aligned16(y) || (attn_out && !aligned16(attn_out))) return LA_ERR_ARG;
+  const size_t need = carve_step(m, B, W, max_len, nullptr, false).bytes;
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  StepWs s = carve_step(m, B, W, max_len, workspace, false);
+  const int T = B * W;
+  const int H = m->hidden;
+  s.h = y;  // the layer runs in place on y
+  if (y != x) LA_TRY(hipMemcpyAsync(y, x, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice, stream));
+  PrologueArgs p = base_prologue(m, kv, prefix_len, B, W, max_len, s);
+  LA_TRY(launch_prologue(p, stream));
+  return run_layer(m, layer, kv, prefix_len, B, W, max_len, s, attn_out, stream);
+}
+
+size_t la_pbd_step_workspace(const la_model* m, int32_t B, int32_t W, int32_t max_len) {
+  if (check_model(m) != LA_OK || B < 1 || W < 1 || max_len < W) return 0;
+  return carve_step(m, B, W, max_len, nullptr, true).bytes;
+}
+
+la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                      const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
+                      int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
+                      size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  la_status st = check_model(m);
+  if (st != LA_OK) return st;
+  if ((st = check_cache(kv, m, B)) != LA_OK) return st;
+  if ((st = check_step_shape(m, B, W, max_len)) != LA_OK) return st;
+  if (!window_ids || !prefix_len || !out_ids) return LA_ERR_ARG;
+  if (out_hidden && !aligned16(out_hidden)) return LA_ERR_ARG;
+  const size_t need = carve_step(m, B, W, max_len, nullptr, true).bytes;
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  const StepWs s = carve_step(m, B, W, max_len, workspace, true);
+  const int T = B * W;
+  const int H = m->hidden;
+
+  PrologueArgs p = base_prologue(m, kv, prefix_len, B, W, max_len, s);
+  p.ids = window_ids;
+  p.emb = m->embed;
+  p.out = s.h;
+  p.err = err;
+  LA_TRY(launch_prologue(p, stream));
+  for (int l = 0; l < m->n_layers; ++l) {
+    st = run_layer(m, l, kv, prefix_len, B, W, max_len, s, nullptr, stream);
+    if (st != LA_OK) return st;
+  }
+  if (out_hidden)
+    LA_TRY(hipMemcpyAsync(out_hidden, s.h, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice,
+                          stream));
+  const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
+  const bool int4 = lm->fmt == LA_W_INT4;
+  GemmArgs g = base_gemm(lm, T);
+  g.amax = s.amax;
+  if ((st = gemm_from_rows(g, s.h, H, m->final_norm, m->rms_eps, s.apack, s.asum, EPI_ARGMAX, int4,
+                           stream)) != LA_OK)
+    return st;
+  return hip_status(launch_argmax_reduce(s.amax, T, s.vocab_parts, s.flags, out_ids, nullptr, out_gap,
+                                         nullptr, stream));
+}
+
+}  // extern "C"

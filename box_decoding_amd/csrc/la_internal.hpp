@@ -1,0 +1,119 @@
+// Internal launch interface shared by the kernels' translation units and the
+// C ABI layer.  Everything here is host code plus argument structs.
+#pragma once
+
+#include "la_common.hpp"
+
+namespace la {
+
+enum GemmEpi { EPI_STORE = 0, EPI_SILU = 1, EPI_QKV = 2, EPI_ARGMAX = 3 };
+
+// Arguments of one small-M GEMM launch (rows m_base .. m_base+31 at most).
+struct GemmArgs {
+  // Activation source: either fp32 rows x (packed in LDS by the workgroup,
+  // with the RMSNorm when gain != NULL) or pre-packed rows in global memory.
+  const float* x;            // fp32 [M][ldx] (LDS packing mode)
+  int ldx;
+  const uint16_t* gain;      // RMSNorm gain (nullable)
+  float eps;
+  const uint16_t* apack;     // packed activations of all M rows (global mode)
+  const float* asum;         // INT4 only: [MT][K/128][16] per-group sums of the packed rows
+  const void* w;             // weight data
+  const uint16_t* wscale;    // INT4 scales [N][K/128]
+  int M;                     // total rows of the problem
+  int m_base;                // first row handled by this launch (multiple of 32)
+  int N, K;                  // weight rows / reduction length
+  int n_tiles;               // column tiles (16 columns each)
+  int nt;                    // column tiles per workgroup
+  int nw;                    // waves per workgroup (nw / nt waves share a tile along K)
+  // epilogue
+  const uint16_t* bias;      // bf16, indexed by weight row (nullable)
+  const float* residual;     // fp32 [M][ldy] (nullable)
+  float* y;                  // fp32 [M][ldy]
+  int ldy;
+  uint16_t* y_apack;         // SiLU epilogue: also pack the output rows here (nullable)
+  // QKV epilogue
+  const float2* rope;        // [M][64] (cos, sin) of the row's position
+  const int32_t* prefix_len; // [B]
+  const int32_t* flags;      // [M] nonzero: row must not write the cache (nullable)
+  int W, n_heads, n_kv_heads;
+  const int32_t* block_table;
+  int max_blocks, num_blocks;
+  uint16_t* kc;              // layer base of the K pages
+  uint16_t* vc;              // layer base of the V pages
+  // ARGMAX epilogue
+  float* amax;               // [M][n_parts][3] (top1, index bits, top2), one part per workgroup
+  int n_parts;
+};
+
+struct PackArgs {
+  const float* x;
+  int ldx;
+  int M, K;
+  const uint16_t* gain;  // nullable: no RMSNorm
+  float eps;
+  uint16_t* apack;
+  float* asum;           // INT4 only (nullable otherwise)
+  bool int4;
+};
+
+struct AttnArgs {
+  const float* q;            // [B*W][Hq*D]
+  const uint16_t* kc;        // layer base of the K pages
+  const uint16_t* vc;        // layer base of the V pages
+  const int32_t* block_table;
+  const int32_t* prefix_len;
+  int B, W, Hq, Hkv;
+  int num_blocks, max_blocks;
+  int cap;                   // key capacity bound (min(max_len, max_blocks*16))
+  int pages_per_split;
+  int max_splits;            // splits per (b, kv head)
+  float* part_o;             // [B][Hkv][max_splits][NQP][D]
+  float* part_ml;            // [B][Hkv][max_splits][NQP][2]
+  float* out;                // fp32 [B*W][Hq*D] (nullable)
+  uint16_t* out_apack;       // packed output for the next GEMM (nullable)
+  bool out_int4;
+  int nqp;                   // padded queries per kv head (multiple of 16)
+};
+
+struct PrologueArgs {
+  const int32_t* ids;        // [T] (nullable: no gather)
+  int T;
+  la_weight emb;
+  float* out;                // fp32 [T][H]
+  int32_t* err;              // nullable
+  // step bookkeeping (all nullable)
+  const int32_t* prefix_len; // [B]
+  int W;
+  float2* rope;              // [T][64]
+  double rope_theta;
+  int32_t* flags;            // [T]
+  const int32_t* block_table;
+  int max_blocks, num_blocks, cap;
+};
+
+struct GemmPlan {
+  int n_tiles;
+  int nt, nw;
+  int mt;        // row tiles per launch (1, 2 or 4)
+  int launches;  // ceil(M / 32)
+  bool lds;      // activations packed in LDS by each workgroup
+  int grid;      // workgroups per launch
+  size_t smem;   // dynamic LDS bytes
+};
+
+GemmPlan plan_gemm(int M, int N, int K, bool int4, int epi, bool x_available);
+
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s);
+hipError_t launch_argmax_reduce(const float* amax, int M, int n_tiles, const int32_t* flags,
+                                int32_t* ids, float* top1, float* gap, int32_t* err,
+                                hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// attention split planning
+void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits);
+inline int attn_nqp(int W, int G) { return ((W * G + 15) / 16) * 16; }
+
+}  // namespace la

@@ -1,0 +1,91 @@
+// Step prologue: embedding gather (bf16 rows or INT4 group-32 rows), the RoPE
+// cos/sin of every window position and per-row data-error flags.
+#include "la_internal.hpp"
+
+namespace la {
+
+// One workgroup per window row t.
+__global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  int id_bad = 0;
+  if (a.ids) {
+    const int id = a.ids[t];
+    const int K = a.emb.k;
+    float* out = a.out + (size_t)t * K;
+    id_bad = (id < 0 || id >= a.emb.n);
+    if (id_bad) {
+      for (int k = tid * 4; k < K; k += 1024) *(float4*)(out + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (a.emb.fmt == LA_W_BF16) {
+      const uint16_t* row = (const uint16_t*)a.emb.data + (size_t)id * K;
+      for (int k = tid * 8; k < K; k += 2048) {
+        const uint4 w = *(const uint4*)(row + k);
+        *(float4*)(out + k) = make_float4(bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16),
+                                          bf16_to_f32(w.y & 0xFFFFu), bf16_to_f32(w.y >> 16));
+        *(float4*)(out + k + 4) = make_float4(bf16_to_f32(w.z & 0xFFFFu), bf16_to_f32(w.z >> 16),
+                                              bf16_to_f32(w.w & 0xFFFFu), bf16_to_f32(w.w >> 16));
+      }
+    } else {
+      // INT4: element j = (q_j - 8) * scale[j / group], q_j the low nibble of byte
+      // j/2 for even j and its high nibble for odd j (exact in fp32).
+      const uint8_t* row = (const uint8_t*)a.emb.data + (size_t)id * (K / 2);
+      const uint16_t* sc = (const uint16_t*)a.emb.scales + (size_t)id * (K / a.emb.group);
+      for (int k = tid * 8; k < K; k += 2048) {
+        const uint32_t w = *(const uint32_t*)(row + k / 2);
+        const float s = fp16_to_f32(sc[k / a.emb.group]);
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (float)((int)((w >> (4 * j)) & 0xFu) - 8) * s;
+        *(float4*)(out + k) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)(out + k + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+
+  if (a.prefix_len) {
+    const int b = t / a.W, j = t - b * a.W;
+    const int P = a.prefix_len[b];
+    const long pos = (long)P + j;
+    if (a.rope && tid < 64) {
+      // angle = pos * theta^(-2i/128), evaluated in fp64, stored as fp32 cos/sin
+      const double inv_freq = pow(a.rope_theta, -2.0 * (double)tid / (double)kHeadDim);
+      const double ang = (double)pos * inv_freq;
+      a.rope[(size_t)t * 64 + tid] = make_float2((float)cos(ang), (float)sin(ang));
+    }
+    if (a.flags) {
+      // a data error anywhere in the window poisons the whole sequence (its rows
+      // attend to each other)
+      int f = 0;
+      if (a.ids) {
+        for (int jj = 0; jj < a.W; ++jj) {
+          const int idj = a.ids[b * a.W + jj];
+          if (idj < 0 || idj >= a.emb.n) f = LA_DERR_TOKEN_ID;
+        }
+      }
+      const long n = (long)P + a.W;
+      if (P < 0 || n > a.cap) f |= LA_DERR_CAPACITY;
+      int blk_bad = 0;
+      if (!(f & LA_DERR_CAPACITY)) {
+        const int pages = (int)((n + kBlock - 1) / kBlock);
+        for (int p = tid; p < pages; p += 256) {
+          const int blk = a.block_table[(size_t)b * a.max_blocks + p];
+          if (blk < 0 || blk >= a.num_blocks) blk_bad = 1;
+        }
+      }
+      if (__syncthreads_or(blk_bad)) f |= LA_DERR_BLOCK_ID;
+      if (tid == 0) {
+        a.flags[t] = f;
+        if (f && a.err) atomicOr(a.err, f);
+      }
+    }
+  } else if (id_bad && a.err && tid == 0) {
+    atomicOr(a.err, LA_DERR_TOKEN_ID);
+  }
+}
+
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_prologue, dim3(a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,206 @@
+/*
+ * la_pbd.h — C ABI of the MI355X (gfx950) Parallel Box Decoding window step.
+ *
+ * The step: a window of W tokens (the last accepted token followed by mask
+ * tokens) sits at positions P_b .. P_b+W-1 after a cached prefix of P_b tokens.
+ * Its rows go through a Qwen2-style decoder whose attention is causal to the
+ * cached prefix and bidirectional inside the window, and the step ends with a
+ * per-position argmax over the lm_head tied to the input embedding.
+ * Sources: "LocateAnything-3B for RK3588 (RKLLM + RKNN)", section "How it
+ * differs from the original", item 1 (window make-up, bidirectional window,
+ * prefix KV reuse without rollback, original positions); "LocateAnything-3B on
+ * Jetson Orin Nano", Part 1 sections 1.2-1.4 (Qwen2 decoder, block mask, greedy
+ * selection); "LocateAnything-3B — ONNX WebGPU (INT4 + 4-bit embeddings)",
+ * sections "Why this repo exists", "Files", "Embedding gather / dequant (JS
+ * reference)" and "KV-cache graph for in-browser use" (tied lm_head, INT4
+ * formats, GQA KV of 2 heads x 128).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *    buffer; the library allocates and frees nothing and keeps no pointer after
+ *    a call returns.
+ *  - Every call only enqueues work on `stream` and returns; nothing is
+ *    synchronised.  Results are valid once the stream has reached that point.
+ *  - Shape and argument errors are detected on the host before any launch and
+ *    returned as la_status; nothing is enqueued then.  Launch failures return
+ *    LA_ERR_HIP.
+ *  - bf16 values are passed as uint16 bit patterns; fp16 scales likewise.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Supported model shapes: head_dim 128, n_heads a multiple of n_kv_heads,
+ *    hidden, n_heads*head_dim and inter multiples of 256, KV block size 16,
+ *    window 1 <= W <= 8 with W * (n_heads / n_kv_heads) <= 64, batch 1..64.
+ */
+#ifndef LA_PBD_H
+#define LA_PBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_ARG = -1,         /* NULL where required, negative size, bad enum */
+  LA_ERR_SHAPE = -2,       /* shape outside the supported set */
+  LA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than the *_workspace() size */
+  LA_ERR_UNSUPPORTED = -4, /* valid request this build does not implement */
+  LA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} la_status;
+
+/* Weight formats. */
+enum { LA_W_BF16 = 0, LA_W_INT4 = 1 };
+
+/* A weight matrix W[n, k] (y = x . W^T).
+ *  LA_W_BF16: data = bf16 [n][k] row-major, scales = NULL, group ignored.
+ *  LA_W_INT4: group-wise symmetric INT4 (WebGPU page, "Embedding gather /
+ *    dequant"): data = uint8 [n][k/2], byte i of a row holds element 2i in its
+ *    low nibble and element 2i+1 in its high nibble; scales = fp16 [n][k/group];
+ *    element j of row r is (q - 8) * scales[r][j / group].  group is 32 for the
+ *    embedding and 128 for the linears and the lm_head. */
+typedef struct {
+  int32_t fmt;
+  int32_t n;
+  int32_t k;
+  int32_t group;
+  const void* data;
+  const void* scales;
+} la_weight;
+
+/* One decoder layer.  qkv is [q | k | v] stacked along n (n = (Hq + 2 Hkv) D);
+ * gate_up is [gate | up] stacked along n (n = 2 F); o is [H, Hq D]; down is
+ * [H, F].  Gains are bf16 [H]; qkv_bias is bf16 [(Hq + 2 Hkv) D] or NULL. */
+typedef struct {
+  const uint16_t* in_norm;
+  const uint16_t* post_norm;
+  la_weight qkv;
+  const uint16_t* qkv_bias;
+  la_weight o;
+  la_weight gate_up;
+  la_weight down;
+} la_layer;
+
+/* The decoder.  `layers` is a HOST array of n_layers entries (its device
+ * pointers are read during the call only).  The lm_head is tied: with
+ * lm_head.data == NULL the (bf16) embedding matrix is the lm_head; an INT4
+ * model passes its group-128 copy of the tied matrix in lm_head. */
+typedef struct {
+  int32_t hidden, n_heads, n_kv_heads, head_dim, inter, n_layers, vocab;
+  float rms_eps;
+  float rope_theta;
+  const la_layer* layers;
+  la_weight embed;
+  la_weight lm_head;
+  const uint16_t* final_norm;
+} la_model;
+
+/* Paged bf16 KV cache (the pages' KV graph keeps [1, 2, seq, 128] per layer;
+ * here the sequence axis is paged in blocks of `block_size` = 16 tokens):
+ *   k: bf16 [n_layers][num_blocks][n_kv_heads][block_size][head_dim]
+ *   v: bf16 [n_layers][num_blocks][n_kv_heads][head_dim][block_size]  (dim-major page)
+ *   block_table: int32 [B][max_blocks]; token t of sequence b lives in block
+ *   block_table[b][t / 16] at offset t % 16. */
+typedef struct {
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t n_layers;
+} la_kv_cache;
+
+/* Error bits written (OR-ed) into the optional device word `err`. */
+enum {
+  LA_DERR_TOKEN_ID = 1,   /* a window id outside [0, vocab) */
+  LA_DERR_CAPACITY = 2,   /* P_b + W exceeds max_len or max_blocks * 16 */
+  LA_DERR_BLOCK_ID = 4    /* a block-table entry needed by the step is outside [0, num_blocks) */
+};
+
+/* la_pbd_step epilogue selectors for la_wgemm. */
+enum {
+  LA_EPI_NONE = 0,      /* y[M][n] = x' . W^T (+ bias) (+ residual) */
+  LA_EPI_SILU_GATE = 1  /* y[M][n/2] = SiLU(g) * u, g = columns [0, n/2), u = [n/2, n) */
+};
+
+/* Embedding gather: out[t][:] = E[ids[t]] as fp32, from a bf16 table or an INT4
+ * group-32 table decoded as (q - 8) * scale (WebGPU page, "Embedding gather /
+ * dequant (JS reference)").  ids int32 [T]; out fp32 [T][emb->k].  An id outside
+ * [0, emb->n) yields a zero row and sets LA_DERR_TOKEN_ID in *err (err may be
+ * NULL).  Exact: no rounding happens. */
+la_status la_int4_embed_gather(const int32_t* ids, int32_t T, const la_weight* emb, float* out,
+                               int32_t* err, hipStream_t stream);
+
+/* Weight-streaming GEMM for small M (M = 6 x batch rows):
+ *   x' = RMSNorm(x; norm_gain, rms_eps) if norm_gain != NULL, else x;
+ *   LA_EPI_NONE:      y = x' . W^T + bias + residual  (bias bf16 [n] / residual fp32 [M][n], each nullable)
+ *   LA_EPI_SILU_GATE: y = SiLU(x' . Wg^T) * (x' . Wu^T), Wg / Wu the two halves of W's rows.
+ * x fp32 [M][w->k]; y fp32 [M][n] (or [M][n/2]).  y may alias residual.
+ * Arithmetic: weights exact, activations split into bf16 hi + lo parts, fp32
+ * accumulation on the matrix cores.  1 <= M <= 64. */
+size_t la_wgemm_workspace(int32_t M, const la_weight* w, int32_t epilogue);
+la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t* norm_gain,
+                   float rms_eps, const uint16_t* bias, const float* residual, int32_t epilogue,
+                   float* y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Block-masked GQA attention of the window rows over the paged cache of one
+ * layer.  q fp32 [B][W][n_heads][head_dim] (RoPE already applied); the keys of
+ * sequence b are cache slots 0 .. P_b+W-1 (the window's own K/V must already be
+ * stored at P_b .. P_b+W-1): every window row sees all of them (prefix causal,
+ * window bidirectional).  out fp32 [B][W][n_heads][head_dim] =
+ * softmax(q.K^T / sqrt(D)) . V, query head h reading KV head h / (n_heads /
+ * n_kv_heads).  prefix_len int32 [B] (device); max_len (host) is an upper bound
+ * of every P_b + W and sizes the split-K grid; keys beyond the cache capacity
+ * are ignored. */
+size_t la_pbd_attention_workspace(int32_t B, int32_t W, int32_t n_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t max_len);
+la_status la_pbd_attention(const float* q, const la_kv_cache* kv, int32_t layer, int32_t n_heads,
+                           int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
+                           int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Tied lm_head with per-row argmax (greedy selection; Jetson page, section 1.4).
+ * f = RMSNorm(h; norm_gain, rms_eps) if norm_gain != NULL else h; logits =
+ * f . E^T over the lm->n vocabulary rows (never stored).  ids int32 [M] = argmax
+ * (lowest index on an exact tie); top1 fp32 [M] = max logit; gap fp32 [M] =
+ * top1 - second largest logit (0 on a tie).  top1 / gap nullable. */
+size_t la_lm_head_argmax_workspace(int32_t M, const la_weight* lm);
+la_status la_lm_head_argmax(const float* h, int32_t M, const la_weight* lm,
+                            const uint16_t* norm_gain, float rms_eps, int32_t* ids, float* top1,
+                            float* gap, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* One decoder layer for the window rows (RMSNorm, QKV + bias, RoPE at positions
+ * P_b + j, bf16 K/V written to the cache at slots P_b + j, window attention, O
+ * projection + residual, RMSNorm, SiLU-gated MLP + residual).  x, y fp32
+ * [B*W][hidden] (y may alias x); attn_out (nullable) fp32 [B*W][n_heads*head_dim]
+ * receives the attention output. */
+la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, const float* x,
+                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len, float* y,
+                       float* attn_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* The whole PBD window step: embedding gather of window_ids int32 [B][W]; all
+ * layers (writing each window's K/V into the cache at slots P_b .. P_b+W-1);
+ * final RMSNorm; tied lm_head argmax.  out_ids int32 [B][W]; out_gap (nullable)
+ * fp32 [B][W] top-2 logit gaps; out_hidden (nullable) fp32 [B*W][hidden] final
+ * hidden state before the final norm.  prefix_len is not modified: the caller
+ * commits accepted tokens by advancing it (nothing to roll back otherwise; the
+ * next step overwrites the slots).  Rows of a sequence with a data error get
+ * out_ids = -1 and set bits in *err (nullable; OR-ed, never cleared). */
+size_t la_pbd_step_workspace(const la_model* m, int32_t B, int32_t W, int32_t max_len);
+la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                      const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
+                      int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
+                      size_t workspace_bytes, int32_t* err, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* la_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_PBD_H */

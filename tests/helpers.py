@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU parity tests (inputs come from box_decoding_amd.synth;
+expected values from the oracle only)."""
+import numpy as np
+import torch
+
+from box_decoding_amd import synth
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def np_tree(x):
+    return synth.to_numpy_tree(x)
+
+
+def ids_match(gpu_ids, ref_ids, ref_gap, thr=1e-3):
+    """Argmax ids must match wherever the oracle's top-2 gap is >= thr.
+
+    Returns (n_compared, n_mismatch, n_excluded)."""
+    g = np.asarray(gpu_ids).reshape(-1)
+    r = np.asarray(ref_ids).reshape(-1)
+    gap = np.asarray(ref_gap).reshape(-1)
+    keep = gap >= thr
+    return int(keep.sum()), int((g[keep] != r[keep]).sum()), int((~keep).sum())
+
+
+def bf16_ulp_diff(a_bits, b_bits):
+    """Distance in bf16 units of the last place between two bf16 bit arrays."""
+    def ordered(x):
+        x = np.asarray(x).view(np.uint16).astype(np.int64)
+        return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + x)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def cache_slots(cache_np, layer, b, positions):
+    """bf16 bits of K and V at the given token positions of sequence b: [n, Hkv, D]."""
+    bs = int(cache_np["block"])
+    pos = np.asarray(positions)
+    blk = np.asarray(cache_np["block_table"])[b, pos // bs].astype(np.int64)
+    off = pos % bs
+    k = cache_np["k"][layer][blk, :, off, :]
+    v = cache_np["v"][layer][blk, :, :, off]
+    return k.view(np.uint16), v.view(np.uint16)
+
+
+def poison_unused_slots(cache: dict, prefix_len, window: int):
+    """Fill every cache slot at or beyond P_b + window (and unreferenced blocks) with NaN."""
+    k, v, table = cache["k"], cache["v"], cache["block_table"].cpu().numpy()
+    bs = int(cache["block"])
+    used = np.zeros((k.shape[1], bs), dtype=bool)
+    for b, P in enumerate(torch.as_tensor(prefix_len).cpu().tolist()):
+        for t in range(P + window):
+            used[table[b, t // bs], t % bs] = True
+    mask = torch.from_numpy(~used).to(k.device)  # [NB, bs]
+    nan = torch.tensor(0x7FC0, dtype=torch.int32).to(torch.int16).item()
+    km = mask[None, :, None, :, None].expand_as(k)
+    vm = mask[None, :, None, None, :].expand_as(v)
+    k.masked_fill_(km, nan)
+    v.masked_fill_(vm, nan)

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry
+point, sizes workspaces, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from box_decoding_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_pbd.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:la_status|size_t|const char\*)\s+(la_\w+)\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.library_path()):
+        from box_decoding_amd import build
+        build.build()
+    return b.load()
+
+
+def test_header_declares_the_named_entry_points():
+    names = _declared()
+    for n in ("la_pbd_step", "la_pbd_attention", "la_wgemm", "la_int4_embed_gather",
+              "la_lm_head_argmax"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert sorted(b.EXPORTED) == _declared()
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = lib.la_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.la_status_str(7).decode() == "unknown status"
+
+
+def _w(fmt=0, n=2560, k=2048, group=0, data=256, scales=None):
+    return b.LaWeight(fmt, n, k, group, ctypes.c_void_p(data), ctypes.c_void_p(scales) if scales else None)
+
+
+def test_wgemm_rejects_bad_arguments_before_launch(lib):
+    w = _w()
+    ws = lib.la_wgemm_workspace(6, ctypes.byref(w), 0)
+    assert ws > 0
+    fake = ctypes.c_void_p(4096)
+    # NULL x / y
+    assert lib.la_wgemm(None, 6, ctypes.byref(w), None, 1e-6, None, None, 0, fake, fake, ws, None) == -1
+    # bad epilogue
+    assert lib.la_wgemm(fake, 6, ctypes.byref(w), None, 1e-6, None, None, 9, fake, fake, ws, None) == -1
+    # M out of range
+    assert lib.la_wgemm(fake, 0, ctypes.byref(w), None, 1e-6, None, None, 0, fake, fake, ws, None) == -2
+    # K not a multiple of 256
+    w2 = _w(k=2000)
+    assert lib.la_wgemm(fake, 6, ctypes.byref(w2), None, 1e-6, None, None, 0, fake, fake, ws, None) == -2
+    # INT4 without scales / with a wrong group
+    w3 = _w(fmt=1, group=128)
+    assert lib.la_wgemm(fake, 6, ctypes.byref(w3), None, 1e-6, None, None, 0, fake, fake, ws, None) == -2
+    w4 = _w(fmt=1, group=64, scales=4096)
+    assert lib.la_wgemm(fake, 6, ctypes.byref(w4), None, 1e-6, None, None, 0, fake, fake, ws, None) == -2
+    # misaligned activations
+    assert lib.la_wgemm(ctypes.c_void_p(4100), 6, ctypes.byref(w), None, 1e-6, None, None, 0, fake,
+                        fake, ws, None) == -1
+    # workspace too small / missing
+    assert lib.la_wgemm(fake, 6, ctypes.byref(w), None, 1e-6, None, None, 0, fake, fake, ws - 1,
+                        None) == -3
+    assert lib.la_wgemm(fake, 6, ctypes.byref(w), None, 1e-6, None, None, 0, fake, None, ws, None) == -3
+
+
+def test_attention_rejects_bad_shapes(lib):
+    kv = b.LaKvCache(ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(256), 10, 4, 16, 1)
+    fake = ctypes.c_void_p(4096)
+    ws = lib.la_pbd_attention_workspace(1, 6, 16, 2, 128, 64)
+    assert ws > 0
+    call = lambda **k: lib.la_pbd_attention(
+        fake, ctypes.byref(k.get("kv", kv)), k.get("layer", 0), k.get("hq", 16), k.get("hkv", 2),
+        k.get("d", 128), fake, k.get("B", 1), k.get("W", 6), k.get("max_len", 64), fake, fake,
+        k.get("ws", ws), None)
+    assert call(d=64) == -2
+    assert call(hq=15) == -2
+    assert call(W=9) == -2
+    assert call(B=65) == -2
+    assert call(layer=1) == -1
+    assert call(ws=ws - 1) == -3
+    bad = b.LaKvCache(ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(256), 10, 4, 32, 1)
+    assert call(kv=bad) == -2
+
+
+def test_step_workspace_rejects_bad_model(lib):
+    m = b.LaModel()
+    assert lib.la_pbd_step_workspace(ctypes.byref(m), 1, 6, 64) == 0
+
+
+def test_lm_head_rejects(lib):
+    w = _w(n=152681)
+    ws = lib.la_lm_head_argmax_workspace(6, ctypes.byref(w))
+    assert ws >= 6 * ((152681 + 15) // 16 // 4) * 12  # one top-2 record per workgroup of 4 tiles
+    fake = ctypes.c_void_p(4096)
+    assert lib.la_lm_head_argmax(None, 6, ctypes.byref(w), None, 1e-6, fake, None, None, fake, ws,
+                                 None) == -1
+    assert lib.la_lm_head_argmax(fake, 6, ctypes.byref(w), None, 1e-6, fake, None, None, fake, ws - 1,
+                                 None) == -3
+
+
+def test_gather_rejects(lib):
+    fake = ctypes.c_void_p(4096)
+    e = _w(fmt=1, n=100, k=2048, group=32)  # INT4 without scales
+    assert lib.la_int4_embed_gather(fake, 6, ctypes.byref(e), fake, None, None) == -2
+    e2 = _w(fmt=3, n=100, k=2048)
+    assert lib.la_int4_embed_gather(fake, 6, ctypes.byref(e2), fake, None, None) == -1
+    e3 = _w(n=100, k=2048)
+    assert lib.la_int4_embed_gather(fake, 0, ctypes.byref(e3), fake, None, None) == 0  # empty: no-op

@@ -1,0 +1,339 @@
+"""GPU parity: every entry point of libla_pbd.so against the CPU oracle.
+
+Bars: bit-exact for the gather/dequant and the argmax ids (except where the
+oracle's top-2 logit gap is < 1e-3); rel-L2 <= 2e-3 for attention and layer
+outputs with bf16 weights and <= 5e-3 with INT4 weights; the window K/V written
+to the bf16 cache within 1 bf16 ulp (the rounding decision is taken on values
+computed in a different order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from box_decoding_amd import binding as B
+from box_decoding_amd import synth
+from helpers import bf16_ulp_diff, cache_slots, ids_match, np_tree, poison_unused_slots, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_BF16 = 2e-3
+TOL_INT4 = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+    torch.cuda.set_device(0)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- gather
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+def test_embed_gather_bit_exact(fmt):
+    d = synth.ModelDims(n_layers=1, vocab=3001)
+    m = synth.make_model(d, fmt, seed=31, device=DEV)
+    emb = m["embed"]
+    ids = torch.tensor([0, 3000, 17, 17, 2999, 1234, 5, 600, 2048, 77, 1, 2], dtype=torch.int32,
+                       device=DEV)
+    out = B.embed_gather(ids, emb)
+    torch.cuda.synchronize()
+    ref = O.embed_rows(ids.cpu().numpy(), np_tree(emb))
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+def test_embed_gather_flags_bad_ids():
+    d = synth.ModelDims(n_layers=1, vocab=500)
+    m = synth.make_model(d, "int4", seed=32, device=DEV)
+    ids = torch.tensor([3, -1, 500, 499], dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = B.embed_gather(ids, m["embed"], err=err).cpu().numpy()
+    assert int(err.item()) == B.LA_DERR_TOKEN_ID
+    assert np.all(out[1] == 0) and np.all(out[2] == 0)
+    ref = O.embed_rows(np.array([3, 499]), np_tree(m["embed"]))
+    assert np.array_equal(out[[0, 3]].astype(np.float64), ref)
+
+
+# ---------------------------------------------------------------- GEMM
+
+def _gemm_ref(x, w, gain=None, eps=1e-6, bias=None, residual=None, silu=False):
+    a = np.asarray(x, dtype=np.float64)
+    if gain is not None:
+        a = O.rmsnorm(a, O.bf16_to_float(gain), eps)
+    y = a @ O.decode_weight(w).T
+    if silu:
+        n = y.shape[1] // 2
+        return O.silu(y[:, :n]) * y[:, n:]
+    if bias is not None:
+        y = y + O.bf16_to_float(bias)
+    if residual is not None:
+        y = y + residual
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+@pytest.mark.parametrize("M", [1, 6, 13, 48, 70])
+def test_wgemm_store(fmt, M):
+    g = torch.Generator(device=DEV).manual_seed(100 + M)
+    N, K = 2560, 2048
+    w = synth._weight(fmt, N, K, DEV, 41, M)
+    x = torch.randn((M, K), generator=g, device=DEV)
+    gain = synth.normal_bf16((K,), 0.02, 1.0, DEV, 42, M)
+    bias = synth.normal_bf16((N,), 0.02, 0.0, DEV, 43, M)
+    res = torch.randn((M, N), generator=g, device=DEV)
+    y = B.wgemm(x, w, norm_gain=gain, bias=bias, residual=res)
+    y2 = B.wgemm(x, w)
+    torch.cuda.synchronize()
+    wn = np_tree(w)
+    ref = _gemm_ref(x.cpu().numpy(), wn, gain.cpu().numpy(), 1e-6, bias.cpu().numpy(),
+                    res.cpu().numpy().astype(np.float64))
+    ref2 = _gemm_ref(x.cpu().numpy(), wn)
+    tol = TOL_BF16 if fmt == "bf16" else TOL_INT4
+    e1, e2 = rel_l2(y.cpu().numpy(), ref), rel_l2(y2.cpu().numpy(), ref2)
+    _log(f"wgemm {fmt} M={M}: rel-L2 {e1:.2e} / plain {e2:.2e}")
+    assert e1 <= tol and e2 <= tol
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+@pytest.mark.parametrize("M,K,F", [(6, 2048, 11008), (48, 2048, 1024), (7, 11008, 2048)])
+def test_wgemm_silu_gate(fmt, M, K, F):
+    g = torch.Generator(device=DEV).manual_seed(7 * M + K)
+    w = synth._weight(fmt, 2 * F, K, DEV, 51, M, K)
+    x = torch.randn((M, K), generator=g, device=DEV)
+    y = B.wgemm(x, w, silu_gate=True)
+    torch.cuda.synchronize()
+    ref = _gemm_ref(x.cpu().numpy(), np_tree(w), silu=True)
+    e = rel_l2(y.cpu().numpy(), ref)
+    _log(f"wgemm silu {fmt} M={M} K={K} F={F}: rel-L2 {e:.2e}")
+    assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+
+
+def test_wgemm_is_deterministic():
+    w = synth._weight("bf16", 2048, 11008, DEV, 61)
+    x = torch.randn((6, 11008), generator=torch.Generator(device=DEV).manual_seed(5), device=DEV)
+    a = B.wgemm(x, w)
+    b = B.wgemm(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attention_case(P_list, W, seed, max_len=None, poison=True):
+    d = synth.ModelDims(n_layers=2)
+    P = torch.tensor(P_list, dtype=torch.int32)
+    cache = synth.make_cache(d, P, W, extra_tokens=5, seed=seed, device=DEV)
+    if poison:
+        poison_unused_slots(cache, P, W)
+    Bn = len(P_list)
+    q = torch.randn((Bn * W, d.n_heads * d.head_dim), device=DEV,
+                    generator=torch.Generator(device=DEV).manual_seed(seed))
+    ml = max_len or (max(P_list) + W)
+    dc = B.DeviceCache(cache, d.n_layers)
+    out = B.pbd_attention(q, dc, 1, d.n_heads, d.n_kv_heads, P.to(DEV), Bn, W, ml)
+    torch.cuda.synchronize()
+    cn = np_tree(cache)
+    qn = q.cpu().numpy().astype(np.float64).reshape(Bn, W, d.n_heads, d.head_dim)
+    errs = []
+    for b in range(Bn):
+        k, v = O.cache_read(cn, 1, b, P_list[b] + W)
+        ref = O.window_attention(qn[b], k, v)
+        got = out.cpu().numpy().reshape(Bn, W, d.n_heads, d.head_dim)[b]
+        assert np.all(np.isfinite(got))
+        errs.append(rel_l2(got, ref))
+    return errs
+
+
+@pytest.mark.parametrize("P_list,W", [([0, 37, 300], 6), ([1280], 6), ([5, 16, 17, 4096], 6),
+                                      ([100, 9], 1), ([63, 64], 4), ([200], 8)])
+def test_attention_matches_oracle(P_list, W):
+    errs = _attention_case(P_list, W, seed=sum(P_list) + W)
+    _log(f"attention P={P_list} W={W}: rel-L2 max {max(errs):.2e}")
+    assert max(errs) <= TOL_BF16
+
+
+def test_attention_long_context_probe():
+    errs = _attention_case([32768], 6, seed=9, poison=False)
+    _log(f"attention P=32768: rel-L2 {errs[0]:.2e}")
+    assert errs[0] <= TOL_BF16
+
+
+def test_attention_grid_size_invariance():
+    # a larger max_len only adds empty splits: same result bit for bit
+    a = _attention_case([300, 40], 6, seed=3, max_len=306)
+    b = _attention_case([300, 40], 6, seed=3, max_len=4000)
+    assert a == b
+
+
+# ---------------------------------------------------------------- lm_head
+
+@pytest.mark.parametrize("fmt,V", [("bf16", 152681), ("int4", 152681), ("bf16", 1000)])
+def test_lm_head_argmax(fmt, V):
+    d = synth.ModelDims(n_layers=1, vocab=V)
+    m = synth.make_model(d, fmt, seed=71, device=DEV)
+    lm = m["lm_head"] if m["lm_head"] is not None else m["embed"]
+    M = 13
+    h = torch.randn((M, d.hidden), device=DEV, generator=torch.Generator(device=DEV).manual_seed(V))
+    ids, top1, gap = B.lm_head_argmax(h, lm, norm_gain=m["final_norm"])
+    torch.cuda.synchronize()
+    f = O.rmsnorm(h.cpu().numpy().astype(np.float64), O.bf16_to_float(m["final_norm"].cpu().numpy()),
+                  d.rms_eps)
+    rid, rtop, rgap = O.lm_head_argmax(f, np_tree(lm))
+    n, bad, excl = ids_match(ids.cpu().numpy(), rid, rgap)
+    _log(f"lm_head {fmt} V={V}: {n} compared, {bad} mismatches, {excl} near-ties excluded")
+    assert bad == 0
+    assert np.max(np.abs(top1.cpu().numpy() - rtop)) < 1e-3
+    assert np.max(np.abs(gap.cpu().numpy() - rgap)) < 1e-3
+
+
+# ---------------------------------------------------------------- one layer
+
+def _layer_case(wname, P_override=None, fmt=None):
+    w = synth.WORKLOADS[wname]
+    d = w.dims
+    fmt = fmt or w.wfmt
+    P = torch.tensor(P_override, dtype=torch.int32) if P_override else synth.draw_prefix_lens(w)
+    Bn, W = len(P), w.window
+    model = synth.make_model(d, fmt, w.model_seed, DEV)
+    cache = synth.make_cache(d, P, W, seed=w.input_seed, device=DEV)
+    x = synth.make_hidden(Bn * W, d.hidden, w.input_seed, DEV)
+    mn, cn = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    y, attn = B.pbd_layer(dm, 0, dc, x, P.to(DEV), Bn, W, int(P.max()) + W, want_attn=True)
+    torch.cuda.synchronize()
+    parts = {}
+    ref, kb, vb = O.decoder_layer(x.cpu().numpy().astype(np.float64), mn["layers"][0], d, cn, 0,
+                                  P.numpy(), W, parts=parts)
+    cg = np_tree(cache)
+    kd, vd = [], []
+    for b in range(Bn):
+        pos = np.arange(int(P[b]), int(P[b]) + W)
+        kg, vg = cache_slots(cg, 0, b, pos)
+        kd.append(bf16_ulp_diff(kg, kb[b * W:(b + 1) * W]).max())
+        vd.append(bf16_ulp_diff(vg, vb[b * W:(b + 1) * W]).max())
+    return rel_l2(y.cpu().numpy(), ref), rel_l2(attn.cpu().numpy(), parts["attn"]), max(kd), max(vd)
+
+
+def test_layer_b1_p512():
+    e_out, e_attn, kd, vd = _layer_case("layer_b1_p512")
+    _log(f"layer b1 p512: out rel-L2 {e_out:.2e}, attn rel-L2 {e_attn:.2e}, K/V ulp {kd}/{vd}")
+    assert e_out <= TOL_BF16 and e_attn <= TOL_BF16
+    assert kd <= 1 and vd <= 1
+
+
+def test_layer_ragged_batch_int4():
+    e_out, e_attn, kd, vd = _layer_case("layer_b1_p512", P_override=[0, 33, 511, 700], fmt="int4")
+    _log(f"layer int4 ragged: out rel-L2 {e_out:.2e}, attn rel-L2 {e_attn:.2e}, K/V ulp {kd}/{vd}")
+    assert e_out <= TOL_INT4 and e_attn <= TOL_INT4
+    assert kd <= 1 and vd <= 1
+
+
+# ---------------------------------------------------------------- whole step
+
+def _step_case(d, fmt, P_list, W, seed, mask_id=None):
+    model = synth.make_model(d, fmt, seed, DEV)
+    P = torch.tensor(P_list, dtype=torch.int32)
+    cache = synth.make_cache(d, P, W, seed=seed + 1, device=DEV)
+    poison_unused_slots(cache, P, W)
+    ids = synth.draw_window_ids(len(P_list), W, d.vocab, seed + 2, mask_id=mask_id, device=DEV)
+    mn, cn = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out_ids, gap, hid = B.pbd_step(dm, dc, ids, P.to(DEV), int(P.max()) + W, want_hidden=True,
+                                   err=err)
+    torch.cuda.synchronize()
+    ref = O.pbd_step(mn, cn, ids.cpu().numpy(), P.numpy(), return_hidden=True)
+    return out_ids.cpu().numpy(), gap.cpu().numpy(), hid.cpu().numpy(), ref, int(err.item())
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+def test_step_small_ragged(fmt):
+    d = synth.ModelDims(n_layers=2, vocab=5003)
+    got_ids, got_gap, hid, ref, err = _step_case(d, fmt, [0, 17, 100, 1000], 6, seed=81)
+    n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
+    e = rel_l2(hid, ref["hidden"])
+    _log(f"step {fmt} 2 layers: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
+    assert err == 0
+    assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+    assert bad == 0
+
+
+def test_step_error_rows_get_minus_one():
+    d = synth.ModelDims(n_layers=1, vocab=1000)
+    model = synth.make_model(d, "bf16", 91, DEV)
+    P = torch.tensor([10, 20], dtype=torch.int32)
+    cache = synth.make_cache(d, P, 6, seed=92, device=DEV)
+    ids = torch.tensor([[1, 2, 3, 4, 5, 6], [7, 8, 1000, 9, 9, 9]], dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    out, _, _ = B.pbd_step(dm, dc, ids, P.to(DEV), 26, err=err)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(out[1] == -1) and np.all(out[0] >= 0)
+    assert int(err.item()) & B.LA_DERR_TOKEN_ID
+    # a prefix that overflows the cache capacity
+    P2 = torch.tensor([10, 10_000], dtype=torch.int32, device=DEV)
+    err.zero_()
+    out, _, _ = B.pbd_step(dm, dc, ids.clamp(max=999), P2, 10_006, err=err)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(out[1] == -1) and np.all(out[0] >= 0)
+    assert int(err.item()) & B.LA_DERR_CAPACITY
+
+
+@pytest.mark.timeout(900)
+def test_step_full_b1_p1280():
+    """The full 36-layer step with the 152681-token tied lm_head, batch 1, prefix 1280."""
+    w = synth.WORKLOADS["step_b1_p1280"]
+    d = w.dims
+    model = synth.make_model(d, "bf16", w.model_seed, DEV)
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=DEV)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=DEV)
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    mn, cn = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    out_ids, gap, hid = B.pbd_step(dm, dc, ids, P.to(DEV), int(P.max()) + w.window, want_hidden=True)
+    torch.cuda.synchronize()
+    ref = O.pbd_step(mn, cn, ids.cpu().numpy(), P.numpy(), return_hidden=True)
+    n, bad, excl = ids_match(out_ids.cpu().numpy(), ref["ids"], ref["gap"])
+    e = rel_l2(hid.cpu().numpy(), ref["hidden"])
+    _log(f"full step b1 p1280: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded;"
+         f" ids {out_ids.cpu().numpy().tolist()} gaps {np.round(ref['gap'], 4).tolist()}")
+    assert bad == 0
+    assert e <= TOL_BF16
+
+
+def test_step_graph_replay_matches_eager():
+    """The captured step replays to the eager result every time, with eager work
+    and synchronisations in between."""
+    d = synth.ModelDims(n_layers=2, vocab=2003)
+    model = synth.make_model(d, "bf16", 95, DEV)
+    P = torch.tensor([300, 7], dtype=torch.int32)
+    cache = synth.make_cache(d, P, 6, seed=96, device=DEV)
+    ids = synth.draw_window_ids(2, 6, d.vocab, 97, mask_id=-1, device=DEV)
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(DEV)
+    ref_ids, ref_gap, _ = B.pbd_step(dm, dc, ids, Pd, 306)
+    torch.cuda.synchronize()
+    out_ids = torch.full((2, 6), -7, dtype=torch.int32, device=DEV)
+    out_gap = torch.zeros((2, 6), dtype=torch.float32, device=DEV)
+    g = B.StepGraph(dm, dc, ids, Pd, 306, out_ids, out_gap)
+    for r in range(3):
+        out_ids.fill_(-7)
+        out_gap.zero_()
+        B.pbd_step(dm, dc, ids, Pd, 306)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_ids, ref_ids), r
+        assert torch.equal(out_gap, ref_gap), r
