@@ -27,10 +27,11 @@ def log(msg):
 
 
 def weight_bytes(w):
-    n = w["data"].numel() * w["data"].element_size()
-    if w.get("scales") is not None:
-        n += w["scales"].numel() * w["scales"].element_size()
-    return n
+    """Bytes of the matrix itself (tile padding rows excluded)."""
+    n, k = int(w["n"]), int(w["k"])
+    if w["fmt"] == "bf16":
+        return n * k * 2
+    return n * k // 2 + n * (k // int(w["group"])) * 2
 
 
 def step_bytes(model, dims, prefix_len, W):
@@ -99,6 +100,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=72)
+    ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the PBD step here is a single-GPU path "
@@ -120,6 +122,10 @@ def main():
     d = w.dims
     log(f"bench: building {args.workload} on the GPU")
     model = synth.make_model(d, w.wfmt, w.model_seed, dev)
+    if not args.row_major:
+        # the serving layout: weights regrouped once into 16-row tiles
+        model = B.pack_model(model)
+        torch.cuda.synchronize()
     P = synth.draw_prefix_lens(w)
     cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
     ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
@@ -202,7 +208,7 @@ def main():
         "data": "synthetic (seeded random-init weights and KV cache, uniform token ids)",
         "config": {"workload": args.workload, "batch": w.batch, "window": w.window,
                    "prefix": int(P.max()), "layers": d.n_layers, "vocab": d.vocab,
-                   "weights": w.wfmt},
+                   "weights": w.wfmt, "layout": "row-major" if args.row_major else "tiled16"},
         "tokens_per_s": round(steps_per_s * T, 2),
         "windows_per_s": round(steps_per_s * w.batch, 3),
         "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),

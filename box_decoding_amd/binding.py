@@ -20,17 +20,19 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_pbd.
 LA_W_BF16, LA_W_INT4 = 0, 1
 LA_EPI_NONE, LA_EPI_SILU_GATE = 0, 1
 LA_DERR_TOKEN_ID, LA_DERR_CAPACITY, LA_DERR_BLOCK_ID = 1, 2, 4
+LA_LAYOUT_ROWS, LA_LAYOUT_TILED, LA_LAYOUT_TILED_GU, LA_LAYOUT_TILED_QKV = 0, 1, 2, 3
 
 EXPORTED = [
     "la_int4_embed_gather", "la_wgemm_workspace", "la_wgemm", "la_pbd_attention_workspace",
     "la_pbd_attention", "la_lm_head_argmax_workspace", "la_lm_head_argmax", "la_pbd_layer",
-    "la_pbd_step_workspace", "la_pbd_step", "la_status_str",
+    "la_pbd_step_workspace", "la_pbd_step", "la_status_str", "la_pack_weight_bytes",
+    "la_pack_weight",
 ]
 
 
 class LaWeight(ctypes.Structure):
     _fields_ = [("fmt", c_int32), ("n", c_int32), ("k", c_int32), ("group", c_int32),
-                ("data", c_void_p), ("scales", c_void_p)]
+                ("layout", c_int32), ("reserved", c_int32), ("data", c_void_p), ("scales", c_void_p)]
 
 
 class LaLayer(ctypes.Structure):
@@ -93,6 +95,8 @@ def load() -> ctypes.CDLL:
                                   c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_size_t, c_void_p, c_void_p]),
         "la_status_str": (ctypes.c_char_p, [c_int32]),
+        "la_pack_weight_bytes": (c_size_t, [W, c_int32, c_int32]),
+        "la_pack_weight": (c_int32, [W, c_int32, c_void_p, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -124,11 +128,49 @@ def _require_cuda(*ts):
 
 def weight_desc(w: dict) -> LaWeight:
     if w is None:
-        return LaWeight(LA_W_BF16, 0, 0, 0, None, None)
+        return LaWeight(LA_W_BF16, 0, 0, 0, 0, 0, None, None)
     fmt = LA_W_BF16 if w["fmt"] == "bf16" else LA_W_INT4
     _require_cuda(w["data"], w.get("scales"))
-    return LaWeight(fmt, int(w["n"]), int(w["k"]), int(w.get("group") or 0), _ptr(w["data"]),
-                    _ptr(w.get("scales")))
+    return LaWeight(fmt, int(w["n"]), int(w["k"]), int(w.get("group") or 0),
+                    int(w.get("layout", LA_LAYOUT_ROWS)), 0, _ptr(w["data"]), _ptr(w.get("scales")))
+
+
+def pack_weight(w: dict, layout: int) -> dict:
+    """Tiled copy of a row-major weight (device memory from torch)."""
+    lib = load()
+    src = weight_desc(w)
+    nd = lib.la_pack_weight_bytes(ctypes.byref(src), layout, 0)
+    ns = lib.la_pack_weight_bytes(ctypes.byref(src), layout, 1)
+    if nd == 0:
+        raise LaError("la_pack_weight_bytes rejected the weight")
+    dev = w["data"].device
+    data = torch.empty(nd, dtype=torch.uint8, device=dev)
+    scales = torch.empty(ns, dtype=torch.uint8, device=dev) if ns else None
+    _check(lib.la_pack_weight(ctypes.byref(src), layout, _ptr(data), _ptr(scales), _stream()),
+           "la_pack_weight")
+    out = dict(w)
+    out.update(data=data, scales=scales, layout=layout)
+    return out
+
+
+def pack_model(model: dict) -> dict:
+    """Model dict whose linears and lm_head use the tiled layouts (the INT4
+    group-32 embedding stays row-major: it is only gathered)."""
+    out = dict(model)
+    layers = []
+    for lay in model["layers"]:
+        nl = dict(lay)
+        nl["qkv"] = pack_weight(lay["qkv"], LA_LAYOUT_TILED_QKV)
+        nl["o"] = pack_weight(lay["o"], LA_LAYOUT_TILED)
+        nl["gate_up"] = pack_weight(lay["gate_up"], LA_LAYOUT_TILED_GU)
+        nl["down"] = pack_weight(lay["down"], LA_LAYOUT_TILED)
+        layers.append(nl)
+    out["layers"] = layers
+    if model["wfmt"] == "bf16":
+        out["embed"] = pack_weight(model["embed"], LA_LAYOUT_TILED)  # tied lm_head
+    else:
+        out["lm_head"] = pack_weight(model["lm_head"], LA_LAYOUT_TILED)
+    return out
 
 
 class Workspace:

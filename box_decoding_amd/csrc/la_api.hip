@@ -28,10 +28,14 @@ struct Carver {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int int4_group) {
+// `tiled`: the tiled layout this use accepts besides row-major (-1: none).
+la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int int4_group,
+                       int tiled) {
   if (!w || !w->data) return LA_ERR_ARG;
   if (w->n != n || w->k != k) return LA_ERR_SHAPE;
   if (!aligned16(w->data)) return LA_ERR_ARG;
+  if (w->layout != LA_LAYOUT_ROWS && w->layout != tiled) return LA_ERR_UNSUPPORTED;
+  if (w->layout != LA_LAYOUT_ROWS && k % 128) return LA_ERR_SHAPE;
   if (w->fmt == LA_W_BF16) return LA_OK;
   if (w->fmt != LA_W_INT4) return LA_ERR_ARG;
   if (!allow_int4) return LA_ERR_UNSUPPORTED;
@@ -39,16 +43,20 @@ la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int in
   return LA_OK;
 }
 
-la_status check_gemm_weight(const la_weight* w) {
+la_status check_gemm_weight(const la_weight* w, int tiled) {
   if (!w || !w->data) return LA_ERR_ARG;
   if (w->n < 1 || w->k < 256 || w->k % 256) return LA_ERR_SHAPE;
-  return check_weight(w, w->n, w->k, true, 128);
+  return check_weight(w, w->n, w->k, true, 128, tiled);
 }
 
 // ---------------------------------------------------------------- workspace plans
 
 int gemm_parts(int M, const la_weight* w, int epi) {
-  return plan_gemm(M, w->n, w->k, w->fmt == LA_W_INT4, epi, true).grid;
+  return plan_gemm(M, w->n, w->k, w->fmt == LA_W_INT4, epi, false).grid;
+}
+
+int gemm_ksplit(int M, const la_weight* w) {
+  return plan_gemm(M, w->n, w->k, w->fmt == LA_W_INT4, EPI_STORE, true).ksplit;
 }
 
 struct StepWs {
@@ -65,6 +73,7 @@ struct StepWs {
   float* part_o;
   float* part_ml;
   float* amax;
+  float* parts;       // K-slice partial sums of the O and down projections
   int pps, max_splits, nqp, vocab_parts;
   size_t bytes;
 };
@@ -93,6 +102,8 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
   const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
   s.vocab_parts = gemm_parts(T, lm, EPI_ARGMAX);
   s.amax = lm_head ? c.take<float>((size_t)T * s.vocab_parts * 3) : nullptr;
+  const int ksp = std::max(gemm_ksplit(T, &m->layers[0].o), gemm_ksplit(T, &m->layers[0].down));
+  s.parts = c.take<float>((size_t)ksp * T * H);
   s.bytes = c.off;
   return s;
 }
@@ -113,25 +124,26 @@ la_status check_model(const la_model* m) {
     if (!L.in_norm || !L.post_norm) return LA_ERR_ARG;
     if (!aligned16(L.in_norm) || !aligned16(L.post_norm)) return LA_ERR_ARG;
     la_status st;
-    if ((st = check_weight(&L.qkv, NQKV, H, true, 128)) != LA_OK) return st;
-    if ((st = check_weight(&L.o, H, HQ, true, 128)) != LA_OK) return st;
-    if ((st = check_weight(&L.gate_up, 2 * m->inter, H, true, 128)) != LA_OK) return st;
-    if ((st = check_weight(&L.down, H, m->inter, true, 128)) != LA_OK) return st;
+    if ((st = check_weight(&L.qkv, NQKV, H, true, 128, LA_LAYOUT_TILED_QKV)) != LA_OK) return st;
+    if ((st = check_weight(&L.o, H, HQ, true, 128, LA_LAYOUT_TILED)) != LA_OK) return st;
+    if ((st = check_weight(&L.gate_up, 2 * m->inter, H, true, 128, LA_LAYOUT_TILED_GU)) != LA_OK)
+      return st;
+    if ((st = check_weight(&L.down, H, m->inter, true, 128, LA_LAYOUT_TILED)) != LA_OK) return st;
     if (L.qkv.fmt != fmt || L.o.fmt != fmt || L.gate_up.fmt != fmt || L.down.fmt != fmt)
       return LA_ERR_UNSUPPORTED;
   }
   if (!m->final_norm || !aligned16(m->final_norm)) return LA_ERR_ARG;
   if (fmt == LA_W_BF16) {
-    la_status st = check_weight(&m->embed, m->vocab, H, false, 0);
+    la_status st = check_weight(&m->embed, m->vocab, H, false, 0, LA_LAYOUT_TILED);
     if (st != LA_OK) return st;
     if (m->lm_head.data) {
-      if ((st = check_weight(&m->lm_head, m->vocab, H, false, 0)) != LA_OK) return st;
+      if ((st = check_weight(&m->lm_head, m->vocab, H, false, 0, LA_LAYOUT_TILED)) != LA_OK) return st;
     }
   } else {
-    la_status st = check_weight(&m->embed, m->vocab, H, true, 32);
+    la_status st = check_weight(&m->embed, m->vocab, H, true, 32, -1);
     if (st != LA_OK) return st;
     if (!m->lm_head.data) return LA_ERR_ARG;
-    if ((st = check_weight(&m->lm_head, m->vocab, H, true, 128)) != LA_OK) return st;
+    if ((st = check_weight(&m->lm_head, m->vocab, H, true, 128, LA_LAYOUT_TILED)) != LA_OK) return st;
   }
   return LA_OK;
 }
@@ -168,44 +180,68 @@ GemmArgs base_gemm(const la_weight* w, int M) {
   memset(&g, 0, sizeof(g));
   g.w = w->data;
   g.wscale = (const uint16_t*)w->scales;
+  g.layout = w->layout;
   g.M = M;
   g.N = w->n;
   g.K = w->k;
   return g;
 }
 
-// GEMM whose activations are fp32 rows x (RMSNorm'd when gain != NULL): packed
-// by the GEMM's own workgroups when M is small, else by one packing launch.
+// Pack fp32 rows (h plus pending partial sums, RMSNorm'd when gain != NULL)
+// into the matrix-core operand; the summed rows are written back to h_out.
+la_status pack_rows(const float* x, int ldx, int M, int K, const uint16_t* gain, float eps,
+                    uint16_t* apack, float* asum, bool int4, const float* parts, int n_parts,
+                    float* h_out, hipStream_t st) {
+  PackArgs p;
+  memset(&p, 0, sizeof(p));
+  p.x = x;
+  p.ldx = ldx;
+  p.M = M;
+  p.K = K;
+  p.gain = gain;
+  p.eps = eps;
+  p.apack = apack;
+  p.asum = asum;
+  p.int4 = int4;
+  p.parts = parts;
+  p.n_parts = parts ? n_parts : 0;
+  p.h_out = h_out;
+  LA_TRY(launch_pack(p, st));
+  return LA_OK;
+}
+
 la_status gemm_from_rows(GemmArgs g, const float* x, int ldx, const uint16_t* gain, float eps,
                          uint16_t* apack, float* asum, int epi, bool int4, hipStream_t st) {
-  const GemmPlan p = plan_gemm(g.M, g.N, g.K, int4, epi, true);
-  if (p.lds) {
-    g.x = x;
-    g.ldx = ldx;
-    g.gain = gain;
-    g.eps = eps;
-  } else {
-    LA_TRY(launch_pack({x, ldx, g.M, g.K, gain, eps, apack, asum, int4}, st));
-    g.apack = apack;
-    g.asum = asum;
-  }
+  la_status rs = pack_rows(x, ldx, g.M, g.K, gain, eps, apack, asum, int4, nullptr, 0, nullptr, st);
+  if (rs != LA_OK) return rs;
+  g.apack = apack;
+  g.asum = asum;
   LA_TRY(launch_gemm(g, epi, int4, st));
   return LA_OK;
 }
 
-// One decoder layer on the rows in s.h (in place).
+// One decoder layer on the rows in s.h.  `pending` partial sums of the previous
+// projection (in s.parts) are added to h by the first packing; on return
+// *pending holds the number of partial sums the down projection left.
 la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
-                    int B, int W, int max_len, const StepWs& s, float* attn_out,
+                    int B, int W, int max_len, const StepWs& s, float* attn_out, int* pending,
                     hipStream_t st) {
   const la_layer& L = m->layers[l];
   const int T = B * W;
-  const int H = m->hidden, HQ = m->n_heads * m->head_dim, F = m->inter;
+  const int H = m->hidden, HQ = m->n_heads * m->head_dim;
   const bool int4 = L.qkv.fmt == LA_W_INT4;
   const size_t le = kv_layer_elems(kv, m);
   la_status rs;
 
-  // RMSNorm + QKV + bias + RoPE + K/V write
+  // h += pending partial sums; RMSNorm; pack
+  if ((rs = pack_rows(s.h, H, T, H, L.in_norm, m->rms_eps, s.apack, s.asum, int4, s.parts, *pending,
+                      *pending ? s.h : nullptr, st)) != LA_OK)
+    return rs;
+
+  // QKV + bias + RoPE + K/V write
   GemmArgs g = base_gemm(&L.qkv, T);
+  g.apack = s.apack;
+  g.asum = s.asum;
   g.bias = L.qkv_bias;
   g.y = s.q;
   g.ldy = HQ;
@@ -220,8 +256,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   g.num_blocks = kv->num_blocks;
   g.kc = (uint16_t*)kv->k + (size_t)l * le;
   g.vc = (uint16_t*)kv->v + (size_t)l * le;
-  if ((rs = gemm_from_rows(g, s.h, H, L.in_norm, m->rms_eps, s.apack, s.asum, EPI_QKV, int4, st)) != LA_OK)
-    return rs;
+  LA_TRY(launch_gemm(g, EPI_QKV, int4, st));
 
   // window attention -> packed O-projection operand
   AttnArgs at;
@@ -247,37 +282,60 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   at.out_apack = int4 ? nullptr : s.apack;
   at.out_int4 = false;
   LA_TRY(launch_attention(at, st));
-  if (int4) LA_TRY(launch_pack({at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true}, st));
+  if (int4)
+    if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true, nullptr, 0, nullptr,
+                        st)) != LA_OK)
+      return rs;
 
-  // O projection + residual
+  // O projection: K-slice partial sums (or h += directly)
+  const int ks_o = gemm_ksplit(T, &L.o);
   g = base_gemm(&L.o, T);
   g.apack = s.apack;
   g.asum = s.asum;
-  g.residual = s.h;
-  g.y = s.h;
-  g.ldy = H;
+  if (ks_o > 1) {
+    g.partial = s.parts;
+  } else {
+    g.residual = s.h;
+    g.y = s.h;
+    g.ldy = H;
+  }
   LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
 
-  // RMSNorm + gate/up + SiLU (bf16: packed straight into the down operand)
+  // h += O partial sums; RMSNorm; gate/up + SiLU (bf16: packed straight into
+  // the down operand)
+  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+                      ks_o > 1 ? ks_o : 0, ks_o > 1 ? s.h : nullptr, st)) != LA_OK)
+    return rs;
+  const int F = m->inter;
   g = base_gemm(&L.gate_up, T);
+  g.apack = s.apack;
+  g.asum = s.asum;
   if (int4) {
     g.y = s.mlp;
     g.ldy = F;
   } else {
     g.y_apack = s.apack_m;
   }
-  if ((rs = gemm_from_rows(g, s.h, H, L.post_norm, m->rms_eps, s.apack, s.asum, EPI_SILU, int4, st)) != LA_OK)
-    return rs;
-  if (int4) LA_TRY(launch_pack({s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true}, st));
+  LA_TRY(launch_gemm(g, EPI_SILU, int4, st));
+  if (int4)
+    if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true, nullptr, 0, nullptr,
+                        st)) != LA_OK)
+      return rs;
 
-  // down + residual
+  // down projection: K-slice partial sums left for the next packing
+  const int ks_d = gemm_ksplit(T, &L.down);
   g = base_gemm(&L.down, T);
   g.apack = s.apack_m;
   g.asum = s.asum_m;
-  g.residual = s.h;
-  g.y = s.h;
-  g.ldy = H;
+  if (ks_d > 1) {
+    g.partial = s.parts;
+  } else {
+    g.residual = s.h;
+    g.y = s.h;
+    g.ldy = H;
+  }
   LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
+  *pending = ks_d > 1 ? ks_d : 0;
   return LA_OK;
 }
 
@@ -320,8 +378,11 @@ la_status la_int4_embed_gather(const int32_t* ids, int32_t T, const la_weight* e
   if (emb->k < 8 || emb->k % 8 || emb->n < 1) return LA_ERR_SHAPE;
   if (emb->fmt == LA_W_INT4) {
     if (!emb->scales || emb->group < 8 || emb->group % 8 || emb->k % emb->group) return LA_ERR_SHAPE;
+    if (emb->layout != LA_LAYOUT_ROWS) return LA_ERR_UNSUPPORTED;
   } else if (emb->fmt != LA_W_BF16) {
     return LA_ERR_ARG;
+  } else if (emb->layout != LA_LAYOUT_ROWS && (emb->layout != LA_LAYOUT_TILED || emb->k % 32)) {
+    return LA_ERR_UNSUPPORTED;
   }
   if (!aligned16(out) || !aligned16(emb->data)) return LA_ERR_ARG;
   if (T == 0) return LA_OK;
@@ -350,9 +411,9 @@ la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t
   if (!x || !y || !w) return LA_ERR_ARG;
   if (epilogue != LA_EPI_NONE && epilogue != LA_EPI_SILU_GATE) return LA_ERR_ARG;
   if (M < 1 || M > 512) return LA_ERR_SHAPE;
-  la_status st = check_gemm_weight(w);
-  if (st != LA_OK) return st;
   const int epi = epilogue == LA_EPI_SILU_GATE ? EPI_SILU : EPI_STORE;
+  la_status st = check_gemm_weight(w, epi == EPI_SILU ? LA_LAYOUT_TILED_GU : LA_LAYOUT_TILED);
+  if (st != LA_OK) return st;
   if (epi == EPI_SILU && (w->n % 16 || bias || residual)) return LA_ERR_SHAPE;
   if (!aligned16(x) || (norm_gain && !aligned16(norm_gain))) return LA_ERR_ARG;
   if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
@@ -439,7 +500,7 @@ la_status la_lm_head_argmax(const float* h, int32_t M, const la_weight* lm,
                             hipStream_t stream) {
   if (!h || !ids || !lm) return LA_ERR_ARG;
   if (M < 1 || M > 512) return LA_ERR_SHAPE;
-  la_status st = check_gemm_weight(lm);
+  la_status st = check_gemm_weight(lm, LA_LAYOUT_TILED);
   if (st != LA_OK) return st;
   if (!aligned16(h) || (norm_gain && !aligned16(norm_gain))) return LA_ERR_ARG;
   if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
@@ -478,7 +539,12 @@ la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, 
   if (y != x) LA_TRY(hipMemcpyAsync(y, x, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice, stream));
   PrologueArgs p = base_prologue(m, kv, prefix_len, B, W, max_len, s);
   LA_TRY(launch_prologue(p, stream));
-  return run_layer(m, layer, kv, prefix_len, B, W, max_len, s, attn_out, stream);
+  int pending = 0;
+  if ((st = run_layer(m, layer, kv, prefix_len, B, W, max_len, s, attn_out, &pending, stream)) != LA_OK)
+    return st;
+  if (pending)
+    return pack_rows(y, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, pending, y, stream);
+  return LA_OK;
 }
 
 size_t la_pbd_step_workspace(const la_model* m, int32_t B, int32_t W, int32_t max_len) {
@@ -508,22 +574,47 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
   p.out = s.h;
   p.err = err;
   LA_TRY(launch_prologue(p, stream));
+  int pending = 0;
   for (int l = 0; l < m->n_layers; ++l) {
-    st = run_layer(m, l, kv, prefix_len, B, W, max_len, s, nullptr, stream);
+    st = run_layer(m, l, kv, prefix_len, B, W, max_len, s, nullptr, &pending, stream);
     if (st != LA_OK) return st;
   }
+  const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
+  const bool int4 = lm->fmt == LA_W_INT4;
+  // h += last partial sums (written back for out_hidden); final RMSNorm; pack
+  if ((st = pack_rows(s.h, H, T, H, m->final_norm, m->rms_eps, s.apack, s.asum, int4, s.parts, pending,
+                      pending ? s.h : nullptr, stream)) != LA_OK)
+    return st;
   if (out_hidden)
     LA_TRY(hipMemcpyAsync(out_hidden, s.h, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice,
                           stream));
-  const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
-  const bool int4 = lm->fmt == LA_W_INT4;
   GemmArgs g = base_gemm(lm, T);
   g.amax = s.amax;
-  if ((st = gemm_from_rows(g, s.h, H, m->final_norm, m->rms_eps, s.apack, s.asum, EPI_ARGMAX, int4,
-                           stream)) != LA_OK)
-    return st;
+  g.apack = s.apack;
+  g.asum = s.asum;
+  LA_TRY(launch_gemm(g, EPI_ARGMAX, int4, stream));
   return hip_status(launch_argmax_reduce(s.amax, T, s.vocab_parts, s.flags, out_ids, nullptr, out_gap,
                                          nullptr, stream));
+}
+
+size_t la_pack_weight_bytes(const la_weight* src, int32_t layout, int32_t scales) {
+  if (!src || src->layout != LA_LAYOUT_ROWS || src->n < 1 || src->k < 128 || src->k % 128) return 0;
+  if (layout != LA_LAYOUT_TILED && layout != LA_LAYOUT_TILED_GU && layout != LA_LAYOUT_TILED_QKV) return 0;
+  if (src->fmt != LA_W_BF16 && !(src->fmt == LA_W_INT4 && src->group == 128)) return 0;
+  if (layout == LA_LAYOUT_TILED_GU && src->n % 16) return 0;
+  if (layout == LA_LAYOUT_TILED_QKV && src->n % kHeadDim) return 0;
+  const size_t n_tiles = layout == LA_LAYOUT_TILED_GU ? (size_t)(src->n / 2 + 7) / 8 : (size_t)(src->n + 15) / 16;
+  if (scales) return src->fmt == LA_W_INT4 ? n_tiles * (src->k / 128) * 16 * 2 : 0;
+  return src->fmt == LA_W_INT4 ? n_tiles * 16 * (size_t)(src->k / 2) : n_tiles * 16 * (size_t)src->k * 2;
+}
+
+la_status la_pack_weight(const la_weight* src, int32_t layout, void* dst, void* dst_scales,
+                         hipStream_t stream) {
+  if (!src || !src->data || !dst) return LA_ERR_ARG;
+  if (la_pack_weight_bytes(src, layout, 0) == 0) return LA_ERR_SHAPE;
+  if (src->fmt == LA_W_INT4 && (!src->scales || !dst_scales)) return LA_ERR_ARG;
+  if (!aligned16(src->data) || !aligned16(dst)) return LA_ERR_ARG;
+  return hip_status(launch_pack_weight(*src, layout, dst, dst_scales, stream));
 }
 
 }  // extern "C"

@@ -19,13 +19,15 @@ struct GemmArgs {
   const uint16_t* apack;     // packed activations of all M rows (global mode)
   const float* asum;         // INT4 only: [MT][K/128][16] per-group sums of the packed rows
   const void* w;             // weight data
-  const uint16_t* wscale;    // INT4 scales [N][K/128]
+  const uint16_t* wscale;    // INT4 scales
+  int layout;                // LA_LAYOUT_* of w
   int M;                     // total rows of the problem
   int m_base;                // first row handled by this launch (multiple of 32)
   int N, K;                  // weight rows / reduction length
-  int n_tiles;               // column tiles (16 columns each)
-  int nt;                    // column tiles per workgroup
-  int nw;                    // waves per workgroup (nw / nt waves share a tile along K)
+  int n_tiles;               // column tiles (16 operand columns each)
+  int ksplit;                // K slices per tile (> 1: partial sums go to `partial`)
+  int nw;                    // waves per workgroup (they split a work item's K range)
+  float* partial;            // [ksplit][M][N] partial sums when ksplit > 1
   // epilogue
   const uint16_t* bias;      // bf16, indexed by weight row (nullable)
   const float* residual;     // fp32 [M][ldy] (nullable)
@@ -46,15 +48,20 @@ struct GemmArgs {
   int n_parts;
 };
 
+// Row packing: v = x[m] + sum_s parts[s][m] (fixed order), optionally stored to
+// h_out, then RMSNorm'd (when gain != NULL) and packed into the operand layout.
 struct PackArgs {
   const float* x;
   int ldx;
   int M, K;
   const uint16_t* gain;  // nullable: no RMSNorm
   float eps;
-  uint16_t* apack;
+  uint16_t* apack;       // nullable: no packing
   float* asum;           // INT4 only (nullable otherwise)
   bool int4;
+  const float* parts;    // nullable: [n_parts][M][K] partial sums to add
+  int n_parts;
+  float* h_out;          // nullable: receives v (may alias x)
 };
 
 struct AttnArgs {
@@ -94,15 +101,18 @@ struct PrologueArgs {
 
 struct GemmPlan {
   int n_tiles;
-  int nt, nw;
+  int ksplit;
+  int nw;
   int mt;        // row tiles per launch (1, 2 or 4)
   int launches;  // ceil(M / 32)
-  bool lds;      // activations packed in LDS by each workgroup
   int grid;      // workgroups per launch
   size_t smem;   // dynamic LDS bytes
 };
 
-GemmPlan plan_gemm(int M, int N, int K, bool int4, int epi, bool x_available);
+// allow_split: the caller takes K-slice partial sums (EPI_STORE only)
+GemmPlan plan_gemm(int M, int N, int K, bool int4, int epi, bool allow_split);
+hipError_t launch_pack_weight(const la_weight& src, int layout, void* dst, void* dst_scales,
+                              hipStream_t s);
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);

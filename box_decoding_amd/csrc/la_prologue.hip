@@ -17,9 +17,14 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
     if (id_bad) {
       for (int k = tid * 4; k < K; k += 1024) *(float4*)(out + k) = make_float4(0.f, 0.f, 0.f, 0.f);
     } else if (a.emb.fmt == LA_W_BF16) {
-      const uint16_t* row = (const uint16_t*)a.emb.data + (size_t)id * K;
+      const uint16_t* base = (const uint16_t*)a.emb.data;
+      const int UT = K / 32;
       for (int k = tid * 8; k < K; k += 2048) {
-        const uint4 w = *(const uint4*)(row + k);
+        // row-major, or the 16-row tiled layout of the tied lm_head
+        const size_t off = a.emb.layout == LA_LAYOUT_ROWS
+                               ? (size_t)id * K + k
+                               : (((size_t)(id >> 4) * UT + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (id & 15)) * 8;
+        const uint4 w = *(const uint4*)(base + off);
         *(float4*)(out + k) = make_float4(bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16),
                                           bf16_to_f32(w.y & 0xFFFFu), bf16_to_f32(w.y >> 16));
         *(float4*)(out + k + 4) = make_float4(bf16_to_f32(w.z & 0xFFFFu), bf16_to_f32(w.z >> 16),

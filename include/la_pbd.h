@@ -53,18 +53,38 @@ typedef enum {
 /* Weight formats. */
 enum { LA_W_BF16 = 0, LA_W_INT4 = 1 };
 
+/* Weight layouts.  LA_LAYOUT_ROWS is the plain row-major matrix.  The tiled
+ * layouts hold the same values regrouped in tiles of 16 rows so that the
+ * matrix-core operand of one wave is one contiguous 1 KB block; they are
+ * written once by la_pack_weight.  Which 16 rows form tile t:
+ *   LA_LAYOUT_TILED     rows 16t .. 16t+15 (rows >= n are zero);
+ *   LA_LAYOUT_TILED_GU  rows 8t .. 8t+7 and n/2 + 8t .. n/2 + 8t+7 (the gate
+ *                       rows and the matching up rows of a [gate | up] matrix);
+ *   LA_LAYOUT_TILED_QKV for head h = t / 8, s = t % 8: rows 128h + 8s .. +7
+ *                       and 128h + 64 + 8s .. +7 (the RoPE pairs of a head).
+ * bf16 tiled: data = bf16 [n_tiles][k/32][64][8]; entry [t][u][16g + c][e] is
+ *   row c of tile t at column 32u + 8g + e.
+ * INT4 tiled (group 128): data = uint8 [n_tiles][k/128][64][16]; entry
+ *   [t][u][16g + c] holds the 32 codes of row c of tile t at columns
+ *   128u + 32g .. +31 packed as in row-major storage; scales = fp16
+ *   [n_tiles][k/128][16] (scale of row c of tile t, group u). */
+enum { LA_LAYOUT_ROWS = 0, LA_LAYOUT_TILED = 1, LA_LAYOUT_TILED_GU = 2, LA_LAYOUT_TILED_QKV = 3 };
+
 /* A weight matrix W[n, k] (y = x . W^T).
  *  LA_W_BF16: data = bf16 [n][k] row-major, scales = NULL, group ignored.
  *  LA_W_INT4: group-wise symmetric INT4 (WebGPU page, "Embedding gather /
  *    dequant"): data = uint8 [n][k/2], byte i of a row holds element 2i in its
  *    low nibble and element 2i+1 in its high nibble; scales = fp16 [n][k/group];
  *    element j of row r is (q - 8) * scales[r][j / group].  group is 32 for the
- *    embedding and 128 for the linears and the lm_head. */
+ *    embedding and 128 for the linears and the lm_head.
+ *  layout: one of LA_LAYOUT_*, as above. */
 typedef struct {
   int32_t fmt;
   int32_t n;
   int32_t k;
   int32_t group;
+  int32_t layout;
+  int32_t reserved;
   const void* data;
   const void* scales;
 } la_weight;
@@ -195,6 +215,16 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream);
+
+/* Repack a row-major weight (src->layout == LA_LAYOUT_ROWS) into one of the
+ * tiled layouts (bf16, or INT4 with group 128).  dst receives
+ * la_pack_weight_bytes(src, layout, 0) bytes of data and dst_scales (INT4
+ * only) la_pack_weight_bytes(src, layout, 1) bytes of scales; the caller then
+ * describes the copy with the same fmt/n/k/group and the new layout.  The values
+ * are copied bit for bit. */
+size_t la_pack_weight_bytes(const la_weight* src, int32_t layout, int32_t scales);
+la_status la_pack_weight(const la_weight* src, int32_t layout, void* dst, void* dst_scales,
+                         hipStream_t stream);
 
 /* Static text for a status code. */
 const char* la_status_str(int32_t status);

@@ -337,3 +337,105 @@ def test_step_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out_ids, ref_ids), r
         assert torch.equal(out_gap, ref_gap), r
+
+
+# ---------------------------------------------------------------- tiled weight layouts
+
+def _layout_rows(layout, n, n_tiles):
+    rows = np.zeros((n_tiles, 16), dtype=np.int64)
+    for t in range(n_tiles):
+        for c in range(16):
+            if layout == B.LA_LAYOUT_TILED_GU:
+                rows[t, c] = t * 8 + c if c < 8 else n // 2 + t * 8 + (c - 8)
+            elif layout == B.LA_LAYOUT_TILED_QKV:
+                h, s = t // 8, t % 8
+                rows[t, c] = h * 128 + (s * 8 + c if c < 8 else 64 + s * 8 + (c - 8))
+            else:
+                rows[t, c] = t * 16 + c
+    return rows
+
+
+def _tile_reference(w, layout):
+    """The tiled layout written out with numpy from its description in la_pbd.h."""
+    n, k = int(w["n"]), int(w["k"])
+    n_tiles = (n // 2 + 7) // 8 if layout == B.LA_LAYOUT_TILED_GU else (n + 15) // 16
+    rows = _layout_rows(layout, n, n_tiles).reshape(-1)
+    data = np.asarray(w["data"].cpu().numpy()).view(np.uint8).reshape(n, -1)
+    full = np.zeros((n_tiles * 16, data.shape[1]), dtype=np.uint8)
+    ok = rows < n
+    full[ok] = data[rows[ok]]
+    if w["fmt"] == "bf16":
+        t = full.reshape(n_tiles, 16, k // 32, 4, 16).transpose(0, 2, 3, 1, 4)
+        return t.reshape(-1), None
+    t = full.reshape(n_tiles, 16, k // 128, 4, 16).transpose(0, 2, 3, 1, 4)
+    sc = np.asarray(w["scales"].cpu().numpy()).view(np.uint16).reshape(n, -1)
+    sfull = np.zeros((n_tiles * 16, k // 128), dtype=np.uint16)
+    sfull[ok] = sc[rows[ok]]
+    s = sfull.reshape(n_tiles, 16, k // 128).transpose(0, 2, 1)
+    return t.reshape(-1), s.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+@pytest.mark.parametrize("layout,n", [(1, 2048 + 9), (2, 2 * 1024), (3, 2560)])
+def test_pack_weight_layouts_bit_exact(fmt, layout, n):
+    w = synth._weight(fmt, n, 2048, DEV, 111, layout)
+    p = B.pack_weight(w, layout)
+    torch.cuda.synchronize()
+    ref_d, ref_s = _tile_reference(w, layout)
+    assert np.array_equal(p["data"].cpu().numpy(), ref_d)
+    if fmt == "int4":
+        assert np.array_equal(p["scales"].cpu().numpy().view(np.uint16), ref_s)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+def test_wgemm_tiled_layouts(fmt):
+    g = torch.Generator(device=DEV).manual_seed(7)
+    K = 2048
+    for layout, N, silu in ((B.LA_LAYOUT_TILED, 2048 + 16, False), (B.LA_LAYOUT_TILED_GU, 2 * 1536, True)):
+        w = synth._weight(fmt, N, K, DEV, 121, layout)
+        wp = B.pack_weight(w, layout)
+        x = torch.randn((6, K), generator=g, device=DEV)
+        gain = synth.normal_bf16((K,), 0.02, 1.0, DEV, 122, layout)
+        y = B.wgemm(x, wp, norm_gain=gain, silu_gate=silu)
+        y_rows = B.wgemm(x, w, norm_gain=gain, silu_gate=silu)
+        torch.cuda.synchronize()
+        ref = _gemm_ref(x.cpu().numpy(), np_tree(w), gain.cpu().numpy(), silu=silu)
+        e = rel_l2(y.cpu().numpy(), ref)
+        _log(f"wgemm tiled {fmt} layout {layout}: rel-L2 {e:.2e}")
+        assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+        # the tiled and row-major layouts sum the same products in the same order
+        assert torch.equal(y, y_rows)
+
+
+def test_gather_from_tiled_embedding():
+    d = synth.ModelDims(n_layers=1, vocab=3001)
+    m = synth.make_model(d, "bf16", seed=131, device=DEV)
+    emb = B.pack_weight(m["embed"], B.LA_LAYOUT_TILED)
+    ids = torch.tensor([0, 3000, 2999, 15, 16, 17, 1234], dtype=torch.int32, device=DEV)
+    out = B.embed_gather(ids, emb)
+    torch.cuda.synchronize()
+    ref = O.embed_rows(ids.cpu().numpy(), np_tree(m["embed"]))
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+def test_step_packed_model_matches_oracle_and_row_major(fmt):
+    d = synth.ModelDims(n_layers=2, vocab=5003)
+    model = synth.make_model(d, fmt, 141, DEV)
+    P = torch.tensor([0, 17, 100, 1000], dtype=torch.int32)
+    cache = synth.make_cache(d, P, 6, seed=142, device=DEV)
+    ids = synth.draw_window_ids(4, 6, d.vocab, 143, device=DEV)
+    mn, cn = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    dm = B.DeviceModel(B.pack_model(model))
+    dr = B.DeviceModel(model)
+    dc = B.DeviceCache(cache, d.n_layers)
+    out_p, gap_p, hid_p = B.pbd_step(dm, dc, ids, P.to(DEV), 1006, want_hidden=True)
+    out_r, gap_r, hid_r = B.pbd_step(dr, dc, ids, P.to(DEV), 1006, want_hidden=True)
+    torch.cuda.synchronize()
+    ref = O.pbd_step(mn, cn, ids.cpu().numpy(), P.numpy(), return_hidden=True)
+    n, bad, excl = ids_match(out_p.cpu().numpy(), ref["ids"], ref["gap"])
+    e = rel_l2(hid_p.cpu().numpy(), ref["hidden"])
+    _log(f"step packed {fmt}: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
+    assert bad == 0 and e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+    assert torch.equal(out_p, out_r) and torch.equal(hid_p, hid_r)
