@@ -6,9 +6,9 @@
 // (RKLLM + RKNN)", "How it differs from the original", item 1; the Jetson
 // page, section 1.3, block mask).
 //
-// Work split: one wave per (sequence, KV head, run of pages).  The 8 query
-// heads of a KV head times W window rows form up to 64 query columns that share
-// every K/V page, so a page is read once for all of them:
+// Work split: a workgroup takes one run of pages of one (sequence, KV head),
+// one wave per tile of 16 query columns.  The 8 query heads of a KV head times
+// W window rows form up to 64 query columns that share every K/V page:
 //   S^T[key, query] = K_page . Q^T        16x16x32 bf16 matrix-core steps, Q split
 //                                         into bf16 hi + lo columns (K is exact bf16)
 //   online softmax per query column       exp2 on pre-scaled scores, one max per page
@@ -16,8 +16,11 @@
 //                                         S^T accumulator layout is exactly the P^T
 //                                         operand layout, so P never leaves registers
 // V pages are stored dim-major ([D][16 keys]) so a V^T operand fragment is one
-// 8-byte load.  Each wave writes (max, sum, unnormalised O) for its run; a merge
-// kernel combines the runs with the usual log-sum-exp rescaling in a fixed order.
+// 8-byte load.  The step is latency bound (a layer reads about a megabyte of KV
+// at batch 1), so a run is short and issues all of its loads before it waits.
+// Each run writes (max, sum, unnormalised O); a merge kernel combines the runs
+// with log-sum-exp rescaling in a fixed order.  A sequence that fits one run
+// is normalised and stored directly.
 #include "la_internal.hpp"
 
 namespace la {
@@ -29,259 +32,322 @@ __device__ __forceinline__ int attn_keys(const AttnArgs& a, int b) {
   return n;
 }
 
-template <int NQT>
-__global__ __launch_bounds__(256) void k_attn_partial(AttnArgs a) {
-  __shared__ bf16x8 qf[2 * NQT][4][64];
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, r = lane & 15;
-  const int G = a.Hq / a.Hkv;
-  const int NQ = a.W * G;
-  const int D = kHeadDim;
-  const int n_keys = attn_keys(a, b);
-  const int kps = a.pages_per_split * kBlock;
-  const int split0 = blockIdx.x * 4;
-  if (split0 * kps >= n_keys) return;  // uniform over the workgroup
+// K and V of one page for this lane: K rows are keys, V^T rows are dims.
+struct PageRegs {
+  bf16x8 k[4];
+  s16x4 v[8];
+};
 
-  // Q^T operand fragments, hi tiles [0, NQT) and lo tiles [NQT, 2 NQT).
-  for (int idx = threadIdx.x; idx < NQT * 16 * 16; idx += 256) {
-    const int qi = idx >> 4, c = idx & 15;
-    const int kb = c >> 2, gg = c & 3;
-    float v[8];
-    if (qi < NQ) {
-      const int wr = qi / G, hg = qi - wr * G;
-      const float* src = a.q + ((size_t)(b * a.W + wr) * a.Hq + kvh * G + hg) * D + c * 8;
-      const float4 v0 = *(const float4*)src, v1 = *(const float4*)(src + 4);
-      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-    } else {
+__device__ __forceinline__ void load_page(const AttnArgs& a, int blk, int kvh, PageRegs& pg) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+  const uint16_t* Kp = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlock * kHeadDim;
+  const uint16_t* Vp = a.vc + ((size_t)blk * a.Hkv + kvh) * kHeadDim * kBlock;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-    uint32_t hi[8], lo[8];
+  for (int kb = 0; kb < 4; ++kb) pg.k[kb] = *(const bf16x8*)(Kp + r * kHeadDim + kb * 32 + g * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_hi_lo(v[e], hi[e], lo[e]);
-    const u32x4 H = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
-                     hi[6] | (hi[7] << 16)};
-    const u32x4 L = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                     lo[6] | (lo[7] << 16)};
-    const int ct = qi >> 4, fl = gg * 16 + (qi & 15);
-    qf[ct][kb][fl] = __builtin_bit_cast(bf16x8, H);
-    qf[NQT + ct][kb][fl] = __builtin_bit_cast(bf16x8, L);
-  }
-  __syncthreads();
+  for (int dt = 0; dt < 8; ++dt) pg.v[dt] = *(const s16x4*)(Vp + (dt * 16 + r) * kBlock + 4 * g);
+}
 
-  const int split = split0 + wave;
-  const int k0 = split * kps;
-  if (k0 >= n_keys) return;
-  const int k1 = min(n_keys, k0 + kps);
+// Running state of one wave: online-softmax max and sum of its 16 query
+// columns and the unnormalised O^T tile (dims x queries).
+struct AttnState {
+  float m, l;
+  f32x4 acc[8];
+};
+
+// One page (keys p0 .. p0+nvalid-1 valid, nvalid >= 1) into the running state.
+__device__ __forceinline__ void attn_page(PageRegs& pg, int nvalid, const bf16x8 (&qh)[4],
+                                          const bf16x8 (&ql)[4], AttnState& st) {
+  const int lane = threadIdx.x & 63, g = lane >> 4;
   const float sl2 = 0.08838834764831845f * 1.4426950408889634f;  // log2(e) / sqrt(128)
-
-  float mrun[NQT], lrun[NQT];
-  f32x4 acc[8][NQT];
+  if (nvalid < kBlock) {
+    // keys past the bound: zero their values (unused slots may hold anything)
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    mrun[qt] = -INFINITY;
-    lrun[qt] = 0.f;
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 4; ++e)
+        if (4 * g + e >= nvalid) pg.v[dt][e] = 0;
   }
-
-  // K and V of one page for this lane: K rows are keys, V^T rows are dims
-  auto load_page = [&](int p0, bf16x8 (&ka)[4], s16x4 (&va)[8]) {
-    int blk = a.block_table[(size_t)b * a.max_blocks + p0 / kBlock];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    const uint16_t* Kp = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlock * D;
-    const uint16_t* Vp = a.vc + ((size_t)blk * a.Hkv + kvh) * D * kBlock;
+  f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) ka[kb] = *(const bf16x8*)(Kp + r * D + kb * 32 + g * 8);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) va[dt] = *(const s16x4*)(Vp + (dt * 16 + r) * kBlock + 4 * g);
-  };
-  bf16x8 ka[4], kn[4];
-  s16x4 va[8], vn[8];
-  load_page(k0, ka, va);
-  for (int p0 = k0; p0 < k1; p0 += kBlock) {
-    // the next page is in flight while this one is processed
-    if (p0 + kBlock < k1) load_page(p0 + kBlock, kn, vn);
-    const int nvalid = k1 - p0;
-    if (nvalid < kBlock) {
-      // keys past the bound: zero their values (unused slots may hold anything)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * g + e >= nvalid) va[dt][e] = 0;
-    }
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        sh = mfma_16x16x32(ka[kb], qf[qt][kb][lane], sh);
-        sl = mfma_16x16x32(ka[kb], qf[NQT + qt][kb][lane], sl);
-      }
-      float s[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[e] = (sh[e] + sl[e]) * sl2;
-        if (4 * g + e >= nvalid) s[e] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[qt], mx);
-      const float alpha = exp2f(mrun[qt] - mnew);
-      float p[4], ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = exp2f(s[e] - mnew);
-        ps += p[e];
-      }
-      lrun[qt] = lrun[qt] * alpha + ps;
-      mrun[qt] = mnew;
-      s16x4 ph, pl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t h, l;
-        split_hi_lo(p[e], h, l);
-        ph[e] = (short)h;
-        pl[e] = (short)l;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        acc[dt][qt] *= alpha;
-        acc[dt][qt] = mfma_16x16x16(va[dt], ph, acc[dt][qt]);
-        acc[dt][qt] = mfma_16x16x16(va[dt], pl, acc[dt][qt]);
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) ka[kb] = kn[kb];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) va[dt] = vn[dt];
+  for (int kb = 0; kb < 4; ++kb) {
+    sh = mfma_16x16x32(pg.k[kb], qh[kb], sh);
+    sl = mfma_16x16x32(pg.k[kb], ql[kb], sl);
   }
-
-  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.max_splits + split;
+  float sc[4];
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    float l = lrun[qt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int qi = qt * 16 + r;
-    if (g == 0) {
-      float2* ml = (float2*)a.part_ml + unit * a.nqp + qi;
-      *ml = make_float2(mrun[qt], l);
-    }
-    float* po = a.part_o + (unit * a.nqp + qi) * D + 4 * g;
+  for (int e = 0; e < 4; ++e) {
+    sc[e] = (sh[e] + sl[e]) * sl2;
+    if (4 * g + e >= nvalid) sc[e] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(st.m, mx);
+  const float alpha = exp2f(st.m - mnew);
+  float p[4], ps = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = acc[dt][qt];
+  for (int e = 0; e < 4; ++e) {
+    p[e] = exp2f(sc[e] - mnew);
+    ps += p[e];
+  }
+  st.l = st.l * alpha + ps;
+  st.m = mnew;
+  s16x4 ph, pl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t h, l;
+    split_hi_lo(p[e], h, l);
+    ph[e] = (short)h;
+    pl[e] = (short)l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    st.acc[dt] *= alpha;
+    st.acc[dt] = mfma_16x16x16(pg.v[dt], ph, st.acc[dt]);
+    st.acc[dt] = mfma_16x16x16(pg.v[dt], pl, st.acc[dt]);
   }
 }
 
-// One workgroup per (query column, KV head, sequence): 512 threads = 128 dims x
-// 4 interleaved subsets of the splits; the log-sum-exp weights are computed once
-// in LDS and the four partial sums are added in a fixed order.
-__global__ __launch_bounds__(512) void k_attn_merge(AttnArgs a) {
-  extern __shared__ float wsh[];  // [max_splits] weights
-  __shared__ float red[512];
-  __shared__ float so[kHeadDim];
-  __shared__ float s_M, s_den;
-  const int qi = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, d = tid & 127, part = tid >> 7;
+// Store the normalised output of query column qi, dims [d0, d0 + 8).
+__device__ __forceinline__ void attn_store8(const AttnArgs& a, int b, int kvh, int qi, int d0,
+                                            const float v[8]) {
   const int G = a.Hq / a.Hkv;
+  const int wr = qi / G, hg = qi - wr * G;
+  const int row = b * a.W + wr;
+  const int h = kvh * G + hg;
+  const int ldo = a.Hq * kHeadDim;
+  if (a.out) {
+    float* o = a.out + (size_t)row * ldo + h * kHeadDim + d0;
+    *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  if (a.out_apack) apack_store_chunk(a.out_apack, ldo, row, (h * kHeadDim + d0) / 8, v, a.out_int4);
+}
+
+// One workgroup per (run of pages_per_split pages, KV head, sequence); wave qt
+// takes query tile qt.  Every load the run needs is issued before any result
+// is waited for: the block ids of all its pages (one per lane), the wave's Q
+// fragments (kept in registers), then the pages two at a time.  With a single
+// run per sequence the result is normalised and stored here; otherwise
+// (max, sum, unnormalised O) goes to the run's partial slot.
+template <int NQT>
+__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int qt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.Hq / a.Hkv;
+  const int NQ = a.W * G;
+  const bool direct = a.max_splits == 1;
+  const int n_keys = attn_keys(a, b);
+  const int kps = a.pages_per_split * kBlock;
+  const int k0 = split * kps;
+  const int qi = qt * 16 + r;
+  if (k0 >= n_keys) {  // uniform over the workgroup
+    if (direct && qi < NQ && (g & 1) == 0) {
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < 8; ++dt) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, z);
+    }
+    return;
+  }
+  const int k1 = min(n_keys, k0 + kps);
+  const int first = k0 / kBlock;
+  const int npages = (k1 - k0 + kBlock - 1) / kBlock;  // 1 .. pages_per_split (<= 64)
+  int bt = a.block_table[(size_t)b * a.max_blocks + first + min(lane, npages - 1)];
+  bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
+
+  // Q^T operand of this wave's tile: lane (g, r) holds dims kb*32 + 8g .. +8 of
+  // query column qi as bf16 hi and lo (absent columns: zeros).
+  bf16x8 qh[4], ql[4];
+  {
+    const int qc = qi < NQ ? qi : 0;
+    const int wr = qc / G, hg = qc - wr * G;
+    const float* src = a.q + ((size_t)(b * a.W + wr) * a.Hq + kvh * G + hg) * kHeadDim + g * 8;
+    float4 v[8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      v[2 * kb] = *(const float4*)(src + kb * 32);
+      v[2 * kb + 1] = *(const float4*)(src + kb * 32 + 4);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float x[8] = {v[2 * kb].x, v[2 * kb].y, v[2 * kb].z, v[2 * kb].w,
+                          v[2 * kb + 1].x, v[2 * kb + 1].y, v[2 * kb + 1].z, v[2 * kb + 1].w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_hi_lo(qi < NQ ? x[e] : 0.f, hi[e], lo[e]);
+      const u32x4 H = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
+                       hi[6] | (hi[7] << 16)};
+      const u32x4 L = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+                       lo[6] | (lo[7] << 16)};
+      qh[kb] = __builtin_bit_cast(bf16x8, H);
+      ql[kb] = __builtin_bit_cast(bf16x8, L);
+    }
+  }
+
+  AttnState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < npages; c += 2) {
+    // both pages of the pair in flight at once (the second clamped to a real
+    // page, so the load is unconditional)
+    PageRegs p0, p1;
+    load_page(a, __builtin_amdgcn_readlane(bt, c), kvh, p0);
+    load_page(a, __builtin_amdgcn_readlane(bt, min(c + 1, npages - 1)), kvh, p1);
+    const int key = k0 + c * kBlock;
+    attn_page(p0, k1 - key, qh, ql, st);
+    if (c + 1 < npages) attn_page(p1, k1 - key - kBlock, qh, ql, st);
+  }
+  float lsum = st.l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  if (direct) {
+    // lane (g, r) holds dims dt*16 + 4g .. +4 of column qi; even g lanes take
+    // the next 4 dims from lane (g+1, r) and store 8
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = st.acc[dt][e] * inv;
+        v[4 + e] = __shfl_xor(v[e], 16);
+      }
+      if (qi < NQ && (g & 1) == 0) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, v);
+    }
+    return;
+  }
+  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.max_splits + split;
+  if (g == 0) {
+    float2* ml = (float2*)a.part_ml + unit * a.nqp + qi;
+    *ml = make_float2(st.m, lsum);
+  }
+  float* po = a.part_o + (unit * a.nqp + qi) * kHeadDim + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = st.acc[dt];
+}
+
+// Merge of the runs.  A workgroup of 256 threads takes one query column of a
+// (sequence, KV head): thread (chunk c of 4 dims, group j of 8) combines runs
+// j, j+8, j+16, ... (eight at a time, all loads of a group in flight together),
+// then the 8 groups are combined across lanes in a fixed butterfly, so the
+// result does not depend on timing.  Combination is the usual log-sum-exp
+// rescaling of (max, sum, unnormalised O).
+constexpr int kMergeGroups = 8;
+constexpr int kMergeBatch = 8;
+
+struct MergeAcc {
+  float m, den;
+  float4 num;
+};
+
+__device__ __forceinline__ MergeAcc merge_pair(const MergeAcc& x, const MergeAcc& y) {
+  MergeAcc r;
+  r.m = fmaxf(x.m, y.m);
+  const float sx = x.m == -INFINITY ? 0.f : exp2f(x.m - r.m);
+  const float sy = y.m == -INFINITY ? 0.f : exp2f(y.m - r.m);
+  r.den = x.den * sx + y.den * sy;
+  r.num.x = x.num.x * sx + y.num.x * sy;
+  r.num.y = x.num.y * sx + y.num.y * sy;
+  r.num.z = x.num.z * sx + y.num.z * sy;
+  r.num.w = x.num.w * sx + y.num.w * sy;
+  return r;
+}
+
+__device__ __forceinline__ MergeAcc shfl_xor_acc(const MergeAcc& x, int mask) {
+  MergeAcc r;
+  r.m = __shfl_xor(x.m, mask);
+  r.den = __shfl_xor(x.den, mask);
+  r.num.x = __shfl_xor(x.num.x, mask);
+  r.num.y = __shfl_xor(x.num.y, mask);
+  r.num.z = __shfl_xor(x.num.z, mask);
+  r.num.w = __shfl_xor(x.num.w, mask);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int qi = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 3;                              // run group
+  const int c4 = (threadIdx.x >> 6) * 8 + (lane & 7);  // 4-dim chunk
   const int n_keys = attn_keys(a, b);
   const int kps = a.pages_per_split * kBlock;
   const int ns = (n_keys + kps - 1) / kps;
   const size_t base = ((size_t)b * a.Hkv + kvh) * a.max_splits;
   const float2* ml = (const float2*)a.part_ml;
-  float mx = -INFINITY;
-  for (int s = tid; s < ns; s += 512) mx = fmaxf(mx, ml[(base + s) * a.nqp + qi].x);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = 256; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float den = 0.f;
-  for (int s = tid; s < ns; s += 512) {
-    const float2 v = ml[(base + s) * a.nqp + qi];
-    const float w = exp2f(v.x - M);
-    wsh[s] = w;
-    den += w * v.y;
-  }
-  red[tid] = den;
-  __syncthreads();
-  for (int o = 256; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  if (tid == 0) s_den = red[0];
-  __syncthreads();
-  float num = 0.f;
-  const float* po = a.part_o + ((base)*a.nqp + qi) * kHeadDim + d;
-  const size_t sstride = (size_t)a.nqp * kHeadDim;
-  int s = part;
-  for (; s + 12 < ns; s += 16) {
-    const float o0 = po[(size_t)s * sstride], o1 = po[(size_t)(s + 4) * sstride];
-    const float o2 = po[(size_t)(s + 8) * sstride], o3 = po[(size_t)(s + 12) * sstride];
-    num += wsh[s] * o0;
-    num += wsh[s + 4] * o1;
-    num += wsh[s + 8] * o2;
-    num += wsh[s + 12] * o3;
-  }
-  for (; s < ns; s += 4) num += wsh[s] * po[(size_t)s * sstride];
-  red[tid] = num;
-  __syncthreads();
-  (void)s_M;
-  if (part == 0) {
-    const float o = ns > 0 ? (red[d] + red[d + 128] + red[d + 256] + red[d + 384]) / s_den : 0.f;
-    const int wr = qi / G, hg = qi - wr * G;
-    const int row = b * a.W + wr;
-    const int h = kvh * G + hg;
-    const int ldo = a.Hq * kHeadDim;
-    if (a.out) a.out[(size_t)row * ldo + h * kHeadDim + d] = o;
-    so[d] = o;
-  }
-  if (a.out_apack) {
-    __syncthreads();
-    if (tid < 16) {
-      const int wr = qi / G, hg = qi - wr * G;
-      const int row = b * a.W + wr;
-      const int h = kvh * G + hg;
-      float v[8];
+  MergeAcc acc;
+  acc.m = -INFINITY;
+  acc.den = 0.f;
+  acc.num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = j; s0 < ns; s0 += kMergeGroups * kMergeBatch) {
+    float2 m[kMergeBatch];
+    float4 o[kMergeBatch];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = so[tid * 8 + e];
-      apack_store_chunk(a.out_apack, a.Hq * kHeadDim, row, (h * kHeadDim) / 8 + tid, v, a.out_int4);
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int s = s0 + i * kMergeGroups;
+      const size_t u = base + (s < ns ? s : 0);  // clamped to a slot inside the buffer
+      m[i] = ml[u * a.nqp + qi];
+      o[i] = *(const float4*)(a.part_o + (u * a.nqp + qi) * kHeadDim + 4 * c4);
     }
+    float bm = acc.m;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (s0 + i * kMergeGroups < ns) bm = fmaxf(bm, m[i].x);
+    const float sc = acc.m == -INFINITY ? 0.f : exp2f(acc.m - bm);
+    acc.den *= sc;
+    acc.num.x *= sc; acc.num.y *= sc; acc.num.z *= sc; acc.num.w *= sc;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i * kMergeGroups < ns) {
+        const float w = exp2f(m[i].x - bm);
+        acc.den += w * m[i].y;
+        acc.num.x += w * o[i].x; acc.num.y += w * o[i].y;
+        acc.num.z += w * o[i].z; acc.num.w += w * o[i].w;
+      }
+    }
+    acc.m = bm;
   }
+  // groups j and j^1, j^2, j^4 (lanes 8, 16, 32 apart); both partners compute
+  // the same sums, so every lane of a chunk ends with one identical result
+  acc = merge_pair(acc, shfl_xor_acc(acc, 8));
+  acc = merge_pair(acc, shfl_xor_acc(acc, 16));
+  acc = merge_pair(acc, shfl_xor_acc(acc, 32));
+  const float inv = ns > 0 ? 1.f / acc.den : 0.f;
+  float v[8];
+  v[0] = acc.num.x * inv; v[1] = acc.num.y * inv; v[2] = acc.num.z * inv; v[3] = acc.num.w * inv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[4 + e] = __shfl_xor(v[e], 1);
+  if (j == 0 && (c4 & 1) == 0) attn_store8(a, b, kvh, qi, 4 * c4, v);
 }
 
+// Runs of pages_per_split pages: two pages per run while that keeps the grid
+// within about 1024 workgroups, longer runs (fewer partial results) beyond.
 void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits) {
   const int max_pages = (max_len + kBlock - 1) / kBlock;
-  const long total = (long)B * Hkv * max_pages;
-  int pps = (int)((total + 1023) / 1024);  // about 1024 waves in flight
-  if (pps < 2) pps = 2;                     // at least two pages: the second overlaps the first
-  if (pps > max_pages) pps = max_pages > 0 ? max_pages : 1;
+  int pps = 2;
+  while (pps < 64 && (long)B * Hkv * ((max_pages + pps - 1) / pps) > 1024) pps *= 2;
+  if (pps > max_pages) pps = max_pages;
+  if (pps < 1) pps = 1;
   *pages_per_split = pps;
   *max_splits = (max_pages + pps - 1) / pps;
-  if (*max_splits < 1) *max_splits = 1;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int nqt = a.nqp / 16;
-  const dim3 grid((a.max_splits + 3) / 4, a.Hkv, a.B);
+  const dim3 grid(a.max_splits, a.Hkv, a.B), block(nqt * 64);
   switch (nqt) {
-    case 1: hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(k_attn_partial<3>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(k_attn_split<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_attn_split<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(k_attn_split<3>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(k_attn_split<4>, grid, block, 0, s, a); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.max_splits == 1) return e;
   const int NQ = a.W * (a.Hq / a.Hkv);
-  hipLaunchKernelGGL(k_attn_merge, dim3(NQ, a.Hkv, a.B), dim3(512), (size_t)a.max_splits * 4, s, a);
+  hipLaunchKernelGGL(k_attn_merge, dim3(NQ, a.Hkv, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
