@@ -29,10 +29,32 @@ struct Carver {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // `tiled`: the tiled layout this use accepts besides row-major (-1: none).
+// Bytes of a weight's data and INT4 scales in its layout.
+void weight_storage(const la_weight* w, size_t* data, size_t* scales) {
+  const bool int4 = w->fmt == LA_W_INT4;
+  if (w->layout == LA_LAYOUT_ROWS) {
+    *data = int4 ? (size_t)w->n * (w->k / 2) : (size_t)w->n * w->k * 2;
+    *scales = int4 && w->group > 0 ? (size_t)w->n * (w->k / w->group) * 2 : 0;
+    return;
+  }
+  const size_t n_tiles = w->layout == LA_LAYOUT_TILED_GU ? (size_t)(w->n / 2 + 7) / 8
+                                                         : (size_t)(w->n + 15) / 16;
+  *data = int4 ? n_tiles * 16 * (size_t)(w->k / 2) : n_tiles * 16 * (size_t)w->k * 2;
+  *scales = int4 ? n_tiles * (w->k / 128) * 16 * 2 : 0;
+}
+
+// The kernels address a weight with 32-bit offsets.
+constexpr size_t kMaxWeightBytes = (size_t)1 << 31;
+
 la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int int4_group,
                        int tiled) {
   if (!w || !w->data) return LA_ERR_ARG;
   if (w->n != n || w->k != k) return LA_ERR_SHAPE;
+  {
+    size_t wb, sb;
+    weight_storage(w, &wb, &sb);
+    if (wb >= kMaxWeightBytes) return LA_ERR_SHAPE;
+  }
   if (!aligned16(w->data)) return LA_ERR_ARG;
   if (w->layout != LA_LAYOUT_ROWS && w->layout != tiled) return LA_ERR_UNSUPPORTED;
   if (w->layout != LA_LAYOUT_ROWS && k % 128) return LA_ERR_SHAPE;
@@ -180,6 +202,10 @@ GemmArgs base_gemm(const la_weight* w, int M) {
   memset(&g, 0, sizeof(g));
   g.w = w->data;
   g.wscale = (const uint16_t*)w->scales;
+  size_t wb, sb;
+  weight_storage(w, &wb, &sb);
+  g.w_bytes = (uint32_t)wb;
+  g.s_bytes = (uint32_t)sb;
   g.layout = w->layout;
   g.M = M;
   g.N = w->n;

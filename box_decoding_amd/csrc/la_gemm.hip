@@ -11,14 +11,17 @@
 // 12 of the 16 operand rows.  The vector ALUs are left for the epilogues.
 //
 // Work decomposition: a work item is one tile of 16 operand columns (weight
-// rows) and one slice of K; a workgroup walks the items blockIdx.x,
-// blockIdx.x + gridDim.x, ... and its waves split the item's K range, then
-// combine their partial sums through LDS.  No workgroup ever waits for
-// another: a device-wide fence costs more than a kernel boundary on this chip,
-// so a K-sliced GEMM writes partial sums that the next kernel adds up.  A
-// wave's weight loads form one stream across work items (two stages in
-// flight); loads are branch-free (clamped address, masked value) so that the
-// compiler never drains the stream.
+// rows) and one slice of K; workgroup b takes slice b % ksplit and every
+// (gridDim.x / ksplit)-th tile, and its loading waves split the slice, then
+// combine their partial sums through LDS; one more wave per workgroup runs the
+// epilogues.  No workgroup ever waits for another: a device-wide fence costs
+// more than a kernel boundary on this chip, so a K-sliced GEMM writes partial
+// sums that the next kernel adds up.  A loading wave's weight loads form one
+// stream across its work items with up to 7 stages in flight; the loads are
+// raw buffer loads whose masked units carry an out-of-range offset (they read
+// zero and touch no memory), so no branch ever splits the stream and the
+// loading waves never store to global memory: the compiler counts the loads
+// in flight exactly and never drains the ring.
 #include "la_internal.hpp"
 
 namespace la {
@@ -26,6 +29,17 @@ namespace la {
 // Rows per GEMM launch: four 8-row tiles keep the accumulators and the operand
 // fragments of a wave in registers.
 constexpr int kRowsPerLaunch = 32;
+
+// Activation pieces (16 bytes) per thread of the one-batch LDS copy, and the
+// INT4 group sums per thread.
+__host__ __device__ constexpr int copy_batch(int mt) { return mt == 1 ? 12 : 16; }
+constexpr int kCopySums = 2;
+
+// LDS of the cross-wave reduction: [nw][MT][64] f32x4 partial tiles plus the
+// [MT*8][17] output tile, rounded up to 16 bytes.
+__host__ __device__ constexpr size_t gemm_red_bytes(int nw, int mt) {
+  return ((size_t)nw * mt * 64 * 16 + (size_t)mt * 8 * 17 * 4 + 15) / 16 * 16;
+}
 
 // ---------------------------------------------------------------- column maps
 
@@ -56,93 +70,174 @@ __host__ __device__ __forceinline__ int layout_row(int layout, int N, int tile, 
 
 // ---------------------------------------------------------------- stages
 
-// One pipeline stage for one lane: U units of 32 (bf16) or 128 (INT4) reduction
-// elements of the lane's weight column, plus (bf16) the matching activation
-// fragments, so that neither waits on its load.
-template <bool INT4, int MT, int U>
+// Kernel modes, chosen by the host per GEMM:
+//   single: every wave has exactly one stage; its activations are loaded with
+//           its weights (QKV and O projections at small M)
+//   ring:   a 2-deep ring, activations loaded with every stage (4 row tiles)
+//   lds:    the workgroup's activation slice is copied to LDS once and a deep
+//           ring of weight-only stages streams through it (gate/up, down,
+//           lm_head)
+// Every load instruction costs address-unit time even when it fetches
+// nothing, so the modes avoid loads that carry no data.
+constexpr int kModeSingle = 0;
+constexpr int kModeRing = 1;
+constexpr int kModeLds = 2;
+
+// Chunks of 8 reduction elements per unit (a unit is 32 bf16 or 128 INT4 k).
+template <bool INT4>
+__host__ __device__ constexpr int unit_chunks() { return INT4 ? 16 : 4; }
+
+// Units per stage and stages in the ring.
+template <bool INT4, int MT, int MODE>
+__host__ __device__ constexpr int stage_units() {
+  return INT4 ? 2 : (MODE == kModeRing ? (MT == 4 ? 2 : MT == 2 ? 4 : 8) : 8);
+}
+template <bool INT4, int MT, int MODE>
+__host__ __device__ constexpr int ring_depth() {
+  return MODE == kModeSingle ? 1 : MODE == kModeRing ? 2 : (INT4 ? 8 : (MT == 1 ? 4 : 3));
+}
+// Activation fragments travel in the stage (else: LDS, or for INT4 in the
+// 2-deep ring, global loads at multiply time).
+template <bool INT4, int MODE>
+__host__ __device__ constexpr bool a_in_stage() {
+  return MODE == kModeSingle || (MODE == kModeRing && !INT4);
+}
+
+// One pipeline stage for one lane: U units of the lane's weight column, their
+// INT4 scales and, when a_in_stage, the matching activation fragments (and
+// INT4 group sums).
+template <bool INT4, int MT, int U, bool AIN>
 struct Stage {
   u32x4 w[U];
-  float s[INT4 ? U : 1];
-  bf16x8 af[INT4 ? 1 : U][MT];
+  uint16_t s[INT4 ? U : 1];  // fp16 bits, converted at multiply time
+  bf16x8 af[AIN ? (INT4 ? 4 * U : U) : 1][MT];
+  f32x4 as[(AIN && INT4) ? U : 1][MT];
 };
 
-// Weight location of this lane for a work item: base pointers for the unit loop.
+// Weight location of this lane for a work item, as byte offsets into the
+// weight (and INT4 scale) buffer resources.
 struct WPtr {
-  const uint8_t* w;     // byte address of unit 0 for this lane
-  size_t ustride;       // bytes between consecutive units
-  const uint16_t* s;    // INT4: scale of unit 0 for this lane
-  int sstride;          // INT4: scale elements between consecutive units
+  uint32_t w;           // unit 0 of this lane
+  uint32_t ustride;     // between consecutive units
+  uint32_t s;           // INT4: scale of unit 0 for this lane
+  uint32_t sstride;     // INT4: between consecutive units
 };
 
 template <bool INT4, int EPI>
 __device__ __forceinline__ WPtr wptr(const GemmArgs& a, int tile) {
   const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
   WPtr p;
-  p.s = nullptr;
+  p.s = 0;
   p.sstride = 0;
   if (a.layout != LA_LAYOUT_ROWS) {
     const int UT = INT4 ? (a.K >> 7) : (a.K >> 5);
-    p.w = (const uint8_t*)a.w + ((size_t)tile * UT * 64 + lane) * 16;
+    p.w = ((uint32_t)tile * UT * 64 + lane) * 16;
     p.ustride = 1024;
     if (INT4) {
-      p.s = a.wscale + (size_t)tile * UT * 16 + c;
-      p.sstride = 16;
+      p.s = ((uint32_t)tile * UT * 16 + c) * 2;
+      p.sstride = 32;
     }
   } else {
     int r = col_row<EPI>(a.N, tile, c);
     if (r >= a.N) r = a.N - 1;  // lm_head tail columns: read a valid row, drop the result
     if (!INT4) {
-      p.w = (const uint8_t*)a.w + ((size_t)r * a.K + g * 8) * 2;
+      p.w = ((uint32_t)r * a.K + g * 8) * 2;
       p.ustride = 64;
     } else {
-      p.w = (const uint8_t*)a.w + (size_t)r * (a.K >> 1) + g * 16;
+      p.w = (uint32_t)r * (a.K >> 1) + g * 16;
       p.ustride = 64;
-      p.s = a.wscale + (size_t)r * (a.K >> 7);
-      p.sstride = 1;
+      p.s = (uint32_t)r * (a.K >> 7) * 2;
+      p.sstride = 2;
     }
   }
   return p;
 }
 
-// Loads are branch-free: a unit past the wave's range reads a clamped (valid)
-// address and is masked to zero at compute time.
-template <bool INT4, int MT, int U>
-__device__ __forceinline__ void load_stage(Stage<INT4, MT, U>& b, const WPtr& wp,
-                                           const uint16_t* ap, int K8, int u, int ulo, int uhi,
-                                           int mtv) {
+// Buffer loads: an offset at or past the end of the resource reads zero and
+// touches no memory, which masks a unit without a branch.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kCfgDword = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;        // cache policy: streaming
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kCfgDword);
+}
+
+template <int POLICY>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
+// Where a stage reads its activations when they are not in the stage: the
+// workgroup's LDS copy of the K slice (chunk index relative to the slice start)
+// or the packed rows in global memory.
+struct ASrc {
+  const uint16_t* p;    // lane base (row l%16 folded in)
+  const float* s;       // INT4 group sums, lane base (4 (l/16) folded in)
+  int tstride;          // elements between row tiles
+  int sts;              // group-sum floats between row tiles
+  int c0;               // chunk index of the slice start (0 for global)
+  int u0;               // unit index of the slice start (0 for global)
+  int mtv;              // valid row tiles
+};
+
+__device__ __forceinline__ bf16x8 a_frag(const ASrc& A, int mt, int kc) {
+  return *(const bf16x8*)(A.p + (size_t)min(mt, A.mtv - 1) * A.tstride + (size_t)(kc - A.c0) * 128);
+}
+__device__ __forceinline__ f32x4 a_sums(const ASrc& A, int mt, int uu) {
+  return *(const f32x4*)(A.s + (size_t)min(mt, A.mtv - 1) * A.sts + (size_t)(uu - A.u0) * 16);
+}
+
+// Loads are branch-free: a unit past the wave's range (or a stage past the
+// end) reads zero weights and a zero scale; its activation loads repeat the
+// wave's last unit.
+template <bool INT4, int MT, int U, bool AIN>
+__device__ __forceinline__ void load_stage(Stage<INT4, MT, U, AIN>& b, const WPtr& wp,
+                                           __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs,
+                                           const ASrc& G, int u, int ulo, int uhi) {
   const int g = (threadIdx.x & 63) >> 4;
   const int ulast = uhi > ulo ? uhi - 1 : ulo;
 #pragma unroll
   for (int i = 0; i < U; ++i) {
+    // a masked unit gets bit 31 set (offsets of real units stay below 2^31):
+    // arithmetic, not a select, so that no branch ever splits the stream
+    const uint32_t dead = (uint32_t)(u + i >= uhi) << 31;  // wave-uniform
     const int uu = min(u + i, ulast);
-    b.w[i] = __builtin_nontemporal_load((const u32x4*)(wp.w + (size_t)uu * wp.ustride));
-    if (INT4) b.s[INT4 ? i : 0] = fp16_to_f32(wp.s[(size_t)uu * wp.sstride]);
-    if (!INT4) {
+    b.w[i] = bload16<kNonTemporal>(rw, (wp.w + (uint32_t)uu * wp.ustride) | dead);
+    if (INT4) {
+      const uint32_t so = (wp.s + (uint32_t)uu * wp.sstride) | dead;
+      b.s[INT4 ? i : 0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+    }
+    if (AIN) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        b.af[INT4 ? 0 : i][mt] = *(const bf16x8*)(ap + ((size_t)min(mt, mtv - 1) * K8 + uu * 4 + g) * 128);
+      for (int mt = 0; mt < MT; ++mt) {
+        if (INT4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b.af[AIN ? (INT4 ? 4 * i + j : i) : 0][mt] = a_frag(G, mt, uu * 16 + g * 4 + j);
+          b.as[(AIN && INT4) ? i : 0][mt] = a_sums(G, mt, uu);
+        } else {
+          b.af[AIN ? i : 0][mt] = a_frag(G, mt, uu * 4 + g);
+        }
+      }
     }
   }
 }
 
-// Activation fragment of row tile mt, 8-wide chunk kc, for this lane (row l%16).
-__device__ __forceinline__ bf16x8 a_frag(const uint16_t* ap, int K8, int mt, int kc) {
-  return *(const bf16x8*)(ap + ((size_t)mt * K8 + kc) * 128);
-}
-
-template <int MT, bool INT4, int U>
-__device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U>& b, const uint16_t* ap,
-                                              const float* asp, int K8, int KG, int u, int ulo,
-                                              int uhi, int mtv, f32x4 (&acc)[MT]) {
+template <int MT, bool INT4, int U, bool AIN>
+__device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U, AIN>& b, const ASrc& A,
+                                              int u, int ulo, int uhi, f32x4 (&acc)[MT]) {
   const int g = (threadIdx.x & 63) >> 4;
   const int ulast = uhi > ulo ? uhi - 1 : ulo;
   if (!INT4) {
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const uint32_t keep = (u + i < uhi) ? 0xFFFFFFFFu : 0u;  // wave-uniform
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, b.w[i] & keep);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, b.w[i]);  // zero for a masked unit
+      const int uu = min(u + i, ulast);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_16x16x32(b.af[INT4 ? 0 : i][mt], bv, acc[mt]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 af = AIN ? b.af[AIN ? i : 0][mt] : a_frag(A, mt, uu * 4 + g);
+        acc[mt] = mfma_16x16x32(af, bv, acc[mt]);
+      }
     }
   } else {
     // Every 4-byte word expands with two masks and an OR into four bf16 pairs
@@ -151,7 +246,7 @@ __device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U>& b, const
     // sum a_k (128 + q_k) - 136 sum a_k = sum a_k (q_k - 8).
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const float sc = (u + i < uhi) ? b.s[INT4 ? i : 0] : 0.f;  // wave-uniform mask
+      const float sc = fp16_to_f32(b.s[INT4 ? i : 0]);  // zero for a masked unit
       const int uu = min(u + i, ulast);
       f32x4 t[MT];
 #pragma unroll
@@ -166,12 +261,14 @@ __device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U>& b, const
         bb[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
         const bf16x8 bv = __builtin_bit_cast(bf16x8, bb);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          t[mt] = mfma_16x16x32(a_frag(ap, K8, min(mt, mtv - 1), uu * 16 + g * 4 + j), bv, t[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 af = AIN ? b.af[AIN ? (INT4 ? 4 * i + j : i) : 0][mt] : a_frag(A, mt, uu * 16 + g * 4 + j);
+          t[mt] = mfma_16x16x32(af, bv, t[mt]);
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 as = *(const f32x4*)(asp + ((size_t)min(mt, mtv - 1) * KG + uu) * 16);
+        const f32x4 as = AIN ? b.as[(AIN && INT4) ? i : 0][mt] : a_sums(A, mt, uu);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[mt][e] += sc * (t[mt][e] - 136.0f * as[e]);
       }
@@ -189,8 +286,9 @@ struct Top2 {
 template <int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, int rows,
                                          const float* outv, Top2& t2) {
-  // outv[row * 17 + c]: operand column c of output row m_base + row
-  const int tid = threadIdx.x, nthr = a.nw * 64;
+  // outv[row * 17 + c]: operand column c of output row m_base + row; run by
+  // the workgroup's epilogue wave
+  const int tid = threadIdx.x & 63, nthr = 64;
   if (EPI == EPI_STORE) {
     for (int idx = tid; idx < rows * 16; idx += nthr) {
       const int ml = idx >> 4, c = idx & 15;
@@ -289,50 +387,155 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, in
 
 // ---------------------------------------------------------------- GEMM kernel
 
-template <int MT, bool INT4, int EPI>
-__global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
+// Workgroup b takes K slice b % ksplit and the column tiles b / ksplit,
+// b / ksplit + gridDim.x / ksplit, ...; its nw loading waves split the slice
+// and one more wave runs the epilogues.  A loading wave's stages run through
+// its tiles in order, ring_depth - 1 of them in flight while one is
+// multiplied; it never stores to global memory, so the compiler can count its
+// loads in flight exactly and never has to drain the ring.
+template <int MT, bool INT4, int EPI, int MODE>
+__global__ __launch_bounds__(576) __attribute__((amdgpu_waves_per_eu(1, 3)))
+void k_gemm(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int U = INT4 ? (MT <= 2 ? 4 : 2) : (MT <= 2 ? 8 : 4);
+  constexpr bool ALDS = MODE == kModeLds;
+  constexpr bool AIN = a_in_stage<INT4, MODE>();
+  constexpr int U = stage_units<INT4, MT, MODE>();
+  constexpr int D = ring_depth<INT4, MT, MODE>();
+  constexpr int CPU = unit_chunks<INT4>();
+  constexpr int CB = copy_batch(MT);
   // the wave index is made provably uniform: segment bounds live in scalar
   // registers and every branch on them is a scalar branch
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int nw = a.nw;
+  const int nw = a.nw, nthr = nw * 64;
   const int K8 = a.K >> 3, KG = a.K >> 7;
   const int units = INT4 ? (a.K >> 7) : (a.K >> 5);
-  const int ks_units = units / a.ksplit;  // K slice length (ksplit divides units)
-  const int w0 = ks_units * wave / nw, w1 = ks_units * (wave + 1) / nw;  // within a slice
-  const int nb = ((ks_units + nw - 1) / nw + U - 1) / U;  // same stage count for every wave
-  const int n_items = a.n_tiles * a.ksplit;
-  const int n_my = (n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int ks = (int)blockIdx.x % a.ksplit;
+  const int tb = (int)blockIdx.x / a.ksplit, gt = (int)gridDim.x / a.ksplit;
+  const int s_lo = units * ks / a.ksplit, s_hi = units * (ks + 1) / a.ksplit;
+  const int s_len = s_hi - s_lo;
+  const int nb = ((s_len + nw - 1) / nw + U - 1) / U;  // same stage count for every wave
+  const int n_my = (a.n_tiles - tb + gt - 1) / gt;
   const int total = n_my * nb;
+  if (total <= 0) return;  // uniform over the workgroup
   const int rows = min(min(kRowsPerLaunch, a.M - a.m_base), MT * 8);
   const int mtv = (rows + 7) >> 3;
 
   f32x4* red = (f32x4*)smem;                                    // [nw][MT][64]
   float* outv = (float*)(smem + (size_t)nw * MT * 64 * 16);     // [MT*8][17]
+  uint16_t* lds_a = (uint16_t*)(smem + gemm_red_bytes(nw, MT)); // [MT][s_len*CPU][16][8]
+  float* lds_s = (float*)(lds_a + (size_t)MT * s_len * CPU * 128);  // [MT][s_len][16]
 
-  const uint16_t* ap = a.apack + (size_t)(a.m_base >> 3) * K8 * 128 + (lane & 15) * 8;
-  const float* asp = a.asum ? a.asum + (size_t)(a.m_base >> 3) * KG * 16 + 4 * (lane >> 4) : nullptr;
+  if (wave == nw) {
+    // the epilogue wave: the same barriers as the loading waves (the LDS
+    // copy, then two per work item), an epilogue after each item
+    if (ALDS) __syncthreads();
+    Top2 t2 = {-INFINITY, -INFINITY, 0x7FFFFFFF};
+    for (int it = 0; it < n_my; ++it) {
+      __syncthreads();
+      __syncthreads();
+      epilogue<EPI>(a, tb + it * gt, ks, rows, outv, t2);
+    }
+    if (EPI == EPI_ARGMAX && lane < rows) {
+      float* o = a.amax + ((size_t)(a.m_base + lane) * a.n_parts + blockIdx.x) * 3;
+      o[0] = t2.v1;
+      o[1] = __int_as_float(t2.i1);
+      o[2] = t2.v2;
+    }
+    return;
+  }
 
-  auto item_of = [&](int bi) { return (int)blockIdx.x + (bi / nb) * (int)gridDim.x; };
-  auto u_of = [&](int bi, int ks) { return ks * ks_units + w0 + (bi % nb) * U; };
+  const int ulo = s_lo + s_len * wave / nw, uhi = s_lo + s_len * (wave + 1) / nw;
 
-  Stage<INT4, MT, U> s0, s1;
-  WPtr p0, p1;
-  int it0 = 0, it1 = 0;
-  if (total > 0) {
-    it0 = item_of(0);
-    p0 = wptr<INT4, EPI>(a, it0 / a.ksplit);
-    const int ks = it0 % a.ksplit;
-    load_stage<INT4, MT, U>(s0, p0, ap, K8, u_of(0, ks), ks * ks_units + w0, ks * ks_units + w1, mtv);
+  // activations in global memory (for the stage loads) and where the multiply
+  // reads them when they are not in the stage
+  ASrc G;
+  G.p = a.apack + (size_t)(a.m_base >> 3) * K8 * 128 + (lane & 15) * 8;
+  G.s = a.asum ? a.asum + (size_t)(a.m_base >> 3) * KG * 16 + 4 * (lane >> 4) : nullptr;
+  G.tstride = K8 * 128;
+  G.sts = KG * 16;
+  G.c0 = 0;
+  G.u0 = 0;
+  G.mtv = mtv;
+  ASrc A = G;
+  if (ALDS) {
+    A.p = lds_a + (lane & 15) * 8;
+    A.s = lds_s + 4 * (lane >> 4);
+    A.tstride = s_len * CPU * 128;
+    A.sts = s_len * 16;
+    A.c0 = s_lo * CPU;
+    A.u0 = s_lo;
+  }
+
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(INT4 ? (const void*)a.wscale : a.w, INT4 ? a.s_bytes : 0u);
+
+  // lds mode: copy this slice of the packed rows (and INT4 group sums) in one
+  // batch of unconditional loads, issued before the weights so that storing
+  // them waits for nothing else (the host guarantees the batch suffices)
+  const int n16 = s_len * CPU * 16;  // 16-byte pieces per row tile
+  u32x4 cbuf[ALDS ? CB : 1];
+  float sbuf[ALDS && INT4 ? kCopySums : 1];
+  if (ALDS) {
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(a.apack + (size_t)(a.m_base >> 3) * K8 * 128, (uint32_t)mtv * K8 * 256);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int p = i * nthr + (int)threadIdx.x;
+      const int mt = p / n16, q = p - mt * n16;
+      const uint32_t off = ((uint32_t)min(mt, mtv - 1) * K8 + (uint32_t)s_lo * CPU) * 256 + (uint32_t)q * 16;
+      cbuf[i] = bload16<0>(ra, p < MT * n16 ? off : kOOB);
+    }
+    if (INT4) {
+      const __amdgpu_buffer_rsrc_t rg =
+          make_rsrc(a.asum + (size_t)(a.m_base >> 3) * KG * 16, (uint32_t)mtv * KG * 64);
+      const int ns = s_len * 16;
+#pragma unroll
+      for (int i = 0; i < (ALDS && INT4 ? kCopySums : 1); ++i) {
+        const int p = i * nthr + (int)threadIdx.x;
+        const int mt = p / ns, q = p - mt * ns;
+        const uint32_t off = (((uint32_t)min(mt, mtv - 1) * KG + s_lo) * 16 + q) * 4;
+        sbuf[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, p < MT * ns ? off : kOOB, 0, 0));
+      }
+    }
+  }
+
+  auto tile_of = [&](int bi) { return tb + (bi / nb) * gt; };
+  // stage bi's first unit; past the end it is uhi, so every unit is masked
+  auto u_of = [&](int bi) { return bi < total ? ulo + (bi % nb) * U : uhi; };
+  Stage<INT4, MT, U, AIN> st[D];
+  auto issue = [&](int bi, Stage<INT4, MT, U, AIN>& s) {
+    const WPtr wp = wptr<INT4, EPI>(a, tile_of(min(bi, total - 1)));
+    load_stage<INT4, MT, U, AIN>(s, wp, rw, rs, G, u_of(bi), ulo, uhi);
+  };
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, st[j]);
+  // every load of a stage goes out before the multiplies (with four row tiles
+  // the registers do not allow it; the compiler interleaves instead)
+  if (MT <= 2) __builtin_amdgcn_sched_barrier(0);
+
+  if (ALDS) {
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int p = i * nthr + (int)threadIdx.x;
+      if (p < MT * n16) *(u32x4*)(lds_a + (size_t)p * 8) = cbuf[i];
+    }
+    if (INT4) {
+#pragma unroll
+      for (int i = 0; i < (ALDS && INT4 ? kCopySums : 1); ++i) {
+        const int p = i * nthr + (int)threadIdx.x;
+        if (p < MT * s_len * 16) lds_s[p] = sbuf[i];
+      }
+    }
+    __syncthreads();
   }
 
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  Top2 t2 = {-INFINITY, -INFINITY, 0x7FFFFFFF};
 
-  auto finish_item = [&](int item) {
+  // a work item's partial sums: through LDS to one output tile (outv), which
+  // the epilogue wave takes after the second barrier
+  auto finish_item = [&]() {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       red[((size_t)wave * MT + mt) * 64 + lane] = acc[mt];
@@ -340,7 +543,7 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
     }
     __syncthreads();
     // real row r of tile mt = operand row r (hi) + operand row r + 8 (lo)
-    for (int idx = threadIdx.x; idx < MT * 128; idx += nw * 64) {
+    for (int idx = threadIdx.x; idx < MT * 128; idx += nthr) {
       const int mt = idx >> 7, r = (idx >> 4) & 7, c = idx & 15;
       const int lh = (r >> 2) * 16 + c, ll = ((r + 8) >> 2) * 16 + c, e = r & 3;
       float v = 0.f;
@@ -349,42 +552,22 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
       outv[(mt * 8 + r) * 17 + c] = v;
     }
     __syncthreads();
-    epilogue<EPI>(a, item / a.ksplit, item % a.ksplit, rows, outv, t2);
   };
 
-  for (int bi = 0; bi < total;) {
-    if (bi + 1 < total) {
-      const int it = item_of(bi + 1);
-      p1 = (it != it0) ? wptr<INT4, EPI>(a, it / a.ksplit) : p0;
-      it1 = it;
-      const int ks = it % a.ksplit;
-      load_stage<INT4, MT, U>(s1, p1, ap, K8, u_of(bi + 1, ks), ks * ks_units + w0, ks * ks_units + w1, mtv);
+  // the ring: stage bi is multiplied while stages bi+1 .. bi+D-1 are in
+  // flight; past the last stage the loop is left at once (the loads issued
+  // for stages past the end are masked and read nothing)
+  for (int bi0 = 0;; bi0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int bi = bi0 + j;
+      if (D > 1) issue(bi + D - 1, st[(j + D - 1) % D]);
+      else issue(bi, st[0]);
+      if (MT <= 2) __builtin_amdgcn_sched_barrier(0);
+      compute_stage<MT, INT4, U, AIN>(st[j], A, u_of(bi), ulo, uhi, acc);
+      if (bi % nb == nb - 1) finish_item();
+      if (bi + 1 >= total) return;  // uniform
     }
-    {
-      const int ks = it0 % a.ksplit;
-      compute_stage<MT, INT4, U>(s0, ap, asp, K8, KG, u_of(bi, ks), ks * ks_units + w0, ks * ks_units + w1, mtv, acc);
-    }
-    if (bi % nb == nb - 1) finish_item(it0);
-    if (++bi >= total) break;
-    if (bi + 1 < total) {
-      const int it = item_of(bi + 1);
-      p0 = (it != it1) ? wptr<INT4, EPI>(a, it / a.ksplit) : p1;
-      it0 = it;
-      const int ks = it % a.ksplit;
-      load_stage<INT4, MT, U>(s0, p0, ap, K8, u_of(bi + 1, ks), ks * ks_units + w0, ks * ks_units + w1, mtv);
-    }
-    {
-      const int ks = it1 % a.ksplit;
-      compute_stage<MT, INT4, U>(s1, ap, asp, K8, KG, u_of(bi, ks), ks * ks_units + w0, ks * ks_units + w1, mtv, acc);
-    }
-    if (bi % nb == nb - 1) finish_item(it1);
-    ++bi;
-  }
-  if (EPI == EPI_ARGMAX && (int)threadIdx.x < rows) {
-    float* o = a.amax + ((size_t)(a.m_base + threadIdx.x) * a.n_parts + blockIdx.x) * 3;
-    o[0] = t2.v1;
-    o[1] = __int_as_float(t2.i1);
-    o[2] = t2.v2;
   }
 }
 
@@ -587,58 +770,115 @@ static int cu_count() {
   return n;
 }
 
-static size_t gemm_smem(int nw, int mt) {
-  return (size_t)nw * mt * 64 * 16 + (size_t)mt * 8 * 17 * 4;
+// LDS of the activation slice (and INT4 group sums) of a K slice of `len` units.
+static size_t gemm_alds_bytes(int mt, int len, bool int4) {
+  return (size_t)mt * len * (int4 ? 16 : 4) * 256 + (int4 ? (size_t)mt * len * 64 : 0);
+}
+
+constexpr size_t kLdsBudget = 160 * 1024;
+
+// The lds mode holds one or two row tiles, and its copy is one batch: at most
+// copy_batch pieces (and kCopySums group sums) per thread.
+static bool alds_fits(int mt, int len, bool int4, int nw) {
+  const long pieces = (long)mt * len * (int4 ? 16 : 4) * 16;
+  const long sums = int4 ? (long)mt * len * 16 : 0;
+  return mt <= 2 && gemm_red_bytes(nw, mt) + gemm_alds_bytes(mt, len, int4) <= kLdsBudget &&
+         pieces <= (long)copy_batch(mt) * nw * 64 && sums <= (long)kCopySums * nw * 64;
+}
+
+static int mode_units(bool int4, int mt, int mode) {
+  if (int4) return stage_units<true, 1, kModeSingle>();
+  if (mode != kModeRing) return stage_units<false, 1, kModeSingle>();
+  return mt == 4 ? stage_units<false, 4, kModeRing>()
+                 : mt == 2 ? stage_units<false, 2, kModeRing>() : stage_units<false, 1, kModeRing>();
+}
+
+// Mode, waves and shared memory of one launch with `mt` row tiles, given the
+// column tiles, K slices and tiles per workgroup.
+static void plan_launch(GemmPlan& p, int mt, int units, bool int4, int per) {
+  p.mt = mt;
+  const int len = (units + p.ksplit - 1) / p.ksplit;
+  const int us = mode_units(int4, mt, kModeSingle);
+  if (per == 1 && len <= 8 * us) {
+    // one stage per wave: as many waves as the slice needs
+    p.mode = kModeSingle;
+    p.nw = (len + us - 1) / us;
+  } else {
+    p.nw = 8;
+    p.mode = alds_fits(mt, len, int4, p.nw) ? kModeLds : kModeRing;
+  }
+  p.smem = gemm_red_bytes(p.nw, mt) + (p.mode == kModeLds ? gemm_alds_bytes(mt, len, int4) : 0);
 }
 
 GemmPlan plan_gemm(int M, int N, int K, bool int4, int epi, bool allow_split) {
   GemmPlan p;
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
   const int rows = M < kRowsPerLaunch ? M : kRowsPerLaunch;
-  const int mt = (rows + 7) / 8;
-  p.mt = mt <= 1 ? 1 : mt <= 2 ? 2 : 4;
+  const int mt8 = (rows + 7) / 8;
+  const int mt = mt8 <= 1 ? 1 : mt8 <= 2 ? 2 : 4;
   p.launches = (M + kRowsPerLaunch - 1) / kRowsPerLaunch;
-  p.nw = 8;
   const int units = int4 ? K / 128 : K / 32;
   const int cus = cu_count();
-  // K slices so that narrow GEMMs still cover every compute unit; a slice keeps
-  // at least 4 units per wave and the slices divide K evenly
+  // K slices (partial sums for the next kernel, EPI_STORE only) so that narrow
+  // GEMMs still cover every compute unit and, for one or two row tiles, the
+  // activation slice fits in LDS; every wave keeps at least one unit
   p.ksplit = 1;
   if (allow_split && epi == EPI_STORE) {
-    while (p.n_tiles * p.ksplit < cus && units % (p.ksplit * 2) == 0 &&
-           units / (p.ksplit * 2) >= 4 * p.nw)
+    while (p.ksplit < 16 &&
+           (p.n_tiles * p.ksplit < cus ||
+            (mt <= 2 && !alds_fits(mt, (units + p.ksplit - 1) / p.ksplit, int4, 8))) &&
+           units / (p.ksplit * 2) >= 8)
       p.ksplit *= 2;
   }
-  // one 8-wave workgroup per compute unit; the items are dealt out evenly
-  const int items = p.n_tiles * p.ksplit;
-  const int per = (items + cus - 1) / cus;
-  p.grid = (items + per - 1) / per;
-  p.smem = gemm_smem(p.nw, p.mt);
+  // workgroups per slice: the slice's tiles dealt out evenly over cus/ksplit
+  const int per_slice = cus / p.ksplit > 0 ? cus / p.ksplit : 1;
+  p.per = (p.n_tiles + per_slice - 1) / per_slice;
+  const int gt = (p.n_tiles + p.per - 1) / p.per;
+  p.grid = gt * p.ksplit;
+  plan_launch(p, mt, units, int4, p.per);
   return p;
 }
 
-template <int MT, bool INT4, int EPI>
+template <int MT, bool INT4, int EPI, int MODE>
 static hipError_t launch_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<MT, INT4, EPI>), dim3(p.grid), dim3(p.nw * 64), p.smem, s, a);
+  static bool attr = false;  // allow the full LDS once per instantiation
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<MT, INT4, EPI, MODE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_gemm<MT, INT4, EPI, MODE>), dim3(p.grid), dim3(p.nw * 64 + 64), p.smem, s, a);
   return hipGetLastError();
 }
 
-template <int MT, bool INT4>
-static hipError_t launch_gemm_mt(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s) {
+template <int MT, bool INT4, int MODE>
+static hipError_t launch_gemm_epi(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_one<MT, INT4, EPI_STORE>(a, p, s);
-    case EPI_SILU: return launch_one<MT, INT4, EPI_SILU>(a, p, s);
-    case EPI_QKV: return launch_one<MT, INT4, EPI_QKV>(a, p, s);
-    default: return launch_one<MT, INT4, EPI_ARGMAX>(a, p, s);
+    case EPI_STORE: return launch_one<MT, INT4, EPI_STORE, MODE>(a, p, s);
+    case EPI_SILU: return launch_one<MT, INT4, EPI_SILU, MODE>(a, p, s);
+    case EPI_QKV: return launch_one<MT, INT4, EPI_QKV, MODE>(a, p, s);
+    default: return launch_one<MT, INT4, EPI_ARGMAX, MODE>(a, p, s);
   }
 }
 
 template <bool INT4>
 static hipError_t launch_gemm_fmt(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s) {
+  if (p.mode == kModeLds) {
+    if (p.mt == 1) return launch_gemm_epi<1, INT4, kModeLds>(a, epi, p, s);
+    return launch_gemm_epi<2, INT4, kModeLds>(a, epi, p, s);
+  }
+  if (p.mode == kModeSingle) {
+    switch (p.mt) {
+      case 1: return launch_gemm_epi<1, INT4, kModeSingle>(a, epi, p, s);
+      case 2: return launch_gemm_epi<2, INT4, kModeSingle>(a, epi, p, s);
+      default: return launch_gemm_epi<4, INT4, kModeSingle>(a, epi, p, s);
+    }
+  }
   switch (p.mt) {
-    case 1: return launch_gemm_mt<1, INT4>(a, epi, p, s);
-    case 2: return launch_gemm_mt<2, INT4>(a, epi, p, s);
-    default: return launch_gemm_mt<4, INT4>(a, epi, p, s);
+    case 1: return launch_gemm_epi<1, INT4, kModeRing>(a, epi, p, s);
+    case 2: return launch_gemm_epi<2, INT4, kModeRing>(a, epi, p, s);
+    default: return launch_gemm_epi<4, INT4, kModeRing>(a, epi, p, s);
   }
 }
 
@@ -646,15 +886,16 @@ hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s) {
   const GemmPlan p = plan_gemm(a.M, a.N, a.K, int4, epi, a.partial != nullptr);
   a.n_tiles = p.n_tiles;
   a.ksplit = p.ksplit;
-  a.nw = p.nw;
   a.n_parts = p.grid;
+  const int units = int4 ? a.K / 128 : a.K / 32;
   for (int l = 0; l < p.launches; ++l) {
     a.m_base = l * kRowsPerLaunch;
     const int rows = (a.M - a.m_base) < kRowsPerLaunch ? (a.M - a.m_base) : kRowsPerLaunch;
+    // the last launch may hold fewer rows: fewer row tiles, perhaps another mode
     const int mt8 = (rows + 7) / 8;
     GemmPlan pl = p;
-    pl.mt = mt8 <= 1 ? 1 : mt8 <= 2 ? 2 : 4;
-    pl.smem = gemm_smem(pl.nw, pl.mt);
+    plan_launch(pl, mt8 <= 1 ? 1 : mt8 <= 2 ? 2 : 4, units, int4, p.per);
+    a.nw = pl.nw;
     hipError_t e = int4 ? launch_gemm_fmt<true>(a, epi, pl, s) : launch_gemm_fmt<false>(a, epi, pl, s);
     if (e != hipSuccess) return e;
   }

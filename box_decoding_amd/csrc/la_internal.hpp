@@ -10,22 +10,19 @@ enum GemmEpi { EPI_STORE = 0, EPI_SILU = 1, EPI_QKV = 2, EPI_ARGMAX = 3 };
 
 // Arguments of one small-M GEMM launch (rows m_base .. m_base+31 at most).
 struct GemmArgs {
-  // Activation source: either fp32 rows x (packed in LDS by the workgroup,
-  // with the RMSNorm when gain != NULL) or pre-packed rows in global memory.
-  const float* x;            // fp32 [M][ldx] (LDS packing mode)
-  int ldx;
-  const uint16_t* gain;      // RMSNorm gain (nullable)
-  float eps;
-  const uint16_t* apack;     // packed activations of all M rows (global mode)
+  const uint16_t* apack;     // packed activations of all M rows
   const float* asum;         // INT4 only: [MT][K/128][16] per-group sums of the packed rows
   const void* w;             // weight data
   const uint16_t* wscale;    // INT4 scales
+  uint32_t w_bytes;          // size of the weight data (buffer range)
+  uint32_t s_bytes;          // size of the INT4 scales
   int layout;                // LA_LAYOUT_* of w
   int M;                     // total rows of the problem
   int m_base;                // first row handled by this launch (multiple of 32)
   int N, K;                  // weight rows / reduction length
   int n_tiles;               // column tiles (16 operand columns each)
-  int ksplit;                // K slices per tile (> 1: partial sums go to `partial`)
+  int ksplit;                // K slices per tile (> 1: partial sums go to `partial`);
+                             // slice s covers units [units*s/ksplit, units*(s+1)/ksplit)
   int nw;                    // waves per workgroup (they split a work item's K range)
   float* partial;            // [ksplit][M][N] partial sums when ksplit > 1
   // epilogue
@@ -106,6 +103,8 @@ struct GemmPlan {
   int mt;        // row tiles per launch (1, 2 or 4)
   int launches;  // ceil(M / 32)
   int grid;      // workgroups per launch
+  int per;       // column tiles per workgroup (at most)
+  int mode;      // kernel mode (single stage, 2-deep ring, LDS-staged ring)
   size_t smem;   // dynamic LDS bytes
 };
 
