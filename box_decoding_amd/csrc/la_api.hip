@@ -87,6 +87,8 @@ struct StepWs {
   float* o;
   float* mlp;
   uint16_t* apack;    // packed operand with K <= max(hidden, heads * head_dim)
+  uint16_t* apack_o;  // packed attention output (K = heads * head_dim), bf16 path
+  float* ss;          // [T][hidden / 16] per-tile sums of squares of h, bf16 path
   float* asum;
   uint16_t* apack_m;  // packed MLP activations (K = inter)
   float* asum_m;
@@ -111,6 +113,8 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
   s.o = c.take<float>((size_t)T * HQ);
   s.mlp = c.take<float>((size_t)T * F);
   s.apack = c.take<uint16_t>(apack_elems(T, Kx));
+  s.apack_o = c.take<uint16_t>(apack_elems(T, HQ));
+  s.ss = c.take<float>((size_t)T * (H / 16));
   s.asum = c.take<float>((size_t)((T + 7) / 8) * (Kx / 128) * 16);
   s.apack_m = c.take<uint16_t>(apack_elems(T, F));
   s.asum_m = c.take<float>((size_t)((T + 7) / 8) * (F / 128) * 16);
@@ -246,12 +250,23 @@ la_status gemm_from_rows(GemmArgs g, const float* x, int ldx, const uint16_t* ga
   return LA_OK;
 }
 
-// One decoder layer on the rows in s.h.  `pending` partial sums of the previous
-// projection (in s.parts) are added to h by the first packing; on return
-// *pending holds the number of partial sums the down projection left.
+// What the previous kernel left for the next layer's input: `pending` K-slice
+// partial sums still to be added to h (INT4 path), or `packed`: the operand of
+// h * in_norm is in s.apack and the per-tile sums of squares of h in s.ss, so
+// the QKV projection applies 1/rms itself (bf16 path).
+struct Carry {
+  int pending = 0;
+  bool packed = false;
+};
+
+// One decoder layer on the rows in s.h.  bf16 weights: the O projection (and
+// the down projection when it is not K-sliced) adds the residual, keeps h,
+// packs h * gain for the next GEMM and leaves per-tile sums of squares; the
+// next GEMM scales its outputs by 1/rms, so no normalisation kernel runs.  `next_gain` is the RMSNorm gain after this
+// layer (the next layer's input norm or the final norm; NULL: h only).
 la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
-                    int B, int W, int max_len, const StepWs& s, float* attn_out, int* pending,
-                    hipStream_t st) {
+                    int B, int W, int max_len, const StepWs& s, float* attn_out, Carry* carry,
+                    const uint16_t* next_gain, hipStream_t st) {
   const la_layer& L = m->layers[l];
   const int T = B * W;
   const int H = m->hidden, HQ = m->n_heads * m->head_dim;
@@ -259,15 +274,26 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   const size_t le = kv_layer_elems(kv, m);
   la_status rs;
 
-  // h += pending partial sums; RMSNorm; pack
-  if ((rs = pack_rows(s.h, H, T, H, L.in_norm, m->rms_eps, s.apack, s.asum, int4, s.parts, *pending,
-                      *pending ? s.h : nullptr, st)) != LA_OK)
-    return rs;
+  // input operand: h (+ pending partial sums), RMSNorm, pack, unless the
+  // previous projection already packed it
+  const bool in_packed = carry->packed;
+  if (!in_packed) {
+    if ((rs = pack_rows(s.h, H, T, H, L.in_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+                        carry->pending, carry->pending ? s.h : nullptr, st)) != LA_OK)
+      return rs;
+  }
+  carry->pending = 0;
+  carry->packed = false;
 
   // QKV + bias + RoPE + K/V write
   GemmArgs g = base_gemm(&L.qkv, T);
   g.apack = s.apack;
   g.asum = s.asum;
+  if (in_packed) {
+    g.ss_in = s.ss;
+    g.ss_tiles = H / 16;
+    g.eps = m->rms_eps;
+  }
   g.bias = L.qkv_bias;
   g.y = s.q;
   g.ldy = HQ;
@@ -305,7 +331,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   at.part_ml = s.part_ml;
   at.nqp = s.nqp;
   at.out = (int4 || attn_out) ? (attn_out ? attn_out : s.o) : nullptr;
-  at.out_apack = int4 ? nullptr : s.apack;
+  at.out_apack = int4 ? nullptr : s.apack_o;
   at.out_int4 = false;
   LA_TRY(launch_attention(at, st));
   if (int4)
@@ -313,7 +339,52 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
                         st)) != LA_OK)
       return rs;
 
-  // O projection: K-slice partial sums (or h += directly)
+  const int F = m->inter;
+  if (!int4) {
+    // O projection: h += attn . Wo^T, h * post_norm packed for gate/up
+    g = base_gemm(&L.o, T);
+    g.apack = s.apack_o;
+    g.residual = s.h;
+    g.y = s.h;
+    g.ldy = H;
+    g.y_apack = s.apack;
+    g.out_gain = L.post_norm;
+    g.ss_out = s.ss;
+    LA_TRY(launch_gemm(g, EPI_STORE, false, st));
+    // gate/up + 1/rms + SiLU, packed straight into the down operand
+    g = base_gemm(&L.gate_up, T);
+    g.apack = s.apack;
+    g.ss_in = s.ss;
+    g.ss_tiles = H / 16;
+    g.eps = m->rms_eps;
+    g.y_apack = s.apack_m;
+    LA_TRY(launch_gemm(g, EPI_SILU, false, st));
+    // down projection: K-slice partial sums when its plan splits K (a sliced
+    // stream over every compute unit beats an unsplit one; the next input
+    // packing adds them up), else h += directly with h * next_gain packed for
+    // the next GEMM
+    const int ks_d = gemm_ksplit(T, &L.down);
+    g = base_gemm(&L.down, T);
+    g.apack = s.apack_m;
+    if (ks_d > 1) {
+      g.partial = s.parts;
+      carry->pending = ks_d;
+    } else {
+      g.residual = s.h;
+      g.y = s.h;
+      g.ldy = H;
+      if (next_gain) {
+        g.y_apack = s.apack;
+        g.out_gain = next_gain;
+        g.ss_out = s.ss;
+        carry->packed = true;
+      }
+    }
+    LA_TRY(launch_gemm(g, EPI_STORE, false, st));
+    return LA_OK;
+  }
+
+  // INT4: O projection as K-slice partial sums (or h += directly)
   const int ks_o = gemm_ksplit(T, &L.o);
   g = base_gemm(&L.o, T);
   g.apack = s.apack;
@@ -325,28 +396,21 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.y = s.h;
     g.ldy = H;
   }
-  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
+  LA_TRY(launch_gemm(g, EPI_STORE, true, st));
 
-  // h += O partial sums; RMSNorm; gate/up + SiLU (bf16: packed straight into
-  // the down operand)
-  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+  // h += O partial sums; RMSNorm; gate/up + SiLU
+  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, true, s.parts,
                       ks_o > 1 ? ks_o : 0, ks_o > 1 ? s.h : nullptr, st)) != LA_OK)
     return rs;
-  const int F = m->inter;
   g = base_gemm(&L.gate_up, T);
   g.apack = s.apack;
   g.asum = s.asum;
-  if (int4) {
-    g.y = s.mlp;
-    g.ldy = F;
-  } else {
-    g.y_apack = s.apack_m;
-  }
-  LA_TRY(launch_gemm(g, EPI_SILU, int4, st));
-  if (int4)
-    if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true, nullptr, 0, nullptr,
-                        st)) != LA_OK)
-      return rs;
+  g.y = s.mlp;
+  g.ldy = F;
+  LA_TRY(launch_gemm(g, EPI_SILU, true, st));
+  if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true, nullptr, 0, nullptr,
+                      st)) != LA_OK)
+    return rs;
 
   // down projection: K-slice partial sums left for the next packing
   const int ks_d = gemm_ksplit(T, &L.down);
@@ -360,8 +424,8 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.y = s.h;
     g.ldy = H;
   }
-  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
-  *pending = ks_d > 1 ? ks_d : 0;
+  LA_TRY(launch_gemm(g, EPI_STORE, true, st));
+  carry->pending = ks_d > 1 ? ks_d : 0;
   return LA_OK;
 }
 
@@ -565,11 +629,13 @@ la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, 
   if (y != x) LA_TRY(hipMemcpyAsync(y, x, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice, stream));
   PrologueArgs p = base_prologue(m, kv, prefix_len, B, W, max_len, s);
   LA_TRY(launch_prologue(p, stream));
-  int pending = 0;
-  if ((st = run_layer(m, layer, kv, prefix_len, B, W, max_len, s, attn_out, &pending, stream)) != LA_OK)
+  Carry carry;
+  if ((st = run_layer(m, layer, kv, prefix_len, B, W, max_len, s, attn_out, &carry, nullptr,
+                      stream)) != LA_OK)
     return st;
-  if (pending)
-    return pack_rows(y, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, pending, y, stream);
+  if (carry.pending)
+    return pack_rows(y, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, carry.pending, y,
+                     stream);
   return LA_OK;
 }
 
@@ -600,17 +666,23 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
   p.out = s.h;
   p.err = err;
   LA_TRY(launch_prologue(p, stream));
-  int pending = 0;
-  for (int l = 0; l < m->n_layers; ++l) {
-    st = run_layer(m, l, kv, prefix_len, B, W, max_len, s, nullptr, &pending, stream);
-    if (st != LA_OK) return st;
-  }
+  Carry carry;
   const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
   const bool int4 = lm->fmt == LA_W_INT4;
-  // h += last partial sums (written back for out_hidden); final RMSNorm; pack
-  if ((st = pack_rows(s.h, H, T, H, m->final_norm, m->rms_eps, s.apack, s.asum, int4, s.parts, pending,
-                      pending ? s.h : nullptr, stream)) != LA_OK)
-    return st;
+  for (int l = 0; l < m->n_layers; ++l) {
+    // the gain after layer l: the next input norm, or the final norm when the
+    // lm_head takes the packed rows directly (bf16)
+    const uint16_t* next_gain = l + 1 < m->n_layers ? m->layers[l + 1].in_norm
+                                                    : (int4 ? nullptr : m->final_norm);
+    st = run_layer(m, l, kv, prefix_len, B, W, max_len, s, nullptr, &carry, next_gain, stream);
+    if (st != LA_OK) return st;
+  }
+  if (!carry.packed) {
+    // h += last partial sums (written back for out_hidden); final RMSNorm; pack
+    if ((st = pack_rows(s.h, H, T, H, m->final_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+                        carry.pending, carry.pending ? s.h : nullptr, stream)) != LA_OK)
+      return st;
+  }
   if (out_hidden)
     LA_TRY(hipMemcpyAsync(out_hidden, s.h, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice,
                           stream));
@@ -618,6 +690,11 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
   g.amax = s.amax;
   g.apack = s.apack;
   g.asum = s.asum;
+  if (carry.packed) {
+    g.ss_in = s.ss;
+    g.ss_tiles = H / 16;
+    g.eps = m->rms_eps;
+  }
   LA_TRY(launch_gemm(g, EPI_ARGMAX, int4, stream));
   return hip_status(launch_argmax_reduce(s.amax, T, s.vocab_parts, s.flags, out_ids, nullptr, out_gap,
                                          nullptr, stream));

@@ -139,22 +139,14 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int NQ = a.W * G;
   const bool direct = a.max_splits == 1;
-  const int n_keys = attn_keys(a, b);
   const int kps = a.pages_per_split * kBlock;
   const int k0 = split * kps;
   const int qi = qt * 16 + r;
-  if (k0 >= n_keys) {  // uniform over the workgroup
-    if (direct && qi < NQ && (g & 1) == 0) {
-      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int dt = 0; dt < 8; ++dt) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, z);
-    }
-    return;
-  }
-  const int k1 = min(n_keys, k0 + kps);
   const int first = k0 / kBlock;
-  const int npages = (k1 - k0 + kBlock - 1) / kBlock;  // 1 .. pages_per_split (<= 64)
-  int bt = a.block_table[(size_t)b * a.max_blocks + first + min(lane, npages - 1)];
-  bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
+  // the block ids of the run's pages (one per lane, clamped to the table) and
+  // the Q fragments are loaded together with the sequence length, not after it
+  int bt = a.block_table[(size_t)b * a.max_blocks +
+                         min(first + min(lane, a.pages_per_split - 1), a.max_blocks - 1)];
 
   // Q^T operand of this wave's tile: lane (g, r) holds dims kb*32 + 8g .. +8 of
   // query column qi as bf16 hi and lo (absent columns: zeros).
@@ -184,6 +176,17 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       ql[kb] = __builtin_bit_cast(bf16x8, L);
     }
   }
+  const int n_keys = attn_keys(a, b);
+  if (k0 >= n_keys) {  // uniform over the workgroup
+    if (direct && qi < NQ && (g & 1) == 0) {
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < 8; ++dt) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, z);
+    }
+    return;
+  }
+  const int k1 = min(n_keys, k0 + kps);
+  const int npages = (k1 - k0 + kBlock - 1) / kBlock;  // 1 .. pages_per_split (<= 64)
+  bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
 
   AttnState st;
   st.m = -INFINITY;
@@ -273,22 +276,23 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int j = lane >> 3;                              // run group
   const int c4 = (threadIdx.x >> 6) * 8 + (lane & 7);  // 4-dim chunk
-  const int n_keys = attn_keys(a, b);
   const int kps = a.pages_per_split * kBlock;
-  const int ns = (n_keys + kps - 1) / kps;
   const size_t base = ((size_t)b * a.Hkv + kvh) * a.max_splits;
   const float2* ml = (const float2*)a.part_ml;
   MergeAcc acc;
   acc.m = -INFINITY;
   acc.den = 0.f;
   acc.num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = j; s0 < ns; s0 += kMergeGroups * kMergeBatch) {
+  // slot addresses do not depend on the sequence length (it only masks), so
+  // the loads need not wait for it
+  const int ns = (attn_keys(a, b) + kps - 1) / kps;
+  for (int s0 = j; s0 < a.max_splits; s0 += kMergeGroups * kMergeBatch) {
     float2 m[kMergeBatch];
     float4 o[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const int s = s0 + i * kMergeGroups;
-      const size_t u = base + (s < ns ? s : 0);  // clamped to a slot inside the buffer
+      const size_t u = base + (s < a.max_splits ? s : 0);  // a slot inside the buffer
       m[i] = ml[u * a.nqp + qi];
       o[i] = *(const float4*)(a.part_o + (u * a.nqp + qi) * kHeadDim + 4 * c4);
     }
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   acc = merge_pair(acc, shfl_xor_acc(acc, 8));
   acc = merge_pair(acc, shfl_xor_acc(acc, 16));
   acc = merge_pair(acc, shfl_xor_acc(acc, 32));
-  const float inv = ns > 0 ? 1.f / acc.den : 0.f;
+  const float inv = acc.den > 0.f ? 1.f / acc.den : 0.f;
   float v[8];
   v[0] = acc.num.x * inv; v[1] = acc.num.y * inv; v[2] = acc.num.z * inv; v[3] = acc.num.w * inv;
 #pragma unroll

@@ -90,11 +90,13 @@ __host__ __device__ constexpr int unit_chunks() { return INT4 ? 16 : 4; }
 // Units per stage and stages in the ring.
 template <bool INT4, int MT, int MODE>
 __host__ __device__ constexpr int stage_units() {
-  return INT4 ? 2 : (MODE == kModeRing ? (MT == 4 ? 2 : MT == 2 ? 4 : 8) : 8);
+  return INT4 ? 2 : (MODE == kModeRing ? (MT == 4 ? 2 : 4) : 8);
 }
 template <bool INT4, int MT, int MODE>
 __host__ __device__ constexpr int ring_depth() {
-  return MODE == kModeSingle ? 1 : MODE == kModeRing ? 2 : (INT4 ? 8 : (MT == 1 ? 4 : 3));
+  return MODE == kModeSingle ? 1
+         : MODE == kModeRing ? ((MT == 1 && !INT4) ? 4 : 2)
+                             : (INT4 ? 8 : (MT == 1 ? 4 : 3));
 }
 // Activation fragments travel in the stage (else: LDS, or for INT4 in the
 // 2-deep ring, global loads at multiply time).
@@ -283,34 +285,159 @@ struct Top2 {
   int i1;
 };
 
+// The epilogue wave's operands, loaded before it waits for a work item: per
+// lane and iteration (idx = lane + 64 * it) two values, and per row (lane =
+// row) where its K/V goes.
+constexpr int kEpiIters = kRowsPerLaunch * 16 / 64;
+struct EpiPre {
+  float p0[kEpiIters], p1[kEpiIters], p2[kEpiIters];
+  float2 cs[kEpiIters];
+  float inv[kRowsPerLaunch / 8];  // 1/rms of rows 8 rb + (lane >> 3)
+  int blk;       // QKV: page of the row's cache position (-1: no write)
+  int slot;      // QKV: slot within the page
+};
+
+// Per-row cache location (QKV): row m writes position prefix_len[b] + j of
+// sequence b unless it is flagged or the position has no valid page.
+__device__ __forceinline__ void epi_rows(const GemmArgs& a, int rows, EpiPre& e) {
+  const int lane = threadIdx.x & 63;
+  e.blk = -1;
+  e.slot = 0;
+  if (lane >= rows) return;
+  const int m = a.m_base + lane;
+  const int b = m / a.W, j = m - b * a.W;
+  const int pos = a.prefix_len[b] + j;
+  const int f = a.flags ? a.flags[m] : 0;
+  if (f != 0 || pos < 0 || pos >= a.max_blocks * kBlock) return;
+  const int blk = a.block_table[(size_t)b * a.max_blocks + pos / kBlock];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  e.blk = blk;
+  e.slot = pos % kBlock;
+}
+
+// 1/rms of the launch's rows from the producer's per-tile sums of squares:
+// lane l sums tiles (l & 7), (l & 7) + 8, ... of row 8 rb + (l >> 3), then the
+// 8 lanes of a row combine in a fixed butterfly.
+__device__ __forceinline__ void epi_inv(const GemmArgs& a, int rows, EpiPre& e) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rb = 0; rb < kRowsPerLaunch / 8; ++rb) e.inv[rb] = 1.f;
+  if (!a.ss_in) return;
+#pragma unroll
+  for (int rb = 0; rb < kRowsPerLaunch / 8; ++rb) {
+    if (rb * 8 >= rows) break;  // uniform
+    const int row = min(rb * 8 + (lane >> 3), rows - 1);
+    const float* src = a.ss_in + (size_t)(a.m_base + row) * a.ss_tiles;
+    // 16 loads at a time, all in flight together (128 tiles: one batch)
+    float sum = 0.f;
+    for (int t0 = 0; t0 < a.ss_tiles; t0 += 128) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int t = t0 + (lane & 7) + 8 * k;
+        v[k] = src[min(t, a.ss_tiles - 1)];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (t0 + (lane & 7) + 8 * k < a.ss_tiles) sum += v[k];
+    }
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    e.inv[rb] = 1.0f / sqrtf(sum / (float)a.K + a.eps);
+  }
+}
+
+// 1/rms of row ml (any lane may ask for any row < 32).
+__device__ __forceinline__ float row_inv(const EpiPre& e, int ml) {
+  float iv = 1.f;
+#pragma unroll
+  for (int rb = 0; rb < kRowsPerLaunch / 8; ++rb) {
+    const float t = __shfl(e.inv[rb], (ml & 7) * 8);
+    if ((ml >> 3) == rb) iv = t;
+  }
+  return iv;
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile, int rows, EpiPre& e) {
+  const int lane = threadIdx.x & 63;
+  if (EPI == EPI_STORE) {
+    if (a.ksplit > 1) return;
+#pragma unroll
+    for (int it = 0; it < kEpiIters; ++it) {
+      const int idx = lane + it * 64;
+      const int ml = min(idx >> 4, rows - 1), c = idx & 15;
+      const int n = min(tile * 16 + c, a.N - 1);
+      e.p0[it] = a.residual ? a.residual[(size_t)(a.m_base + ml) * a.ldy + n] : 0.f;
+      e.p1[it] = a.bias ? bf16_to_f32(a.bias[n]) : 0.f;
+      e.p2[it] = a.out_gain ? bf16_to_f32(a.out_gain[n]) : 0.f;
+    }
+  } else if (EPI == EPI_QKV) {
+    const int head = tile >> 3, sub = tile & 7;
+#pragma unroll
+    for (int it = 0; it < kEpiIters / 2; ++it) {
+      const int idx = lane + it * 64;
+      const int ml = min(idx >> 3, rows - 1), c = idx & 7;
+      const int i = sub * 8 + c;
+      const int r1 = head * kHeadDim + i, r2 = r1 + 64;
+      e.cs[it] = a.rope[(size_t)(a.m_base + ml) * 64 + i];
+      e.p0[it] = a.bias ? bf16_to_f32(a.bias[r1]) : 0.f;
+      e.p1[it] = a.bias ? bf16_to_f32(a.bias[r2]) : 0.f;
+    }
+  }
+}
+
+// outv[row * 17 + c]: operand column c of output row m_base + row; run by the
+// workgroup's epilogue wave with the operands it prefetched.
 template <int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, int rows,
-                                         const float* outv, Top2& t2) {
-  // outv[row * 17 + c]: operand column c of output row m_base + row; run by
-  // the workgroup's epilogue wave
-  const int tid = threadIdx.x & 63, nthr = 64;
+                                         const float* outv, const EpiPre& e, Top2& t2) {
+  const int lane = threadIdx.x & 63;
   if (EPI == EPI_STORE) {
-    for (int idx = tid; idx < rows * 16; idx += nthr) {
+#pragma unroll
+    for (int it = 0; it < kEpiIters; ++it) {
+      const int idx = lane + it * 64;
       const int ml = idx >> 4, c = idx & 15;
       const int m = a.m_base + ml;
       const int n = tile * 16 + c;
-      if (n >= a.N) continue;
-      float v = outv[ml * 17 + c];
+      const bool ok = ml < rows && n < a.N;
+      float v = ok ? outv[ml * 17 + c] : 0.f;
       if (a.ksplit > 1) {
-        a.partial[((size_t)ks * a.M + m) * a.N + n] = v;
-      } else {
-        if (a.bias) v += bf16_to_f32(a.bias[n]);
-        if (a.residual) v += a.residual[(size_t)m * a.ldy + n];
-        a.y[(size_t)m * a.ldy + n] = v;
+        if (ok) a.partial[((size_t)ks * a.M + m) * a.N + n] = v;
+        continue;
+      }
+      v = v + e.p1[it] + e.p0[it];
+      if (ok) a.y[(size_t)m * a.ldy + n] = v;
+      if (a.ss_out) {
+        // this tile's share of the row's sum of squares (16 lanes, fixed order)
+        float q = ok ? v * v : 0.f;
+        q += __shfl_xor(q, 1);
+        q += __shfl_xor(q, 2);
+        q += __shfl_xor(q, 4);
+        q += __shfl_xor(q, 8);
+        if (ml < rows && c == 0) a.ss_out[(size_t)m * a.n_tiles + tile] = q;
+      }
+      if (a.y_apack && ok) {
+        // y * gain as bf16 hi/lo into the next GEMM's packed operand (K = N)
+        uint32_t h, l;
+        split_hi_lo(v * e.p2[it], h, l);
+        const size_t base = (((size_t)(m >> 3) * (a.N / 8) + (n >> 3)) * 16 + (m & 7)) * 8 + (n & 7);
+        a.y_apack[base] = (uint16_t)h;
+        a.y_apack[base + 64] = (uint16_t)l;
       }
     }
   } else if (EPI == EPI_SILU) {
     const int F = a.N / 2;
-    for (int idx = tid; idx < rows * 8; idx += nthr) {
+#pragma unroll
+    for (int it = 0; it < kEpiIters / 2; ++it) {
+      const int idx = lane + it * 64;
       const int ml = idx >> 3, c = idx & 7;
+      const float iv = row_inv(e, ml);
+      if (ml >= rows) continue;
       const int m = a.m_base + ml;
       const float* o = outv + ml * 17;
-      const float v = silu_f(o[c]) * o[c + 8];
+      const float v = silu_f(o[c] * iv) * (o[c + 8] * iv);
       const int n = tile * 8 + c;
       if (a.y) a.y[(size_t)m * a.ldy + n] = v;
       if (a.y_apack) {
@@ -325,19 +452,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, in
   } else if (EPI == EPI_QKV) {
     const int Hq = a.n_heads, Hkv = a.n_kv_heads;
     const int head = tile >> 3, sub = tile & 7;
-    for (int idx = tid; idx < rows * 8; idx += nthr) {
+#pragma unroll
+    for (int it = 0; it < kEpiIters / 2; ++it) {
+      const int idx = lane + it * 64;
       const int ml = idx >> 3, c = idx & 7;
+      // the row's cache location lives in lane ml
+      const int blk = __shfl(e.blk, ml & 63), slot = __shfl(e.slot, ml & 63);
+      const float iv = row_inv(e, ml);
+      if (ml >= rows) continue;
       const int m = a.m_base + ml;
       const int i = sub * 8 + c;  // rotary pair index
       const int r1 = head * kHeadDim + i, r2 = r1 + 64;
       const float* o = outv + ml * 17;
-      float x1 = o[c], x2 = o[c + 8];
-      if (a.bias) {
-        x1 += bf16_to_f32(a.bias[r1]);
-        x2 += bf16_to_f32(a.bias[r2]);
-      }
+      float x1 = o[c] * iv + e.p0[it], x2 = o[c + 8] * iv + e.p1[it];
       if (head < Hq + Hkv) {
-        const float2 cs = a.rope[(size_t)m * 64 + i];
+        const float2 cs = e.cs[it];
         const float y1 = x1 * cs.x - x2 * cs.y;
         const float y2 = x2 * cs.x + x1 * cs.y;
         x1 = y1;
@@ -348,13 +477,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, in
         a.y[(size_t)m * a.ldy + r2] = x2;
         continue;
       }
-      if (a.flags && a.flags[m] != 0) continue;
-      const int b = m / a.W, j = m - b * a.W;
-      const int pos = a.prefix_len[b] + j;
-      if (pos < 0 || pos >= a.max_blocks * kBlock) continue;
-      const int blk = a.block_table[(size_t)b * a.max_blocks + pos / kBlock];
-      if (blk < 0 || blk >= a.num_blocks) continue;
-      const int slot = pos % kBlock;
+      if (blk < 0) continue;
       if (head < Hq + Hkv) {
         const int kvh = head - Hq;
         uint16_t* kp = a.kc + (((size_t)blk * Hkv + kvh) * kBlock + slot) * kHeadDim;
@@ -368,11 +491,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, in
       }
     }
   } else {  // EPI_ARGMAX: running per-row top-2 over this workgroup's columns
-    if (tid < rows) {
+    if (lane < rows) {
       for (int c = 0; c < 16; ++c) {
         const int n = tile * 16 + c;
         if (n >= a.N) break;
-        const float v = outv[tid * 17 + c];
+        const float v = outv[lane * 17 + c];
         if (v > t2.v1) {
           t2.v2 = t2.v1;
           t2.v1 = v;
@@ -428,18 +551,26 @@ void k_gemm(GemmArgs a) {
   if (wave == nw) {
     // the epilogue wave: the same barriers as the loading waves (the LDS
     // copy, then two per work item), an epilogue after each item
+    EpiPre e;
+    if (EPI == EPI_QKV) epi_rows(a, rows, e);
+    if (EPI != EPI_STORE) epi_inv(a, rows, e);
     if (ALDS) __syncthreads();
     Top2 t2 = {-INFINITY, -INFINITY, 0x7FFFFFFF};
     for (int it = 0; it < n_my; ++it) {
+      epi_prefetch<EPI>(a, tb + it * gt, rows, e);  // in flight during the item
       __syncthreads();
       __syncthreads();
-      epilogue<EPI>(a, tb + it * gt, ks, rows, outv, t2);
+      epilogue<EPI>(a, tb + it * gt, ks, rows, outv, e, t2);
     }
-    if (EPI == EPI_ARGMAX && lane < rows) {
-      float* o = a.amax + ((size_t)(a.m_base + lane) * a.n_parts + blockIdx.x) * 3;
-      o[0] = t2.v1;
-      o[1] = __int_as_float(t2.i1);
-      o[2] = t2.v2;
+    if (EPI == EPI_ARGMAX) {
+      // the row scale is positive: it changes no ranking, only the values
+      const float iv = row_inv(e, lane);
+      if (lane < rows) {
+        float* o = a.amax + ((size_t)(a.m_base + lane) * a.n_parts + blockIdx.x) * 3;
+        o[0] = t2.v1 * iv;
+        o[1] = __int_as_float(t2.i1);
+        o[2] = t2.v2 * iv;
+      }
     }
     return;
   }
@@ -573,19 +704,24 @@ void k_gemm(GemmArgs a) {
 
 // ---------------------------------------------------------------- packing kernel
 
-// One workgroup per operand row: v = x + sum of partial sums (fixed order),
+// One workgroup per operand row: v = x + sum of NP partial sums (fixed order),
 // optionally written back, then RMSNorm (optional) and the bf16 hi/lo split into
-// the packed layout (plus per-group sums for INT4 consumers).
-__global__ __launch_bounds__(256) void k_pack(PackArgs a) {
-  __shared__ float red[4];
+// the packed layout (plus per-group sums for INT4 consumers).  A thread holds C
+// chunks of 8 values; every load of the row (x, partial sums, gain) is issued
+// before the first is used, so the kernel waits on memory once.
+template <int NP, int C>
+__global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
+  __shared__ float red[16];
   const int m = blockIdx.x;
   const int K8 = a.K >> 3;
   const int KG = a.K >> 7;
+  const int bd = blockDim.x;
   if (m >= a.M) {
+    // padding rows of the last tile: zero operand rows and group sums
     if (a.apack)
-      for (int kc = threadIdx.x; kc < K8; kc += 256) apack_store_zero_chunk(a.apack, a.K, m, kc);
+      for (int kc = threadIdx.x; kc < K8; kc += bd) apack_store_zero_chunk(a.apack, a.K, m, kc);
     if (a.int4 && a.asum) {
-      for (int gi = threadIdx.x; gi < KG; gi += 256) {
+      for (int gi = threadIdx.x; gi < KG; gi += bd) {
         float* as = a.asum + ((size_t)(m >> 3) * KG + gi) * 16;
         as[m & 7] = 0.f;
         as[(m & 7) + 8] = 0.f;
@@ -593,24 +729,39 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
     }
     return;
   }
-  // every thread keeps its chunks in registers: K <= 256 * 8 * 8
-  constexpr int MAXC = 8;
-  float v[MAXC][8];
+  float v[C][8];
+  uint4 gg[C];
   const float* x = a.x + (size_t)m * a.ldx;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int kc = min((int)threadIdx.x + j * bd, K8 - 1);  // clamped; masked below
+    float4 p[2 * NP + 2];
+    p[0] = *(const float4*)(x + kc * 8);
+    p[1] = *(const float4*)(x + kc * 8 + 4);
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+      const float* pp = a.parts + ((size_t)s * a.M + m) * a.K + kc * 8;
+      p[2 * s + 2] = *(const float4*)pp;
+      p[2 * s + 3] = *(const float4*)(pp + 4);
+    }
+    if (a.gain) gg[j] = *(const uint4*)(a.gain + kc * 8);
+    // x first, then the partial sums in order
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float4 t = p[h];
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        const float4 q = p[2 * s + 2 + h];
+        t.x += q.x; t.y += q.y; t.z += q.z; t.w += q.w;
+      }
+      v[j][4 * h + 0] = t.x; v[j][4 * h + 1] = t.y; v[j][4 * h + 2] = t.z; v[j][4 * h + 3] = t.w;
+    }
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    const int kc = threadIdx.x + j * 256;
+  for (int j = 0; j < C; ++j) {
+    const int kc = (int)threadIdx.x + j * bd;
     if (kc < K8) {
-      const float4 v0 = *(const float4*)(x + kc * 8), v1 = *(const float4*)(x + kc * 8 + 4);
-      v[j][0] = v0.x; v[j][1] = v0.y; v[j][2] = v0.z; v[j][3] = v0.w;
-      v[j][4] = v1.x; v[j][5] = v1.y; v[j][6] = v1.z; v[j][7] = v1.w;
-      for (int s = 0; s < a.n_parts; ++s) {
-        const float* pp = a.parts + ((size_t)s * a.M + m) * a.K + kc * 8;
-        const float4 p0 = *(const float4*)pp, p1 = *(const float4*)(pp + 4);
-        v[j][0] += p0.x; v[j][1] += p0.y; v[j][2] += p0.z; v[j][3] += p0.w;
-        v[j][4] += p1.x; v[j][5] += p1.y; v[j][6] += p1.z; v[j][7] += p1.w;
-      }
       if (a.h_out) {
         float* ho = a.h_out + (size_t)m * a.ldx + kc * 8;
         *(float4*)ho = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
@@ -629,17 +780,17 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
     ss = warp_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    ss = red[0] + red[1] + red[2] + red[3];
+    ss = 0.f;
+    for (int w = 0; w < (bd >> 6); ++w) ss += red[w];  // fixed order
     inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
   }
 #pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    const int kc = threadIdx.x + j * 256;
+  for (int j = 0; j < C; ++j) {
+    const int kc = (int)threadIdx.x + j * bd;
     float hs = 0.f, ls = 0.f;
     if (kc < K8) {
       if (a.gain) {
-        const uint4 gg = *(const uint4*)(a.gain + kc * 8);
-        const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+        const uint32_t gw[4] = {gg[j].x, gg[j].y, gg[j].z, gg[j].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * inv * bf16_to_f32((gw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
       }
@@ -655,7 +806,7 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
       }
     }
     if (a.int4 && a.asum) {
-      // 16 consecutive chunks form one 128-wide group
+      // 16 consecutive chunks (consecutive lanes) form one 128-wide group
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
         hs += __shfl_xor(hs, o);
@@ -902,11 +1053,29 @@ hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s) {
   return hipSuccess;
 }
 
+template <int NP>
+static hipError_t launch_pack_np(const PackArgs& a, int rows, hipStream_t s) {
+  const int K8 = a.K / 8;
+  const int C = K8 <= 1024 ? 1 : 2;
+  const int bd = ((K8 + C - 1) / C + 63) / 64 * 64;
+  if (C == 1) hipLaunchKernelGGL((k_pack<NP, 1>), dim3(rows), dim3(bd), 0, s, a);
+  else hipLaunchKernelGGL((k_pack<NP, 2>), dim3(rows), dim3(bd), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   // every operand row of the last tile is written (rows >= M become zero)
   const int rows = a.apack ? ((a.M + 7) / 8) * 8 : a.M;
-  hipLaunchKernelGGL(k_pack, dim3(rows), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.K / 8 > 2048) return hipErrorInvalidValue;
+  switch (a.parts ? a.n_parts : 0) {
+    case 0: return launch_pack_np<0>(a, rows, s);
+    case 1: return launch_pack_np<1>(a, rows, s);
+    case 2: return launch_pack_np<2>(a, rows, s);
+    case 4: return launch_pack_np<4>(a, rows, s);
+    case 8: return launch_pack_np<8>(a, rows, s);
+    case 16: return launch_pack_np<16>(a, rows, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_argmax_reduce(const float* amax, int M, int n_parts, const int32_t* flags,

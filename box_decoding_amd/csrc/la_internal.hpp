@@ -30,7 +30,15 @@ struct GemmArgs {
   const float* residual;     // fp32 [M][ldy] (nullable)
   float* y;                  // fp32 [M][ldy]
   int ldy;
-  uint16_t* y_apack;         // SiLU epilogue: also pack the output rows here (nullable)
+  uint16_t* y_apack;         // SiLU: also pack the output rows here; STORE (ksplit 1):
+                             // pack y * out_gain for the next bf16 GEMM (nullable)
+  const uint16_t* out_gain;  // STORE: RMSNorm gain of the next consumer (with y_apack)
+  float* ss_out;             // STORE (ksplit 1): [M][n_tiles] sums of squares of y per tile
+  // consumers of an RMSNorm'd operand whose 1/rms is not applied yet: outputs
+  // are scaled by 1/sqrt(sum(ss_in[m][*]) / K + eps) (nullable)
+  const float* ss_in;
+  int ss_tiles;
+  float eps;
   // QKV epilogue
   const float2* rope;        // [M][64] (cos, sin) of the row's position
   const int32_t* prefix_len; // [B]
