@@ -10,6 +10,7 @@ on the host as a reference.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -19,6 +20,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+CAL_COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic_step_b1_p1280.json")
 METRIC = "PBD window steps/sec (≈boxes/sec) at batch 1 and 32; achieved HBM GB/s vs peak"
 
 
@@ -32,6 +35,74 @@ def weight_bytes(w):
     if w["fmt"] == "bf16":
         return n * k * 2
     return n * k // 2 + n * (k // int(w["group"])) * 2
+
+
+def gate_up_bytes(w, T, H, F):
+    """Algorithmic bytes of one gate/up launch: the weights once, the packed
+    operand (bf16 hi + lo of T rows) once, the fp32 output once."""
+    return weight_bytes(w) + T * H * 4 + T * F * 4
+
+
+def kernel_source_digest():
+    """Digest of the GEMM kernel source: counter-based traffic is only reported
+    for the kernel it was measured on."""
+    src = os.path.join(ROOT, "box_decoding_amd", "csrc", "la_gemm.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or None
+    when it was taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def pmc_summary(fetch_db, write_db, out_path):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE) into HBM bytes per gate/up launch, each counter scaled by what
+    it reads for the calibration copy of CAL_COPY_BYTES."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute(
+            "select kernel_name, dispatch_id, sum(value) from counters_collection "
+            "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+        con.close()
+        return rows
+
+    def summarize(db, counter):
+        rows = per_kernel(db, counter)
+        gu = [v for name, _, v in rows if "k_gemm<1, false, 1, 2>" in name]
+        # the calibration copy is the runtime's copy kernel moving CAL_COPY_BYTES,
+        # the largest such dispatch of the run
+        copies = [v for name, _, v in rows if name.startswith("__amd_rocclr_copyBuffer")]
+        cal = max(copies)
+        factor = CAL_COPY_BYTES / (cal * 1024.0)
+        return sum(gu) / len(gu) * 1024.0 * factor, factor, len(gu), cal
+
+    f_bytes, f_factor, n_f, f_cal = summarize(fetch_db, "FETCH_SIZE")
+    w_bytes, w_factor, n_w, w_cal = summarize(write_db, "WRITE_SIZE")
+    rec = {
+        "kernel": "k_gemm<1, false, 1, 2> (gate/up + SiLU, LDS-staged ring)",
+        "kernel_source_sha256_16": kernel_source_digest(),
+        "fetch_bytes_per_launch": round(f_bytes), "write_bytes_per_launch": round(w_bytes),
+        "traffic_bytes_per_launch": round(f_bytes + w_bytes),
+        "fetch_scale": f_factor, "write_scale": w_factor,
+        "calibration_copy_bytes": CAL_COPY_BYTES,
+        "calibration_fetch_kib": f_cal, "calibration_write_kib": w_cal,
+        "dispatches": [n_f, n_w],
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def step_bytes(model, dims, prefix_len, W):
@@ -101,7 +172,12 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="summarise two rocprofv3 --pmc runs of this script into the traffic file")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the PBD step here is a single-GPU path "
               "(data-parallel serving would run one independent copy per GPU).", file=sys.stderr)
@@ -169,28 +245,38 @@ def main():
         f"{steps_per_s:.1f} steps/s, {sbytes / ms_step / 1e6:.0f} GB/s algorithmic")
 
     # Dominant kernel: the gate/up projection with the SiLU epilogue (58% of a
-    # layer's weight bytes).  Timed with HIP events on the launch stream, cycling
-    # through the 36 layers' weights so that they stream from HBM.
+    # layer's weight bytes), the GEMM alone on a pre-packed operand.  Timed with
+    # HIP events on the stream the library launches on (torch's current
+    # stream), cycling through the 36 layers' weights so that they stream from
+    # HBM.
     F, H = d.inter, d.hidden
     T = w.batch * w.window
     xin = torch.randn((T, H), device=dev, generator=torch.Generator(device=dev).manual_seed(1))
     gain = model["layers"][0]["post_norm"]
+    packed = B.pack_rows(xin, w.wfmt, norm_gain=gain)
     yout = torch.empty((T, F), dtype=torch.float32, device=dev)
-    kws = B.Workspace(dev)
     for l in range(4):
-        B.wgemm(xin, model["layers"][l]["gate_up"], norm_gain=gain, silu_gate=True, out=yout, ws=kws)
+        B.wgemm_packed(packed, T, model["layers"][l]["gate_up"], silu_gate=True, out=yout)
     torch.cuda.synchronize()
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for r in range(args.kernel_reps):
-        B.wgemm(xin, model["layers"][r % d.n_layers]["gate_up"], norm_gain=gain, silu_gate=True,
-                out=yout, ws=kws)
+        B.wgemm_packed(packed, T, model["layers"][r % d.n_layers]["gate_up"], silu_gate=True,
+                       out=yout)
     k1.record(stream)
     torch.cuda.synchronize()
     k_ms = k0.elapsed_time(k1) / args.kernel_reps
-    gu_bytes = weight_bytes(model["layers"][0]["gate_up"]) + T * H * 4 + T * F * 4
+    gu_bytes = gate_up_bytes(model["layers"][0]["gate_up"], T, H, F)
     k_gbps = gu_bytes / (k_ms * 1e-3) / 1e9
-    log(f"bench: gate_up call {k_ms * 1e3:.1f} us, {k_gbps:.0f} GB/s")
+    log(f"bench: gate_up GEMM {k_ms * 1e3:.1f} us, {k_gbps:.0f} GB/s")
+
+    # a plain copy of known size: the scale for the HBM byte counters
+    cal_src = torch.empty(CAL_COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+    traffic = measured_traffic()
 
     result = {
         "metric": METRIC,
@@ -214,9 +300,9 @@ def main():
         "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
         "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
         "step_bytes": sbytes,
-        "roofline": {"bound": "hbm", "kernel": "gate_up GEMM + SiLU (la_wgemm call)",
+        "roofline": {"bound": "hbm", "kernel": "gate_up GEMM + SiLU (la_wgemm_packed)",
                      "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu_baseline:

@@ -26,7 +26,7 @@ EXPORTED = [
     "la_int4_embed_gather", "la_wgemm_workspace", "la_wgemm", "la_pbd_attention_workspace",
     "la_pbd_attention", "la_lm_head_argmax_workspace", "la_lm_head_argmax", "la_pbd_layer",
     "la_pbd_step_workspace", "la_pbd_step", "la_status_str", "la_pack_weight_bytes",
-    "la_pack_weight",
+    "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed",
 ]
 
 
@@ -97,6 +97,11 @@ def load() -> ctypes.CDLL:
         "la_status_str": (ctypes.c_char_p, [c_int32]),
         "la_pack_weight_bytes": (c_size_t, [W, c_int32, c_int32]),
         "la_pack_weight": (c_int32, [W, c_int32, c_void_p, c_void_p, c_void_p]),
+        "la_packed_rows_bytes": (c_size_t, [c_int32, c_int32]),
+        "la_pack_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_float, c_int32, c_void_p,
+                                   c_size_t, c_void_p]),
+        "la_wgemm_packed": (c_int32, [c_void_p, c_int32, W, c_void_p, c_void_p, c_int32, c_void_p,
+                                      c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -259,6 +264,38 @@ def wgemm(x: torch.Tensor, w: dict, norm_gain=None, eps: float = 1e-6, bias=None
     _check(lib.la_wgemm(_ptr(x), M, ctypes.byref(wd), _ptr(norm_gain), eps, _ptr(bias),
                         _ptr(residual), epi, _ptr(y), _ptr(buf), buf.numel(), _stream()),
            "la_wgemm")
+    return y
+
+
+def pack_rows(x: torch.Tensor, fmt: str = "bf16", norm_gain=None, eps: float = 1e-6,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The packed matrix-core operand of x (RMSNorm'd when norm_gain is given)
+    for a weight of format fmt, as a uint8 device buffer."""
+    lib = load()
+    _require_cuda(x, norm_gain)
+    M, K = x.shape
+    need = lib.la_packed_rows_bytes(M, K)
+    if need == 0:
+        raise LaError(f"no packed layout for M={M}, K={K}")
+    buf = out if out is not None else torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib.la_pack_rows(_ptr(x), M, K, _ptr(norm_gain), eps,
+                            LA_W_INT4 if fmt == "int4" else LA_W_BF16, _ptr(buf), buf.numel(),
+                            _stream()), "la_pack_rows")
+    return buf
+
+
+def wgemm_packed(packed: torch.Tensor, M: int, w: dict, bias=None, residual=None,
+                 silu_gate: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """la_wgemm on an operand made by pack_rows."""
+    lib = load()
+    _require_cuda(packed, bias, residual)
+    wd = weight_desc(w)
+    n_out = int(w["n"]) // 2 if silu_gate else int(w["n"])
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.float32,
+                                                device=packed.device)
+    _check(lib.la_wgemm_packed(_ptr(packed), M, ctypes.byref(wd), _ptr(bias), _ptr(residual),
+                               LA_EPI_SILU_GATE if silu_gate else LA_EPI_NONE, _ptr(y), _stream()),
+           "la_wgemm_packed")
     return y
 
 

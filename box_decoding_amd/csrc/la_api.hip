@@ -486,13 +486,55 @@ la_status la_int4_embed_gather(const int32_t* ids, int32_t T, const la_weight* e
   return hip_status(launch_prologue(p, stream));
 }
 
-size_t la_wgemm_workspace(int32_t M, const la_weight* w, int32_t epilogue) {
-  if (!w || M < 1 || w->k < 256) return 0;
+size_t la_packed_rows_bytes(int32_t M, int32_t K) {
+  if (M < 1 || K < 256 || K % 256) return 0;
   Carver c(nullptr);
-  c.take<uint16_t>(apack_elems(M, w->k));
-  c.take<float>((size_t)((M + 7) / 8) * (w->k / 128) * 16);
-  (void)epilogue;
+  c.take<uint16_t>(apack_elems(M, K));
+  c.take<float>((size_t)((M + 7) / 8) * (K / 128) * 16);
   return c.off;
+}
+
+la_status la_pack_rows(const float* x, int32_t M, int32_t K, const uint16_t* norm_gain,
+                       float rms_eps, int32_t fmt, void* packed, size_t packed_bytes,
+                       hipStream_t stream) {
+  if (!x || !packed) return LA_ERR_ARG;
+  if (fmt != LA_W_BF16 && fmt != LA_W_INT4) return LA_ERR_ARG;
+  if (M < 1 || M > 512 || K < 256 || K % 256 || K > 16384) return LA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(packed) || (norm_gain && !aligned16(norm_gain))) return LA_ERR_ARG;
+  if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
+  if (packed_bytes < la_packed_rows_bytes(M, K)) return LA_ERR_WORKSPACE;
+  Carver c(packed);
+  uint16_t* apack = c.take<uint16_t>(apack_elems(M, K));
+  float* asum = c.take<float>((size_t)((M + 7) / 8) * (K / 128) * 16);
+  return pack_rows(x, K, M, K, norm_gain, rms_eps, apack, asum, fmt == LA_W_INT4, nullptr, 0, nullptr,
+                   stream);
+}
+
+la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, const uint16_t* bias,
+                          const float* residual, int32_t epilogue, float* y, hipStream_t stream) {
+  if (!packed || !y || !w) return LA_ERR_ARG;
+  if (epilogue != LA_EPI_NONE && epilogue != LA_EPI_SILU_GATE) return LA_ERR_ARG;
+  if (M < 1 || M > 512) return LA_ERR_SHAPE;
+  const int epi = epilogue == LA_EPI_SILU_GATE ? EPI_SILU : EPI_STORE;
+  la_status st = check_gemm_weight(w, epi == EPI_SILU ? LA_LAYOUT_TILED_GU : LA_LAYOUT_TILED);
+  if (st != LA_OK) return st;
+  if (epi == EPI_SILU && (w->n % 16 || bias || residual)) return LA_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(y)) return LA_ERR_ARG;
+  Carver c(const_cast<void*>(packed));
+  GemmArgs g = base_gemm(w, M);
+  g.apack = c.take<uint16_t>(apack_elems(M, w->k));
+  g.asum = c.take<float>((size_t)((M + 7) / 8) * (w->k / 128) * 16);
+  g.bias = bias;
+  g.residual = residual;
+  g.y = y;
+  g.ldy = epi == EPI_SILU ? w->n / 2 : w->n;
+  return hip_status(launch_gemm(g, epi, w->fmt == LA_W_INT4, stream));
+}
+
+size_t la_wgemm_workspace(int32_t M, const la_weight* w, int32_t epilogue) {
+  if (!w) return 0;
+  (void)epilogue;
+  return la_packed_rows_bytes(M, w->k);
 }
 
 la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t* norm_gain,
@@ -509,16 +551,10 @@ la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t
   if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
   const size_t need = la_wgemm_workspace(M, w, epilogue);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
-  const bool int4 = w->fmt == LA_W_INT4;
-  Carver c(workspace);
-  uint16_t* apack = c.take<uint16_t>(apack_elems(M, w->k));
-  float* asum = c.take<float>((size_t)((M + 7) / 8) * (w->k / 128) * 16);
-  GemmArgs g = base_gemm(w, M);
-  g.bias = bias;
-  g.residual = residual;
-  g.y = y;
-  g.ldy = epi == EPI_SILU ? w->n / 2 : w->n;
-  return gemm_from_rows(g, x, w->k, norm_gain, rms_eps, apack, asum, epi, int4, stream);
+  if ((st = la_pack_rows(x, M, w->k, norm_gain, rms_eps, w->fmt, workspace, workspace_bytes,
+                         stream)) != LA_OK)
+    return st;
+  return la_wgemm_packed(workspace, M, w, bias, residual, epilogue, y, stream);
 }
 
 size_t la_pbd_attention_workspace(int32_t B, int32_t W, int32_t n_heads, int32_t n_kv_heads,

@@ -165,6 +165,21 @@ la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t
                    float rms_eps, const uint16_t* bias, const float* residual, int32_t epilogue,
                    float* y, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The two halves of la_wgemm, for callers that reuse one packed operand or
+ * time the GEMM alone.  la_pack_rows writes x' (as above) for a weight of
+ * format fmt (LA_W_BF16 / LA_W_INT4: the operand layout differs) into `packed`
+ * (caller-owned device memory of la_packed_rows_bytes(M, K) bytes, 16-byte
+ * aligned; x fp32 [M][K], 256 <= K <= 16384, K % 256 == 0).  la_wgemm_packed
+ * runs the GEMM and epilogue of la_wgemm on such an operand; w->k must equal
+ * the K it was packed with and w->fmt its fmt (not checkable: the operand
+ * carries no header).  Errors as la_wgemm; no workspace is needed. */
+size_t la_packed_rows_bytes(int32_t M, int32_t K);
+la_status la_pack_rows(const float* x, int32_t M, int32_t K, const uint16_t* norm_gain,
+                       float rms_eps, int32_t fmt, void* packed, size_t packed_bytes,
+                       hipStream_t stream);
+la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, const uint16_t* bias,
+                          const float* residual, int32_t epilogue, float* y, hipStream_t stream);
+
 /* Block-masked GQA attention of the window rows over the paged cache of one
  * layer.  q fp32 [B][W][n_heads][head_dim] (RoPE already applied); the keys of
  * sequence b are cache slots 0 .. P_b+W-1 (the window's own K/V must already be

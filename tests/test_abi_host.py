@@ -121,3 +121,23 @@ def test_gather_rejects(lib):
     assert lib.la_int4_embed_gather(fake, 6, ctypes.byref(e2), fake, None, None) == -1
     e3 = _w(n=100, k=2048)
     assert lib.la_int4_embed_gather(fake, 0, ctypes.byref(e3), fake, None, None) == 0  # empty: no-op
+
+
+def test_pack_rows_and_packed_gemm_reject_bad_arguments(lib):
+    fake = ctypes.c_void_p(4096)
+    need = lib.la_packed_rows_bytes(6, 2048)
+    assert need > 0 and lib.la_packed_rows_bytes(6, 2000) == 0 and lib.la_packed_rows_bytes(0, 2048) == 0
+    # bad format, K, alignment, too small a buffer
+    assert lib.la_pack_rows(fake, 6, 2048, None, 1e-6, 7, fake, need, None) == -1
+    assert lib.la_pack_rows(fake, 6, 2000, None, 1e-6, 0, fake, need, None) == -2
+    assert lib.la_pack_rows(ctypes.c_void_p(4100), 6, 2048, None, 1e-6, 0, fake, need, None) == -1
+    assert lib.la_pack_rows(fake, 6, 2048, None, 1e-6, 0, fake, need - 1, None) == -3
+    # a gain with a non-positive epsilon
+    assert lib.la_pack_rows(fake, 6, 2048, fake, 0.0, 0, fake, need, None) == -1
+    w = _w(layout=1)
+    assert lib.la_wgemm_packed(None, 6, ctypes.byref(w), None, None, 0, fake, None) == -1
+    assert lib.la_wgemm_packed(fake, 6, ctypes.byref(w), None, None, 5, fake, None) == -1
+    assert lib.la_wgemm_packed(fake, 0, ctypes.byref(w), None, None, 0, fake, None) == -2
+    # SiLU gating needs the gate/up layout and takes no bias or residual
+    wg = _w(n=2 * 1024, layout=2)
+    assert lib.la_wgemm_packed(fake, 6, ctypes.byref(wg), fake, None, 1, fake, None) == -2

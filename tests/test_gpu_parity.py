@@ -381,6 +381,23 @@ def _tile_reference(w, layout):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "int4"])
+@pytest.mark.parametrize("silu", [False, True])
+def test_wgemm_packed_matches_wgemm(fmt, silu):
+    # the two halves of la_wgemm give the same bits as the whole call
+    d = synth.ModelDims(n_layers=1)
+    model = B.pack_model(synth.make_model(d, fmt, 77, DEV))
+    w = model["layers"][0]["gate_up" if silu else "o"]
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn((13, int(w["k"])), device=DEV, generator=g)
+    gain = model["layers"][0]["post_norm"]
+    ref = B.wgemm(x, w, norm_gain=gain, silu_gate=silu)
+    packed = B.pack_rows(x, fmt, norm_gain=gain)
+    got = B.wgemm_packed(packed, 13, w, silu_gate=silu)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
 @pytest.mark.parametrize("layout,n", [(1, 2048 + 9), (2, 2 * 1024), (3, 2560)])
 def test_pack_weight_layouts_bit_exact(fmt, layout, n):
     w = synth._weight(fmt, n, 2048, DEV, 111, layout)
