@@ -124,7 +124,7 @@ def step_bytes(model, dims, prefix_len, W):
     return total
 
 
-def cpu_baseline(workload_name, sample_layers):
+def cpu_baseline(workload_name, sample_layers, min_seconds=10.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
     import torch
@@ -143,22 +143,32 @@ def cpu_baseline(workload_name, sample_layers):
     P = synth.draw_prefix_lens(w)
     cache = synth.to_numpy_tree(synth.make_cache(ds, P, w.window, seed=w.input_seed, device="cpu"))
     ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed).numpy()
-    h = O.embed_rows(ids.reshape(-1), model["embed"])
-    t0 = time.perf_counter()
-    for l in range(sample_layers):
-        h, _, _ = O.decoder_layer(h, model["layers"][l], ds, cache, l, P.numpy(), w.window)
-    t_layers = time.perf_counter() - t0
-    f = O.rmsnorm(h, O.bf16_to_float(model["final_norm"]), d.rms_eps)
+    h0 = O.embed_rows(ids.reshape(-1), model["embed"])
     lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
-    t0 = time.perf_counter()
-    O.lm_head_argmax(f, lm)
-    t_lm = time.perf_counter() - t0
+    # whole passes over the sample (its layers, then the final norm and the
+    # full lm_head argmax) until at least min_seconds of work are measured
+    t_layers = t_lm = 0.0
+    passes = 0
+    while passes == 0 or t_layers + t_lm < min_seconds:
+        h = h0
+        t0 = time.perf_counter()
+        for l in range(sample_layers):
+            h, _, _ = O.decoder_layer(h, model["layers"][l], ds, cache, l, P.numpy(), w.window)
+        t_layers += time.perf_counter() - t0
+        f = O.rmsnorm(h, O.bf16_to_float(model["final_norm"]), d.rms_eps)
+        t0 = time.perf_counter()
+        O.lm_head_argmax(f, lm)
+        t_lm += time.perf_counter() - t0
+        passes += 1
+    t_layers /= passes
+    t_lm /= passes
     t_step = t_layers / sample_layers * d.n_layers + t_lm
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{workload_name}: {sample_layers} of {d.n_layers} decoder layers "
-                      f"({t_layers:.1f} s) + the full lm_head argmax ({t_lm:.1f} s), float64 numpy, "
-                      f"extrapolated to one {d.n_layers}-layer step ({t_step:.1f} s)",
+            "sample": f"{workload_name}: {passes} pass(es) over {sample_layers} of {d.n_layers} "
+                      f"decoder layers ({t_layers:.2f} s per pass) + the full lm_head argmax "
+                      f"({t_lm:.2f} s per pass), float64 numpy, extrapolated to one "
+                      f"{d.n_layers}-layer step ({t_step:.2f} s)",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -169,7 +179,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="step_b1_p1280")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-layers", type=int, default=3)
+    ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
