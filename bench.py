@@ -44,11 +44,13 @@ def gate_up_bytes(w, T, H, F):
 
 
 def kernel_source_digest():
-    """Digest of the GEMM kernel source: counter-based traffic is only reported
-    for the kernel it was measured on."""
-    src = os.path.join(ROOT, "box_decoding_amd", "csrc", "la_gemm.hip")
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the small-batch GEMM kernel's sources: counter-based traffic
+    is only reported for the kernel it was measured on."""
+    h = hashlib.sha256()
+    for name in ("la_gemm.hip", "la_gemm_common.hpp", "la_common.hpp"):
+        with open(os.path.join(ROOT, "box_decoding_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

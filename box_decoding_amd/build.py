@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libla_pbd.so")
-SOURCES = ["la_prologue.hip", "la_gemm.hip", "la_attn.hip", "la_api.hip"]
+SOURCES = ["la_prologue.hip", "la_gemm.hip", "la_gemm_big.hip", "la_attn.hip", "la_api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -73,12 +73,20 @@ la_status check_gemm_weight(const la_weight* w, int tiled) {
 
 // ---------------------------------------------------------------- workspace plans
 
+// Launch plans as launch_gemm makes them: up to 32 rows the small-M kernel,
+// beyond that the large-M kernel (whose first launch fixes the plan).
 int gemm_parts(int M, const la_weight* w, int epi) {
-  return plan_gemm(M, w->n, w->k, w->fmt == LA_W_INT4, epi, false).grid;
+  const bool int4 = w->fmt == LA_W_INT4;
+  if (use_big_gemm(M, w->k, int4))
+    return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, epi, false).grid;
+  return plan_gemm(M, w->n, w->k, int4, epi, false).grid;
 }
 
 int gemm_ksplit(int M, const la_weight* w) {
-  return plan_gemm(M, w->n, w->k, w->fmt == LA_W_INT4, EPI_STORE, true).ksplit;
+  const bool int4 = w->fmt == LA_W_INT4;
+  if (use_big_gemm(M, w->k, int4))
+    return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_STORE, true).ksplit;
+  return plan_gemm(M, w->n, w->k, int4, EPI_STORE, true).ksplit;
 }
 
 struct StepWs {
@@ -340,7 +348,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
       return rs;
 
   const int F = m->inter;
-  if (!int4) {
+  if (!int4 && T <= 32) {
     // O projection: h += attn . Wo^T, h * post_norm packed for gate/up
     g = base_gemm(&L.o, T);
     g.apack = s.apack_o;
@@ -384,10 +392,11 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     return LA_OK;
   }
 
-  // INT4: O projection as K-slice partial sums (or h += directly)
+  // INT4, or more than 32 rows: O projection as K-slice partial sums (or h +=
+  // directly), then a packing kernel adds them and normalises
   const int ks_o = gemm_ksplit(T, &L.o);
   g = base_gemm(&L.o, T);
-  g.apack = s.apack;
+  g.apack = int4 ? s.apack : s.apack_o;  // bf16: packed by the attention merge
   g.asum = s.asum;
   if (ks_o > 1) {
     g.partial = s.parts;
@@ -396,21 +405,27 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.y = s.h;
     g.ldy = H;
   }
-  LA_TRY(launch_gemm(g, EPI_STORE, true, st));
+  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
 
-  // h += O partial sums; RMSNorm; gate/up + SiLU
-  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, true, s.parts,
+  // h += O partial sums; RMSNorm; gate/up + SiLU (bf16: packed straight into
+  // the down operand)
+  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
                       ks_o > 1 ? ks_o : 0, ks_o > 1 ? s.h : nullptr, st)) != LA_OK)
     return rs;
   g = base_gemm(&L.gate_up, T);
   g.apack = s.apack;
   g.asum = s.asum;
-  g.y = s.mlp;
-  g.ldy = F;
-  LA_TRY(launch_gemm(g, EPI_SILU, true, st));
-  if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true, nullptr, 0, nullptr,
-                      st)) != LA_OK)
-    return rs;
+  if (int4) {
+    g.y = s.mlp;
+    g.ldy = F;
+  } else {
+    g.y_apack = s.apack_m;
+  }
+  LA_TRY(launch_gemm(g, EPI_SILU, int4, st));
+  if (int4)
+    if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true, nullptr, 0, nullptr,
+                        st)) != LA_OK)
+      return rs;
 
   // down projection: K-slice partial sums left for the next packing
   const int ks_d = gemm_ksplit(T, &L.down);
@@ -424,7 +439,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.y = s.h;
     g.ldy = H;
   }
-  LA_TRY(launch_gemm(g, EPI_STORE, true, st));
+  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
   carry->pending = ks_d > 1 ? ks_d : 0;
   return LA_OK;
 }

@@ -1,0 +1,108 @@
+// Device helpers shared by the small-M and the large-M GEMM kernels: column
+// maps of the weight layouts, per-lane weight addressing and buffer loads.
+#pragma once
+
+#include "la_internal.hpp"
+
+namespace la {
+
+// ---------------------------------------------------------------- column maps
+
+// Weight row read by operand column c (0..15) of column tile `tile`.
+template <int EPI>
+__device__ __forceinline__ int col_row(int N, int tile, int c) {
+  if (EPI == EPI_SILU) {
+    // columns 0..7: gate rows, 8..15: the matching up rows
+    return c < 8 ? tile * 8 + c : N / 2 + tile * 8 + (c - 8);
+  } else if (EPI == EPI_QKV) {
+    // tile = (head, sub): dims sub*8 + c and 64 + sub*8 + c of one head, so each
+    // RoPE pair (i, i + 64) stays inside the tile
+    const int head = tile >> 3, sub = tile & 7;
+    return head * kHeadDim + (c < 8 ? sub * 8 + c : 64 + sub * 8 + (c - 8));
+  } else {
+    return tile * 16 + c;
+  }
+}
+
+__host__ __device__ __forceinline__ int layout_row(int layout, int N, int tile, int c) {
+  if (layout == LA_LAYOUT_TILED_GU) return c < 8 ? tile * 8 + c : N / 2 + tile * 8 + (c - 8);
+  if (layout == LA_LAYOUT_TILED_QKV) {
+    const int head = tile >> 3, sub = tile & 7;
+    return head * kHeadDim + (c < 8 ? sub * 8 + c : 64 + sub * 8 + (c - 8));
+  }
+  return tile * 16 + c;
+}
+
+// Weight location of this lane for a work item, as byte offsets into the
+// weight (and INT4 scale) buffer resources.
+struct WPtr {
+  uint32_t w;           // unit 0 of this lane
+  uint32_t ustride;     // between consecutive units
+  uint32_t s;           // INT4: scale of unit 0 for this lane
+  uint32_t sstride;     // INT4: between consecutive units
+};
+
+template <bool INT4, int EPI>
+__device__ __forceinline__ WPtr wptr(const GemmArgs& a, int tile) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  WPtr p;
+  p.s = 0;
+  p.sstride = 0;
+  if (a.layout != LA_LAYOUT_ROWS) {
+    const int UT = INT4 ? (a.K >> 7) : (a.K >> 5);
+    p.w = ((uint32_t)tile * UT * 64 + lane) * 16;
+    p.ustride = 1024;
+    if (INT4) {
+      p.s = ((uint32_t)tile * UT * 16 + c) * 2;
+      p.sstride = 32;
+    }
+  } else {
+    int r = col_row<EPI>(a.N, tile, c);
+    if (r >= a.N) r = a.N - 1;  // lm_head tail columns: read a valid row, drop the result
+    if (!INT4) {
+      p.w = ((uint32_t)r * a.K + g * 8) * 2;
+      p.ustride = 64;
+    } else {
+      p.w = (uint32_t)r * (a.K >> 1) + g * 16;
+      p.ustride = 64;
+      p.s = (uint32_t)r * (a.K >> 7) * 2;
+      p.sstride = 2;
+    }
+  }
+  return p;
+}
+
+// Buffer loads: an offset at or past the end of the resource reads zero and
+// touches no memory, which masks a unit without a branch.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kCfgDword = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;        // cache policy: streaming
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kCfgDword);
+}
+
+template <int POLICY>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
+// Running top-2 of a row: (v1, i1) the best value and its column (lowest index
+// on ties), v2 the second best value.
+struct Top2 {
+  float v1, v2;
+  int i1;
+};
+
+__device__ __forceinline__ void top2_merge(float& v1, int& i1, float& v2, float b1, int bi,
+                                           float b2) {
+  if (b1 > v1 || (b1 == v1 && bi < i1)) {
+    v2 = fmaxf(b2, v1);
+    v1 = b1;
+    i1 = bi;
+  } else {
+    v2 = fmaxf(v2, b1);
+  }
+}
+
+}  // namespace la

@@ -129,6 +129,20 @@ hipError_t launch_argmax_reduce(const float* amax, int M, int n_tiles, const int
                                 hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// Large-M GEMMs (more than 32 rows): every weight fragment meets all rows of a
+// launch (up to 192 bf16 / 48 INT4 rows) while it is in registers.
+struct BigPlan {
+  int n_tiles;
+  int rt, rw, cw;  // row tiles per consumer wave, rows and columns of consumer waves
+  int ksplit;
+  int grid, threads;
+  size_t smem;
+};
+int big_rows_per_launch(bool int4);
+bool use_big_gemm(int M, int K, bool int4);
+BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_split);
+hipError_t launch_gemm_big(GemmArgs a, int epi, bool int4, hipStream_t s);
+
 // attention split planning
 void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits);
 inline int attn_nqp(int W, int G) { return ((W * G + 15) / 16) * 16; }

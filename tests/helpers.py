@@ -35,6 +35,25 @@ def bf16_ulp_diff(a_bits, b_bits):
     return np.abs(ordered(a_bits) - ordered(b_bits))
 
 
+def bf16_kv_mismatch(got_bits, ref_bits, rel_floor=1e-4):
+    """Largest disagreement between bf16 K/V entries written by the GPU and the
+    oracle's rounding of the exact value, in bf16 ulps of the reference value.
+
+    The GPU rounds an fp32 result whose absolute error is a small fraction of
+    the tensor's scale; where the reference value is so small that this
+    fraction exceeds its bf16 ulp, any entry within rel_floor * rms of the
+    reference counts as 0 ulps.  Elsewhere one ulp (a rounding decision taken
+    on the other side of a tie point) is the bar."""
+    g = np.asarray(got_bits).view(np.uint16).astype(np.uint32) << 16
+    r = np.asarray(ref_bits).view(np.uint16).astype(np.uint32) << 16
+    gf = g.view(np.float32).astype(np.float64)
+    rf = r.view(np.float32).astype(np.float64)
+    rms = np.sqrt(np.mean(rf * rf)) if rf.size else 0.0
+    ulps = bf16_ulp_diff(got_bits, ref_bits)
+    small = np.abs(gf - rf) <= rel_floor * rms
+    return int(np.max(np.where(small, 0, ulps))) if ulps.size else 0
+
+
 def cache_slots(cache_np, layer, b, positions):
     """bf16 bits of K and V at the given token positions of sequence b: [n, Hkv, D]."""
     bs = int(cache_np["block"])

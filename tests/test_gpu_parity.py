@@ -13,7 +13,7 @@ import torch
 import oracle as O
 from box_decoding_amd import binding as B
 from box_decoding_amd import synth
-from helpers import bf16_ulp_diff, cache_slots, ids_match, np_tree, poison_unused_slots, rel_l2
+from helpers import bf16_kv_mismatch, bf16_ulp_diff, cache_slots, ids_match, np_tree, poison_unused_slots, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -180,11 +180,11 @@ def test_attention_grid_size_invariance():
 # ---------------------------------------------------------------- lm_head
 
 @pytest.mark.parametrize("fmt,V", [("bf16", 152681), ("int4", 152681), ("bf16", 1000)])
-def test_lm_head_argmax(fmt, V):
+@pytest.mark.parametrize("M", [13, 48])
+def test_lm_head_argmax(fmt, V, M):
     d = synth.ModelDims(n_layers=1, vocab=V)
     m = synth.make_model(d, fmt, seed=71, device=DEV)
     lm = m["lm_head"] if m["lm_head"] is not None else m["embed"]
-    M = 13
     h = torch.randn((M, d.hidden), device=DEV, generator=torch.Generator(device=DEV).manual_seed(V))
     ids, top1, gap = B.lm_head_argmax(h, lm, norm_gain=m["final_norm"])
     torch.cuda.synchronize()
@@ -192,7 +192,7 @@ def test_lm_head_argmax(fmt, V):
                   d.rms_eps)
     rid, rtop, rgap = O.lm_head_argmax(f, np_tree(lm))
     n, bad, excl = ids_match(ids.cpu().numpy(), rid, rgap)
-    _log(f"lm_head {fmt} V={V}: {n} compared, {bad} mismatches, {excl} near-ties excluded")
+    _log(f"lm_head {fmt} V={V} M={M}: {n} compared, {bad} mismatches, {excl} near-ties excluded")
     assert bad == 0
     assert np.max(np.abs(top1.cpu().numpy() - rtop)) < 1e-3
     assert np.max(np.abs(gap.cpu().numpy() - rgap)) < 1e-3
@@ -222,8 +222,8 @@ def _layer_case(wname, P_override=None, fmt=None):
     for b in range(Bn):
         pos = np.arange(int(P[b]), int(P[b]) + W)
         kg, vg = cache_slots(cg, 0, b, pos)
-        kd.append(bf16_ulp_diff(kg, kb[b * W:(b + 1) * W]).max())
-        vd.append(bf16_ulp_diff(vg, vb[b * W:(b + 1) * W]).max())
+        kd.append(bf16_kv_mismatch(kg, kb[b * W:(b + 1) * W]))
+        vd.append(bf16_kv_mismatch(vg, vb[b * W:(b + 1) * W]))
     return rel_l2(y.cpu().numpy(), ref), rel_l2(attn.cpu().numpy(), parts["attn"]), max(kd), max(vd)
 
 
@@ -238,6 +238,17 @@ def test_layer_ragged_batch_int4():
     e_out, e_attn, kd, vd = _layer_case("layer_b1_p512", P_override=[0, 33, 511, 700], fmt="int4")
     _log(f"layer int4 ragged: out rel-L2 {e_out:.2e}, attn rel-L2 {e_attn:.2e}, K/V ulp {kd}/{vd}")
     assert e_out <= TOL_INT4 and e_attn <= TOL_INT4
+    assert kd <= 1 and vd <= 1
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+def test_layer_batch8_large_m(fmt):
+    # 48 rows: every GEMM of the layer on the large-M path
+    P = [0, 5, 33, 130, 257, 511, 640, 700]
+    e_out, e_attn, kd, vd = _layer_case("layer_b1_p512", P_override=P, fmt=fmt)
+    _log(f"layer {fmt} batch 8: out rel-L2 {e_out:.2e}, attn rel-L2 {e_attn:.2e}, K/V ulp {kd}/{vd}")
+    tol = TOL_BF16 if fmt == "bf16" else TOL_INT4
+    assert e_out <= tol and e_attn <= tol
     assert kd <= 1 and vd <= 1
 
 
@@ -267,6 +278,21 @@ def test_step_small_ragged(fmt):
     n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
     e = rel_l2(hid, ref["hidden"])
     _log(f"step {fmt} 2 layers: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
+    assert err == 0
+    assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+    assert bad == 0
+
+
+@pytest.mark.parametrize("fmt,B_", [("bf16", 8), ("int4", 8), ("bf16", 32)])
+def test_step_batched_large_m(fmt, B_):
+    # more than 32 rows: the large-M GEMM path (48 rows, and 192 rows with two
+    # rows of consumer waves)
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    P_list = [int(p) for p in torch.randint(0, 700, (B_,), generator=torch.Generator().manual_seed(B_))]
+    got_ids, got_gap, hid, ref, err = _step_case(d, fmt, P_list, 6, seed=83 + B_)
+    n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
+    e = rel_l2(hid, ref["hidden"])
+    _log(f"step {fmt} B={B_} 2 layers: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
     assert err == 0
     assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
     assert bad == 0
