@@ -154,7 +154,11 @@ __global__ __launch_bounds__((RW * kBigMaxCW + kBigProducers) * 64) void k_gemm_
         wait_vmcnt<WAIT>();  // unit bi + 1 has landed
         stage_barrier();
       }
-      if (EPI == EPI_ARGMAX) __syncthreads();
+      // Both roles end on a full barrier.  Without it the compiler may share
+      // the final stage barrier between the roles, and the consumers' loop then
+      // inherits the producers' outstanding LDS copies: it waits for all
+      // memory (weights included) once per ring turn.
+      __syncthreads();
     };
     if (pw == 0) run(std::integral_constant<int, 0>{});
     else run(std::integral_constant<int, 1>{});
@@ -416,10 +420,10 @@ __global__ __launch_bounds__((RW * kBigMaxCW + kBigProducers) * 64) void k_gemm_
     }
     epilogue(cblock_of(it * nup));
   }
+  __syncthreads();  // pairs with the producers' last barrier
   if (EPI == EPI_ARGMAX) {
     // merge the column waves' row states (fixed order) and write one partial
     // per row and workgroup
-    __syncthreads();
     if (cw == 0) {
       for (int r = lane; r < RT * 8; r += 64) {
         const int ml = (rw * RT) * 8 + r;
