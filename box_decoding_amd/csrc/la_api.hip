@@ -89,6 +89,14 @@ int gemm_ksplit(int M, const la_weight* w) {
   return plan_gemm(M, w->n, w->k, int4, EPI_STORE, true).ksplit;
 }
 
+// K slices of the QKV projection: past 32 rows it writes slice sums that a
+// finishing kernel turns into q and the window's K/V (0: no slice buffer).
+int qkv_ksplit(int M, const la_weight* w) {
+  const bool int4 = w->fmt == LA_W_INT4;
+  if (!use_big_gemm(M, w->k, int4)) return 0;
+  return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_QKV, true).ksplit;
+}
+
 struct StepWs {
   float* h;
   float* q;
@@ -137,7 +145,9 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
   s.vocab_parts = gemm_parts(T, lm, EPI_ARGMAX);
   s.amax = lm_head ? c.take<float>((size_t)T * s.vocab_parts * 3) : nullptr;
   const int ksp = std::max(gemm_ksplit(T, &m->layers[0].o), gemm_ksplit(T, &m->layers[0].down));
-  s.parts = c.take<float>((size_t)ksp * T * H);
+  const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+  const size_t qkv_parts = (size_t)qkv_ksplit(T, &m->layers[0].qkv) * T * NQKV;
+  s.parts = c.take<float>(std::max((size_t)ksp * T * H, qkv_parts));
   s.bytes = c.off;
   return s;
 }
@@ -316,6 +326,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   g.num_blocks = kv->num_blocks;
   g.kc = (uint16_t*)kv->k + (size_t)l * le;
   g.vc = (uint16_t*)kv->v + (size_t)l * le;
+  if (qkv_ksplit(T, &L.qkv) > 0) g.partial = s.parts;  // slice sums + finishing kernel
   LA_TRY(launch_gemm(g, EPI_QKV, int4, st));
 
   // window attention -> packed O-projection operand

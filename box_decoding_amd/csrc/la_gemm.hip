@@ -654,9 +654,13 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
     p[1] = *(const float4*)(x + kc * 8 + 4);
 #pragma unroll
     for (int s = 0; s < NP; ++s) {
-      const float* pp = a.parts + ((size_t)s * a.M + m) * a.K + kc * 8;
-      p[2 * s + 2] = *(const float4*)pp;
-      p[2 * s + 3] = *(const float4*)(pp + 4);
+      // NP bounds the count; slices past a.n_parts read the last one and
+      // add it times zero (no branch, so every load is in flight at once)
+      const float* pp = a.parts + ((size_t)min(s, a.n_parts - 1) * a.M + m) * a.K + kc * 8;
+      const float on = s < a.n_parts ? 1.f : 0.f;
+      const float4 q0 = *(const float4*)pp, q1 = *(const float4*)(pp + 4);
+      p[2 * s + 2] = make_float4(q0.x * on, q0.y * on, q0.z * on, q0.w * on);
+      p[2 * s + 3] = make_float4(q1.x * on, q1.y * on, q1.z * on, q1.w * on);
     }
     if (a.gain) gg[j] = *(const uint4*)(a.gain + kc * 8);
     // x first, then the partial sums in order
@@ -971,15 +975,15 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   // every operand row of the last tile is written (rows >= M become zero)
   const int rows = a.apack ? ((a.M + 7) / 8) * 8 : a.M;
   if (a.K / 8 > 2048) return hipErrorInvalidValue;
-  switch (a.parts ? a.n_parts : 0) {
-    case 0: return launch_pack_np<0>(a, rows, s);
-    case 1: return launch_pack_np<1>(a, rows, s);
-    case 2: return launch_pack_np<2>(a, rows, s);
-    case 4: return launch_pack_np<4>(a, rows, s);
-    case 8: return launch_pack_np<8>(a, rows, s);
-    case 16: return launch_pack_np<16>(a, rows, s);
-    default: return hipErrorInvalidValue;
-  }
+  const int n = a.parts ? a.n_parts : 0;
+  if (n < 0 || n > 16) return hipErrorInvalidValue;
+  if (n == 0) return launch_pack_np<0>(a, rows, s);
+  if (n == 1) return launch_pack_np<1>(a, rows, s);
+  if (n == 2) return launch_pack_np<2>(a, rows, s);
+  if (n <= 4) return launch_pack_np<4>(a, rows, s);
+  if (n <= 8) return launch_pack_np<8>(a, rows, s);
+  if (n <= 12) return launch_pack_np<12>(a, rows, s);
+  return launch_pack_np<16>(a, rows, s);
 }
 
 hipError_t launch_argmax_reduce(const float* amax, int M, int n_parts, const int32_t* flags,

@@ -1,22 +1,30 @@
 // Weight-streaming GEMMs for 33 .. 192 rows (batched PBD windows) on the gfx950
 // matrix cores.
 //
-// At M = 6 x batch rows in the hundreds every weight must meet every row while
-// it is in registers: a weight fragment read once from HBM feeds one
-// 16x16x32 step per 8-row tile of the launch (24 steps at 192 rows), so the
-// stream stays near the HBM rate while the matrix cores do the hi + lo work.
+// At M = 6 x batch rows in the hundreds the contraction is dense enough for the
+// matrix cores to set the pace: 192 rows in bf16 hi + lo halves are 384
+// operand rows, so every weight fragment feeds a dozen 32x32x16 products.
 //
-// Work decomposition: workgroup b takes K slice b % ksplit and column blocks
-// b / ksplit, b / ksplit + gridDim.x / ksplit, ...; a column block is CW pairs
-// of 16-column tiles.  Its consumer waves form an RW x CW grid: wave (rw, cw)
-// keeps the accumulators of RT row tiles x 2 column tiles, loads the weights of
-// its two column tiles through a deep ring of registers (raw buffer loads; a
-// masked unit reads zero), and reads the activation fragments from LDS.  One
-// producer wave copies each K unit of the packed activations (all row tiles of
-// the launch) into a ring of LDS slots with direct-to-LDS loads; the waves
-// meet at one barrier per unit.  The producer keeps its own load counter, so a
-// consumer only ever waits for its weights.  Epilogues run in the consumer
-// waves straight from the accumulators.
+// One workgroup is four waves, one per SIMD, so each wave may hold 512
+// registers; the 32x32x16 product keeps a lone wave's matrix core near its
+// peak (the 16x16x32 one does not).  Waves (rw, cw) form a 2 x 2 grid: rw takes
+// half of the operand rows, cw half of a work item's 128 columns; an item is
+// those 128 columns over one K slice.  Per K unit (32 columns of K for bf16,
+// one 128-group for INT4) a stage
+//   - waits for this wave's copies of the unit read next and meets the other
+//     waves at one barrier, after which that unit is complete in LDS,
+//   - runs the stage's products, and among them
+//   - reads the next unit's activation fragments into registers (bf16),
+//   - copies a later unit of the packed activations into a ring of NS LDS
+//     slots with direct-to-LDS loads (each wave a quarter of it), into the
+//     slot whose reads completed before the barrier,
+//   - issues the weight loads of stage bi + DW into a register ring (raw
+//     buffer loads; a masked stage reads zero).
+// Loads complete in issue order, so a wave that waits for its copies has also
+// received every weight issued before them.  An item's stages are padded to
+// whole turns of the weight ring; its epilogue goes through a small LDS
+// staging area 8 rows at a time.  INT4 weights keep the 16x16x32 product
+// (its dequantisation runs between the steps) and the same item shape.
 #include <algorithm>
 #include <type_traits>
 
@@ -24,35 +32,50 @@
 
 namespace la {
 
-constexpr int kBigSlots = 5;  // LDS slots of the activation ring
+constexpr int kWideWaves = 4;
+constexpr int kItemTiles = 8;  // 16-column tiles per work item
 
-template <bool INT4>
-__host__ __device__ constexpr int big_depth() { return INT4 ? 3 : 5; }
+template <int RT, bool INT4>
+struct Wide {
+  // bf16: RT tiles of 32 operand rows (16 real rows) per row wave, CT = 2
+  // tiles of 32 columns per column wave.  INT4: RT tiles of 16 operand rows
+  // (8 real rows), CT = 4 tiles of 16 columns.
+  static constexpr int RTW = INT4 ? 2 * RT : 4 * RT;  // packed 16-row tiles of a launch
+  static constexpr int NP = INT4 ? RT : 2 * RT;       // epilogue parts of 8 real rows per row wave
+  static constexpr int CT = INT4 ? 4 : 2;
+  static constexpr int CPU = INT4 ? 16 : 4;           // 256-byte chunks per packed tile and K unit
+  static constexpr int FR = INT4 ? RT : 2 * RT;       // fragments per bf16 stage / INT4 K step
+  static constexpr int SUMS = INT4 ? RTW * 64 : 0;    // INT4 group sums of a slot (bytes)
+  static constexpr int SLOT = RTW * CPU * 256 + SUMS;
+  static constexpr int NS = INT4 ? 4 : 6;             // LDS slots
+  // bf16 reads the next stage's fragments during a stage (registers for two
+  // stages); INT4 reads its own stage's, one K step ahead
+  static constexpr bool PREFETCH = !INT4;
+  static constexpr int LA = NS - 1;                   // copy lead (stages)
+  static constexpr int R = INT4 ? 3 : 4;              // weight ring entries; loop unroll
+  static constexpr int DW = R - 1;                    // weight lead (stages)
+  static constexpr int NCOPY = RTW * CPU / 16;        // 1 KB copies per wave and stage
+  static constexpr int NC = NCOPY + (INT4 ? 1 : 0);
+  static constexpr int NW = 2 * CT;                   // bf16: CT tiles x 2 K steps; INT4: + scales
+  // A wave waits for its own copies of the unit read next before the barrier.
+  // Whatever their order inside a stage, at least LA - 1 whole stages of
+  // loads were issued after them (LA whole stages before the first read).
+  static constexpr int WAIT = (LA - 1) * (NC + NW);
+  static constexpr int WAIT0 = LA * (NC + NW);
+  static_assert(RTW % 4 == 0 && (R % 2 == 0 || !PREFETCH) && DW >= 1, "wide GEMM shape");
+  static_assert(WAIT0 < 64 && DW * (NC + NW) < 64, "vmcnt range");
+  static_assert(CT * (INT4 ? 16 : 32) * 2 == kItemTiles * 16, "item shape");
+};
 
-// LDS bytes of one activation slot: RTW row tiles x one K unit (+ INT4 group sums).
-__host__ __device__ constexpr int big_slot_bytes(int rtw, bool int4) {
-  return rtw * (int4 ? 16 : 4) * 256 + (int4 ? (rtw + 3) / 4 * 256 : 0);
+// Direct-to-LDS copies through a buffer resource: lane l's bytes at voff +
+// soff land at lds_dst + l * size.  (The buffer form keeps these loads in the
+// same in-order class as the weight loads, so the compiler's waits on the
+// weights stay exact.)
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 16, voff, soff, 0, 0);
 }
-
-// Two producer waves split the copies of a unit: producer 0 the first half of
-// the row tiles, producer 1 the rest (and the INT4 group sums).  Each issues a
-// fixed count per unit, so its waits are compile-time constants.
-constexpr int kBigProducers = 2;
-
-template <int RTW, bool INT4>
-__host__ __device__ constexpr int big_tiles_of(int p) {
-  return p == 0 ? RTW / 2 : RTW - RTW / 2;
-}
-template <int RTW, bool INT4>
-__host__ __device__ constexpr int big_copies(int p) {
-  return big_tiles_of<RTW, INT4>(p) * (INT4 ? 4 : 1) + ((INT4 && p == 1) ? (RTW + 3) / 4 : 0);
-}
-
-__device__ __forceinline__ void lds_copy16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_copy4(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)lds_dst, 4, 0, 0);
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) with the other counters untouched (gfx9 encoding).
@@ -62,14 +85,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// At most 3 column-pair waves per row of waves, plus the producer.
-constexpr int kBigMaxCW = 3;
-
-// The per-unit meeting point of producers and consumers.  A plain
-// __syncthreads would make the producers drain every copy in flight (its
-// release fence waits for all LDS-bound loads); instead each side waits for
-// exactly what it must before the hardware barrier: the producers for the unit
-// the consumers read next (wait_vmcnt), the consumers for their own LDS reads.
+// The per-stage meeting point: this wave's LDS reads are complete, then the
+// hardware barrier.  Unlike __syncthreads it does not wait for the copies in
+// flight (each wave waits for exactly its own before arriving).
 __device__ __forceinline__ void stage_barrier() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
@@ -77,360 +95,485 @@ __device__ __forceinline__ void stage_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <int RT, int RW, bool INT4, int EPI>
-__global__ __launch_bounds__((RW * kBigMaxCW + kBigProducers) * 64) void k_gemm_big(GemmArgs a) {
+// bf16 lanes holding 128 + q for the 8 nibbles of w (two masks and an OR each).
+__device__ __forceinline__ bf16x8 int4_as_bf16(uint32_t w) {
+  u32x4 bb;
+  bb[0] = (w & 0x000F000Fu) | 0x43004300u;
+  bb[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  bb[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  bb[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8, bb);
+}
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// D[32x32] += A[32x16] . B[16x32]: lane l holds A row l%32 and B column l%32
+// with k = 8*(l/32) .. +7; D lane l holds column l%32, rows 8*(q/4) + 4*(l/32)
+// + q%4 for q = 0..15.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+template <int RT, bool INT4, int EPI>
+__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_big(GemmArgs a) {
+  using C = Wide<RT, INT4>;
+  constexpr int RTW = C::RTW, NP = C::NP, CT = C::CT, CPU = C::CPU, FR = C::FR, NS = C::NS,
+                LA = C::LA, DW = C::DW, SLOT = C::SLOT;
+  using AccT = std::conditional_t<INT4, f32x4, f32x16>;
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int RTW = RT * RW;
-  constexpr int CPU = INT4 ? 16 : 4;
-  constexpr int D = big_depth<INT4>();
-  constexpr int SLOT = big_slot_bytes(RTW, INT4);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int CW = a.nw;  // column-pair waves per row of waves
-  const int n_cons = RW * CW;
+  const int rw = wave >> 1, cw = wave & 1;
+  const int g = lane >> 4, c = lane & 15;
   const int K8 = a.K >> 3, KG = a.K >> 7;
   const int units = INT4 ? (a.K >> 7) : (a.K >> 5);
   const int ks = (int)blockIdx.x % a.ksplit;
   const int cb0 = (int)blockIdx.x / a.ksplit, gt = (int)gridDim.x / a.ksplit;
   const int s_lo = units * ks / a.ksplit, s_hi = units * (ks + 1) / a.ksplit;
   const int nu = s_hi - s_lo;
-  // an item's stages are padded to whole turns of the weight ring (the padding
-  // stages read zero weights), so items end where a turn ends
-  const int nup = (nu + D - 1) / D * D;
-  const int n_cb = (a.n_tiles + 2 * CW - 1) / (2 * CW);
-  const int n_my = (n_cb - cb0 + gt - 1) / gt;
+  const int nup = (nu + C::R - 1) / C::R * C::R;  // stages per item: whole ring turns
+  const int n_cb = (a.n_tiles + kItemTiles - 1) / kItemTiles;
+  const int n_my = cb0 < n_cb ? (n_cb - cb0 + gt - 1) / gt : 0;
   const int total = n_my * nup;
-  if (total <= 0) return;  // uniform over the workgroup
   const int rows = min(a.M - a.m_base, RTW * 8);
   const int mtv = (rows + 7) >> 3;
-  unsigned char* slots = smem;                                  // [kBigSlots][SLOT]
-  float* stage_lds = (float*)(smem + kBigSlots * SLOT);         // [n_cons][3*8][33]
-  float* amax_lds = stage_lds + (size_t)n_cons * 3 * 8 * 33;    // ARGMAX: [n_cons][RT*8][3]
 
-  auto slot_of = [&](int bi) { return slots + (bi % kBigSlots) * SLOT; };
-  // unit of stage bi (a padding stage repeats the item's last unit)
-  auto unit_of = [&](int bi) { return s_lo + min(bi % nup, nu - 1); };
-  auto live_of = [&](int bi) { return bi < total && bi % nup < nu; };
-  auto cblock_of = [&](int bi) { return cb0 + (bi / nup) * gt; };
-
-  if (wave >= n_cons) {
-    // ---------------------------------------------------------------- producers
-    const int pw = wave - n_cons;  // 0 or 1
-    const uint16_t* ap = a.apack + (size_t)(a.m_base >> 3) * K8 * 128;
-    const float* asp = INT4 ? a.asum + (size_t)(a.m_base >> 3) * KG * 16 : nullptr;
-    auto copy_unit = [&](auto pc, int bi) {
-      constexpr int P = decltype(pc)::value;
-      constexpr int T0 = P == 0 ? 0 : RTW / 2;
-      constexpr int NT = big_tiles_of<RTW, INT4>(P);
-      // a stage past the end re-copies the last one into a slot nobody reads again
-      const int b = min(bi, total - 1);
-      const int u = unit_of(b);
-      unsigned char* dst = slot_of(bi);
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        const int t = T0 + tt;
-        const uint16_t* src = ap + ((size_t)min(t, mtv - 1) * K8 + (size_t)u * CPU) * 128;
-#pragma unroll
-        for (int q = 0; q < CPU / 4; ++q)
-          lds_copy16(src + q * 512 + lane * 8, dst + (t * CPU + q * 4) * 256);
-      }
-      if (INT4 && P == 1) {
-        float* sdst = (float*)(dst + RTW * CPU * 256);
-#pragma unroll
-        for (int q = 0; q < (RTW + 3) / 4; ++q) {
-          const int t = min(q * 4 + (lane >> 4), RTW - 1);
-          lds_copy4(asp + ((size_t)min(t, mtv - 1) * KG + u) * 16 + (lane & 15), sdst + q * 64);
-        }
-      }
-    };
-    auto run = [&](auto pc) {
-      constexpr int P = decltype(pc)::value;
-      constexpr int WAIT = (kBigSlots - 2) * big_copies<RTW, INT4>(P);
-#pragma unroll
-      for (int j = 0; j < kBigSlots - 1; ++j) copy_unit(pc, j);
-      wait_vmcnt<WAIT>();
-      stage_barrier();
-      for (int bi = 0; bi < total; ++bi) {
-        copy_unit(pc, bi + kBigSlots - 1);
-        wait_vmcnt<WAIT>();  // unit bi + 1 has landed
-        stage_barrier();
-      }
-      // Both roles end on a full barrier.  Without it the compiler may share
-      // the final stage barrier between the roles, and the consumers' loop then
-      // inherits the producers' outstanding LDS copies: it waits for all
-      // memory (weights included) once per ring turn.
-      __syncthreads();
-    };
-    if (pw == 0) run(std::integral_constant<int, 0>{});
-    else run(std::integral_constant<int, 1>{});
-    return;
-  }
-
-  // ---------------------------------------------------------------- consumers
-  const int rw = wave / CW, cw = wave - rw * CW;
-  const int g = lane >> 4, c = lane & 15;
-  const __amdgpu_buffer_rsrc_t rwt = make_rsrc(a.w, a.w_bytes);
-  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(INT4 ? (const void*)a.wscale : a.w, INT4 ? a.s_bytes : 0u);
-
-  struct WStage {
-    u32x4 w[2];
-    uint16_t s[INT4 ? 2 : 1];
-  };
-  WStage st[D];
-  auto issue = [&](int bi, WStage& s) {
-    const int b = min(bi, total - 1);
-    const int u = unit_of(b);
-    const int tile0 = (cblock_of(b) * CW + cw) * 2;
-    const bool live_stage = live_of(bi);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int tile = tile0 + t;
-      const bool live = live_stage && tile < a.n_tiles;  // wave-uniform
-      const WPtr wp = wptr<INT4, EPI>(a, min(tile, a.n_tiles - 1));
-      const uint32_t dead = (uint32_t)(!live) << 31;  // out of range: reads zero
-      s.w[t] = bload16<kNonTemporal>(rwt, (wp.w + (uint32_t)u * wp.ustride) | dead);
-      if (INT4) s.s[INT4 ? t : 0] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (wp.s + (uint32_t)u * wp.sstride) | dead, 0, 0);
-    }
-  };
-
-  f32x4 acc[RT][2];
-#pragma unroll
-  for (int i = 0; i < RT; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const WStage& s, const unsigned char* slot) {
-    const uint16_t* A = (const uint16_t*)slot + (size_t)(rw * RT) * CPU * 128 + c * 8;
-    if (!INT4) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, s.w[0]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, s.w[1]);
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        const bf16x8 af = *(const bf16x8*)(A + (i * CPU + g) * 128);
-        acc[i][0] = mfma_16x16x32(af, b0, acc[i][0]);
-        acc[i][1] = mfma_16x16x32(af, b1, acc[i][1]);
-      }
-    } else {
-      // 128 + q as bf16 from two masks and an OR; per group:
-      // acc += scale * (sum - 136 * sum_k a_k)
-      const float* AS = (const float*)(slot + RTW * CPU * 256) + (size_t)(rw * RT) * 16 + 4 * g;
-      f32x4 tacc[RT][2];
-#pragma unroll
-      for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) tacc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 bv[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t w = s.w[t][j];
-          u32x4 bb;
-          bb[0] = (w & 0x000F000Fu) | 0x43004300u;
-          bb[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-          bb[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-          bb[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-          bv[t] = __builtin_bit_cast(bf16x8, bb);
-        }
-#pragma unroll
-        for (int i = 0; i < RT; ++i) {
-          const bf16x8 af = *(const bf16x8*)(A + (i * CPU + g * 4 + j) * 128);
-          tacc[i][0] = mfma_16x16x32(af, bv[0], tacc[i][0]);
-          tacc[i][1] = mfma_16x16x32(af, bv[1], tacc[i][1]);
-        }
-        // the next step's fragments are not read ahead of time (registers)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const float sc0 = fp16_to_f32(s.s[0]), sc1 = fp16_to_f32(s.s[INT4 ? 1 : 0]);
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        const f32x4 as = *(const f32x4*)(AS + i * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[i][0][e] += sc0 * (tacc[i][0][e] - 136.0f * as[e]);
-          acc[i][1][e] += sc1 * (tacc[i][1][e] - 136.0f * as[e]);
-        }
-      }
-    }
-  };
-
-  // Epilogue of one column block.  The accumulators go through this wave's
-  // small LDS staging area RP row tiles at a time (hi + lo rows added; lanes
-  // 0..31 hold real rows 4g + e, column c), and one rolled loop does the
-  // epilogue of each part, so its code exists once.
-  constexpr int RP = 3;  // row tiles per staged part
-  constexpr int NPART = RT / RP;
-  static_assert(RT % RP == 0, "parts");
-  float* stage = stage_lds + (size_t)wave * RP * 8 * 33;
-  float* my_amax = EPI == EPI_ARGMAX ? amax_lds + (size_t)wave * RT * 8 * 3 : nullptr;
+  constexpr int SW = kItemTiles / 2 * 16;  // columns of a column wave
+  constexpr int SROW = SW + 4;  // 16-byte aligned rows, column writes spread over banks
+  unsigned char* slots = smem;                                              // [NS][SLOT]
+  float* stage = (float*)(smem + NS * SLOT) + (size_t)wave * 8 * SROW;      // [8][SROW] per wave
+  float* amax_lds = (float*)(smem + NS * SLOT) + (size_t)kWideWaves * 8 * SROW;
+  float* my_amax = amax_lds + (size_t)wave * NP * 8 * 3;                    // ARGMAX: [NP*8][3]
   if (EPI == EPI_ARGMAX) {
-    for (int i = lane; i < RT * 8; i += 64) {
+    for (int i = lane; i < NP * 8; i += 64) {
       my_amax[i * 3 + 0] = -INFINITY;
       my_amax[i * 3 + 1] = __int_as_float(0x7FFFFFFF);
       my_amax[i * 3 + 2] = -INFINITY;
     }
   }
-  auto stage_part = [&](auto pc) {
-    constexpr int P = decltype(pc)::value;
+
+  // A stream walks the stages in order: item `it`, stage `uu` of the item's
+  // nup, LDS slot.  Stepping is scalar and branch-free.  Past the last item
+  // a stream keeps producing valid (unused) stages.
+  struct Pos {
+    int it, uu, slot;
+  };
+  auto step = [&](Pos& q) {
+    const bool wrap = q.uu + 1 == nup;
+    q.uu = wrap ? 0 : q.uu + 1;
+    q.it += wrap ? 1 : 0;
+    q.slot = q.slot + 1 == NS ? 0 : q.slot + 1;
+  };
+  auto slot_ptr = [&](int slot) { return slots + slot * SLOT; };
+
+  // ---- activation copies: 1 KB pieces wave, wave + 4, ... of the unit
+  const __amdgpu_buffer_rsrc_t rap =
+      make_rsrc(a.apack + (size_t)(a.m_base >> 3) * K8 * 128, (uint32_t)mtv * K8 * 256);
+  const __amdgpu_buffer_rsrc_t ras =
+      make_rsrc(INT4 ? (const void*)(a.asum + (size_t)(a.m_base >> 3) * KG * 16) : a.apack,
+                INT4 ? (uint32_t)mtv * KG * 64 : 0u);
+  // INT4 group sums: RTW packed tiles x 16 floats = RTW / 4 pieces of 256 B;
+  // waves beyond the piece count repeat the first ones (same bytes, same place)
+  static_assert(!INT4 || RTW / 4 <= 4, "sum pieces");
+  const int sum_q = INT4 ? wave % (RTW / 4) : 0;
+  const uint32_t sum_voff =
+      INT4 ? ((uint32_t)min(min(sum_q * 4 + (lane >> 4), RTW - 1), mtv - 1) * KG * 16 + (lane & 15)) * 4 : 0u;
+  auto copy_stage = [&](const Pos& q) {
+    const uint32_t u = (uint32_t)(s_lo + min(q.uu, nu - 1));
+    unsigned char* dst = slot_ptr(q.slot);
 #pragma unroll
-    for (int ii = 0; ii < RP; ++ii) {
-      constexpr int dummy = 0;
-      (void)dummy;
-      const int i = P * RP + ii;
+    for (int k = 0; k < C::NCOPY; ++k) {
+      const int p = wave + 4 * k;
+      const int t = p / (CPU / 4), part = p % (CPU / 4);
+      const uint32_t soff = ((uint32_t)min(t, mtv - 1) * K8 + u * CPU + part * 4) * 256;
+      lds_copy16(rap, lane * 16, soff, dst + (t * CPU + part * 4) * 256);
+    }
+    if (INT4) lds_copy4(ras, sum_voff, u * 64, dst + RTW * CPU * 256 + sum_q * 256);
+  };
+
+  // ---- weights of the column wave's 16-column tiles tile0 .. tile0 + 3.  A
+  // lane's offset is a fixed part (which operand column and K slice it holds)
+  // plus a wave-uniform part (tile and unit), so a load needs no vector
+  // arithmetic.  bf16 (32x32x16): lane l holds column l%32 of a 32-column
+  // tile (16-column tile 2T + (l/16)%2, column l%16) and K values
+  // 16*kk + 8*(l/32) .. +7 of the unit; in the 16-column tile's layout those
+  // are lane (2*kk + l/32)*16 + l%16's bytes.
+  const __amdgpu_buffer_rsrc_t rwt = make_rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(INT4 ? (const void*)a.wscale : a.w, INT4 ? a.s_bytes : 0u);
+  const bool tiled = a.layout != LA_LAYOUT_ROWS;
+  const int UT = units;
+  // row layout: weight row of operand column c of a tile = row_of_tile + row_of_lane
+  const int row_of_lane = EPI == EPI_SILU ? (c < 8 ? c : a.N / 2 + c - 8)
+                          : EPI == EPI_QKV ? (c < 8 ? c : 56 + c) : c;
+  const int odd = (lane >> 4) & 1;  // bf16: second 16-column tile of the pair
+  const int tile_rows = EPI == EPI_STORE || EPI == EPI_ARGMAX ? 16 : 8;  // row step of a 16-column tile
+  uint32_t w_lane, s_lane = 0;
+  if (INT4) {
+    w_lane = tiled ? (uint32_t)lane * 16 : (uint32_t)row_of_lane * (a.K >> 1) + g * 16;
+    s_lane = tiled ? (uint32_t)c * 2 : (uint32_t)row_of_lane * KG * 2;
+  } else {
+    w_lane = tiled ? (uint32_t)((lane >> 5) * 16 + c) * 16 + (uint32_t)odd * UT * 1024
+                   : ((uint32_t)(row_of_lane + odd * tile_rows) * a.K + (lane >> 5) * 8) * 2;
+  }
+  const uint32_t kk_step = tiled ? 512u : 32u;  // bf16: second K step of the unit
+  const uint32_t ustride = tiled ? 1024u : 64u;
+  const uint32_t sstride = tiled ? 32u : 2u;
+  auto tile_row = [&](int tile) {
+    return EPI == EPI_SILU ? tile * 8 : EPI == EPI_QKV ? (tile >> 3) * 128 + (tile & 7) * 8 : tile * 16;
+  };
+  auto tile_w = [&](int tile) -> uint32_t {
+    if (tiled) return (uint32_t)tile * UT * 1024;
+    return INT4 ? (uint32_t)tile_row(tile) * (a.K >> 1) : (uint32_t)tile_row(tile) * a.K * 2;
+  };
+  auto tile_s = [&](int tile) -> uint32_t {
+    return tiled ? (uint32_t)tile * UT * 32 : (uint32_t)tile_row(tile) * KG * 2;
+  };
+  struct WStage {
+    u32x4 w[2 * CT / (INT4 ? 2 : 1)];  // bf16: [tile][K step]; INT4: [tile]
+    uint32_t s[INT4 ? CT : 1];         // fp16 bits; 32-bit so no wait to pack halves
+  };
+  WStage st[C::R];
+  auto issue_w = [&](const Pos& q, WStage& d) {
+    const bool live_stage = q.it < n_my && q.uu < nu;
+    const uint32_t u = (uint32_t)(s_lo + min(q.uu, nu - 1));
+    const int tile0 = ((cb0 + q.it * gt) * 2 + cw) * (kItemTiles / 2);
+    if (INT4) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = acc[P * RP + ii][t][e] + __shfl_xor(acc[P * RP + ii][t][e], 32);
-          if (g < 2) stage[(ii * 8 + 4 * g + e) * 33 + t * 16 + c] = v;
-        }
-        acc[P * RP + ii][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < CT; ++t) {
+        const int tile = tile0 + t;
+        const bool live = live_stage && tile < a.n_tiles;  // wave-uniform
+        // a dead load starts past the end of the buffer and reads zero
+        const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
+        d.w[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwt, w_lane, so, kNonTemporal));
+        const uint32_t ss = live ? tile_s(tile) + u * sstride : 0x7FFFFFFFu;
+        d.s[INT4 ? t : 0] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane, ss, 0);
       }
-      (void)i;
+    } else {
+#pragma unroll
+      for (int T = 0; T < CT; ++T) {
+        const int tile = tile0 + 2 * T;
+        // both 16-column tiles of the pair live or dead together (n_tiles is
+        // even for every bf16 weight with N % 32 == 0; the tail of an odd one
+        // reads past its end, which is zero)
+        const bool live = live_stage && tile < a.n_tiles;
+        const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          d.w[T * 2 + kk] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwt, w_lane + kk * kk_step, so, kNonTemporal));
+      }
     }
   };
-  auto epi_part = [&](int cblock, int part) {
-    const int tile0 = (cblock * CW + cw) * 2;
-    const int row0 = rw * RT * 8 + part * RP * 8;  // first staged row within the launch
-    if (EPI == EPI_ARGMAX) {
-      // lane r < RP*8 takes staged row r: its 32 columns into the row's state
-      if (lane < RP * 8) {
-        const float* src = stage + lane * 33;
-        float* s3 = my_amax + (part * RP * 8 + lane) * 3;
-        float v1 = s3[0], v2 = s3[2];
-        int i1 = __float_as_int(s3[1]);
-        for (int cc = 0; cc < 32; ++cc) {
-          const int tile = tile0 + (cc >> 4);
-          const int n = tile * 16 + (cc & 15);
-          if (tile >= a.n_tiles || n >= a.N) break;
-          top2_merge(v1, i1, v2, src[cc], n, -INFINITY);
-        }
-        s3[0] = v1;
-        s3[1] = __int_as_float(i1);
-        s3[2] = v2;
-      }
-      return;
+
+  // ---- activation fragments.  bf16: fragment 2i + kk is row tile i (packed
+  // tiles 2i, 2i + 1 of the wave's rows), K step kk; INT4: row tile i of K
+  // step j.
+  const uint32_t a_lane = INT4 ? (uint32_t)(rw * RT) * CPU * 256 + c * 16
+                               : ((uint32_t)((2 * rw * RT + odd) * CPU + (lane >> 5)) * 16 + c) * 16;
+  auto frag_base = [&](int slot) { return (const unsigned char*)(slot_ptr(slot) + a_lane); };
+  auto read_frags = [&](const unsigned char* A, int j, bf16x8 (&d)[FR]) {
+    if (INT4) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) d[i] = *(const bf16x8*)(A + (i * CPU + g * 4 + j) * 256);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) d[2 * i + kk] = *(const bf16x8*)(A + (2 * i * CPU + 2 * kk) * 256);
     }
-    for (int idx = lane; idx < RP * 8 * 32; idx += 64) {
-      const int r = idx >> 5, cc = idx & 31;
-      const int t = cc >> 4, cl = cc & 15;
-      const int tile = tile0 + t;
-      const int ml = row0 + r;
-      if (tile >= a.n_tiles || ml >= rows) continue;
-      const int m = a.m_base + ml;
-      const float v = stage[r * 33 + cc];
-      if (EPI == EPI_STORE) {
-        const int n = tile * 16 + cl;
-        if (n >= a.N) continue;
-        if (a.ksplit > 1) {
-          a.partial[((size_t)ks * a.M + m) * a.N + n] = v;
+  };
+
+  AccT acc[RT][CT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int t = 0; t < CT; ++t) acc[i][t] = AccT{};
+
+  // bf16: the products of one stage from fragments read one stage earlier
+  auto compute_bf16 = [&](const WStage& s, const bf16x8 (&f)[FR]) {
+    if constexpr (!INT4) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int T = 0; T < CT; ++T)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            acc[i][T] = mfma_32x32x16(f[2 * i + kk], __builtin_bit_cast(bf16x8, s.w[T * 2 + kk]), acc[i][T]);
+    }
+  };
+  // INT4: one 128-group per stage, per group
+  //   acc += scale * (sum_k a_k (128 + q_k) - 136 * sum_k a_k),
+  // the fragments of step j + 1 read while step j multiplies
+  auto compute_int4 = [&](int slot, const WStage& s) {
+    if constexpr (INT4) {
+      const unsigned char* A = frag_base(slot);
+      const float* AS = (const float*)(slot_ptr(slot) + RTW * CPU * 256) + (size_t)(rw * RT) * 16 + 4 * g;
+      f32x4 sums[RT];
+#pragma unroll
+      for (int i = 0; i < RT; ++i) sums[i] = *(const f32x4*)(AS + i * 16);
+      bf16x8 fa[2][FR];
+      read_frags(A, 0, fa[0]);
+      f32x4 tacc[RT][CT];
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int t = 0; t < CT; ++t) tacc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < 3) read_frags(A, j + 1, fa[(j + 1) & 1]);
+        bf16x8 bv[CT];
+#pragma unroll
+        for (int t = 0; t < CT; ++t) bv[t] = int4_as_bf16(s.w[t][j]);
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int t = 0; t < CT; ++t) tacc[i][t] = mfma_16x16x32(fa[j & 1][i], bv[t], tacc[i][t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        const float sc = fp16_to_f32(s.s[INT4 ? t : 0]);
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][t][e] += sc * (tacc[i][t][e] - 136.0f * sums[i][e]);
+      }
+    }
+  };
+
+  // ---- epilogue of one column block, 8 real rows (a part) at a time: the
+  // part's accumulators go through this wave's LDS staging rows (hi + lo
+  // added), and one rolled loop does the per-element work, so its code exists
+  // once.
+  auto stage_part = [&](auto pc) {
+    constexpr int P = decltype(pc)::value;
+    if constexpr (INT4) {
+      // 16x16x32: lanes g < 2 hold real rows 4g + e after the xor-32 exchange
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[P][t][e] + __shfl_xor(acc[P][t][e], 32);
+          if (g < 2) stage[(4 * g + e) * SROW + t * 16 + c] = v;
+        }
+        acc[P][t] = AccT{};
+      }
+    } else {
+      // 32x32x16: rows 8h + 4*(l/32) + e (hi) and 8h + 8 + ... (lo) of tile
+      // P/2 sit in the same lane at q = 8*(P%2) + e and q + 4
+      constexpr int i = P / 2, h = P % 2;
+#pragma unroll
+      for (int T = 0; T < CT; ++T) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          stage[((lane >> 5) * 4 + e) * SROW + T * 32 + (lane & 31)] = acc[i][T][8 * h + e] + acc[i][T][8 * h + e + 4];
+        if (h == 1) acc[i][T] = AccT{};
+      }
+    }
+  };
+  // One lane per 8 consecutive staged columns of a row (r = lane / 8, column
+  // group lane % 8: 16-column tile (lane % 8) / 2, half lane % 2), so the
+  // outputs go out as 16-byte pieces.
+  auto epi_part = [&](int cblock, int part) {
+    const int tile0 = (cblock * 2 + cw) * (kItemTiles / 2);
+    const int r = lane >> 3, grp = lane & 7;
+    const int t = grp >> 1, half = grp & 1;
+    const int tile = tile0 + t;
+    const int ml = (rw * NP + part) * 8 + r;  // row within the launch
+    const bool row_ok = ml < rows, tile_ok = tile < a.n_tiles;
+    const int m = a.m_base + ml;
+    const float* src = stage + r * SROW + grp * 8;
+    if (EPI == EPI_ARGMAX) {
+      float v1 = -INFINITY, v2 = -INFINITY;
+      int i1 = 0x7FFFFFFF;
+      const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = tile * 16 + half * 8 + e;
+        if (tile_ok && n < a.N) top2_merge(v1, i1, v2, e < 4 ? x0[e] : x1[e - 4], n, -INFINITY);
+      }
+#pragma unroll
+      for (int x = 1; x < 8; x <<= 1) {
+        const float o1 = __shfl_xor(v1, x), o2 = __shfl_xor(v2, x);
+        const int oi = __shfl_xor(i1, x);
+        top2_merge(v1, i1, v2, o1, oi, o2);
+      }
+      if (grp == 0) {
+        float* s3 = my_amax + (part * 8 + r) * 3;
+        float w1 = s3[0], w2 = s3[2];
+        int wi = __float_as_int(s3[1]);
+        top2_merge(w1, wi, w2, v1, i1, v2);
+        s3[0] = w1;
+        s3[1] = __int_as_float(wi);
+        s3[2] = w2;
+      }
+    } else if (EPI == EPI_SILU) {
+      // lanes 0..31: row lane / 4, tile lane % 4; columns 0..7 of the tile are
+      // gate rows tile*8 + c, 8..15 the matching up rows
+      const int rs = lane >> 2, ts = lane & 3;
+      const int tile_s = tile0 + ts;
+      const int ml_s = (rw * NP + part) * 8 + rs;
+      if (lane < 32 && tile_s < a.n_tiles && ml_s < rows) {
+        const int ms = a.m_base + ml_s;
+        const float* gsrc = stage + rs * SROW + ts * 16;
+        const int F = a.N / 2;
+        const int n0 = tile_s * 8;
+        uint16_t* base = a.y_apack ? a.y_apack + (((size_t)(ms >> 3) * (F / 8) + tile_s) * 16 + (ms & 7)) * 8 : nullptr;
+        // two halves of 4 columns: 8-byte hi and lo pieces
+#pragma unroll 1
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 gv = *(const f32x4*)(gsrc + 4 * hf), uv = *(const f32x4*)(gsrc + 8 + 4 * hf);
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = silu_f(gv[e]) * uv[e];
+          if (a.y) {
+            float* yo = a.y + (size_t)ms * a.ldy + n0 + 4 * hf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yo[e] = y[e];
+          }
+          if (base) {
+            u32x2 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              uint32_t h0, l0, h1, l1;
+              split_hi_lo(y[2 * e], h0, l0);
+              split_hi_lo(y[2 * e + 1], h1, l1);
+              hi[e] = h0 | (h1 << 16);
+              lo[e] = l0 | (l1 << 16);
+            }
+            *(u32x2*)(base + 4 * hf) = hi;
+            *(u32x2*)(base + 64 + 4 * hf) = lo;
+          }
+        }
+      }
+    } else if (EPI == EPI_QKV || a.partial) {
+      // K-slice partial sums (QKV: at the natural column of the operand; the
+      // 8 columns of a half tile are consecutive there)
+      if (row_ok && tile_ok) {
+        const int n0 = EPI == EPI_QKV ? col_row<EPI_QKV>(a.N, tile, half * 8) : tile * 16 + half * 8;
+        float* po = a.partial + ((size_t)ks * a.M + m) * a.N + n0;
+        if (n0 + 8 <= a.N && (a.N & 3) == 0) {
+          *(f32x4*)po = *(const f32x4*)src;
+          *(f32x4*)(po + 4) = *(const f32x4*)(src + 4);
         } else {
-          float y = v;
+          for (int e = 0; e < 8 && n0 + e < a.N; ++e) po[e] = src[e];
+        }
+      }
+    } else {
+      // y = v (+ bias + residual)
+      if (row_ok && tile_ok) {
+        const int n0 = tile * 16 + half * 8;
+#pragma unroll 1
+        for (int e = 0; e < 8; ++e) {
+          const int n = n0 + e;
+          if (n >= a.N) break;
+          float y = src[e];
           if (a.bias) y += bf16_to_f32(a.bias[n]);
           if (a.residual) y += a.residual[(size_t)m * a.ldy + n];
           a.y[(size_t)m * a.ldy + n] = y;
         }
-      } else if (EPI == EPI_SILU) {
-        // columns 0..7: gate rows tile*8 + c, 8..15: the matching up rows
-        if (cl >= 8) continue;
-        const int F = a.N / 2;
-        const int n = tile * 8 + cl;
-        const float y = silu_f(v) * stage[r * 33 + cc + 8];
-        if (a.y) a.y[(size_t)m * a.ldy + n] = y;
-        if (a.y_apack) {
-          uint32_t h, l;
-          split_hi_lo(y, h, l);
-          const size_t base = (((size_t)(m >> 3) * (F / 8) + (n >> 3)) * 16 + (m & 7)) * 8 + (n & 7);
-          a.y_apack[base] = (uint16_t)h;
-          a.y_apack[base + 64] = (uint16_t)l;
-        }
-      } else if (EPI == EPI_QKV) {
-        // tile = (head, sub): columns c < 8 are dims sub*8 + c, c >= 8 the
-        // RoPE partners 64 + sub*8 + c - 8
-        if (cl >= 8) continue;
-        const int Hq = a.n_heads, Hkv = a.n_kv_heads;
-        const int head = tile >> 3, sub = tile & 7;
-        const int i2 = sub * 8 + cl;
-        const int r1 = head * kHeadDim + i2, r2 = r1 + 64;
-        float x1 = v, x2 = stage[r * 33 + cc + 8];
-        if (a.bias) {
-          x1 += bf16_to_f32(a.bias[r1]);
-          x2 += bf16_to_f32(a.bias[r2]);
-        }
-        if (head < Hq + Hkv) {
-          const float2 cs = a.rope[(size_t)m * 64 + i2];
-          const float y1 = x1 * cs.x - x2 * cs.y;
-          const float y2 = x2 * cs.x + x1 * cs.y;
-          x1 = y1;
-          x2 = y2;
-        }
-        if (head < Hq) {
-          a.y[(size_t)m * a.ldy + r1] = x1;
-          a.y[(size_t)m * a.ldy + r2] = x2;
-          continue;
-        }
-        if (a.flags && a.flags[m] != 0) continue;
-        const int b = m / a.W, jw = m - b * a.W;
-        const int pos = a.prefix_len[b] + jw;
-        if (pos < 0 || pos >= a.max_blocks * kBlock) continue;
-        const int blk = a.block_table[(size_t)b * a.max_blocks + pos / kBlock];
-        if (blk < 0 || blk >= a.num_blocks) continue;
-        const int slot = pos % kBlock;
-        if (head < Hq + Hkv) {
-          uint16_t* kp = a.kc + (((size_t)blk * Hkv + (head - Hq)) * kBlock + slot) * kHeadDim;
-          kp[i2] = (uint16_t)f32_to_bf16_rne(x1);
-          kp[i2 + 64] = (uint16_t)f32_to_bf16_rne(x2);
-        } else {
-          uint16_t* vp = a.vc + ((size_t)blk * Hkv + (head - Hq - Hkv)) * kHeadDim * kBlock;
-          vp[(size_t)i2 * kBlock + slot] = (uint16_t)f32_to_bf16_rne(x1);
-          vp[(size_t)(i2 + 64) * kBlock + slot] = (uint16_t)f32_to_bf16_rne(x2);
-        }
       }
     }
   };
+  // parts in straight-line order, so each reads only its own accumulators
+  // (a rolled loop over parts makes the compiler copy all of them out first)
   auto epilogue = [&](int cblock) {
-    for (int part = 0; part < NPART; ++part) {
-      switch (part) {  // each case stages fixed accumulators
-        case 0: stage_part(std::integral_constant<int, 0>{}); break;
-        case 1: stage_part(std::integral_constant<int, 1 % NPART>{}); break;
-        case 2: stage_part(std::integral_constant<int, 2 % NPART>{}); break;
-        default: stage_part(std::integral_constant<int, 3 % NPART>{}); break;
-      }
-      epi_part(cblock, part);
-    }
+    static_for<NP>([&](auto pc) {
+      stage_part(pc);
+      epi_part(cblock, decltype(pc)::value);
+      __builtin_amdgcn_sched_barrier(0);  // one part's temporaries live at a time
+    });
   };
 
-  // the weight ring: stage bi is multiplied while stages bi+1 .. bi+D-1 are in
-  // flight; one barrier per stage pairs the consumers with the producer.  An
-  // item is a whole number of ring turns, so its epilogue has one site.
+  if (total > 0) {
+    // Stage bi: wait for my copies of the unit read next, barrier, then the
+    // products of stage bi with the next unit's fragment reads (PREFETCH),
+    // the copies of a later unit and the weights of stage bi + DW issued
+    // among them.  The copies of stage bi + LA (+ 1 with PREFETCH) go to
+    // the slot whose reads completed before this barrier.
+    Pos cpos{0, 0, 0}, wpos{0, 0, 0};
+    int rslot = 0;  // slot of stage bi
+    // ---- prologue: DW stages' loads in the loop's pattern (a stage with no
+    // copy due repeats stage 0's: same bytes to the same place)
+    constexpr int CLEAD = C::PREFETCH ? LA + 1 : LA;  // copies of stage s + CLEAD at stage s
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j) issue(j, st[j]);
-  __builtin_amdgcn_sched_barrier(0);
-  stage_barrier();
-  for (int it = 0; it < n_my; ++it) {
-    for (int u0 = 0; u0 < nup; u0 += D) {
-      const int bb = it * nup + u0;
-#pragma unroll
-      for (int j = 0; j < D; ++j) {
-        const int bi = bb + j;
-        issue(bi + D - 1, st[(j + D - 1) % D]);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st[j], slot_of(bi));
-        stage_barrier();
+    for (int s = -DW; s < 0; ++s) {
+      if (s + CLEAD >= 0) {
+        copy_stage(cpos);
+        step(cpos);
+      } else {
+        copy_stage(Pos{0, 0, 0});
       }
+      issue_w(wpos, st[s + DW]);
+      step(wpos);
     }
-    epilogue(cblock_of(it * nup));
+    // copy streams still owed before stage 0 (a lead beyond DW stages)
+#pragma unroll
+    for (int s = DW; s < CLEAD; ++s) {
+      copy_stage(cpos);
+      step(cpos);
+    }
+    bf16x8 af[2][FR];  // PREFETCH: fragments of the current and the next stage
+    if (C::PREFETCH) {
+      wait_vmcnt<C::WAIT0>();
+      stage_barrier();
+      read_frags(frag_base(0), 0, af[0]);
+    }
+
+    for (int it = 0; it < n_my; ++it) {
+      for (int u0 = 0; u0 < nup; u0 += C::R) {
+#pragma unroll
+        for (int j = 0; j < C::R; ++j) {
+          wait_vmcnt<C::WAIT>();
+          stage_barrier();
+          const int nslot = rslot + 1 == NS ? 0 : rslot + 1;
+          if (C::PREFETCH) read_frags(frag_base(nslot), 0, af[(j + 1) & 1]);
+          copy_stage(cpos);
+          step(cpos);
+          issue_w(wpos, st[(j + DW) % C::R]);
+          step(wpos);
+          if (C::PREFETCH) {
+            compute_bf16(st[j], af[j & 1]);
+            // one lone wave per SIMD: spread the stage's other instructions
+            // between the products so they issue in the matrix core's shadow
+#pragma unroll
+            for (int k = 0; k < 2 * RT * CT; ++k) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an LDS read
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a global load
+              __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);  // scalar work
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // vector work
+            }
+          } else {
+            compute_int4(rslot, st[j]);
+          }
+          rslot = nslot;
+        }
+      }
+      epilogue(cb0 + it * gt);
+    }
   }
-  __syncthreads();  // pairs with the producers' last barrier
+
   if (EPI == EPI_ARGMAX) {
-    // merge the column waves' row states (fixed order) and write one partial
-    // per row and workgroup
+    // merge the two column waves' row states (fixed order) and write one
+    // partial per row and workgroup (a workgroup without items writes -inf)
+    __syncthreads();
     if (cw == 0) {
-      for (int r = lane; r < RT * 8; r += 64) {
-        const int ml = (rw * RT) * 8 + r;
+      for (int r = lane; r < NP * 8; r += 64) {
+        const int ml = (rw * NP) * 8 + r;
         float v1 = -INFINITY, v2 = -INFINITY;
         int i1 = 0x7FFFFFFF;
-        for (int w = 0; w < CW; ++w) {
-          const float* s3 = amax_lds + ((size_t)(rw * CW + w) * RT * 8 + r) * 3;
+        for (int w = 0; w < 2; ++w) {
+          const float* s3 = amax_lds + ((size_t)(rw * 2 + w) * NP * 8 + r) * 3;
           top2_merge(v1, i1, v2, s3[0], __float_as_int(s3[1]), s3[2]);
         }
         if (ml < rows) {
@@ -441,6 +584,53 @@ __global__ __launch_bounds__((RW * kBigMaxCW + kBigProducers) * 64) void k_gemm_
         }
       }
     }
+  }
+}
+
+// QKV from K-slice partial sums: bias, RoPE, q rows to y, window K/V (bf16)
+// into the cache pages.  One workgroup per row and head, lane i2 < 64 takes the
+// RoPE pair (i2, i2 + 64).
+__global__ __launch_bounds__(64) void k_qkv_finish(GemmArgs a) {
+  const int m = blockIdx.x, head = blockIdx.y, i2 = threadIdx.x;
+  const int Hq = a.n_heads, Hkv = a.n_kv_heads;
+  const int r1 = head * kHeadDim + i2, r2 = r1 + 64;
+  float x1 = 0.f, x2 = 0.f;
+  for (int s = 0; s < a.ksplit; ++s) {
+    const float* p = a.partial + ((size_t)s * a.M + m) * a.N;
+    x1 += p[r1];
+    x2 += p[r2];
+  }
+  if (a.bias) {
+    x1 += bf16_to_f32(a.bias[r1]);
+    x2 += bf16_to_f32(a.bias[r2]);
+  }
+  if (head < Hq + Hkv) {
+    const float2 cs = a.rope[(size_t)m * 64 + i2];
+    const float y1 = x1 * cs.x - x2 * cs.y;
+    const float y2 = x2 * cs.x + x1 * cs.y;
+    x1 = y1;
+    x2 = y2;
+  }
+  if (head < Hq) {
+    a.y[(size_t)m * a.ldy + r1] = x1;
+    a.y[(size_t)m * a.ldy + r2] = x2;
+    return;
+  }
+  if (a.flags && a.flags[m] != 0) return;
+  const int b = m / a.W, jw = m - b * a.W;
+  const int pos = a.prefix_len[b] + jw;
+  if (pos < 0 || pos >= a.max_blocks * kBlock) return;
+  const int blk = a.block_table[(size_t)b * a.max_blocks + pos / kBlock];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  const int slot = pos % kBlock;
+  if (head < Hq + Hkv) {
+    uint16_t* kp = a.kc + (((size_t)blk * Hkv + (head - Hq)) * kBlock + slot) * kHeadDim;
+    kp[i2] = (uint16_t)f32_to_bf16_rne(x1);
+    kp[i2 + 64] = (uint16_t)f32_to_bf16_rne(x2);
+  } else {
+    uint16_t* vp = a.vc + ((size_t)blk * Hkv + (head - Hq - Hkv)) * kHeadDim * kBlock;
+    vp[(size_t)i2 * kBlock + slot] = (uint16_t)f32_to_bf16_rne(x1);
+    vp[(size_t)(i2 + 64) * kBlock + slot] = (uint16_t)f32_to_bf16_rne(x2);
   }
 }
 
@@ -459,14 +649,15 @@ static int big_cus() {
   return n;
 }
 
-static size_t big_smem(const BigPlan& p, bool int4, int epi) {
-  const size_t waves = (size_t)p.rw * p.cw;
-  return (size_t)kBigSlots * big_slot_bytes(p.rt * p.rw, int4) + waves * 3 * 8 * 33 * 4 +
-         (epi == EPI_ARGMAX ? waves * p.rt * 8 * 3 * 4 : 0);
+template <int RT, bool INT4>
+static constexpr size_t wide_smem(int epi) {
+  using C = Wide<RT, INT4>;
+  return (size_t)C::NS * C::SLOT + (size_t)kWideWaves * 8 * (kItemTiles / 2 * 16 + 4) * 4 +
+         (epi == EPI_ARGMAX ? (size_t)kWideWaves * C::NP * 8 * 3 * 4 : 0);
 }
 
-// Rows per launch: 192 (bf16) or 48 (INT4).
-int big_rows_per_launch(bool int4) { return int4 ? 48 : 192; }
+// Rows per launch: 192 (bf16) or 64 (INT4).
+int big_rows_per_launch(bool int4) { return int4 ? 64 : 192; }
 
 // The large-M kernel serves every M > 32 rows.
 bool use_big_gemm(int M, int K, bool int4) {
@@ -475,106 +666,106 @@ bool use_big_gemm(int M, int K, bool int4) {
   return M > 32;
 }
 
+// Row tiles per row wave for a launch of `rows` rows: INT4 4 tiles of 16
+// operand rows (64 rows); bf16 tiles of 32 operand rows (16 real rows).
+static int big_rt(int rows, bool int4) {
+  const int mt = (rows + 7) / 8;
+  if (int4) return 4;
+  return mt <= 8 ? 2 : mt <= 12 ? 3 : 6;
+}
+
 BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_split) {
   BigPlan p;
+  p.rt = big_rt(rows, int4);
+  p.ct = int4 ? 4 : 2;
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
-  const int mt = (rows + 7) / 8;
-  if (int4) {
-    p.rt = 6;
-    p.rw = 1;
-  } else if (mt <= 6) {
-    p.rt = 6;
-    p.rw = 1;
-  } else if (mt <= 12) {
-    p.rt = 12;
-    p.rw = 1;
-  } else {
-    p.rt = 12;
-    p.rw = 2;
-  }
+  const int n_cb = (p.n_tiles + kItemTiles - 1) / kItemTiles;
   const int cus = big_cus();
   const int units = int4 ? K / 128 : K / 32;
-  // column-pair waves per row of waves and K slices: the fewest rounds of
-  // column blocks times the work of one block (columns x units of its slice);
-  // on a tie the wider block, which reuses each activation unit for more
-  // columns
-  double best = 1e30;
-  p.cw = 1;
+  const int dw = int4 ? Wide<4, true>::R : Wide<6, false>::R;  // stages per ring turn
+  // K slices (QKV always writes slice sums; STORE when the caller takes them):
+  // the fewest rounds of items times the padded stages of one item, plus the
+  // slice sums' write and read-back counted in stage times (about 0.35 us a
+  // stage of 192 rows; slice traffic at about 3 TB/s); on a tie the fewer
+  // slices
+  const bool can_split = epi == EPI_QKV || (allow_split && epi == EPI_STORE);
+  const double stage_us = 0.35 * std::max(rows, 32) / 192.0;
+  const double slice_stages = (double)rows * N * 8 / 3e6 / stage_us;
+  double best = -1;
   p.ksplit = 1;
-  for (int cw = 1; cw <= kBigMaxCW; ++cw) {
-    const int n_cb = (p.n_tiles + 2 * cw - 1) / (2 * cw);
-    for (int ks = 1; ks <= 16; ks *= 2) {
-      if (ks > 1 && !(allow_split && epi == EPI_STORE)) break;
-      if (ks > 1 && units / ks < 8) break;
-      const int per_slice = cus / ks > 0 ? cus / ks : 1;
-      const int rounds = (n_cb + per_slice - 1) / per_slice;
-      // partial sums cost a write and a read of the output per slice
-      const double cost = (double)rounds * cw * ((units + ks - 1) / ks) * (1.0 + 0.02 * (ks - 1));
-      if (cost < best - 1e-9 || (cost < best + 1e-9 && cw > p.cw)) {
-        best = cost;
-        p.cw = cw;
-        p.ksplit = ks;
-      }
+  for (int ks = 1; ks <= (can_split ? 16 : 1); ++ks) {
+    if (ks > 1 && units / ks < 4) break;
+    const long items = (long)n_cb * ks;
+    const long rounds = (items + cus - 1) / cus;
+    const int per = (units + ks - 1) / ks;
+    const double cost = (double)rounds * ((per + dw - 1) / dw * dw) + (ks > 1 ? ks * slice_stages : 0.0);
+    if (best < 0 || cost < best - 1e-9) {
+      best = cost;
+      p.ksplit = ks;
     }
   }
-  const int n_cb = (p.n_tiles + 2 * p.cw - 1) / (2 * p.cw);
-  const int per_slice = cus / p.ksplit > 0 ? cus / p.ksplit : 1;
+  const int per_slice = std::max(1, cus / p.ksplit);
   const int per = (n_cb + per_slice - 1) / per_slice;
   const int gt = (n_cb + per - 1) / per;
   p.grid = gt * p.ksplit;
-  p.threads = (p.rw * p.cw + kBigProducers) * 64;
-  p.smem = big_smem(p, int4, epi);
+  p.threads = kWideWaves * 64;
+  p.smem = int4 ? wide_smem<4, true>(epi)
+                : (p.rt == 2 ? wide_smem<2, false>(epi) : p.rt == 3 ? wide_smem<3, false>(epi) : wide_smem<6, false>(epi));
   return p;
 }
 
-template <int RT, int RW, bool INT4, int EPI>
+template <int RT, bool INT4, int EPI>
 static hipError_t launch_big_one(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<RT, RW, INT4, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<RT, INT4, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_gemm_big<RT, RW, INT4, EPI>), dim3(p.grid), dim3(p.threads), p.smem, s, a);
+  hipLaunchKernelGGL((k_gemm_big<RT, INT4, EPI>), dim3(p.grid), dim3(p.threads), p.smem, s, a);
   return hipGetLastError();
 }
 
-template <int RT, int RW, bool INT4>
+template <int RT, bool INT4>
 static hipError_t launch_big_epi(const GemmArgs& a, int epi, const BigPlan& p, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_big_one<RT, RW, INT4, EPI_STORE>(a, p, s);
-    case EPI_SILU: return launch_big_one<RT, RW, INT4, EPI_SILU>(a, p, s);
-    case EPI_QKV: return launch_big_one<RT, RW, INT4, EPI_QKV>(a, p, s);
-    default: return launch_big_one<RT, RW, INT4, EPI_ARGMAX>(a, p, s);
+    case EPI_STORE: return launch_big_one<RT, INT4, EPI_STORE>(a, p, s);
+    case EPI_SILU: return launch_big_one<RT, INT4, EPI_SILU>(a, p, s);
+    case EPI_QKV: return launch_big_one<RT, INT4, EPI_QKV>(a, p, s);
+    default: return launch_big_one<RT, INT4, EPI_ARGMAX>(a, p, s);
   }
 }
 
 hipError_t launch_gemm_big(GemmArgs a, int epi, bool int4, hipStream_t s) {
+  // QKV writes K-slice sums and a finishing kernel does bias, RoPE and the
+  // cache writes; its caller provides the slice buffer
+  if (epi == EPI_QKV && !a.partial) return hipErrorInvalidValue;
+  if (a.y_apack && epi == EPI_STORE) return hipErrorInvalidValue;  // fused RMSNorm: small M only
+  if (a.ss_in) return hipErrorInvalidValue;
   const int per_launch = big_rows_per_launch(int4);
-  const BigPlan p0 = plan_gemm_big(std::min(a.M, per_launch), a.N, a.K, int4, epi, a.partial != nullptr);
+  // one plan for every launch (the slice sums and the lm_head parts are laid
+  // out by it); a shorter last launch pads its row tiles
+  const BigPlan p = plan_gemm_big(std::min(a.M, per_launch), a.N, a.K, int4, epi, a.partial != nullptr);
   for (int m0 = 0; m0 < a.M; m0 += per_launch) {
-    const int rows = std::min(a.M - m0, per_launch);
-    BigPlan p = plan_gemm_big(rows, a.N, a.K, int4, epi, a.partial != nullptr);
-    // one plan of K slices and workgroups for every launch (the partial sums
-    // and the lm_head parts are laid out by the first)
-    p.ksplit = p0.ksplit;
-    p.cw = p0.cw;
-    p.grid = p0.grid;
-    p.threads = (p.rw * p.cw + kBigProducers) * 64;
-    p.smem = big_smem(p, int4, epi);
     GemmArgs g = a;
     g.m_base = m0;
     g.n_tiles = p.n_tiles;
     g.ksplit = p.ksplit;
-    g.nw = p.cw;
     g.n_parts = p.grid;
     hipError_t e;
-    if (int4) e = launch_big_epi<6, 1, true>(g, epi, p, s);
-    else if (p.rt == 6) e = launch_big_epi<6, 1, false>(g, epi, p, s);
-    else if (p.rw == 1) e = launch_big_epi<12, 1, false>(g, epi, p, s);
-    else e = launch_big_epi<12, 2, false>(g, epi, p, s);
+    if (int4) e = launch_big_epi<4, true>(g, epi, p, s);
+    else if (p.rt == 2) e = launch_big_epi<2, false>(g, epi, p, s);
+    else if (p.rt == 3) e = launch_big_epi<3, false>(g, epi, p, s);
+    else e = launch_big_epi<6, false>(g, epi, p, s);
     if (e != hipSuccess) return e;
+  }
+  if (epi == EPI_QKV) {
+    GemmArgs g = a;
+    g.ksplit = p.ksplit;
+    const int heads = a.n_heads + 2 * a.n_kv_heads;
+    hipLaunchKernelGGL(k_qkv_finish, dim3(a.M, heads), dim3(64), 0, s, g);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

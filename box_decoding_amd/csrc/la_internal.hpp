@@ -130,10 +130,11 @@ hipError_t launch_argmax_reduce(const float* amax, int M, int n_tiles, const int
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // Large-M GEMMs (more than 32 rows): every weight fragment meets all rows of a
-// launch (up to 192 bf16 / 48 INT4 rows) while it is in registers.
+// launch (up to 192 bf16 / 64 INT4 rows) while it is in registers.  QKV goes
+// through K-slice sums in `partial` and a finishing kernel.
 struct BigPlan {
   int n_tiles;
-  int rt, rw, cw;  // row tiles per consumer wave, rows and columns of consumer waves
+  int rt, ct;  // row tiles (per row wave) and column tiles (per column wave)
   int ksplit;
   int grid, threads;
   size_t smem;
