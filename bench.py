@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 CAL_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic_step_b1_p1280.json")
 METRIC = "PBD window steps/sec (≈boxes/sec) at batch 1 and 32; achieved HBM GB/s vs peak"
@@ -174,6 +175,60 @@ def cpu_baseline(workload_name, sample_layers, min_seconds=10.0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
+    """Steps/s of the batched step (32 ragged sequences, same model) and the
+    useful matrix-core rate of its gate/up GEMM (192 rows), against the dense
+    bf16 peak.  The kernel splits activations into bf16 hi + lo halves, so the
+    matrix cores do twice the useful work."""
+    w = synth.WORKLOADS["step_b32_ragged"]
+    d = w.dims
+    log("bench: batch-32 leg")
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    max_len = int(P.max()) + w.window
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
+    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
+    for _ in range(max(2, args.warmup)):
+        graph.replay()
+    steps = max(5, args.steps // 3)
+    ms_step, _ = timed(graph.replay, steps)
+    sbytes = step_bytes(model, d, P, w.window)
+    T = w.batch * w.window
+    F, H = d.inter, d.hidden
+    xin = torch.randn((T, H), device=dev, generator=torch.Generator(device=dev).manual_seed(1))
+    packed = B.pack_rows(xin, w.wfmt, norm_gain=model["layers"][0]["post_norm"])
+    yout = torch.empty((T, F), dtype=torch.float32, device=dev)
+    for l in range(3):
+        B.wgemm_packed(packed, T, model["layers"][l]["gate_up"], silu_gate=True, out=yout)
+    reps = max(8, args.kernel_reps // 4)
+
+    def gemm():
+        for r in range(reps):
+            B.wgemm_packed(packed, T, model["layers"][r % d.n_layers]["gate_up"], silu_gate=True, out=yout)
+
+    k_ms = timed(gemm, 1)[0] / reps
+    flops = 2.0 * T * H * 2 * F
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    log(f"bench: batch 32: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; "
+        f"gate_up GEMM {k_ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s useful")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": w.name, "batch": w.batch, "window": w.window, "steps": steps,
+            "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
+            "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
+            "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
+            "gate_up_gemm": {"rows": T, "launch_us": round(k_ms * 1e3, 2),
+                             "useful_tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "matrix_core_frac_with_hi_lo": round(2 * tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +239,8 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
+    ap.add_argument("--no-batch32", action="store_true",
+                    help="skip the batch-32 leg reported beside the batch-1 step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 --pmc runs of this script into the traffic file")
     args = ap.parse_args()
@@ -317,6 +374,11 @@ def main():
                      "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes},
     }
+    if args.workload == "step_b1_p1280" and not args.no_batch32 and not args.row_major:
+        # the metric's second batch size: the same model, 32 ragged sequences
+        del cache, dc
+        torch.cuda.synchronize()
+        result["batch32"] = batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)
