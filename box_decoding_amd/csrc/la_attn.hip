@@ -38,14 +38,30 @@ struct PageRegs {
   s16x4 v[8];
 };
 
-__device__ __forceinline__ void load_page(const AttnArgs& a, int blk, int kvh, PageRegs& pg) {
+// A page in LDS: K [16 keys][128 dims] with the 16-byte chunks of key k
+// rotated by XOR with k (so the 16 lanes that read one chunk of 16 different
+// keys hit 16 different bank groups), then V^T [128 dims][16 keys] as stored.
+constexpr int kPageBytes = 2 * kBlock * kHeadDim * 2;  // 8 KB
+
+// Piece q (0..7, 1 KB each) of a page: the 16-byte granule lane l writes in
+// LDS (q * 64 + l) and where it comes from in the cache page.
+__device__ __forceinline__ uint32_t page_piece_src(int q, int lane) {
+  const int p = (q & 3) * 64 + lane;  // granule within the K or V half
+  if (q < 4) {
+    const int k = p >> 4, cch = (p & 15) ^ (k & 15);
+    return (uint32_t)(k * 256 + cch * 16);
+  }
+  return (uint32_t)p * 16;
+}
+
+__device__ __forceinline__ void read_page(const unsigned char* pg_lds, PageRegs& pg) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-  const uint16_t* Kp = a.kc + ((size_t)blk * a.Hkv + kvh) * kBlock * kHeadDim;
-  const uint16_t* Vp = a.vc + ((size_t)blk * a.Hkv + kvh) * kHeadDim * kBlock;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) pg.k[kb] = *(const bf16x8*)(Kp + r * kHeadDim + kb * 32 + g * 8);
+  for (int kb = 0; kb < 4; ++kb)
+    pg.k[kb] = *(const bf16x8*)(pg_lds + r * 256 + (((kb * 4 + g) ^ r) * 16));
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) pg.v[dt] = *(const s16x4*)(Vp + (dt * 16 + r) * kBlock + 4 * g);
+  for (int dt = 0; dt < 8; ++dt)
+    pg.v[dt] = *(const s16x4*)(pg_lds + 4096 + (dt * 16 + r) * 32 + g * 8);
 }
 
 // Running state of one wave: online-softmax max and sum of its 16 query
@@ -126,13 +142,18 @@ __device__ __forceinline__ void attn_store8(const AttnArgs& a, int b, int kvh, i
 }
 
 // One workgroup per (run of pages_per_split pages, KV head, sequence); wave qt
-// takes query tile qt.  Every load the run needs is issued before any result
-// is waited for: the block ids of all its pages (one per lane), the wave's Q
-// fragments (kept in registers), then the pages two at a time.  With a single
-// run per sequence the result is normalised and stored here; otherwise
-// (max, sum, unnormalised O) goes to the run's partial slot.
-template <int NQT>
+// takes query tile qt.  The run's pages stream through a ring of LA + 1 LDS
+// page slots with direct-to-LDS loads, LA pages ahead; each wave copies a
+// share of every page (8 pieces of 1 KB) and the waves meet at one barrier
+// per page, after which that page is complete and the slot being refilled
+// has been read by everybody.  With a single run per sequence the result is
+// normalised and stored here; otherwise (max, sum, unnormalised O) goes to
+// the run's partial slot.
+template <int NQT, int LA>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
+  constexpr int NSP = LA + 1;
+  constexpr int PPW = (8 + NQT - 1) / NQT;  // pieces per wave and page
+  __shared__ __align__(16) unsigned char ring[NSP * kPageBytes];
   const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int qt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -188,20 +209,43 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   const int npages = (k1 - k0 + kBlock - 1) / kBlock;  // 1 .. pages_per_split (<= 64)
   bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
 
+  // copies: this wave's pieces of page c (a page past the run repeats the
+  // last one into a slot nobody reads before it is refilled)
+  const uint32_t cache_bytes = (uint32_t)a.num_blocks * a.Hkv * (kPageBytes / 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc, cache_bytes);
+  uint32_t psrc[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) psrc[i] = page_piece_src(min(qt + NQT * i, 7), lane);
+  auto copy_page = [&](int c) {
+    const int blk = __builtin_amdgcn_readlane(bt, min(c, npages - 1));
+    const uint32_t base = ((uint32_t)blk * a.Hkv + kvh) * (kPageBytes / 2);
+    unsigned char* slot = ring + (c % NSP) * kPageBytes;
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int q = min(qt + NQT * i, 7);
+      if (q < 4) lds_copy16(rk, psrc[i], base, slot + q * 1024);
+      else lds_copy16(rv, psrc[i], base, slot + q * 1024);
+    }
+  };
+
   AttnState st;
   st.m = -INFINITY;
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < npages; c += 2) {
-    // both pages of the pair in flight at once (the second clamped to a real
-    // page, so the load is unconditional)
-    PageRegs p0, p1;
-    load_page(a, __builtin_amdgcn_readlane(bt, c), kvh, p0);
-    load_page(a, __builtin_amdgcn_readlane(bt, min(c + 1, npages - 1)), kvh, p1);
-    const int key = k0 + c * kBlock;
-    attn_page(p0, k1 - key, qh, ql, st);
-    if (c + 1 < npages) attn_page(p1, k1 - key - kBlock, qh, ql, st);
+#pragma unroll
+  for (int c = 0; c < LA; ++c) copy_page(c);
+  for (int c = 0; c < npages; ++c) {
+    wait_vmcnt<(LA - 1) * PPW>();  // my pieces of page c (LA - 1 pages' pieces follow them)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): my reads of page c - 1 are done
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    copy_page(c + LA);  // into the slot of page c - 1
+    PageRegs pg;
+    read_page(ring + (c % NSP) * kPageBytes, pg);
+    attn_page(pg, k1 - (k0 + c * kBlock), qh, ql, st);
   }
   float lsum = st.l;
   lsum += __shfl_xor(lsum, 16);
@@ -221,16 +265,18 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       }
       if (qi < NQ && (g & 1) == 0) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, v);
     }
-    return;
-  }
-  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.max_splits + split;
-  if (g == 0) {
-    float2* ml = (float2*)a.part_ml + unit * a.nqp + qi;
-    *ml = make_float2(st.m, lsum);
-  }
-  float* po = a.part_o + (unit * a.nqp + qi) * kHeadDim + 4 * g;
+  } else {
+    const size_t unit = ((size_t)b * a.Hkv + kvh) * a.max_splits + split;
+    if (g == 0) {
+      float2* ml = (float2*)a.part_ml + unit * a.nqp + qi;
+      *ml = make_float2(st.m, lsum);
+    }
+    float* po = a.part_o + (unit * a.nqp + qi) * kHeadDim + 4 * g;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = st.acc[dt];
+    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = st.acc[dt];
+  }
+  // copies still in flight land in LDS this workgroup owns until it ends
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Merge of the runs.  A workgroup of 256 threads takes one query column of a
@@ -240,7 +286,6 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 // result does not depend on timing.  Combination is the usual log-sum-exp
 // rescaling of (max, sum, unnormalised O).
 constexpr int kMergeGroups = 8;
-constexpr int kMergeBatch = 8;
 
 struct MergeAcc {
   float m, den;
@@ -271,7 +316,12 @@ __device__ __forceinline__ MergeAcc shfl_xor_acc(const MergeAcc& x, int mask) {
   return r;
 }
 
+// MB: runs per group loaded at once (the host picks the smallest power of two
+// with MB * kMergeGroups >= max_splits, so no group loads clamped duplicates
+// beyond its last batch).
+template <int MB>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int kMergeBatch = MB;
   const int qi = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 3;                              // run group
@@ -339,19 +389,33 @@ void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_
   *max_splits = (max_pages + pps - 1) / pps;
 }
 
+template <int NQT>
+static void launch_split(const AttnArgs& a, bool deep, dim3 grid, dim3 block, hipStream_t s) {
+  if (deep) hipLaunchKernelGGL((k_attn_split<NQT, 7>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_attn_split<NQT, 2>), grid, block, 0, s, a);
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int nqt = a.nqp / 16;
   const dim3 grid(a.max_splits, a.Hkv, a.B), block(nqt * 64);
+  // a deep page ring for long runs, a short one for the two-page runs of
+  // short sequences
+  const bool deep = a.pages_per_split > 2;
   switch (nqt) {
-    case 1: hipLaunchKernelGGL(k_attn_split<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_attn_split<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(k_attn_split<3>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(k_attn_split<4>, grid, block, 0, s, a); break;
+    case 1: launch_split<1>(a, deep, grid, block, s); break;
+    case 2: launch_split<2>(a, deep, grid, block, s); break;
+    case 3: launch_split<3>(a, deep, grid, block, s); break;
+    default: launch_split<4>(a, deep, grid, block, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   const int NQ = a.W * (a.Hq / a.Hkv);
-  hipLaunchKernelGGL(k_attn_merge, dim3(NQ, a.Hkv, a.B), dim3(256), 0, s, a);
+  const dim3 mgrid(NQ, a.Hkv, a.B);
+  const int per_group = (a.max_splits + kMergeGroups - 1) / kMergeGroups;
+  if (per_group <= 1) hipLaunchKernelGGL(k_attn_merge<1>, mgrid, dim3(256), 0, s, a);
+  else if (per_group <= 2) hipLaunchKernelGGL(k_attn_merge<2>, mgrid, dim3(256), 0, s, a);
+  else if (per_group <= 4) hipLaunchKernelGGL(k_attn_merge<4>, mgrid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_attn_merge<8>, mgrid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

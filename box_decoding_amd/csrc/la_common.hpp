@@ -46,6 +46,42 @@ __device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo)
   lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
 }
 
+// ---------------------------------------------------------------- buffer loads
+
+// Buffer loads: an offset at or past the end of the resource reads zero and
+// touches no memory, which masks a unit without a branch.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kCfgDword = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;        // cache policy: streaming
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kCfgDword);
+}
+
+template <int POLICY>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
+// Direct-to-LDS copies through a buffer resource: lane l's bytes at voff +
+// soff land at lds_dst + l * size.  (The buffer form keeps these loads in the
+// same in-order class as the weight loads, so the compiler's waits on the
+// weights stay exact.)  The LDS address-space cast lives here, in device-only
+// code.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------- matrix cores
 
 // D[16x16] += A[16x32] . B[32x16]; lane l holds A row l%16, B column l%16 and

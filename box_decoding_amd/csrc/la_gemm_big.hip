@@ -67,24 +67,6 @@ struct Wide {
   static_assert(CT * (INT4 ? 16 : 32) * 2 == kItemTiles * 16, "item shape");
 };
 
-// Direct-to-LDS copies through a buffer resource: lane l's bytes at voff +
-// soff land at lds_dst + l * size.  (The buffer form keeps these loads in the
-// same in-order class as the weight loads, so the compiler's waits on the
-// weights stay exact.)
-__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 4, voff, soff, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) with the other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // The per-stage meeting point: this wave's LDS reads are complete, then the
 // hardware barrier.  Unlike __syncthreads it does not wait for the copies in
 // flight (each wave waits for exactly its own before arriving).

@@ -72,21 +72,6 @@ __device__ __forceinline__ WPtr wptr(const GemmArgs& a, int tile) {
   return p;
 }
 
-// Buffer loads: an offset at or past the end of the resource reads zero and
-// touches no memory, which masks a unit without a branch.
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kCfgDword = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kNonTemporal = 2;        // cache policy: streaming
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kCfgDword);
-}
-
-template <int POLICY>
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
-}
-
 // Running top-2 of a row: (v1, i1) the best value and its column (lowest index
 // on ties), v2 the second best value.
 struct Top2 {
