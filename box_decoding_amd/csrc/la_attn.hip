@@ -11,11 +11,13 @@
 // W window rows form up to 64 query columns that share every K/V page:
 //   S^T[key, query] = K_page . Q^T        16x16x32 bf16 matrix-core steps, Q split
 //                                         into bf16 hi + lo columns (K is exact bf16)
-//   online softmax per query column       exp2 on pre-scaled scores, one max per page
-//   O^T[d, query] += V_page^T . P^T       16x16x16 steps; P split into hi + lo; the
-//                                         S^T accumulator layout is exactly the P^T
-//                                         operand layout, so P never leaves registers
-// V pages are stored dim-major ([D][16 keys]) so a V^T operand fragment is one
+//   online softmax per query column       exp2 on pre-scaled scores, a reference max
+//                                         that moves only when a score passes it by 2^8
+//   O^T[d, query] += V_pair^T . P^T       16x16x32 steps over the 32 keys of two
+//                                         pages; P split into hi + lo; the two pages'
+//                                         S^T accumulators are exactly the P^T
+//                                         operand, so P never leaves registers
+// V pages are stored dim-major ([D][16 keys]) so a V^T operand half is one
 // 8-byte load.  The step is latency bound (a layer reads about a megabyte of KV
 // at batch 1), so a run is short and issues all of its loads before it waits.
 // Each run writes (max, sum, unnormalised O); a merge kernel combines the runs
@@ -32,16 +34,11 @@ __device__ __forceinline__ int attn_keys(const AttnArgs& a, int b) {
   return n;
 }
 
-// K and V of one page for this lane: K rows are keys, V^T rows are dims.
-struct PageRegs {
-  bf16x8 k[4];
-  s16x4 v[8];
-};
-
 // A page in LDS: K [16 keys][128 dims] with the 16-byte chunks of key k
 // rotated by XOR with k (so the 16 lanes that read one chunk of 16 different
 // keys hit 16 different bank groups), then V^T [128 dims][16 keys] as stored.
 constexpr int kPageBytes = 2 * kBlock * kHeadDim * 2;  // 8 KB
+constexpr int kPairBytes = 2 * kPageBytes;
 
 // Piece q (0..7, 1 KB each) of a page: the 16-byte granule lane l writes in
 // LDS (q * 64 + l) and where it comes from in the cache page.
@@ -54,74 +51,117 @@ __device__ __forceinline__ uint32_t page_piece_src(int q, int lane) {
   return (uint32_t)p * 16;
 }
 
-__device__ __forceinline__ void read_page(const unsigned char* pg_lds, PageRegs& pg) {
+// K of two pages and V^T of both for this lane.  The products run over the 32
+// keys of the pair in one step; key slot 8g + e of lane group g is key 4g + e
+// of the first page for e < 4 and key 4g + e - 4 of the second page for e >= 4,
+// which is where the score accumulators of the two pages leave them.
+struct PairRegs {
+  bf16x8 ka[4], kb[4];
+  s16x4 va[8], vb[8];
+};
+
+__device__ __forceinline__ void read_pair(const unsigned char* pr_lds, PairRegs& pr) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    pg.k[kb] = *(const bf16x8*)(pg_lds + r * 256 + (((kb * 4 + g) ^ r) * 16));
+  for (int kb = 0; kb < 4; ++kb) {
+    const int off = r * 256 + (((kb * 4 + g) ^ r) * 16);
+    pr.ka[kb] = *(const bf16x8*)(pr_lds + off);
+    pr.kb[kb] = *(const bf16x8*)(pr_lds + kPageBytes + off);
+  }
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    pg.v[dt] = *(const s16x4*)(pg_lds + 4096 + (dt * 16 + r) * 32 + g * 8);
+  for (int dt = 0; dt < 8; ++dt) {
+    const int off = 4096 + (dt * 16 + r) * 32 + g * 8;
+    pr.va[dt] = *(const s16x4*)(pr_lds + off);
+    pr.vb[dt] = *(const s16x4*)(pr_lds + kPageBytes + off);
+  }
 }
 
-// Running state of one wave: online-softmax max and sum of its 16 query
-// columns and the unnormalised O^T tile (dims x queries).
+// Running state of one wave: online-softmax reference max and sum of its 16
+// query columns and the unnormalised O^T tile (dims x queries).
 struct AttnState {
   float m, l;
   f32x4 acc[8];
 };
 
-// One page (keys p0 .. p0+nvalid-1 valid, nvalid >= 1) into the running state.
-__device__ __forceinline__ void attn_page(PageRegs& pg, int nvalid, const bf16x8 (&qh)[4],
+// The reference max moves only when a score exceeds it by more than this
+// (log2 units): exp2 of at most 2^8 stays far inside fp32, and most pages then
+// need no cross-lane max and no rescale.  The result is the same softmax.
+constexpr float kLazyMax = 8.f;
+
+__device__ __forceinline__ bf16x8 cat_s16x4(s16x4 a, s16x4 b) {
+  const uint32_t x0 = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+  const uint32_t x1 = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+  const uint32_t x2 = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+  const uint32_t x3 = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  const u32x4 u = {x0, x1, x2, x3};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// One pair of pages (keys p0 .. p0 + nvalid - 1 valid, nvalid >= 1) into the
+// running state.
+__device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, const bf16x8 (&qh)[4],
                                           const bf16x8 (&ql)[4], AttnState& st) {
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const float sl2 = 0.08838834764831845f * 1.4426950408889634f;  // log2(e) / sqrt(128)
-  if (nvalid < kBlock) {
+  if (nvalid < 2 * kBlock) {
     // keys past the bound: zero their values (unused slots may hold anything)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * g + e >= nvalid) pg.v[dt][e] = 0;
+      for (int e = 0; e < 4; ++e) {
+        if (4 * g + e >= nvalid) pr.va[dt][e] = 0;
+        if (kBlock + 4 * g + e >= nvalid) pr.vb[dt][e] = 0;
+      }
   }
-  f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+  f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = ah, bh = ah, bl = ah;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    sh = mfma_16x16x32(pg.k[kb], qh[kb], sh);
-    sl = mfma_16x16x32(pg.k[kb], ql[kb], sl);
+    ah = mfma_16x16x32(pr.ka[kb], qh[kb], ah);
+    bh = mfma_16x16x32(pr.kb[kb], qh[kb], bh);
+    al = mfma_16x16x32(pr.ka[kb], ql[kb], al);
+    bl = mfma_16x16x32(pr.kb[kb], ql[kb], bl);
   }
-  float sc[4];
+  float sc[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sc[e] = (sh[e] + sl[e]) * sl2;
-    if (4 * g + e >= nvalid) sc[e] = -INFINITY;
+    sc[e] = 4 * g + e < nvalid ? (ah[e] + al[e]) * sl2 : -INFINITY;
+    sc[4 + e] = kBlock + 4 * g + e < nvalid ? (bh[e] + bl[e]) * sl2 : -INFINITY;
   }
-  float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(st.m, mx);
-  const float alpha = exp2f(st.m - mnew);
-  float p[4], ps = 0.f;
+  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazyMax) != 0) {  // uniform over the wave
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);  // 0 while st.m is -inf
+    st.l *= alpha;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    p[e] = exp2f(sc[e] - mnew);
+    for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
+    st.m = mnew;
+  }
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(sc[e] - st.m);
     ps += p[e];
   }
-  st.l = st.l * alpha + ps;
-  st.m = mnew;
-  s16x4 ph, pl;
+  st.l += ps;
+  // P^T operand, bf16 hi (truncated) + lo (the exact remainder, rounded)
+  u32x4 H, L;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t h, l;
-    split_hi_lo(p[e], h, l);
-    ph[e] = (short)h;
-    pl[e] = (short)l;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b0 = __float_as_uint(p[2 * i]), b1 = __float_as_uint(p[2 * i + 1]);
+    const uint32_t h0 = b0 & 0xFFFF0000u, h1 = b1 & 0xFFFF0000u;
+    H[i] = (h0 >> 16) | h1;
+    L[i] = f32_to_bf16_rne(p[2 * i] - __uint_as_float(h0)) |
+           (f32_to_bf16_rne(p[2 * i + 1] - __uint_as_float(h1)) << 16);
   }
+  const bf16x8 ph = __builtin_bit_cast(bf16x8, H), pl = __builtin_bit_cast(bf16x8, L);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    st.acc[dt] *= alpha;
-    st.acc[dt] = mfma_16x16x16(pg.v[dt], ph, st.acc[dt]);
-    st.acc[dt] = mfma_16x16x16(pg.v[dt], pl, st.acc[dt]);
+    const bf16x8 v = cat_s16x4(pr.va[dt], pr.vb[dt]);
+    st.acc[dt] = mfma_16x16x32(v, ph, st.acc[dt]);
+    st.acc[dt] = mfma_16x16x32(v, pl, st.acc[dt]);
   }
 }
 
@@ -142,20 +182,22 @@ __device__ __forceinline__ void attn_store8(const AttnArgs& a, int b, int kvh, i
 }
 
 // One workgroup per (run of pages_per_split pages, KV head, sequence); wave qt
-// takes query tile qt.  The run's pages stream through a ring of LA + 1 LDS
-// page slots with direct-to-LDS loads, LA pages ahead; each wave copies a
-// share of every page (8 pieces of 1 KB) and the waves meet at one barrier
-// per page, after which that page is complete and the slot being refilled
-// has been read by everybody.  With a single run per sequence the result is
+// takes query tile qt.  The run's pages stream in pairs through a ring of
+// LA + 1 LDS pair slots with direct-to-LDS loads, LA pairs ahead; each wave
+// copies a share of every pair (16 pieces of 1 KB) and the waves meet at one
+// barrier per pair, after which that pair is complete and the slot being
+// refilled has been read by everybody.  With a single run per sequence the result is
 // normalised and stored here; otherwise (max, sum, unnormalised O) goes to
 // the run's partial slot.
 template <int NQT, int LA>
-__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LA == 1 && NQT > 1 ? 3 : 1))) void k_attn_split(AttnArgs a) {
   constexpr int NSP = LA + 1;
-  constexpr int PPW = (8 + NQT - 1) / NQT;  // pieces per wave and page
-  __shared__ __align__(16) unsigned char ring[NSP * kPageBytes];
+  constexpr int PPW = (16 + NQT - 1) / NQT;  // pieces per wave and pair
+  __shared__ __align__(16) unsigned char ring[NSP * kPairBytes];
   const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // sequences vary fastest, so the runs that exist (all first runs, then the
+  // second runs of longer sequences, ...) come first in dispatch order
+  const int b = blockIdx.x, split = blockIdx.y, kvh = blockIdx.z;
   const int qt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.Hq / a.Hkv;
   const int NQ = a.W * G;
@@ -170,18 +212,30 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
                          min(first + min(lane, a.pages_per_split - 1), a.max_blocks - 1)];
 
   // Q^T operand of this wave's tile: lane (g, r) holds dims kb*32 + 8g .. +8 of
-  // query column qi as bf16 hi and lo (absent columns: zeros).
-  bf16x8 qh[4], ql[4];
+  // query column qi as bf16 hi and lo (absent columns: zeros).  The loads go
+  // out before the run is known to exist; a run past the sequence leaves
+  // without waiting for them.
+  float4 v[8];
   {
     const int qc = qi < NQ ? qi : 0;
     const int wr = qc / G, hg = qc - wr * G;
     const float* src = a.q + ((size_t)(b * a.W + wr) * a.Hq + kvh * G + hg) * kHeadDim + g * 8;
-    float4 v[8];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       v[2 * kb] = *(const float4*)(src + kb * 32);
       v[2 * kb + 1] = *(const float4*)(src + kb * 32 + 4);
     }
+  }
+  const int n_keys = attn_keys(a, b);
+  if (k0 >= n_keys) {  // uniform over the workgroup
+    if (direct && qi < NQ && (g & 1) == 0) {
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < 8; ++dt) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, z);
+    }
+    return;
+  }
+  bf16x8 qh[4], ql[4];
+  {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const float x[8] = {v[2 * kb].x, v[2 * kb].y, v[2 * kb].z, v[2 * kb].w,
@@ -197,35 +251,30 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       ql[kb] = __builtin_bit_cast(bf16x8, L);
     }
   }
-  const int n_keys = attn_keys(a, b);
-  if (k0 >= n_keys) {  // uniform over the workgroup
-    if (direct && qi < NQ && (g & 1) == 0) {
-      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int dt = 0; dt < 8; ++dt) attn_store8(a, b, kvh, qi, dt * 16 + 4 * g, z);
-    }
-    return;
-  }
   const int k1 = min(n_keys, k0 + kps);
   const int npages = (k1 - k0 + kBlock - 1) / kBlock;  // 1 .. pages_per_split (<= 64)
   bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
 
-  // copies: this wave's pieces of page c (a page past the run repeats the
-  // last one into a slot nobody reads before it is refilled)
+  // copies: this wave's pieces of pair c (a page past the run repeats the
+  // last one into a slot nobody reads before it is refilled, or that only
+  // masked keys read)
+  const int npairs = (npages + 1) >> 1;
   const uint32_t cache_bytes = (uint32_t)a.num_blocks * a.Hkv * (kPageBytes / 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc, cache_bytes);
   uint32_t psrc[PPW];
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) psrc[i] = page_piece_src(min(qt + NQT * i, 7), lane);
-  auto copy_page = [&](int c) {
-    const int blk = __builtin_amdgcn_readlane(bt, min(c, npages - 1));
-    const uint32_t base = ((uint32_t)blk * a.Hkv + kvh) * (kPageBytes / 2);
-    unsigned char* slot = ring + (c % NSP) * kPageBytes;
+  for (int i = 0; i < PPW; ++i) psrc[i] = page_piece_src(min(qt + NQT * i, 15) & 7, lane);
+  auto copy_pair = [&](int c) {
+    unsigned char* slot = ring + (c % NSP) * kPairBytes;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-      const int q = min(qt + NQT * i, 7);
-      if (q < 4) lds_copy16(rk, psrc[i], base, slot + q * 1024);
-      else lds_copy16(rv, psrc[i], base, slot + q * 1024);
+      const int piece = min(qt + NQT * i, 15);
+      const int h = piece >> 3, q = piece & 7;
+      const int blk = __builtin_amdgcn_readlane(bt, min(2 * c + h, npages - 1));
+      const uint32_t base = ((uint32_t)blk * a.Hkv + kvh) * (kPageBytes / 2);
+      if (q < 4) lds_copy16(rk, psrc[i], base, slot + h * kPageBytes + q * 1024);
+      else lds_copy16(rv, psrc[i], base, slot + h * kPageBytes + q * 1024);
     }
   };
 
@@ -235,17 +284,17 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < LA; ++c) copy_page(c);
-  for (int c = 0; c < npages; ++c) {
-    wait_vmcnt<(LA - 1) * PPW>();  // my pieces of page c (LA - 1 pages' pieces follow them)
+  for (int c = 0; c < LA; ++c) copy_pair(c);
+  for (int c = 0; c < npairs; ++c) {
+    wait_vmcnt<(LA - 1) * PPW>();  // my pieces of pair c (LA - 1 pairs' pieces follow them)
     __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): my reads of page c - 1 are done
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): my reads of pair c - 1 are done
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    copy_page(c + LA);  // into the slot of page c - 1
-    PageRegs pg;
-    read_page(ring + (c % NSP) * kPageBytes, pg);
-    attn_page(pg, k1 - (k0 + c * kBlock), qh, ql, st);
+    copy_pair(c + LA);  // into the slot of pair c - 1
+    PairRegs pr;
+    read_pair(ring + (c % NSP) * kPairBytes, pr);
+    attn_pair(pr, k1 - (k0 + 2 * c * kBlock), qh, ql, st);
   }
   float lsum = st.l;
   lsum += __shfl_xor(lsum, 16);
@@ -378,11 +427,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 }
 
 // Runs of pages_per_split pages: two pages per run while that keeps the grid
-// within about 1024 workgroups, longer runs (fewer partial results) beyond.
+// within about 640 workgroups, longer runs beyond.  Many short runs cost
+// workgroup launches and partial results (24 KB each, written and merged);
+// few long ones leave compute units idle and make long dependent chains.
 void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits) {
   const int max_pages = (max_len + kBlock - 1) / kBlock;
   int pps = 2;
-  while (pps < 64 && (long)B * Hkv * ((max_pages + pps - 1) / pps) > 1024) pps *= 2;
+  while (pps < 64 && (long)B * Hkv * ((max_pages + pps - 1) / pps) > 640) pps *= 2;
   if (pps > max_pages) pps = max_pages;
   if (pps < 1) pps = 1;
   *pages_per_split = pps;
@@ -391,15 +442,15 @@ void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_
 
 template <int NQT>
 static void launch_split(const AttnArgs& a, bool deep, dim3 grid, dim3 block, hipStream_t s) {
-  if (deep) hipLaunchKernelGGL((k_attn_split<NQT, 7>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_attn_split<NQT, 2>), grid, block, 0, s, a);
+  if (deep) hipLaunchKernelGGL((k_attn_split<NQT, 3>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_attn_split<NQT, 1>), grid, block, 0, s, a);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int nqt = a.nqp / 16;
-  const dim3 grid(a.max_splits, a.Hkv, a.B), block(nqt * 64);
-  // a deep page ring for long runs, a short one for the two-page runs of
-  // short sequences
+  const dim3 grid(a.B, a.max_splits, a.Hkv), block(nqt * 64);
+  // a deep ring for long runs, a short one for the two-page runs of short
+  // sequences
   const bool deep = a.pages_per_split > 2;
   switch (nqt) {
     case 1: launch_split<1>(a, deep, grid, block, s); break;
