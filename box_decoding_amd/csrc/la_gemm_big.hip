@@ -33,6 +33,7 @@
 namespace la {
 
 constexpr int kWideWaves = 4;
+constexpr int kPfSink = 1024;  // LDS bytes the L2 prefetches land in (never read)
 constexpr int kItemTiles = 8;  // 16-column tiles per work item
 
 template <int RT, bool INT4>
@@ -57,13 +58,51 @@ struct Wide {
   static constexpr int NCOPY = RTW * CPU / 16;        // 1 KB copies per wave and stage
   static constexpr int NC = NCOPY + (INT4 ? 1 : 0);
   static constexpr int NW = 2 * CT;                   // bf16: CT tiles x 2 K steps; INT4: + scales
-  // A wave waits for its own copies of the unit read next before the barrier.
-  // Whatever their order inside a stage, at least LA - 1 whole stages of
-  // loads were issued after them (LA whole stages before the first read).
-  static constexpr int WAIT = (LA - 1) * (NC + NW);
-  static constexpr int WAIT0 = LA * (NC + NW);
+  // Optional L2 prefetch: the weights of stage s + PF pulled into L2 at stage
+  // s (direct-to-LDS loads into a scratch kilobyte nobody reads).  Measured
+  // slower at PF 8..16 (the loop is not waiting on weights: with every
+  // workgroup reading the same L2-resident weights it runs no faster), so off.
+  static constexpr int PF = 0;
+  static constexpr int NPF = PF > DW ? CT : 0;       // prefetch loads per wave and stage
+  // A wave waits for its own copies of the unit read next before the barrier
+  // (loads complete in issue order).  The wait counts come from a replay of
+  // the issue order: the prologue (L2 prefetches, DW stages of weights,
+  // CLEAD stages of copies), then per stage one copy batch, one weight batch
+  // and one prefetch batch.  At each
+  // stage's wait it counts the loads issued after the last copy of the unit
+  // read next; the smallest count over the first stages (after which the
+  // pattern repeats) is the wait of every stage, and the prologue's own
+  // count is the wait before the first fragment reads.
+  static constexpr int CLEAD = PREFETCH ? LA + 1 : LA;  // copies of stage s + CLEAD at stage s
+  struct Waits {
+    int first, loop;
+  };
+  static constexpr Waits waits() {
+    int endc[64] = {};
+    int e = 0, cp = 0;
+    for (int s = -DW; s < 0; ++s) {
+      e += NC;  // a copy (of stage 0's bytes when no real copy is due yet)
+      if (s + CLEAD >= 0) endc[cp++] = e;
+      e += NW;
+    }
+    for (int s = DW; s < CLEAD; ++s) {
+      e += NC;
+      endc[cp++] = e;
+    }
+    Waits r{PREFETCH ? e - endc[0] : 0, 1 << 20};
+    for (int j = 0; j < 2 * NS + 2 * R; ++j) {
+      const int after = e - endc[PREFETCH ? j + 1 : j];
+      r.loop = after < r.loop ? after : r.loop;
+      e += NC;
+      endc[cp++] = e;
+      e += NW + NPF;
+    }
+    return r;
+  }
+  static constexpr int WAIT = waits().loop;
+  static constexpr int WAIT0 = waits().first;
   static_assert(RTW % 4 == 0 && (R % 2 == 0 || !PREFETCH) && DW >= 1, "wide GEMM shape");
-  static_assert(WAIT0 < 64 && DW * (NC + NW) < 64, "vmcnt range");
+  static_assert(WAIT >= 0 && WAIT0 >= 0 && WAIT < 64 && WAIT0 < 64, "vmcnt range");
   static_assert(CT * (INT4 ? 16 : 32) * 2 == kItemTiles * 16, "item shape");
 };
 
@@ -132,8 +171,9 @@ void k_gemm_big(GemmArgs a) {
   constexpr int SW = kItemTiles / 2 * 16;  // columns of a column wave
   constexpr int SROW = SW + 4;  // 16-byte aligned rows, column writes spread over banks
   unsigned char* slots = smem;                                              // [NS][SLOT]
-  float* stage = (float*)(smem + NS * SLOT) + (size_t)wave * 8 * SROW;      // [8][SROW] per wave
-  float* amax_lds = (float*)(smem + NS * SLOT) + (size_t)kWideWaves * 8 * SROW;
+  unsigned char* pf_sink = smem + NS * SLOT;                                // [kPfSink]
+  float* stage = (float*)(pf_sink + kPfSink) + (size_t)wave * 8 * SROW;     // [8][SROW] per wave
+  float* amax_lds = (float*)(pf_sink + kPfSink) + (size_t)kWideWaves * 8 * SROW;
   float* my_amax = amax_lds + (size_t)wave * NP * 8 * 3;                    // ARGMAX: [NP*8][3]
   if (EPI == EPI_ARGMAX) {
     for (int i = lane; i < NP * 8; i += 64) {
@@ -256,6 +296,24 @@ void k_gemm_big(GemmArgs a) {
     }
   };
 
+  // L2 prefetch of a stage's bf16 weights: this wave takes loads rw*CT ..
+  // rw*CT + CT - 1 (load T*2 + kk) of its column wave's stage
+  auto issue_pf = [&](const Pos& q) {
+    if constexpr (C::NPF > 0) {
+      const bool live_stage = q.it < n_my && q.uu < nu;
+      const uint32_t u = (uint32_t)(s_lo + min(q.uu, nu - 1));
+      const int tile0 = ((cb0 + q.it * gt) * 2 + cw) * (kItemTiles / 2);
+#pragma unroll
+      for (int i = 0; i < C::NPF; ++i) {
+        const int idx = rw * CT + i, T = idx >> 1, kk = idx & 1;
+        const int tile = tile0 + 2 * T;
+        const bool live = live_stage && tile < a.n_tiles;
+        const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
+        lds_copy16(rwt, w_lane + kk * kk_step, so, pf_sink);
+      }
+    }
+  };
+
   // ---- activation fragments.  bf16: fragment 2i + kk is row tile i (packed
   // tiles 2i, 2i + 1 of the wave's rows), K step kk; INT4: row tile i of K
   // step j.
@@ -283,12 +341,13 @@ void k_gemm_big(GemmArgs a) {
   // bf16: the products of one stage from fragments read one stage earlier
   auto compute_bf16 = [&](const WStage& s, const bf16x8 (&f)[FR]) {
     if constexpr (!INT4) {
+      // K step outermost: consecutive products go to different accumulators
 #pragma unroll
-      for (int i = 0; i < RT; ++i)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int T = 0; T < CT; ++T)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
+          for (int T = 0; T < CT; ++T)
             acc[i][T] = mfma_32x32x16(f[2 * i + kk], __builtin_bit_cast(bf16x8, s.w[T * 2 + kk]), acc[i][T]);
     }
   };
@@ -482,11 +541,21 @@ void k_gemm_big(GemmArgs a) {
     // the copies of a later unit and the weights of stage bi + DW issued
     // among them.  The copies of stage bi + LA (+ 1 with PREFETCH) go to
     // the slot whose reads completed before this barrier.
-    Pos cpos{0, 0, 0}, wpos{0, 0, 0};
+    Pos cpos{0, 0, 0}, wpos{0, 0, 0}, ppos{0, 0, 0};
     int rslot = 0;  // slot of stage bi
+    // ---- L2 prefetches of the stages whose weights the loop loads first
+    if constexpr (C::NPF > 0) {
+#pragma unroll
+      for (int s = 0; s < DW; ++s) step(ppos);
+#pragma unroll
+      for (int s = DW; s < C::PF; ++s) {
+        issue_pf(ppos);
+        step(ppos);
+      }
+    }
     // ---- prologue: DW stages' loads in the loop's pattern (a stage with no
     // copy due repeats stage 0's: same bytes to the same place)
-    constexpr int CLEAD = C::PREFETCH ? LA + 1 : LA;  // copies of stage s + CLEAD at stage s
+    constexpr int CLEAD = C::CLEAD;
 #pragma unroll
     for (int s = -DW; s < 0; ++s) {
       if (s + CLEAD >= 0) {
@@ -523,6 +592,10 @@ void k_gemm_big(GemmArgs a) {
           step(cpos);
           issue_w(wpos, st[(j + DW) % C::R]);
           step(wpos);
+          if constexpr (C::NPF > 0) {
+            issue_pf(ppos);
+            step(ppos);
+          }
           if (C::PREFETCH) {
             compute_bf16(st[j], af[j & 1]);
             // one lone wave per SIMD: spread the stage's other instructions
@@ -634,7 +707,7 @@ static int big_cus() {
 template <int RT, bool INT4>
 static constexpr size_t wide_smem(int epi) {
   using C = Wide<RT, INT4>;
-  return (size_t)C::NS * C::SLOT + (size_t)kWideWaves * 8 * (kItemTiles / 2 * 16 + 4) * 4 +
+  return (size_t)C::NS * C::SLOT + kPfSink + (size_t)kWideWaves * 8 * (kItemTiles / 2 * 16 + 4) * 4 +
          (epi == EPI_ARGMAX ? (size_t)kWideWaves * C::NP * 8 * 3 * 4 : 0);
 }
 
@@ -670,11 +743,11 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   const int dw = int4 ? Wide<4, true>::R : Wide<6, false>::R;  // stages per ring turn
   // K slices (QKV always writes slice sums; STORE when the caller takes them):
   // the fewest rounds of items times the padded stages of one item, plus the
-  // slice sums' write and read-back counted in stage times (about 0.35 us a
-  // stage of 192 rows; slice traffic at about 3 TB/s); on a tie the fewer
-  // slices
+  // slice sums' write and read-back counted in stage times (a stage of 192
+  // rows measured at about 0.73 us; slice traffic at about 3 TB/s); on a tie
+  // the fewer slices
   const bool can_split = epi == EPI_QKV || (allow_split && epi == EPI_STORE);
-  const double stage_us = 0.35 * std::max(rows, 32) / 192.0;
+  const double stage_us = 0.73 * std::max(rows, 32) / 192.0;
   const double slice_stages = (double)rows * N * 8 / 3e6 / stage_us;
   double best = -1;
   p.ksplit = 1;
