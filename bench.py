@@ -229,6 +229,87 @@ def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
                              "matrix_core_frac_with_hi_lo": round(2 * tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
+def emission_leg(B, synth, torch, dm, model, dev, stream, args):
+    """The dense-scene emission loop: 16 sequences from prefix 2048 run 40
+    consecutive window steps, each committed on the device (prefix += 6, next
+    window = [last output id, mask x 5]) -- one captured graph of step + commit,
+    replayed 40 times per loop."""
+    w = synth.WORKLOADS["emit_b16_p2048_x40"]
+    d = w.dims
+    log("bench: emission-loop leg")
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, extra_tokens=w.steps * w.window, seed=w.input_seed,
+                             device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    mask_id = int(ids[0, 1].item())
+    ids0, P0 = ids.clone(), P.to(dev)
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P0.clone()
+    max_len = int(P.max()) + (w.steps + 1) * w.window
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
+    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws, commit_mask_id=mask_id)
+
+    def run_loop():
+        ids.copy_(ids0)
+        Pd.copy_(P0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(w.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run_loop()  # warm-up loop
+    loop_ms = run_loop()
+    assert int((Pd - P0).min().item()) == w.steps * w.window
+    ms_step = loop_ms / w.steps
+    mid = P + w.window * (w.steps - 1) // 2
+    sbytes = step_bytes(model, d, mid, w.window)
+    log(f"bench: emission loop: {loop_ms:.2f} ms for {w.steps} steps, {ms_step:.3f} ms/step, "
+        f"{w.batch * 1000.0 / ms_step:.0f} windows/s")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": w.name, "batch": w.batch, "window": w.window, "steps_per_loop": w.steps,
+            "prefix_start": int(P.max()), "loop_ms": round(loop_ms, 3), "ms_per_step": round(ms_step, 4),
+            "steps_per_s": round(1000.0 / ms_step, 3),
+            "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
+            "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
+            "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
+
+
+def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
+    """The long-context probe: one sequence at prefix 32768, window 6."""
+    w = synth.WORKLOADS["probe_b1_p32768"]
+    d = w.dims
+    log("bench: long-context leg")
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    max_len = int(P.max()) + w.window
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
+    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
+    for _ in range(max(2, args.warmup)):
+        graph.replay()
+    steps = max(5, args.steps // 3)
+    ms_step, _ = timed(graph.replay, steps)
+    sbytes = step_bytes(model, d, P, w.window)
+    log(f"bench: prefix 32768: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": w.name, "batch": w.batch, "window": w.window, "prefix": int(P.max()),
+            "steps": steps, "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
+            "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +320,8 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="skip the emission-loop and prefix-32768 legs")
     ap.add_argument("--no-batch32", action="store_true",
                     help="skip the batch-32 leg reported beside the batch-1 step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -380,6 +463,10 @@ def main():
         del cache, dc
         torch.cuda.synchronize()
         result["batch32"] = batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args)
+    if args.workload == "step_b1_p1280" and not args.no_extra_legs and not args.row_major:
+        # the other bf16 workloads on the same model
+        result["emission_loop"] = emission_leg(B, synth, torch, dm, model, dev, stream, args)
+        result["prefix_32768"] = probe_leg(B, synth, torch, dm, model, dev, stream, timed, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)

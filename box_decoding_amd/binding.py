@@ -26,7 +26,7 @@ EXPORTED = [
     "la_int4_embed_gather", "la_wgemm_workspace", "la_wgemm", "la_pbd_attention_workspace",
     "la_pbd_attention", "la_lm_head_argmax_workspace", "la_lm_head_argmax", "la_pbd_layer",
     "la_pbd_step_workspace", "la_pbd_step", "la_status_str", "la_pack_weight_bytes",
-    "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed",
+    "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
 ]
 
 
@@ -102,6 +102,8 @@ def load() -> ctypes.CDLL:
                                    c_size_t, c_void_p]),
         "la_wgemm_packed": (c_int32, [c_void_p, c_int32, W, c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p]),
+        "la_pbd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                    c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -377,6 +379,17 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
     return ids, gap, hid
 
 
+def pbd_commit(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_len: torch.Tensor,
+               mask_id: int):
+    """Commit a fully accepted window on the device: prefix_len += W and
+    window_ids <- [out_ids[:, W-1], mask_id x (W-1)] (in place)."""
+    lib = load()
+    _require_cuda(out_ids, window_ids, prefix_len)
+    B, W = window_ids.shape
+    _check(lib.la_pbd_commit(_ptr(out_ids), _ptr(window_ids), _ptr(prefix_len), B, W, int(mask_id),
+                             _stream()), "la_pbd_commit")
+
+
 class StepGraph:
     """One la_pbd_step call captured in a HIP graph (torch.cuda.CUDAGraph) and
     replayed; inputs and outputs are the tensors given at capture time."""
@@ -384,24 +397,30 @@ class StepGraph:
     def __init__(self, model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
                  prefix_len: torch.Tensor, max_len: int, out_ids: torch.Tensor,
                  out_gap: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None,
-                 err: Optional[torch.Tensor] = None):
+                 err: Optional[torch.Tensor] = None, commit_mask_id: Optional[int] = None):
+        # commit_mask_id: also capture la_pbd_commit after the step, so each
+        # replay is one step of an emission loop (the window and prefix
+        # lengths advance on the device)
         self.args = (model, cache, window_ids, prefix_len, max_len)
+        self.commit_mask_id = commit_mask_id
         self.ws = ws or Workspace(window_ids.device)
         self.out_ids, self.out_gap, self.err = out_ids, out_gap, err
         side = torch.cuda.Stream(device=window_ids.device)
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            self._call()  # sizes the workspace before capture
+            self._call(commit=False)  # sizes the workspace before capture
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
             self._call()
 
-    def _call(self):
+    def _call(self, commit: bool = True):
         m, c, ids, P, ml = self.args
         pbd_step(m, c, ids, P, ml, want_gap=self.out_gap is not None, ws=self.ws,
                  out_ids=self.out_ids, out_gap=self.out_gap, err=self.err)
+        if commit and self.commit_mask_id is not None:
+            pbd_commit(self.out_ids, ids, P, self.commit_mask_id)
 
     def replay(self):
         self.graph.replay()

@@ -782,4 +782,12 @@ la_status la_pack_weight(const la_weight* src, int32_t layout, void* dst, void* 
   return hip_status(launch_pack_weight(*src, layout, dst, dst_scales, stream));
 }
 
+la_status la_pbd_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len,
+                        int32_t B, int32_t W, int32_t mask_id, hipStream_t stream) {
+  if (!out_ids || !window_ids || !prefix_len) return LA_ERR_ARG;
+  if ((const void*)out_ids == (const void*)window_ids) return LA_ERR_ARG;
+  if (B < 1 || B > 64 || W < 1 || W > 8) return LA_ERR_SHAPE;
+  return hip_status(launch_commit(out_ids, window_ids, prefix_len, B, W, mask_id, stream));
+}
+
 }  // extern "C"

@@ -122,6 +122,8 @@ hipError_t launch_pack_weight(const la_weight& src, int layout, void* dst, void*
                               hipStream_t s);
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+hipError_t launch_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len, int B,
+                         int W, int mask_id, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s);
 hipError_t launch_argmax_reduce(const float* amax, int M, int n_tiles, const int32_t* flags,

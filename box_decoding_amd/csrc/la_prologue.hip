@@ -93,4 +93,22 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Commit of a fully accepted window: one thread per window slot of each
+// sequence; the slot-0 thread also advances the prefix length.
+__global__ __launch_bounds__(1024) void k_commit(const int32_t* out_ids, int32_t* window_ids,
+                                                 int32_t* prefix_len, int B, int W, int mask_id) {
+  const int t = threadIdx.x;
+  if (t >= B * W) return;
+  const int b = t / W, j = t - b * W;
+  window_ids[t] = j == 0 ? out_ids[b * W + W - 1] : mask_id;
+  if (j == 0) prefix_len[b] += W;
+}
+
+hipError_t launch_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len, int B,
+                         int W, int mask_id, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit, dim3(1), dim3(((B * W + 63) / 64) * 64), 0, s, out_ids, window_ids,
+                     prefix_len, B, W, mask_id);
+  return hipGetLastError();
+}
+
 }  // namespace la

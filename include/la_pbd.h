@@ -231,6 +231,19 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream);
 
+/* Commit a fully accepted window and form the next one, for a loop of window
+ * steps (the cached prefix grows by the accepted tokens and is reused, with
+ * no explicit rollback: RK3588 page, "How it differs from the original", item
+ * 1): prefix_len[b] += W, and window_ids[b] becomes [out_ids[b][W-1], mask_id
+ * x (W-1)].  The window's K/V are already in the cache: la_pbd_step wrote them
+ * at slots P_b .. P_b+W-1.  out_ids and window_ids int32 [B][W] (distinct
+ * buffers), prefix_len int32 [B], all device memory owned by the caller.  Only
+ * enqueues on the stream (graph-capturable).  Returns LA_ERR_ARG for NULL
+ * pointers or aliased ids, LA_ERR_SHAPE outside 1 <= B <= 64, 1 <= W <= 8 (the
+ * step's limits). */
+la_status la_pbd_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len,
+                        int32_t B, int32_t W, int32_t mask_id, hipStream_t stream);
+
 /* Repack a row-major weight (src->layout == LA_LAYOUT_ROWS) into one of the
  * tiled layouts (bf16, or INT4 with group 128).  dst receives
  * la_pack_weight_bytes(src, layout, 0) bytes of data and dst_scales (INT4

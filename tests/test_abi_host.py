@@ -141,3 +141,16 @@ def test_pack_rows_and_packed_gemm_reject_bad_arguments(lib):
     # SiLU gating needs the gate/up layout and takes no bias or residual
     wg = _w(n=2 * 1024, layout=2)
     assert lib.la_wgemm_packed(fake, 6, ctypes.byref(wg), fake, None, 1, fake, None) == -2
+
+
+def test_commit_rejects_bad_arguments_before_launch(lib):
+    a, b_ = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    p = ctypes.c_void_p(12288)
+    assert lib.la_pbd_commit(None, b_, p, 2, 6, 7, None) == -1
+    assert lib.la_pbd_commit(a, None, p, 2, 6, 7, None) == -1
+    assert lib.la_pbd_commit(a, b_, None, 2, 6, 7, None) == -1
+    assert lib.la_pbd_commit(a, a, p, 2, 6, 7, None) == -1     # ids aliased
+    assert lib.la_pbd_commit(a, b_, p, 0, 6, 7, None) == -2
+    assert lib.la_pbd_commit(a, b_, p, 65, 6, 7, None) == -2
+    assert lib.la_pbd_commit(a, b_, p, 2, 0, 7, None) == -2
+    assert lib.la_pbd_commit(a, b_, p, 2, 9, 7, None) == -2

@@ -370,6 +370,63 @@ def test_step_graph_replay_matches_eager():
         assert torch.equal(out_gap, ref_gap), r
 
 
+@pytest.mark.parametrize("graph", [False, True])
+def test_emission_loop_matches_oracle(graph):
+    """Window steps each committed on the device (prefix += W, next window =
+    [last output id, mask x (W-1)]) against the oracle's loop from the same
+    windows: ids exact where the oracle's gap is >= 1e-3, the device's next
+    window and prefix lengths exact, and every committed slot's K/V within one
+    bf16 ulp.  With graph=True each replay of one captured graph is a step and
+    its commit."""
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    steps, W, mask = 4, 6, 17
+    P0 = [0, 33, 200]
+    model = synth.make_model(d, "bf16", 101, DEV)
+    P = torch.tensor(P0, dtype=torch.int32)
+    cache = synth.make_cache(d, P, W, extra_tokens=steps * W, seed=102, device=DEV)
+    ids = synth.draw_window_ids(len(P0), W, d.vocab, 103, mask_id=mask, device=DEV)
+    mn, c = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(DEV)
+    max_len = max(P0) + (steps + 1) * W
+    out_ids = torch.empty((len(P0), W), dtype=torch.int32, device=DEV)
+    out_gap = torch.empty((len(P0), W), dtype=torch.float32, device=DEV)
+    g = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, commit_mask_id=mask) if graph else None
+    ref_P = P.numpy().astype(np.int64)
+    compared = 0
+    for s in range(steps):
+        win = ids.cpu().numpy()
+        if graph:
+            g.replay()
+        else:
+            B.pbd_step(dm, dc, ids, Pd, max_len, out_ids=out_ids, out_gap=out_gap)
+            B.pbd_commit(out_ids, ids, Pd, mask)
+        torch.cuda.synchronize()
+        got = out_ids.cpu().numpy()
+        ref = O.pbd_step(mn, c, win, ref_P)
+        n, bad, excl = ids_match(got, ref["ids"], ref["gap"])
+        compared += n
+        assert bad == 0, s
+        _, ref_P, c = O.pbd_emission_loop(mn, c, win, ref_P, 1, mask)
+        expect = np.full_like(win, mask)
+        expect[:, 0] = got[:, W - 1]
+        assert np.array_equal(ids.cpu().numpy(), expect), s
+        assert np.array_equal(Pd.cpu().numpy().astype(np.int64), ref_P), s
+    cg = np_tree(cache)
+    kd = vd = 0
+    for layer in range(d.n_layers):
+        for b in range(len(P0)):
+            pos = np.arange(P0[b], P0[b] + steps * W)
+            kg, vg = cache_slots(cg, layer, b, pos)
+            kr, vr = cache_slots(c, layer, b, pos)
+            kd = max(kd, bf16_kv_mismatch(kg, kr))
+            vd = max(vd, bf16_kv_mismatch(vg, vr))
+    _log(f"emission loop (graph={graph}): {steps} steps, ids {compared} compared; K/V ulp {kd}/{vd}")
+    assert compared >= steps * len(P0) * W - 4
+    assert kd <= 1 and vd <= 1
+
+
 # ---------------------------------------------------------------- tiled weight layouts
 
 def _layout_rows(layout, n, n_tiles):
