@@ -153,7 +153,9 @@ def _attention_case(P_list, W, seed, max_len=None, poison=True):
 
 @pytest.mark.parametrize("P_list,W", [([0, 37, 300], 6), ([1280], 6), ([5, 16, 17, 4096], 6),
                                       ([100, 9], 1), ([63, 64], 4), ([200], 8),
-                                      ([0, 3, 20], 6), ([10], 6)])
+                                      ([0, 3, 20], 6), ([10], 6),
+                                      # 24 ragged sequences
+                                      ([(37 * i) % 500 for i in range(24)], 6)])
 def test_attention_matches_oracle(P_list, W):
     errs = _attention_case(P_list, W, seed=sum(P_list) + W)
     _log(f"attention P={P_list} W={W}: rel-L2 max {max(errs):.2e}")
