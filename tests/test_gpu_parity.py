@@ -285,10 +285,11 @@ def test_step_small_ragged(fmt):
     assert bad == 0
 
 
-@pytest.mark.parametrize("fmt,B_", [("bf16", 8), ("int4", 8), ("bf16", 32)])
+@pytest.mark.parametrize("fmt,B_", [("bf16", 8), ("int4", 8), ("bf16", 32), ("int4", 16), ("bf16", 64)])
 def test_step_batched_large_m(fmt, B_):
-    # more than 32 rows: the large-M GEMM path (48 rows, and 192 rows with two
-    # rows of consumer waves)
+    # more than 32 rows: the large-M GEMM path (bf16 48 and 192 rows; 384 rows
+    # in two launches; INT4 96 rows in launches of 64 and 32; INT4 48 rows on
+    # the small-M kernel in two launches)
     d = synth.ModelDims(n_layers=2, vocab=3001)
     P_list = [int(p) for p in torch.randint(0, 700, (B_,), generator=torch.Generator().manual_seed(B_))]
     got_ids, got_gap, hid, ref, err = _step_case(d, fmt, P_list, 6, seed=83 + B_)
@@ -344,6 +345,19 @@ def test_step_full_b1_p1280():
          f" ids {out_ids.cpu().numpy().tolist()} gaps {np.round(ref['gap'], 4).tolist()}")
     assert bad == 0
     assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("W", [1, 8])
+def test_step_window_sizes(W):
+    # W = 1 is ordinary decode; W = 8 the widest window (64 query columns)
+    d = synth.ModelDims(n_layers=2, vocab=4001)
+    got_ids, got_gap, hid, ref, err = _step_case(d, "bf16", [0, 29, 333], W, seed=120 + W)
+    n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
+    e = rel_l2(hid, ref["hidden"])
+    _log(f"step W={W}: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
+    assert err == 0
+    assert e <= TOL_BF16
+    assert bad == 0
 
 
 def test_step_graph_replay_matches_eager():
