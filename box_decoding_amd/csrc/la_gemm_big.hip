@@ -32,18 +32,32 @@
 
 namespace la {
 
-constexpr int kWideWaves = 4;
 constexpr int kPfSink = 1024;  // LDS bytes the L2 prefetches land in (never read)
-constexpr int kItemTiles = 8;  // 16-column tiles per work item
 
-template <int RT, bool INT4>
+// Wave grids (LAY): 0: 2 row waves x 2 column waves (bf16 2 tiles of 32
+// columns each, INT4 4 tiles of 16: items of 128 columns); 1 (bf16): 4 row
+// waves x 1 column wave of 3 tiles of 32 (items of 96 columns, so more
+// workgroups for a GEMM that cannot take K slices); 2: 4 x 2, eight waves
+// (two per SIMD, so one wave's other instructions run beside another's
+// products).
+constexpr int lay_row_waves(int lay) { return lay == 0 ? 2 : 4; }
+constexpr int lay_col_waves(int lay) { return lay == 1 ? 1 : 2; }
+constexpr int lay_threads(int lay) { return lay_row_waves(lay) * lay_col_waves(lay) * 64; }
+constexpr int lay_waves_per_eu(int lay) { return lay == 2 ? 2 : 1; }
+
+template <int RT, bool INT4, int LAY = 0>
 struct Wide {
-  // bf16: RT tiles of 32 operand rows (16 real rows) per row wave, CT = 2
-  // tiles of 32 columns per column wave.  INT4: RT tiles of 16 operand rows
-  // (8 real rows), CT = 4 tiles of 16 columns.
-  static constexpr int RTW = INT4 ? 2 * RT : 4 * RT;  // packed 16-row tiles of a launch
+  // bf16: RT tiles of 32 operand rows (16 real rows) per row wave, CT tiles
+  // of 32 columns per column wave.  INT4: RT tiles of 16 operand rows (8 real
+  // rows), CT = 4 tiles of 16 columns.
+  static constexpr int RWV = lay_row_waves(LAY), CW = lay_col_waves(LAY), WAVES = RWV * CW;
+  static constexpr int RTW = RWV * RT * (INT4 ? 1 : 2);  // packed 16-row tiles of a launch
   static constexpr int NP = INT4 ? RT : 2 * RT;       // epilogue parts of 8 real rows per row wave
-  static constexpr int CT = INT4 ? 4 : 2;
+  static constexpr int CT = INT4 ? 4 : (LAY == 1 ? 3 : 2);
+  static constexpr int TPW = INT4 ? CT : 2 * CT;      // 16-column tiles per column wave
+  static constexpr int ITEM = CW * TPW;               // 16-column tiles per work item
+  static constexpr int SW = TPW * 16;                 // staged columns per wave
+  static constexpr int NG = SW / 8;                   // 8-column epilogue groups per staged row
   static constexpr int CPU = INT4 ? 16 : 4;           // 256-byte chunks per packed tile and K unit
   static constexpr int FR = INT4 ? RT : 2 * RT;       // fragments per bf16 stage / INT4 K step
   static constexpr int SUMS = INT4 ? RTW * 64 : 0;    // INT4 group sums of a slot (bytes)
@@ -55,7 +69,7 @@ struct Wide {
   static constexpr int LA = NS - 1;                   // copy lead (stages)
   static constexpr int R = INT4 ? 3 : 4;              // weight ring entries; loop unroll
   static constexpr int DW = R - 1;                    // weight lead (stages)
-  static constexpr int NCOPY = RTW * CPU / 16;        // 1 KB copies per wave and stage
+  static constexpr int NCOPY = RTW * CPU / 4 / WAVES;  // 1 KB copies per wave and stage
   static constexpr int NC = NCOPY + (INT4 ? 1 : 0);
   static constexpr int NW = 2 * CT;                   // bf16: CT tiles x 2 K steps; INT4: + scales
   // Optional L2 prefetch: the weights of stage s + PF pulled into L2 at stage
@@ -102,8 +116,9 @@ struct Wide {
   static constexpr int WAIT = waits().loop;
   static constexpr int WAIT0 = waits().first;
   static_assert(RTW % 4 == 0 && (R % 2 == 0 || !PREFETCH) && DW >= 1, "wide GEMM shape");
+  static_assert((RTW * CPU / 4) % WAVES == 0 && (!INT4 || LAY != 1), "wide GEMM shape");
   static_assert(WAIT >= 0 && WAIT0 >= 0 && WAIT < 64 && WAIT0 < 64, "vmcnt range");
-  static_assert(CT * (INT4 ? 16 : 32) * 2 == kItemTiles * 16, "item shape");
+  static_assert(NG <= 16 && SW % 8 == 0, "item shape");
 };
 
 // The per-stage meeting point: this wave's LDS reads are complete, then the
@@ -144,16 +159,18 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int RT, bool INT4, int EPI>
-__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int RT, bool INT4, int EPI, int LAY>
+__global__ __launch_bounds__(lay_threads(LAY))
+__attribute__((amdgpu_waves_per_eu(lay_waves_per_eu(LAY), lay_waves_per_eu(LAY))))
 void k_gemm_big(GemmArgs a) {
-  using C = Wide<RT, INT4>;
+  using C = Wide<RT, INT4, LAY>;
   constexpr int RTW = C::RTW, NP = C::NP, CT = C::CT, CPU = C::CPU, FR = C::FR, NS = C::NS,
-                LA = C::LA, DW = C::DW, SLOT = C::SLOT;
+                LA = C::LA, DW = C::DW, SLOT = C::SLOT, WAVES = C::WAVES, CW = C::CW,
+                TPW = C::TPW, ITEM = C::ITEM;
   using AccT = std::conditional_t<INT4, f32x4, f32x16>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int rw = wave >> 1, cw = wave & 1;
+  const int rw = wave / CW, cw = wave % CW;
   const int g = lane >> 4, c = lane & 15;
   const int K8 = a.K >> 3, KG = a.K >> 7;
   const int units = INT4 ? (a.K >> 7) : (a.K >> 5);
@@ -162,18 +179,18 @@ void k_gemm_big(GemmArgs a) {
   const int s_lo = units * ks / a.ksplit, s_hi = units * (ks + 1) / a.ksplit;
   const int nu = s_hi - s_lo;
   const int nup = (nu + C::R - 1) / C::R * C::R;  // stages per item: whole ring turns
-  const int n_cb = (a.n_tiles + kItemTiles - 1) / kItemTiles;
+  const int n_cb = (a.n_tiles + ITEM - 1) / ITEM;
   const int n_my = cb0 < n_cb ? (n_cb - cb0 + gt - 1) / gt : 0;
   const int total = n_my * nup;
   const int rows = min(a.M - a.m_base, RTW * 8);
   const int mtv = (rows + 7) >> 3;
 
-  constexpr int SW = kItemTiles / 2 * 16;  // columns of a column wave
+  constexpr int SW = C::SW;      // columns of a column wave
   constexpr int SROW = SW + 4;  // 16-byte aligned rows, column writes spread over banks
   unsigned char* slots = smem;                                              // [NS][SLOT]
   unsigned char* pf_sink = smem + NS * SLOT;                                // [kPfSink]
   float* stage = (float*)(pf_sink + kPfSink) + (size_t)wave * 8 * SROW;     // [8][SROW] per wave
-  float* amax_lds = (float*)(pf_sink + kPfSink) + (size_t)kWideWaves * 8 * SROW;
+  float* amax_lds = (float*)(pf_sink + kPfSink) + (size_t)WAVES * 8 * SROW;
   float* my_amax = amax_lds + (size_t)wave * NP * 8 * 3;                    // ARGMAX: [NP*8][3]
   if (EPI == EPI_ARGMAX) {
     for (int i = lane; i < NP * 8; i += 64) {
@@ -214,7 +231,7 @@ void k_gemm_big(GemmArgs a) {
     unsigned char* dst = slot_ptr(q.slot);
 #pragma unroll
     for (int k = 0; k < C::NCOPY; ++k) {
-      const int p = wave + 4 * k;
+      const int p = wave + WAVES * k;
       const int t = p / (CPU / 4), part = p % (CPU / 4);
       const uint32_t soff = ((uint32_t)min(t, mtv - 1) * K8 + u * CPU + part * 4) * 256;
       lds_copy16(rap, lane * 16, soff, dst + (t * CPU + part * 4) * 256);
@@ -267,7 +284,7 @@ void k_gemm_big(GemmArgs a) {
   auto issue_w = [&](const Pos& q, WStage& d) {
     const bool live_stage = q.it < n_my && q.uu < nu;
     const uint32_t u = (uint32_t)(s_lo + min(q.uu, nu - 1));
-    const int tile0 = ((cb0 + q.it * gt) * 2 + cw) * (kItemTiles / 2);
+    const int tile0 = ((cb0 + q.it * gt) * CW + cw) * TPW;
     if (INT4) {
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
@@ -302,7 +319,7 @@ void k_gemm_big(GemmArgs a) {
     if constexpr (C::NPF > 0) {
       const bool live_stage = q.it < n_my && q.uu < nu;
       const uint32_t u = (uint32_t)(s_lo + min(q.uu, nu - 1));
-      const int tile0 = ((cb0 + q.it * gt) * 2 + cw) * (kItemTiles / 2);
+      const int tile0 = ((cb0 + q.it * gt) * CW + cw) * TPW;
 #pragma unroll
       for (int i = 0; i < C::NPF; ++i) {
         const int idx = rw * CT + i, T = idx >> 1, kk = idx & 1;
@@ -422,25 +439,31 @@ void k_gemm_big(GemmArgs a) {
     }
   };
   // One lane per 8 consecutive staged columns of a row (r = lane / 8, column
-  // group lane % 8: 16-column tile (lane % 8) / 2, half lane % 2), so the
-  // outputs go out as 16-byte pieces.
+  // group lane % 8, + 8 in a second pass when a wave stages 96 columns: the
+  // group's 16-column tile is group / 2, its half group % 2), so the outputs
+  // go out as 16-byte pieces.
   auto epi_part = [&](int cblock, int part) {
-    const int tile0 = (cblock * 2 + cw) * (kItemTiles / 2);
-    const int r = lane >> 3, grp = lane & 7;
-    const int t = grp >> 1, half = grp & 1;
-    const int tile = tile0 + t;
+    const int tile0 = (cblock * CW + cw) * TPW;
+    const int r = lane >> 3;
     const int ml = (rw * NP + part) * 8 + r;  // row within the launch
-    const bool row_ok = ml < rows, tile_ok = tile < a.n_tiles;
+    const bool row_ok = ml < rows;
     const int m = a.m_base + ml;
-    const float* src = stage + r * SROW + grp * 8;
     if (EPI == EPI_ARGMAX) {
       float v1 = -INFINITY, v2 = -INFINITY;
       int i1 = 0x7FFFFFFF;
-      const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int n = tile * 16 + half * 8 + e;
-        if (tile_ok && n < a.N) top2_merge(v1, i1, v2, e < 4 ? x0[e] : x1[e - 4], n, -INFINITY);
+      for (int gp = 0; gp < (C::NG + 7) / 8; ++gp) {
+        const int grp = gp * 8 + (lane & 7);
+        const int tile = tile0 + (grp >> 1), half = grp & 1;
+        if (grp < C::NG && tile < a.n_tiles) {
+          const float* src = stage + r * SROW + grp * 8;
+          const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int n = tile * 16 + half * 8 + e;
+            if (n < a.N) top2_merge(v1, i1, v2, e < 4 ? x0[e] : x1[e - 4], n, -INFINITY);
+          }
+        }
       }
 #pragma unroll
       for (int x = 1; x < 8; x <<= 1) {
@@ -448,7 +471,7 @@ void k_gemm_big(GemmArgs a) {
         const int oi = __shfl_xor(i1, x);
         top2_merge(v1, i1, v2, o1, oi, o2);
       }
-      if (grp == 0) {
+      if ((lane & 7) == 0) {
         float* s3 = my_amax + (part * 8 + r) * 3;
         float w1 = s3[0], w2 = s3[2];
         int wi = __float_as_int(s3[1]);
@@ -458,12 +481,12 @@ void k_gemm_big(GemmArgs a) {
         s3[2] = w2;
       }
     } else if (EPI == EPI_SILU) {
-      // lanes 0..31: row lane / 4, tile lane % 4; columns 0..7 of the tile are
-      // gate rows tile*8 + c, 8..15 the matching up rows
-      const int rs = lane >> 2, ts = lane & 3;
+      // lanes 0 .. 8 TPW - 1: row lane / TPW, tile lane % TPW; columns 0..7 of
+      // the tile are gate rows tile*8 + c, 8..15 the matching up rows
+      const int rs = lane / TPW, ts = lane % TPW;
       const int tile_s = tile0 + ts;
       const int ml_s = (rw * NP + part) * 8 + rs;
-      if (lane < 32 && tile_s < a.n_tiles && ml_s < rows) {
+      if (lane < 8 * TPW && tile_s < a.n_tiles && ml_s < rows) {
         const int ms = a.m_base + ml_s;
         const float* gsrc = stage + rs * SROW + ts * 16;
         const int F = a.N / 2;
@@ -496,31 +519,36 @@ void k_gemm_big(GemmArgs a) {
           }
         }
       }
-    } else if (EPI == EPI_QKV || a.partial) {
-      // K-slice partial sums (QKV: at the natural column of the operand; the
-      // 8 columns of a half tile are consecutive there)
-      if (row_ok && tile_ok) {
-        const int n0 = EPI == EPI_QKV ? col_row<EPI_QKV>(a.N, tile, half * 8) : tile * 16 + half * 8;
-        float* po = a.partial + ((size_t)ks * a.M + m) * a.N + n0;
-        if (n0 + 8 <= a.N && (a.N & 3) == 0) {
-          *(f32x4*)po = *(const f32x4*)src;
-          *(f32x4*)(po + 4) = *(const f32x4*)(src + 4);
-        } else {
-          for (int e = 0; e < 8 && n0 + e < a.N; ++e) po[e] = src[e];
-        }
-      }
     } else {
-      // y = v (+ bias + residual)
-      if (row_ok && tile_ok) {
-        const int n0 = tile * 16 + half * 8;
+#pragma unroll
+      for (int gp = 0; gp < (C::NG + 7) / 8; ++gp) {
+        const int grp = gp * 8 + (lane & 7);
+        const int tile = tile0 + (grp >> 1), half = grp & 1;
+        if (grp >= C::NG || !row_ok || tile >= a.n_tiles) continue;
+        const float* src = stage + r * SROW + grp * 8;
+        if (EPI == EPI_QKV || a.partial) {
+          // K-slice partial sums (QKV: at the natural column of the operand;
+          // the 8 columns of a half tile are consecutive there)
+          const int n0 = EPI == EPI_QKV ? col_row<EPI_QKV>(a.N, tile, half * 8) : tile * 16 + half * 8;
+          float* po = a.partial + ((size_t)ks * a.M + m) * a.N + n0;
+          if (n0 + 8 <= a.N && (a.N & 3) == 0) {
+            *(f32x4*)po = *(const f32x4*)src;
+            *(f32x4*)(po + 4) = *(const f32x4*)(src + 4);
+          } else {
+            for (int e = 0; e < 8 && n0 + e < a.N; ++e) po[e] = src[e];
+          }
+        } else {
+          // y = v (+ bias + residual)
+          const int n0 = tile * 16 + half * 8;
 #pragma unroll 1
-        for (int e = 0; e < 8; ++e) {
-          const int n = n0 + e;
-          if (n >= a.N) break;
-          float y = src[e];
-          if (a.bias) y += bf16_to_f32(a.bias[n]);
-          if (a.residual) y += a.residual[(size_t)m * a.ldy + n];
-          a.y[(size_t)m * a.ldy + n] = y;
+          for (int e = 0; e < 8; ++e) {
+            const int n = n0 + e;
+            if (n >= a.N) break;
+            float y = src[e];
+            if (a.bias) y += bf16_to_f32(a.bias[n]);
+            if (a.residual) y += a.residual[(size_t)m * a.ldy + n];
+            a.y[(size_t)m * a.ldy + n] = y;
+          }
         }
       }
     }
@@ -619,16 +647,16 @@ void k_gemm_big(GemmArgs a) {
   }
 
   if (EPI == EPI_ARGMAX) {
-    // merge the two column waves' row states (fixed order) and write one
-    // partial per row and workgroup (a workgroup without items writes -inf)
+    // merge the column waves' row states (fixed order) and write one partial
+    // per row and workgroup (a workgroup without items writes -inf)
     __syncthreads();
     if (cw == 0) {
       for (int r = lane; r < NP * 8; r += 64) {
         const int ml = (rw * NP) * 8 + r;
         float v1 = -INFINITY, v2 = -INFINITY;
         int i1 = 0x7FFFFFFF;
-        for (int w = 0; w < 2; ++w) {
-          const float* s3 = amax_lds + ((size_t)(rw * 2 + w) * NP * 8 + r) * 3;
+        for (int w = 0; w < CW; ++w) {
+          const float* s3 = amax_lds + ((size_t)(rw * CW + w) * NP * 8 + r) * 3;
           top2_merge(v1, i1, v2, s3[0], __float_as_int(s3[1]), s3[2]);
         }
         if (ml < rows) {
@@ -704,11 +732,11 @@ static int big_cus() {
   return n;
 }
 
-template <int RT, bool INT4>
+template <int RT, bool INT4, int LAY>
 static constexpr size_t wide_smem(int epi) {
-  using C = Wide<RT, INT4>;
-  return (size_t)C::NS * C::SLOT + kPfSink + (size_t)kWideWaves * 8 * (kItemTiles / 2 * 16 + 4) * 4 +
-         (epi == EPI_ARGMAX ? (size_t)kWideWaves * C::NP * 8 * 3 * 4 : 0);
+  using C = Wide<RT, INT4, LAY>;
+  return (size_t)C::NS * C::SLOT + kPfSink + (size_t)C::WAVES * 8 * (C::SW + 4) * 4 +
+         (epi == EPI_ARGMAX ? (size_t)C::WAVES * C::NP * 8 * 3 * 4 : 0);
 }
 
 // Rows per launch: 192 (bf16) or 64 (INT4).
@@ -724,20 +752,37 @@ bool use_big_gemm(int M, int K, bool int4) {
   return int4 ? M > 64 : M > 32;
 }
 
-// Row tiles per row wave for a launch of `rows` rows: INT4 4 tiles of 16
-// operand rows (64 rows); bf16 tiles of 32 operand rows (16 real rows).
-static int big_rt(int rows, bool int4) {
+// Wave grid of a GEMM (see Wide).
+static int big_lay(bool int4, int epi) {
+  if (int4) return 0;
+  return epi == EPI_SILU ? 1 : 0;
+}
+
+// Row tiles per row wave for a launch of `rows` rows: INT4 tiles of 16
+// operand rows (64 rows in all); bf16 tiles of 32 operand rows (16 real rows).
+static int big_rt(int rows, bool int4, int lay) {
   const int mt = (rows + 7) / 8;
-  if (int4) return 4;
-  return mt <= 8 ? 2 : mt <= 12 ? 3 : 6;
+  if (int4) return lay == 0 ? 4 : 2;
+  if (lay == 0) return mt <= 8 ? 2 : mt <= 12 ? 3 : 6;
+  return mt <= 8 ? 1 : mt <= 16 ? 2 : 3;
+}
+
+template <bool INT4, int LAY>
+static size_t big_smem(int rt, int epi) {
+  if (INT4) return LAY == 0 ? wide_smem<4, true, 0>(epi) : wide_smem<2, true, 2>(epi);
+  if (LAY == 0) return rt == 2 ? wide_smem<2, false, 0>(epi) : rt == 3 ? wide_smem<3, false, 0>(epi)
+                                                                     : wide_smem<6, false, 0>(epi);
+  return rt == 1 ? wide_smem<1, false, 1>(epi) : rt == 2 ? wide_smem<2, false, 1>(epi)
+                                                         : wide_smem<3, false, 1>(epi);
 }
 
 BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_split) {
   BigPlan p;
-  p.rt = big_rt(rows, int4);
-  p.ct = int4 ? 4 : 2;
+  p.lay = big_lay(int4, epi);
+  p.rt = big_rt(rows, int4, p.lay);
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
-  const int n_cb = (p.n_tiles + kItemTiles - 1) / kItemTiles;
+  const int item = int4 ? Wide<4, true, 0>::ITEM : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
+  const int n_cb = (p.n_tiles + item - 1) / item;
   const int cus = big_cus();
   const int units = int4 ? K / 128 : K / 32;
   const int dw = int4 ? Wide<4, true>::R : Wide<6, false>::R;  // stages per ring turn
@@ -769,33 +814,47 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   const int per = (n_cb + per_slice - 1) / per_slice;
   const int gt = (n_cb + per - 1) / per;
   p.grid = gt * p.ksplit;
-  p.threads = kWideWaves * 64;
-  p.smem = int4 ? wide_smem<4, true>(epi)
-                : (p.rt == 2 ? wide_smem<2, false>(epi) : p.rt == 3 ? wide_smem<3, false>(epi) : wide_smem<6, false>(epi));
+  p.threads = lay_threads(p.lay);
+  p.smem = int4 ? (p.lay == 0 ? big_smem<true, 0>(p.rt, epi) : big_smem<true, 2>(p.rt, epi))
+                : (p.lay == 0 ? big_smem<false, 0>(p.rt, epi) : big_smem<false, 1>(p.rt, epi));
   return p;
 }
 
-template <int RT, bool INT4, int EPI>
+template <int RT, bool INT4, int EPI, int LAY>
 static hipError_t launch_big_one(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<RT, INT4, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<RT, INT4, EPI, LAY>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_gemm_big<RT, INT4, EPI>), dim3(p.grid), dim3(p.threads), p.smem, s, a);
+  hipLaunchKernelGGL((k_gemm_big<RT, INT4, EPI, LAY>), dim3(p.grid), dim3(p.threads), p.smem, s, a);
   return hipGetLastError();
 }
 
-template <int RT, bool INT4>
+template <int RT, bool INT4, int LAY>
 static hipError_t launch_big_epi(const GemmArgs& a, int epi, const BigPlan& p, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_big_one<RT, INT4, EPI_STORE>(a, p, s);
-    case EPI_SILU: return launch_big_one<RT, INT4, EPI_SILU>(a, p, s);
-    case EPI_QKV: return launch_big_one<RT, INT4, EPI_QKV>(a, p, s);
-    default: return launch_big_one<RT, INT4, EPI_ARGMAX>(a, p, s);
+    case EPI_STORE: return launch_big_one<RT, INT4, EPI_STORE, LAY>(a, p, s);
+    case EPI_SILU: return launch_big_one<RT, INT4, EPI_SILU, LAY>(a, p, s);
+    case EPI_QKV: return launch_big_one<RT, INT4, EPI_QKV, LAY>(a, p, s);
+    default: return launch_big_one<RT, INT4, EPI_ARGMAX, LAY>(a, p, s);
   }
+}
+
+static hipError_t launch_big_plan(const GemmArgs& g, int epi, bool int4, const BigPlan& p,
+                                  hipStream_t s) {
+  if (int4) return p.lay == 0 ? launch_big_epi<4, true, 0>(g, epi, p, s)
+                              : launch_big_epi<2, true, 2>(g, epi, p, s);
+  if (p.lay == 0) {
+    if (p.rt == 2) return launch_big_epi<2, false, 0>(g, epi, p, s);
+    if (p.rt == 3) return launch_big_epi<3, false, 0>(g, epi, p, s);
+    return launch_big_epi<6, false, 0>(g, epi, p, s);
+  }
+  if (p.rt == 1) return launch_big_epi<1, false, 1>(g, epi, p, s);
+  if (p.rt == 2) return launch_big_epi<2, false, 1>(g, epi, p, s);
+  return launch_big_epi<3, false, 1>(g, epi, p, s);
 }
 
 hipError_t launch_gemm_big(GemmArgs a, int epi, bool int4, hipStream_t s) {
@@ -814,11 +873,7 @@ hipError_t launch_gemm_big(GemmArgs a, int epi, bool int4, hipStream_t s) {
     g.n_tiles = p.n_tiles;
     g.ksplit = p.ksplit;
     g.n_parts = p.grid;
-    hipError_t e;
-    if (int4) e = launch_big_epi<4, true>(g, epi, p, s);
-    else if (p.rt == 2) e = launch_big_epi<2, false>(g, epi, p, s);
-    else if (p.rt == 3) e = launch_big_epi<3, false>(g, epi, p, s);
-    else e = launch_big_epi<6, false>(g, epi, p, s);
+    const hipError_t e = launch_big_plan(g, epi, int4, p, s);
     if (e != hipSuccess) return e;
   }
   if (epi == EPI_QKV) {

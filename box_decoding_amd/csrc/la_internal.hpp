@@ -136,7 +136,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // through K-slice sums in `partial` and a finishing kernel.
 struct BigPlan {
   int n_tiles;
-  int rt, ct;  // row tiles (per row wave) and column tiles (per column wave)
+  int lay;     // wave grid
+  int rt;      // row tiles per row wave
   int ksplit;
   int grid, threads;
   size_t smem;
