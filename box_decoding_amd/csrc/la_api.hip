@@ -77,14 +77,14 @@ la_status check_gemm_weight(const la_weight* w, int tiled) {
 // beyond that the large-M kernel (whose first launch fixes the plan).
 int gemm_parts(int M, const la_weight* w, int epi) {
   const bool int4 = w->fmt == LA_W_INT4;
-  if (use_big_gemm(M, w->k, int4))
+  if (use_big_gemm(M, w->k, int4, epi))
     return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, epi, false).grid;
   return plan_gemm(M, w->n, w->k, int4, epi, false).grid;
 }
 
 int gemm_ksplit(int M, const la_weight* w) {
   const bool int4 = w->fmt == LA_W_INT4;
-  if (use_big_gemm(M, w->k, int4))
+  if (use_big_gemm(M, w->k, int4, EPI_STORE))
     return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_STORE, true).ksplit;
   return plan_gemm(M, w->n, w->k, int4, EPI_STORE, true).ksplit;
 }
@@ -93,7 +93,7 @@ int gemm_ksplit(int M, const la_weight* w) {
 // finishing kernel turns into q and the window's K/V (0: no slice buffer).
 int qkv_ksplit(int M, const la_weight* w) {
   const bool int4 = w->fmt == LA_W_INT4;
-  if (!use_big_gemm(M, w->k, int4)) return 0;
+  if (!use_big_gemm(M, w->k, int4, EPI_QKV)) return 0;
   return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_QKV, true).ksplit;
 }
 

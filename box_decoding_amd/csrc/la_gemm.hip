@@ -941,7 +941,7 @@ static hipError_t launch_gemm_fmt(const GemmArgs& a, int epi, const GemmPlan& p,
 }
 
 hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s) {
-  if (use_big_gemm(a.M, a.K, int4)) return launch_gemm_big(a, epi, int4, s);
+  if (use_big_gemm(a.M, a.K, int4, epi)) return launch_gemm_big(a, epi, int4, s);
   const GemmPlan p = plan_gemm(a.M, a.N, a.K, int4, epi, a.partial != nullptr);
   a.n_tiles = p.n_tiles;
   a.ksplit = p.ksplit;

@@ -743,20 +743,23 @@ static constexpr size_t wide_smem(int epi) {
 int big_rows_per_launch(bool int4) { return int4 ? 64 : 192; }
 
 // The large-M kernel serves bf16 GEMMs of more than 32 rows and INT4 ones of
-// more than 64.  Up to 64 INT4 rows the small-M kernel's two launches of 32
-// rows are faster: measured on a batch of 8 windows (48 rows), 4.9 ms per
-// 36-layer step against 6.1 ms, since this kernel's INT4 weight ring is only
-// two stages deep (its register budget is spent) and latency bound.
-bool use_big_gemm(int M, int K, bool int4) {
+// more than 64; from 33 to 64 INT4 rows it serves gate/up and the lm_head,
+// while the small-M kernel's two launches of 32 rows serve QKV, O and down
+// (measured at 48 rows: gate/up 36.5 against 43.6 us, the lm_head 173
+// against 268 us; O, down and QKV 8% slower here).
+bool use_big_gemm(int M, int K, bool int4, int epi) {
   (void)K;
-  return int4 ? M > 64 : M > 32;
+  if (!int4) return M > 32;
+  return M > 64 || (M > 32 && (epi == EPI_SILU || epi == EPI_ARGMAX));
 }
 
 // Wave grid of a GEMM (see Wide).  Measured at 192 rows: 96-column items
 // (4 x 1) for the projections (gate/up 56.5 -> 51.8 us; O, down and QKV a
 // little faster), 128-column items (2 x 2) for the lm_head (282 against 367 us).
+// INT4 runs eight waves (4 x 2): the dequantisation and per-group scaling of
+// one wave run beside the products of the other wave on its SIMD.
 static int big_lay(bool int4, int epi) {
-  if (int4) return 0;
+  if (int4) return 2;
   return epi == EPI_ARGMAX ? 0 : 1;
 }
 
@@ -764,14 +767,14 @@ static int big_lay(bool int4, int epi) {
 // operand rows (64 rows in all); bf16 tiles of 32 operand rows (16 real rows).
 static int big_rt(int rows, bool int4, int lay) {
   const int mt = (rows + 7) / 8;
-  if (int4) return lay == 0 ? 4 : 2;
+  if (int4) return 2;
   if (lay == 0) return mt <= 8 ? 2 : mt <= 12 ? 3 : 6;
   return mt <= 8 ? 1 : mt <= 16 ? 2 : 3;
 }
 
 template <bool INT4, int LAY>
 static size_t big_smem(int rt, int epi) {
-  if (INT4) return LAY == 0 ? wide_smem<4, true, 0>(epi) : wide_smem<2, true, 2>(epi);
+  if (INT4) return wide_smem<2, true, 2>(epi);
   if (LAY == 0) return rt == 2 ? wide_smem<2, false, 0>(epi) : rt == 3 ? wide_smem<3, false, 0>(epi)
                                                                      : wide_smem<6, false, 0>(epi);
   return rt == 1 ? wide_smem<1, false, 1>(epi) : rt == 2 ? wide_smem<2, false, 1>(epi)
@@ -783,11 +786,11 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   p.lay = big_lay(int4, epi);
   p.rt = big_rt(rows, int4, p.lay);
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
-  const int item = int4 ? Wide<4, true, 0>::ITEM : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
+  const int item = int4 ? Wide<2, true, 2>::ITEM : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
   const int n_cb = (p.n_tiles + item - 1) / item;
   const int cus = big_cus();
   const int units = int4 ? K / 128 : K / 32;
-  const int dw = int4 ? Wide<4, true>::R : Wide<6, false>::R;  // stages per ring turn
+  const int dw = int4 ? Wide<2, true, 2>::R : Wide<6, false>::R;  // stages per ring turn
   // K slices (QKV always writes slice sums; STORE when the caller takes them):
   // the fewest rounds of items times the padded stages of one item, plus the
   // slice sums' write and read-back counted in stage times (a stage of 192
@@ -817,7 +820,7 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   const int gt = (n_cb + per - 1) / per;
   p.grid = gt * p.ksplit;
   p.threads = lay_threads(p.lay);
-  p.smem = int4 ? (p.lay == 0 ? big_smem<true, 0>(p.rt, epi) : big_smem<true, 2>(p.rt, epi))
+  p.smem = int4 ? big_smem<true, 2>(p.rt, epi)
                 : (p.lay == 0 ? big_smem<false, 0>(p.rt, epi) : big_smem<false, 1>(p.rt, epi));
   return p;
 }
@@ -847,8 +850,7 @@ static hipError_t launch_big_epi(const GemmArgs& a, int epi, const BigPlan& p, h
 
 static hipError_t launch_big_plan(const GemmArgs& g, int epi, bool int4, const BigPlan& p,
                                   hipStream_t s) {
-  if (int4) return p.lay == 0 ? launch_big_epi<4, true, 0>(g, epi, p, s)
-                              : launch_big_epi<2, true, 2>(g, epi, p, s);
+  if (int4) return launch_big_epi<2, true, 2>(g, epi, p, s);
   if (p.lay == 0) {
     if (p.rt == 2) return launch_big_epi<2, false, 0>(g, epi, p, s);
     if (p.rt == 3) return launch_big_epi<3, false, 0>(g, epi, p, s);
