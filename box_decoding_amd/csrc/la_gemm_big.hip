@@ -758,9 +758,11 @@ bool use_big_gemm(int M, int K, bool int4, int epi) {
 // little faster), 128-column items (2 x 2) for the lm_head (282 against 367 us).
 // INT4 runs eight waves (4 x 2): the dequantisation and per-group scaling of
 // one wave run beside the products of the other wave on its SIMD.
-static int big_lay(bool int4, int epi) {
+static int big_lay(int rows, bool int4, int epi) {
   if (int4) return 2;
-  return epi == EPI_ARGMAX ? 0 : 1;
+  // 65..96 rows fill three 2 x 2 row tiles exactly, where 4 x 1 would pad to 128
+  const int mt = (rows + 7) / 8;
+  return epi == EPI_ARGMAX || (mt > 8 && mt <= 12) ? 0 : 1;
 }
 
 // Row tiles per row wave for a launch of `rows` rows: INT4 tiles of 16
@@ -783,7 +785,7 @@ static size_t big_smem(int rt, int epi) {
 
 BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_split) {
   BigPlan p;
-  p.lay = big_lay(int4, epi);
+  p.lay = big_lay(rows, int4, epi);
   p.rt = big_rt(rows, int4, p.lay);
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
   const int item = int4 ? Wide<2, true, 2>::ITEM : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
