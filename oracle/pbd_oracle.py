@@ -171,21 +171,30 @@ def cache_read(cache, layer, b, n, dtype=np.float64):
     return bf16_to_float(k, dtype), bf16_to_float(v, dtype)
 
 
-def window_attention(q, k, v, dtype=np.float64):
+def window_attention(q, k, v, dtype=np.float64, causal=False):
     """Attention of the W window rows over n keys (prefix + window).
 
     q: [W, Hq, D]; k, v: [n, Hkv, D].  Every window row sees all n keys: the
     prefix is before it (causal) and the window is bidirectional.  Query head h
     reads KV head h // (Hq / Hkv).  softmax(q.k / sqrt(D)) . v.
+
+    causal=True is the causal window of the RK3588 conversion ("LocateAnything-3B
+    for RK3588 (RKLLM + RKNN)", "How it differs from the original", item 1):
+    window row j sees the prefix and window rows 0..j only, i.e. the first
+    n - W + j + 1 keys.
     """
     W, Hq, D = q.shape
     Hkv = k.shape[1]
+    n = k.shape[0]
     G = Hq // Hkv
     out = np.zeros((W, Hq, D), dtype=dtype)
     scale = 1.0 / np.sqrt(D)
     for h in range(Hq):
         kv = h // G
         s = (q[:, h, :] @ k[:, kv, :].T) * scale        # [W, n]
+        if causal:
+            for j in range(W):
+                s[j, n - W + j + 1:] = -np.inf
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p = p / p.sum(axis=1, keepdims=True)
@@ -197,7 +206,8 @@ def window_attention(q, k, v, dtype=np.float64):
 # Decoder layer, lm_head, step
 # ---------------------------------------------------------------------------
 
-def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float64, parts=None):
+def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float64, parts=None,
+                  causal=False):
     """One decoder layer on the window rows of every sequence.
 
     h: [B*W, H] hidden states (row b*W + j is window position j of sequence b).
@@ -241,7 +251,7 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
         kp, vp = cache_read(cache, layer, b, int(P[b]), dtype)
         kk = np.concatenate([kp, kw[rows]], axis=0)
         vv = np.concatenate([vp, vw[rows]], axis=0)
-        o[rows] = window_attention(q[rows], kk, vv, dtype)
+        o[rows] = window_attention(q[rows], kk, vv, dtype, causal=causal)
 
     h1 = h + o.reshape(T, Hq * D) @ decode_weight(lay["o"], dtype=dtype).T
     a2 = rmsnorm(h1, bf16_to_float(lay["post_norm"], dtype), eps)
@@ -285,7 +295,7 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64):
 
 
 def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidden=False,
-             layers=None):
+             layers=None, causal=False):
     """One PBD window step for every sequence.
 
     window_ids [B, W] -> per-position argmax ids [B, W] and top-2 gaps [B, W].
@@ -299,7 +309,8 @@ def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidd
     kv = []
     n_layers = len(model["layers"]) if layers is None else layers
     for l in range(n_layers):
-        h, kb, vb = decoder_layer(h, model["layers"][l], dims, cache, l, prefix_len, W, dtype)
+        h, kb, vb = decoder_layer(h, model["layers"][l], dims, cache, l, prefix_len, W, dtype,
+                                  causal=causal)
         kv.append((kb, vb))
     f = rmsnorm(h, bf16_to_float(model["final_norm"], dtype), float(_dim(dims, "rms_eps")))
     lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]

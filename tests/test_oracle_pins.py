@@ -178,6 +178,50 @@ def test_window_is_bidirectional():
             assert np.abs(a[P:P + j] - b[P:P + j]).max() == 0.0
 
 
+@pytest.mark.parametrize("P,W", [(0, 6), (5, 6), (13, 6), (7, 4)])
+def test_causal_window_equals_dense_causal_bruteforce(P, W):
+    # the RK3588 page's causal window: a plain lower-triangular mask over prefix
+    # and window together; brute force and torch SDPA's is_causal (a library
+    # routine) fix it
+    Hq, Hkv, D = 4, 2, 8
+    N = P + W
+    q = _rand((N, Hq, D), 61)
+    k = _rand((N, Hkv, D), 62)
+    v = _rand((N, Hkv, D), 63)
+    ref = _dense_bruteforce(q, k, v, np.tril(np.ones((N, N), dtype=bool)), Hq // Hkv)
+    got = O.window_attention(q[P:], k, v, causal=True)
+    np.testing.assert_allclose(got, ref[P:], rtol=1e-12, atol=1e-12)
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1)).permute(1, 0, 2)[None]
+    sd = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    np.testing.assert_allclose(got, sd[0].permute(1, 0, 2).numpy()[P:], rtol=1e-12, atol=1e-12)
+
+
+def test_causal_window_special_cases():
+    Hq, Hkv, D, P, W = 4, 2, 8, 10, 6
+    N = P + W
+    q = _rand((W, Hq, D), 71)
+    k = _rand((N, Hkv, D), 72)
+    v = _rand((N, Hkv, D), 73)
+    causal = O.window_attention(q, k, v, causal=True)
+    bidir = O.window_attention(q, k, v)
+    # the last window row sees every key either way; the others differ
+    np.testing.assert_array_equal(causal[W - 1], bidir[W - 1])
+    assert np.abs(causal[0] - bidir[0]).max() > 1e-6
+    # W = 1: the two masks are one
+    np.testing.assert_array_equal(O.window_attention(q[:1], k[:P + 1], v[:P + 1], causal=True),
+                                  O.window_attention(q[:1], k[:P + 1], v[:P + 1]))
+    # changing window key j changes rows j.. only
+    for j in range(1, W):
+        k2, v2 = k.copy(), v.copy()
+        k2[P + j] += 0.5
+        v2[P + j] += 0.5
+        pert = O.window_attention(q, k2, v2, causal=True)
+        assert np.abs(pert[:j] - causal[:j]).max() == 0.0
+        assert np.abs(pert[j] - causal[j]).max() > 1e-6
+
+
 def test_equal_scores_give_mean_of_values():
     Hq, Hkv, D, n = 4, 2, 8, 9
     q = np.zeros((3, Hq, D))
