@@ -310,6 +310,33 @@ def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
 
 
+def causal_leg(B, synth, torch, model, dev, timed, args):
+    """The batch-1 step with the RK3588 conversion's causal window (window row j
+    sees the prefix and window rows 0..j) instead of the bidirectional one."""
+    w = synth.WORKLOADS["step_b1_p1280"]
+    d = w.dims
+    log("bench: causal-window leg")
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    dmc = B.DeviceModel(model, causal_window=True)
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
+    graph = B.StepGraph(dmc, dc, ids, Pd, int(P.max()) + w.window, out_ids, out_gap, ws=ws)
+    for _ in range(max(2, args.warmup)):
+        graph.replay()
+    steps = max(5, args.steps // 3)
+    ms_step, _ = timed(graph.replay, steps)
+    log(f"bench: causal window, batch 1: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": w.name, "window_mask": "causal", "steps": steps,
+            "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,7 +348,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
     ap.add_argument("--no-extra-legs", action="store_true",
-                    help="skip the emission-loop and prefix-32768 legs")
+                    help="skip the emission-loop, prefix-32768 and causal-window legs")
     ap.add_argument("--no-batch32", action="store_true",
                     help="skip the batch-32 leg reported beside the batch-1 step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -467,6 +494,7 @@ def main():
         # the other bf16 workloads on the same model
         result["emission_loop"] = emission_leg(B, synth, torch, dm, model, dev, stream, args)
         result["prefix_32768"] = probe_leg(B, synth, torch, dm, model, dev, stream, timed, args)
+        result["causal_window"] = causal_leg(B, synth, torch, model, dev, timed, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)

@@ -21,12 +21,14 @@ LA_W_BF16, LA_W_INT4 = 0, 1
 LA_EPI_NONE, LA_EPI_SILU_GATE = 0, 1
 LA_DERR_TOKEN_ID, LA_DERR_CAPACITY, LA_DERR_BLOCK_ID = 1, 2, 4
 LA_LAYOUT_ROWS, LA_LAYOUT_TILED, LA_LAYOUT_TILED_GU, LA_LAYOUT_TILED_QKV = 0, 1, 2, 3
+LA_MASK_BIDIRECTIONAL, LA_MASK_CAUSAL = 0, 1
 
 EXPORTED = [
     "la_int4_embed_gather", "la_wgemm_workspace", "la_wgemm", "la_pbd_attention_workspace",
     "la_pbd_attention", "la_lm_head_argmax_workspace", "la_lm_head_argmax", "la_pbd_layer",
     "la_pbd_step_workspace", "la_pbd_step", "la_status_str", "la_pack_weight_bytes",
     "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
+    "la_pbd_attention_masked",
 ]
 
 
@@ -46,7 +48,7 @@ class LaModel(ctypes.Structure):
                 ("head_dim", c_int32), ("inter", c_int32), ("n_layers", c_int32),
                 ("vocab", c_int32), ("rms_eps", c_float), ("rope_theta", c_float),
                 ("layers", POINTER(LaLayer)), ("embed", LaWeight), ("lm_head", LaWeight),
-                ("final_norm", c_void_p)]
+                ("final_norm", c_void_p), ("window_mask", c_int32)]
 
 
 class LaKvCache(ctypes.Structure):
@@ -104,6 +106,10 @@ def load() -> ctypes.CDLL:
                                       c_void_p]),
         "la_pbd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                     c_void_p]),
+        "la_pbd_attention_masked": (c_int32, [c_void_p, POINTER(LaKvCache), c_int32, c_int32,
+                                              c_int32, c_int32, c_void_p, c_int32, c_int32,
+                                              c_int32, c_int32, c_void_p, c_void_p, c_size_t,
+                                              c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -209,7 +215,9 @@ def _ws(ws: Optional[Workspace]) -> Workspace:
 class DeviceModel:
     """A model dict (from synth.make_model, tensors on the GPU) plus its ABI struct."""
 
-    def __init__(self, model: dict):
+    def __init__(self, model: dict, causal_window: bool = False):
+        # causal_window: window row j sees the prefix and window rows 0..j (the
+        # RK3588 conversion's mask) instead of the whole window
         d: synth.ModelDims = model["dims"]
         self.model = model
         self.dims = d
@@ -224,7 +232,8 @@ class DeviceModel:
                               d.vocab, d.rms_eps, d.rope_theta,
                               ctypes.cast(self.layers, POINTER(LaLayer)),
                               weight_desc(model["embed"]), weight_desc(model.get("lm_head")),
-                              _ptr(model["final_norm"]))
+                              _ptr(model["final_norm"]),
+                              LA_MASK_CAUSAL if causal_window else LA_MASK_BIDIRECTIONAL)
 
 
 class DeviceCache:
@@ -303,15 +312,21 @@ def wgemm_packed(packed: torch.Tensor, M: int, w: dict, bias=None, residual=None
 
 def pbd_attention(q: torch.Tensor, cache: DeviceCache, layer: int, n_heads: int, n_kv_heads: int,
                   prefix_len: torch.Tensor, B: int, W: int, max_len: int,
-                  ws: Optional[Workspace] = None) -> torch.Tensor:
+                  ws: Optional[Workspace] = None, causal_window: bool = False) -> torch.Tensor:
     lib = load()
     _require_cuda(q, prefix_len)
     out = torch.empty_like(q)
     need = lib.la_pbd_attention_workspace(B, W, n_heads, n_kv_heads, 128, max_len)
     buf = _ws(ws).get(need)
-    _check(lib.la_pbd_attention(_ptr(q), ctypes.byref(cache.struct), layer, n_heads, n_kv_heads, 128,
-                                _ptr(prefix_len), B, W, max_len, _ptr(out), _ptr(buf), buf.numel(),
-                                _stream()), "la_pbd_attention")
+    if causal_window:
+        _check(lib.la_pbd_attention_masked(_ptr(q), ctypes.byref(cache.struct), layer, n_heads,
+                                           n_kv_heads, 128, _ptr(prefix_len), B, W, max_len,
+                                           LA_MASK_CAUSAL, _ptr(out), _ptr(buf), buf.numel(),
+                                           _stream()), "la_pbd_attention_masked")
+    else:
+        _check(lib.la_pbd_attention(_ptr(q), ctypes.byref(cache.struct), layer, n_heads, n_kv_heads,
+                                    128, _ptr(prefix_len), B, W, max_len, _ptr(out), _ptr(buf),
+                                    buf.numel(), _stream()), "la_pbd_attention")
     return out
 
 

@@ -163,6 +163,7 @@ la_status check_model(const la_model* m) {
   const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
   const int fmt = m->layers[0].qkv.fmt;
   if (fmt != LA_W_BF16 && fmt != LA_W_INT4) return LA_ERR_ARG;
+  if (m->window_mask != LA_MASK_BIDIRECTIONAL && m->window_mask != LA_MASK_CAUSAL) return LA_ERR_ARG;
   for (int l = 0; l < m->n_layers; ++l) {
     const la_layer& L = m->layers[l];
     if (!L.in_norm || !L.post_norm) return LA_ERR_ARG;
@@ -352,6 +353,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   at.out = (int4 || attn_out) ? (attn_out ? attn_out : s.o) : nullptr;
   at.out_apack = int4 ? nullptr : s.apack_o;
   at.out_int4 = false;
+  at.causal = m->window_mask == LA_MASK_CAUSAL;
   LA_TRY(launch_attention(at, st));
   if (int4)
     if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true, nullptr, 0, nullptr,
@@ -601,7 +603,18 @@ la_status la_pbd_attention(const float* q, const la_kv_cache* kv, int32_t layer,
                            int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
                            int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
+  return la_pbd_attention_masked(q, kv, layer, n_heads, n_kv_heads, head_dim, prefix_len, B, W,
+                                 max_len, LA_MASK_BIDIRECTIONAL, out, workspace, workspace_bytes,
+                                 stream);
+}
+
+la_status la_pbd_attention_masked(const float* q, const la_kv_cache* kv, int32_t layer,
+                                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
+                                  int32_t window_mask, float* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
   if (!q || !out || !prefix_len) return LA_ERR_ARG;
+  if (window_mask != LA_MASK_BIDIRECTIONAL && window_mask != LA_MASK_CAUSAL) return LA_ERR_ARG;
   la_status st = check_cache(kv, nullptr, B);
   if (st != LA_OK) return st;
   if (head_dim != kHeadDim || n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads)
@@ -634,6 +647,7 @@ la_status la_pbd_attention(const float* q, const la_kv_cache* kv, int32_t layer,
   at.part_o = c.take<float>(units * kHeadDim);
   at.part_ml = c.take<float>(units * 2);
   at.out = out;
+  at.causal = window_mask == LA_MASK_CAUSAL;
   return hip_status(launch_attention(at, stream));
 }
 

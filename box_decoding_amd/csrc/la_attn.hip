@@ -4,7 +4,8 @@
 // prefix lies before it and the window is bidirectional, so one key bound
 // serves all rows and no per-element mask exists ("LocateAnything-3B for RK3588
 // (RKLLM + RKNN)", "How it differs from the original", item 1; the Jetson
-// page, section 1.3, block mask).
+// page, section 1.3, block mask).  The causal window that RK3588 conversion
+// runs instead (same item) is a per-row bound: row j sees slots 0 .. P_b+j.
 //
 // Work split: a workgroup takes one run of pages of one (sequence, KV head),
 // one wave per tile of 16 query columns.  The 8 query heads of a KV head times
@@ -98,8 +99,9 @@ __device__ __forceinline__ bf16x8 cat_s16x4(s16x4 a, s16x4 b) {
 }
 
 // One pair of pages (keys p0 .. p0 + nvalid - 1 valid, nvalid >= 1) into the
-// running state.
-__device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, const bf16x8 (&qh)[4],
+// running state; this lane's query column sees the first nsc <= nvalid of
+// them (fewer under the causal window, possibly none).
+__device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, int nsc, const bf16x8 (&qh)[4],
                                           const bf16x8 (&ql)[4], AttnState& st) {
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const float sl2 = 0.08838834764831845f * 1.4426950408889634f;  // log2(e) / sqrt(128)
@@ -124,8 +126,8 @@ __device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, const bf16x8
   float sc[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sc[e] = 4 * g + e < nvalid ? (ah[e] + al[e]) * sl2 : -INFINITY;
-    sc[4 + e] = kBlock + 4 * g + e < nvalid ? (bh[e] + bl[e]) * sl2 : -INFINITY;
+    sc[e] = 4 * g + e < nsc ? (ah[e] + al[e]) * sl2 : -INFINITY;
+    sc[4 + e] = kBlock + 4 * g + e < nsc ? (bh[e] + bl[e]) * sl2 : -INFINITY;
   }
   float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                    fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -133,7 +135,8 @@ __device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, const bf16x8
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(st.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);  // 0 while st.m is -inf
+    // 0 while st.m is -inf (mnew too may be -inf: a column that saw no key yet)
+    const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mnew);
     st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
@@ -142,7 +145,7 @@ __device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, const bf16x8
   float p[8], ps = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = __builtin_amdgcn_exp2f(sc[e] - st.m);
+    p[e] = sc[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[e] - st.m);
     ps += p[e];
   }
   st.l += ps;
@@ -227,6 +230,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LA == 1 && 
     }
   }
   const int n_keys = attn_keys(a, b);
+  // keys this lane's query column sees: all of them, or under the causal
+  // window the prefix and the window rows up to its own (at least one key)
+  const int kcol = a.causal ? max(min(n_keys, a.prefix_len[b] + (qi < NQ ? qi : 0) / G + 1), min(n_keys, 1))
+                            : n_keys;
   if (k0 >= n_keys) {  // uniform over the workgroup
     if (direct && qi < NQ && (g & 1) == 0) {
       const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -294,7 +301,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LA == 1 && 
     copy_pair(c + LA);  // into the slot of pair c - 1
     PairRegs pr;
     read_pair(ring + (c % NSP) * kPairBytes, pr);
-    attn_pair(pr, k1 - (k0 + 2 * c * kBlock), qh, ql, st);
+    const int p0 = k0 + 2 * c * kBlock;
+    attn_pair(pr, k1 - p0, min(k1, kcol) - p0, qh, ql, st);
   }
   float lsum = st.l;
   lsum += __shfl_xor(lsum, 16);
@@ -405,7 +413,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       if (s0 + i * kMergeGroups < ns) {
-        const float w = exp2f(m[i].x - bm);
+        const float w = m[i].x == -INFINITY ? 0.f : exp2f(m[i].x - bm);
         acc.den += w * m[i].y;
         acc.num.x += w * o[i].x; acc.num.y += w * o[i].y;
         acc.num.z += w * o[i].z; acc.num.w += w * o[i].w;

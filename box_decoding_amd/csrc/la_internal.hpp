@@ -86,6 +86,7 @@ struct AttnArgs {
   uint16_t* out_apack;       // packed output for the next GEMM (nullable)
   bool out_int4;
   int nqp;                   // padded queries per kv head (multiple of 16)
+  int causal;                // nonzero: window row j sees slots 0 .. P_b + j only
 };
 
 struct PrologueArgs {

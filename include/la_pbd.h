@@ -114,7 +114,15 @@ typedef struct {
   la_weight embed;
   la_weight lm_head;
   const uint16_t* final_norm;
+  int32_t window_mask;  /* LA_MASK_BIDIRECTIONAL (0) or LA_MASK_CAUSAL */
 } la_model;
+
+/* Attention mask inside the window.  Bidirectional is the PBD window of the
+ * original model (Jetson page, Part 1 section 1.3); causal is the mask the
+ * RK3588 conversion evaluates it with ("LocateAnything-3B for RK3588 (RKLLM +
+ * RKNN)", "How it differs from the original", item 1): window row j sees the
+ * prefix and window rows 0..j. */
+enum { LA_MASK_BIDIRECTIONAL = 0, LA_MASK_CAUSAL = 1 };
 
 /* Paged bf16 KV cache (the pages' KV graph keeps [1, 2, seq, 128] per layer;
  * here the sequence axis is paged in blocks of `block_size` = 16 tokens):
@@ -191,6 +199,14 @@ la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, con
  * are ignored. */
 size_t la_pbd_attention_workspace(int32_t B, int32_t W, int32_t n_heads, int32_t n_kv_heads,
                                   int32_t head_dim, int32_t max_len);
+/* The same with the window mask chosen: LA_MASK_BIDIRECTIONAL (as
+ * la_pbd_attention) or LA_MASK_CAUSAL (window row j sees slots 0 .. P_b + j).
+ * Any other value returns LA_ERR_ARG. */
+la_status la_pbd_attention_masked(const float* q, const la_kv_cache* kv, int32_t layer,
+                                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
+                                  int32_t window_mask, float* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 la_status la_pbd_attention(const float* q, const la_kv_cache* kv, int32_t layer, int32_t n_heads,
                            int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
                            int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,

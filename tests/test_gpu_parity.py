@@ -126,7 +126,7 @@ def test_wgemm_is_deterministic():
 
 # ---------------------------------------------------------------- attention
 
-def _attention_case(P_list, W, seed, max_len=None, poison=True):
+def _attention_case(P_list, W, seed, max_len=None, poison=True, causal=False):
     d = synth.ModelDims(n_layers=2)
     P = torch.tensor(P_list, dtype=torch.int32)
     cache = synth.make_cache(d, P, W, extra_tokens=5, seed=seed, device=DEV)
@@ -137,14 +137,15 @@ def _attention_case(P_list, W, seed, max_len=None, poison=True):
                     generator=torch.Generator(device=DEV).manual_seed(seed))
     ml = max_len or (max(P_list) + W)
     dc = B.DeviceCache(cache, d.n_layers)
-    out = B.pbd_attention(q, dc, 1, d.n_heads, d.n_kv_heads, P.to(DEV), Bn, W, ml)
+    out = B.pbd_attention(q, dc, 1, d.n_heads, d.n_kv_heads, P.to(DEV), Bn, W, ml,
+                          causal_window=causal)
     torch.cuda.synchronize()
     cn = np_tree(cache)
     qn = q.cpu().numpy().astype(np.float64).reshape(Bn, W, d.n_heads, d.head_dim)
     errs = []
     for b in range(Bn):
         k, v = O.cache_read(cn, 1, b, P_list[b] + W)
-        ref = O.window_attention(qn[b], k, v)
+        ref = O.window_attention(qn[b], k, v, causal=causal)
         got = out.cpu().numpy().reshape(Bn, W, d.n_heads, d.head_dim)[b]
         assert np.all(np.isfinite(got))
         errs.append(rel_l2(got, ref))
@@ -159,6 +160,16 @@ def _attention_case(P_list, W, seed, max_len=None, poison=True):
 def test_attention_matches_oracle(P_list, W):
     errs = _attention_case(P_list, W, seed=sum(P_list) + W)
     _log(f"attention P={P_list} W={W}: rel-L2 max {max(errs):.2e}")
+    assert max(errs) <= TOL_BF16
+
+
+@pytest.mark.parametrize("P_list,W", [([0, 37, 300], 6), ([31, 5, 16], 6), ([5, 16, 17, 4096], 6),
+                                      ([100, 9], 1), ([63, 64], 4), ([200], 8), ([1280], 6)])
+def test_attention_causal_window_matches_oracle(P_list, W):
+    # the causal window: row j sees slots 0 .. P + j; P = 31 puts a run boundary
+    # inside the window, so one run holds no key some columns may see
+    errs = _attention_case(P_list, W, seed=sum(P_list) + 3 * W, causal=True)
+    _log(f"causal attention P={P_list} W={W}: rel-L2 max {max(errs):.2e}")
     assert max(errs) <= TOL_BF16
 
 
@@ -256,7 +267,7 @@ def test_layer_batch8_large_m(fmt):
 
 # ---------------------------------------------------------------- whole step
 
-def _step_case(d, fmt, P_list, W, seed, mask_id=None):
+def _step_case(d, fmt, P_list, W, seed, mask_id=None, causal=False):
     model = synth.make_model(d, fmt, seed, DEV)
     P = torch.tensor(P_list, dtype=torch.int32)
     cache = synth.make_cache(d, P, W, seed=seed + 1, device=DEV)
@@ -264,12 +275,12 @@ def _step_case(d, fmt, P_list, W, seed, mask_id=None):
     ids = synth.draw_window_ids(len(P_list), W, d.vocab, seed + 2, mask_id=mask_id, device=DEV)
     mn, cn = np_tree(model), np_tree(cache)
     mn["dims"] = d
-    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    dm, dc = B.DeviceModel(model, causal_window=causal), B.DeviceCache(cache, d.n_layers)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     out_ids, gap, hid = B.pbd_step(dm, dc, ids, P.to(DEV), int(P.max()) + W, want_hidden=True,
                                    err=err)
     torch.cuda.synchronize()
-    ref = O.pbd_step(mn, cn, ids.cpu().numpy(), P.numpy(), return_hidden=True)
+    ref = O.pbd_step(mn, cn, ids.cpu().numpy(), P.numpy(), return_hidden=True, causal=causal)
     return out_ids.cpu().numpy(), gap.cpu().numpy(), hid.cpu().numpy(), ref, int(err.item())
 
 
@@ -345,6 +356,21 @@ def test_step_full_b1_p1280():
          f" ids {out_ids.cpu().numpy().tolist()} gaps {np.round(ref['gap'], 4).tolist()}")
     assert bad == 0
     assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("fmt,B_", [("bf16", 3), ("int4", 3), ("bf16", 32)])
+def test_step_causal_window(fmt, B_):
+    # the RK3588 conversion's causal window through the whole step
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    P_list = [0, 31, 450] if B_ == 3 else [int(p) for p in torch.randint(
+        0, 700, (B_,), generator=torch.Generator().manual_seed(7))]
+    got_ids, got_gap, hid, ref, err = _step_case(d, fmt, P_list, 6, seed=130 + B_, causal=True)
+    n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
+    e = rel_l2(hid, ref["hidden"])
+    _log(f"causal step {fmt} B={B_}: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
+    assert err == 0
+    assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+    assert bad == 0
 
 
 @pytest.mark.parametrize("W", [1, 8])
