@@ -48,6 +48,7 @@ __all__ = [
     "bf16_to_float", "fp16_to_float", "round_to_bf16_bits", "int4_dequant", "decode_weight",
     "embed_rows", "rmsnorm", "silu", "rope_angles", "rope_apply", "window_attention",
     "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "pbd_emission_loop",
+    "refeed_commit", "pbd_refeed_loop",
 ]
 
 
@@ -171,30 +172,44 @@ def cache_read(cache, layer, b, n, dtype=np.float64):
     return bf16_to_float(k, dtype), bf16_to_float(v, dtype)
 
 
-def window_attention(q, k, v, dtype=np.float64, causal=False):
+def window_attention(q, k, v, dtype=np.float64, causal=False, causal_rows=0, window_len=None):
     """Attention of the W window rows over n keys (prefix + window).
 
-    q: [W, Hq, D]; k, v: [n, Hkv, D].  Every window row sees all n keys: the
-    prefix is before it (causal) and the window is bidirectional.  Query head h
-    reads KV head h // (Hq / Hkv).  softmax(q.k / sqrt(D)) . v.
+    q: [W, Hq, D]; k, v: [n, Hkv, D] with the W window rows' keys last.  Every
+    window row sees all n keys: the prefix is before it (causal) and the window
+    is bidirectional.  Query head h reads KV head h // (Hq / Hkv).
+    softmax(q.k / sqrt(D)) . v.
 
     causal=True is the causal window of the RK3588 conversion ("LocateAnything-3B
     for RK3588 (RKLLM + RKNN)", "How it differs from the original", item 1):
     window row j sees the prefix and window rows 0..j only, i.e. the first
     n - W + j + 1 keys.
+
+    A re-fed window puts accepted tokens, attended causally, before the
+    bidirectional block (the same page, same item: the accepted tokens are
+    sent again with the mask tokens each step).  Its first ``causal_rows`` rows
+    are the re-fed tokens: row j < causal_rows sees the prefix and window rows
+    0..j.  The rows from causal_rows up to ``window_len`` (default W) are the
+    block: each sees the prefix and window rows 0..window_len-1.  Rows at or
+    past window_len are padding that no real row sees; they see what the block
+    sees.  causal=True is causal_rows = W.
     """
     W, Hq, D = q.shape
     Hkv = k.shape[1]
     n = k.shape[0]
+    P = n - W
     G = Hq // Hkv
+    c = W if causal else int(causal_rows)
+    w = W if window_len is None else int(window_len)
+    assert 0 <= c <= W and 1 <= w <= W and P >= 0
     out = np.zeros((W, Hq, D), dtype=dtype)
     scale = 1.0 / np.sqrt(D)
     for h in range(Hq):
         kv = h // G
         s = (q[:, h, :] @ k[:, kv, :].T) * scale        # [W, n]
-        if causal:
-            for j in range(W):
-                s[j, n - W + j + 1:] = -np.inf
+        for j in range(W):
+            last = j if j < c else w - 1                 # the last window row row j sees
+            s[j, P + last + 1:] = -np.inf
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p = p / p.sum(axis=1, keepdims=True)
@@ -207,10 +222,12 @@ def window_attention(q, k, v, dtype=np.float64, causal=False):
 # ---------------------------------------------------------------------------
 
 def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float64, parts=None,
-                  causal=False):
+                  causal=False, causal_rows=None, window_len=None):
     """One decoder layer on the window rows of every sequence.
 
     h: [B*W, H] hidden states (row b*W + j is window position j of sequence b).
+    causal_rows / window_len: per-sequence [B] re-fed rows and window lengths
+    of a re-fed window (window_attention), None for the plain window.
     Returns (h_out, k_bits, v_bits) where k_bits/v_bits [B*W, Hkv, D] are the
     bf16 K/V the step stores at slots P_b + j.  ``parts`` (a dict) receives
     intermediate values when given.
@@ -251,7 +268,10 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
         kp, vp = cache_read(cache, layer, b, int(P[b]), dtype)
         kk = np.concatenate([kp, kw[rows]], axis=0)
         vv = np.concatenate([vp, vw[rows]], axis=0)
-        o[rows] = window_attention(q[rows], kk, vv, dtype, causal=causal)
+        o[rows] = window_attention(
+            q[rows], kk, vv, dtype, causal=causal,
+            causal_rows=0 if causal_rows is None else int(causal_rows[b]),
+            window_len=None if window_len is None else int(window_len[b]))
 
     h1 = h + o.reshape(T, Hq * D) @ decode_weight(lay["o"], dtype=dtype).T
     a2 = rmsnorm(h1, bf16_to_float(lay["post_norm"], dtype), eps)
@@ -295,10 +315,11 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64):
 
 
 def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidden=False,
-             layers=None, causal=False):
+             layers=None, causal=False, causal_rows=None, window_len=None):
     """One PBD window step for every sequence.
 
     window_ids [B, W] -> per-position argmax ids [B, W] and top-2 gaps [B, W].
+    causal_rows / window_len [B] make it a re-fed window (window_attention).
     The step writes nothing into ``cache``; it returns the bf16 K/V it would
     store at slots P_b .. P_b+W-1 of each layer.
     """
@@ -310,7 +331,7 @@ def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidd
     n_layers = len(model["layers"]) if layers is None else layers
     for l in range(n_layers):
         h, kb, vb = decoder_layer(h, model["layers"][l], dims, cache, l, prefix_len, W, dtype,
-                                  causal=causal)
+                                  causal=causal, causal_rows=causal_rows, window_len=window_len)
         kv.append((kb, vb))
     f = rmsnorm(h, bf16_to_float(model["final_norm"], dtype), float(_dim(dims, "rms_eps")))
     lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
@@ -350,3 +371,73 @@ def pbd_emission_loop(model, cache, window_ids, prefix_len, steps, mask_id, dtyp
         ids = np.full((B, W), mask_id, dtype=np.int32)
         ids[:, 0] = r["ids"][:, W - 1]
     return outs, P, c
+
+
+def refeed_commit(out_ids, window_ids, prefix_len, causal_rows, window_len, block, mask_id,
+                  n_accept=None):
+    """The next re-fed window after a step of a decode loop that re-feeds what it accepts.
+
+    Sequence b's block is rows c_b .. w_b - 1 of its window.  Window row i sits
+    at position P_b + i and its argmax is read as the token after it, so the
+    block's outputs are the tokens at P_b + c_b + 1 onwards.  The first n_b of
+    them are accepted (all S_b = w_b - c_b when n_accept is None; n_b is clamped
+    to 1 .. S_b).  Every row up to the block's first is then final, and the next
+    window starts right after it, re-feeding the accepted tokens; the last of
+    them opens a new block of ``block`` rows with block - 1 mask tokens:
+        ids'_b = [out_b[c_b] .. out_b[c_b + n_b - 1], mask x (block - 1), mask ...]
+        c'_b = n_b - 1,  w'_b = n_b + block - 1,  P'_b = P_b + c_b + 1.
+    The window keeps its width W (w'_b <= W is required).  Source: "LocateAnything-3B
+    for RK3588 (RKLLM + RKNN)", "How it differs from the original", item 1 (the
+    accepted tokens and the mask tokens are sent each step, the cached common
+    prefix is reused).  Returns (ids', P', c', w').
+    """
+    out = np.asarray(out_ids)
+    B, W = np.asarray(window_ids).shape
+    P = np.asarray(prefix_len, dtype=np.int64)
+    c = np.asarray(causal_rows, dtype=np.int64)
+    w = np.asarray(window_len, dtype=np.int64)
+    ids = np.full((B, W), mask_id, dtype=np.int32)
+    P2 = np.zeros(B, dtype=np.int64)
+    c2 = np.zeros(B, dtype=np.int64)
+    w2 = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        S = int(w[b] - c[b])
+        n = S if n_accept is None else min(max(int(n_accept[b]), 1), S)
+        assert n + block - 1 <= W
+        ids[b, :n] = out[b, c[b]:c[b] + n]
+        P2[b] = P[b] + c[b] + 1
+        c2[b] = n - 1
+        w2[b] = n + block - 1
+    return ids, P2, c2, w2
+
+
+def pbd_refeed_loop(model, cache, window_ids, prefix_len, causal_rows, window_len, steps, block,
+                    mask_id, n_accept=None, dtype=np.float64):
+    """Consecutive re-fed window steps (refeed_commit between them).
+
+    After each step the K/V of every real window row (j < w_b) are stored at
+    slots P_b + j; padding rows store nothing.  n_accept: None (accept every
+    block output) or one [B] array per step.  ``cache`` is copied, never
+    modified.  Returns (per-step ids, final (ids, P, c, w), cache).
+    """
+    cc = {k: (np.array(v, copy=True) if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+    ids = np.array(window_ids, copy=True)
+    P = np.array(prefix_len, dtype=np.int64, copy=True)
+    c = np.array(causal_rows, dtype=np.int64, copy=True)
+    w = np.array(window_len, dtype=np.int64, copy=True)
+    B, W = ids.shape
+    bs = int(cc["block"])
+    outs = []
+    for s in range(steps):
+        r = pbd_step(model, cc, ids, P, dtype, causal_rows=c, window_len=w)
+        outs.append(r["ids"])
+        for l, (kb, vb) in enumerate(r["kv"]):
+            for b in range(B):
+                for j in range(int(w[b])):
+                    t = int(P[b]) + j
+                    blk = int(cc["block_table"][b, t // bs])
+                    cc["k"][l, blk, :, t % bs, :] = kb[b * W + j].view(np.int16)
+                    cc["v"][l, blk, :, :, t % bs] = vb[b * W + j].view(np.int16)
+        ids, P, c, w = refeed_commit(r["ids"], ids, P, c, w, block, mask_id,
+                                     None if n_accept is None else n_accept[s])
+    return outs, (ids, P, c, w), cc

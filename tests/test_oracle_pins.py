@@ -503,3 +503,153 @@ def test_emission_loop_commits_window_kv():
     nxt[:, 0] = r0["ids"][:, 2]
     r1 = O.pbd_step(model, c2, nxt, [8, 12])
     np.testing.assert_array_equal(outs[1], r1["ids"])
+
+
+# ---------------------------------------------------------------- re-fed window
+
+def _sdpa(q, k, v, G, is_causal=False):
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(np.repeat(k, G, axis=1)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.repeat(v, G, axis=1)).permute(1, 0, 2)[None]
+    sd = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=is_causal)
+    return sd[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("P,W,c,w", [(0, 6, 0, 6), (5, 11, 5, 11), (13, 11, 2, 8), (7, 16, 10, 16),
+                                     (9, 8, 3, 3), (4, 12, 0, 6)])
+def test_refeed_window_rows_match_library_attention(P, W, c, w):
+    # re-fed rows are ordinary causal decode rows (torch SDPA is_causal over the
+    # whole sequence); block rows attend, unmasked, to every key before the
+    # window's end P + w (torch SDPA without a mask over those keys)
+    Hq, Hkv, D = 4, 2, 8
+    N = P + W
+    q = _rand((N, Hq, D), 81)
+    k = _rand((N, Hkv, D), 82)
+    v = _rand((N, Hkv, D), 83)
+    got = O.window_attention(q[P:], k, v, causal_rows=c, window_len=w)
+    causal = _sdpa(q, k, v, Hq // Hkv, is_causal=True)
+    for j in range(c):
+        np.testing.assert_allclose(got[j], causal[P + j], rtol=1e-12, atol=1e-12)
+    block = _sdpa(q[P + c:P + w], k[:P + w], v[:P + w], Hq // Hkv)
+    np.testing.assert_allclose(got[c:w], block, rtol=1e-12, atol=1e-12)
+    # padding rows' keys and values never reach a real row
+    k2, v2 = k.copy(), v.copy()
+    k2[P + w:] = 1e3 * _rand(k2[P + w:].shape, 84)
+    v2[P + w:] = 1e3 * _rand(v2[P + w:].shape, 85)
+    got2 = O.window_attention(q[P:], k2, v2, causal_rows=c, window_len=w)
+    np.testing.assert_array_equal(got2[:w], got[:w])
+
+
+def test_refeed_window_special_cases_and_locality():
+    Hq, Hkv, D, P, W = 4, 2, 8, 10, 11
+    N = P + W
+    q = _rand((W, Hq, D), 91)
+    k = _rand((N, Hkv, D), 92)
+    v = _rand((N, Hkv, D), 93)
+    # no re-fed rows is the PBD window; every row re-fed is the causal window
+    np.testing.assert_array_equal(O.window_attention(q, k, v, causal_rows=0),
+                                  O.window_attention(q, k, v))
+    np.testing.assert_array_equal(O.window_attention(q, k, v, causal_rows=W),
+                                  O.window_attention(q, k, v, causal=True))
+    c = 5
+    base = O.window_attention(q, k, v, causal_rows=c)
+    for j in range(W):
+        k2, v2 = k.copy(), v.copy()
+        k2[P + j] += 0.5
+        v2[P + j] += 0.5
+        pert = O.window_attention(q, k2, v2, causal_rows=c)
+        changed = [bool(np.abs(pert[r] - base[r]).max() > 1e-9) for r in range(W)]
+        # a re-fed row sees the rows up to its own; a block row sees them all
+        assert changed == [(r >= j) if r < c else True for r in range(W)]
+
+
+def _store_kv(cache, kv, P, B, W, real_rows):
+    bs = int(cache["block"])
+    for l, (kb, vb) in enumerate(kv):
+        for b in range(B):
+            for j in range(real_rows[b]):
+                t = int(P[b]) + j
+                blk = int(cache["block_table"][b, t // bs])
+                cache["k"][l, blk, :, t % bs, :] = kb[b * W + j].view(np.int16)
+                cache["v"][l, blk, :, :, t % bs] = vb[b * W + j].view(np.int16)
+
+
+def test_refeed_step_equals_token_by_token_decode():
+    # A re-fed window [r tokens | block of S] at P gives the same K/V for the r
+    # tokens and the same block outputs as decoding the r tokens one at a time
+    # (W = 1 steps, each storing its K/V) and then running the S-row block at
+    # P + r: re-feeding is causal decoding batched into the window.
+    d = TINY
+    W = 7
+    Ps, cs, ws = (5, 9), (2, 1), (6, 4)  # sequence 0: 2 re-fed + 4-block; 1: 1 + 3, 3 padding rows
+    model, _, _ = _tiny_setup(seed=31)
+    cache = _np(synth.make_cache(d, torch.tensor(list(Ps)), W, seed=32))
+    ids = synth.draw_window_ids(2, W, d.vocab, 33, mask_id=-1).numpy()
+    r = O.pbd_step(model, cache, ids, Ps, causal_rows=cs, window_len=ws, return_hidden=True)
+    for b in range(2):
+        sub = {k: (np.array(v, copy=True) if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+        sub["block_table"] = sub["block_table"][[b]]
+        P = Ps[b]
+        for j in range(cs[b]):
+            rj = O.pbd_step(model, sub, ids[b:b + 1, j:j + 1], [P + j])
+            for l, (kb, vb) in enumerate(rj["kv"]):
+                np.testing.assert_array_equal(r["kv"][l][0][b * W + j], kb[0])
+                np.testing.assert_array_equal(r["kv"][l][1][b * W + j], vb[0])
+            _store_kv(sub, rj["kv"], [P + j], 1, 1, [1])
+        S = ws[b] - cs[b]
+        rb = O.pbd_step(model, sub, ids[b:b + 1, cs[b]:ws[b]], [P + cs[b]], return_hidden=True)
+        rows = slice(b * W + cs[b], b * W + ws[b])
+        np.testing.assert_allclose(r["hidden"][rows], rb["hidden"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(r["ids"][b, cs[b]:ws[b]], rb["ids"][0])
+        for l, (kb, vb) in enumerate(rb["kv"]):
+            assert np.abs(r["kv"][l][0][rows].astype(np.int32) - kb.astype(np.int32)).max() <= 1
+            assert np.abs(r["kv"][l][1][rows].astype(np.int32) - vb.astype(np.int32)).max() <= 1
+        assert S == rb["ids"].shape[1]
+
+
+def test_refeed_commit_worked_example():
+    out = np.array([[10, 11, 12, 13, 14, 15, 16], [20, 21, 22, 23, 24, 25, 26]])
+    win = np.zeros((2, 7), dtype=np.int32)
+    ids, P, c, w = O.refeed_commit(out, win, [100, 200], [1, 0], [5, 3], 3, 99)
+    # sequence 0: block rows 1..4 accepted (11..14), the last opens a 3-row block
+    np.testing.assert_array_equal(ids, [[11, 12, 13, 14, 99, 99, 99], [20, 21, 22, 99, 99, 99, 99]])
+    assert list(P) == [102, 201] and list(c) == [3, 2] and list(w) == [6, 5]
+    ids, P, c, w = O.refeed_commit(out, win, [100, 200], [1, 0], [5, 3], 3, 99, n_accept=[2, 9])
+    np.testing.assert_array_equal(ids, [[11, 12, 99, 99, 99, 99, 99], [20, 21, 22, 99, 99, 99, 99]])
+    assert list(P) == [102, 201] and list(c) == [1, 2] and list(w) == [4, 5]
+    ids, P, c, w = O.refeed_commit(out, win, [100, 200], [1, 0], [5, 3], 3, 99, n_accept=[0, 1])
+    np.testing.assert_array_equal(ids[:, :3], [[11, 99, 99], [20, 99, 99]])
+    assert list(c) == [0, 0] and list(w) == [3, 3]
+
+
+def test_refeed_loop_places_every_accepted_token_at_its_position():
+    # Across a loop with partial acceptance, every real window row holds the
+    # token predicted for its position (row i of a window is at P + i; the
+    # argmax of row i is the token at P + i + 1), and the K/V of committed
+    # slots are the ones the step that last held them as a real row computed.
+    d = TINY
+    W, block, mask = 7, 4, 3
+    model, _, _ = _tiny_setup(seed=41)
+    cache = _np(synth.make_cache(d, torch.tensor([5, 9]), W, extra_tokens=16, seed=42))
+    ids = np.full((2, W), mask, dtype=np.int32)
+    ids[:, 0] = [17, 29]
+    acc = [np.array([4, 2]), np.array([1, 3]), np.array([2, 4])]
+    outs, (ids_f, P_f, c_f, w_f), cc = O.pbd_refeed_loop(
+        model, cache, ids, [5, 9], [0, 0], [block, block], 3, block, mask, n_accept=acc)
+    tok = {0: {5: 17}, 1: {9: 29}}
+    win, P, c, w = ids, np.array([5, 9]), np.array([0, 0]), np.array([block, block])
+    for s in range(3):
+        for b in range(2):
+            for i in range(int(w[b])):
+                if win[b, i] != mask or i <= c[b]:
+                    assert tok[b][int(P[b]) + i] == win[b, i]
+            n = min(max(int(acc[s][b]), 1), int(w[b] - c[b]))
+            for i in range(n):
+                tok[b][int(P[b] + c[b]) + i + 1] = int(outs[s][b, c[b] + i])
+        win, P, c, w = O.refeed_commit(outs[s], win, P, c, w, block, mask, acc[s])
+    np.testing.assert_array_equal(win, ids_f)
+    assert list(P) == list(P_f)
+    # the committed cache is what the next step reads: a fresh step on it
+    # gives the loop's next outputs
+    r = O.pbd_step(model, cc, ids_f, P_f, causal_rows=c_f, window_len=w_f)
+    assert r["ids"].shape == (2, W)
