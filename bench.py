@@ -310,6 +310,61 @@ def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
 
 
+def refeed_leg(B, synth, torch, dm, model, dev, stream, args):
+    """The emission loop of the dense-scene workload with re-feeding: every
+    step re-sends the 6 tokens it accepted last time causally before a new
+    block of 6 (window W = 11: 5 re-fed rows, the block; the first step has
+    the block only), and a device-side commit accepts the whole block -- one
+    captured graph of la_pbd_step_refeed + la_pbd_commit_refeed, 40 replays."""
+    w = synth.WORKLOADS["emit_b16_p2048_x40"]
+    d = w.dims
+    block, W = w.window, 2 * w.window - 1
+    log("bench: re-fed emission-loop leg")
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, W, extra_tokens=w.steps * block, seed=w.input_seed, device=dev)
+    first = synth.draw_window_ids(w.batch, block, d.vocab, w.input_seed, device=dev)
+    mask_id = int(first[0, 1].item())
+    ids0 = torch.full((w.batch, W), mask_id, dtype=torch.int32, device=dev)
+    ids0[:, 0] = first[:, 0]
+    ids, P0 = ids0.clone(), P.to(dev)
+    cr0 = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    wl0 = torch.full((w.batch,), block, dtype=torch.int32, device=dev)
+    cr, wl = cr0.clone(), wl0.clone()
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P0.clone()
+    max_len = int(P.max()) + W + w.steps * block
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, W), dtype=torch.int32, device=dev)
+    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, None, ws=ws, commit_mask_id=mask_id,
+                        refeed=(cr, wl, block, None))
+
+    def run_loop():
+        for t, t0 in ((ids, ids0), (Pd, P0), (cr, cr0), (wl, wl0)):
+            t.copy_(t0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(w.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run_loop()  # warm-up loop
+    loop_ms = run_loop()
+    # the first step commits its block's first row, every later one 6 rows
+    assert int((Pd - P0).min().item()) == 1 + (w.steps - 1) * block
+    ms_step = loop_ms / w.steps
+    log(f"bench: re-fed emission loop: {loop_ms:.2f} ms for {w.steps} steps, {ms_step:.3f} ms/step, "
+        f"{w.batch * 1000.0 / ms_step:.0f} windows/s")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": w.name + "_refeed", "batch": w.batch, "window": W, "block": block,
+            "steps_per_loop": w.steps, "prefix_start": int(P.max()), "loop_ms": round(loop_ms, 3),
+            "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "windows_per_s": round(1000.0 / ms_step * w.batch, 2)}
+
+
 def causal_leg(B, synth, torch, model, dev, timed, args):
     """The batch-1 step with the RK3588 conversion's causal window (window row j
     sees the prefix and window rows 0..j) instead of the bidirectional one."""
@@ -348,7 +403,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
     ap.add_argument("--no-extra-legs", action="store_true",
-                    help="skip the emission-loop, prefix-32768 and causal-window legs")
+                    help="skip the emission-loop, prefix-32768, causal-window and re-fed loop legs")
     ap.add_argument("--no-batch32", action="store_true",
                     help="skip the batch-32 leg reported beside the batch-1 step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -495,6 +550,7 @@ def main():
         result["emission_loop"] = emission_leg(B, synth, torch, dm, model, dev, stream, args)
         result["prefix_32768"] = probe_leg(B, synth, torch, dm, model, dev, stream, timed, args)
         result["causal_window"] = causal_leg(B, synth, torch, model, dev, timed, args)
+        result["refeed_loop"] = refeed_leg(B, synth, torch, dm, model, dev, stream, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_pbd.
 
 LA_W_BF16, LA_W_INT4 = 0, 1
 LA_EPI_NONE, LA_EPI_SILU_GATE = 0, 1
-LA_DERR_TOKEN_ID, LA_DERR_CAPACITY, LA_DERR_BLOCK_ID = 1, 2, 4
+LA_DERR_TOKEN_ID, LA_DERR_CAPACITY, LA_DERR_BLOCK_ID, LA_DERR_WINDOW = 1, 2, 4, 8
 LA_LAYOUT_ROWS, LA_LAYOUT_TILED, LA_LAYOUT_TILED_GU, LA_LAYOUT_TILED_QKV = 0, 1, 2, 3
 LA_MASK_BIDIRECTIONAL, LA_MASK_CAUSAL = 0, 1
 
@@ -28,7 +28,8 @@ EXPORTED = [
     "la_pbd_attention", "la_lm_head_argmax_workspace", "la_lm_head_argmax", "la_pbd_layer",
     "la_pbd_step_workspace", "la_pbd_step", "la_status_str", "la_pack_weight_bytes",
     "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
-    "la_pbd_attention_masked",
+    "la_pbd_attention_masked", "la_pbd_attention_refeed", "la_pbd_step_refeed",
+    "la_pbd_commit_refeed",
 ]
 
 
@@ -110,6 +111,17 @@ def load() -> ctypes.CDLL:
                                               c_int32, c_int32, c_void_p, c_int32, c_int32,
                                               c_int32, c_int32, c_void_p, c_void_p, c_size_t,
                                               c_void_p]),
+        "la_pbd_attention_refeed": (c_int32, [c_void_p, POINTER(LaKvCache), c_int32, c_int32,
+                                              c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                              c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                              c_size_t, c_void_p]),
+        "la_pbd_step_refeed": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
+                                         c_void_p]),
+        "la_pbd_commit_refeed": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                           c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -312,13 +324,22 @@ def wgemm_packed(packed: torch.Tensor, M: int, w: dict, bias=None, residual=None
 
 def pbd_attention(q: torch.Tensor, cache: DeviceCache, layer: int, n_heads: int, n_kv_heads: int,
                   prefix_len: torch.Tensor, B: int, W: int, max_len: int,
-                  ws: Optional[Workspace] = None, causal_window: bool = False) -> torch.Tensor:
+                  ws: Optional[Workspace] = None, causal_window: bool = False,
+                  causal_rows: Optional[torch.Tensor] = None,
+                  window_len: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Window attention; causal_rows / window_len (int32 [B], both or neither)
+    make it a re-fed window."""
     lib = load()
-    _require_cuda(q, prefix_len)
+    _require_cuda(q, prefix_len, causal_rows, window_len)
     out = torch.empty_like(q)
     need = lib.la_pbd_attention_workspace(B, W, n_heads, n_kv_heads, 128, max_len)
     buf = _ws(ws).get(need)
-    if causal_window:
+    if causal_rows is not None or window_len is not None:
+        _check(lib.la_pbd_attention_refeed(_ptr(q), ctypes.byref(cache.struct), layer, n_heads,
+                                           n_kv_heads, 128, _ptr(prefix_len), _ptr(causal_rows),
+                                           _ptr(window_len), B, W, max_len, _ptr(out), _ptr(buf),
+                                           buf.numel(), _stream()), "la_pbd_attention_refeed")
+    elif causal_window:
         _check(lib.la_pbd_attention_masked(_ptr(q), ctypes.byref(cache.struct), layer, n_heads,
                                            n_kv_heads, 128, _ptr(prefix_len), B, W, max_len,
                                            LA_MASK_CAUSAL, _ptr(out), _ptr(buf), buf.numel(),
@@ -373,10 +394,12 @@ def step_workspace_bytes(model: DeviceModel, B: int, W: int, max_len: int) -> in
 def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
              prefix_len: torch.Tensor, max_len: int, want_gap: bool = True,
              want_hidden: bool = False, ws: Optional[Workspace] = None, out_ids=None, out_gap=None,
-             err: Optional[torch.Tensor] = None):
-    """One PBD window step; returns (ids [B,W], gap [B,W] or None, hidden or None)."""
+             err: Optional[torch.Tensor] = None, causal_rows: Optional[torch.Tensor] = None,
+             window_len: Optional[torch.Tensor] = None):
+    """One PBD window step; returns (ids [B,W], gap [B,W] or None, hidden or None).
+    causal_rows / window_len (int32 [B]) make it a re-fed window step."""
     lib = load()
-    _require_cuda(window_ids, prefix_len, err)
+    _require_cuda(window_ids, prefix_len, err, causal_rows, window_len)
     B, W = window_ids.shape
     dev = window_ids.device
     ids = out_ids if out_ids is not None else torch.empty((B, W), dtype=torch.int32, device=dev)
@@ -388,9 +411,17 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
     if need == 0:
         raise LaError("la_pbd_step_workspace rejected the model or shape")
     buf = _ws(ws).get(need)
-    _check(lib.la_pbd_step(ctypes.byref(model.struct), ctypes.byref(cache.struct), _ptr(window_ids),
-                           _ptr(prefix_len), B, W, max_len, _ptr(ids), _ptr(gap), _ptr(hid),
-                           _ptr(buf), buf.numel(), _ptr(err), _stream()), "la_pbd_step")
+    if causal_rows is not None or window_len is not None:
+        _check(lib.la_pbd_step_refeed(ctypes.byref(model.struct), ctypes.byref(cache.struct),
+                                      _ptr(window_ids), _ptr(prefix_len), _ptr(causal_rows),
+                                      _ptr(window_len), B, W, max_len, _ptr(ids), _ptr(gap),
+                                      _ptr(hid), _ptr(buf), buf.numel(), _ptr(err), _stream()),
+               "la_pbd_step_refeed")
+    else:
+        _check(lib.la_pbd_step(ctypes.byref(model.struct), ctypes.byref(cache.struct),
+                               _ptr(window_ids), _ptr(prefix_len), B, W, max_len, _ptr(ids),
+                               _ptr(gap), _ptr(hid), _ptr(buf), buf.numel(), _ptr(err), _stream()),
+               "la_pbd_step")
     return ids, gap, hid
 
 
@@ -405,6 +436,20 @@ def pbd_commit(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_len: torc
                              _stream()), "la_pbd_commit")
 
 
+def pbd_commit_refeed(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_len: torch.Tensor,
+                      causal_rows: torch.Tensor, window_len: torch.Tensor, block: int, mask_id: int,
+                      n_accept: Optional[torch.Tensor] = None):
+    """Commit of a re-fed window step on the device (in place): accept the
+    first n_accept[b] block outputs (all when None), re-feed them, and open a
+    new block of `block` rows."""
+    lib = load()
+    _require_cuda(out_ids, window_ids, prefix_len, causal_rows, window_len, n_accept)
+    B, W = window_ids.shape
+    _check(lib.la_pbd_commit_refeed(_ptr(out_ids), _ptr(n_accept), _ptr(window_ids),
+                                    _ptr(prefix_len), _ptr(causal_rows), _ptr(window_len), B, W,
+                                    int(block), int(mask_id), _stream()), "la_pbd_commit_refeed")
+
+
 class StepGraph:
     """One la_pbd_step call captured in a HIP graph (torch.cuda.CUDAGraph) and
     replayed; inputs and outputs are the tensors given at capture time."""
@@ -412,12 +457,16 @@ class StepGraph:
     def __init__(self, model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
                  prefix_len: torch.Tensor, max_len: int, out_ids: torch.Tensor,
                  out_gap: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None,
-                 err: Optional[torch.Tensor] = None, commit_mask_id: Optional[int] = None):
+                 err: Optional[torch.Tensor] = None, commit_mask_id: Optional[int] = None,
+                 refeed: Optional[tuple] = None):
         # commit_mask_id: also capture la_pbd_commit after the step, so each
         # replay is one step of an emission loop (the window and prefix
-        # lengths advance on the device)
+        # lengths advance on the device).  refeed = (causal_rows, window_len,
+        # block, n_accept or None): re-fed window steps, committed with
+        # la_pbd_commit_refeed when commit_mask_id is given.
         self.args = (model, cache, window_ids, prefix_len, max_len)
         self.commit_mask_id = commit_mask_id
+        self.refeed = refeed
         self.ws = ws or Workspace(window_ids.device)
         self.out_ids, self.out_gap, self.err = out_ids, out_gap, err
         side = torch.cuda.Stream(device=window_ids.device)
@@ -432,10 +481,16 @@ class StepGraph:
 
     def _call(self, commit: bool = True):
         m, c, ids, P, ml = self.args
+        cr, wl = (self.refeed[0], self.refeed[1]) if self.refeed else (None, None)
         pbd_step(m, c, ids, P, ml, want_gap=self.out_gap is not None, ws=self.ws,
-                 out_ids=self.out_ids, out_gap=self.out_gap, err=self.err)
+                 out_ids=self.out_ids, out_gap=self.out_gap, err=self.err, causal_rows=cr,
+                 window_len=wl)
         if commit and self.commit_mask_id is not None:
-            pbd_commit(self.out_ids, ids, P, self.commit_mask_id)
+            if self.refeed:
+                pbd_commit_refeed(self.out_ids, ids, P, cr, wl, self.refeed[2], self.commit_mask_id,
+                                  self.refeed[3])
+            else:
+                pbd_commit(self.out_ids, ids, P, self.commit_mask_id)
 
     def replay(self):
         self.graph.replay()

@@ -45,6 +45,16 @@ void weight_storage(const la_weight* w, size_t* data, size_t* scales) {
 
 // The kernels address a weight with 32-bit offsets.
 constexpr size_t kMaxWeightBytes = (size_t)1 << 31;
+// Window rows, and window rows times query heads per KV head (one attention
+// wave per 16 of them, at most 8 waves).
+constexpr int kMaxWindow = 16;
+constexpr int kMaxQueryCols = 128;
+
+la_status attention_entry(const float* q, const la_kv_cache* kv, int32_t layer, int32_t n_heads,
+                          int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
+                          bool causal, const int32_t* causal_rows, const int32_t* window_len,
+                          int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int int4_group,
                        int tiled) {
@@ -203,8 +213,8 @@ la_status check_cache(const la_kv_cache* kv, const la_model* m, int B) {
 }
 
 la_status check_step_shape(const la_model* m, int B, int W, int max_len) {
-  if (B < 1 || B > 64 || W < 1 || W > 8 || max_len < W) return LA_ERR_SHAPE;
-  if (W * (m->n_heads / m->n_kv_heads) > 64) return LA_ERR_SHAPE;
+  if (B < 1 || B > 64 || W < 1 || W > kMaxWindow || max_len < W) return LA_ERR_SHAPE;
+  if (W * (m->n_heads / m->n_kv_heads) > kMaxQueryCols) return LA_ERR_SHAPE;
   return LA_OK;
 }
 
@@ -284,7 +294,8 @@ struct Carry {
 // next GEMM scales its outputs by 1/rms, so no normalisation kernel runs.  `next_gain` is the RMSNorm gain after this
 // layer (the next layer's input norm or the final norm; NULL: h only).
 la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
-                    int B, int W, int max_len, const StepWs& s, float* attn_out, Carry* carry,
+                    const int32_t* causal_rows, const int32_t* window_len, int B, int W,
+                    int max_len, const StepWs& s, float* attn_out, Carry* carry,
                     const uint16_t* next_gain, hipStream_t st) {
   const la_layer& L = m->layers[l];
   const int T = B * W;
@@ -354,6 +365,8 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   at.out_apack = int4 ? nullptr : s.apack_o;
   at.out_int4 = false;
   at.causal = m->window_mask == LA_MASK_CAUSAL;
+  at.causal_rows = causal_rows;
+  at.window_len = window_len;
   LA_TRY(launch_attention(at, st));
   if (int4)
     if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true, nullptr, 0, nullptr,
@@ -613,13 +626,40 @@ la_status la_pbd_attention_masked(const float* q, const la_kv_cache* kv, int32_t
                                   const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                                   int32_t window_mask, float* out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !out || !prefix_len) return LA_ERR_ARG;
   if (window_mask != LA_MASK_BIDIRECTIONAL && window_mask != LA_MASK_CAUSAL) return LA_ERR_ARG;
+  return attention_entry(q, kv, layer, n_heads, n_kv_heads, head_dim, prefix_len,
+                         window_mask == LA_MASK_CAUSAL, nullptr, nullptr, B, W, max_len, out,
+                         workspace, workspace_bytes, stream);
+}
+
+la_status la_pbd_attention_refeed(const float* q, const la_kv_cache* kv, int32_t layer,
+                                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  const int32_t* prefix_len, const int32_t* causal_rows,
+                                  const int32_t* window_len, int32_t B, int32_t W, int32_t max_len,
+                                  float* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (!causal_rows || !window_len) return LA_ERR_ARG;
+  return attention_entry(q, kv, layer, n_heads, n_kv_heads, head_dim, prefix_len, false,
+                         causal_rows, window_len, B, W, max_len, out, workspace, workspace_bytes,
+                         stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+la_status attention_entry(const float* q, const la_kv_cache* kv, int32_t layer, int32_t n_heads,
+                          int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
+                          bool causal, const int32_t* causal_rows, const int32_t* window_len,
+                          int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !out || !prefix_len) return LA_ERR_ARG;
   la_status st = check_cache(kv, nullptr, B);
   if (st != LA_OK) return st;
   if (head_dim != kHeadDim || n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads)
     return LA_ERR_SHAPE;
-  if (B < 1 || B > 64 || W < 1 || W > 8 || W * (n_heads / n_kv_heads) > 64 || max_len < 1)
+  if (B < 1 || B > 64 || W < 1 || W > kMaxWindow || W * (n_heads / n_kv_heads) > kMaxQueryCols ||
+      max_len < 1)
     return LA_ERR_SHAPE;
   if (layer < 0 || layer >= kv->n_layers) return LA_ERR_ARG;
   if (!aligned16(q) || !aligned16(out)) return LA_ERR_ARG;
@@ -647,9 +687,15 @@ la_status la_pbd_attention_masked(const float* q, const la_kv_cache* kv, int32_t
   at.part_o = c.take<float>(units * kHeadDim);
   at.part_ml = c.take<float>(units * 2);
   at.out = out;
-  at.causal = window_mask == LA_MASK_CAUSAL;
+  at.causal = causal;
+  at.causal_rows = causal_rows;
+  at.window_len = window_len;
   return hip_status(launch_attention(at, stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t la_lm_head_argmax_workspace(int32_t M, const la_weight* lm) {
   if (!lm || M < 1 || lm->k < 256) return 0;
@@ -706,8 +752,8 @@ la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, 
   PrologueArgs p = base_prologue(m, kv, prefix_len, B, W, max_len, s);
   LA_TRY(launch_prologue(p, stream));
   Carry carry;
-  if ((st = run_layer(m, layer, kv, prefix_len, B, W, max_len, s, attn_out, &carry, nullptr,
-                      stream)) != LA_OK)
+  if ((st = run_layer(m, layer, kv, prefix_len, nullptr, nullptr, B, W, max_len, s, attn_out,
+                      &carry, nullptr, stream)) != LA_OK)
     return st;
   if (carry.pending)
     return pack_rows(y, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, carry.pending, y,
@@ -724,6 +770,15 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  return la_pbd_step_refeed(m, kv, window_ids, prefix_len, nullptr, nullptr, B, W, max_len, out_ids,
+                            out_gap, out_hidden, workspace, workspace_bytes, err, stream);
+}
+
+la_status la_pbd_step_refeed(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                             const int32_t* prefix_len, const int32_t* causal_rows,
+                             const int32_t* window_len, int32_t B, int32_t W, int32_t max_len,
+                             int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
+                             size_t workspace_bytes, int32_t* err, hipStream_t stream) {
   la_status st = check_model(m);
   if (st != LA_OK) return st;
   if ((st = check_cache(kv, m, B)) != LA_OK) return st;
@@ -741,6 +796,8 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
   p.emb = m->embed;
   p.out = s.h;
   p.err = err;
+  p.causal_rows = causal_rows;
+  p.window_len = window_len;
   LA_TRY(launch_prologue(p, stream));
   Carry carry;
   const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
@@ -750,7 +807,8 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
     // lm_head takes the packed rows directly (bf16)
     const uint16_t* next_gain = l + 1 < m->n_layers ? m->layers[l + 1].in_norm
                                                     : (int4 ? nullptr : m->final_norm);
-    st = run_layer(m, l, kv, prefix_len, B, W, max_len, s, nullptr, &carry, next_gain, stream);
+    st = run_layer(m, l, kv, prefix_len, causal_rows, window_len, B, W, max_len, s, nullptr, &carry,
+                   next_gain, stream);
     if (st != LA_OK) return st;
   }
   if (!carry.packed) {
@@ -800,8 +858,21 @@ la_status la_pbd_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* pr
                         int32_t B, int32_t W, int32_t mask_id, hipStream_t stream) {
   if (!out_ids || !window_ids || !prefix_len) return LA_ERR_ARG;
   if ((const void*)out_ids == (const void*)window_ids) return LA_ERR_ARG;
-  if (B < 1 || B > 64 || W < 1 || W > 8) return LA_ERR_SHAPE;
+  if (B < 1 || B > 64 || W < 1 || W > kMaxWindow) return LA_ERR_SHAPE;
   return hip_status(launch_commit(out_ids, window_ids, prefix_len, B, W, mask_id, stream));
+}
+
+la_status la_pbd_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,
+                               int32_t* prefix_len, int32_t* causal_rows, int32_t* window_len,
+                               int32_t B, int32_t W, int32_t block, int32_t mask_id,
+                               hipStream_t stream) {
+  if (!out_ids || !window_ids || !prefix_len || !causal_rows || !window_len) return LA_ERR_ARG;
+  const void* state[4] = {window_ids, prefix_len, causal_rows, window_len};
+  for (const void* p : state)
+    if (p == (const void*)out_ids || (n_accept && p == (const void*)n_accept)) return LA_ERR_ARG;
+  if (B < 1 || B > 64 || W < 1 || W > kMaxWindow || block < 1 || block > W) return LA_ERR_SHAPE;
+  return hip_status(launch_commit_refeed(out_ids, n_accept, window_ids, prefix_len, causal_rows,
+                                         window_len, B, W, block, mask_id, stream));
 }
 
 }  // extern "C"

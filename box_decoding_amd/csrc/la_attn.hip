@@ -6,10 +6,13 @@
 // (RKLLM + RKNN)", "How it differs from the original", item 1; the Jetson
 // page, section 1.3, block mask).  The causal window that RK3588 conversion
 // runs instead (same item) is a per-row bound: row j sees slots 0 .. P_b+j.
+// So is a re-fed window, whose first c_b rows re-send accepted tokens
+// causally (row j < c_b sees slots 0 .. P_b+j) before the block, whose rows
+// see slots 0 .. P_b+w_b-1 (w_b real rows; rows past them are padding).
 //
 // Work split: a workgroup takes one run of pages of one (sequence, KV head),
 // one wave per tile of 16 query columns.  The 8 query heads of a KV head times
-// W window rows form up to 64 query columns that share every K/V page:
+// W window rows form up to 128 query columns that share every K/V page:
 //   S^T[key, query] = K_page . Q^T        16x16x32 bf16 matrix-core steps, Q split
 //                                         into bf16 hi + lo columns (K is exact bf16)
 //   online softmax per query column       exp2 on pre-scaled scores, a reference max
@@ -28,8 +31,13 @@
 
 namespace la {
 
+// Real window rows of sequence b (1 .. W).
+__device__ __forceinline__ int attn_wlen(const AttnArgs& a, int b) {
+  return a.window_len ? min(max(a.window_len[b], 1), a.W) : a.W;
+}
+
 __device__ __forceinline__ int attn_keys(const AttnArgs& a, int b) {
-  int n = a.prefix_len[b] + a.W;
+  int n = a.prefix_len[b] + attn_wlen(a, b);
   if (n > a.cap) n = a.cap;
   if (n < 0) n = 0;
   return n;
@@ -193,7 +201,8 @@ __device__ __forceinline__ void attn_store8(const AttnArgs& a, int b, int kvh, i
 // normalised and stored here; otherwise (max, sum, unnormalised O) goes to
 // the run's partial slot.
 template <int NQT, int LA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LA == 1 && NQT > 1 ? 3 : 1))) void k_attn_split(AttnArgs a) {
+__global__ __launch_bounds__(NQT > 4 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(LA == 1 && NQT > 1 ? 3 : (NQT > 4 ? 2 : 1)))) void k_attn_split(AttnArgs a) {
   constexpr int NSP = LA + 1;
   constexpr int PPW = (16 + NQT - 1) / NQT;  // pieces per wave and pair
   __shared__ __align__(16) unsigned char ring[NSP * kPairBytes];
@@ -230,10 +239,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LA == 1 && 
     }
   }
   const int n_keys = attn_keys(a, b);
-  // keys this lane's query column sees: all of them, or under the causal
-  // window the prefix and the window rows up to its own (at least one key)
-  const int kcol = a.causal ? max(min(n_keys, a.prefix_len[b] + (qi < NQ ? qi : 0) / G + 1), min(n_keys, 1))
-                            : n_keys;
+  // keys this lane's query column sees: all of them, or for a causal row (the
+  // causal window, the re-fed rows) the prefix and the window rows up to its
+  // own (at least one key)
+  const int crows = a.causal_rows ? min(max(a.causal_rows[b], 0), a.W) : (a.causal ? a.W : 0);
+  const int wrow = (qi < NQ ? qi : 0) / G;
+  const int kcol = wrow < crows ? max(min(n_keys, a.prefix_len[b] + wrow + 1), min(n_keys, 1)) : n_keys;
   if (k0 >= n_keys) {  // uniform over the workgroup
     if (direct && qi < NQ && (g & 1) == 0) {
       const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -464,7 +475,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     case 1: launch_split<1>(a, deep, grid, block, s); break;
     case 2: launch_split<2>(a, deep, grid, block, s); break;
     case 3: launch_split<3>(a, deep, grid, block, s); break;
-    default: launch_split<4>(a, deep, grid, block, s); break;
+    case 4: launch_split<4>(a, deep, grid, block, s); break;
+    case 5: launch_split<5>(a, deep, grid, block, s); break;
+    case 6: launch_split<6>(a, deep, grid, block, s); break;
+    case 7: launch_split<7>(a, deep, grid, block, s); break;
+    default: launch_split<8>(a, deep, grid, block, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;

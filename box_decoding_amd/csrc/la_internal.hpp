@@ -87,6 +87,8 @@ struct AttnArgs {
   bool out_int4;
   int nqp;                   // padded queries per kv head (multiple of 16)
   int causal;                // nonzero: window row j sees slots 0 .. P_b + j only
+  const int32_t* causal_rows; // [B] re-fed rows (nullable; overrides `causal`)
+  const int32_t* window_len;  // [B] real window rows (nullable: W)
 };
 
 struct PrologueArgs {
@@ -101,6 +103,8 @@ struct PrologueArgs {
   float2* rope;              // [T][64]
   double rope_theta;
   int32_t* flags;            // [T]
+  const int32_t* causal_rows; // [B] re-fed rows (nullable)
+  const int32_t* window_len;  // [B] real window rows (nullable)
   const int32_t* block_table;
   int max_blocks, num_blocks, cap;
 };
@@ -125,6 +129,9 @@ hipError_t launch_pack_weight(const la_weight& src, int layout, void* dst, void*
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len, int B,
                          int W, int mask_id, hipStream_t s);
+hipError_t launch_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,
+                                int32_t* prefix_len, int32_t* causal_rows, int32_t* window_len, int B,
+                                int W, int block, int mask_id, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s);
 hipError_t launch_argmax_reduce(const float* amax, int M, int n_tiles, const int32_t* flags,

@@ -69,6 +69,12 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
       }
       const long n = (long)P + a.W;
       if (P < 0 || n > a.cap) f |= LA_DERR_CAPACITY;
+      if (a.causal_rows || a.window_len) {
+        // a re-fed window: c causal rows, then the block up to w real rows
+        const int c = a.causal_rows ? a.causal_rows[b] : 0;
+        const int w = a.window_len ? a.window_len[b] : a.W;
+        if (w < 1 || w > a.W || c < 0 || c > w) f |= LA_DERR_WINDOW;
+      }
       int blk_bad = 0;
       if (!(f & LA_DERR_CAPACITY)) {
         const int pages = (int)((n + kBlock - 1) / kBlock);
@@ -108,6 +114,49 @@ hipError_t launch_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* p
                          int W, int mask_id, hipStream_t s) {
   hipLaunchKernelGGL(k_commit, dim3(1), dim3(((B * W + 63) / 64) * 64), 0, s, out_ids, window_ids,
                      prefix_len, B, W, mask_id);
+  return hipGetLastError();
+}
+
+// Commit of a re-fed window.  Sequence b accepts the first n_b outputs of its
+// block (rows c_b .. w_b - 1; n_b clamped to 1 .. w_b - c_b and to
+// W - block + 1); every row up to the block's first is final, so the prefix
+// becomes P_b + c_b + 1, and the next window re-feeds the accepted tokens, the
+// last of them opening a block of `block` rows with block - 1 mask tokens:
+// [out[c_b] .. out[c_b + n_b - 1], mask ...], c' = n_b - 1, w' = n_b + block - 1.
+// Every thread reads before any writes (the state is updated in place).
+__global__ __launch_bounds__(1024) void k_commit_refeed(const int32_t* out_ids, const int32_t* n_accept,
+                                                        int32_t* window_ids, int32_t* prefix_len,
+                                                        int32_t* causal_rows, int32_t* window_len,
+                                                        int B, int W, int block, int mask_id) {
+  const int t = threadIdx.x;
+  const bool live = t < B * W;
+  const int b = live ? t / W : 0, j = t - b * W;
+  int c = 0, n = 1, P = 0, id = mask_id;
+  if (live) {
+    c = min(max(causal_rows[b], 0), W - 1);
+    const int w = min(max(window_len[b], c + 1), W);
+    const int S = w - c;
+    n = n_accept ? min(max(n_accept[b], 1), S) : S;
+    n = min(n, W - block + 1);
+    P = prefix_len[b];
+    if (j < n) id = out_ids[b * W + c + j];
+  }
+  __syncthreads();
+  if (live) {
+    window_ids[t] = id;
+    if (j == 0) {
+      prefix_len[b] = P + c + 1;
+      causal_rows[b] = n - 1;
+      window_len[b] = n + block - 1;
+    }
+  }
+}
+
+hipError_t launch_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,
+                                int32_t* prefix_len, int32_t* causal_rows, int32_t* window_len, int B,
+                                int W, int block, int mask_id, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit_refeed, dim3(1), dim3(((B * W + 63) / 64) * 64), 0, s, out_ids, n_accept,
+                     window_ids, prefix_len, causal_rows, window_len, B, W, block, mask_id);
   return hipGetLastError();
 }
 

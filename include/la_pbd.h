@@ -28,7 +28,7 @@
  *  - Results are deterministic: the same inputs give bit-identical outputs.
  *  - Supported model shapes: head_dim 128, n_heads a multiple of n_kv_heads,
  *    hidden, n_heads*head_dim and inter multiples of 256, KV block size 16,
- *    window 1 <= W <= 8 with W * (n_heads / n_kv_heads) <= 64, batch 1..64.
+ *    window 1 <= W <= 16 with W * (n_heads / n_kv_heads) <= 128, batch 1..64.
  */
 #ifndef LA_PBD_H
 #define LA_PBD_H
@@ -144,7 +144,8 @@ typedef struct {
 enum {
   LA_DERR_TOKEN_ID = 1,   /* a window id outside [0, vocab) */
   LA_DERR_CAPACITY = 2,   /* P_b + W exceeds max_len or max_blocks * 16 */
-  LA_DERR_BLOCK_ID = 4    /* a block-table entry needed by the step is outside [0, num_blocks) */
+  LA_DERR_BLOCK_ID = 4,   /* a block-table entry needed by the step is outside [0, num_blocks) */
+  LA_DERR_WINDOW = 8      /* re-fed window: window_len[b] outside 1..W or causal_rows[b] outside 0..window_len[b] */
 };
 
 /* la_pbd_step epilogue selectors for la_wgemm. */
@@ -211,6 +212,23 @@ la_status la_pbd_attention(const float* q, const la_kv_cache* kv, int32_t layer,
                            int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
                            int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+/* Re-fed window ("LocateAnything-3B for RK3588 (RKLLM + RKNN)", "How it
+ * differs from the original", item 1: each step sends the accepted tokens
+ * again together with the mask tokens).  causal_rows and window_len are int32
+ * [B] device arrays (both required).  The first c_b = causal_rows[b] rows of
+ * sequence b re-feed accepted tokens causally: row j < c_b sees slots
+ * 0 .. P_b + j.  Rows c_b .. w_b - 1 (w_b = window_len[b]) form the
+ * bidirectional block: each sees slots 0 .. P_b + w_b - 1.  Rows from w_b to W
+ * are padding; no real row sees them, and they see what the block sees.
+ * Values outside 1 <= w_b <= W, 0 <= c_b <= W are clamped into them.  c_b = 0,
+ * w_b = W is la_pbd_attention; c_b = W is the causal window.  Same workspace
+ * and errors as la_pbd_attention. */
+la_status la_pbd_attention_refeed(const float* q, const la_kv_cache* kv, int32_t layer,
+                                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  const int32_t* prefix_len, const int32_t* causal_rows,
+                                  const int32_t* window_len, int32_t B, int32_t W, int32_t max_len,
+                                  float* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /* Tied lm_head with per-row argmax (greedy selection; Jetson page, section 1.4).
  * f = RMSNorm(h; norm_gain, rms_eps) if norm_gain != NULL else h; logits =
@@ -246,6 +264,19 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream);
+/* The step on a re-fed window (la_pbd_attention_refeed): causal_rows and
+ * window_len are int32 [B] device arrays; either may be NULL (then 0 re-fed
+ * rows, or m->window_mask decides; W real rows).  Every row, padding
+ * included, is computed and writes its K/V at slot P_b + j, so P_b + W must
+ * fit the cache; padding rows' slots lie past the window and are rewritten
+ * before any later prefix covers them.  A sequence whose w_b is outside 1..W
+ * or whose c_b is outside 0..w_b sets LA_DERR_WINDOW and gets out_ids = -1.
+ * Workspace as la_pbd_step_workspace. */
+la_status la_pbd_step_refeed(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                             const int32_t* prefix_len, const int32_t* causal_rows,
+                             const int32_t* window_len, int32_t B, int32_t W, int32_t max_len,
+                             int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
+                             size_t workspace_bytes, int32_t* err, hipStream_t stream);
 
 /* Commit a fully accepted window and form the next one, for a loop of window
  * steps (the cached prefix grows by the accepted tokens and is reused, with
@@ -255,10 +286,34 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
  * at slots P_b .. P_b+W-1.  out_ids and window_ids int32 [B][W] (distinct
  * buffers), prefix_len int32 [B], all device memory owned by the caller.  Only
  * enqueues on the stream (graph-capturable).  Returns LA_ERR_ARG for NULL
- * pointers or aliased ids, LA_ERR_SHAPE outside 1 <= B <= 64, 1 <= W <= 8 (the
+ * pointers or aliased ids, LA_ERR_SHAPE outside 1 <= B <= 64, 1 <= W <= 16 (the
  * step's limits). */
 la_status la_pbd_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len,
                         int32_t B, int32_t W, int32_t mask_id, hipStream_t stream);
+
+/* Commit of a re-fed window step, with partial acceptance (same page and item:
+ * the accepted tokens are sent again with the mask tokens, over the reused
+ * prefix).  Window row i of sequence b sits at position P_b + i and its argmax
+ * is read as the token at P_b + i + 1, so the block (rows c_b .. w_b - 1)
+ * predicts the tokens after position P_b + c_b.  Sequence b accepts the first
+ * n_b of them: n_accept[b] clamped to 1 .. w_b - c_b and to W - block + 1
+ * (n_accept NULL: the whole block).  Rows up to the block's first are then
+ * final, and the state becomes, in place:
+ *   window_ids[b] = [out_ids[b][c_b] .. out_ids[b][c_b + n_b - 1], mask_id ...]
+ *   prefix_len[b] += c_b + 1;  causal_rows[b] = n_b - 1;  window_len[b] = n_b + block - 1
+ * i.e. the accepted tokens are re-fed causally and the last of them opens a
+ * new block of `block` rows (it and block - 1 mask tokens).  The K/V of the
+ * final rows are already in the cache (la_pbd_step_refeed wrote them).  All
+ * arrays are int32 device memory: out_ids, window_ids [B][W]; n_accept,
+ * prefix_len, causal_rows, window_len [B]; out_ids and n_accept must not alias
+ * the state arrays.  Stored c_b, w_b are clamped (c_b to 0 .. W - 1, w_b to
+ * c_b + 1 .. W) before use.  Only enqueues (graph-capturable).  Returns
+ * LA_ERR_ARG for NULL or aliased pointers, LA_ERR_SHAPE outside 1 <= B <= 64,
+ * 1 <= W <= 16, 1 <= block <= W. */
+la_status la_pbd_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,
+                               int32_t* prefix_len, int32_t* causal_rows, int32_t* window_len,
+                               int32_t B, int32_t W, int32_t block, int32_t mask_id,
+                               hipStream_t stream);
 
 /* Repack a row-major weight (src->layout == LA_LAYOUT_ROWS) into one of the
  * tiled layouts (bf16, or INT4 with group 128).  dst receives

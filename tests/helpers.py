@@ -79,3 +79,10 @@ def poison_unused_slots(cache: dict, prefix_len, window: int):
     vm = mask[None, :, None, None, :].expand_as(v)
     k.masked_fill_(km, nan)
     v.masked_fill_(vm, nan)
+
+
+def bf16_bits_rel_l2(got_bits, ref_bits):
+    """rel-L2 between two bf16 bit arrays, as decoded values."""
+    def dec(x):
+        return (np.asarray(x).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return rel_l2(dec(got_bits), dec(ref_bits))

@@ -89,7 +89,8 @@ def test_attention_rejects_bad_shapes(lib):
         k.get("ws", ws), None)
     assert call(d=64) == -2
     assert call(hq=15) == -2
-    assert call(W=9) == -2
+    assert call(W=17) == -2
+    assert call(hq=32, W=9) == -2   # 9 rows x 16 query heads per KV head > 128 columns
     assert call(B=65) == -2
     assert call(layer=1) == -1
     assert call(ws=ws - 1) == -3
@@ -153,4 +154,26 @@ def test_commit_rejects_bad_arguments_before_launch(lib):
     assert lib.la_pbd_commit(a, b_, p, 0, 6, 7, None) == -2
     assert lib.la_pbd_commit(a, b_, p, 65, 6, 7, None) == -2
     assert lib.la_pbd_commit(a, b_, p, 2, 0, 7, None) == -2
-    assert lib.la_pbd_commit(a, b_, p, 2, 9, 7, None) == -2
+    assert lib.la_pbd_commit(a, b_, p, 2, 17, 7, None) == -2
+
+
+def test_refeed_entry_points_reject_bad_arguments_before_launch(lib):
+    a, w_ = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    p, c, l, n = ctypes.c_void_p(12288), ctypes.c_void_p(16384), ctypes.c_void_p(20480), ctypes.c_void_p(24576)
+    ok = lambda *x: lib.la_pbd_commit_refeed(*x)
+    assert ok(None, n, w_, p, c, l, 2, 11, 6, 7, None) == -1
+    assert ok(a, n, w_, p, None, l, 2, 11, 6, 7, None) == -1
+    assert ok(a, n, w_, p, c, None, 2, 11, 6, 7, None) == -1
+    assert ok(a, n, a, p, c, l, 2, 11, 6, 7, None) == -1     # out_ids is the window
+    assert ok(a, c, w_, p, c, l, 2, 11, 6, 7, None) == -1    # n_accept is causal_rows
+    assert ok(a, n, w_, p, c, l, 0, 11, 6, 7, None) == -2
+    assert ok(a, n, w_, p, c, l, 2, 17, 6, 7, None) == -2
+    assert ok(a, n, w_, p, c, l, 2, 11, 12, 7, None) == -2   # block wider than the window
+    assert ok(a, n, w_, p, c, l, 2, 11, 0, 7, None) == -2
+    kv = b.LaKvCache(ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(256), 10, 4, 16, 1)
+    ws = lib.la_pbd_attention_workspace(1, 11, 16, 2, 128, 64)
+    att = lambda cr, wl, W=11: lib.la_pbd_attention_refeed(
+        a, ctypes.byref(kv), 0, 16, 2, 128, p, cr, wl, 1, W, 64, a, a, ws, None)
+    assert att(None, l) == -1
+    assert att(c, None) == -1
+    assert att(c, l, W=17) == -2
