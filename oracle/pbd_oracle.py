@@ -47,6 +47,7 @@ import numpy as np
 __all__ = [
     "bf16_to_float", "fp16_to_float", "round_to_bf16_bits", "int4_dequant", "decode_weight",
     "embed_rows", "rmsnorm", "silu", "rope_angles", "rope_apply", "window_attention",
+    "repetition_penalty",
     "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "pbd_emission_loop",
     "refeed_commit", "pbd_refeed_loop",
 ]
@@ -283,11 +284,26 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
     return h2, k_bits, v_bits
 
 
-def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64):
+def repetition_penalty(z, theta):
+    """A logit of a token already in the sequence, penalised: z / theta where
+    z > 0, z * theta otherwise (theta > 1 lowers it either way).
+
+    The Jetson page's generate call (Part 1 section 1.4) passes
+    repetition_penalty=1.1 with greedy selection; the pages give no formula,
+    and this is the plain one: the penalty divides a positive score and
+    multiplies a negative one, so the token is always made less likely.
+    """
+    z = np.asarray(z)
+    return np.where(z > 0, z / theta, z * theta)
+
+
+def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64, rep_sets=None, rep_penalty=1.0):
     """Per-row argmax of f . E^T over the vocabulary, with top-1 and top-2 gap.
 
     Lowest index wins an exact tie.  gap = logit[id] - max_{v != id} logit[v].
-    The vocabulary is processed in chunks only to bound memory.
+    The vocabulary is processed in chunks only to bound memory.  rep_sets: one
+    array of vocabulary ids per row (or None); those ids' logits go through
+    repetition_penalty(., rep_penalty) before the ranking.
     """
     f = np.asarray(f, dtype=dtype)
     T = f.shape[0]
@@ -295,10 +311,17 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64):
     best = np.full(T, -np.inf)
     best_id = np.full(T, -1, dtype=np.int64)
     second = np.full(T, -np.inf)
+    sets = None
+    if rep_sets is not None:
+        sets = [np.unique(np.asarray(x, dtype=np.int64)) for x in rep_sets]
     for v0 in range(0, V, chunk):
         v1 = min(V, v0 + chunk)
         E = decode_weight(lm, rows=np.arange(v0, v1), dtype=dtype)
         logits = f @ E.T                               # [T, v1-v0]
+        if sets is not None:
+            for t in range(T):
+                idx = sets[t][(sets[t] >= v0) & (sets[t] < v1)] - v0
+                logits[t, idx] = repetition_penalty(logits[t, idx], rep_penalty)
         for t in range(T):
             row = logits[t]
             i = int(np.argmax(row))                    # first (lowest) index of the max
@@ -315,11 +338,15 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64):
 
 
 def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidden=False,
-             layers=None, causal=False, causal_rows=None, window_len=None):
+             layers=None, causal=False, causal_rows=None, window_len=None, rep_sets=None,
+             rep_penalty=1.0):
     """One PBD window step for every sequence.
 
     window_ids [B, W] -> per-position argmax ids [B, W] and top-2 gaps [B, W].
     causal_rows / window_len [B] make it a re-fed window (window_attention).
+    rep_sets: per sequence, the vocabulary ids already in it (or None); every
+    row of the sequence ranks its logits with those penalised
+    (repetition_penalty, rep_penalty).
     The step writes nothing into ``cache``; it returns the bf16 K/V it would
     store at slots P_b .. P_b+W-1 of each layer.
     """
@@ -335,7 +362,8 @@ def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidd
         kv.append((kb, vb))
     f = rmsnorm(h, bf16_to_float(model["final_norm"], dtype), float(_dim(dims, "rms_eps")))
     lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
-    out_ids, top1, gap = lm_head_argmax(f, lm, dtype=dtype)
+    row_sets = None if rep_sets is None else [rep_sets[t // W] for t in range(B * W)]
+    out_ids, top1, gap = lm_head_argmax(f, lm, dtype=dtype, rep_sets=row_sets, rep_penalty=rep_penalty)
     res = {"ids": out_ids.reshape(B, W), "top1": top1.reshape(B, W), "gap": gap.reshape(B, W),
            "kv": kv}
     if return_hidden:

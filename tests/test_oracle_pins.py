@@ -653,3 +653,72 @@ def test_refeed_loop_places_every_accepted_token_at_its_position():
     # gives the loop's next outputs
     r = O.pbd_step(model, cc, ids_f, P_f, causal_rows=c_f, window_len=w_f)
     assert r["ids"].shape == (2, W)
+
+
+# ---------------------------------------------------------------- repetition penalty
+
+def _lm_of(values):
+    """A tied lm_head whose column 0 holds `values` (bf16-exact), so that the
+    logits of f = e_0 are exactly those values."""
+    V = len(values)
+    E = np.zeros((V, 4))
+    E[:, 0] = values
+    bits = O.round_to_bf16_bits(E)
+    assert np.array_equal(O.bf16_to_float(bits)[:, 0], values)
+    return {"fmt": "bf16", "data": bits, "n": V}
+
+
+def test_repetition_penalty_worked_examples():
+    # logits 3, 2.75, -1, -0.9375, 0.5 (exact in bf16) for the row f = e_0
+    lm = _lm_of(np.array([3.0, 2.75, -1.0, -0.9375, 0.5]))
+    f = np.zeros((1, 4))
+    f[0, 0] = 1.0
+    ids, top1, gap = O.lm_head_argmax(f, lm)
+    assert ids[0] == 0 and top1[0] == 3.0 and gap[0] == 0.25
+    # id 0 already used: 3 / 1.1 = 2.7272... < 2.75, so id 1 wins by 0.0227...
+    ids, top1, gap = O.lm_head_argmax(f, lm, rep_sets=[[0]], rep_penalty=1.1)
+    assert ids[0] == 1 and top1[0] == 2.75
+    assert abs(gap[0] - (2.75 - 3.0 / 1.1)) < 1e-15
+    # ids 0 and 1 used: 2.7272... beats 2.5
+    ids, top1, gap = O.lm_head_argmax(f, lm, rep_sets=[[1, 0]], rep_penalty=1.1)
+    assert ids[0] == 0 and abs(top1[0] - 3.0 / 1.1) < 1e-15 and abs(gap[0] - (3.0 / 1.1 - 2.5)) < 1e-15
+    # a negative logit is multiplied: -0.9375 * 1.1 = -1.03125 falls below -1
+    neg = _lm_of(np.array([-1.0, -0.9375, -2.0]))
+    ids, top1, gap = O.lm_head_argmax(f, neg)
+    assert ids[0] == 1
+    ids, top1, gap = O.lm_head_argmax(f, neg, rep_sets=[[1]], rep_penalty=1.1)
+    assert ids[0] == 0 and top1[0] == -1.0 and abs(gap[0] - (-1.0 + 1.03125)) < 1e-15
+    # zero is not positive: multiplied, and stays zero
+    np.testing.assert_array_equal(O.repetition_penalty(np.array([0.0, 2.2, -2.0]), 1.1),
+                                  [0.0, 2.2 / 1.1, -2.0 * 1.1])
+
+
+def test_repetition_penalty_special_cases():
+    rng = np.random.default_rng(71)
+    V, H = 9000, 16
+    bits = O.round_to_bf16_bits(rng.standard_normal((V, H)) * 0.5)
+    lm = {"fmt": "bf16", "data": bits, "n": V}
+    f = rng.standard_normal((5, H))
+    base = O.lm_head_argmax(f, lm, chunk=4096)
+    sets = [rng.choice(V, size=300, replace=False) for _ in range(5)]
+    # a penalty of 1 changes nothing
+    same = O.lm_head_argmax(f, lm, chunk=4096, rep_sets=sets, rep_penalty=1.0)
+    for a, b in zip(base, same):
+        np.testing.assert_array_equal(a, b)
+    # penalising only tokens that are not the argmax never changes the argmax
+    # (every penalised logit only goes down)
+    others = [np.setdiff1d(s_, [base[0][t]]) for t, s_ in enumerate(sets)]
+    got = O.lm_head_argmax(f, lm, chunk=4096, rep_sets=others, rep_penalty=1.3)
+    np.testing.assert_array_equal(got[0], base[0])
+    np.testing.assert_array_equal(got[1], base[1])
+    # penalising the argmax: the new winner is the best of the penalised top-1
+    # and the unpenalised rest, found by sorting the full logit row
+    logits = f @ O.bf16_to_float(bits).T
+    got = O.lm_head_argmax(f, lm, chunk=4096, rep_sets=[[i] for i in base[0]], rep_penalty=1.3)
+    for t in range(5):
+        row = logits[t].copy()
+        i = base[0][t]
+        row[i] = row[i] / 1.3 if row[i] > 0 else row[i] * 1.3
+        order = np.argsort(-row, kind="stable")
+        assert got[0][t] == order[0]
+        assert abs(got[2][t] - (row[order[0]] - row[order[1]])) < 1e-12
