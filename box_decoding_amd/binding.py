@@ -29,7 +29,7 @@ EXPORTED = [
     "la_pbd_step_workspace", "la_pbd_step", "la_status_str", "la_pack_weight_bytes",
     "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
     "la_pbd_attention_masked", "la_pbd_attention_refeed", "la_pbd_step_refeed",
-    "la_pbd_commit_refeed",
+    "la_pbd_commit_refeed", "la_pbd_step_opts", "la_lm_head_argmax_penalized", "la_pbd_mark_tokens",
 ]
 
 
@@ -56,6 +56,11 @@ class LaKvCache(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("block_table", c_void_p),
                 ("num_blocks", c_int32), ("max_blocks", c_int32), ("block_size", c_int32),
                 ("n_layers", c_int32)]
+
+
+class LaStepOpts(ctypes.Structure):
+    _fields_ = [("causal_rows", c_void_p), ("window_len", c_void_p), ("rep_bits", c_void_p),
+                ("rep_words", c_int32), ("rep_penalty", c_float)]
 
 
 class LaError(RuntimeError):
@@ -122,6 +127,14 @@ def load() -> ctypes.CDLL:
         "la_pbd_commit_refeed": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_int32, c_int32, c_int32, c_int32,
                                            c_void_p]),
+        "la_pbd_step_opts": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
+                                       POINTER(LaStepOpts), c_int32, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+        "la_lm_head_argmax_penalized": (c_int32, [c_void_p, c_int32, W, c_void_p, c_float, c_void_p,
+                                                  c_int32, c_int32, c_float, c_void_p, c_void_p,
+                                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+        "la_pbd_mark_tokens": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                         c_int32, c_int32, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -352,9 +365,12 @@ def pbd_attention(q: torch.Tensor, cache: DeviceCache, layer: int, n_heads: int,
 
 
 def lm_head_argmax(h: torch.Tensor, lm: dict, norm_gain=None, eps: float = 1e-6,
-                   ws: Optional[Workspace] = None):
+                   ws: Optional[Workspace] = None, rep_bits: Optional[torch.Tensor] = None,
+                   rep_rows: int = 1, rep_penalty: float = 1.0):
+    """Tied lm_head argmax; rep_bits (int32 [rows / rep_rows, words], the
+    vocabulary bitmaps) applies the repetition penalty."""
     lib = load()
-    _require_cuda(h, norm_gain)
+    _require_cuda(h, norm_gain, rep_bits)
     M = h.shape[0]
     wd = weight_desc(lm)
     ids = torch.empty(M, dtype=torch.int32, device=h.device)
@@ -362,9 +378,16 @@ def lm_head_argmax(h: torch.Tensor, lm: dict, norm_gain=None, eps: float = 1e-6,
     gap = torch.empty(M, dtype=torch.float32, device=h.device)
     need = lib.la_lm_head_argmax_workspace(M, ctypes.byref(wd))
     buf = _ws(ws).get(need)
-    _check(lib.la_lm_head_argmax(_ptr(h), M, ctypes.byref(wd), _ptr(norm_gain), eps, _ptr(ids),
-                                 _ptr(top1), _ptr(gap), _ptr(buf), buf.numel(), _stream()),
-           "la_lm_head_argmax")
+    if rep_bits is not None:
+        _check(lib.la_lm_head_argmax_penalized(_ptr(h), M, ctypes.byref(wd), _ptr(norm_gain), eps,
+                                               _ptr(rep_bits), rep_bits.shape[1], rep_rows,
+                                               float(rep_penalty), _ptr(ids), _ptr(top1), _ptr(gap),
+                                               _ptr(buf), buf.numel(), _stream()),
+               "la_lm_head_argmax_penalized")
+    else:
+        _check(lib.la_lm_head_argmax(_ptr(h), M, ctypes.byref(wd), _ptr(norm_gain), eps, _ptr(ids),
+                                     _ptr(top1), _ptr(gap), _ptr(buf), buf.numel(), _stream()),
+               "la_lm_head_argmax")
     return ids, top1, gap
 
 
@@ -395,11 +418,13 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
              prefix_len: torch.Tensor, max_len: int, want_gap: bool = True,
              want_hidden: bool = False, ws: Optional[Workspace] = None, out_ids=None, out_gap=None,
              err: Optional[torch.Tensor] = None, causal_rows: Optional[torch.Tensor] = None,
-             window_len: Optional[torch.Tensor] = None):
+             window_len: Optional[torch.Tensor] = None, rep_bits: Optional[torch.Tensor] = None,
+             rep_penalty: float = 1.0):
     """One PBD window step; returns (ids [B,W], gap [B,W] or None, hidden or None).
-    causal_rows / window_len (int32 [B]) make it a re-fed window step."""
+    causal_rows / window_len (int32 [B]) make it a re-fed window step; rep_bits
+    (int32 [B, words] vocabulary bitmaps) applies the repetition penalty."""
     lib = load()
-    _require_cuda(window_ids, prefix_len, err, causal_rows, window_len)
+    _require_cuda(window_ids, prefix_len, err, causal_rows, window_len, rep_bits)
     B, W = window_ids.shape
     dev = window_ids.device
     ids = out_ids if out_ids is not None else torch.empty((B, W), dtype=torch.int32, device=dev)
@@ -411,7 +436,14 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
     if need == 0:
         raise LaError("la_pbd_step_workspace rejected the model or shape")
     buf = _ws(ws).get(need)
-    if causal_rows is not None or window_len is not None:
+    if rep_bits is not None:
+        opts = LaStepOpts(_ptr(causal_rows), _ptr(window_len), _ptr(rep_bits), rep_bits.shape[1],
+                          float(rep_penalty))
+        _check(lib.la_pbd_step_opts(ctypes.byref(model.struct), ctypes.byref(cache.struct),
+                                    _ptr(window_ids), _ptr(prefix_len), ctypes.byref(opts), B, W,
+                                    max_len, _ptr(ids), _ptr(gap), _ptr(hid), _ptr(buf), buf.numel(),
+                                    _ptr(err), _stream()), "la_pbd_step_opts")
+    elif causal_rows is not None or window_len is not None:
         _check(lib.la_pbd_step_refeed(ctypes.byref(model.struct), ctypes.byref(cache.struct),
                                       _ptr(window_ids), _ptr(prefix_len), _ptr(causal_rows),
                                       _ptr(window_len), B, W, max_len, _ptr(ids), _ptr(gap),
@@ -448,6 +480,20 @@ def pbd_commit_refeed(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_le
     _check(lib.la_pbd_commit_refeed(_ptr(out_ids), _ptr(n_accept), _ptr(window_ids),
                                     _ptr(prefix_len), _ptr(causal_rows), _ptr(window_len), B, W,
                                     int(block), int(mask_id), _stream()), "la_pbd_commit_refeed")
+
+
+def mark_tokens(ids: torch.Tensor, rep_bits: torch.Tensor, vocab: int,
+                first: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None):
+    """Set the repetition-bitmap bits of the selected ids (in place, on the device)."""
+    lib = load()
+    _require_cuda(ids, rep_bits, first, count)
+    B, W = ids.shape
+    _check(lib.la_pbd_mark_tokens(_ptr(ids), B, W, _ptr(first), _ptr(count), _ptr(rep_bits),
+                                  rep_bits.shape[1], int(vocab), _stream()), "la_pbd_mark_tokens")
+
+
+def rep_words(vocab: int) -> int:
+    return (vocab + 31) // 32
 
 
 class StepGraph:

@@ -710,7 +710,20 @@ la_status la_lm_head_argmax(const float* h, int32_t M, const la_weight* lm,
                             const uint16_t* norm_gain, float rms_eps, int32_t* ids, float* top1,
                             float* gap, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
+  return la_lm_head_argmax_penalized(h, M, lm, norm_gain, rms_eps, nullptr, 0, 1, 1.f, ids, top1,
+                                     gap, workspace, workspace_bytes, stream);
+}
+
+la_status la_lm_head_argmax_penalized(const float* h, int32_t M, const la_weight* lm,
+                                      const uint16_t* norm_gain, float rms_eps,
+                                      const uint32_t* rep_bits, int32_t rep_words,
+                                      int32_t rep_rows, float rep_penalty, int32_t* ids,
+                                      float* top1, float* gap, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
   if (!h || !ids || !lm) return LA_ERR_ARG;
+  if (rep_bits && (rep_rows < 1 || (int64_t)rep_words * 32 < (int64_t)lm->n ||
+                   !(rep_penalty > 0.f) || !(rep_penalty < INFINITY)))
+    return LA_ERR_ARG;
   if (M < 1 || M > 512) return LA_ERR_SHAPE;
   la_status st = check_gemm_weight(lm, LA_LAYOUT_TILED);
   if (st != LA_OK) return st;
@@ -726,6 +739,10 @@ la_status la_lm_head_argmax(const float* h, int32_t M, const la_weight* lm,
   float* amax = c.take<float>((size_t)M * parts * 3);
   GemmArgs g = base_gemm(lm, M);
   g.amax = amax;
+  g.rep_bits = rep_bits;
+  g.rep_words = rep_words;
+  g.rep_rows = rep_rows;
+  g.rep_theta = rep_penalty;
   if ((st = gemm_from_rows(g, h, lm->k, norm_gain, rms_eps, apack, asum, EPI_ARGMAX, int4, stream)) != LA_OK)
     return st;
   return hip_status(launch_argmax_reduce(amax, M, parts, nullptr, ids, top1, gap, nullptr, stream));
@@ -770,8 +787,8 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream) {
-  return la_pbd_step_refeed(m, kv, window_ids, prefix_len, nullptr, nullptr, B, W, max_len, out_ids,
-                            out_gap, out_hidden, workspace, workspace_bytes, err, stream);
+  return la_pbd_step_opts(m, kv, window_ids, prefix_len, nullptr, B, W, max_len, out_ids, out_gap,
+                          out_hidden, workspace, workspace_bytes, err, stream);
 }
 
 la_status la_pbd_step_refeed(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
@@ -779,8 +796,28 @@ la_status la_pbd_step_refeed(const la_model* m, const la_kv_cache* kv, const int
                              const int32_t* window_len, int32_t B, int32_t W, int32_t max_len,
                              int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                              size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  la_step_opts o;
+  memset(&o, 0, sizeof(o));
+  o.causal_rows = causal_rows;
+  o.window_len = window_len;
+  o.rep_penalty = 1.f;
+  return la_pbd_step_opts(m, kv, window_ids, prefix_len, &o, B, W, max_len, out_ids, out_gap,
+                          out_hidden, workspace, workspace_bytes, err, stream);
+}
+
+la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                           const int32_t* prefix_len, const la_step_opts* opts, int32_t B, int32_t W,
+                           int32_t max_len, int32_t* out_ids, float* out_gap, float* out_hidden,
+                           void* workspace, size_t workspace_bytes, int32_t* err,
+                           hipStream_t stream) {
   la_status st = check_model(m);
   if (st != LA_OK) return st;
+  const int32_t* causal_rows = opts ? opts->causal_rows : nullptr;
+  const int32_t* window_len = opts ? opts->window_len : nullptr;
+  if (opts && opts->rep_bits &&
+      (!(opts->rep_penalty > 0.f) || !(opts->rep_penalty < INFINITY) ||
+       (int64_t)opts->rep_words * 32 < (int64_t)(m->lm_head.data ? m->lm_head.n : m->embed.n)))
+    return LA_ERR_ARG;
   if ((st = check_cache(kv, m, B)) != LA_OK) return st;
   if ((st = check_step_shape(m, B, W, max_len)) != LA_OK) return st;
   if (!window_ids || !prefix_len || !out_ids) return LA_ERR_ARG;
@@ -824,6 +861,12 @@ la_status la_pbd_step_refeed(const la_model* m, const la_kv_cache* kv, const int
   g.amax = s.amax;
   g.apack = s.apack;
   g.asum = s.asum;
+  if (opts && opts->rep_bits) {
+    g.rep_bits = opts->rep_bits;
+    g.rep_words = opts->rep_words;
+    g.rep_rows = W;
+    g.rep_theta = opts->rep_penalty;
+  }
   if (carry.packed) {
     g.ss_in = s.ss;
     g.ss_tiles = H / 16;
@@ -860,6 +903,15 @@ la_status la_pbd_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* pr
   if ((const void*)out_ids == (const void*)window_ids) return LA_ERR_ARG;
   if (B < 1 || B > 64 || W < 1 || W > kMaxWindow) return LA_ERR_SHAPE;
   return hip_status(launch_commit(out_ids, window_ids, prefix_len, B, W, mask_id, stream));
+}
+
+la_status la_pbd_mark_tokens(const int32_t* ids, int32_t B, int32_t W, const int32_t* first,
+                             const int32_t* count, uint32_t* bits, int32_t words, int32_t vocab,
+                             hipStream_t stream) {
+  if (!ids || !bits) return LA_ERR_ARG;
+  if (B < 1 || B > 64 || W < 1 || W > kMaxWindow || vocab < 1 || (int64_t)words * 32 < vocab)
+    return LA_ERR_SHAPE;
+  return hip_status(launch_mark_tokens(ids, B, W, first, count, bits, words, vocab, stream));
 }
 
 la_status la_pbd_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,

@@ -411,10 +411,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int ks, in
     }
   } else {  // EPI_ARGMAX: running per-row top-2 over this workgroup's columns
     if (lane < rows) {
+      // the tile's 16 bits of this row's bitmap (repetition penalty)
+      const uint32_t used = rep_word(a, a.m_base + lane, tile * 16) >> ((tile * 16) & 31);
       for (int c = 0; c < 16; ++c) {
         const int n = tile * 16 + c;
         if (n >= a.N) break;
-        const float v = outv[lane * 17 + c];
+        float v = outv[lane * 17 + c];
+        if ((used >> c) & 1u) v = rep_penalise(v, a.rep_theta);
         if (v > t2.v1) {
           t2.v2 = t2.v1;
           t2.v1 = v;

@@ -458,10 +458,15 @@ void k_gemm_big(GemmArgs a) {
         if (grp < C::NG && tile < a.n_tiles) {
           const float* src = stage + r * SROW + grp * 8;
           const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+          const int n0 = tile * 16 + half * 8;
+          // the group's 8 bits of this row's bitmap (repetition penalty)
+          const uint32_t used = row_ok ? rep_word(a, m, n0) >> (n0 & 31) : 0u;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int n = tile * 16 + half * 8 + e;
-            if (n < a.N) top2_merge(v1, i1, v2, e < 4 ? x0[e] : x1[e - 4], n, -INFINITY);
+            const int n = n0 + e;
+            float x = e < 4 ? x0[e] : x1[e - 4];
+            if ((used >> e) & 1u) x = rep_penalise(x, a.rep_theta);
+            if (n < a.N) top2_merge(v1, i1, v2, x, n, -INFINITY);
           }
         }
       }

@@ -74,6 +74,19 @@ __device__ __forceinline__ WPtr wptr(const GemmArgs& a, int tile) {
 
 // Running top-2 of a row: (v1, i1) the best value and its column (lowest index
 // on ties), v2 the second best value.
+// Repetition penalty of a used token's logit: divided by theta when
+// positive, multiplied otherwise (a positive per-row scale applied before or
+// after gives the same ranking).
+__device__ __forceinline__ float rep_penalise(float v, float theta) {
+  return v > 0.f ? v / theta : v * theta;
+}
+
+// The bitmap word of row m holding vocabulary id n (bit n % 32), 0 without a
+// bitmap.
+__device__ __forceinline__ uint32_t rep_word(const GemmArgs& a, int m, int n) {
+  return a.rep_bits ? a.rep_bits[(size_t)(m / a.rep_rows) * a.rep_words + (n >> 5)] : 0u;
+}
+
 struct Top2 {
   float v1, v2;
   int i1;

@@ -51,6 +51,11 @@ struct GemmArgs {
   // ARGMAX epilogue
   float* amax;               // [M][n_parts][3] (top1, index bits, top2), one part per workgroup
   int n_parts;
+  // repetition penalty of the ARGMAX epilogue (rep_bits nullable): row m ranks
+  // its logits with those of the tokens set in bitmap m / rep_rows penalised
+  const uint32_t* rep_bits;  // [M / rep_rows][rep_words] vocabulary bitmaps
+  int rep_words, rep_rows;
+  float rep_theta;
 };
 
 // Row packing: v = x[m] + sum_s parts[s][m] (fixed order), optionally stored to
@@ -129,6 +134,8 @@ hipError_t launch_pack_weight(const la_weight& src, int layout, void* dst, void*
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len, int B,
                          int W, int mask_id, hipStream_t s);
+hipError_t launch_mark_tokens(const int32_t* ids, int B, int W, const int32_t* first, const int32_t* count,
+                              uint32_t* bits, int words, int vocab, hipStream_t s);
 hipError_t launch_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,
                                 int32_t* prefix_len, int32_t* causal_rows, int32_t* window_len, int B,
                                 int W, int block, int mask_id, hipStream_t s);

@@ -160,4 +160,27 @@ hipError_t launch_commit_refeed(const int32_t* out_ids, const int32_t* n_accept,
   return hipGetLastError();
 }
 
+// Set the bitmap bit of every selected window id: ids[b][j] for first[b] <= j
+// < first[b] + count[b] (defaults 0 and W); ids outside [0, vocab) are skipped.
+__global__ __launch_bounds__(256) void k_mark_tokens(const int32_t* ids, int B, int W, const int32_t* first,
+                                                     const int32_t* count, uint32_t* bits, int words,
+                                                     int vocab) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= B * W) return;
+  const int b = t / W, j = t - b * W;
+  const int j0 = first ? first[b] : 0;
+  const int n = count ? count[b] : W;
+  if (j < j0 || j >= j0 + n) return;
+  const int id = ids[t];
+  if (id < 0 || id >= vocab) return;
+  atomicOr(bits + (size_t)b * words + (id >> 5), 1u << (id & 31));
+}
+
+hipError_t launch_mark_tokens(const int32_t* ids, int B, int W, const int32_t* first, const int32_t* count,
+                              uint32_t* bits, int words, int vocab, hipStream_t s) {
+  hipLaunchKernelGGL(k_mark_tokens, dim3((B * W + 255) / 256), dim3(256), 0, s, ids, B, W, first, count,
+                     bits, words, vocab);
+  return hipGetLastError();
+}
+
 }  // namespace la

@@ -240,6 +240,20 @@ la_status la_lm_head_argmax(const float* h, int32_t M, const la_weight* lm,
                             const uint16_t* norm_gain, float rms_eps, int32_t* ids, float* top1,
                             float* gap, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+/* The same with a repetition penalty (the Jetson page's generate call, Part 1
+ * section 1.4, passes repetition_penalty=1.1 beside greedy selection; the pages
+ * give no formula, and this is the plain one): row m's logit z of a vocabulary
+ * id whose bit is set in bitmap m / rep_rows is ranked as z / rep_penalty when
+ * z > 0 and z * rep_penalty otherwise; top1 and gap are the penalised values.
+ * rep_bits uint32 [ceil(M / rep_rows)][rep_words] (id v is bit v % 32 of word
+ * v / 32), or NULL for none.  LA_ERR_ARG when rep_bits is given with rep_rows
+ * < 1, rep_words * 32 < lm->n, or rep_penalty not positive and finite. */
+la_status la_lm_head_argmax_penalized(const float* h, int32_t M, const la_weight* lm,
+                                      const uint16_t* norm_gain, float rms_eps,
+                                      const uint32_t* rep_bits, int32_t rep_words,
+                                      int32_t rep_rows, float rep_penalty, int32_t* ids,
+                                      float* top1, float* gap, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 /* One decoder layer for the window rows (RMSNorm, QKV + bias, RoPE at positions
  * P_b + j, bf16 K/V written to the cache at slots P_b + j, window attention, O
@@ -264,6 +278,38 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream);
+/* Options of la_pbd_step_opts (zero-initialise, then set what is used):
+ *  - causal_rows, window_len: int32 [B] device arrays of a re-fed window
+ *    (la_pbd_step_refeed), or NULL;
+ *  - rep_bits: uint32 [B][rep_words] device bitmaps of the vocabulary ids
+ *    already in each sequence (id v is bit v % 32 of word v / 32), or NULL;
+ *    every window row of sequence b ranks its logits with those ids'
+ *    penalised by rep_penalty as in la_lm_head_argmax_penalized;
+ *    rep_words * 32 >= the lm_head's vocabulary, rep_penalty positive and
+ *    finite (else LA_ERR_ARG). */
+typedef struct {
+  const int32_t* causal_rows;
+  const int32_t* window_len;
+  const uint32_t* rep_bits;
+  int32_t rep_words;
+  float rep_penalty;
+} la_step_opts;
+la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                           const int32_t* prefix_len, const la_step_opts* opts, int32_t B, int32_t W,
+                           int32_t max_len, int32_t* out_ids, float* out_gap, float* out_hidden,
+                           void* workspace, size_t workspace_bytes, int32_t* err,
+                           hipStream_t stream);
+
+/* Mark tokens in the repetition bitmaps (uint32 [B][words], device): for
+ * each sequence b, ids[b][j] for first[b] <= j < first[b] + count[b] (first
+ * NULL: 0; count NULL: W) gets its bit set; ids outside [0, vocab) are
+ * skipped.  ids int32 [B][W].  For a decode loop: mark the tokens it accepts.
+ * Only enqueues (graph-capturable).  LA_ERR_ARG for NULL ids or bits,
+ * LA_ERR_SHAPE outside 1 <= B <= 64, 1 <= W <= 16, words * 32 >= vocab >= 1. */
+la_status la_pbd_mark_tokens(const int32_t* ids, int32_t B, int32_t W, const int32_t* first,
+                             const int32_t* count, uint32_t* bits, int32_t words, int32_t vocab,
+                             hipStream_t stream);
+
 /* The step on a re-fed window (la_pbd_attention_refeed): causal_rows and
  * window_len are int32 [B] device arrays; either may be NULL (then 0 re-fed
  * rows, or m->window_mask decides; W real rows).  Every row, padding

@@ -157,6 +157,25 @@ def test_commit_rejects_bad_arguments_before_launch(lib):
     assert lib.la_pbd_commit(a, b_, p, 2, 17, 7, None) == -2
 
 
+def test_repetition_penalty_entry_points_reject_bad_arguments(lib):
+    a = ctypes.c_void_p(4096)
+    w = b.LaWeight(fmt=0, n=1000, k=2048, group=0, layout=1, data=a)
+    ws = lib.la_lm_head_argmax_workspace(6, ctypes.byref(w))
+    pen = lambda bits, words=32, rows=6, theta=1.1: lib.la_lm_head_argmax_penalized(
+        a, 6, ctypes.byref(w), None, 1e-6, bits, words, rows, theta, a, None, None, a, ws, None)
+    assert pen(a, words=31) == -1           # 31 words hold 992 < 1000 ids
+    assert pen(a, rows=0) == -1
+    assert pen(a, theta=0.0) == -1
+    assert pen(a, theta=float("inf")) == -1
+    mark = lambda *x: lib.la_pbd_mark_tokens(*x)
+    assert mark(None, 2, 6, None, None, a, 32, 1000, None) == -1
+    assert mark(a, 2, 6, None, None, None, 32, 1000, None) == -1
+    assert mark(a, 0, 6, None, None, a, 32, 1000, None) == -2
+    assert mark(a, 2, 17, None, None, a, 32, 1000, None) == -2
+    assert mark(a, 2, 6, None, None, a, 31, 1000, None) == -2
+    assert mark(a, 2, 6, None, None, a, 32, 0, None) == -2
+
+
 def test_refeed_entry_points_reject_bad_arguments_before_launch(lib):
     a, w_ = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     p, c, l, n = ctypes.c_void_p(12288), ctypes.c_void_p(16384), ctypes.c_void_p(20480), ctypes.c_void_p(24576)

@@ -236,6 +236,76 @@ def test_lm_head_argmax(fmt, V, M):
     assert np.max(np.abs(gap.cpu().numpy() - rgap)) < 1e-3
 
 
+def _rep_sets(rng, n_sets, V, per_set, must=None):
+    """Random vocabulary sets, each also holding the ids in must[i] (if any)."""
+    sets = []
+    for i in range(n_sets):
+        x = rng.choice(V, size=per_set, replace=False)
+        if must is not None:
+            x = np.concatenate([x, np.asarray(must[i]).reshape(-1)])
+        sets.append(np.unique(x))
+    return sets
+
+
+def _rep_bitmaps(sets, V):
+    words = B.rep_words(V)
+    bits = np.zeros((len(sets), words), dtype=np.uint32)
+    for i, x in enumerate(sets):
+        for v in x:
+            bits[i, v >> 5] |= np.uint32(1) << np.uint32(v & 31)
+    return torch.from_numpy(bits.view(np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("fmt,V,M", [("bf16", 20011, 12), ("bf16", 20011, 192), ("int4", 20011, 48)])
+def test_lm_head_argmax_repetition_penalty(fmt, V, M):
+    # every row's unpenalised winner is in its set, so the penalty decides
+    d = synth.ModelDims(n_layers=1, vocab=V)
+    m = synth.make_model(d, fmt, seed=73, device=DEV)
+    lm = m["lm_head"] if m["lm_head"] is not None else m["embed"]
+    h = torch.randn((M, d.hidden), device=DEV, generator=torch.Generator(device=DEV).manual_seed(V + M))
+    f = O.rmsnorm(h.cpu().numpy().astype(np.float64), O.bf16_to_float(m["final_norm"].cpu().numpy()),
+                  d.rms_eps)
+    rid0, _, _ = O.lm_head_argmax(f, np_tree(lm))
+    rows = 6
+    rng = np.random.default_rng(M)
+    sets = _rep_sets(rng, M // rows, V, 400, must=[rid0[i * rows:(i + 1) * rows] for i in range(M // rows)])
+    bits = _rep_bitmaps(sets, V)
+    ids, top1, gap = B.lm_head_argmax(h, lm, norm_gain=m["final_norm"], rep_bits=bits, rep_rows=rows,
+                                      rep_penalty=1.1)
+    torch.cuda.synchronize()
+    rid, rtop, rgap = O.lm_head_argmax(f, np_tree(lm), rep_sets=[sets[t // rows] for t in range(M)],
+                                       rep_penalty=1.1)
+    n, bad, excl = ids_match(ids.cpu().numpy(), rid, rgap)
+    changed = int((rid != rid0).sum())
+    _log(f"lm_head penalised {fmt} V={V} M={M}: {n} compared, {bad} mismatches, {excl} near-ties "
+         f"excluded; the penalty moved {changed} of {M} winners")
+    assert bad == 0 and changed > M // 4
+    assert np.max(np.abs(top1.cpu().numpy() - rtop)) < 1e-3
+    assert np.max(np.abs(gap.cpu().numpy() - rgap)) < 1e-3
+
+
+def test_mark_tokens_sets_the_selected_bits():
+    V, Bn, W = 3001, 5, 11
+    g = torch.Generator().manual_seed(3)
+    ids = torch.randint(-5, V + 5, (Bn, W), generator=g, dtype=torch.int32)
+    first = torch.tensor([0, 2, 5, 10, 3], dtype=torch.int32)
+    count = torch.tensor([11, 4, 0, 1, 8], dtype=torch.int32)
+    bits = torch.zeros((Bn, B.rep_words(V)), dtype=torch.int32, device=DEV)
+    B.mark_tokens(ids.to(DEV), bits, V, first.to(DEV), count.to(DEV))
+    B.mark_tokens(ids.to(DEV), bits, V, count=torch.full((Bn,), 1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    want = [set() for _ in range(Bn)]
+    for b in range(Bn):
+        for j in list(range(int(first[b]), int(first[b] + count[b]))) + [0]:
+            v = int(ids[b, j])
+            if 0 <= v < V:
+                want[b].add(v)
+    got = bits.cpu().numpy().view(np.uint32)
+    for b in range(Bn):
+        have = {w * 32 + k for w in range(got.shape[1]) for k in range(32) if (got[b, w] >> k) & 1}
+        assert have == want[b], b
+
+
 # ---------------------------------------------------------------- one layer
 
 def _layer_case(wname, P_override=None, fmt=None):
@@ -292,7 +362,7 @@ def test_layer_batch8_large_m(fmt):
 
 # ---------------------------------------------------------------- whole step
 
-def _step_case(d, fmt, P_list, W, seed, mask_id=None, causal=False, refeed=None):
+def _step_case(d, fmt, P_list, W, seed, mask_id=None, causal=False, refeed=None, rep=None):
     model = synth.make_model(d, fmt, seed, DEV)
     P = torch.tensor(P_list, dtype=torch.int32)
     cache = synth.make_cache(d, P, W, seed=seed + 1, device=DEV)
@@ -306,12 +376,16 @@ def _step_case(d, fmt, P_list, W, seed, mask_id=None, causal=False, refeed=None)
     if refeed is not None:
         cr = torch.tensor(refeed[0], dtype=torch.int32, device=DEV)
         wl = torch.tensor(refeed[1], dtype=torch.int32, device=DEV)
+    rb = None if rep is None else _rep_bitmaps(rep[0], d.vocab)
     out_ids, gap, hid = B.pbd_step(dm, dc, ids, P.to(DEV), int(P.max()) + W, want_hidden=True,
-                                   err=err, causal_rows=cr, window_len=wl)
+                                   err=err, causal_rows=cr, window_len=wl, rep_bits=rb,
+                                   rep_penalty=1.0 if rep is None else rep[1])
     torch.cuda.synchronize()
     ref = O.pbd_step(mn, cn, ids.cpu().numpy(), P.numpy(), return_hidden=True, causal=causal,
                      causal_rows=None if refeed is None else refeed[0],
-                     window_len=None if refeed is None else refeed[1])
+                     window_len=None if refeed is None else refeed[1],
+                     rep_sets=None if rep is None else rep[0],
+                     rep_penalty=1.0 if rep is None else rep[1])
     return out_ids.cpu().numpy(), gap.cpu().numpy(), hid.cpu().numpy(), ref, int(err.item())
 
 
@@ -437,6 +511,25 @@ def test_step_refeed(fmt, B_, W):
     assert err == 0
     assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
     assert bad == 0
+
+
+@pytest.mark.parametrize("fmt,B_", [("bf16", 3), ("int4", 3), ("bf16", 32)])
+def test_step_repetition_penalty(fmt, B_):
+    # each sequence's set holds its unpenalised winners and a random tenth of
+    # the vocabulary; every row of the window ranks with it
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    P_list = [0, 31, 450][:B_] if B_ <= 3 else [int(p) for p in torch.randint(
+        0, 700, (B_,), generator=torch.Generator().manual_seed(11))]
+    _, _, _, ref0, _ = _step_case(d, fmt, P_list, 6, seed=170 + B_)
+    rng = np.random.default_rng(B_)
+    sets = _rep_sets(rng, B_, d.vocab, 300, must=list(ref0["ids"]))
+    got_ids, got_gap, hid, ref, err = _step_case(d, fmt, P_list, 6, seed=170 + B_, rep=(sets, 1.1))
+    n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
+    changed = int((ref["ids"] != ref0["ids"]).sum())
+    _log(f"step with repetition penalty {fmt} B={B_}: ids {n} compared, {bad} bad, {excl} excluded; "
+         f"{changed} of {ref['ids'].size} winners moved by the penalty")
+    assert err == 0 and bad == 0 and changed > ref["ids"].size // 4
+    assert np.max(np.abs(got_gap - ref["gap"])) < 1e-3
 
 
 def test_step_refeed_flags_bad_rows():
