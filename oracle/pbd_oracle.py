@@ -49,7 +49,7 @@ __all__ = [
     "embed_rows", "rmsnorm", "silu", "rope_angles", "rope_apply", "window_attention",
     "repetition_penalty",
     "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "pbd_emission_loop",
-    "refeed_commit", "pbd_refeed_loop",
+    "refeed_commit", "pbd_refeed_loop", "pbd_prefill",
 ]
 
 
@@ -339,21 +339,26 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64, rep_sets=None, rep_penal
 
 def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidden=False,
              layers=None, causal=False, causal_rows=None, window_len=None, rep_sets=None,
-             rep_penalty=1.0):
+             rep_penalty=1.0, input_embeds=None):
     """One PBD window step for every sequence.
 
     window_ids [B, W] -> per-position argmax ids [B, W] and top-2 gaps [B, W].
     causal_rows / window_len [B] make it a re-fed window (window_attention).
     rep_sets: per sequence, the vocabulary ids already in it (or None); every
     row of the sequence ranks its logits with those penalised
-    (repetition_penalty, rep_penalty).
+    (repetition_penalty, rep_penalty).  input_embeds [B, W, H] (or None):
+    rows whose id is negative take this row instead of an embedding row.
     The step writes nothing into ``cache``; it returns the bf16 K/V it would
     store at slots P_b .. P_b+W-1 of each layer.
     """
     dims = model["dims"]
     ids = np.asarray(window_ids)
     B, W = ids.shape
-    h = embed_rows(ids.reshape(-1), model["embed"], dtype)
+    flat = ids.reshape(-1)
+    h = embed_rows(np.where(flat < 0, 0, flat), model["embed"], dtype)
+    if input_embeds is not None:
+        emb_in = np.asarray(input_embeds, dtype=dtype).reshape(B * W, -1)
+        h[flat < 0] = emb_in[flat < 0]
     kv = []
     n_layers = len(model["layers"]) if layers is None else layers
     for l in range(n_layers):
@@ -469,3 +474,27 @@ def pbd_refeed_loop(model, cache, window_ids, prefix_len, causal_rows, window_le
         ids, P, c, w = refeed_commit(r["ids"], ids, P, c, w, block, mask_id,
                                      None if n_accept is None else n_accept[s])
     return outs, (ids, P, c, w), cc
+
+
+def pbd_prefill(model, cache, ids, prefix_len, input_embeds=None, dtype=np.float64):
+    """Prefill of L prompt positions per sequence after a cached prefix of P_b.
+
+    The prompt is the image tokens and the text: rows whose id is negative take
+    their input row from input_embeds [B, L, H] (the vision encoder's features
+    spliced in over the image-token positions: "LocateAnything-3B — ONNX
+    WebGPU (INT4 + 4-bit embeddings)", sections "Why this repo exists" and
+    "Embedding gather / dequant (JS reference)"), the others an embedding row.
+    The prefill is the fixed cost before decoding in the Jetson page's latency
+    breakdown (section 3.1).  Every row attends causally (a plain causal LM pass over
+    the prompt: the re-fed window with every row causal).  Returns the argmax
+    id, top-2 gap and final hidden state of each sequence's last row, and the
+    bf16 K/V of every row (as pbd_step).
+    """
+    ids = np.asarray(ids)
+    B, L = ids.shape
+    r = pbd_step(model, cache, ids, prefix_len, dtype, return_hidden=True, causal=True,
+                 input_embeds=input_embeds)
+    last = np.arange(B) * L + (L - 1)
+    return {"ids": r["ids"][:, L - 1], "gap": r["gap"][:, L - 1], "hidden": r["hidden"][last],
+            "kv": r["kv"]}
+

@@ -722,3 +722,51 @@ def test_repetition_penalty_special_cases():
         order = np.argsort(-row, kind="stable")
         assert got[0][t] == order[0]
         assert abs(got[2][t] - (row[order[0]] - row[order[1]])) < 1e-12
+
+
+# ---------------------------------------------------------------- prefill
+
+def test_prefill_equals_token_by_token_decode():
+    # A causal pass over L prompt positions gives the K/V of every position
+    # and the last position's hidden state and id that L single-token decode
+    # steps (W = 1, each storing its K/V) give.
+    d = TINY
+    L, Ps = 7, (0, 9)
+    model, _, _ = _tiny_setup(seed=51)
+    cache = _np(synth.make_cache(d, torch.tensor(list(Ps)), L, seed=52))
+    ids = synth.draw_window_ids(2, L, d.vocab, 53, mask_id=-1).numpy()
+    r = O.pbd_prefill(model, cache, ids, Ps)
+    for b in range(2):
+        sub = {k: (np.array(v, copy=True) if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+        sub["block_table"] = sub["block_table"][[b]]
+        for j in range(L):
+            rj = O.pbd_step(model, sub, ids[b:b + 1, j:j + 1], [Ps[b] + j], return_hidden=True)
+            for l, (kb, vb) in enumerate(rj["kv"]):
+                assert np.abs(r["kv"][l][0][b * L + j].astype(np.int32) - kb[0].astype(np.int32)).max() <= 1
+                assert np.abs(r["kv"][l][1][b * L + j].astype(np.int32) - vb[0].astype(np.int32)).max() <= 1
+            _store_kv(sub, rj["kv"], [Ps[b] + j], 1, 1, [1])
+        np.testing.assert_allclose(r["hidden"][b], rj["hidden"][0], rtol=1e-12, atol=1e-12)
+        assert r["ids"][b] == rj["ids"][0, 0]
+
+
+def test_prefill_spliced_rows_equal_their_embedding_rows():
+    # a spliced input row that equals an embedding row gives the same result,
+    # bit for bit, as that row's id; another spliced row changes the result
+    d = TINY
+    L, Ps = 6, (3, 5)
+    model, _, _ = _tiny_setup(seed=61)
+    cache = _np(synth.make_cache(d, torch.tensor(list(Ps)), L, seed=62))
+    ids = synth.draw_window_ids(2, L, d.vocab, 63, mask_id=-1).numpy()
+    ref = O.pbd_prefill(model, cache, ids, Ps)
+    emb = np.zeros((2, L, d.hidden))
+    spliced = ids.copy()
+    for b, j in ((0, 1), (0, 2), (1, 0)):
+        emb[b, j] = O.embed_rows([ids[b, j]], model["embed"])[0]
+        spliced[b, j] = -1
+    got = O.pbd_prefill(model, cache, spliced, Ps, input_embeds=emb)
+    np.testing.assert_array_equal(got["hidden"], ref["hidden"])
+    np.testing.assert_array_equal(got["ids"], ref["ids"])
+    emb[0, 2] += 0.5
+    other = O.pbd_prefill(model, cache, spliced, Ps, input_embeds=emb)
+    assert np.abs(other["hidden"][0] - ref["hidden"][0]).max() > 1e-6
+    np.testing.assert_array_equal(other["hidden"][1], ref["hidden"][1])
