@@ -365,6 +365,40 @@ def refeed_leg(B, synth, torch, dm, model, dev, stream, args):
             "windows_per_s": round(1000.0 / ms_step * w.batch, 2)}
 
 
+def prefill_leg(B, synth, torch, dm, model, dev, timed, args):
+    """Prefill of the batch-1 workload's prompt: 256 image-token rows (N(0,1)
+    features spliced in) and 64 prompt tokens, all causal, as one captured
+    graph replayed; K/V of the 320 rows written, the first generated id out."""
+    w = synth.WORKLOADS["step_b1_p1280"]
+    d = w.dims
+    n_img, n_txt = 256, 64
+    L = n_img + n_txt
+    log("bench: prefill leg")
+    P = torch.zeros(1, dtype=torch.int32)
+    cache = synth.make_cache(d, P, L, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(1, L, d.vocab, w.input_seed, mask_id=-1, device=dev)
+    ids[:, :n_img] = -1
+    emb = torch.randn((1, L, d.hidden), device=dev, generator=torch.Generator(device=dev).manual_seed(5))
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    ws = B.Workspace(dev)
+    B.pbd_prefill(dm, dc, ids, Pd, L, embeds=emb, ws=ws)  # sizes the workspace
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.pbd_prefill(dm, dc, ids, Pd, L, embeds=emb, ws=ws)
+    for _ in range(max(2, args.warmup)):
+        graph.replay()
+    reps = max(3, args.steps // 6)
+    ms, _ = timed(graph.replay, reps)
+    log(f"bench: prefill of {L} rows ({n_img} spliced + {n_txt} tokens): {ms:.3f} ms, "
+        f"{L * 1000.0 / ms:.0f} rows/s")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": "prefill_b1_l320", "batch": 1, "rows": L, "spliced_rows": n_img, "reps": reps,
+            "ms": round(ms, 4), "rows_per_s": round(L * 1000.0 / ms, 1)}
+
+
 def causal_leg(B, synth, torch, model, dev, timed, args):
     """The batch-1 step with the RK3588 conversion's causal window (window row j
     sees the prefix and window rows 0..j) instead of the bidirectional one."""
@@ -403,7 +437,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=72)
     ap.add_argument("--row-major", action="store_true", help="keep the row-major weight layout")
     ap.add_argument("--no-extra-legs", action="store_true",
-                    help="skip the emission-loop, prefix-32768, causal-window and re-fed loop legs")
+                    help="skip the emission-loop, prefix-32768, causal-window, re-fed loop and prefill legs")
     ap.add_argument("--no-batch32", action="store_true",
                     help="skip the batch-32 leg reported beside the batch-1 step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -551,6 +585,7 @@ def main():
         result["prefix_32768"] = probe_leg(B, synth, torch, dm, model, dev, stream, timed, args)
         result["causal_window"] = causal_leg(B, synth, torch, model, dev, timed, args)
         result["refeed_loop"] = refeed_leg(B, synth, torch, dm, model, dev, stream, args)
+        result["prefill"] = prefill_leg(B, synth, torch, dm, model, dev, timed, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)

@@ -30,6 +30,7 @@ EXPORTED = [
     "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
     "la_pbd_attention_masked", "la_pbd_attention_refeed", "la_pbd_step_refeed",
     "la_pbd_commit_refeed", "la_pbd_step_opts", "la_lm_head_argmax_penalized", "la_pbd_mark_tokens",
+    "la_pbd_prefill_workspace", "la_pbd_prefill",
 ]
 
 
@@ -135,6 +136,10 @@ def load() -> ctypes.CDLL:
                                                   c_void_p, c_void_p, c_size_t, c_void_p]),
         "la_pbd_mark_tokens": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                          c_int32, c_int32, c_void_p]),
+        "la_pbd_prefill_workspace": (c_size_t, [POINTER(LaModel), c_int32, c_int32, c_int32]),
+        "la_pbd_prefill": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
+                                     c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -480,6 +485,29 @@ def pbd_commit_refeed(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_le
     _check(lib.la_pbd_commit_refeed(_ptr(out_ids), _ptr(n_accept), _ptr(window_ids),
                                     _ptr(prefix_len), _ptr(causal_rows), _ptr(window_len), B, W,
                                     int(block), int(mask_id), _stream()), "la_pbd_commit_refeed")
+
+
+def pbd_prefill(model: DeviceModel, cache: DeviceCache, ids: torch.Tensor, prefix_len: torch.Tensor,
+                max_len: int, embeds: Optional[torch.Tensor] = None, want_hidden: bool = False,
+                ws: Optional[Workspace] = None, err: Optional[torch.Tensor] = None):
+    """Prefill of ids [B, L] (negative ids take their row of embeds [B, L, H]);
+    returns (first generated id [B], gap [B], last-row hidden [B, H] or None)."""
+    lib = load()
+    _require_cuda(ids, prefix_len, embeds, err)
+    B, L = ids.shape
+    dev = ids.device
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    gap = torch.empty(B, dtype=torch.float32, device=dev)
+    hid = torch.empty((B, model.dims.hidden), dtype=torch.float32, device=dev) if want_hidden else None
+    need = lib.la_pbd_prefill_workspace(ctypes.byref(model.struct), B, L, max_len)
+    if need == 0:
+        raise LaError("la_pbd_prefill_workspace rejected the model or shape")
+    buf = _ws(ws).get(need)
+    _check(lib.la_pbd_prefill(ctypes.byref(model.struct), ctypes.byref(cache.struct), _ptr(ids),
+                              _ptr(embeds), _ptr(prefix_len), B, L, max_len, _ptr(out), _ptr(gap),
+                              _ptr(hid), _ptr(buf), buf.numel(), _ptr(err), _stream()),
+           "la_pbd_prefill")
+    return out, gap, hid
 
 
 def mark_tokens(ids: torch.Tensor, rep_bits: torch.Tensor, vocab: int,

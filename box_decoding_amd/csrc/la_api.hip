@@ -49,6 +49,8 @@ constexpr size_t kMaxWeightBytes = (size_t)1 << 31;
 // wave per 16 of them, at most 8 waves).
 constexpr int kMaxWindow = 16;
 constexpr int kMaxQueryCols = 128;
+// Rows of one prefill call (B times the prompt length rounded up to 16).
+constexpr int64_t kMaxPrefillRows = 8192;
 
 la_status attention_entry(const float* q, const la_kv_cache* kv, int32_t layer, int32_t n_heads,
                           int32_t n_kv_heads, int32_t head_dim, const int32_t* prefix_len,
@@ -124,14 +126,32 @@ struct StepWs {
   float* part_ml;
   float* amax;
   float* parts;       // K-slice partial sums of the O and down projections
+  // prefill: the attention's view of the prompt as 16-row windows, the
+  // per-sequence flags and the last rows
+  int32_t* pre_prefix;
+  int32_t* pre_causal;
+  int32_t* pre_wlen;
+  int32_t* pre_flags;
+  float* h_last;
   int pps, max_splits, nqp, vocab_parts;
   size_t bytes;
 };
 
-StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool lm_head) {
+// Rows of one attention window of a prefill (the attention sees the prompt as
+// windows of this many causal rows).
+constexpr int kPrefillChunk = 16;
+
+// Workspace of a step (chunks = 0) or of a prefill of B sequences of W =
+// 16 * chunks rows, whose attention runs as B * chunks windows of 16 rows and
+// whose lm_head takes one row per sequence.
+StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool lm_head,
+                  int chunks = 0) {
   StepWs s;
+  memset(&s, 0, sizeof(s));
   Carver c(ws);
   const int T = B * W;
+  const int aB = chunks ? B * chunks : B, aW = chunks ? kPrefillChunk : W;
+  const int lm_rows = chunks ? B : T;
   const int H = m->hidden, HQ = m->n_heads * m->head_dim, F = m->inter;
   const int Kx = H > HQ ? H : HQ;
   s.h = c.take<float>((size_t)T * H);
@@ -146,14 +166,21 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
   s.asum_m = c.take<float>((size_t)((T + 7) / 8) * (F / 128) * 16);
   s.rope = c.take<float2>((size_t)T * 64);
   s.flags = c.take<int32_t>(T);
-  plan_attention(B, m->n_kv_heads, max_len, &s.pps, &s.max_splits);
-  s.nqp = attn_nqp(W, m->n_heads / m->n_kv_heads);
-  const size_t units = (size_t)B * m->n_kv_heads * s.max_splits * s.nqp;
+  plan_attention(aB, m->n_kv_heads, max_len, &s.pps, &s.max_splits);
+  s.nqp = attn_nqp(aW, m->n_heads / m->n_kv_heads);
+  const size_t units = (size_t)aB * m->n_kv_heads * s.max_splits * s.nqp;
   s.part_o = c.take<float>(units * kHeadDim);
   s.part_ml = c.take<float>(units * 2);
   const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
-  s.vocab_parts = gemm_parts(T, lm, EPI_ARGMAX);
-  s.amax = lm_head ? c.take<float>((size_t)T * s.vocab_parts * 3) : nullptr;
+  s.vocab_parts = gemm_parts(lm_rows, lm, EPI_ARGMAX);
+  s.amax = lm_head ? c.take<float>((size_t)lm_rows * s.vocab_parts * 3) : nullptr;
+  if (chunks) {
+    s.pre_prefix = c.take<int32_t>(aB);
+    s.pre_causal = c.take<int32_t>(aB);
+    s.pre_wlen = c.take<int32_t>(aB);
+    s.pre_flags = c.take<int32_t>(B);
+    s.h_last = c.take<float>((size_t)B * H);
+  }
   const int ksp = std::max(gemm_ksplit(T, &m->layers[0].o), gemm_ksplit(T, &m->layers[0].down));
   const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
   const size_t qkv_parts = (size_t)qkv_ksplit(T, &m->layers[0].qkv) * T * NQKV;
@@ -293,10 +320,20 @@ struct Carry {
 // packs h * gain for the next GEMM and leaves per-tile sums of squares; the
 // next GEMM scales its outputs by 1/rms, so no normalisation kernel runs.  `next_gain` is the RMSNorm gain after this
 // layer (the next layer's input norm or the final norm; NULL: h only).
+// The attention's view of the rows when it differs from the layer's (a
+// prefill: B sequences of W rows seen as windows of kPrefillChunk rows).
+struct AttnView {
+  int B, W;
+  const int32_t* prefix_len;
+  const int32_t* causal_rows;
+  const int32_t* window_len;
+  int bt_div;  // windows per block-table row
+};
+
 la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
                     const int32_t* causal_rows, const int32_t* window_len, int B, int W,
                     int max_len, const StepWs& s, float* attn_out, Carry* carry,
-                    const uint16_t* next_gain, hipStream_t st) {
+                    const uint16_t* next_gain, hipStream_t st, const AttnView* av = nullptr) {
   const la_layer& L = m->layers[l];
   const int T = B * W;
   const int H = m->hidden, HQ = m->n_heads * m->head_dim;
@@ -367,6 +404,15 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   at.causal = m->window_mask == LA_MASK_CAUSAL;
   at.causal_rows = causal_rows;
   at.window_len = window_len;
+  at.bt_div = 1;
+  if (av) {
+    at.B = av->B;
+    at.W = av->W;
+    at.prefix_len = av->prefix_len;
+    at.causal_rows = av->causal_rows;
+    at.window_len = av->window_len;
+    at.bt_div = av->bt_div;
+  }
   LA_TRY(launch_attention(at, st));
   if (int4)
     if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true, nullptr, 0, nullptr,
@@ -687,6 +733,7 @@ la_status attention_entry(const float* q, const la_kv_cache* kv, int32_t layer, 
   at.part_o = c.take<float>(units * kHeadDim);
   at.part_ml = c.take<float>(units * 2);
   at.out = out;
+  at.bt_div = 1;
   at.causal = causal;
   at.causal_rows = causal_rows;
   at.window_len = window_len;
@@ -875,6 +922,74 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   LA_TRY(launch_gemm(g, EPI_ARGMAX, int4, stream));
   return hip_status(launch_argmax_reduce(s.amax, T, s.vocab_parts, s.flags, out_ids, nullptr, out_gap,
                                          nullptr, stream));
+}
+
+size_t la_pbd_prefill_workspace(const la_model* m, int32_t B, int32_t L, int32_t max_len) {
+  if (check_model(m) != LA_OK || B < 1 || B > 64 || L < 1) return 0;
+  const int chunks = (L + kPrefillChunk - 1) / kPrefillChunk, Lp = chunks * kPrefillChunk;
+  if (max_len < Lp || (int64_t)B * Lp > kMaxPrefillRows) return 0;
+  return carve_step(m, B, Lp, max_len, nullptr, true, chunks).bytes;
+}
+
+la_status la_pbd_prefill(const la_model* m, const la_kv_cache* kv, const int32_t* ids,
+                         const float* embeds, const int32_t* prefix_len, int32_t B, int32_t L,
+                         int32_t max_len, int32_t* out_ids, float* out_gap, float* out_hidden,
+                         void* workspace, size_t workspace_bytes, int32_t* err,
+                         hipStream_t stream) {
+  la_status st = check_model(m);
+  if (st != LA_OK) return st;
+  if ((st = check_cache(kv, m, B)) != LA_OK) return st;
+  if (B < 1 || B > 64 || L < 1) return LA_ERR_SHAPE;
+  const int chunks = (L + kPrefillChunk - 1) / kPrefillChunk, Lp = chunks * kPrefillChunk;
+  if (max_len < Lp || (int64_t)B * Lp > kMaxPrefillRows) return LA_ERR_SHAPE;
+  if (!ids || !prefix_len || !out_ids) return LA_ERR_ARG;
+  if ((embeds && !aligned16(embeds)) || (out_hidden && !aligned16(out_hidden))) return LA_ERR_ARG;
+  const size_t need = carve_step(m, B, Lp, max_len, nullptr, true, chunks).bytes;
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  const StepWs s = carve_step(m, B, Lp, max_len, workspace, true, chunks);
+  const int T = B * Lp;
+  const int H = m->hidden;
+
+  // the prompt rows: gathered or spliced, RoPE at P_b + j, flags; the
+  // attention's 16-row windows
+  LA_TRY(launch_prefill_views(prefix_len, B, L, chunks, s.pre_prefix, s.pre_causal, s.pre_wlen, stream));
+  PrologueArgs p = base_prologue(m, kv, prefix_len, B, Lp, max_len, s);
+  p.ids = ids;
+  p.emb = m->embed;
+  p.out = s.h;
+  p.err = err;
+  p.in_w = L;
+  p.embeds = embeds;
+  LA_TRY(launch_prologue(p, stream));
+  const AttnView av{B * chunks, kPrefillChunk, s.pre_prefix, s.pre_causal, s.pre_wlen, chunks};
+  Carry carry;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const uint16_t* next_gain = l + 1 < m->n_layers ? m->layers[l + 1].in_norm : nullptr;
+    st = run_layer(m, l, kv, prefix_len, nullptr, nullptr, B, Lp, max_len, s, nullptr, &carry,
+                   next_gain, stream, &av);
+    if (st != LA_OK) return st;
+  }
+  if (carry.pending &&
+      (st = pack_rows(s.h, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, carry.pending,
+                      s.h, stream)) != LA_OK)
+    return st;
+  // each sequence's last prompt row (and its flags) -> final norm, lm_head, argmax
+  LA_TRY(hipMemcpy2DAsync(s.h_last, (size_t)H * sizeof(float), s.h + (size_t)(L - 1) * H,
+                          (size_t)Lp * H * sizeof(float), (size_t)H * sizeof(float), B,
+                          hipMemcpyDeviceToDevice, stream));
+  LA_TRY(hipMemcpy2DAsync(s.pre_flags, sizeof(int32_t), s.flags + (L - 1), (size_t)Lp * sizeof(int32_t),
+                          sizeof(int32_t), B, hipMemcpyDeviceToDevice, stream));
+  if (out_hidden)
+    LA_TRY(hipMemcpyAsync(out_hidden, s.h_last, (size_t)B * H * sizeof(float), hipMemcpyDeviceToDevice,
+                          stream));
+  const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
+  GemmArgs g = base_gemm(lm, B);
+  g.amax = s.amax;
+  if ((st = gemm_from_rows(g, s.h_last, H, m->final_norm, m->rms_eps, s.apack, s.asum, EPI_ARGMAX,
+                           lm->fmt == LA_W_INT4, stream)) != LA_OK)
+    return st;
+  return hip_status(launch_argmax_reduce(s.amax, B, s.vocab_parts, s.pre_flags, out_ids, nullptr,
+                                         out_gap, nullptr, stream));
 }
 
 size_t la_pack_weight_bytes(const la_weight* src, int32_t layout, int32_t scales) {

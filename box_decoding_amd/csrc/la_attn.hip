@@ -220,7 +220,8 @@ __attribute__((amdgpu_waves_per_eu(LA == 1 && NQT > 1 ? 3 : (NQT > 4 ? 2 : 1))))
   const int first = k0 / kBlock;
   // the block ids of the run's pages (one per lane, clamped to the table) and
   // the Q fragments are loaded together with the sequence length, not after it
-  int bt = a.block_table[(size_t)b * a.max_blocks +
+  const int bt_row = a.bt_div > 1 ? b / a.bt_div : b;
+  int bt = a.block_table[(size_t)bt_row * a.max_blocks +
                          min(first + min(lane, a.pages_per_split - 1), a.max_blocks - 1)];
 
   // Q^T operand of this wave's tile: lane (g, r) holds dims kb*32 + 8g .. +8 of

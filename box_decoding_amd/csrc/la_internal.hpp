@@ -94,6 +94,7 @@ struct AttnArgs {
   int causal;                // nonzero: window row j sees slots 0 .. P_b + j only
   const int32_t* causal_rows; // [B] re-fed rows (nullable; overrides `causal`)
   const int32_t* window_len;  // [B] real window rows (nullable: W)
+  int bt_div;                 // windows per block-table row (a prefill's 16-row windows)
 };
 
 struct PrologueArgs {
@@ -112,6 +113,11 @@ struct PrologueArgs {
   const int32_t* window_len;  // [B] real window rows (nullable)
   const int32_t* block_table;
   int max_blocks, num_blocks, cap;
+  // prefill: ids / embeds hold in_w rows per sequence (rows j >= in_w of the
+  // W are padding: zero input, no error); a negative id takes its row of
+  // embeds ([B][in_w][H] fp32, nullable)
+  int in_w;
+  const float* embeds;
 };
 
 struct GemmPlan {
@@ -134,6 +140,8 @@ hipError_t launch_pack_weight(const la_weight& src, int layout, void* dst, void*
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_commit(const int32_t* out_ids, int32_t* window_ids, int32_t* prefix_len, int B,
                          int W, int mask_id, hipStream_t s);
+hipError_t launch_prefill_views(const int32_t* prefix_len, int B, int L, int chunks, int32_t* pp,
+                                int32_t* pc, int32_t* pw, hipStream_t s);
 hipError_t launch_mark_tokens(const int32_t* ids, int B, int W, const int32_t* first, const int32_t* count,
                               uint32_t* bits, int words, int vocab, hipStream_t s);
 hipError_t launch_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, int32_t* window_ids,

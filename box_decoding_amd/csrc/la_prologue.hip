@@ -4,17 +4,36 @@
 
 namespace la {
 
+// Where row t's input comes from: its index in ids / embeds, or -1 for a
+// padding row of a prefill (rows past in_w of each sequence).
+__device__ __forceinline__ int prologue_src(const PrologueArgs& a, int t) {
+  if (a.in_w <= 0) return t;
+  const int b = t / a.W, j = t - b * a.W;
+  return j < a.in_w ? b * a.in_w + j : -1;
+}
+
+// A window id's data error: outside [0, vocab), except a negative id that
+// takes a spliced input row.
+__device__ __forceinline__ bool prologue_id_bad(const PrologueArgs& a, int id) {
+  return id >= a.emb.n || (id < 0 && !a.embeds);
+}
+
 // One workgroup per window row t.
 __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   int id_bad = 0;
   if (a.ids) {
-    const int id = a.ids[t];
+    const int src = prologue_src(a, t);
+    const int id = src >= 0 ? a.ids[src] : 0;
     const int K = a.emb.k;
     float* out = a.out + (size_t)t * K;
-    id_bad = (id < 0 || id >= a.emb.n);
-    if (id_bad) {
+    id_bad = src >= 0 && prologue_id_bad(a, id);
+    if (src >= 0 && id < 0 && a.embeds) {
+      // a spliced input row (the vision features at an image-token position)
+      const float* e = a.embeds + (size_t)src * K;
+      for (int k = tid * 4; k < K; k += 1024) *(float4*)(out + k) = *(const float4*)(e + k);
+    } else if (src < 0 || id_bad) {
       for (int k = tid * 4; k < K; k += 1024) *(float4*)(out + k) = make_float4(0.f, 0.f, 0.f, 0.f);
     } else if (a.emb.fmt == LA_W_BF16) {
       const uint16_t* base = (const uint16_t*)a.emb.data;
@@ -62,10 +81,10 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
       // attend to each other)
       int f = 0;
       if (a.ids) {
-        for (int jj = 0; jj < a.W; ++jj) {
-          const int idj = a.ids[b * a.W + jj];
-          if (idj < 0 || idj >= a.emb.n) f = LA_DERR_TOKEN_ID;
-        }
+        const int nw = a.in_w > 0 ? a.in_w : a.W;
+        for (int jj = tid; jj < nw; jj += 256)
+          if (prologue_id_bad(a, a.ids[b * nw + jj])) f = LA_DERR_TOKEN_ID;
+        if (__syncthreads_or(f)) f = LA_DERR_TOKEN_ID;
       }
       const long n = (long)P + a.W;
       if (P < 0 || n > a.cap) f |= LA_DERR_CAPACITY;
@@ -92,6 +111,26 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   } else if (id_bad && a.err && tid == 0) {
     atomicOr(a.err, LA_DERR_TOKEN_ID);
   }
+}
+
+// The attention's view of a prefill of L rows per sequence: window k of
+// sequence b holds prompt rows 16k .. 16k + 15 at prefix P_b + 16k, every row
+// causal, min(16, L - 16k) of them real.
+__global__ __launch_bounds__(256) void k_prefill_views(const int32_t* prefix_len, int B, int L, int chunks,
+                                                       int32_t* pp, int32_t* pc, int32_t* pw) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * chunks) return;
+  const int b = i / chunks, k = i - b * chunks;
+  pp[i] = prefix_len[b] + 16 * k;
+  pc[i] = 16;
+  pw[i] = min(16, L - 16 * k);
+}
+
+hipError_t launch_prefill_views(const int32_t* prefix_len, int B, int L, int chunks, int32_t* pp,
+                                int32_t* pc, int32_t* pw, hipStream_t s) {
+  hipLaunchKernelGGL(k_prefill_views, dim3((B * chunks + 255) / 256), dim3(256), 0, s, prefix_len, B, L,
+                     chunks, pp, pc, pw);
+  return hipGetLastError();
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {

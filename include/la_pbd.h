@@ -300,6 +300,31 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
                            void* workspace, size_t workspace_bytes, int32_t* err,
                            hipStream_t stream);
 
+/* Prefill of a prompt of L positions per sequence after its cached prefix of
+ * P_b (the fixed cost before decoding in the Jetson page's latency breakdown,
+ * section 3.1).  ids int32 [B][L]: a token id, or a negative id for a row
+ * that takes its input from embeds fp32 [B][L][hidden] (the vision encoder's
+ * features spliced in over the image-token positions, as the WebGPU page's
+ * language graph takes them: "LocateAnything-3B — ONNX WebGPU (INT4 + 4-bit
+ * embeddings)", sections "Why this repo exists" and "Embedding gather /
+ * dequant (JS reference)"); embeds may be NULL when every id is a token.  Every
+ * row attends causally to the prefix and the prompt rows up to its own (a
+ * plain causal pass), and its K/V go to slots P_b .. P_b+L-1 of every layer.
+ * out_ids int32 [B] = the argmax of each sequence's last prompt row (the first
+ * generated token); out_gap fp32 [B] and out_hidden fp32 [B][hidden] (its
+ * final hidden state before the final norm) are nullable.  prefix_len is not
+ * modified.  Rows are processed in windows of 16: max_len >= P_b +
+ * ceil(L/16)*16 and the cache must hold that many slots (the slots past L are
+ * written and lie past the prompt).  B*ceil(L/16)*16 <= 8192, B <= 64.  Data
+ * errors as la_pbd_step (out_ids -1 and bits in *err); a negative id with
+ * embeds NULL is LA_DERR_TOKEN_ID. */
+size_t la_pbd_prefill_workspace(const la_model* m, int32_t B, int32_t L, int32_t max_len);
+la_status la_pbd_prefill(const la_model* m, const la_kv_cache* kv, const int32_t* ids,
+                         const float* embeds, const int32_t* prefix_len, int32_t B, int32_t L,
+                         int32_t max_len, int32_t* out_ids, float* out_gap, float* out_hidden,
+                         void* workspace, size_t workspace_bytes, int32_t* err,
+                         hipStream_t stream);
+
 /* Mark tokens in the repetition bitmaps (uint32 [B][words], device): for
  * each sequence b, ids[b][j] for first[b] <= j < first[b] + count[b] (first
  * NULL: 0; count NULL: W) gets its bit set; ids outside [0, vocab) are

@@ -176,6 +176,11 @@ def test_repetition_penalty_entry_points_reject_bad_arguments(lib):
     assert mark(a, 2, 6, None, None, a, 32, 0, None) == -2
 
 
+def test_prefill_workspace_rejects_bad_shapes(lib):
+    m = b.LaModel()
+    assert lib.la_pbd_prefill_workspace(ctypes.byref(m), 1, 16, 64) == 0   # no layers: bad model
+
+
 def test_refeed_entry_points_reject_bad_arguments_before_launch(lib):
     a, w_ = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     p, c, l, n = ctypes.c_void_p(12288), ctypes.c_void_p(16384), ctypes.c_void_p(20480), ctypes.c_void_p(24576)

@@ -532,6 +532,67 @@ def test_step_repetition_penalty(fmt, B_):
     assert np.max(np.abs(got_gap - ref["gap"])) < 1e-3
 
 
+@pytest.mark.parametrize("fmt,P_list,L,spliced", [
+    ("bf16", [0], 40, (3, 11)),          # 3 windows, the last with 8 real rows
+    ("bf16", [0, 37], 100, (1, 65)),     # 224 rows: the large-M GEMMs
+    ("int4", [5, 0], 24, (0, 10)),
+    ("bf16", [20], 9, (2, 4)),           # 16 rows: the small-M GEMMs
+])
+def test_prefill_matches_oracle(fmt, P_list, L, spliced):
+    """A causal pass over the prompt (rows spliced[0] .. spliced[1]-1 take
+    N(0,1) feature rows instead of embeddings): the first generated id exact
+    where the oracle's gap is >= 1e-3, the last rows' hidden state and every
+    written K/V within the bf16 rel-L2 bar."""
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    Bn, Lp = len(P_list), (L + 15) // 16 * 16
+    model = synth.make_model(d, fmt, 190 + L, DEV)
+    P = torch.tensor(P_list, dtype=torch.int32)
+    cache = synth.make_cache(d, P, Lp, seed=191, device=DEV)
+    poison_unused_slots(cache, P, Lp)
+    ids = synth.draw_window_ids(Bn, L, d.vocab, 192, mask_id=-1, device=DEV)
+    ids[:, spliced[0]:spliced[1]] = -1
+    emb = torch.randn((Bn, L, d.hidden), device=DEV, generator=torch.Generator(device=DEV).manual_seed(193))
+    mn, cn = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, gap, hid = B.pbd_prefill(dm, dc, ids, P.to(DEV), int(P.max()) + Lp, embeds=emb, want_hidden=True,
+                                  err=err)
+    torch.cuda.synchronize()
+    ref = O.pbd_prefill(mn, cn, ids.cpu().numpy(), P.numpy(), input_embeds=emb.cpu().numpy())
+    n, bad, excl = ids_match(out.cpu().numpy(), ref["ids"], ref["gap"])
+    e = rel_l2(hid.cpu().numpy(), ref["hidden"])
+    cg = np_tree(cache)
+    kr_ = vr_ = 0.0
+    for layer in range(d.n_layers):
+        kb, vb = ref["kv"][layer]
+        for b in range(Bn):
+            kg, vg = cache_slots(cg, layer, b, np.arange(P_list[b], P_list[b] + L))
+            kr_ = max(kr_, bf16_bits_rel_l2(kg, kb[b * L:(b + 1) * L]))
+            vr_ = max(vr_, bf16_bits_rel_l2(vg, vb[b * L:(b + 1) * L]))
+    _log(f"prefill {fmt} P={P_list} L={L}: last hidden rel-L2 {e:.2e}, K/V rel-L2 {kr_:.1e}/{vr_:.1e}; "
+         f"ids {n} compared, {bad} bad")
+    assert int(err.item()) == 0 and bad == 0
+    assert e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
+    assert kr_ <= TOL_BF16 and vr_ <= TOL_BF16
+    assert np.max(np.abs(gap.cpu().numpy() - ref["gap"])) < 1e-3
+
+
+def test_prefill_without_embeds_flags_negative_ids():
+    d = synth.ModelDims(n_layers=1, vocab=1000)
+    model = synth.make_model(d, "bf16", 197, DEV)
+    P = torch.tensor([3, 8], dtype=torch.int32)
+    cache = synth.make_cache(d, P, 32, seed=198, device=DEV)
+    ids = torch.ones((2, 20), dtype=torch.int32, device=DEV)
+    ids[1, 7] = -1
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, _, _ = B.pbd_prefill(dm, dc, ids, P.to(DEV), 40, err=err)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert int(err.item()) == B.LA_DERR_TOKEN_ID and o[1] == -1 and o[0] >= 0
+
+
 def test_step_refeed_flags_bad_rows():
     d = synth.ModelDims(n_layers=1, vocab=1000)
     model = synth.make_model(d, "bf16", 93, DEV)
