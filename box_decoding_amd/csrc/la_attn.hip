@@ -355,6 +355,8 @@ __attribute__((amdgpu_waves_per_eu(LA == 1 && NQT > 1 ? 3 : (NQT > 4 ? 2 : 1))))
 // result does not depend on timing.  Combination is the usual log-sum-exp
 // rescaling of (max, sum, unnormalised O).
 constexpr int kMergeGroups = 8;
+// Up to this many runs per sequence the column-group merge serves.
+constexpr int kMergeColsMaxRuns = 32;
 
 struct MergeAcc {
   float m, den;
@@ -446,6 +448,59 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   if (j == 0 && (c4 & 1) == 0) attn_store8(a, b, kvh, qi, 4 * c4, v);
 }
 
+// Merge for few runs (at most 32 per sequence): a workgroup takes 8 query
+// columns of a (sequence, KV head); thread (column j of 8, chunk of 4 dims)
+// combines every run of its column in run order, MB runs' loads in flight
+// together.  Many short workgroups of one column each (k_attn_merge) cost more
+// dispatch than they save once the runs are few.
+template <int MB>
+__global__ __launch_bounds__(256) void k_attn_merge_cols(AttnArgs a) {
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int qi = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int c4 = threadIdx.x & 31;
+  const int NQ = a.W * (a.Hq / a.Hkv);
+  const int kps = a.pages_per_split * kBlock;
+  const size_t base = ((size_t)b * a.Hkv + kvh) * a.max_splits;
+  const float2* ml = (const float2*)a.part_ml;
+  const int ns = (attn_keys(a, b) + kps - 1) / kps;
+  const int q = qi < NQ ? qi : NQ - 1;  // a column past the last repeats it (not stored)
+  float bm = -INFINITY, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < ns; s0 += MB) {
+    float2 m[MB];
+    float4 o[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const size_t u = base + (s0 + i < a.max_splits ? s0 + i : 0);
+      m[i] = ml[u * a.nqp + q];
+      o[i] = *(const float4*)(a.part_o + (u * a.nqp + q) * kHeadDim + 4 * c4);
+    }
+    float nm = bm;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (s0 + i < ns) nm = fmaxf(nm, m[i].x);
+    const float sc = bm == -INFINITY ? 0.f : exp2f(bm - nm);
+    den *= sc;
+    num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if (s0 + i < ns) {
+        const float w = m[i].x == -INFINITY ? 0.f : exp2f(m[i].x - nm);
+        den += w * m[i].y;
+        num.x += w * o[i].x; num.y += w * o[i].y;
+        num.z += w * o[i].z; num.w += w * o[i].w;
+      }
+    }
+    bm = nm;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float v[8];
+  v[0] = num.x * inv; v[1] = num.y * inv; v[2] = num.z * inv; v[3] = num.w * inv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[4 + e] = __shfl_xor(v[e], 1);
+  if (qi < NQ && (c4 & 1) == 0) attn_store8(a, b, kvh, qi, 4 * c4, v);
+}
+
 // Runs of pages_per_split pages: two pages per run while that keeps the grid
 // within about 640 workgroups, longer runs beyond.  Many short runs cost
 // workgroup launches and partial results (24 KB each, written and merged);
@@ -485,6 +540,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   const int NQ = a.W * (a.Hq / a.Hkv);
+  if (a.max_splits <= kMergeColsMaxRuns) {
+    const dim3 cgrid((NQ + 7) / 8, a.Hkv, a.B);
+    if (a.max_splits <= 4) hipLaunchKernelGGL(k_attn_merge_cols<4>, cgrid, dim3(256), 0, s, a);
+    else if (a.max_splits <= 8) hipLaunchKernelGGL(k_attn_merge_cols<8>, cgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_attn_merge_cols<16>, cgrid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 mgrid(NQ, a.Hkv, a.B);
   const int per_group = (a.max_splits + kMergeGroups - 1) / kMergeGroups;
   if (per_group <= 1) hipLaunchKernelGGL(k_attn_merge<1>, mgrid, dim3(256), 0, s, a);

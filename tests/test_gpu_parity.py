@@ -205,14 +205,16 @@ def test_attention_long_context_probe():
 
 
 def test_attention_grid_size_invariance():
-    # a larger max_len with the same run length changes nothing, bit for bit;
-    # longer runs (forced by a long max_len, one of them an odd page count)
-    # agree with the oracle as well
+    # a larger max_len with the same run length and the same merge (up to 32
+    # runs: the column-group merge) changes nothing, bit for bit; past 32 runs
+    # the per-column merge sums in another fixed order; longer runs (forced by
+    # a long max_len, one of them an odd page count) agree with the oracle too
     a = _attention_case([300, 40], 6, seed=3, max_len=306)
-    b = _attention_case([300, 40], 6, seed=3, max_len=1500)
-    c = _attention_case([300, 40], 6, seed=3, max_len=9000)
+    b = _attention_case([300, 40], 6, seed=3, max_len=500)
+    c = _attention_case([300, 40], 6, seed=3, max_len=1500)
+    d = _attention_case([300, 40], 6, seed=3, max_len=9000)
     assert a == b
-    assert max(c) <= TOL_BF16
+    assert max(c) <= TOL_BF16 and max(d) <= TOL_BF16
 
 
 # ---------------------------------------------------------------- lm_head
