@@ -448,11 +448,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   if (j == 0 && (c4 & 1) == 0) attn_store8(a, b, kvh, qi, 4 * c4, v);
 }
 
-// Merge for few runs (at most 32 per sequence): a workgroup takes 8 query
-// columns of a (sequence, KV head); thread (column j of 8, chunk of 4 dims)
-// combines every run of its column in run order, MB runs' loads in flight
-// together.  Many short workgroups of one column each (k_attn_merge) cost more
-// dispatch than they save once the runs are few.
+// Merge for few runs (at most 16, or 32 with 16 sequences and more): a
+// workgroup takes 8 query columns of a (sequence, KV head); thread (column j
+// of 8, chunk of 4 dims) combines every run of its column in run order, MB
+// runs' loads in flight together.  Many short workgroups of one column each
+// (k_attn_merge) cost more dispatch than they save once the runs are few.
 template <int MB>
 __global__ __launch_bounds__(256) void k_attn_merge_cols(AttnArgs a) {
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -540,7 +540,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   const int NQ = a.W * (a.Hq / a.Hkv);
-  if (a.max_splits <= kMergeColsMaxRuns) {
+  // the column-group merge for few runs, or for up to 32 where the per-column
+  // grid is large (measured: batch 8 with 21 runs 6.3 against 4.8 us per-column,
+  // batch 16 with 18 runs faster by column groups)
+  if (a.max_splits <= kMergeColsMaxRuns / 2 || (a.max_splits <= kMergeColsMaxRuns && a.B >= 16)) {
     const dim3 cgrid((NQ + 7) / 8, a.Hkv, a.B);
     if (a.max_splits <= 4) hipLaunchKernelGGL(k_attn_merge_cols<4>, cgrid, dim3(256), 0, s, a);
     else if (a.max_splits <= 8) hipLaunchKernelGGL(k_attn_merge_cols<8>, cgrid, dim3(256), 0, s, a);
