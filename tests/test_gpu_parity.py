@@ -906,3 +906,92 @@ def test_step_packed_model_matches_oracle_and_row_major(fmt):
     _log(f"step packed {fmt}: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
     assert bad == 0 and e <= (TOL_BF16 if fmt == "bf16" else TOL_INT4)
     assert torch.equal(out_p, out_r) and torch.equal(hid_p, hid_r)
+
+
+def test_decode_pipeline_matches_oracle():
+    """Prefill of a prompt with spliced feature rows, then re-fed window steps
+    with the repetition penalty, the accepted tokens marked in the bitmaps and
+    committed on the device with partial acceptance; against the oracle's
+    composition of the same pieces: every real row's ids exact where the
+    oracle's gap is >= 1e-3, the device's state after each commit exact."""
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    L, W, block, mask, steps, theta = 24, 11, 6, 17, 3, 1.1
+    P0 = [0, 40]
+    nb = len(P0)
+    acc = [np.array(a, dtype=np.int32) for a in ([6, 2], [3, 6], [5, 4])]
+    model = synth.make_model(d, "bf16", 211, DEV)
+    P = torch.tensor(P0, dtype=torch.int32)
+    cache = synth.make_cache(d, P, L + 16, extra_tokens=steps * W, seed=212, device=DEV)
+    prompt = synth.draw_window_ids(nb, L, d.vocab, 213, mask_id=-1, device=DEV)
+    prompt[:, 2:10] = -1
+    emb = torch.randn((nb, L, d.hidden), device=DEV, generator=torch.Generator(device=DEV).manual_seed(214))
+    mn, c = np_tree(model), np_tree(cache)
+    mn["dims"] = d
+    dm, dc = B.DeviceModel(model), B.DeviceCache(cache, d.n_layers)
+    max_len = max(P0) + L + 16 + steps * W
+    # oracle: prefill, then the first window
+    pr = O.pbd_prefill(mn, c, prompt.cpu().numpy(), np.array(P0), input_embeds=emb.cpu().numpy())
+    for l, (kb, vb) in enumerate(pr["kv"]):
+        for b in range(nb):
+            for j in range(L):
+                t = P0[b] + j
+                blk = int(c["block_table"][b, t // c["block"]])
+                c["k"][l, blk, :, t % c["block"], :] = kb[b * L + j].view(np.int16)
+                c["v"][l, blk, :, :, t % c["block"]] = vb[b * L + j].view(np.int16)
+    pn = prompt.cpu().numpy()
+    sets = [set(int(x) for x in pn[b] if x >= 0) | {int(pr["ids"][b])} for b in range(nb)]
+    win_o = np.full((nb, W), mask, dtype=np.int32)
+    win_o[:, 0] = pr["ids"]
+    P_o = np.array(P0, dtype=np.int64) + L
+    c_o = np.zeros(nb, dtype=np.int64)
+    w_o = np.full(nb, block, dtype=np.int64)
+    # device: the same
+    out0, _, _ = B.pbd_prefill(dm, dc, prompt, P.to(DEV), max_len, embeds=emb)
+    bits = torch.zeros((nb, B.rep_words(d.vocab)), dtype=torch.int32, device=DEV)
+    for j0 in range(0, L, 12):  # the prompt's tokens (spliced rows are skipped: negative ids)
+        B.mark_tokens(prompt[:, j0:j0 + 12].contiguous(), bits, d.vocab)
+    ids = torch.full((nb, W), mask, dtype=torch.int32, device=DEV)
+    ids[:, 0] = out0
+    B.mark_tokens(ids, bits, d.vocab, count=torch.ones(nb, dtype=torch.int32, device=DEV))
+    Pd = (P + L).to(DEV)
+    cr = torch.zeros(nb, dtype=torch.int32, device=DEV)
+    wl = torch.full((nb,), block, dtype=torch.int32, device=DEV)
+    out_ids = torch.empty((nb, W), dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    live = out0.cpu().numpy() == pr["ids"]
+    compared = 0
+    for s in range(steps):
+        n_acc = torch.from_numpy(acc[s]).to(DEV)
+        first = cr.clone()
+        B.pbd_step(dm, dc, ids, Pd, max_len, out_ids=out_ids, causal_rows=cr, window_len=wl,
+                   rep_bits=bits, rep_penalty=theta)
+        B.mark_tokens(out_ids, bits, d.vocab, first=first, count=n_acc)
+        B.pbd_commit_refeed(out_ids, ids, Pd, cr, wl, block, mask, n_acc)
+        torch.cuda.synchronize()
+        got = out_ids.cpu().numpy()
+        ref = O.pbd_step(mn, c, win_o, P_o, causal_rows=c_o, window_len=w_o,
+                         rep_sets=[np.array(sorted(x)) for x in sets], rep_penalty=theta)
+        for b in np.flatnonzero(live):
+            w = int(w_o[b])
+            n, bad, excl = ids_match(got[b, :w], ref["ids"][b, :w], ref["gap"][b, :w])
+            compared += n
+            assert bad == 0, (s, b)
+            if not np.array_equal(got[b, :w], ref["ids"][b, :w]):
+                live[b] = False
+        for b in range(nb):
+            for i in range(int(acc[s][b])):
+                sets[b].add(int(ref["ids"][b, c_o[b] + i]))
+            for l, (kb, vb) in enumerate(ref["kv"]):
+                for j in range(int(w_o[b])):
+                    t = int(P_o[b]) + j
+                    blk = int(c["block_table"][b, t // c["block"]])
+                    c["k"][l, blk, :, t % c["block"], :] = kb[b * W + j].view(np.int16)
+                    c["v"][l, blk, :, :, t % c["block"]] = vb[b * W + j].view(np.int16)
+        win_o, P_o, c_o, w_o = O.refeed_commit(ref["ids"], win_o, P_o, c_o, w_o, block, mask, acc[s])
+        gw, gp, gc, gl = (t.cpu().numpy().astype(np.int64) for t in (ids, Pd, cr, wl))
+        for b in np.flatnonzero(live):
+            assert np.array_equal(gw[b], win_o[b]), (s, b)
+            assert (gp[b], gc[b], gl[b]) == (P_o[b], c_o[b], w_o[b]), (s, b)
+    _log(f"decode pipeline: prefill {L} rows, {steps} re-fed steps with the penalty; ids {compared} "
+         f"compared, {nb - live.sum()} sequences left at a near-tie")
+    assert compared >= 30
