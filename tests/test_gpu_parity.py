@@ -515,6 +515,22 @@ def test_step_refeed(fmt, B_, W):
     assert bad == 0
 
 
+def test_step_maximum_shape():
+    # the largest step the boundary takes: 64 sequences of 16 rows (1024 rows,
+    # 128 query columns per KV head), ragged prefixes, re-fed rows and padding
+    d = synth.ModelDims(n_layers=2, vocab=3001)
+    B_, W = 64, 16
+    g = torch.Generator().manual_seed(64)
+    P_list = [int(p) for p in torch.randint(0, 300, (B_,), generator=g)]
+    w = [int(x) for x in torch.randint(1, W + 1, (B_,), generator=g)]
+    c = [int(torch.randint(0, x + 1, (1,), generator=g)) for x in w]
+    got_ids, got_gap, hid, ref, err = _step_case(d, "bf16", P_list, W, seed=230, refeed=(c, w))
+    n, bad, excl = ids_match(got_ids, ref["ids"], ref["gap"])
+    e = rel_l2(hid, ref["hidden"])
+    _log(f"step B=64 W=16: hidden rel-L2 {e:.2e}; ids {n} compared, {bad} bad, {excl} excluded")
+    assert err == 0 and e <= TOL_BF16 and bad == 0
+
+
 @pytest.mark.parametrize("fmt,B_", [("bf16", 3), ("int4", 3), ("bf16", 32)])
 def test_step_repetition_penalty(fmt, B_):
     # each sequence's set holds its unpenalised winners and a random tenth of
@@ -539,6 +555,7 @@ def test_step_repetition_penalty(fmt, B_):
     ("bf16", [0, 37], 100, (1, 65)),     # 224 rows: the large-M GEMMs
     ("int4", [5, 0], 24, (0, 10)),
     ("bf16", [20], 9, (2, 4)),           # 16 rows: the small-M GEMMs
+    ("bf16", [0, 100], 320, (0, 256)),   # the bench's prompt: 256 spliced rows + 64 tokens, 20 windows
 ])
 def test_prefill_matches_oracle(fmt, P_list, L, spliced):
     """A causal pass over the prompt (rows spliced[0] .. spliced[1]-1 take
