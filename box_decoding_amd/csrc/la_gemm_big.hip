@@ -39,11 +39,12 @@ constexpr int kPfSink = 1024;  // LDS bytes the L2 prefetches land in (never rea
 // waves x 1 column wave of 3 tiles of 32 (items of 96 columns, so more
 // workgroups for a GEMM that cannot take K slices); 2: 4 x 2, eight waves
 // (two per SIMD, so one wave's other instructions run beside another's
-// products).
+// products); 3 (INT4): 4 x 2 with 3 tiles of 16 columns per column wave
+// (items of 96 columns: more workgroups for the gate/up projection).
 constexpr int lay_row_waves(int lay) { return lay == 0 ? 2 : 4; }
 constexpr int lay_col_waves(int lay) { return lay == 1 ? 1 : 2; }
 constexpr int lay_threads(int lay) { return lay_row_waves(lay) * lay_col_waves(lay) * 64; }
-constexpr int lay_waves_per_eu(int lay) { return lay == 2 ? 2 : 1; }
+constexpr int lay_waves_per_eu(int lay) { return lay >= 2 ? 2 : 1; }
 
 template <int RT, bool INT4, int LAY = 0>
 struct Wide {
@@ -53,7 +54,7 @@ struct Wide {
   static constexpr int RWV = lay_row_waves(LAY), CW = lay_col_waves(LAY), WAVES = RWV * CW;
   static constexpr int RTW = RWV * RT * (INT4 ? 1 : 2);  // packed 16-row tiles of a launch
   static constexpr int NP = INT4 ? RT : 2 * RT;       // epilogue parts of 8 real rows per row wave
-  static constexpr int CT = INT4 ? 4 : (LAY == 1 ? 3 : 2);
+  static constexpr int CT = INT4 ? (LAY == 3 ? 3 : 4) : (LAY == 1 ? 3 : 2);
   static constexpr int TPW = INT4 ? CT : 2 * CT;      // 16-column tiles per column wave
   static constexpr int ITEM = CW * TPW;               // 16-column tiles per work item
   static constexpr int SW = TPW * 16;                 // staged columns per wave
@@ -764,7 +765,9 @@ bool use_big_gemm(int M, int K, bool int4, int epi) {
 // INT4 runs eight waves (4 x 2): the dequantisation and per-group scaling of
 // one wave run beside the products of the other wave on its SIMD.
 static int big_lay(int rows, bool int4, int epi) {
-  if (int4) return 2;
+  // INT4 gate/up cannot take K slices: 96-column items (at 48 rows 30.7 us
+  // against 37.2 with 128-column items; the lm_head is faster with 128)
+  if (int4) return epi == EPI_SILU ? 3 : 2;
   // 65..96 rows fill three 2 x 2 row tiles exactly, where 4 x 1 would pad to 128
   const int mt = (rows + 7) / 8;
   return epi == EPI_ARGMAX || (mt > 8 && mt <= 12) ? 0 : 1;
@@ -781,7 +784,7 @@ static int big_rt(int rows, bool int4, int lay) {
 
 template <bool INT4, int LAY>
 static size_t big_smem(int rt, int epi) {
-  if (INT4) return wide_smem<2, true, 2>(epi);
+  if (INT4) return LAY == 3 ? wide_smem<2, true, 3>(epi) : wide_smem<2, true, 2>(epi);
   if (LAY == 0) return rt == 2 ? wide_smem<2, false, 0>(epi) : rt == 3 ? wide_smem<3, false, 0>(epi)
                                                                      : wide_smem<6, false, 0>(epi);
   return rt == 1 ? wide_smem<1, false, 1>(epi) : rt == 2 ? wide_smem<2, false, 1>(epi)
@@ -793,7 +796,8 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   p.lay = big_lay(rows, int4, epi);
   p.rt = big_rt(rows, int4, p.lay);
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
-  const int item = int4 ? Wide<2, true, 2>::ITEM : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
+  const int item = int4 ? (p.lay == 3 ? Wide<2, true, 3>::ITEM : Wide<2, true, 2>::ITEM)
+                        : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
   const int n_cb = (p.n_tiles + item - 1) / item;
   const int cus = big_cus();
   const int units = int4 ? K / 128 : K / 32;
@@ -827,7 +831,7 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   const int gt = (n_cb + per - 1) / per;
   p.grid = gt * p.ksplit;
   p.threads = lay_threads(p.lay);
-  p.smem = int4 ? big_smem<true, 2>(p.rt, epi)
+  p.smem = int4 ? (p.lay == 3 ? big_smem<true, 3>(p.rt, epi) : big_smem<true, 2>(p.rt, epi))
                 : (p.lay == 0 ? big_smem<false, 0>(p.rt, epi) : big_smem<false, 1>(p.rt, epi));
   return p;
 }
@@ -857,7 +861,7 @@ static hipError_t launch_big_epi(const GemmArgs& a, int epi, const BigPlan& p, h
 
 static hipError_t launch_big_plan(const GemmArgs& g, int epi, bool int4, const BigPlan& p,
                                   hipStream_t s) {
-  if (int4) return launch_big_epi<2, true, 2>(g, epi, p, s);
+  if (int4) return p.lay == 3 ? launch_big_epi<2, true, 3>(g, epi, p, s) : launch_big_epi<2, true, 2>(g, epi, p, s);
   if (p.lay == 0) {
     if (p.rt == 2) return launch_big_epi<2, false, 0>(g, epi, p, s);
     if (p.rt == 3) return launch_big_epi<3, false, 0>(g, epi, p, s);
