@@ -162,7 +162,12 @@ enum {
 la_status la_int4_embed_gather(const int32_t* ids, int32_t T, const la_weight* emb, float* out,
                                int32_t* err, hipStream_t stream);
 
-/* Weight-streaming GEMM for small M (M = 6 x batch rows):
+/* Weight-streaming GEMM for small M (M = 6 x batch rows): one linear layer of
+ * the decoder, y = x' . W^T, as the standard Qwen2 layers apply them ("LocateAnything-3B
+ * on Jetson Orin Nano", Part 1 section 1.2: the language model is a plain Qwen2
+ * causal LM; its projections are the QKV, O, gate/up and down linears, with
+ * group-wise INT4 weights as in "LocateAnything-3B — ONNX WebGPU (INT4 + 4-bit
+ * embeddings)", section "Files", block 128):
  *   x' = RMSNorm(x; norm_gain, rms_eps) if norm_gain != NULL, else x;
  *   LA_EPI_NONE:      y = x' . W^T + bias + residual  (bias bf16 [n] / residual fp32 [M][n], each nullable)
  *   LA_EPI_SILU_GATE: y = SiLU(x' . Wg^T) * (x' . Wu^T), Wg / Wu the two halves of W's rows.
@@ -190,7 +195,11 @@ la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, con
                           const float* residual, int32_t epilogue, float* y, hipStream_t stream);
 
 /* Block-masked GQA attention of the window rows over the paged cache of one
- * layer.  q fp32 [B][W][n_heads][head_dim] (RoPE already applied); the keys of
+ * layer: the window rows attend to the whole cached prefix and to every row of
+ * the window ("LocateAnything-3B on Jetson Orin Nano", Part 1 section 1.3: a
+ * block mask instead of a strictly causal one; "LocateAnything-3B for RK3588
+ * (RKLLM + RKNN)", "How it differs from the original", item 1: the prefix KV is
+ * reused and the window sits at the original positions after it).  q fp32 [B][W][n_heads][head_dim] (RoPE already applied); the keys of
  * sequence b are cache slots 0 .. P_b+W-1 (the window's own K/V must already be
  * stored at P_b .. P_b+W-1): every window row sees all of them (prefix causal,
  * window bidirectional).  out fp32 [B][W][n_heads][head_dim] =
@@ -198,6 +207,9 @@ la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, con
  * n_kv_heads).  prefix_len int32 [B] (device); max_len (host) is an upper bound
  * of every P_b + W and sizes the split-K grid; keys beyond the cache capacity
  * are ignored. */
+/* Workspace of la_pbd_attention (and its masked / re-fed forms): the split-K
+ * partial results (per run: running max, sum and unnormalised output) that the
+ * log-sum-exp merge combines; 0 for an unsupported shape. */
 size_t la_pbd_attention_workspace(int32_t B, int32_t W, int32_t n_heads, int32_t n_kv_heads,
                                   int32_t head_dim, int32_t max_len);
 /* The same with the window mask chosen: LA_MASK_BIDIRECTIONAL (as
@@ -265,7 +277,12 @@ la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, 
                        float* attn_out, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
-/* The whole PBD window step: embedding gather of window_ids int32 [B][W]; all
+/* The whole PBD window step ("LocateAnything-3B for RK3588 (RKLLM + RKNN)", "How
+ * it differs from the original", item 1: each step sends the last accepted token
+ * and the mask tokens over the reused prefix, at their original positions, and
+ * reads one prediction per window position; "LocateAnything-3B on Jetson Orin
+ * Nano", Part 1 sections 1.2-1.4: a Qwen2 decoder, the block mask, greedy
+ * selection): embedding gather of window_ids int32 [B][W]; all
  * layers (writing each window's K/V into the cache at slots P_b .. P_b+W-1);
  * final RMSNorm; tied lm_head argmax.  out_ids int32 [B][W]; out_gap (nullable)
  * fp32 [B][W] top-2 logit gaps; out_hidden (nullable) fp32 [B*W][hidden] final
@@ -273,6 +290,10 @@ la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, 
  * commits accepted tokens by advancing it (nothing to roll back otherwise; the
  * next step overwrites the slots).  Rows of a sequence with a data error get
  * out_ids = -1 and set bits in *err (nullable; OR-ed, never cleared). */
+/* Workspace of la_pbd_step (and la_pbd_step_refeed / la_pbd_step_opts / la_pbd_layer)
+ * for B sequences of W window rows and keys up to max_len: the residual stream,
+ * packed operands, attention partials and lm_head partials of the step above;
+ * 0 for an invalid model or shape. */
 size_t la_pbd_step_workspace(const la_model* m, int32_t B, int32_t W, int32_t max_len);
 la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
@@ -349,12 +370,16 @@ la_status la_pbd_step_refeed(const la_model* m, const la_kv_cache* kv, const int
                              int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                              size_t workspace_bytes, int32_t* err, hipStream_t stream);
 
-/* Commit a fully accepted window and form the next one, for a loop of window
- * steps (the cached prefix grows by the accepted tokens and is reused, with
- * no explicit rollback: RK3588 page, "How it differs from the original", item
- * 1): prefix_len[b] += W, and window_ids[b] becomes [out_ids[b][W-1], mask_id
- * x (W-1)].  The window's K/V are already in the cache: la_pbd_step wrote them
- * at slots P_b .. P_b+W-1.  out_ids and window_ids int32 [B][W] (distinct
+/* Commit a fully accepted window and form the next one without re-feeding:
+ * prefix_len[b] += W, and window_ids[b] becomes [out_ids[b][W-1], mask_id
+ * x (W-1)].  The K/V that stay in the cache at slots P_b .. P_b+W-1 are the
+ * ones la_pbd_step wrote: those of the window's own inputs.  With W = 1 (plain
+ * token-by-token decoding, the slow mode) that input is the accepted token, so
+ * the cache is exact.  With W > 1 slots P_b+1 .. P_b+W-1 keep the mask tokens'
+ * K/V instead of the accepted tokens': a cheaper approximation of the method
+ * that serves as a throughput proxy.  The method's loop re-feeds the accepted
+ * tokens so that their K/V enter the cache: la_pbd_step_refeed with
+ * la_pbd_commit_refeed below.  out_ids and window_ids int32 [B][W] (distinct
  * buffers), prefix_len int32 [B], all device memory owned by the caller.  Only
  * enqueues on the stream (graph-capturable).  Returns LA_ERR_ARG for NULL
  * pointers or aliased ids, LA_ERR_SHAPE outside 1 <= B <= 64, 1 <= W <= 16 (the

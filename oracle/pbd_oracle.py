@@ -47,8 +47,8 @@ import numpy as np
 __all__ = [
     "bf16_to_float", "fp16_to_float", "round_to_bf16_bits", "int4_dequant", "decode_weight",
     "embed_rows", "rmsnorm", "silu", "rope_angles", "rope_apply", "window_attention",
-    "repetition_penalty",
-    "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "pbd_emission_loop",
+    "repetition_penalty", "logits_of",
+    "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "emission_commit", "pbd_emission_loop",
     "refeed_commit", "pbd_refeed_loop", "pbd_prefill",
 ]
 
@@ -87,20 +87,15 @@ def round_to_bf16_bits(x):
 def int4_dequant(packed, scales, group, dtype=np.float64):
     """Group-wise symmetric INT4 -> float.
 
-    packed: uint8 [..., k/2]; element 2i is the low nibble of byte i, element
-    2i+1 its high nibble.  scales: fp16 bits [..., k/group].  Element j decodes
-    to (q_j - 8) * scale[j // group] (WebGPU page, embedding gather/dequant).
+    packed: uint8 [..., k/2]; scales: fp16 bits [..., k/group].  Element j of a
+    row has the 4-bit code q_j = (byte[j // 2] >> (4 * (j % 2))) & 0xF (the even
+    element in the low nibble) and decodes to (q_j - 8) * scale[j // group]
+    (WebGPU page, section "Embedding gather / dequant (JS reference)").
     """
     packed = np.asarray(packed).view(np.uint8)
-    low = (packed & 0x0F).astype(np.int64)
-    high = (packed >> 4).astype(np.int64)
-    k = 2 * packed.shape[-1]
-    q = np.empty(packed.shape[:-1] + (k,), dtype=np.int64)
-    q[..., 0::2] = low
-    q[..., 1::2] = high
-    s = fp16_to_float(scales, dtype)
-    j = np.arange(k)
-    return (q - 8).astype(dtype) * s[..., j // group]
+    j = np.arange(2 * packed.shape[-1])
+    q = (packed[..., j // 2].astype(np.int64) >> (4 * (j % 2))) & 0xF
+    return (q - 8).astype(dtype) * fp16_to_float(scales, dtype)[..., j // group]
 
 
 def decode_weight(w, rows=None, dtype=np.float64):
@@ -297,6 +292,21 @@ def repetition_penalty(z, theta):
     return np.where(z > 0, z / theta, z * theta)
 
 
+def logits_of(f, lm, ids, dtype=np.float64, rep_sets=None, rep_penalty=1.0):
+    """The logit f[t] . E[ids[t]] of one given vocabulary id per row (after the
+    repetition penalty when rep_sets holds the id), for rows whose ranking is
+    checked for validity rather than exactly."""
+    f = np.asarray(f, dtype=dtype)
+    ids = np.asarray(ids).reshape(-1).astype(np.int64)
+    E = decode_weight(lm, rows=ids, dtype=dtype)          # [T, H]
+    z = np.einsum("th,th->t", f, E)
+    if rep_sets is not None:
+        for t in range(len(ids)):
+            if np.isin(ids[t], np.asarray(rep_sets[t])):
+                z[t] = repetition_penalty(z[t], rep_penalty)
+    return z
+
+
 def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64, rep_sets=None, rep_penalty=1.0):
     """Per-row argmax of f . E^T over the vocabulary, with top-1 and top-2 gap.
 
@@ -370,11 +380,21 @@ def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidd
     row_sets = None if rep_sets is None else [rep_sets[t // W] for t in range(B * W)]
     out_ids, top1, gap = lm_head_argmax(f, lm, dtype=dtype, rep_sets=row_sets, rep_penalty=rep_penalty)
     res = {"ids": out_ids.reshape(B, W), "top1": top1.reshape(B, W), "gap": gap.reshape(B, W),
-           "kv": kv}
+           "kv": kv, "final": f}
     if return_hidden:
         res["hidden"] = h
-        res["final"] = f
     return res
+
+
+def emission_commit(out_ids, prefix_len, mask_id):
+    """The next window after a step whose window is accepted as it stands (no
+    re-feeding): the prefix grows by W and the next window is [the last
+    row's output, mask x (W-1)].  Returns (ids', P')."""
+    out = np.asarray(out_ids)
+    B, W = out.shape
+    ids = np.full((B, W), mask_id, dtype=np.int32)
+    ids[:, 0] = out[:, W - 1]
+    return ids, np.asarray(prefix_len, dtype=np.int64) + W
 
 
 def pbd_emission_loop(model, cache, window_ids, prefix_len, steps, mask_id, dtype=np.float64):
@@ -400,9 +420,7 @@ def pbd_emission_loop(model, cache, window_ids, prefix_len, steps, mask_id, dtyp
                     blk = int(c["block_table"][b, t // bs])
                     c["k"][l, blk, :, t % bs, :] = kb[b * W + j].view(np.int16)
                     c["v"][l, blk, :, :, t % bs] = vb[b * W + j].view(np.int16)
-        P = P + W
-        ids = np.full((B, W), mask_id, dtype=np.int32)
-        ids[:, 0] = r["ids"][:, W - 1]
+        ids, P = emission_commit(r["ids"], P, mask_id)
     return outs, P, c
 
 
@@ -487,14 +505,14 @@ def pbd_prefill(model, cache, ids, prefix_len, input_embeds=None, dtype=np.float
     The prefill is the fixed cost before decoding in the Jetson page's latency
     breakdown (section 3.1).  Every row attends causally (a plain causal LM pass over
     the prompt: the re-fed window with every row causal).  Returns the argmax
-    id, top-2 gap and final hidden state of each sequence's last row, and the
-    bf16 K/V of every row (as pbd_step).
+    id, top-2 gap, top-1 logit, final hidden state and final-normed row of
+    each sequence's last row, and the bf16 K/V of every row (as pbd_step).
     """
     ids = np.asarray(ids)
     B, L = ids.shape
     r = pbd_step(model, cache, ids, prefix_len, dtype, return_hidden=True, causal=True,
                  input_embeds=input_embeds)
     last = np.arange(B) * L + (L - 1)
-    return {"ids": r["ids"][:, L - 1], "gap": r["gap"][:, L - 1], "hidden": r["hidden"][last],
-            "kv": r["kv"]}
+    return {"ids": r["ids"][:, L - 1], "gap": r["gap"][:, L - 1], "top1": r["top1"][:, L - 1],
+            "hidden": r["hidden"][last], "final": r["final"][last], "kv": r["kv"]}
 
