@@ -145,3 +145,10 @@ def bf16_bits_rel_l2(got_bits, ref_bits):
     def dec(x):
         return (np.asarray(x).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return rel_l2(dec(got_bits), dec(ref_bits))
+
+
+def bf16_kv_row_rel_l2(got_bits, ref_bits, row_width):
+    """Largest per-row rel-L2 between two bf16 K/V bit arrays, as decoded values."""
+    def dec(x):
+        return (np.asarray(x).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return rel_l2_rows(dec(got_bits), dec(ref_bits), row_width)

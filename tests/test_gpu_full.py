@@ -8,8 +8,14 @@ exact ties in the lm_head.
   oracle checks a subset of a batch it is the same computation as for all.
 * Loops are teacher-forced: before every step the oracle takes the cache, the
   window and the prefix lengths the GPU holds, so each step is compared on
-  its own (ids, the K/V it writes within one bf16 ulp, the state after the
-  device-side commit exactly) with no drift carried from earlier steps.
+  its own (ids, the K/V it writes, the state after the device-side commit
+  exactly) with no drift carried from earlier steps.
+* K/V written to the bf16 cache: the rounding is taken on fp32 values that
+  carry the rounding of every layer before.  Where that error is far below
+  half a bf16 ulp (layer 0, and every layer of the 2-layer models) the bar is
+  one ulp of the oracle's rounding (entries within 1e-4 of the rms of the
+  tensor excepted); in every layer each row (one token's K or V of one head)
+  is held to the rel-L2 bar.
 * Exact ties: copies of a row's winning lm_head row planted at lower and
   higher vocabulary ids, in the same tile and in other workgroups' ranges;
   the lowest index must win.
@@ -21,8 +27,8 @@ import torch
 import oracle as O
 from box_decoding_amd import binding as B
 from box_decoding_amd import synth
-from helpers import (bf16_kv_mismatch, cache_slots, ids_match, max_abs, np_tree, oracle_lm,
-                     rel_l2, rel_l2_rows, step_ids_match)
+from helpers import (bf16_kv_mismatch, bf16_kv_row_rel_l2, cache_slots, ids_match, max_abs, np_tree,
+                     oracle_lm, rel_l2, rel_l2_rows, step_ids_match)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,25 +102,30 @@ def _full_step(wname, seqs=None, tol=TOL_BF16):
     n, bad, near = step_ids_match(got_ids, ref)
     h = hid.cpu().numpy()[rows]
     e, er = rel_l2(h, ref["hidden"]), rel_l2_rows(h, ref["hidden"], d.hidden)
-    # the window's K/V of the first and last layer, every checked sequence
+    # the window's K/V: layer 0 within one ulp, every layer per row
     cg = cn  # the step wrote slots P_b .. P_b+W-1; the oracle read only the slots before
     kd = vd = 0
-    for layer in (0, d.n_layers - 1):
+    kr = 0.0
+    for layer in range(d.n_layers):
         kb, vb = ref["kv"][layer]
         for i, b in enumerate(seqs):
             pos = np.arange(int(P[b]), int(P[b]) + W)
             kg, vg = cache_slots(cg, layer, i, pos)
-            kd = max(kd, bf16_kv_mismatch(kg, kb[i * W:(i + 1) * W]))
-            vd = max(vd, bf16_kv_mismatch(vg, vb[i * W:(i + 1) * W]))
+            if layer == 0:
+                kd = max(kd, bf16_kv_mismatch(kg, kb[i * W:(i + 1) * W]))
+                vd = max(vd, bf16_kv_mismatch(vg, vb[i * W:(i + 1) * W]))
+            kr = max(kr, bf16_kv_row_rel_l2(kg, kb[i * W:(i + 1) * W], d.head_dim),
+                     bf16_kv_row_rel_l2(vg, vb[i * W:(i + 1) * W], d.head_dim))
     gd = max_abs(gap.cpu().numpy().reshape(-1)[rows][ref["gap"].reshape(-1) >= 1e-3],
                  ref["gap"].reshape(-1)[ref["gap"].reshape(-1) >= 1e-3])
     _log(f"full step {wname} ({len(seqs)} of {w.batch} sequences checked): hidden rel-L2 {e:.2e} "
-         f"(worst row {er:.2e}); ids {n} compared, {bad} bad, {near} near-ties; K/V ulp {kd}/{vd}; "
+         f"(worst row {er:.2e}); ids {n} compared, {bad} bad, {near} near-ties; layer-0 K/V ulp {kd}/{vd}, "
+         f"worst K/V row rel-L2 {kr:.1e}; "
          f"max |gap diff| {gd:.1e}")
     assert int(err.item()) == 0
     assert bad == 0
     assert e <= tol and er <= tol
-    assert kd <= 1 and vd <= 1
+    assert kd <= 1 and vd <= 1 and kr <= tol
     assert gd < 1e-3
 
 
@@ -145,14 +156,17 @@ def test_full_step_probe_b1_p32768():
 # ---------------------------------------------------------------- loops, teacher-forced
 
 def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, acc, graph, max_len,
-                         seqs, refeed, tol_kv=1):
+                         seqs, refeed, ulp_layers=None, tol=TOL_BF16):
     """Run ``steps`` steps (each a step and its device-side commit) and check
     every one against the oracle run on the state the GPU holds before it.
 
     refeed=False: la_pbd_step + la_pbd_commit (window [last id, mask x (W-1)],
     prefix += W); refeed=True: la_pbd_step_refeed + la_pbd_commit_refeed with
     n_accept = acc[s] (None: the whole block).  seqs: the sequences the oracle
-    recomputes (the commit is checked on all).  Returns the counts."""
+    recomputes (the commit is checked on all).  ulp_layers: the layers whose
+    K/V are held to one ulp (default all); every layer's rows to the rel-L2
+    bar.  Returns the counts."""
+    ulp_layers = range(d.n_layers) if ulp_layers is None else ulp_layers
     nb, W = ids.shape
     out_ids = torch.empty((nb, W), dtype=torch.int32, device=DEV)
     out_gap = torch.empty((nb, W), dtype=torch.float32, device=DEV)
@@ -162,7 +176,7 @@ def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, 
     if graph:
         g = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, commit_mask_id=mask,
                         refeed=(cr, wl, block, n_acc if acc is not None else None) if refeed else None)
-    tot = dict(ids=0, near=0, kd=0, vd=0)
+    tot = dict(ids=0, near=0, kd=0, vd=0, kv_row=0.0)
     for s in range(steps):
         win = ids.cpu().numpy()
         P = Pd.cpu().numpy().astype(np.int64)
@@ -198,8 +212,12 @@ def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, 
             for i, b in enumerate(seqs):
                 pos = np.arange(int(P[b]), int(P[b]) + int(w[b]))
                 kg, vg = cache_slots(after, layer, i, pos)
-                tot["kd"] = max(tot["kd"], bf16_kv_mismatch(kg, kb[i * W:i * W + int(w[b])]))
-                tot["vd"] = max(tot["vd"], bf16_kv_mismatch(vg, vb[i * W:i * W + int(w[b])]))
+                kr, vr = kb[i * W:i * W + int(w[b])], vb[i * W:i * W + int(w[b])]
+                if layer in ulp_layers:
+                    tot["kd"] = max(tot["kd"], bf16_kv_mismatch(kg, kr))
+                    tot["vd"] = max(tot["vd"], bf16_kv_mismatch(vg, vr))
+                tot["kv_row"] = max(tot["kv_row"], bf16_kv_row_rel_l2(kg, kr, d.head_dim),
+                                    bf16_kv_row_rel_l2(vg, vr, d.head_dim))
         # the device-side commit, from the GPU's own ids, exactly
         gw, gp = ids.cpu().numpy(), Pd.cpu().numpy().astype(np.int64)
         if refeed:
@@ -210,7 +228,7 @@ def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, 
         else:
             ew, ep = O.emission_commit(got, P, mask)
             assert np.array_equal(gw, ew) and np.array_equal(gp, ep), s
-    assert tot["kd"] <= tol_kv and tot["vd"] <= tol_kv, tot
+    assert tot["kd"] <= 1 and tot["vd"] <= 1 and tot["kv_row"] <= tol, tot
     return tot
 
 
@@ -279,7 +297,7 @@ def test_full_refeed_loop_b16_p2048():
     wl = torch.full((w.batch,), block, dtype=torch.int32, device=DEV)
     Pd = P.to(DEV)
     tot = _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, None, True,
-                               int(P.max()) + W + steps * block, [0, 5, 10, 15], True)
+                               int(P.max()) + W + steps * block, [0, 5, 10, 15], True, ulp_layers=(0,))
     _log(f"full re-fed loop b16 p2048, teacher-forced: {tot}")
     assert np.array_equal(Pd.cpu().numpy(), P.numpy() + 1 + (steps - 1) * block)
 

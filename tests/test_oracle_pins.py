@@ -14,6 +14,7 @@ import torch
 from scipy.special import expit
 
 import oracle as O
+import oracle.sampling as OS
 from box_decoding_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -770,3 +771,95 @@ def test_prefill_spliced_rows_equal_their_embedding_rows():
     other = O.pbd_prefill(model, cache, spliced, Ps, input_embeds=emb)
     assert np.abs(other["hidden"][0] - ref["hidden"][0]).max() > 1e-6
     np.testing.assert_array_equal(other["hidden"][1], ref["hidden"][1])
+
+
+# ---------------------------------------------------------------- sampling (temperature, top-p)
+
+def test_philox_known_answer_vectors():
+    # Philox4x32-10 known-answer vectors of the Random123 distribution
+    # (counter, key) -> output
+    kat = [
+        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
+        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
+        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
+         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
+    ]
+    for ctr, key, want in kat:
+        assert OS.philox4x32_10(ctr, key) == want
+    u = OS.philox_uniform(0, 0, 0)
+    assert u == (0x6627E8D5 >> 8) / 2 ** 24 and 0.0 <= u < 1.0
+
+
+def test_nucleus_hand_worked():
+    # probabilities 0.1, 0.5, 0.05, 0.15, 0.2 (T = 1): top_p 0.8 keeps the three
+    # largest, ids 1 (0.5), 4 (0.2), 3 (0.15): 0.5 + 0.2 = 0.7 < 0.8 <= 0.85
+    p = np.array([0.1, 0.5, 0.05, 0.15, 0.2])
+    z = np.log(p)
+    kept, pk, total = OS.nucleus(z, 1.0, 0.8)
+    assert kept.tolist() == [1, 3, 4]
+    np.testing.assert_allclose(pk / total, [0.5, 0.15, 0.2], rtol=1e-12)
+    # the draw walks the kept ids in ascending id order (not probability
+    # order): cumulative 0.5, 0.65, 0.85 of the kept mass 0.85, i.e. u
+    # boundaries at 0.588 and 0.765
+    for u, want in ((0.0, 1), (0.58, 1), (0.59, 3), (0.76, 3), (0.77, 4), (0.999, 4)):
+        assert OS.sample_row(z, 1.0, 0.8, u) == want, u
+    # just below and just above the mass of the first two (0.7)
+    assert OS.nucleus(z, 1.0, 0.69)[0].tolist() == [1, 4]
+    assert OS.nucleus(z, 1.0, 0.71)[0].tolist() == [1, 3, 4]
+    # temperature sharpens: T = 0.5 squares the ratios, 0.25 : 0.04 : 0.0225 :
+    # 0.01 : 0.0025, i.e. 0.769, 0.123, 0.069, ... of the total: the first two
+    # hold 0.892
+    assert OS.nucleus(z, 0.5, 0.88)[0].tolist() == [1, 4]
+    assert OS.nucleus(z, 0.5, 0.9)[0].tolist() == [1, 3, 4]
+
+
+def test_nucleus_ties_take_lower_ids_first():
+    z = np.array([0.0, 2.0, 1.0, 2.0, 2.0])
+    # three ids tie at the top; top_p small keeps only the lowest of them
+    assert OS.nucleus(z, 1.0, 1e-6)[0].tolist() == [1]
+    # two thirds of the tied mass needs two of them: ids 1 and 3
+    kept, pk, total = OS.nucleus(z, 1.0, 0.5)
+    assert kept.tolist() == [1, 3]
+
+
+def test_sampling_limits():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal(1000)
+    top = int(np.argmax(z))
+    # T <= 0 and T -> 0 select the argmax
+    assert OS.sample_row(z, 0.0, 0.9, 0.7) == top
+    assert OS.sample_row(z, 1e-4, 0.9, 0.7) == top
+    # top_p -> 0 keeps the argmax only
+    assert OS.sample_row(z, 1.0, 1e-9, 0.99) == top
+    # top_p = 1 keeps everything: the draw is the plain inverse CDF in id order
+    kept, pk, total = OS.nucleus(z, 0.7, 1.0)
+    assert kept.size == z.size
+    p = np.exp((z - z.max()) / 0.7)
+    cdf = np.cumsum(p) / p.sum()
+    for u in (0.0, 0.3, 0.77, 0.999999):
+        assert OS.sample_row(z, 0.7, 1.0, u) == int(np.searchsorted(cdf, u, side="right"))
+
+
+def test_sampling_frequencies_match_the_nucleus():
+    # many draws (Philox over rows) against the renormalised nucleus: chi-square
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal(12) * 1.5
+    T, top_p = 0.7, 0.9
+    kept, pk, total = OS.nucleus(z, T, top_p)
+    n = 20000
+    counts = np.zeros(z.size)
+    for t in range(n):
+        counts[OS.sample_row(z, T, top_p, OS.philox_uniform(t, 1234, 99))] += 1
+    assert counts[np.setdiff1d(np.arange(z.size), kept)].sum() == 0
+    expect = n * pk / pk.sum()
+    chi2 = float(((counts[kept] - expect) ** 2 / expect).sum())
+    # 99.9th percentile of chi-square with up to 11 degrees of freedom is < 32
+    assert chi2 < 32.0, (chi2, kept.size)
+
+
+def test_sample_rows_uses_the_row_counter():
+    z = np.zeros((4, 50))
+    # uniform logits: the id is floor(u * 50) for each row's own draw
+    ids = OS.sample_rows(z, 1.0, 1.0, seed=7, offset=5)
+    want = [int(OS.philox_uniform(t, 7, 5) * 50) for t in range(4)]
+    assert ids.tolist() == want
