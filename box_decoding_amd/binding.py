@@ -30,7 +30,7 @@ EXPORTED = [
     "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
     "la_pbd_attention_masked", "la_pbd_attention_refeed", "la_pbd_step_refeed",
     "la_pbd_commit_refeed", "la_pbd_step_opts", "la_lm_head_argmax_penalized", "la_pbd_mark_tokens",
-    "la_pbd_prefill_workspace", "la_pbd_prefill",
+    "la_pbd_prefill_workspace", "la_pbd_prefill", "la_pbd_step_noalloc",
 ]
 
 
@@ -136,6 +136,9 @@ def load() -> ctypes.CDLL:
                                                   c_void_p, c_void_p, c_size_t, c_void_p]),
         "la_pbd_mark_tokens": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                          c_int32, c_int32, c_void_p]),
+        "la_pbd_step_noalloc": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
+                                          c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p]),
         "la_pbd_prefill_workspace": (c_size_t, [POINTER(LaModel), c_int32, c_int32, c_int32]),
         "la_pbd_prefill": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
                                      c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
@@ -460,6 +463,21 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
                                _ptr(gap), _ptr(hid), _ptr(buf), buf.numel(), _ptr(err), _stream()),
                "la_pbd_step")
     return ids, gap, hid
+
+
+def pbd_step_noalloc(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
+                     prefix_len: torch.Tensor, max_len: int, out_ids: torch.Tensor,
+                     out_gap: Optional[torch.Tensor] = None, out_hidden: Optional[torch.Tensor] = None,
+                     err: Optional[torch.Tensor] = None):
+    """la_pbd_step_noalloc: the step on the library's own per-GPU scratch array
+    (no workspace argument); outputs go to the caller's tensors."""
+    lib = load()
+    _require_cuda(window_ids, prefix_len, out_ids, out_gap, out_hidden, err)
+    B, W = window_ids.shape
+    _check(lib.la_pbd_step_noalloc(ctypes.byref(model.struct), ctypes.byref(cache.struct),
+                                   _ptr(window_ids), _ptr(prefix_len), B, W, max_len, _ptr(out_ids),
+                                   _ptr(out_gap), _ptr(out_hidden), _ptr(err), _stream()),
+           "la_pbd_step_noalloc")
 
 
 def pbd_commit(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_len: torch.Tensor,

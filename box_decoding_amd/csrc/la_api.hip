@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "la_internal.hpp"
 
@@ -1043,3 +1044,56 @@ la_status la_pbd_commit_refeed(const int32_t* out_ids, const int32_t* n_accept, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free step
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid it): the step's scratch lives in
+// a fixed array of this library, one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol); it resolves the array's device address
+// once per device with hipGetSymbolAddress and uses that address.
+
+namespace {
+
+constexpr size_t kStepScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kStepScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (resolved on the first call on that
+// device, with that device current).
+la_status step_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" la_status la_pbd_step_noalloc(const la_model* m, const la_kv_cache* kv,
+                                         const int32_t* window_ids, const int32_t* prefix_len,
+                                         int32_t B, int32_t W, int32_t max_len, int32_t* out_ids,
+                                         float* out_gap, float* out_hidden, int32_t* err,
+                                         hipStream_t stream) {
+  la_status st = check_model(m);
+  if (st != LA_OK) return st;
+  if ((st = check_step_shape(m, B, W, max_len)) != LA_OK) return st;
+  const size_t need = carve_step(m, B, W, max_len, nullptr, true).bytes;
+  if (need > kStepScratchBytes) return LA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = step_scratch(&ws)) != LA_OK) return st;
+  return la_pbd_step(m, kv, window_ids, prefix_len, B, W, max_len, out_ids, out_gap, out_hidden, ws,
+                     kStepScratchBytes, err, stream);
+}

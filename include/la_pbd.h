@@ -299,6 +299,24 @@ la_status la_pbd_step(const la_model* m, const la_kv_cache* kv, const int32_t* w
                       const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
                       int32_t* out_ids, float* out_gap, float* out_hidden, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream);
+/* la_pbd_step without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The step's scratch is a fixed array inside this
+ * library: 64 MiB on each GPU the library runs on, held until the process
+ * ends (its device address is resolved once per device, on the first call
+ * made with that device current; the calling thread's current device must be
+ * the stream's).  The call allocates and frees nothing.  Shapes whose
+ * la_pbd_step_workspace() exceeds 64 MiB return LA_ERR_WORKSPACE (e.g. batch 1
+ * up to a 32K-token context, or 16 sequences of 11 rows up to max_len 4102,
+ * fit).  Every call on one GPU uses the same array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that may overlap on one
+ * GPU (two streams, two threads) race and must be serialised by the caller.
+ * Otherwise exactly la_pbd_step: the same arguments, results and errors. */
+la_status la_pbd_step_noalloc(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
+                              const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len,
+                              int32_t* out_ids, float* out_gap, float* out_hidden, int32_t* err,
+                              hipStream_t stream);
+
 /* Options of la_pbd_step_opts (zero-initialise, then set what is used):
  *  - causal_rows, window_len: int32 [B] device arrays of a re-fed window
  *    (la_pbd_step_refeed), or NULL;
