@@ -218,14 +218,18 @@ def window_attention(q, k, v, dtype=np.float64, causal=False, causal_rows=0, win
 # ---------------------------------------------------------------------------
 
 def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float64, parts=None,
-                  causal=False, causal_rows=None, window_len=None):
+                  causal=False, causal_rows=None, window_len=None, window_kv=None):
     """One decoder layer on the window rows of every sequence.
 
     h: [B*W, H] hidden states (row b*W + j is window position j of sequence b).
     causal_rows / window_len: per-sequence [B] re-fed rows and window lengths
     of a re-fed window (window_attention), None for the plain window.
+    window_kv: None, or (k_bits, v_bits) [B*W, Hkv, D] bf16 bit patterns that
+    the attention reads for the window rows in place of this layer's own
+    rounding of k and v (to follow another implementation's rounding
+    decisions; the window's K/V are then inputs, as the prefix's are).
     Returns (h_out, k_bits, v_bits) where k_bits/v_bits [B*W, Hkv, D] are the
-    bf16 K/V the step stores at slots P_b + j.  ``parts`` (a dict) receives
+    bf16 K/V this layer computes for slots P_b + j (its own rounding).  ``parts`` (a dict) receives
     intermediate values when given.
     """
     H = _dim(dims, "hidden")
@@ -255,8 +259,8 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
     k = rope_apply(k, ang)
     k_bits = round_to_bf16_bits(k)
     v_bits = round_to_bf16_bits(v)
-    kw = bf16_to_float(k_bits, dtype)
-    vw = bf16_to_float(v_bits, dtype)
+    kw = bf16_to_float(k_bits if window_kv is None else window_kv[0], dtype)
+    vw = bf16_to_float(v_bits if window_kv is None else window_kv[1], dtype)
 
     o = np.zeros((T, Hq, D), dtype=dtype)
     for b in range(B):
@@ -349,7 +353,7 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64, rep_sets=None, rep_penal
 
 def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidden=False,
              layers=None, causal=False, causal_rows=None, window_len=None, rep_sets=None,
-             rep_penalty=1.0, input_embeds=None):
+             rep_penalty=1.0, input_embeds=None, window_kv=None):
     """One PBD window step for every sequence.
 
     window_ids [B, W] -> per-position argmax ids [B, W] and top-2 gaps [B, W].
@@ -358,8 +362,11 @@ def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidd
     row of the sequence ranks its logits with those penalised
     (repetition_penalty, rep_penalty).  input_embeds [B, W, H] (or None):
     rows whose id is negative take this row instead of an embedding row.
+    window_kv: None, or per layer the (k_bits, v_bits) the attention reads for
+    the window rows (decoder_layer).
     The step writes nothing into ``cache``; it returns the bf16 K/V it would
-    store at slots P_b .. P_b+W-1 of each layer.
+    store at slots P_b .. P_b+W-1 of each layer ("kv") and their values
+    before the rounding ("kv_exact").
     """
     dims = model["dims"]
     ids = np.asarray(window_ids)
@@ -369,18 +376,22 @@ def pbd_step(model, cache, window_ids, prefix_len, dtype=np.float64, return_hidd
     if input_embeds is not None:
         emb_in = np.asarray(input_embeds, dtype=dtype).reshape(B * W, -1)
         h[flat < 0] = emb_in[flat < 0]
-    kv = []
+    kv, kv_exact = [], []
     n_layers = len(model["layers"]) if layers is None else layers
     for l in range(n_layers):
+        parts = {}
         h, kb, vb = decoder_layer(h, model["layers"][l], dims, cache, l, prefix_len, W, dtype,
-                                  causal=causal, causal_rows=causal_rows, window_len=window_len)
+                                  parts=parts, causal=causal, causal_rows=causal_rows,
+                                  window_len=window_len,
+                                  window_kv=None if window_kv is None else window_kv[l])
         kv.append((kb, vb))
+        kv_exact.append((parts["k"], parts["v"]))
     f = rmsnorm(h, bf16_to_float(model["final_norm"], dtype), float(_dim(dims, "rms_eps")))
     lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
     row_sets = None if rep_sets is None else [rep_sets[t // W] for t in range(B * W)]
     out_ids, top1, gap = lm_head_argmax(f, lm, dtype=dtype, rep_sets=row_sets, rep_penalty=rep_penalty)
     res = {"ids": out_ids.reshape(B, W), "top1": top1.reshape(B, W), "gap": gap.reshape(B, W),
-           "kv": kv, "final": f}
+           "kv": kv, "kv_exact": kv_exact, "final": f}
     if return_hidden:
         res["hidden"] = h
     return res

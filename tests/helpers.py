@@ -147,8 +147,12 @@ def bf16_bits_rel_l2(got_bits, ref_bits):
     return rel_l2(dec(got_bits), dec(ref_bits))
 
 
-def bf16_kv_row_rel_l2(got_bits, ref_bits, row_width):
-    """Largest per-row rel-L2 between two bf16 K/V bit arrays, as decoded values."""
-    def dec(x):
-        return (np.asarray(x).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return rel_l2_rows(dec(got_bits), dec(ref_bits), row_width)
+def kv_rows_vs_exact(got_bits, exact, row_width):
+    """Largest per-row rel-L2 of the bf16 K/V the GPU stored against the
+    oracle's values before rounding.  A bf16 store alone moves each value by up
+    to half an ulp (2^-9 of it), so a bar on this is a tolerance plus 2^-9."""
+    dec = (np.asarray(got_bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return rel_l2_rows(dec.astype(np.float64), exact, row_width)
+
+
+BF16_HALF_ULP = 2.0 ** -9

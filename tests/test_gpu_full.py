@@ -10,12 +10,19 @@ exact ties in the lm_head.
   window and the prefix lengths the GPU holds, so each step is compared on
   its own (ids, the K/V it writes, the state after the device-side commit
   exactly) with no drift carried from earlier steps.
-* K/V written to the bf16 cache: the rounding is taken on fp32 values that
-  carry the rounding of every layer before.  Where that error is far below
-  half a bf16 ulp (layer 0, and every layer of the 2-layer models) the bar is
-  one ulp of the oracle's rounding (entries within 1e-4 of the rms of the
-  tensor excepted); in every layer each row (one token's K or V of one head)
-  is held to the rel-L2 bar.
+* K/V written to the bf16 cache: each value is a rounding decision taken on
+  an fp32 value.  Layer 0's values carry no earlier rounding, so they are
+  held to one bf16 ulp of the oracle's rounding (entries within 1e-4 of the
+  tensor's rms excepted).  A decision taken the other way (the GPU's fp32
+  value and the oracle's float64 one straddle a rounding point) is correct on
+  both sides but moves what follows, most on a short context (attention over
+  a handful of keys); the loops therefore run the oracle following the GPU's
+  decisions (the window's K/V read back from the cache, as the prefix is),
+  which holds every layer of the 2-layer models to one ulp.  Deeper layers
+  carry fp32 accumulation over the earlier layers (about 1e-5 relative), which
+  also flips roundings of values near zero: every layer's K/V rows (one
+  token's K or V of one head) are held to the rel-L2 bar against the
+  oracle's values before rounding, plus the half ulp of the bf16 store.
 * Exact ties: copies of a row's winning lm_head row planted at lower and
   higher vocabulary ids, in the same tile and in other workgroups' ranges;
   the lowest index must win.
@@ -27,8 +34,8 @@ import torch
 import oracle as O
 from box_decoding_amd import binding as B
 from box_decoding_amd import synth
-from helpers import (bf16_kv_mismatch, bf16_kv_row_rel_l2, cache_slots, ids_match, max_abs, np_tree,
-                     oracle_lm, rel_l2, rel_l2_rows, step_ids_match)
+from helpers import (BF16_HALF_ULP, bf16_kv_mismatch, cache_slots, ids_match, kv_rows_vs_exact, max_abs,
+                     np_tree, oracle_lm, rel_l2, rel_l2_rows, step_ids_match)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +87,17 @@ def sub_cache_np(cache, seqs):
             "block": int(cache["block"])}
 
 
+def gpu_window_kv(cache_np, seqs, P, W, n_layers):
+    """Per layer, the bf16 K/V the GPU wrote at slots P_b .. P_b+W-1 of the
+    sequences seqs (row i of cache_np's block table is sequence seqs[i])."""
+    out = []
+    for layer in range(n_layers):
+        ks, vs = zip(*[cache_slots(cache_np, layer, i, np.arange(int(P[b]), int(P[b]) + W))
+                       for i, b in enumerate(seqs)])
+        out.append((np.concatenate(ks), np.concatenate(vs)))
+    return out
+
+
 def _full_step(wname, seqs=None, tol=TOL_BF16):
     w = synth.WORKLOADS[wname]
     d = w.dims
@@ -108,24 +126,24 @@ def _full_step(wname, seqs=None, tol=TOL_BF16):
     kr = 0.0
     for layer in range(d.n_layers):
         kb, vb = ref["kv"][layer]
+        ke, ve = ref["kv_exact"][layer]
         for i, b in enumerate(seqs):
             pos = np.arange(int(P[b]), int(P[b]) + W)
             kg, vg = cache_slots(cg, layer, i, pos)
             if layer == 0:
                 kd = max(kd, bf16_kv_mismatch(kg, kb[i * W:(i + 1) * W]))
                 vd = max(vd, bf16_kv_mismatch(vg, vb[i * W:(i + 1) * W]))
-            kr = max(kr, bf16_kv_row_rel_l2(kg, kb[i * W:(i + 1) * W], d.head_dim),
-                     bf16_kv_row_rel_l2(vg, vb[i * W:(i + 1) * W], d.head_dim))
+            kr = max(kr, kv_rows_vs_exact(kg, ke[i * W:(i + 1) * W], d.head_dim),
+                     kv_rows_vs_exact(vg, ve[i * W:(i + 1) * W], d.head_dim))
     gd = max_abs(gap.cpu().numpy().reshape(-1)[rows][ref["gap"].reshape(-1) >= 1e-3],
                  ref["gap"].reshape(-1)[ref["gap"].reshape(-1) >= 1e-3])
     _log(f"full step {wname} ({len(seqs)} of {w.batch} sequences checked): hidden rel-L2 {e:.2e} "
          f"(worst row {er:.2e}); ids {n} compared, {bad} bad, {near} near-ties; layer-0 K/V ulp {kd}/{vd}, "
-         f"worst K/V row rel-L2 {kr:.1e}; "
-         f"max |gap diff| {gd:.1e}")
+         f"worst K/V row rel-L2 against the unrounded values {kr:.2e}; max |gap diff| {gd:.1e}")
     assert int(err.item()) == 0
     assert bad == 0
     assert e <= tol and er <= tol
-    assert kd <= 1 and vd <= 1 and kr <= tol
+    assert kd <= 1 and vd <= 1 and kr <= tol + BF16_HALF_ULP
     assert gd < 1e-3
 
 
@@ -163,9 +181,10 @@ def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, 
     refeed=False: la_pbd_step + la_pbd_commit (window [last id, mask x (W-1)],
     prefix += W); refeed=True: la_pbd_step_refeed + la_pbd_commit_refeed with
     n_accept = acc[s] (None: the whole block).  seqs: the sequences the oracle
-    recomputes (the commit is checked on all).  ulp_layers: the layers whose
-    K/V are held to one ulp (default all); every layer's rows to the rel-L2
-    bar.  Returns the counts."""
+    recomputes (the commit is checked on all); it follows the GPU's K/V
+    rounding decisions; the real rows of the layers in ulp_layers (default
+    all) are held to one ulp, of every layer to the rel-L2 bar against the
+    values before rounding.  Returns the counts."""
     ulp_layers = range(d.n_layers) if ulp_layers is None else ulp_layers
     nb, W = ids.shape
     out_ids = torch.empty((nb, W), dtype=torch.int32, device=DEV)
@@ -196,28 +215,37 @@ def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, 
             B.pbd_commit(out_ids, ids, Pd, mask)
         torch.cuda.synchronize()
         got = out_ids.cpu().numpy()
-        # the oracle on the GPU's own state before the step
+        # the oracle on the GPU's own state before the step, following the
+        # GPU's K/V rounding decisions of this step (read back from the cache)
+        after = sub_cache_np(cache, seqs)
+        kv_gpu = gpu_window_kv(after, seqs, P, W, d.n_layers)
         ref = O.pbd_step(mn, before, win[seqs], P[seqs], causal_rows=c[seqs] if refeed else None,
-                         window_len=w[seqs] if refeed else None)
+                         window_len=w[seqs] if refeed else None, window_kv=kv_gpu)
         ref["lm"] = oracle_lm(mn)
         rows = np.concatenate([np.arange(i * W, i * W + int(w[b])) for i, b in enumerate(seqs)])
-        n, bad, near = step_ids_match(got[seqs].reshape(-1)[rows], ref, rows=rows)
+        n, bad, near = step_ids_match(got[seqs].reshape(-1), ref, rows=rows)
         assert bad == 0, (s, bad)
         tot["ids"] += n
         tot["near"] += near
         # the K/V the step wrote at slots P_b .. P_b + w_b - 1, every layer
-        after = sub_cache_np(cache, seqs)
         for layer in range(d.n_layers):
             kb, vb = ref["kv"][layer]
             for i, b in enumerate(seqs):
                 pos = np.arange(int(P[b]), int(P[b]) + int(w[b]))
                 kg, vg = cache_slots(after, layer, i, pos)
                 kr, vr = kb[i * W:i * W + int(w[b])], vb[i * W:i * W + int(w[b])]
+                ke, ve = (x[i * W:i * W + int(w[b])] for x in ref["kv_exact"][layer])
                 if layer in ulp_layers:
-                    tot["kd"] = max(tot["kd"], bf16_kv_mismatch(kg, kr))
-                    tot["vd"] = max(tot["vd"], bf16_kv_mismatch(vg, vr))
-                tot["kv_row"] = max(tot["kv_row"], bf16_kv_row_rel_l2(kg, kr, d.head_dim),
-                                    bf16_kv_row_rel_l2(vg, vr, d.head_dim))
+                    kd_, vd_ = bf16_kv_mismatch(kg, kr), bf16_kv_mismatch(vg, vr)
+                    if max(kd_, vd_) > 1:
+                        rowk = [bf16_kv_mismatch(kg[j:j + 1], kr[j:j + 1]) for j in range(len(pos))]
+                        rowv = [bf16_kv_mismatch(vg[j:j + 1], vr[j:j + 1]) for j in range(len(pos))]
+                        _log(f"K/V mismatch: step {s} layer {layer} seq {b} P {int(P[b])} c {int(c[b])} "
+                             f"w {int(w[b])}: K ulps by row {rowk}, V ulps by row {rowv}")
+                    tot["kd"] = max(tot["kd"], kd_)
+                    tot["vd"] = max(tot["vd"], vd_)
+                tot["kv_row"] = max(tot["kv_row"], kv_rows_vs_exact(kg, ke, d.head_dim),
+                                    kv_rows_vs_exact(vg, ve, d.head_dim))
         # the device-side commit, from the GPU's own ids, exactly
         gw, gp = ids.cpu().numpy(), Pd.cpu().numpy().astype(np.int64)
         if refeed:
@@ -228,7 +256,7 @@ def _teacher_forced_loop(dm, mn, cache, d, ids, Pd, cr, wl, block, mask, steps, 
         else:
             ew, ep = O.emission_commit(got, P, mask)
             assert np.array_equal(gw, ew) and np.array_equal(gp, ep), s
-    assert tot["kd"] <= 1 and tot["vd"] <= 1 and tot["kv_row"] <= tol, tot
+    assert tot["kd"] <= 1 and tot["vd"] <= 1 and tot["kv_row"] <= tol + BF16_HALF_ULP, tot
     return tot
 
 

@@ -863,3 +863,21 @@ def test_sample_rows_uses_the_row_counter():
     ids = OS.sample_rows(z, 1.0, 1.0, seed=7, offset=5)
     want = [int(OS.philox_uniform(t, 7, 5) * 50) for t in range(4)]
     assert ids.tolist() == want
+
+
+def test_window_kv_override():
+    # the window's own rounding passed back in reproduces the step bit for bit;
+    # one window value changed by one bf16 ulp changes every later layer's output
+    d = TINY
+    model, cache, _ = _tiny_setup(P_list=(4, 9), W=3, seed=71)
+    ids = synth.draw_window_ids(2, 3, d.vocab, 72, mask_id=-1).numpy()
+    P = [4, 9]
+    ref = O.pbd_step(model, cache, ids, P, return_hidden=True)
+    same = O.pbd_step(model, cache, ids, P, return_hidden=True, window_kv=ref["kv"])
+    np.testing.assert_array_equal(same["hidden"], ref["hidden"])
+    forced = [(k.copy(), v.copy()) for k, v in ref["kv"]]
+    forced[0][1][2, 0, 5] ^= 1                      # one V element of layer 0, one ulp
+    other = O.pbd_step(model, cache, ids, P, return_hidden=True, window_kv=forced)
+    assert np.abs(other["hidden"] - ref["hidden"]).max() > 0
+    # the layer's own rounding is still what it returns
+    np.testing.assert_array_equal(other["kv"][0][1], ref["kv"][0][1])
