@@ -127,6 +127,85 @@ def step_bytes(model, dims, prefix_len, W):
     return total
 
 
+def layer_bytes(lay, dims, prefix_len, W):
+    """Algorithmic HBM bytes of one decoder layer: its weights once, the KV
+    read once, the window's K/V written once."""
+    total = sum(weight_bytes(lay[k]) for k in ("qkv", "o", "gate_up", "down"))
+    total += (lay["in_norm"].numel() + lay["post_norm"].numel()) * 2
+    if lay.get("qkv_bias") is not None:
+        total += lay["qkv_bias"].numel() * 2
+    per_tok = 2 * dims.n_kv_heads * dims.head_dim * 2
+    keys = int(sum(int(p) + W for p in prefix_len.tolist()))
+    return total + keys * per_tok + len(prefix_len) * W * per_tok
+
+
+def oracle_rate(workload_name, sample_layers, min_seconds):
+    """Oracle steps/s of a workload: whole passes over `sample_layers` of its
+    decoder layers (then the final norm and the full lm_head argmax, when the
+    workload has one) until min_seconds of work are measured, extrapolated to
+    every layer."""
+    import dataclasses
+
+    import numpy as np  # noqa: F401
+    from box_decoding_amd import synth
+
+    import oracle as O
+
+    w = synth.WORKLOADS[workload_name]
+    d = w.dims
+    ds = dataclasses.replace(d, n_layers=min(sample_layers, d.n_layers))
+    model = synth.to_numpy_tree(synth.make_model(ds, w.wfmt, w.model_seed, "cpu"))
+    model["dims"] = ds
+    P = synth.draw_prefix_lens(w)
+    cache = synth.to_numpy_tree(synth.make_cache(ds, P, w.window, seed=w.input_seed, device="cpu"))
+    if w.lm_head:
+        ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed).numpy()
+        h0 = O.embed_rows(ids.reshape(-1), model["embed"])
+    else:
+        h0 = synth.make_hidden(w.batch * w.window, d.hidden, w.input_seed).numpy().astype("float64")
+    lm = model["lm_head"] if model.get("lm_head") is not None else model["embed"]
+    t_layers = t_lm = 0.0
+    passes = 0
+    while passes == 0 or t_layers + t_lm < min_seconds:
+        h = h0
+        t0 = time.perf_counter()
+        for l in range(ds.n_layers):
+            h, _, _ = O.decoder_layer(h, model["layers"][l], ds, cache, l, P.numpy(), w.window)
+        t_layers += time.perf_counter() - t0
+        if w.lm_head:
+            f = O.rmsnorm(h, O.bf16_to_float(model["final_norm"]), d.rms_eps)
+            t0 = time.perf_counter()
+            O.lm_head_argmax(f, lm)
+            t_lm += time.perf_counter() - t0
+        passes += 1
+    t_layers /= passes
+    t_lm /= passes
+    t_step = t_layers / ds.n_layers * d.n_layers + t_lm
+    return 1.0 / t_step, {"passes": passes, "sampled_layers": ds.n_layers, "layers": d.n_layers,
+                          "s_per_pass_layers": round(t_layers, 3), "s_per_pass_lm_head": round(t_lm, 3),
+                          "s_per_step": round(t_step, 3)}
+
+
+def cpu_baselines():
+    """The oracle on the other workloads (BASELINE's CPU plan): the one-layer
+    workload with every BLAS thread and with one, and one step of the batch-32,
+    INT4 batch-8 and 16-sequence workloads from 2 of their 36 layers."""
+    from threadpoolctl import threadpool_limits
+
+    out = {}
+    log("cpu_baseline: one layer, all threads / one thread")
+    r, info = oracle_rate("layer_b1_p512", 1, 2.0)
+    out["layer_b1_p512"] = {"steps_per_s": round(r, 3), **info}
+    with threadpool_limits(limits=1):
+        r, info = oracle_rate("layer_b1_p512", 1, 2.0)
+    out["layer_b1_p512_1thread"] = {"steps_per_s": round(r, 3), "threads": 1, **info}
+    for name in ("step_b32_ragged", "step_int4_b8_p1280", "emit_b16_p2048_x40"):
+        log(f"cpu_baseline: {name}")
+        r, info = oracle_rate(name, 2, 0.0)
+        out[name] = {"steps_per_s": round(r, 4), **info}
+    return out
+
+
 def cpu_baseline(workload_name, sample_layers, min_seconds=10.0):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -229,58 +308,6 @@ def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
                              "matrix_core_frac_with_hi_lo": round(2 * tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
-def emission_leg(B, synth, torch, dm, model, dev, stream, args):
-    """The dense-scene emission loop: 16 sequences from prefix 2048 run 40
-    consecutive window steps, each committed on the device (prefix += 6, next
-    window = [last output id, mask x 5]) -- one captured graph of step + commit,
-    replayed 40 times per loop."""
-    w = synth.WORKLOADS["emit_b16_p2048_x40"]
-    d = w.dims
-    log("bench: emission-loop leg")
-    P = synth.draw_prefix_lens(w)
-    cache = synth.make_cache(d, P, w.window, extra_tokens=w.steps * w.window, seed=w.input_seed,
-                             device=dev)
-    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
-    mask_id = int(ids[0, 1].item())
-    ids0, P0 = ids.clone(), P.to(dev)
-    dc = B.DeviceCache(cache, d.n_layers)
-    Pd = P0.clone()
-    max_len = int(P.max()) + (w.steps + 1) * w.window
-    ws = B.Workspace(dev)
-    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
-    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
-    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws, commit_mask_id=mask_id)
-
-    def run_loop():
-        ids.copy_(ids0)
-        Pd.copy_(P0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(w.steps):
-            graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
-
-    run_loop()  # warm-up loop
-    loop_ms = run_loop()
-    assert int((Pd - P0).min().item()) == w.steps * w.window
-    ms_step = loop_ms / w.steps
-    mid = P + w.window * (w.steps - 1) // 2
-    sbytes = step_bytes(model, d, mid, w.window)
-    log(f"bench: emission loop: {loop_ms:.2f} ms for {w.steps} steps, {ms_step:.3f} ms/step, "
-        f"{w.batch * 1000.0 / ms_step:.0f} windows/s")
-    del graph, cache, dc, ws
-    torch.cuda.synchronize()
-    return {"workload": w.name, "batch": w.batch, "window": w.window, "steps_per_loop": w.steps,
-            "prefix_start": int(P.max()), "loop_ms": round(loop_ms, 3), "ms_per_step": round(ms_step, 4),
-            "steps_per_s": round(1000.0 / ms_step, 3),
-            "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
-            "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
-            "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
-
-
 def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
     """The long-context probe: one sequence at prefix 32768, window 6."""
     w = synth.WORKLOADS["probe_b1_p32768"]
@@ -310,16 +337,18 @@ def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
 
 
-def refeed_leg(B, synth, torch, dm, model, dev, stream, args):
-    """The emission loop of the dense-scene workload with re-feeding: every
-    step re-sends the 6 tokens it accepted last time causally before a new
-    block of 6 (window W = 11: 5 re-fed rows, the block; the first step has
-    the block only), and a device-side commit accepts the whole block -- one
-    captured graph of la_pbd_step_refeed + la_pbd_commit_refeed, 40 replays."""
+def emission_leg(B, synth, torch, dm, model, dev, stream, args):
+    """The dense-scene emission loop: 16 sequences from prefix 2048, 40
+    consecutive window steps, each appending the K/V of the 6 tokens it
+    accepted: every step re-sends the tokens accepted last time causally before
+    a new block of 6 (window W = 11: 5 re-fed rows, the block; the first step
+    has the block only), and a device-side commit accepts the whole block --
+    one captured graph of la_pbd_step_refeed + la_pbd_commit_refeed, 40
+    replays."""
     w = synth.WORKLOADS["emit_b16_p2048_x40"]
     d = w.dims
     block, W = w.window, 2 * w.window - 1
-    log("bench: re-fed emission-loop leg")
+    log("bench: emission-loop leg (re-fed windows)")
     P = synth.draw_prefix_lens(w)
     cache = synth.make_cache(d, P, W, extra_tokens=w.steps * block, seed=w.input_seed, device=dev)
     first = synth.draw_window_ids(w.batch, block, d.vocab, w.input_seed, device=dev)
@@ -355,14 +384,18 @@ def refeed_leg(B, synth, torch, dm, model, dev, stream, args):
     # the first step commits its block's first row, every later one 6 rows
     assert int((Pd - P0).min().item()) == 1 + (w.steps - 1) * block
     ms_step = loop_ms / w.steps
-    log(f"bench: re-fed emission loop: {loop_ms:.2f} ms for {w.steps} steps, {ms_step:.3f} ms/step, "
+    mid = P + (1 + block * (w.steps - 1)) // 2
+    sbytes = step_bytes(model, d, mid, W)
+    log(f"bench: emission loop: {loop_ms:.2f} ms for {w.steps} steps, {ms_step:.3f} ms/step, "
         f"{w.batch * 1000.0 / ms_step:.0f} windows/s")
     del graph, cache, dc, ws
     torch.cuda.synchronize()
-    return {"workload": w.name + "_refeed", "batch": w.batch, "window": W, "block": block,
+    return {"workload": w.name, "batch": w.batch, "window": W, "block": block, "refeed": True,
             "steps_per_loop": w.steps, "prefix_start": int(P.max()), "loop_ms": round(loop_ms, 3),
             "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
-            "windows_per_s": round(1000.0 / ms_step * w.batch, 2)}
+            "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
+            "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
+            "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
 
 
 def prefill_leg(B, synth, torch, dm, model, dev, timed, args):
@@ -397,6 +430,129 @@ def prefill_leg(B, synth, torch, dm, model, dev, timed, args):
     torch.cuda.synchronize()
     return {"workload": "prefill_b1_l320", "batch": 1, "rows": L, "spliced_rows": n_img, "reps": reps,
             "ms": round(ms, 4), "rows_per_s": round(L * 1000.0 / ms, 1)}
+
+
+def sampling_leg(B, synth, torch, dm, model, dev, timed, args):
+    """The batch-1 step with the sampled selection (temperature 0.7, top-p 0.9,
+    the RK3588 page's defaults) in place of the argmax: the lm_head stores the
+    logits, one workgroup per row samples them; the draw counter lives in device
+    memory and advances on every replay."""
+    w = synth.WORKLOADS["step_b1_p1280"]
+    d = w.dims
+    log("bench: sampling leg")
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    off = torch.zeros(1, dtype=torch.int64, device=dev)
+    smp = B.Sampling(0.7, 0.9, seed=1, offset_dev=off)
+    max_len = int(P.max()) + w.window
+    B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, sampling=smp)  # sizes buffers
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, want_gap=False, sampling=smp)
+    for _ in range(max(2, args.warmup)):
+        graph.replay()
+    steps = max(5, args.steps // 3)
+    ms_step, _ = timed(graph.replay, steps)
+    log(f"bench: sampled step, batch 1: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s")
+    del graph, cache, dc, ws
+    torch.cuda.synchronize()
+    return {"workload": w.name, "selection": "temperature 0.7, top-p 0.9", "steps": steps,
+            "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3)}
+
+
+def layer_leg(B, synth, torch, dev, timed, args, copies=5):
+    """One decoder layer, batch 1, prefix 512 (la_pbd_layer, which also runs its
+    per-call prologue), over `copies` weight copies in turn (770 MB > the 256 MB
+    MALL, so no call finds its weights there), as one captured graph."""
+    w = synth.WORKLOADS["layer_b1_p512"]
+    d = w.dims
+    log("bench: one-layer leg")
+    dms, models = [], []
+    for c in range(copies):
+        m = B.pack_model(synth.make_model(d, "bf16", w.model_seed + 100 * c, dev))
+        models.append(m)
+        dms.append(B.DeviceModel(m))
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    dc = B.DeviceCache(cache, d.n_layers)
+    x = synth.make_hidden(w.batch * w.window, d.hidden, w.input_seed, dev)
+    Pd = P.to(dev)
+    ws = B.Workspace(dev)
+    max_len = int(P.max()) + w.window
+    reps = 4 * copies
+    B.pbd_layer(dms[0], 0, dc, x, Pd, w.batch, w.window, max_len, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(reps):
+            B.pbd_layer(dms[r % copies], 0, dc, x, Pd, w.batch, w.window, max_len, ws=ws)
+    graph.replay()
+    ms, _ = timed(graph.replay, 3)
+    us = ms * 1e3 / reps
+    lbytes = layer_bytes(models[0]["layers"][0], d, P, w.window)
+    log(f"bench: one layer (b1 p512): {us:.1f} us, {lbytes / us / 1e3:.0f} GB/s")
+    del graph, cache, dc, ws, dms, models
+    torch.cuda.synchronize()
+    return {"workload": w.name, "batch": 1, "window": w.window, "prefix": int(P.max()),
+            "weight_copies": copies, "us_per_layer": round(us, 2), "layer_bytes": lbytes,
+            "hbm_gbps": round(lbytes / us / 1e3, 1), "hbm_frac": round(lbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+
+
+def int4_leg(B, synth, torch, dev, stream, timed, args):
+    """The INT4 weight-only step at batch 8, prefix 1280 (group-128 linears and
+    lm_head, group-32 embedding gathered on the device), as graph replays."""
+    w = synth.WORKLOADS["step_int4_b8_p1280"]
+    d = w.dims
+    log("bench: INT4 batch-8 leg")
+    model = B.pack_model(synth.make_model(d, w.wfmt, w.model_seed, dev))
+    dm = B.DeviceModel(model)
+    P = synth.draw_prefix_lens(w)
+    cache = synth.make_cache(d, P, w.window, seed=w.input_seed, device=dev)
+    ids = synth.draw_window_ids(w.batch, w.window, d.vocab, w.input_seed, device=dev)
+    dc = B.DeviceCache(cache, d.n_layers)
+    Pd = P.to(dev)
+    ws = B.Workspace(dev)
+    out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
+    out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
+    graph = B.StepGraph(dm, dc, ids, Pd, int(P.max()) + w.window, out_ids, out_gap, ws=ws)
+    for _ in range(max(2, args.warmup)):
+        graph.replay()
+    steps = max(5, args.steps // 3)
+    ms_step, _ = timed(graph.replay, steps)
+    sbytes = step_bytes(model, d, P, w.window)
+    # its dominant kernel: gate/up with the SiLU epilogue at 48 rows
+    T, F, H = w.batch * w.window, d.inter, d.hidden
+    xin = torch.randn((T, H), device=dev, generator=torch.Generator(device=dev).manual_seed(1))
+    packed = B.pack_rows(xin, "int4", norm_gain=model["layers"][0]["post_norm"])
+    yout = torch.empty((T, F), dtype=torch.float32, device=dev)
+    for l in range(3):
+        B.wgemm_packed(packed, T, model["layers"][l]["gate_up"], silu_gate=True, out=yout)
+    reps = 36
+
+    def gemm():
+        for r in range(reps):
+            B.wgemm_packed(packed, T, model["layers"][r % d.n_layers]["gate_up"], silu_gate=True, out=yout)
+
+    k_ms = timed(gemm, 1)[0] / reps
+    gu_bytes = gate_up_bytes(model["layers"][0]["gate_up"], T, H, F)
+    log(f"bench: INT4 batch 8: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; gate_up "
+        f"{k_ms * 1e3:.1f} us, {gu_bytes / k_ms / 1e6:.0f} GB/s")
+    del graph, cache, dc, ws, dm, model
+    torch.cuda.synchronize()
+    return {"workload": w.name, "batch": w.batch, "window": w.window, "prefix": int(P.max()), "weights": "int4",
+            "steps": steps, "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
+            "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
+            "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
+            "gate_up_gemm": {"rows": T, "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes,
+                             "gbps": round(gu_bytes / k_ms / 1e6, 1),
+                             "frac": round(gu_bytes / k_ms / 1e6 / HBM_PEAK_GBPS, 4)}}
 
 
 def causal_leg(B, synth, torch, model, dev, timed, args):
@@ -584,11 +740,17 @@ def main():
         result["emission_loop"] = emission_leg(B, synth, torch, dm, model, dev, stream, args)
         result["prefix_32768"] = probe_leg(B, synth, torch, dm, model, dev, stream, timed, args)
         result["causal_window"] = causal_leg(B, synth, torch, model, dev, timed, args)
-        result["refeed_loop"] = refeed_leg(B, synth, torch, dm, model, dev, stream, args)
+        result["sampling"] = sampling_leg(B, synth, torch, dm, model, dev, timed, args)
         result["prefill"] = prefill_leg(B, synth, torch, dm, model, dev, timed, args)
+        del dm, model
+        torch.cuda.synchronize()
+        result["layer_b1_p512"] = layer_leg(B, synth, torch, dev, timed, args)
+        result["int4_b8"] = int4_leg(B, synth, torch, dev, stream, timed, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)
+        if args.workload == "step_b1_p1280" and not args.no_extra_legs:
+            result["cpu_baseline"]["other_workloads"] = cpu_baselines()
     print(json.dumps(result), flush=True)
 
 

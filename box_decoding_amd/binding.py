@@ -30,7 +30,7 @@ EXPORTED = [
     "la_pack_weight", "la_packed_rows_bytes", "la_pack_rows", "la_wgemm_packed", "la_pbd_commit",
     "la_pbd_attention_masked", "la_pbd_attention_refeed", "la_pbd_step_refeed",
     "la_pbd_commit_refeed", "la_pbd_step_opts", "la_lm_head_argmax_penalized", "la_pbd_mark_tokens",
-    "la_pbd_prefill_workspace", "la_pbd_prefill", "la_pbd_step_noalloc",
+    "la_pbd_prefill_workspace", "la_pbd_prefill", "la_pbd_step_noalloc", "la_sample_logits",
 ]
 
 
@@ -59,9 +59,15 @@ class LaKvCache(ctypes.Structure):
                 ("n_layers", c_int32)]
 
 
+class LaSampling(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("top_p", c_float), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64), ("offset_dev", c_void_p), ("logits", c_void_p)]
+
+
 class LaStepOpts(ctypes.Structure):
     _fields_ = [("causal_rows", c_void_p), ("window_len", c_void_p), ("rep_bits", c_void_p),
-                ("rep_words", c_int32), ("rep_penalty", c_float)]
+                ("rep_words", c_int32), ("rep_penalty", c_float),
+                ("sampling", POINTER(LaSampling))]
 
 
 class LaError(RuntimeError):
@@ -139,6 +145,8 @@ def load() -> ctypes.CDLL:
         "la_pbd_step_noalloc": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
                                           c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_void_p]),
+        "la_sample_logits": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32, c_int32,
+                                       c_float, POINTER(LaSampling), c_void_p, c_void_p, c_void_p]),
         "la_pbd_prefill_workspace": (c_size_t, [POINTER(LaModel), c_int32, c_int32, c_int32]),
         "la_pbd_prefill": (c_int32, [POINTER(LaModel), POINTER(LaKvCache), c_void_p, c_void_p,
                                      c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
@@ -427,10 +435,12 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
              want_hidden: bool = False, ws: Optional[Workspace] = None, out_ids=None, out_gap=None,
              err: Optional[torch.Tensor] = None, causal_rows: Optional[torch.Tensor] = None,
              window_len: Optional[torch.Tensor] = None, rep_bits: Optional[torch.Tensor] = None,
-             rep_penalty: float = 1.0):
+             rep_penalty: float = 1.0, sampling: Optional["Sampling"] = None):
     """One PBD window step; returns (ids [B,W], gap [B,W] or None, hidden or None).
     causal_rows / window_len (int32 [B]) make it a re-fed window step; rep_bits
-    (int32 [B, words] vocabulary bitmaps) applies the repetition penalty."""
+    (int32 [B, words] vocabulary bitmaps) applies the repetition penalty;
+    sampling (a Sampling) replaces the argmax by the sampled selection (gap
+    then holds the selected logit minus the row's largest)."""
     lib = load()
     _require_cuda(window_ids, prefix_len, err, causal_rows, window_len, rep_bits)
     B, W = window_ids.shape
@@ -444,9 +454,13 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
     if need == 0:
         raise LaError("la_pbd_step_workspace rejected the model or shape")
     buf = _ws(ws).get(need)
-    if rep_bits is not None:
-        opts = LaStepOpts(_ptr(causal_rows), _ptr(window_len), _ptr(rep_bits), rep_bits.shape[1],
-                          float(rep_penalty))
+    if rep_bits is not None or sampling is not None:
+        smp = None
+        if sampling is not None:
+            smp = sampling.struct(B * W, model.dims.vocab, dev)
+        opts = LaStepOpts(_ptr(causal_rows), _ptr(window_len), _ptr(rep_bits),
+                          0 if rep_bits is None else rep_bits.shape[1], float(rep_penalty),
+                          None if smp is None else ctypes.pointer(smp))
         _check(lib.la_pbd_step_opts(ctypes.byref(model.struct), ctypes.byref(cache.struct),
                                     _ptr(window_ids), _ptr(prefix_len), ctypes.byref(opts), B, W,
                                     max_len, _ptr(ids), _ptr(gap), _ptr(hid), _ptr(buf), buf.numel(),
@@ -478,6 +492,44 @@ def pbd_step_noalloc(model: DeviceModel, cache: DeviceCache, window_ids: torch.T
                                    _ptr(window_ids), _ptr(prefix_len), B, W, max_len, _ptr(out_ids),
                                    _ptr(out_gap), _ptr(out_hidden), _ptr(err), _stream()),
            "la_pbd_step_noalloc")
+
+
+class Sampling:
+    """Parameters of the sampled selection (la_sampling): temperature, top_p,
+    seed, offset (or offset_dev, an int64 device word the call reads and then
+    advances by 1); logits: the step's fp32 [rows, vocab] scratch (allocated on
+    first use when not given; it holds the step's logits after a call)."""
+
+    def __init__(self, temperature=0.7, top_p=0.9, seed=0, offset=0,
+                 offset_dev: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None):
+        self.temperature, self.top_p, self.seed, self.offset = temperature, top_p, seed, offset
+        self.offset_dev, self.logits = offset_dev, logits
+        self._keep = None
+
+    def struct(self, rows: int = 0, vocab: int = 0, device=None) -> LaSampling:
+        if rows and (self.logits is None or self.logits.numel() < rows * vocab):
+            self.logits = torch.empty((rows, vocab), dtype=torch.float32, device=device)
+        _require_cuda(self.offset_dev, self.logits)
+        s = LaSampling(float(self.temperature), float(self.top_p), int(self.seed) & (2 ** 64 - 1),
+                       int(self.offset) & (2 ** 64 - 1), _ptr(self.offset_dev), _ptr(self.logits))
+        self._keep = s
+        return s
+
+
+def sample_logits(logits: torch.Tensor, sampling: Sampling, rep_bits: Optional[torch.Tensor] = None,
+                  rep_rows: int = 1, rep_penalty: float = 1.0):
+    """la_sample_logits: sampled ids [M] (and selected logit minus the row max) of logits [M, V]."""
+    lib = load()
+    _require_cuda(logits, rep_bits)
+    M, V = logits.shape
+    ids = torch.empty(M, dtype=torch.int32, device=logits.device)
+    gap = torch.empty(M, dtype=torch.float32, device=logits.device)
+    smp = sampling.struct()
+    _check(lib.la_sample_logits(_ptr(logits), M, V, logits.stride(0), _ptr(rep_bits),
+                                0 if rep_bits is None else rep_bits.shape[1], rep_rows,
+                                float(rep_penalty), ctypes.byref(smp), _ptr(ids), _ptr(gap), _stream()),
+           "la_sample_logits")
+    return ids, gap
 
 
 def pbd_commit(out_ids: torch.Tensor, window_ids: torch.Tensor, prefix_len: torch.Tensor,

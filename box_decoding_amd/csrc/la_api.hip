@@ -534,6 +534,30 @@ PrologueArgs base_prologue(const la_model* m, const la_kv_cache* kv, const int32
   return p;
 }
 
+la_status check_sampling(const la_sampling* smp) {
+  if (!smp) return LA_ERR_ARG;
+  if (!(smp->top_p > 0.f) || !(smp->top_p <= 1.f)) return LA_ERR_ARG;
+  if (!(smp->temperature < INFINITY) || !(smp->temperature > -INFINITY)) return LA_ERR_ARG;
+  return LA_OK;
+}
+
+SampleArgs sample_args(const la_sampling* smp, const float* logits, int M, int V, int ld) {
+  SampleArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.logits = logits;
+  sa.M = M;
+  sa.V = V;
+  sa.ldz = ld;
+  sa.rep_rows = 1;
+  sa.rep_theta = 1.f;
+  sa.temperature = smp->temperature;
+  sa.top_p = smp->top_p;
+  sa.seed = smp->seed;
+  sa.offset = smp->offset;
+  sa.offset_dev = smp->offset_dev;
+  return sa;
+}
+
 }  // namespace
 
 extern "C" {
@@ -796,6 +820,29 @@ la_status la_lm_head_argmax_penalized(const float* h, int32_t M, const la_weight
   return hip_status(launch_argmax_reduce(amax, M, parts, nullptr, ids, top1, gap, nullptr, stream));
 }
 
+la_status la_sample_logits(const float* logits, int32_t M, int32_t V, int32_t ld,
+                           const uint32_t* rep_bits, int32_t rep_words, int32_t rep_rows,
+                           float rep_penalty, const la_sampling* smp, int32_t* ids, float* sel_gap,
+                           hipStream_t stream) {
+  if (!logits || !ids || !smp) return LA_ERR_ARG;
+  la_status st = check_sampling(smp);
+  if (st != LA_OK) return st;
+  if (M < 1 || M > 65535 || V < 1 || ld < V) return LA_ERR_SHAPE;
+  if (rep_bits && (rep_rows < 1 || (int64_t)rep_words * 32 < (int64_t)V || !(rep_penalty > 0.f) ||
+                   !(rep_penalty < INFINITY)))
+    return LA_ERR_ARG;
+  SampleArgs sa = sample_args(smp, logits, M, V, ld);
+  if (rep_bits) {
+    sa.rep_bits = rep_bits;
+    sa.rep_words = rep_words;
+    sa.rep_rows = rep_rows;
+    sa.rep_theta = rep_penalty;
+  }
+  sa.ids = ids;
+  sa.sel_gap = sel_gap;
+  return hip_status(launch_sample(sa, stream));
+}
+
 la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, const float* x,
                        const int32_t* prefix_len, int32_t B, int32_t W, int32_t max_len, float* y,
                        float* attn_out, void* workspace, size_t workspace_bytes,
@@ -862,6 +909,10 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   if (st != LA_OK) return st;
   const int32_t* causal_rows = opts ? opts->causal_rows : nullptr;
   const int32_t* window_len = opts ? opts->window_len : nullptr;
+  const la_sampling* smp = opts ? opts->sampling : nullptr;
+  if (smp && (st = check_sampling(smp)) != LA_OK) return st;
+  const bool sampled = smp && smp->temperature > 0.f;
+  if (sampled && (!smp->logits || !aligned16(smp->logits))) return LA_ERR_ARG;
   if (opts && opts->rep_bits &&
       (!(opts->rep_penalty > 0.f) || !(opts->rep_penalty < INFINITY) ||
        (int64_t)opts->rep_words * 32 < (int64_t)(m->lm_head.data ? m->lm_head.n : m->embed.n)))
@@ -890,8 +941,10 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   for (int l = 0; l < m->n_layers; ++l) {
     // the gain after layer l: the next input norm, or the final norm when the
     // lm_head takes the packed rows directly (bf16)
+    // (sampling stores the logits themselves: the final norm is applied by the
+    // packing below, not folded into the lm_head's epilogue)
     const uint16_t* next_gain = l + 1 < m->n_layers ? m->layers[l + 1].in_norm
-                                                    : (int4 ? nullptr : m->final_norm);
+                                                    : (int4 || sampled ? nullptr : m->final_norm);
     st = run_layer(m, l, kv, prefix_len, causal_rows, window_len, B, W, max_len, s, nullptr, &carry,
                    next_gain, stream);
     if (st != LA_OK) return st;
@@ -905,6 +958,27 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   if (out_hidden)
     LA_TRY(hipMemcpyAsync(out_hidden, s.h, (size_t)T * H * sizeof(float), hipMemcpyDeviceToDevice,
                           stream));
+  if (sampled) {
+    // the logits of every row, then the sampled selection
+    GemmArgs g = base_gemm(lm, T);
+    g.apack = s.apack;
+    g.asum = s.asum;
+    g.y = smp->logits;
+    g.ldy = lm->n;
+    LA_TRY(launch_gemm(g, EPI_STORE, int4, stream));
+    SampleArgs sa = sample_args(smp, smp->logits, T, lm->n, lm->n);
+    if (opts->rep_bits) {
+      sa.rep_bits = opts->rep_bits;
+      sa.rep_words = opts->rep_words;
+      sa.rep_rows = W;
+      sa.rep_theta = opts->rep_penalty;
+    }
+    sa.flags = s.flags;
+    sa.ids = out_ids;
+    sa.sel_gap = out_gap;
+    sa.err = err;
+    return hip_status(launch_sample(sa, stream));
+  }
   GemmArgs g = base_gemm(lm, T);
   g.amax = s.amax;
   g.apack = s.apack;

@@ -170,6 +170,24 @@ bool use_big_gemm(int M, int K, bool int4, int epi);
 BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_split);
 hipError_t launch_gemm_big(GemmArgs a, int epi, bool int4, hipStream_t s);
 
+// Sampled selection (temperature, top-p, Philox draw) from stored logits, one
+// workgroup per row.
+struct SampleArgs {
+  const float* logits;         // [M][ldz]
+  int M, V, ldz;
+  const uint32_t* rep_bits;    // [M / rep_rows][rep_words] (nullable)
+  int rep_words, rep_rows;
+  float rep_theta;
+  float temperature, top_p;    // temperature <= 0: argmax
+  uint64_t seed, offset;
+  const uint64_t* offset_dev;  // nullable: replaces offset and is advanced by 1 afterwards
+  const int32_t* flags;        // [M] nullable: nonzero rows get id -1
+  int32_t* ids;                // [M]
+  float* sel_gap;              // [M] nullable: selected logit minus the row's largest
+  int32_t* err;                // nullable
+};
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+
 // attention split planning
 void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits);
 inline int attn_nqp(int W, int G) { return ((W * G + 15) / 16) * 16; }

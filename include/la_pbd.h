@@ -317,6 +317,46 @@ la_status la_pbd_step_noalloc(const la_model* m, const la_kv_cache* kv, const in
                               int32_t* out_ids, float* out_gap, float* out_hidden, int32_t* err,
                               hipStream_t stream);
 
+/* Sampled selection in place of the greedy argmax (the RK3588 page, "LocateAnything-3B
+ * for RK3588 (RKLLM + RKNN)", sections "Usage (on the board)" and "Evaluation",
+ * runs the model with temperature 0.7, top-p 0.9 and repetition penalty 1.1; the
+ * Jetson page, Part 1 section 1.4, notes that a temperature that is not positive
+ * means greedy selection).  Per row of logits z (after the repetition penalty,
+ * when one is given): p_v ~ exp(z_v / temperature); the nucleus is the shortest
+ * run of the vocabulary ordered by z descending (equal logits: lower id first)
+ * whose probability reaches top_p; a uniform draw u in [0, 1) selects, among the
+ * kept ids in ascending id order, the first whose running kept probability
+ * exceeds u times the kept total.  u is the top 24 bits of the first output word
+ * of Philox4x32-10 at counter (row, offset mod 2^32, offset / 2^32, 0) and key
+ * (seed mod 2^32, seed / 2^32), times 2^-24; row is the call's row index (b * W
+ * + j for a step).  Probabilities are summed as 40-bit fixed point, exactly, so
+ * the result is deterministic.  temperature <= 0 selects the argmax (lowest id
+ * on a tie).  top_p must lie in (0, 1]. */
+typedef struct {
+  float temperature;
+  float top_p;
+  uint64_t seed;
+  uint64_t offset;      /* the draw counter of this call */
+  uint64_t* offset_dev; /* nullable device word: when given, its value is used instead
+                           of `offset` and the call adds 1 to it afterwards (for a
+                           loop replayed from one captured graph) */
+  float* logits;        /* la_pbd_step_opts only: device fp32 [B*W][vocab] scratch,
+                           caller-owned, 16-byte aligned; holds the step's logits
+                           (before the penalty) when the call has run */
+} la_sampling;
+
+/* Sampled selection from given logits: ids int32 [M] for logits fp32 [M][ld]
+ * (the first V of each row), with the repetition penalty of
+ * la_lm_head_argmax_penalized when rep_bits is given (bitmap m / rep_rows for
+ * row m).  sel_gap (nullable) fp32 [M] receives the selected logit minus the
+ * row's largest (after the penalty).  LA_ERR_ARG for NULL logits, ids or s,
+ * top_p outside (0, 1], a temperature that is not finite, or a bad penalty;
+ * LA_ERR_SHAPE outside 1 <= M <= 65535, 1 <= V <= ld. */
+la_status la_sample_logits(const float* logits, int32_t M, int32_t V, int32_t ld,
+                           const uint32_t* rep_bits, int32_t rep_words, int32_t rep_rows,
+                           float rep_penalty, const la_sampling* s, int32_t* ids, float* sel_gap,
+                           hipStream_t stream);
+
 /* Options of la_pbd_step_opts (zero-initialise, then set what is used):
  *  - causal_rows, window_len: int32 [B] device arrays of a re-fed window
  *    (la_pbd_step_refeed), or NULL;
@@ -325,13 +365,19 @@ la_status la_pbd_step_noalloc(const la_model* m, const la_kv_cache* kv, const in
  *    every window row of sequence b ranks its logits with those ids'
  *    penalised by rep_penalty as in la_lm_head_argmax_penalized;
  *    rep_words * 32 >= the lm_head's vocabulary, rep_penalty positive and
- *    finite (else LA_ERR_ARG). */
+ *    finite (else LA_ERR_ARG);
+ *  - sampling: NULL for greedy selection; else the sampled selection above
+ *    over the step's logits (with the repetition bitmaps when given).  Then
+ *    out_gap (nullable) receives each row's selected logit minus its largest
+ *    instead of the top-2 gap.  LA_ERR_ARG when sampling->logits is NULL or
+ *    misaligned, or the parameters are out of range. */
 typedef struct {
   const int32_t* causal_rows;
   const int32_t* window_len;
   const uint32_t* rep_bits;
   int32_t rep_words;
   float rep_penalty;
+  const la_sampling* sampling;
 } la_step_opts;
 la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
                            const int32_t* prefix_len, const la_step_opts* opts, int32_t B, int32_t W,
