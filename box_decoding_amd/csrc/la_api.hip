@@ -1,5 +1,6 @@
 // C ABI of the PBD window step: host-side validation, workspace carving and the
 // launch sequence of every entry point declared in include/la_pbd.h.
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -127,6 +128,10 @@ struct StepWs {
   float* part_ml;
   float* amax;
   float* parts;       // K-slice partial sums of the O and down projections
+  int32_t* sync;      // the front-half launch's flag words (zeroed by the prologue)
+  int n_sync;
+  float* front_ss;    // the front-half launch's per-slice sums of squares
+  int32_t* err;       // the step's error word (nullable)
   // prefill: the attention's view of the prompt as 16-row windows, the
   // per-sequence flags and the last rows
   int32_t* pre_prefix;
@@ -186,6 +191,9 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
   const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
   const size_t qkv_parts = (size_t)qkv_ksplit(T, &m->layers[0].qkv) * T * NQKV;
   s.parts = c.take<float>(std::max((size_t)ksp * T * H, qkv_parts));
+  s.n_sync = 8 * 64 + m->n_kv_heads * 128 + aB * m->n_kv_heads * 16 + 8 * 128;
+  s.sync = c.take<int32_t>(s.n_sync);
+  s.front_ss = c.take<float>(8 * kFrontPackSlices);
   s.bytes = c.off;
   return s;
 }
@@ -331,6 +339,41 @@ struct AttnView {
   int bt_div;  // windows per block-table row
 };
 
+// The front half of a layer (RMSNorm, QKV, attention, O) runs as one
+// persistent launch for at most 8 bf16 rows with K = 2048 tiled weights and at
+// most 4 pending K-slice sums, when the attention runs of every (sequence, KV
+// head) fit beside the QKV tiles on the compute units (at most 16 runs of at
+// most kFrontMaxRunPages pages each); otherwise (and with LA_PBD_FRONT=0 in the
+// environment, a diagnostic switch) each step is a kernel of its own.
+struct FrontPlan {
+  int grid = 0, pps = 0, runs = 0, items = 0;
+};
+
+FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max_len, const StepWs& s,
+                     const AttnView* av, const float* attn_out, int pending) {
+  FrontPlan f;
+  const char* env = getenv("LA_PBD_FRONT");
+  if (env && env[0] == '0') return f;
+  const int T = B * W, H = m->hidden, HQ = m->n_heads * m->head_dim;
+  const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+  if (av || attn_out || T > 8 || H != 2048 || HQ != 2048 || L.qkv.fmt != LA_W_BF16) return f;
+  if (L.qkv.layout != LA_LAYOUT_TILED_QKV || L.o.layout != LA_LAYOUT_TILED || s.nqp > 64 || pending > 4) return f;
+  const int G = cu_count(), n_qkv = NQKV / 16;
+  const int free_wgs = G - n_qkv;
+  if (n_qkv + kFrontPackSlices > G || H / 16 > n_qkv || free_wgs < B * m->n_kv_heads) return f;
+  const int max_pages = (max_len + kBlock - 1) / kBlock;
+  const int runs_max = std::min(16, free_wgs / (B * m->n_kv_heads));
+  int pps = std::max(2, (max_pages + runs_max - 1) / runs_max);
+  if (pps > kFrontMaxRunPages) return f;
+  const int runs = (max_pages + pps - 1) / pps;
+  if (runs > s.max_splits) return f;
+  f.grid = G;
+  f.pps = pps;
+  f.runs = runs;
+  f.items = B * m->n_kv_heads * runs;
+  return f;
+}
+
 la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
                     const int32_t* causal_rows, const int32_t* window_len, int B, int W,
                     int max_len, const StepWs& s, float* attn_out, Carry* carry,
@@ -341,6 +384,68 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   const bool int4 = L.qkv.fmt == LA_W_INT4;
   const size_t le = kv_layer_elems(kv, m);
   la_status rs;
+  const FrontPlan fp = plan_front(m, L, B, W, max_len, s, av, attn_out, carry->pending);
+  GemmArgs g;
+  if (fp.grid) {
+    FrontArgs f;
+    memset(&f, 0, sizeof(f));
+    AttnArgs& at = f.at;
+    at.q = s.q;
+    at.kc = (uint16_t*)kv->k + (size_t)l * le;
+    at.vc = (uint16_t*)kv->v + (size_t)l * le;
+    at.block_table = kv->block_table;
+    at.prefix_len = prefix_len;
+    at.B = B;
+    at.W = W;
+    at.Hq = m->n_heads;
+    at.Hkv = m->n_kv_heads;
+    at.num_blocks = kv->num_blocks;
+    at.max_blocks = kv->max_blocks;
+    at.cap = std::min(max_len, kv->max_blocks * kBlock);
+    at.pages_per_split = fp.pps;
+    at.max_splits = fp.runs;
+    at.part_o = s.part_o;
+    at.part_ml = s.part_ml;
+    at.out_apack = s.apack_o;
+    at.nqp = s.nqp;
+    at.causal = m->window_mask == LA_MASK_CAUSAL;
+    at.causal_rows = causal_rows;
+    at.window_len = window_len;
+    at.bt_div = 1;
+    f.T = T;
+    f.H = H;
+    f.HQ = HQ;
+    f.h = s.h;
+    f.parts = carry->pending ? s.parts : nullptr;
+    f.n_parts = carry->pending;
+    f.in_norm = L.in_norm;
+    f.eps = m->rms_eps;
+    f.xpack = s.apack;
+    f.ss_part = s.front_ss;
+    size_t wb, sb;
+    weight_storage(&L.qkv, &wb, &sb);
+    f.wqkv = L.qkv.data;
+    f.wqkv_bytes = (uint32_t)wb;
+    f.qkv_bias = L.qkv_bias;
+    f.rope = s.rope;
+    f.flags = s.flags;
+    weight_storage(&L.o, &wb, &sb);
+    f.wo = L.o.data;
+    f.wo_bytes = (uint32_t)wb;
+    f.post_norm = L.post_norm;
+    f.gpack = s.apack;
+    f.ss = s.ss;
+    f.n_qkv_tiles = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim / 16;
+    f.n_o_tiles = H / 16;
+    f.n_items = fp.items;
+    f.runs = fp.runs;
+    f.sync = s.sync;
+    f.epoch = l + 1;
+    f.err = s.err;
+    LA_TRY(launch_front(f, fp.grid, st));
+    carry->pending = 0;
+    carry->packed = false;
+  } else {
 
   // input operand: h (+ pending partial sums), RMSNorm, pack, unless the
   // previous projection already packed it
@@ -354,7 +459,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   carry->packed = false;
 
   // QKV + bias + RoPE + K/V write
-  GemmArgs g = base_gemm(&L.qkv, T);
+  g = base_gemm(&L.qkv, T);
   g.apack = s.apack;
   g.asum = s.asum;
   if (in_packed) {
@@ -419,19 +524,22 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true, nullptr, 0, nullptr,
                         st)) != LA_OK)
       return rs;
+  }
 
   const int F = m->inter;
   if (!int4 && T <= 32) {
-    // O projection: h += attn . Wo^T, h * post_norm packed for gate/up
-    g = base_gemm(&L.o, T);
-    g.apack = s.apack_o;
-    g.residual = s.h;
-    g.y = s.h;
-    g.ldy = H;
-    g.y_apack = s.apack;
-    g.out_gain = L.post_norm;
-    g.ss_out = s.ss;
-    LA_TRY(launch_gemm(g, EPI_STORE, false, st));
+    if (!fp.grid) {
+      // O projection: h += attn . Wo^T, h * post_norm packed for gate/up
+      g = base_gemm(&L.o, T);
+      g.apack = s.apack_o;
+      g.residual = s.h;
+      g.y = s.h;
+      g.ldy = H;
+      g.y_apack = s.apack;
+      g.out_gain = L.post_norm;
+      g.ss_out = s.ss;
+      LA_TRY(launch_gemm(g, EPI_STORE, false, st));
+    }
     // gate/up + 1/rms + SiLU, packed straight into the down operand
     g = base_gemm(&L.gate_up, T);
     g.apack = s.apack;
@@ -531,6 +639,8 @@ PrologueArgs base_prologue(const la_model* m, const la_kv_cache* kv, const int32
   p.max_blocks = kv->max_blocks;
   p.num_blocks = kv->num_blocks;
   p.cap = std::min(max_len, kv->max_blocks * kBlock);
+  p.zero = s.sync;
+  p.n_zero = s.n_sync;
   return p;
 }
 
@@ -923,7 +1033,8 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   if (out_hidden && !aligned16(out_hidden)) return LA_ERR_ARG;
   const size_t need = carve_step(m, B, W, max_len, nullptr, true).bytes;
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
-  const StepWs s = carve_step(m, B, W, max_len, workspace, true);
+  StepWs s = carve_step(m, B, W, max_len, workspace, true);
+  s.err = err;
   const int T = B * W;
   const int H = m->hidden;
 

@@ -1,0 +1,735 @@
+// The front half of a decoder layer for at most 8 window rows, as one
+// persistent launch: input RMSNorm, the QKV projection with bias, RoPE and
+// the bf16 K/V write, the window attention over the paged cache with its
+// log-sum-exp merge, and the O projection with the residual and the packed,
+// post-normed operand of the gate/up projection.
+//
+// Why one launch: at a handful of rows every one of these steps is short and
+// latency bound, and as separate kernels each pays a launch boundary and a
+// full HBM round trip before its first product.  Here everything that does
+// not depend on another step is in flight from the first cycle: the QKV
+// weight tiles, the rows and the pending K-slice sums, and every cache page
+// that holds only keys older than this step.
+//
+// The RMSNorm is folded into the QKV product: the operand is (h + pending
+// sums) * in_norm, split into bf16 hi / lo, and the epilogue scales row r by
+// 1 / rms_r, so packing a slice of K needs nothing from the rest of the row.
+//
+// One workgroup per compute unit (the grid never exceeds the compute units,
+// and all its workgroups are resident together); each takes fixed roles:
+//   QKV tile t:     workgroup t, 8 waves split K, wave 0 runs the epilogue;
+//   O tile t:       workgroup t, after its QKV tile (its O weights load while
+//                   the attention runs);
+//   pack slice p:   the 64 workgroups after the QKV tiles, 32 columns of K
+//                   each: the operand slice and its rows' sums of squares;
+//   attention item: workgroups from the top of the grid, one run of at most
+//                   kFrontMaxRunPages pages of one (sequence, KV head) each,
+//                   the whole run staged in LDS; once every run of the
+//                   (sequence, KV head) has stored its partial result, run r
+//                   merges slice r of the query columns.  (A workgroup may be
+//                   both a pack slice and an item: it packs while its pages
+//                   load.)
+// A step waits for its inputs on flag words in device memory: each producer
+// sets its own word to the launch's epoch (the layer index + 1; the step's
+// prologue zeroes every word), so no two producers write one word and no
+// atomic is needed; a waiter reads the whole array with one vector load per
+// poll.  Everything one workgroup hands another inside the launch is written
+// with agent-scope (cross-XCD coherent) stores, completed (s_waitcnt) before
+// the flag is set.  The pack and O-ready flags, which 160 and 128 workgroups
+// wait on, have a copy per XCD (each waiter polls the copy of its XCD).  Every
+// wait is bounded: a wait that runs out sets LA_DERR_SYNC in the error word and
+// goes on, so the launch always ends.
+#include "la_attn_common.hpp"
+
+namespace la {
+
+namespace {
+
+constexpr int kFrontWaves = 8;
+constexpr int kFrontThreads = kFrontWaves * 64;
+constexpr int kFrontUnits = 8;               // 32-k units per wave (K = 2048)
+constexpr int kFrontK = 2048;
+constexpr int kFrontMaxParts = 4;            // pending K-slice sums read in one pass
+constexpr int kFrontMaxRuns = 16;            // runs of one (sequence, KV head)
+constexpr int kSliceK = kFrontK / kFrontPackSlices;  // columns of one pack slice
+constexpr int kFlagCopies = 8;               // copies of a widely waited flag array (one per XCD)
+constexpr int kSpinLimit = 1 << 21;
+constexpr int kCoherent = 16;                // cache policy of agent-scope coherent buffer accesses
+// Cache policy of loads of what another workgroup wrote in this launch: plain.
+// Every such line is first read here only after its writer's counter moved,
+// the writer stored it through to memory (coherent stores), and the launch
+// starts with no line of the workspace in any XCD's L2 (each launch begins with
+// the L2 invalidation that makes the previous kernels' results visible), so no
+// L2 can hold an older copy of it.
+constexpr int kHandOff = 0;
+constexpr uint32_t kNoRow = 0x80000000u;     // buffer offset past every range: the load reads zeros
+static_assert(kSliceK == 32, "a pack slice is 4 chunks of 8 columns");
+
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// LDS: the attention role's page ring, then the reduction tiles.
+constexpr int kRingBytes = kFrontMaxRunPages * kPageBytes;
+constexpr int kRedOff = kRingBytes;
+constexpr int kOutvOff = kRedOff + kFrontWaves * 64 * 16;
+constexpr int kFrontLds = kOutvOff + 8 * 17 * 4;
+
+__device__ __forceinline__ int ld_flag(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void set_flag(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u16(uint16_t* p, uint32_t v) {
+  __hip_atomic_store((short*)p, (short)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Stores made so far have reached the coherent level.
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ u32x4 pack8(const uint32_t (&x)[8]) {
+  const u32x4 v = {x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16)};
+  return v;
+}
+
+// Flag arrays (ints): pack [kFlagCopies][64] (slice), qkv [Hkv][128] (tile
+// of the head), run [B * Hkv][16] (run), ready [kFlagCopies][128] (item).
+__device__ __forceinline__ int32_t* fl_pack(const FrontArgs& f, int copy) { return f.sync + copy * 64; }
+__device__ __forceinline__ int32_t* fl_qkv(const FrontArgs& f, int g) { return f.sync + kFlagCopies * 64 + g * 128; }
+__device__ __forceinline__ int32_t* fl_run(const FrontArgs& f, int b, int g) {
+  return f.sync + kFlagCopies * 64 + f.at.Hkv * 128 + (b * f.at.Hkv + g) * 16;
+}
+__device__ __forceinline__ int32_t* fl_ready(const FrontArgs& f, int copy) {
+  return f.sync + kFlagCopies * 64 + f.at.Hkv * 128 + f.at.B * f.at.Hkv * 16 + copy * 128;
+}
+
+// The whole workgroup waits until p[0 .. n) (n <= 128) all hold the epoch
+// (wave 0 polls, two words per lane at most).
+__device__ __forceinline__ void wait_flags(const FrontArgs& f, const int32_t* p, int n) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int spins = 0;
+    for (;;) {
+      const int v0 = lane < n ? ld_flag(p + lane) : f.epoch;
+      const int v1 = lane + 64 < n ? ld_flag(p + lane + 64) : f.epoch;
+      if (__builtin_amdgcn_ballot_w64(v0 != f.epoch || v1 != f.epoch) == 0) break;  // uniform
+      if (++spins >= kSpinLimit) {
+        if (lane == 0 && f.err) atomicOr(f.err, LA_DERR_SYNC);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// This wave's 8 weight fragments of tile t of a tiled bf16 weight with K = 2048.
+__device__ __forceinline__ void load_tile_weights(const void* w, uint32_t bytes, int t, int wave, u32x4 (&wf)[kFrontUnits]) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, bytes);
+  constexpr int UT = kFrontK / 32;
+#pragma unroll
+  for (int i = 0; i < kFrontUnits; ++i) {
+    const uint32_t u = (uint32_t)wave * kFrontUnits + i;
+    wf[i] = bload16<kNonTemporal>(rw, (((uint32_t)t * UT + u) * 64 + lane) * 16);
+  }
+}
+
+// The 8 x 16 product tile from this wave's A and weight fragments: partial
+// tiles through LDS, real row r = operand row r (hi) + operand row r + 8 (lo),
+// into outv[8][17].
+__device__ __forceinline__ void tile_reduce(const bf16x8 (&af)[kFrontUnits], const u32x4 (&wf)[kFrontUnits], int wave,
+                                            f32x4* red, float* outv) {
+  const int lane = threadIdx.x & 63;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kFrontUnits; ++i) acc = mfma_16x16x32(af[i], __builtin_bit_cast(bf16x8, wf[i]), acc);
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int lh = (r >> 2) * 16 + c, ll = ((r + 8) >> 2) * 16 + c, e = r & 3;
+    float v = 0.f;
+    for (int w = 0; w < kFrontWaves; ++w) v += red[w * 64 + lh][e] + red[w * 64 + ll][e];
+    outv[r * 17 + c] = v;
+  }
+  __syncthreads();
+}
+
+// 1 / rms of window row ml (rows of lanes 8 ml .. 8 ml + 7 of wave 0): the 64
+// pack slices' sums of squares, 8 per lane, then a fixed butterfly.
+__device__ __forceinline__ float row_inv_rms(const FrontArgs& f, u32x4 s0, u32x4 s1) {
+  float t = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t += __uint_as_float(s0[e]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t += __uint_as_float(s1[e]);
+  t += __shfl_xor(t, 1);
+  t += __shfl_xor(t, 2);
+  t += __shfl_xor(t, 4);
+  return 1.0f / sqrtf(t / (float)f.H + f.eps);
+}
+
+// What the QKV epilogue of tile t needs besides the product, read before the
+// product so that its latency hides behind the weights (wave 0, lane (row
+// ml = lane / 8, column c = lane % 8)): the bias, the RoPE rotation and, for
+// K and V tiles, where the row's two values go in the cache (null: not written).
+struct QkvEpi {
+  float b1, b2;
+  float2 cs;
+  uint16_t* p1;
+  uint16_t* p2;
+};
+
+__device__ QkvEpi qkv_epi_prepare(const FrontArgs& f, int t) {
+  const AttnArgs& a = f.at;
+  const int lane = threadIdx.x & 63;
+  const int head = t >> 3, sub = t & 7;
+  const int ml = lane >> 3, c = lane & 7;
+  const int i = sub * 8 + c;
+  const int r1 = head * kHeadDim + i, r2 = r1 + 64;
+  QkvEpi e;
+  e.b1 = e.b2 = 0.f;
+  e.cs = make_float2(1.f, 0.f);
+  e.p1 = e.p2 = nullptr;
+  if (ml >= f.T) return e;
+  if (f.qkv_bias) {
+    e.b1 = bf16_to_f32(f.qkv_bias[r1]);
+    e.b2 = bf16_to_f32(f.qkv_bias[r2]);
+  }
+  if (head < a.Hq + a.Hkv) e.cs = f.rope[(size_t)ml * 64 + i];
+  if (head < a.Hq) return e;
+  const int b = ml / a.W, j = ml - b * a.W;
+  const int pos = a.prefix_len[b] + j;
+  if ((f.flags && f.flags[ml]) || pos < 0 || pos >= a.max_blocks * kBlock) return e;
+  const int blk = a.block_table[(size_t)b * a.max_blocks + pos / kBlock];
+  if (blk < 0 || blk >= a.num_blocks) return e;
+  const int slot = pos % kBlock;
+  if (head < a.Hq + a.Hkv) {
+    uint16_t* kp = const_cast<uint16_t*>(a.kc) + (((size_t)blk * a.Hkv + (head - a.Hq)) * kBlock + slot) * kHeadDim;
+    e.p1 = kp + i;
+    e.p2 = kp + i + 64;
+  } else {
+    uint16_t* vp = const_cast<uint16_t*>(a.vc) + ((size_t)blk * a.Hkv + (head - a.Hq - a.Hkv)) * kHeadDim * kBlock;
+    e.p1 = vp + (size_t)i * kBlock + slot;
+    e.p2 = vp + (size_t)(i + 64) * kBlock + slot;
+  }
+  return e;
+}
+
+// QKV epilogue of tile t (wave 0): 1 / rms, bias, RoPE, q (coherent stores)
+// and the window's bf16 K/V written to the cache (coherent stores).
+__device__ void qkv_epilogue(const FrontArgs& f, int t, const float* outv, float inv, const QkvEpi& e) {
+  const AttnArgs& a = f.at;
+  const int lane = threadIdx.x & 63;
+  const int head = t >> 3, sub = t & 7;
+  const int ml = lane >> 3, c = lane & 7;
+  if (ml >= f.T) return;
+  const int i = sub * 8 + c;
+  const int r1 = head * kHeadDim + i, r2 = r1 + 64;
+  float x1 = outv[ml * 17 + c] * inv + e.b1, x2 = outv[ml * 17 + c + 8] * inv + e.b2;
+  if (head < a.Hq + a.Hkv) {
+    const float y1 = x1 * e.cs.x - x2 * e.cs.y, y2 = x2 * e.cs.x + x1 * e.cs.y;
+    x1 = y1;
+    x2 = y2;
+  }
+  if (head < a.Hq) {
+    float* q = const_cast<float*>(a.q) + (size_t)ml * a.Hq * kHeadDim;
+    st_f32(q + r1, x1);
+    st_f32(q + r2, x2);
+    return;
+  }
+  if (e.p1) {
+    st_u16(e.p1, f32_to_bf16_rne(x1));
+    st_u16(e.p2, f32_to_bf16_rne(x2));
+  }
+}
+
+// KV head g of QKV tile t and its index among the (G + 2) * 8 tiles g's
+// attention waits for: the G query heads' tiles, then K's, then V's.
+__device__ __forceinline__ int2 tile_kv_slot(const AttnArgs& a, int t) {
+  const int head = t >> 3, sub = t & 7, G = a.Hq / a.Hkv;
+  if (head < a.Hq) return make_int2(head / G, (head % G) * 8 + sub);
+  if (head < a.Hq + a.Hkv) return make_int2(head - a.Hq, G * 8 + sub);
+  return make_int2(head - a.Hq - a.Hkv, (G + 1) * 8 + sub);
+}
+
+// h + the pending K-slice sums (slice order) at columns n of rows ml, read
+// through buffer ranges that end at the last valid byte: rows past T and
+// slices past n_parts read as zeros.
+__device__ __forceinline__ void load_rows(const FrontArgs& f, int ml, int n, float (&x)[1 + kFrontMaxParts]) {
+  const uint32_t row_bytes = (uint32_t)f.H * 4;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(f.h, (uint32_t)f.T * row_bytes);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(f.parts, f.parts ? (uint32_t)f.n_parts * f.T * row_bytes : 0u);
+  const bool live = ml < f.T;
+  x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rh, live ? (uint32_t)ml * row_bytes + n * 4 : kNoRow, 0, 0));
+#pragma unroll
+  for (int s = 0; s < kFrontMaxParts; ++s)
+    x[1 + s] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rp, live ? ((uint32_t)s * f.T + ml) * row_bytes + n * 4 : kNoRow, 0, 0));
+}
+
+// O epilogue of tile t (wave 0): h1 = (h + pending sums) + o, the tile's sums
+// of squares, h1 * post_norm packed.  res: this lane's two residual columns,
+// gain: post_norm at its column.
+__device__ void o_epilogue(const FrontArgs& f, int t, const float (&res)[2][1 + kFrontMaxParts], float gain,
+                           const float* outv) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = lane + it * 64;
+    const int ml = idx >> 4, c = idx & 15;
+    const int n = t * 16 + c;
+    const bool ok = ml < f.T;
+    float v = 0.f;
+    if (ok) {
+      float hv = res[it][0];
+#pragma unroll
+      for (int s = 0; s < kFrontMaxParts; ++s) hv += res[it][1 + s];
+      v = hv + outv[ml * 17 + c];
+      f.h[(size_t)ml * f.H + n] = v;
+    }
+    float q = ok ? v * v : 0.f;
+    q += __shfl_xor(q, 1);
+    q += __shfl_xor(q, 2);
+    q += __shfl_xor(q, 4);
+    q += __shfl_xor(q, 8);
+    if (ok && c == 0) f.ss[(size_t)ml * (f.H / 16) + t] = q;
+    if (ok) {
+      uint32_t hb, lb;
+      split_hi_lo(v * gain, hb, lb);
+      const size_t base = ((size_t)(n >> 3) * 16 + ml) * 8 + (n & 7);
+      f.gpack[base] = (uint16_t)hb;
+      f.gpack[base + 64] = (uint16_t)lb;
+    }
+  }
+}
+
+// Pack slice p (wave 0, lanes 0..31: row lane / 4, chunk 4p + lane % 4):
+// (h + pending sums) * in_norm as bf16 hi (operand row r) and lo (row r + 8),
+// written as one contiguous kilobyte; the rows' sums of squares over the slice
+// into ss_part[row][p].
+__device__ void front_pack(const FrontArgs& f, int p) {
+  const int lane = threadIdx.x & 63;
+  const int r = (lane >> 2) & 7, kc = p * (kSliceK / 8) + (lane & 3);
+  const uint32_t row_bytes = (uint32_t)f.H * 4;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(f.h, (uint32_t)f.T * row_bytes);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(f.parts, f.parts ? (uint32_t)f.n_parts * f.T * row_bytes : 0u);
+  const bool live = r < f.T && lane < 32;
+  const uint32_t oh = live ? (uint32_t)r * row_bytes + (uint32_t)kc * 32 : kNoRow;
+  u32x4 x[1 + kFrontMaxParts][2];
+  x[0][0] = bload16<0>(rh, oh);
+  x[0][1] = bload16<0>(rh, oh + 16);
+#pragma unroll
+  for (int s = 0; s < kFrontMaxParts; ++s) {
+    const uint32_t op = live ? ((uint32_t)s * f.T + r) * row_bytes + (uint32_t)kc * 32 : kNoRow;
+    x[1 + s][0] = bload16<0>(rp, op);
+    x[1 + s][1] = bload16<0>(rp, op + 16);
+  }
+  const uint4 gw = *(const uint4*)(f.in_norm + kc * 8);
+  const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
+  float v[8], ss = 0.f;
+  uint32_t hi[8], lo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = __uint_as_float(x[0][e >> 2][e & 3]);
+#pragma unroll
+    for (int s = 0; s < kFrontMaxParts; ++s) v[e] += __uint_as_float(x[1 + s][e >> 2][e & 3]);
+    ss += v[e] * v[e];
+    split_hi_lo(v[e] * bf16_to_f32((gg[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu), hi[e], lo[e]);
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  if (lane < 32) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(f.xpack, kFrontK / 8 * 256);
+    const uint32_t off = ((uint32_t)kc * 16 + r) * 16;
+    __builtin_amdgcn_raw_buffer_store_b128(pack8(hi), rx, off, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b128(pack8(lo), rx, off + 128, 0, kCoherent);
+    if ((lane & 3) == 0) st_f32(f.ss_part + r * kFrontPackSlices + p, ss);
+  }
+  stores_done();
+  if (lane < kFlagCopies) set_flag(fl_pack(f, lane) + p, f.epoch);
+}
+
+// The projection role of tile t up to its QKV counter: the packed operand
+// (read coherently once every pack slice is in), the product, the epilogue.
+__device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  u32x4 wq[kFrontUnits];
+  load_tile_weights(f.wqkv, f.wqkv_bytes, t, wave, wq);
+  QkvEpi epi;
+  if (wave == 0) epi = qkv_epi_prepare(f, t);
+  wait_flags(f, fl_pack(f, blockIdx.x % kFlagCopies), kFrontPackSlices);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.xpack, kFrontK / 8 * 256);
+  bf16x8 af[kFrontUnits];
+#pragma unroll
+  for (int i = 0; i < kFrontUnits; ++i) {
+    const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kHandOff));
+  }
+  // wave 0: this lane's 8 of the 64 sums of squares of row lane / 8
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(f.ss_part, 8 * kFrontPackSlices * 4);
+  u32x4 s0 = {0u, 0u, 0u, 0u}, s1 = s0;
+  if (wave == 0) {
+    const uint32_t so = (uint32_t)((lane >> 3) * kFrontPackSlices + (lane & 7) * 8) * 4;
+    s0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kHandOff));
+    s1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so + 16, 0, kHandOff));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every request in flight before the first product
+  float* outv = (float*)(smem + kOutvOff);
+  tile_reduce(af, wq, wave, (f32x4*)(smem + kRedOff), outv);
+  if (wave == 0) {
+    qkv_epilogue(f, t, outv, row_inv_rms(f, s0, s1), epi);
+    stores_done();
+    if (lane == 0) {
+      const int2 gs = tile_kv_slot(f.at, t);
+      set_flag(fl_qkv(f, gs.x) + gs.y, f.epoch);
+    }
+  }
+}
+
+// The O role of tile t: waits for every attention item, reads the packed
+// attention output coherently, multiplies, runs the epilogue.
+__device__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits], unsigned char* smem) {
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float res[2][1 + kFrontMaxParts];
+  float gain = 0.f;
+  if (wave == 0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) load_rows(f, (lane + it * 64) >> 4, t * 16 + (lane & 15), res[it]);
+    gain = bf16_to_f32(f.post_norm[t * 16 + (lane & 15)]);
+  }
+  wait_flags(f, fl_ready(f, blockIdx.x % kFlagCopies), f.n_items);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.at.out_apack, kFrontK / 8 * 256);
+  bf16x8 af[kFrontUnits];
+#pragma unroll
+  for (int i = 0; i < kFrontUnits; ++i) {
+    const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kHandOff));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all 8 requests in flight before the first product
+  float* outv = (float*)(smem + kOutvOff);
+  tile_reduce(af, wo, wave, (f32x4*)(smem + kRedOff), outv);
+  if (wave == 0) o_epilogue(f, t, res, gain, outv);
+}
+
+// One attention item: sequence b, KV head g, run r of a.pages_per_split
+// pages.  Pages whose keys all precede the window are copied into LDS at once;
+// the rest (keys this launch writes) after the QKV counter of g.  Waves
+// 0..NQT-1 hold query tiles.  A single-run sequence writes its normalised
+// output; otherwise every run stores its (max, sum, unnormalised O) and, once
+// all runs of (b, g) have, merges slice r of the query columns.
+template <int NQT>
+__device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigned char* ring, int slice) {
+  const AttnArgs& a = f.at;
+  const int lane = threadIdx.x & 63, gl = lane >> 4, rr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.Hq / a.Hkv, NQ = a.W * G;
+  const int kps = a.pages_per_split * kBlock;
+  const int n_keys = attn_keys(a, b);
+  const int nruns = (n_keys + kps - 1) / kps;
+  const int k0 = r * kps;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out_apack, (uint32_t)(a.Hq * kHeadDim / 8) * 256);
+  if (k0 >= n_keys) {
+    if (slice >= 0 && threadIdx.x < 64) front_pack(f, slice);
+    if (n_keys == 0 && r == 0) {
+      // no key at all (a prefix the step flags as invalid): zero output
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int idx = threadIdx.x; idx < NQ * 16; idx += kFrontThreads) {
+        const int qi = idx >> 4, ch = idx & 15;
+        const int wr = qi / G, hg = qi - wr * G;
+        const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + ch * 8;
+        const uint32_t off = ((uint32_t)(col >> 3) * 16 + row) * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(z, ro, off, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(z, ro, off + 128, 0, kCoherent);
+      }
+    }
+    return;  // uniform: this run holds no keys
+  }
+  const int k1 = min(n_keys, k0 + kps);
+  const int npages = (k1 - k0 + kBlock - 1) / kBlock;
+  const int first = k0 / kBlock;
+  int bt = a.block_table[(size_t)b * a.max_blocks + min(first + min(lane, npages - 1), a.max_blocks - 1)];
+  bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
+  const uint32_t cache_bytes = (uint32_t)a.num_blocks * a.Hkv * (kPageBytes / 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc, cache_bytes);
+  // page j: wave w copies 1 KB piece w (pieces 0..3 of K, 4..7 of V^T)
+  auto copy_page = [&](int j, bool coherent) {
+    const int blk = __builtin_amdgcn_readlane(bt, j);
+    const uint32_t base = ((uint32_t)blk * a.Hkv + g) * (kPageBytes / 2);
+    void __attribute__((address_space(3)))* dst =
+        (void __attribute__((address_space(3)))*)(ring + j * kPageBytes + wave * 1024);
+    if (coherent)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, kHandOff);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, 0);
+  };
+  // pages [0, early) hold only keys below the prefix length: written before this launch
+  const int early = min(npages, max(0, (a.prefix_len[b] - k0) / kBlock));
+  // wave 0 packs its slice first (the pack's wait for its own stores would
+  // otherwise also wait for the page copies)
+  if (slice >= 0 && wave == 0) front_pack(f, slice);
+  for (int j = 0; j < early; ++j) copy_page(j, false);
+
+  wait_flags(f, fl_qkv(f, g), (G + 2) * 8);  // q of g's query heads, K and V of g: 8 tiles per head
+
+  // wave (tile, group): query tile wave % NQT, pairs group, group + kGroups, ...
+  constexpr int kGroups = kFrontWaves / NQT;
+  const int tile = wave % NQT, grp = wave / NQT;
+  const bool qw = grp < kGroups;  // waves past kGroups * NQT stay idle
+  const int qi = tile * 16 + rr;
+  bf16x8 qh[4], ql[4];
+  if (qw) {
+    const int qc = qi < NQ ? qi : 0;
+    const int wr = qc / G, hg = qc - wr * G;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * a.W * a.Hq * kHeadDim) * 4);
+    const uint32_t qoff = ((uint32_t)((b * a.W + wr) * a.Hq + g * G + hg) * kHeadDim + gl * 8) * 4;
+    u32x4 xq[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      xq[kb][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128, 0, kHandOff));
+      xq[kb][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128 + 16, 0, kHandOff));
+    }
+    for (int j = early; j < npages; ++j) copy_page(j, true);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_hi_lo(qi < NQ ? __uint_as_float(xq[kb][e >> 2][e & 3]) : 0.f, hi[e], lo[e]);
+      qh[kb] = __builtin_bit_cast(bf16x8, pack8(hi));
+      ql[kb] = __builtin_bit_cast(bf16x8, pack8(lo));
+    }
+  } else {
+    for (int j = early; j < npages; ++j) copy_page(j, true);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces of every page
+  __syncthreads();
+
+  AttnState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int crows = a.causal_rows ? min(max(a.causal_rows[b], 0), a.W) : (a.causal ? a.W : 0);
+  const int wrow = (qi < NQ ? qi : 0) / G;
+  const int kcol = wrow < crows ? max(min(n_keys, a.prefix_len[b] + wrow + 1), min(n_keys, 1)) : n_keys;
+  if (qw) {
+    const int npairs = (npages + 1) >> 1;
+    for (int c = grp; c < npairs; c += kGroups) {
+      PairRegs pr;
+      read_pair(ring + c * kPairBytes, pr);
+      const int p0 = k0 + 2 * c * kBlock;
+      attn_pair(pr, k1 - p0, min(k1, kcol) - p0, qh, ql, st);
+    }
+  }
+  if (kGroups > 1) {
+    // group 0 takes in the other groups' states (group order), through the
+    // ring: every wave is done with the pages
+    __syncthreads();
+    float* gs = (float*)ring;
+    constexpr int kStateFloats = 8 * 4 + 2;
+    if (qw && grp > 0) {
+      float* d = gs + ((grp - 1) * NQT + tile) * kStateFloats * 64 + lane;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[(dt * 4 + e) * 64] = st.acc[dt][e];
+      d[32 * 64] = st.m;
+      d[33 * 64] = st.l;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      float M = st.m;
+#pragma unroll
+      for (int g2 = 1; g2 < kGroups; ++g2) M = fmaxf(M, gs[((g2 - 1) * NQT + tile) * kStateFloats * 64 + 32 * 64 + lane]);
+      const float w0 = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
+      st.l *= w0;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= w0;
+#pragma unroll
+      for (int g2 = 1; g2 < kGroups; ++g2) {
+        const float* sp = gs + ((g2 - 1) * NQT + tile) * kStateFloats * 64 + lane;
+        const float m2 = sp[32 * 64];
+        const float w = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
+        st.l += w * sp[33 * 64];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.acc[dt][e] += w * sp[(dt * 4 + e) * 64];
+      }
+      st.m = M;
+    }
+  }
+  const bool ow = grp == 0;  // the waves that hold the run's state
+  float lsum = st.l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (nruns == 1) {
+    if (ow) {
+      const float inv = 1.f / lsum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = st.acc[dt][e] * inv;
+          v[4 + e] = __shfl_xor(v[e], 16);
+        }
+        if (qi < NQ && (gl & 1) == 0) {
+          const int wr = qi / G, hg = qi - wr * G;
+          const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + dt * 16 + 4 * gl;
+          uint32_t hi[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split_hi_lo(v[e], hi[e], lo[e]);
+          const uint32_t off = ((uint32_t)(col >> 3) * 16 + row) * 16;
+          __builtin_amdgcn_raw_buffer_store_b128(pack8(hi), ro, off, 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b128(pack8(lo), ro, off + 128, 0, kCoherent);
+        }
+      }
+    }
+    return;
+  }
+
+  // partial result of this run
+  const size_t base = ((size_t)b * a.Hkv + g) * a.max_splits;
+  const uint32_t units = (uint32_t)(a.B * a.Hkv * a.max_splits * a.nqp);
+  const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, units * 8);
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(a.part_o, units * kHeadDim * 4);
+  if (ow) {
+    const uint32_t u = (uint32_t)((base + r) * a.nqp + qi);
+    if (gl == 0) {
+      const u32x2 ml2 = {__float_as_uint(st.m), __float_as_uint(lsum)};
+      __builtin_amdgcn_raw_buffer_store_b64(ml2, rml, u * 8, 0, kCoherent);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[dt]), rpo, (u * kHeadDim + dt * 16 + 4 * gl) * 4,
+                                            0, kCoherent);
+  }
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) set_flag(fl_run(f, b, g) + r, f.epoch);
+  wait_flags(f, fl_run(f, b, g), nruns);
+
+  // merge of query columns [qa, qb): thread (column, 4-dim chunk c4) combines
+  // every run in run order, normalises, packs (with its neighbouring chunk)
+  const int qa = r * NQ / nruns, qb = (r + 1) * NQ / nruns;
+  for (int idx = threadIdx.x; idx < (qb - qa) * 32; idx += kFrontThreads) {
+    const int q = qa + (idx >> 5), c4 = idx & 31;
+    float mm[kFrontMaxRuns], ll[kFrontMaxRuns];
+    f32x4 o[kFrontMaxRuns];
+#pragma unroll
+    for (int s = 0; s < kFrontMaxRuns; ++s) {
+      const uint32_t u = (uint32_t)((base + min(s, nruns - 1)) * a.nqp + q);
+      const u32x2 ml2 = __builtin_amdgcn_raw_buffer_load_b64(rml, u * 8, 0, kHandOff);
+      mm[s] = __uint_as_float(ml2[0]);
+      ll[s] = __uint_as_float(ml2[1]);
+      o[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpo, (u * kHeadDim + 4 * c4) * 4, 0, kHandOff));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every run's request in flight at once
+    float nm = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kFrontMaxRuns; ++s)
+      if (s < nruns) nm = fmaxf(nm, mm[s]);
+    float den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kFrontMaxRuns; ++s) {
+      if (s < nruns) {
+        const float w = mm[s] == -INFINITY ? 0.f : exp2f(mm[s] - nm);
+        den += w * ll[s];
+        num += w * o[s];
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    float v[4] = {num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+    float w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w4[e] = __shfl_xor(v[e], 1);  // the neighbouring chunk
+    if ((c4 & 1) == 0) {
+      const float xv[8] = {v[0], v[1], v[2], v[3], w4[0], w4[1], w4[2], w4[3]};
+      const int wr = q / G, hg = q - wr * G;
+      const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + 4 * c4;
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_hi_lo(xv[e], hi[e], lo[e]);
+      const uint32_t off = ((uint32_t)(col >> 3) * 16 + row) * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(hi), ro, off, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(lo), ro, off + 128, 0, kCoherent);
+    }
+  }
+}
+
+}  // namespace
+
+template <int NQT>
+__global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const AttnArgs& a = f.at;
+  const int w = blockIdx.x, G = gridDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = G - 1 - w;
+  const int slice = w - f.n_qkv_tiles;
+
+  if (w < f.n_qkv_tiles) {
+    front_qkv(f, w, smem);
+    if (w < f.n_o_tiles) {
+      // the O weights stream in while the attention runs
+      u32x4 wo[kFrontUnits];
+      load_tile_weights(f.wo, f.wo_bytes, w, wave, wo);
+      front_o(f, w, wo, smem);
+    }
+  } else {
+    const bool has_item = item >= 0 && item < f.n_items;
+    const bool has_slice = slice < kFrontPackSlices;
+    if (has_item) {
+      // the host keeps these workgroups free of QKV and O tiles
+      const int per_b = a.Hkv * f.runs;
+      const int b = item / per_b, g = (item - b * per_b) / f.runs, r = item % f.runs;
+      front_attention<NQT>(f, b, g, r, smem, has_slice ? slice : -1);
+      stores_done();
+      __syncthreads();
+      if (threadIdx.x < kFlagCopies) set_flag(fl_ready(f, threadIdx.x) + item, f.epoch);
+    } else if (has_slice && wave == 0) {
+      front_pack(f, slice);
+    }
+  }
+}
+
+template <int NQT>
+static hipError_t launch_front_t(const FrontArgs& f, int grid, hipStream_t s) {
+  static bool attr = false;  // allow the LDS beyond the static default once per instantiation
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_front<NQT>, hipFuncAttributeMaxDynamicSharedMemorySize, kFrontLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(k_front<NQT>, dim3(grid), dim3(kFrontThreads), kFrontLds, s, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
+  if (f.runs > kFrontMaxRuns || f.n_parts > kFrontMaxParts || f.at.pages_per_split > kFrontMaxRunPages ||
+      f.H != kFrontK || f.HQ != kFrontK || f.T > 8 || f.n_o_tiles > f.n_qkv_tiles ||
+      f.n_qkv_tiles + kFrontPackSlices > grid || f.n_qkv_tiles + f.n_items > grid || f.n_items > 128 || f.epoch <= 0)
+    return hipErrorInvalidValue;
+  switch (f.at.nqp / 16) {
+    case 1: return launch_front_t<1>(f, grid, s);
+    case 2: return launch_front_t<2>(f, grid, s);
+    case 3: return launch_front_t<3>(f, grid, s);
+    case 4: return launch_front_t<4>(f, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace la

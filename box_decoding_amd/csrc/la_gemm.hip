@@ -823,7 +823,7 @@ __global__ __launch_bounds__(1024) void k_argmax_reduce(const float* amax, int n
 
 // ---------------------------------------------------------------- host side
 
-static int cu_count() {
+int cu_count() {
   static int n = 0;
   if (!n) {
     int dev = 0, v = 0;

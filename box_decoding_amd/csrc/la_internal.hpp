@@ -113,6 +113,8 @@ struct PrologueArgs {
   const int32_t* window_len;  // [B] real window rows (nullable)
   const int32_t* block_table;
   int max_blocks, num_blocks, cap;
+  int32_t* zero;             // nullable: n_zero words cleared (the front kernel's counters)
+  int n_zero;
   // prefill: ids / embeds hold in_w rows per sequence (rows j >= in_w of the
   // W are padding: zero input, no error); a negative id takes its row of
   // embeds ([B][in_w][H] fp32, nullable)
@@ -187,6 +189,42 @@ struct SampleArgs {
   int32_t* err;                // nullable
 };
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+
+// The front half of a layer (RMSNorm + pack, QKV, attention, O) for up to 8
+// window rows with bf16 tiled weights and K = 2048, as one persistent launch
+// (la_front.hip).
+struct FrontArgs {
+  AttnArgs at;                // the attention (q, kc, vc, partials, out_apack = the O operand)
+  int T, H, HQ;               // window rows, hidden (QKV K, O N), heads x 128 (O K)
+  float* h;                   // [T][H] residual stream, updated in place
+  const float* parts;         // [n_parts][T][H] K-slice sums still to add (nullable)
+  int n_parts;
+  const uint16_t* in_norm;
+  float eps;
+  uint16_t* xpack;            // packed QKV operand (one row tile): (h + sums) * in_norm
+  float* ss_part;             // [8][kFrontPackSlices] sums of squares of the rows per pack slice
+  const void* wqkv;           // tiled QKV weight
+  uint32_t wqkv_bytes;
+  const uint16_t* qkv_bias;   // nullable
+  const float2* rope;         // [T][64]
+  const int32_t* flags;       // [T] nonzero: the row writes no K/V
+  const void* wo;             // tiled O weight
+  uint32_t wo_bytes;
+  const uint16_t* post_norm;
+  uint16_t* gpack;            // packed gate/up operand: h1 * post_norm
+  float* ss;                  // [T][H / 16] per-tile sums of squares of h1
+  int n_qkv_tiles, n_o_tiles, n_items, runs;  // attention items = B * Hkv * runs
+  int32_t* sync;              // flag words (the step's prologue zeroes them)
+  int epoch;                  // the value this launch's flags take: layer index + 1
+  int32_t* err;               // nullable
+};
+// Pages of one attention run of the front-half launch (the whole run sits in
+// LDS), and the slices its operand packing splits K = 2048 into.
+constexpr int kFrontMaxRunPages = 12;
+constexpr int kFrontPackSlices = 64;
+hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s);
+// Compute units of the current device (256 when the query fails).
+int cu_count();
 
 // attention split planning
 void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits);

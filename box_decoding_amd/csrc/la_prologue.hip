@@ -22,6 +22,8 @@ __device__ __forceinline__ bool prologue_id_bad(const PrologueArgs& a, int id) {
 __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  if (a.zero && t == 0)
+    for (int i = tid; i < a.n_zero; i += 256) a.zero[i] = 0;
   int id_bad = 0;
   if (a.ids) {
     const int src = prologue_src(a, t);

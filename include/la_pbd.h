@@ -145,7 +145,9 @@ enum {
   LA_DERR_TOKEN_ID = 1,   /* a window id outside [0, vocab) */
   LA_DERR_CAPACITY = 2,   /* P_b + W exceeds max_len or max_blocks * 16 */
   LA_DERR_BLOCK_ID = 4,   /* a block-table entry needed by the step is outside [0, num_blocks) */
-  LA_DERR_WINDOW = 8      /* re-fed window: window_len[b] outside 1..W or causal_rows[b] outside 0..window_len[b] */
+  LA_DERR_WINDOW = 8,     /* re-fed window: window_len[b] outside 1..W or causal_rows[b] outside 0..window_len[b] */
+  LA_DERR_SYNC = 16       /* a step's persistent front-half launch timed out waiting for its own
+                             workgroups (the device did not run them all together); results invalid */
 };
 
 /* la_pbd_step epilogue selectors for la_wgemm. */
