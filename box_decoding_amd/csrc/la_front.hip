@@ -55,13 +55,6 @@ constexpr int kSliceK = kFrontK / kFrontPackSlices;  // columns of one pack slic
 constexpr int kFlagCopies = 8;               // copies of a widely waited flag array (one per XCD)
 constexpr int kSpinLimit = 1 << 21;
 constexpr int kCoherent = 16;                // cache policy of agent-scope coherent buffer accesses
-// Cache policy of loads of what another workgroup wrote in this launch: plain.
-// Every such line is first read here only after its writer's counter moved,
-// the writer stored it through to memory (coherent stores), and the launch
-// starts with no line of the workspace in any XCD's L2 (each launch begins with
-// the L2 invalidation that makes the previous kernels' results visible), so no
-// L2 can hold an older copy of it.
-constexpr int kHandOff = 0;
 constexpr uint32_t kNoRow = 0x80000000u;     // buffer offset past every range: the load reads zeros
 static_assert(kSliceK == 32, "a pack slice is 4 chunks of 8 columns");
 
@@ -372,15 +365,15 @@ __device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
 #pragma unroll
   for (int i = 0; i < kFrontUnits; ++i) {
     const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
-    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kHandOff));
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kCoherent));
   }
   // wave 0: this lane's 8 of the 64 sums of squares of row lane / 8
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(f.ss_part, 8 * kFrontPackSlices * 4);
   u32x4 s0 = {0u, 0u, 0u, 0u}, s1 = s0;
   if (wave == 0) {
     const uint32_t so = (uint32_t)((lane >> 3) * kFrontPackSlices + (lane & 7) * 8) * 4;
-    s0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kHandOff));
-    s1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so + 16, 0, kHandOff));
+    s0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kCoherent));
+    s1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so + 16, 0, kCoherent));
   }
   __builtin_amdgcn_sched_barrier(0);  // every request in flight before the first product
   float* outv = (float*)(smem + kOutvOff);
@@ -413,7 +406,7 @@ __device__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits
 #pragma unroll
   for (int i = 0; i < kFrontUnits; ++i) {
     const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
-    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kHandOff));
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kCoherent));
   }
   __builtin_amdgcn_sched_barrier(0);  // all 8 requests in flight before the first product
   float* outv = (float*)(smem + kOutvOff);
@@ -469,7 +462,7 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
     void __attribute__((address_space(3)))* dst =
         (void __attribute__((address_space(3)))*)(ring + j * kPageBytes + wave * 1024);
     if (coherent)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, kHandOff);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, kCoherent);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, 0);
   };
@@ -496,8 +489,8 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
     u32x4 xq[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      xq[kb][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128, 0, kHandOff));
-      xq[kb][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128 + 16, 0, kHandOff));
+      xq[kb][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128, 0, kCoherent));
+      xq[kb][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128 + 16, 0, kCoherent));
     }
     for (int j = early; j < npages; ++j) copy_page(j, true);
     __builtin_amdgcn_sched_barrier(0);
@@ -631,10 +624,10 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
 #pragma unroll
     for (int s = 0; s < kFrontMaxRuns; ++s) {
       const uint32_t u = (uint32_t)((base + min(s, nruns - 1)) * a.nqp + q);
-      const u32x2 ml2 = __builtin_amdgcn_raw_buffer_load_b64(rml, u * 8, 0, kHandOff);
+      const u32x2 ml2 = __builtin_amdgcn_raw_buffer_load_b64(rml, u * 8, 0, kCoherent);
       mm[s] = __uint_as_float(ml2[0]);
       ll[s] = __uint_as_float(ml2[1]);
-      o[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpo, (u * kHeadDim + 4 * c4) * 4, 0, kHandOff));
+      o[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpo, (u * kHeadDim + 4 * c4) * 4, 0, kCoherent));
     }
     __builtin_amdgcn_sched_barrier(0);  // every run's request in flight at once
     float nm = -INFINITY;
