@@ -23,6 +23,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CAL_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic_step_b1_p1280.json")
+FRONT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "front_traffic_step_b1_p1280.json")
 METRIC = "PBD window steps/sec (≈boxes/sec) at batch 1 and 32; achieved HBM GB/s vs peak"
 
 
@@ -44,33 +45,71 @@ def gate_up_bytes(w, T, H, F):
     return weight_bytes(w) + T * H * 4 + T * F * 4
 
 
-def kernel_source_digest():
-    """Digest of the small-batch GEMM kernel's sources: counter-based traffic
-    is only reported for the kernel it was measured on."""
+# The kernels with counter-based traffic: (name in the profile, sources it is
+# built from, summary file).
+TRAFFIC_KERNELS = {
+    "gate_up": ("k_gemm<1, false, 1, 2>", ("la_gemm.hip", "la_gemm_common.hpp", "la_common.hpp"),
+                TRAFFIC_FILE, "k_gemm<1, false, 1, 2> (gate/up + SiLU, LDS-staged ring)"),
+    "front": ("k_front<", ("la_front.hip", "la_attn_common.hpp", "la_internal.hpp", "la_common.hpp"),
+              FRONT_TRAFFIC_FILE, "k_front<3> (front half of a layer: RMSNorm, QKV, attention, O)"),
+}
+
+
+def front_bytes(lay, dims, prefix_len, W):
+    """Algorithmic bytes of one front-half launch (a layer's attention block):
+    the QKV and O weights, the QKV bias and the two norm gains once; the K/V of
+    every key read once and the window's K/V written once; the rows h read
+    once; h1, its per-tile sums of squares and the packed gate/up operand (bf16
+    hi + lo) written once.  What the launch hands on between its own steps (q,
+    the packed QKV operand, the attention partials and output) is not counted."""
+    T = len(prefix_len) * W
+    H = dims.hidden
+    total = weight_bytes(lay["qkv"]) + weight_bytes(lay["o"])
+    total += (lay["in_norm"].numel() + lay["post_norm"].numel()) * 2
+    if lay.get("qkv_bias") is not None:
+        total += lay["qkv_bias"].numel() * 2
+    kv_tok = 2 * dims.n_kv_heads * dims.head_dim * 2
+    keys = int(sum(int(p) + W for p in prefix_len.tolist()))
+    total += keys * kv_tok + T * kv_tok
+    total += T * H * 4
+    total += T * H * 4 + T * (H // 16) * 4 + 2 * T * H * 2
+    return total
+
+
+def kernel_source_digest(which="gate_up"):
+    """Digest of a kernel's sources: counter-based traffic is only reported for
+    the kernel it was measured on."""
     h = hashlib.sha256()
-    for name in ("la_gemm.hip", "la_gemm_common.hpp", "la_common.hpp"):
+    for name in TRAFFIC_KERNELS[which][1]:
         with open(os.path.join(ROOT, "box_decoding_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed counter summary, or None
-    when it was taken on another version of the kernel."""
+def measured_traffic(which="gate_up"):
+    """HBM bytes per launch from the committed counter summary, or None when it
+    was taken on another version of the kernel."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_KERNELS[which][2]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest(which):
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
-def pmc_summary(fetch_db, write_db, out_path):
+def pmc_summary(fetch_db, write_db):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE) into HBM bytes per gate/up launch, each counter scaled by what
-    it reads for the calibration copy of CAL_COPY_BYTES."""
+    WRITE_SIZE) into HBM bytes per launch of the gate/up GEMM and of the
+    front-half launch, each counter scaled by what it reads for the
+    calibration copy of CAL_COPY_BYTES."""
+    for which in TRAFFIC_KERNELS:
+        pmc_summary_one(fetch_db, write_db, which)
+
+
+def pmc_summary_one(fetch_db, write_db, which):
+    pattern, _, out_path, label = TRAFFIC_KERNELS[which]
     import sqlite3
 
     def per_kernel(db, counter):
@@ -83,7 +122,7 @@ def pmc_summary(fetch_db, write_db, out_path):
 
     def summarize(db, counter):
         rows = per_kernel(db, counter)
-        gu = [v for name, _, v in rows if "k_gemm<1, false, 1, 2>" in name]
+        gu = [v for name, _, v in rows if pattern in name]
         # the calibration copy is the runtime's copy kernel moving CAL_COPY_BYTES,
         # the largest such dispatch of the run
         copies = [v for name, _, v in rows if name.startswith("__amd_rocclr_copyBuffer")]
@@ -94,8 +133,8 @@ def pmc_summary(fetch_db, write_db, out_path):
     f_bytes, f_factor, n_f, f_cal = summarize(fetch_db, "FETCH_SIZE")
     w_bytes, w_factor, n_w, w_cal = summarize(write_db, "WRITE_SIZE")
     rec = {
-        "kernel": "k_gemm<1, false, 1, 2> (gate/up + SiLU, LDS-staged ring)",
-        "kernel_source_sha256_16": kernel_source_digest(),
+        "kernel": label,
+        "kernel_source_sha256_16": kernel_source_digest(which),
         "fetch_bytes_per_launch": round(f_bytes), "write_bytes_per_launch": round(w_bytes),
         "traffic_bytes_per_launch": round(f_bytes + w_bytes),
         "fetch_scale": f_factor, "write_scale": w_factor,
@@ -600,7 +639,7 @@ def main():
                     help="summarise two rocprofv3 --pmc runs of this script into the traffic file")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1])
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the PBD step here is a single-GPU path "
@@ -668,11 +707,31 @@ def main():
     log(f"bench: {ms_step:.3f} ms/step (wall {wall_ms:.3f} ms), "
         f"{steps_per_s:.1f} steps/s, {sbytes / ms_step / 1e6:.0f} GB/s algorithmic")
 
-    # Dominant kernel: the gate/up projection with the SiLU epilogue (58% of a
-    # layer's weight bytes), the GEMM alone on a pre-packed operand.  Timed with
-    # HIP events on the stream the library launches on (torch's current
-    # stream), cycling through the 36 layers' weights so that they stream from
-    # HBM.
+    # Dominant kernel: the front half of each layer (one persistent launch at
+    # up to 8 bf16 rows: RMSNorm, QKV, attention, O; the workloads with more
+    # rows run it as separate kernels, and their line reports the gate/up GEMM
+    # below), timed live with HIP events
+    # the library records around every layer's attention block on its stream
+    # (eager steps on the same inputs: the window's K/V land in the same slots).
+    bev = B.BlockEvents(d.n_layers)
+    block_ms = []
+    for r in range(4):
+        B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, out_gap=out_gap,
+                   block_events=bev)
+        torch.cuda.synchronize()
+        if r:
+            block_ms.extend(bev.ms())
+    front_us = sum(block_ms) / len(block_ms) * 1e3
+    fbytes = sum(front_bytes(lay, d, P, w.window) for lay in model["layers"]) / d.n_layers
+    front_gbps = fbytes / (front_us * 1e-6) / 1e9
+    front_launch = w.batch * w.window <= 8 and w.wfmt == "bf16" and not args.row_major
+    log(f"bench: attention block (front-half launch) {front_us:.1f} us, {front_gbps:.0f} GB/s")
+
+    # The weight-streaming kernel with the most bytes: the gate/up projection
+    # with the SiLU epilogue (58% of a layer's weight bytes), the GEMM alone on
+    # a pre-packed operand.  Timed with HIP events on the stream the library
+    # launches on (torch's current stream), cycling through the 36 layers'
+    # weights so that they stream from HBM.
     F, H = d.inter, d.hidden
     T = w.batch * w.window
     xin = torch.randn((T, H), device=dev, generator=torch.Generator(device=dev).manual_seed(1))
@@ -700,9 +759,20 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst
-    # the counters were taken on the batch-1 tiled workload's gate/up launch
-    traffic = measured_traffic() if args.workload == "step_b1_p1280" and not args.row_major else None
+    # the counters were taken on the batch-1 tiled workload's launches
+    b1 = args.workload == "step_b1_p1280" and not args.row_major
+    traffic = measured_traffic("gate_up") if b1 else None
+    front_traffic = measured_traffic("front") if b1 else None
 
+    roof_gu = {"bound": "hbm", "kernel": "gate_up GEMM + SiLU (la_wgemm_packed)",
+               "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+               "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+               "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes}
+    roof_front = {"bound": "hbm",
+                  "kernel": "front half of a layer, one persistent launch (k_front: RMSNorm, QKV, attention, O)",
+                  "achieved": round(front_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": round(front_gbps / HBM_PEAK_GBPS, 4), "traffic": front_traffic,
+                  "launch_us": round(front_us, 2), "bytes_per_launch": round(fbytes)}
     result = {
         "metric": METRIC,
         "value": round(steps_per_s, 3),
@@ -725,11 +795,10 @@ def main():
         "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
         "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
         "step_bytes": sbytes,
-        "roofline": {"bound": "hbm", "kernel": "gate_up GEMM + SiLU (la_wgemm_packed)",
-                     "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes},
+        "roofline": roof_front if front_launch else roof_gu,
     }
+    if front_launch:
+        result["roofline_gate_up"] = roof_gu
     if args.workload == "step_b1_p1280" and not args.no_batch32 and not args.row_major:
         # the metric's second batch size: the same model, 32 ragged sequences
         del cache, dc

@@ -67,7 +67,7 @@ class LaSampling(ctypes.Structure):
 class LaStepOpts(ctypes.Structure):
     _fields_ = [("causal_rows", c_void_p), ("window_len", c_void_p), ("rep_bits", c_void_p),
                 ("rep_words", c_int32), ("rep_penalty", c_float),
-                ("sampling", POINTER(LaSampling))]
+                ("sampling", POINTER(LaSampling)), ("block_events", c_void_p)]
 
 
 class LaError(RuntimeError):
@@ -430,17 +430,53 @@ def step_workspace_bytes(model: DeviceModel, B: int, W: int, max_len: int) -> in
     return int(load().la_pbd_step_workspace(ctypes.byref(model.struct), B, W, max_len))
 
 
+class BlockEvents:
+    """2 * n_layers HIP events for la_step_opts.block_events: the time of each
+    layer's attention block in a step (ms() after the step has finished)."""
+
+    def __init__(self, n_layers: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventElapsedTime.argtypes = [POINTER(c_float), c_void_p, c_void_p]
+        self.n = 2 * n_layers
+        self.events = (c_void_p * self.n)()
+        for i in range(self.n):
+            h = c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise LaError("hipEventCreate failed")
+            self.events[i] = h
+        self.address = ctypes.addressof(self.events)
+
+    def ms(self) -> list:
+        """Elapsed milliseconds of each layer's attention block."""
+        out = []
+        for l in range(self.n // 2):
+            t = c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(t), self.events[2 * l], self.events[2 * l + 1]) != 0:
+                raise LaError("hipEventElapsedTime failed")
+            out.append(t.value)
+        return out
+
+    def __del__(self):
+        hip = getattr(self, "_hip", None)
+        if hip is not None:
+            for h in getattr(self, "events", []):
+                if h:
+                    hip.hipEventDestroy(c_void_p(h))
+
+
 def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
              prefix_len: torch.Tensor, max_len: int, want_gap: bool = True,
              want_hidden: bool = False, ws: Optional[Workspace] = None, out_ids=None, out_gap=None,
              err: Optional[torch.Tensor] = None, causal_rows: Optional[torch.Tensor] = None,
              window_len: Optional[torch.Tensor] = None, rep_bits: Optional[torch.Tensor] = None,
-             rep_penalty: float = 1.0, sampling: Optional["Sampling"] = None):
+             rep_penalty: float = 1.0, sampling: Optional["Sampling"] = None,
+             block_events: Optional["BlockEvents"] = None):
     """One PBD window step; returns (ids [B,W], gap [B,W] or None, hidden or None).
     causal_rows / window_len (int32 [B]) make it a re-fed window step; rep_bits
     (int32 [B, words] vocabulary bitmaps) applies the repetition penalty;
     sampling (a Sampling) replaces the argmax by the sampled selection (gap
-    then holds the selected logit minus the row's largest)."""
+    then holds the selected logit minus the row's largest); block_events (a
+    BlockEvents) times every layer's attention block."""
     lib = load()
     _require_cuda(window_ids, prefix_len, err, causal_rows, window_len, rep_bits)
     B, W = window_ids.shape
@@ -454,13 +490,16 @@ def pbd_step(model: DeviceModel, cache: DeviceCache, window_ids: torch.Tensor,
     if need == 0:
         raise LaError("la_pbd_step_workspace rejected the model or shape")
     buf = _ws(ws).get(need)
-    if rep_bits is not None or sampling is not None:
+    if rep_bits is not None or sampling is not None or block_events is not None:
         smp = None
         if sampling is not None:
             smp = sampling.struct(B * W, model.dims.vocab, dev)
+        if block_events is not None and block_events.n != 2 * model.dims.n_layers:
+            raise LaError("block_events must hold 2 events per layer")
         opts = LaStepOpts(_ptr(causal_rows), _ptr(window_len), _ptr(rep_bits),
                           0 if rep_bits is None else rep_bits.shape[1], float(rep_penalty),
-                          None if smp is None else ctypes.pointer(smp))
+                          None if smp is None else ctypes.pointer(smp),
+                          None if block_events is None else block_events.address)
         _check(lib.la_pbd_step_opts(ctypes.byref(model.struct), ctypes.byref(cache.struct),
                                     _ptr(window_ids), _ptr(prefix_len), ctypes.byref(opts), B, W,
                                     max_len, _ptr(ids), _ptr(gap), _ptr(hid), _ptr(buf), buf.numel(),

@@ -377,7 +377,8 @@ FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max
 la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32_t* prefix_len,
                     const int32_t* causal_rows, const int32_t* window_len, int B, int W,
                     int max_len, const StepWs& s, float* attn_out, Carry* carry,
-                    const uint16_t* next_gain, hipStream_t st, const AttnView* av = nullptr) {
+                    const uint16_t* next_gain, hipStream_t st, const AttnView* av = nullptr,
+                    const hipEvent_t* ev = nullptr) {
   const la_layer& L = m->layers[l];
   const int T = B * W;
   const int H = m->hidden, HQ = m->n_heads * m->head_dim;
@@ -386,6 +387,8 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   la_status rs;
   const FrontPlan fp = plan_front(m, L, B, W, max_len, s, av, attn_out, carry->pending);
   GemmArgs g;
+  // timing events around the attention block (input norm .. O projection)
+  if (ev) LA_TRY(hipEventRecord(ev[0], st));
   if (fp.grid) {
     FrontArgs f;
     memset(&f, 0, sizeof(f));
@@ -540,6 +543,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
       g.ss_out = s.ss;
       LA_TRY(launch_gemm(g, EPI_STORE, false, st));
     }
+    if (ev) LA_TRY(hipEventRecord(ev[1], st));
     // gate/up + 1/rms + SiLU, packed straight into the down operand
     g = base_gemm(&L.gate_up, T);
     g.apack = s.apack;
@@ -590,6 +594,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
 
   // h += O partial sums; RMSNorm; gate/up + SiLU (bf16: packed straight into
   // the down operand)
+  if (ev) LA_TRY(hipEventRecord(ev[1], st));
   if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
                       ks_o > 1 ? ks_o : 0, ks_o > 1 ? s.h : nullptr, st)) != LA_OK)
     return rs;
@@ -1056,8 +1061,9 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
     // packing below, not folded into the lm_head's epilogue)
     const uint16_t* next_gain = l + 1 < m->n_layers ? m->layers[l + 1].in_norm
                                                     : (int4 || sampled ? nullptr : m->final_norm);
+    const hipEvent_t* ev = opts && opts->block_events ? opts->block_events + 2 * l : nullptr;
     st = run_layer(m, l, kv, prefix_len, causal_rows, window_len, B, W, max_len, s, nullptr, &carry,
-                   next_gain, stream);
+                   next_gain, stream, nullptr, ev);
     if (st != LA_OK) return st;
   }
   if (!carry.packed) {

@@ -372,7 +372,11 @@ la_status la_sample_logits(const float* logits, int32_t M, int32_t V, int32_t ld
  *    over the step's logits (with the repetition bitmaps when given).  Then
  *    out_gap (nullable) receives each row's selected logit minus its largest
  *    instead of the top-2 gap.  LA_ERR_ARG when sampling->logits is NULL or
- *    misaligned, or the parameters are out of range. */
+ *    misaligned, or the parameters are out of range;
+ *  - block_events: NULL, or 2 * n_layers events (created by the caller) for
+ *    timing: block_events[2 l] is recorded on the stream before layer l's
+ *    attention block (input RMSNorm, QKV, attention, O projection) and
+ *    block_events[2 l + 1] after it. */
 typedef struct {
   const int32_t* causal_rows;
   const int32_t* window_len;
@@ -380,6 +384,7 @@ typedef struct {
   int32_t rep_words;
   float rep_penalty;
   const la_sampling* sampling;
+  const hipEvent_t* block_events;
 } la_step_opts;
 la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32_t* window_ids,
                            const int32_t* prefix_len, const la_step_opts* opts, int32_t B, int32_t W,
