@@ -63,7 +63,7 @@ class Workload:
     batch: int
     window: int
     prefix: tuple  # ("fixed", P) or ("uniform", lo, hi)
-    wfmt: str = "bf16"  # "bf16" or "int4"
+    wfmt: str = "bf16"  # "bf16", "int4" or "w8a8"
     steps: int = 1      # consecutive window steps (emission loop)
     lm_head: bool = True
     model_seed: int = 0
@@ -89,6 +89,11 @@ WORKLOADS = {
     "emit_b16_p2048_x40": Workload("emit_b16_p2048_x40", QWEN25_3B, batch=16, window=6,
                                    prefix=("fixed", 2048), steps=40, model_seed=0,
                                    input_seed=5),
+    # w8a8 weights (int8 codes, per-channel scales, int8 activations per row),
+    # the RK3588 conversion's format, at the batch-1 shape.
+    "step_w8a8_b1_p1280": Workload("step_w8a8_b1_p1280", QWEN25_3B, batch=1, window=6,
+                                   prefix=("fixed", 1280), wfmt="w8a8", model_seed=7,
+                                   input_seed=2),
     # Long-context probe: batch 1, prefix 32768.
     "probe_b1_p32768": Workload("probe_b1_p32768", QWEN25_3B, batch=1, window=6,
                                 prefix=("fixed", 32768), model_seed=0, input_seed=6),
@@ -146,10 +151,22 @@ def int4_tensor(rows, k, group, device, *seed):
     return packed, _bits16(s)
 
 
+def int8_tensor(rows, k, device, *seed):
+    """int8 codes uniform on -127..127 and one fp32 scale per row on
+    [2e-4, 4e-4] (weights of about 0.02 standard deviation)."""
+    g = _gen(device, *seed)
+    q = torch.randint(-127, 128, (rows, k), generator=g, device=device, dtype=torch.int8)
+    s = 2e-4 + 2e-4 * torch.rand((rows,), generator=g, device=device, dtype=torch.float32)
+    return q, s
+
+
 def _weight(fmt, n, k, device, *seed):
     if fmt == "bf16":
         return {"fmt": "bf16", "n": n, "k": k, "group": 0,
                 "data": normal_bf16((n, k), 0.02, 0.0, device, *seed), "scales": None}
+    if fmt == "w8a8":
+        q, s = int8_tensor(n, k, device, *seed)
+        return {"fmt": "w8a8", "n": n, "k": k, "group": 0, "data": q, "scales": s}
     packed, scales = int4_tensor(n, k, 128, device, *seed)
     return {"fmt": "int4", "n": n, "k": k, "group": 128, "data": packed, "scales": scales}
 
@@ -162,7 +179,9 @@ def make_model(dims: ModelDims, wfmt: str = "bf16", seed: int = 0, device="cpu",
     ([Hq*D + 2*Hkv*D, H]); ``gate_up`` is [gate | up] stacked ([2F, H]);
     ``o`` is [H, Hq*D]; ``down`` is [H, F].  The lm_head is tied to the
     embedding in bf16; in INT4 the embedding is a group-32 copy and the lm_head
-    a group-128 copy of the tied matrix.
+    a group-128 copy of the tied matrix; in w8a8 the embedding stays bf16 and
+    the lm_head is an int8 matrix with its own codes and per-row scales (it
+    stands for the quantised copy of the tied matrix).
     """
     d = dims
     H, F = d.hidden, d.inter
@@ -180,11 +199,14 @@ def make_model(dims: ModelDims, wfmt: str = "bf16", seed: int = 0, device="cpu",
         layers.append(lay)
     model = {"dims": d, "wfmt": wfmt, "layers": layers,
              "final_norm": normal_bf16((H,), 0.02, 1.0, device, seed, 1000, 1)}
-    if wfmt == "bf16":
+    if wfmt in ("bf16", "w8a8"):
         model["embed"] = {"fmt": "bf16", "n": d.vocab, "k": H, "group": 0,
                           "data": normal_bf16((d.vocab, H), 0.02, 0.0, device, seed, 1000, 2),
                           "scales": None}
         model["lm_head"] = None  # tied: the embedding matrix itself
+        if wfmt == "w8a8":
+            q, s = int8_tensor(d.vocab, H, device, seed, 1000, 6)
+            model["lm_head"] = {"fmt": "w8a8", "n": d.vocab, "k": H, "group": 0, "data": q, "scales": s}
     else:
         # Tied matrix: one set of INT4 codes, read with group-32 scales by the
         # gather and with group-128 scales by the lm_head.

@@ -24,6 +24,13 @@ float32), with every stored input decoded exactly:
   embedding; g = 128 along the input dim for the linears, section "Files").
 * Greedy selection: the per-position argmax of the logits (Jetson page, Part 1
   section 1.4: temperature 0, no sampling), lowest index on exact ties.
+* w8a8 weights, the RK3588 conversion's format ("LocateAnything-3B for RK3588
+  (RKLLM + RKNN)", "Files" and "How it differs from the original", item 3,
+  which name w8a8 and give no formula).  Read plainly: int8 weight codes with
+  one fp32 scale per output channel; the activations entering each linear
+  layer are quantised per row, s = max|x| / 127 and q = round-half-even(x / s)
+  clamped to [-127, 127], decided in float32 (a zero row has s = 0, q = 0); the
+  integer products are summed exactly and scaled by both scales.
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes): one key bound P+W shared by every window row; the window's
@@ -46,6 +53,7 @@ import numpy as np
 
 __all__ = [
     "bf16_to_float", "fp16_to_float", "round_to_bf16_bits", "int4_dequant", "decode_weight",
+    "quantize_rows_int8", "linear",
     "embed_rows", "rmsnorm", "silu", "rope_angles", "rope_apply", "window_attention",
     "repetition_penalty", "logits_of",
     "cache_read", "decoder_layer", "lm_head_argmax", "pbd_step", "emission_commit", "pbd_emission_loop",
@@ -99,12 +107,41 @@ def int4_dequant(packed, scales, group, dtype=np.float64):
 
 
 def decode_weight(w, rows=None, dtype=np.float64):
-    """Decode a weight descriptor (bf16 or INT4) to a float matrix [n, k]."""
+    """Decode a weight descriptor (bf16, INT4 or w8a8) to a float matrix [n, k]."""
     data = w["data"] if rows is None else w["data"][rows]
     if w["fmt"] == "bf16":
         return bf16_to_float(data, dtype)
     scales = w["scales"] if rows is None else w["scales"][rows]
+    if w["fmt"] == "w8a8":
+        return np.asarray(data).view(np.int8).astype(dtype) * np.asarray(scales, dtype=np.float32).astype(dtype)[:, None]
     return int4_dequant(data, scales, int(w["group"]), dtype)
+
+
+def quantize_rows_int8(x):
+    """Per-row symmetric int8 quantisation of activations (the w8a8 reading in
+    the header), every decision in float32: s = max|x| / 127, q = round half to
+    even of x / s (float32 division), clamped to [-127, 127]; a row of zeros
+    gets s = 0 and q = 0.  Returns (q int64 [..., K], s float32 [...])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    s = (np.max(np.abs(x32), axis=-1) / np.float32(127)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    q = np.rint((x32 / safe[..., None]).astype(np.float32))
+    q = np.where(s[..., None] > 0, np.clip(q, -127, 127), 0)
+    return q.astype(np.int64), s
+
+
+def linear(x, w, rows=None, dtype=np.float64):
+    """x . W^T for a weight descriptor (rows: a subset of W's rows).  bf16 and
+    INT4: the exactly decoded weight.  w8a8: the rows of x quantised to int8
+    (quantize_rows_int8), the integer dot products summed exactly, then scaled
+    by the row's scale and the output channel's scale."""
+    if w["fmt"] != "w8a8":
+        return np.asarray(x, dtype=dtype) @ decode_weight(w, rows=rows, dtype=dtype).T
+    q, s = quantize_rows_int8(x)
+    data = w["data"] if rows is None else w["data"][rows]
+    sw = w["scales"] if rows is None else w["scales"][rows]
+    acc = q @ np.asarray(data).view(np.int8).astype(np.int64).T
+    return acc.astype(dtype) * s.astype(dtype)[..., None] * np.asarray(sw, dtype=np.float32).astype(dtype)
 
 
 def embed_rows(ids, emb, dtype=np.float64):
@@ -246,7 +283,7 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
     assert h.shape == (T, H)
 
     a = rmsnorm(h, bf16_to_float(lay["in_norm"], dtype), eps)
-    qkv = a @ decode_weight(lay["qkv"], dtype=dtype).T
+    qkv = linear(a, lay["qkv"], dtype=dtype)
     if lay.get("qkv_bias") is not None:
         qkv = qkv + bf16_to_float(lay["qkv_bias"], dtype)
     q = qkv[:, :Hq * D].reshape(T, Hq, D)
@@ -273,11 +310,11 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
             causal_rows=0 if causal_rows is None else int(causal_rows[b]),
             window_len=None if window_len is None else int(window_len[b]))
 
-    h1 = h + o.reshape(T, Hq * D) @ decode_weight(lay["o"], dtype=dtype).T
+    h1 = h + linear(o.reshape(T, Hq * D), lay["o"], dtype=dtype)
     a2 = rmsnorm(h1, bf16_to_float(lay["post_norm"], dtype), eps)
-    gu = a2 @ decode_weight(lay["gate_up"], dtype=dtype).T
+    gu = linear(a2, lay["gate_up"], dtype=dtype)
     m = silu(gu[:, :F]) * gu[:, F:]
-    h2 = h1 + m @ decode_weight(lay["down"], dtype=dtype).T
+    h2 = h1 + linear(m, lay["down"], dtype=dtype)
     if parts is not None:
         parts.update(q=q, k=k, v=v, attn=o.reshape(T, Hq * D), h_mid=h1, mlp=m, qkv=qkv)
     return h2, k_bits, v_bits
@@ -302,8 +339,8 @@ def logits_of(f, lm, ids, dtype=np.float64, rep_sets=None, rep_penalty=1.0):
     checked for validity rather than exactly."""
     f = np.asarray(f, dtype=dtype)
     ids = np.asarray(ids).reshape(-1).astype(np.int64)
-    E = decode_weight(lm, rows=ids, dtype=dtype)          # [T, H]
-    z = np.einsum("th,th->t", f, E)
+    z = np.array([linear(f[t:t + 1], lm, rows=ids[t:t + 1], dtype=dtype)[0, 0] for t in range(len(ids))],
+                 dtype=dtype)
     if rep_sets is not None:
         for t in range(len(ids)):
             if np.isin(ids[t], np.asarray(rep_sets[t])):
@@ -330,8 +367,7 @@ def lm_head_argmax(f, lm, chunk=8192, dtype=np.float64, rep_sets=None, rep_penal
         sets = [np.unique(np.asarray(x, dtype=np.int64)) for x in rep_sets]
     for v0 in range(0, V, chunk):
         v1 = min(V, v0 + chunk)
-        E = decode_weight(lm, rows=np.arange(v0, v1), dtype=dtype)
-        logits = f @ E.T                               # [T, v1-v0]
+        logits = linear(f, lm, rows=np.arange(v0, v1), dtype=dtype)   # [T, v1-v0]
         if sets is not None:
             for t in range(T):
                 idx = sets[t][(sets[t] >= v0) & (sets[t] < v1)] - v0

@@ -881,3 +881,79 @@ def test_window_kv_override():
     assert np.abs(other["hidden"] - ref["hidden"]).max() > 0
     # the layer's own rounding is still what it returns
     np.testing.assert_array_equal(other["kv"][0][1], ref["kv"][0][1])
+
+
+# ---------------------------------------------------------------- w8a8
+
+def test_quantize_rows_int8_hand_worked():
+    # max |x| = 127 gives s = 1 exactly, so x / s is exact and the rounding is
+    # visible: halves go to the even integer (-63.5 -> -64, 31.5 -> 32,
+    # 2.5 -> 2, -0.5 -> 0), not away from zero (-64, 32, 3, -1)
+    q, s = O.quantize_rows_int8(np.array([[127.0, -63.5, 31.5, 2.5, -0.5, 0.0]]))
+    assert s.dtype == np.float32 and s.tolist() == [1.0]
+    assert q.tolist() == [[127, -64, 32, 2, 0, 0]]
+    # a negative maximum: s = 254 / 127 = 2; 127 / 2 = 63.5 -> 64
+    q, s = O.quantize_rows_int8(np.array([[-254.0, 127.0, 1.0]]))
+    assert s.tolist() == [2.0] and q.tolist() == [[-127, 64, 0]]
+    # a zero row: s = 0, every code 0 (no division by zero)
+    q, s = O.quantize_rows_int8(np.zeros((2, 5)))
+    assert s.tolist() == [0.0, 0.0] and not q.any()
+    # the decision is taken in float32: x / s of the float32 operands
+    x = np.array([[1.0, 1.0 / 3.0, -0.7]])
+    q, s = O.quantize_rows_int8(x)
+    s32 = np.float32(1.0) / np.float32(127)
+    assert s[0] == s32
+    assert q[0, 1] == int(np.rint(np.float32(np.float32(1.0 / 3.0) / s32)))
+
+
+def _w8a8_weight(rng, n, k):
+    q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    s = rng.uniform(2e-4, 4e-4, size=n).astype(np.float32)
+    return {"fmt": "w8a8", "n": n, "k": k, "group": 0, "data": q, "scales": s}
+
+
+def test_w8a8_linear_scales_the_integer_products():
+    """The integer sum scaled by both scales equals the product of the
+    dequantised operands (two different computations of the same number)."""
+    rng = np.random.default_rng(11)
+    w = _w8a8_weight(rng, 24, 96)
+    x = rng.standard_normal((5, 96))
+    y = O.linear(x, w)
+    qx, sx = O.quantize_rows_int8(x)
+    xd = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+    ref = xd @ O.decode_weight(w).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-15)
+    # a subset of output channels (the lm_head's chunks) gives the same columns
+    rows = np.array([3, 7, 20])
+    np.testing.assert_allclose(O.linear(x, w, rows=rows), y[:, rows], rtol=1e-15)
+
+
+def test_w8a8_linear_error_bound_and_exact_grid():
+    rng = np.random.default_rng(12)
+    w = _w8a8_weight(rng, 16, 128)
+    Wd = O.decode_weight(w)
+    x = rng.standard_normal((7, 128))
+    y = O.linear(x, w)
+    _, sx = O.quantize_rows_int8(x)
+    # rounding moves each activation by at most s / 2 (plus float32 slack)
+    bound = (sx.astype(np.float64)[:, None] * 0.5 * (1 + 1e-6) + 1e-7 * np.abs(x).max(axis=1)[:, None]) \
+        * np.abs(Wd).sum(axis=1)[None, :]
+    assert np.all(np.abs(y - x @ Wd.T) <= bound)
+    # activations already on the grid (s a power of two, max |q| = 127) are kept exactly
+    q = rng.integers(-127, 128, size=(3, 128)).astype(np.float64)
+    q[:, 0] = 127
+    xg = q * 2.0 ** -5
+    np.testing.assert_allclose(O.linear(xg, w), xg @ Wd.T, rtol=1e-12)
+
+
+def test_w8a8_layer_zero_weights_is_identity():
+    d = synth.ModelDims(n_layers=1, vocab=64, hidden=256, n_heads=2, n_kv_heads=1, inter=512)
+    m = synth.to_numpy_tree(synth.make_model(d, "w8a8", 1, "cpu"))
+    lay = m["layers"][0]
+    for k in ("qkv", "o", "gate_up", "down"):
+        lay[k]["data"] = np.zeros_like(lay[k]["data"])
+    P = torch.tensor([9], dtype=torch.int32)
+    cache = synth.to_numpy_tree(synth.make_cache(d, P, 6, seed=2, device="cpu"))
+    h = np.random.default_rng(3).standard_normal((6, 256))
+    out, _, _ = O.decoder_layer(h, lay, d, cache, 0, P.numpy(), 6)
+    np.testing.assert_array_equal(out, h)
