@@ -36,13 +36,17 @@ def weight_bytes(w):
     n, k = int(w["n"]), int(w["k"])
     if w["fmt"] == "bf16":
         return n * k * 2
+    if w["fmt"] == "w8a8":
+        return n * k + n * 4
     return n * k // 2 + n * (k // int(w["group"])) * 2
 
 
 def gate_up_bytes(w, T, H, F):
     """Algorithmic bytes of one gate/up launch: the weights once, the packed
-    operand (bf16 hi + lo of T rows) once, the fp32 output once."""
-    return weight_bytes(w) + T * H * 4 + T * F * 4
+    operand (bf16 hi + lo of T rows; w8a8: int8 rows and their scales) once,
+    the fp32 output once."""
+    op = T * H + T * 4 if w["fmt"] == "w8a8" else T * H * 4
+    return weight_bytes(w) + op + T * F * 4
 
 
 # The kernels with counter-based traffic: (name in the profile, sources it is
@@ -543,12 +547,14 @@ def layer_leg(B, synth, torch, dev, timed, args, copies=5):
             "hbm_gbps": round(lbytes / us / 1e3, 1), "hbm_frac": round(lbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
 
-def int4_leg(B, synth, torch, dev, stream, timed, args):
-    """The INT4 weight-only step at batch 8, prefix 1280 (group-128 linears and
-    lm_head, group-32 embedding gathered on the device), as graph replays."""
-    w = synth.WORKLOADS["step_int4_b8_p1280"]
+def int4_leg(B, synth, torch, dev, stream, timed, args, name="step_int4_b8_p1280"):
+    """A quantised-weight step as graph replays: the INT4 weight-only step at
+    batch 8, prefix 1280 (group-128 linears and lm_head, group-32 embedding
+    gathered on the device), or (name step_w8a8_b1_p1280) the w8a8 step at
+    batch 1 (int8 linears and lm_head, int8 activations per row)."""
+    w = synth.WORKLOADS[name]
     d = w.dims
-    log("bench: INT4 batch-8 leg")
+    log(f"bench: {w.wfmt} batch-{w.batch} leg")
     model = B.pack_model(synth.make_model(d, w.wfmt, w.model_seed, dev))
     dm = B.DeviceModel(model)
     P = synth.draw_prefix_lens(w)
@@ -568,7 +574,7 @@ def int4_leg(B, synth, torch, dev, stream, timed, args):
     # its dominant kernel: gate/up with the SiLU epilogue at 48 rows
     T, F, H = w.batch * w.window, d.inter, d.hidden
     xin = torch.randn((T, H), device=dev, generator=torch.Generator(device=dev).manual_seed(1))
-    packed = B.pack_rows(xin, "int4", norm_gain=model["layers"][0]["post_norm"])
+    packed = B.pack_rows(xin, w.wfmt, norm_gain=model["layers"][0]["post_norm"])
     yout = torch.empty((T, F), dtype=torch.float32, device=dev)
     for l in range(3):
         B.wgemm_packed(packed, T, model["layers"][l]["gate_up"], silu_gate=True, out=yout)
@@ -580,11 +586,11 @@ def int4_leg(B, synth, torch, dev, stream, timed, args):
 
     k_ms = timed(gemm, 1)[0] / reps
     gu_bytes = gate_up_bytes(model["layers"][0]["gate_up"], T, H, F)
-    log(f"bench: INT4 batch 8: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; gate_up "
+    log(f"bench: {w.wfmt} batch {w.batch}: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; gate_up "
         f"{k_ms * 1e3:.1f} us, {gu_bytes / k_ms / 1e6:.0f} GB/s")
     del graph, cache, dc, ws, dm, model
     torch.cuda.synchronize()
-    return {"workload": w.name, "batch": w.batch, "window": w.window, "prefix": int(P.max()), "weights": "int4",
+    return {"workload": w.name, "batch": w.batch, "window": w.window, "prefix": int(P.max()), "weights": w.wfmt,
             "steps": steps, "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
             "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
             "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
@@ -815,6 +821,7 @@ def main():
         torch.cuda.synchronize()
         result["layer_b1_p512"] = layer_leg(B, synth, torch, dev, timed, args)
         result["int4_b8"] = int4_leg(B, synth, torch, dev, stream, timed, args)
+        result["w8a8_b1"] = int4_leg(B, synth, torch, dev, stream, timed, args, name="step_w8a8_b1_p1280")
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_layers)

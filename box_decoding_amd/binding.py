@@ -17,7 +17,8 @@ from . import synth
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla_pbd.so")
 
-LA_W_BF16, LA_W_INT4 = 0, 1
+LA_W_BF16, LA_W_INT4, LA_W_W8A8 = 0, 1, 2
+_FMT = {"bf16": LA_W_BF16, "int4": LA_W_INT4, "w8a8": LA_W_W8A8}
 LA_EPI_NONE, LA_EPI_SILU_GATE = 0, 1
 LA_DERR_TOKEN_ID, LA_DERR_CAPACITY, LA_DERR_BLOCK_ID, LA_DERR_WINDOW = 1, 2, 4, 8
 LA_LAYOUT_ROWS, LA_LAYOUT_TILED, LA_LAYOUT_TILED_GU, LA_LAYOUT_TILED_QKV = 0, 1, 2, 3
@@ -183,7 +184,7 @@ def _require_cuda(*ts):
 def weight_desc(w: dict) -> LaWeight:
     if w is None:
         return LaWeight(LA_W_BF16, 0, 0, 0, 0, 0, None, None)
-    fmt = LA_W_BF16 if w["fmt"] == "bf16" else LA_W_INT4
+    fmt = _FMT[w["fmt"]]
     _require_cuda(w["data"], w.get("scales"))
     return LaWeight(fmt, int(w["n"]), int(w["k"]), int(w.get("group") or 0),
                     int(w.get("layout", LA_LAYOUT_ROWS)), 0, _ptr(w["data"]), _ptr(w.get("scales")))
@@ -209,7 +210,8 @@ def pack_weight(w: dict, layout: int) -> dict:
 
 def pack_model(model: dict) -> dict:
     """Model dict whose linears and lm_head use the tiled layouts (the INT4
-    group-32 embedding stays row-major: it is only gathered)."""
+    group-32 embedding stays row-major: it is only gathered; a w8a8 model's
+    bf16 embedding is tiled too, the gather reads either)."""
     out = dict(model)
     layers = []
     for lay in model["layers"]:
@@ -220,9 +222,9 @@ def pack_model(model: dict) -> dict:
         nl["down"] = pack_weight(lay["down"], LA_LAYOUT_TILED)
         layers.append(nl)
     out["layers"] = layers
-    if model["wfmt"] == "bf16":
-        out["embed"] = pack_weight(model["embed"], LA_LAYOUT_TILED)  # tied lm_head
-    else:
+    if model["wfmt"] in ("bf16", "w8a8"):
+        out["embed"] = pack_weight(model["embed"], LA_LAYOUT_TILED)  # tied lm_head (bf16)
+    if model["wfmt"] != "bf16":
         out["lm_head"] = pack_weight(model["lm_head"], LA_LAYOUT_TILED)
     return out
 
@@ -331,7 +333,7 @@ def pack_rows(x: torch.Tensor, fmt: str = "bf16", norm_gain=None, eps: float = 1
         raise LaError(f"no packed layout for M={M}, K={K}")
     buf = out if out is not None else torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(lib.la_pack_rows(_ptr(x), M, K, _ptr(norm_gain), eps,
-                            LA_W_INT4 if fmt == "int4" else LA_W_BF16, _ptr(buf), buf.numel(),
+                            _FMT[fmt], _ptr(buf), buf.numel(),
                             _stream()), "la_pack_rows")
     return buf
 

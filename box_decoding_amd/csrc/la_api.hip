@@ -34,6 +34,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Bytes of a weight's data and INT4 scales in its layout.
 void weight_storage(const la_weight* w, size_t* data, size_t* scales) {
   const bool int4 = w->fmt == LA_W_INT4;
+  if (w->fmt == LA_W_W8A8) {
+    // int8 codes (tiled: 16-row tiles, zero past n) and fp32 scales per row
+    const size_t rows = w->layout == LA_LAYOUT_ROWS ? (size_t)w->n
+                        : w->layout == LA_LAYOUT_TILED_GU ? (size_t)(w->n / 2 + 7) / 8 * 16
+                                                          : (size_t)(w->n + 15) / 16 * 16;
+    *data = rows * (size_t)w->k;
+    *scales = (size_t)w->n * 4;
+    return;
+  }
   if (w->layout == LA_LAYOUT_ROWS) {
     *data = int4 ? (size_t)w->n * (w->k / 2) : (size_t)w->n * w->k * 2;
     *scales = int4 && w->group > 0 ? (size_t)w->n * (w->k / w->group) * 2 : 0;
@@ -60,6 +69,7 @@ la_status attention_entry(const float* q, const la_kv_cache* kv, int32_t layer, 
                           int32_t B, int32_t W, int32_t max_len, float* out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+// allow_int4: the quantised formats (INT4 with group int4_group, w8a8) are accepted.
 la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int int4_group,
                        int tiled) {
   if (!w || !w->data) return LA_ERR_ARG;
@@ -73,6 +83,11 @@ la_status check_weight(const la_weight* w, int n, int k, bool allow_int4, int in
   if (w->layout != LA_LAYOUT_ROWS && w->layout != tiled) return LA_ERR_UNSUPPORTED;
   if (w->layout != LA_LAYOUT_ROWS && k % 128) return LA_ERR_SHAPE;
   if (w->fmt == LA_W_BF16) return LA_OK;
+  if (w->fmt == LA_W_W8A8) {
+    if (!allow_int4) return LA_ERR_UNSUPPORTED;
+    if (!w->scales || k % 64) return LA_ERR_SHAPE;
+    return LA_OK;
+  }
   if (w->fmt != LA_W_INT4) return LA_ERR_ARG;
   if (!allow_int4) return LA_ERR_UNSUPPORTED;
   if (!w->scales || w->group != int4_group || k % int4_group) return LA_ERR_SHAPE;
@@ -90,6 +105,7 @@ la_status check_gemm_weight(const la_weight* w, int tiled) {
 // Launch plans as launch_gemm makes them: up to 32 rows the small-M kernel,
 // beyond that the large-M kernel (whose first launch fixes the plan).
 int gemm_parts(int M, const la_weight* w, int epi) {
+  if (w->fmt == LA_W_W8A8) return plan_gemm_w8(M, w->n, w->k, epi, false).grid;
   const bool int4 = w->fmt == LA_W_INT4;
   if (use_big_gemm(M, w->k, int4, epi))
     return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, epi, false).grid;
@@ -97,6 +113,7 @@ int gemm_parts(int M, const la_weight* w, int epi) {
 }
 
 int gemm_ksplit(int M, const la_weight* w) {
+  if (w->fmt == LA_W_W8A8) return plan_gemm_w8(M, w->n, w->k, EPI_STORE, true).ksplit;
   const bool int4 = w->fmt == LA_W_INT4;
   if (use_big_gemm(M, w->k, int4, EPI_STORE))
     return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_STORE, true).ksplit;
@@ -106,6 +123,7 @@ int gemm_ksplit(int M, const la_weight* w) {
 // K slices of the QKV projection: past 32 rows it writes slice sums that a
 // finishing kernel turns into q and the window's K/V (0: no slice buffer).
 int qkv_ksplit(int M, const la_weight* w) {
+  if (w->fmt == LA_W_W8A8) return 0;
   const bool int4 = w->fmt == LA_W_INT4;
   if (!use_big_gemm(M, w->k, int4, EPI_QKV)) return 0;
   return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_QKV, true).ksplit;
@@ -208,7 +226,7 @@ la_status check_model(const la_model* m) {
   const int H = m->hidden, HQ = m->n_heads * m->head_dim;
   const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
   const int fmt = m->layers[0].qkv.fmt;
-  if (fmt != LA_W_BF16 && fmt != LA_W_INT4) return LA_ERR_ARG;
+  if (fmt != LA_W_BF16 && fmt != LA_W_INT4 && fmt != LA_W_W8A8) return LA_ERR_ARG;
   if (m->window_mask != LA_MASK_BIDIRECTIONAL && m->window_mask != LA_MASK_CAUSAL) return LA_ERR_ARG;
   for (int l = 0; l < m->n_layers; ++l) {
     const la_layer& L = m->layers[l];
@@ -230,6 +248,12 @@ la_status check_model(const la_model* m) {
     if (m->lm_head.data) {
       if ((st = check_weight(&m->lm_head, m->vocab, H, false, 0, LA_LAYOUT_TILED)) != LA_OK) return st;
     }
+  } else if (fmt == LA_W_W8A8) {
+    // bf16 embedding; the lm_head is the w8a8 copy of the tied matrix
+    la_status st = check_weight(&m->embed, m->vocab, H, false, 0, LA_LAYOUT_TILED);
+    if (st != LA_OK) return st;
+    if (!m->lm_head.data || m->lm_head.fmt != LA_W_W8A8) return LA_ERR_ARG;
+    if ((st = check_weight(&m->lm_head, m->vocab, H, true, 0, LA_LAYOUT_TILED)) != LA_OK) return st;
   } else {
     la_status st = check_weight(&m->embed, m->vocab, H, true, 32, -1);
     if (st != LA_OK) return st;
@@ -284,8 +308,9 @@ GemmArgs base_gemm(const la_weight* w, int M) {
 
 // Pack fp32 rows (h plus pending partial sums, RMSNorm'd when gain != NULL)
 // into the matrix-core operand; the summed rows are written back to h_out.
+// fmt: the consumer's weight format (LA_W_*), which fixes the operand's form.
 la_status pack_rows(const float* x, int ldx, int M, int K, const uint16_t* gain, float eps,
-                    uint16_t* apack, float* asum, bool int4, const float* parts, int n_parts,
+                    uint16_t* apack, float* asum, int fmt, const float* parts, int n_parts,
                     float* h_out, hipStream_t st) {
   PackArgs p;
   memset(&p, 0, sizeof(p));
@@ -297,7 +322,8 @@ la_status pack_rows(const float* x, int ldx, int M, int K, const uint16_t* gain,
   p.eps = eps;
   p.apack = apack;
   p.asum = asum;
-  p.int4 = int4;
+  p.int4 = fmt == LA_W_INT4;
+  p.w8 = fmt == LA_W_W8A8;
   p.parts = parts;
   p.n_parts = parts ? n_parts : 0;
   p.h_out = h_out;
@@ -306,12 +332,12 @@ la_status pack_rows(const float* x, int ldx, int M, int K, const uint16_t* gain,
 }
 
 la_status gemm_from_rows(GemmArgs g, const float* x, int ldx, const uint16_t* gain, float eps,
-                         uint16_t* apack, float* asum, int epi, bool int4, hipStream_t st) {
-  la_status rs = pack_rows(x, ldx, g.M, g.K, gain, eps, apack, asum, int4, nullptr, 0, nullptr, st);
+                         uint16_t* apack, float* asum, int epi, int fmt, hipStream_t st) {
+  la_status rs = pack_rows(x, ldx, g.M, g.K, gain, eps, apack, asum, fmt, nullptr, 0, nullptr, st);
   if (rs != LA_OK) return rs;
   g.apack = apack;
   g.asum = asum;
-  LA_TRY(launch_gemm(g, epi, int4, st));
+  LA_TRY(launch_gemm(g, epi, fmt, st));
   return LA_OK;
 }
 
@@ -382,7 +408,10 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   const la_layer& L = m->layers[l];
   const int T = B * W;
   const int H = m->hidden, HQ = m->n_heads * m->head_dim;
-  const bool int4 = L.qkv.fmt == LA_W_INT4;
+  // quantised weights (INT4, w8a8): every GEMM writes fp32 and a packing kernel
+  // prepares the next operand (a w8a8 operand's per-row scale needs the whole row)
+  const int wf = L.qkv.fmt;
+  const bool quant = wf != LA_W_BF16;
   const size_t le = kv_layer_elems(kv, m);
   la_status rs;
   const FrontPlan fp = plan_front(m, L, B, W, max_len, s, av, attn_out, carry->pending);
@@ -454,7 +483,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   // previous projection already packed it
   const bool in_packed = carry->packed;
   if (!in_packed) {
-    if ((rs = pack_rows(s.h, H, T, H, L.in_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+    if ((rs = pack_rows(s.h, H, T, H, L.in_norm, m->rms_eps, s.apack, s.asum, wf, s.parts,
                         carry->pending, carry->pending ? s.h : nullptr, st)) != LA_OK)
       return rs;
   }
@@ -485,7 +514,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   g.kc = (uint16_t*)kv->k + (size_t)l * le;
   g.vc = (uint16_t*)kv->v + (size_t)l * le;
   if (qkv_ksplit(T, &L.qkv) > 0) g.partial = s.parts;  // slice sums + finishing kernel
-  LA_TRY(launch_gemm(g, EPI_QKV, int4, st));
+  LA_TRY(launch_gemm(g, EPI_QKV, wf, st));
 
   // window attention -> packed O-projection operand
   AttnArgs at;
@@ -507,8 +536,8 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   at.part_o = s.part_o;
   at.part_ml = s.part_ml;
   at.nqp = s.nqp;
-  at.out = (int4 || attn_out) ? (attn_out ? attn_out : s.o) : nullptr;
-  at.out_apack = int4 ? nullptr : s.apack_o;
+  at.out = (quant || attn_out) ? (attn_out ? attn_out : s.o) : nullptr;
+  at.out_apack = quant ? nullptr : s.apack_o;
   at.out_int4 = false;
   at.causal = m->window_mask == LA_MASK_CAUSAL;
   at.causal_rows = causal_rows;
@@ -523,14 +552,14 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     at.bt_div = av->bt_div;
   }
   LA_TRY(launch_attention(at, st));
-  if (int4)
-    if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, true, nullptr, 0, nullptr,
+  if (quant)
+    if ((rs = pack_rows(at.out, HQ, T, HQ, nullptr, 0.f, s.apack, s.asum, wf, nullptr, 0, nullptr,
                         st)) != LA_OK)
       return rs;
   }
 
   const int F = m->inter;
-  if (!int4 && T <= 32) {
+  if (!quant && T <= 32) {
     if (!fp.grid) {
       // O projection: h += attn . Wo^T, h * post_norm packed for gate/up
       g = base_gemm(&L.o, T);
@@ -541,7 +570,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
       g.y_apack = s.apack;
       g.out_gain = L.post_norm;
       g.ss_out = s.ss;
-      LA_TRY(launch_gemm(g, EPI_STORE, false, st));
+      LA_TRY(launch_gemm(g, EPI_STORE, LA_W_BF16, st));
     }
     if (ev) LA_TRY(hipEventRecord(ev[1], st));
     // gate/up + 1/rms + SiLU, packed straight into the down operand
@@ -551,7 +580,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.ss_tiles = H / 16;
     g.eps = m->rms_eps;
     g.y_apack = s.apack_m;
-    LA_TRY(launch_gemm(g, EPI_SILU, false, st));
+    LA_TRY(launch_gemm(g, EPI_SILU, LA_W_BF16, st));
     // down projection: K-slice partial sums when its plan splits K (a sliced
     // stream over every compute unit beats an unsplit one; the next input
     // packing adds them up), else h += directly with h * next_gain packed for
@@ -573,7 +602,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
         carry->packed = true;
       }
     }
-    LA_TRY(launch_gemm(g, EPI_STORE, false, st));
+    LA_TRY(launch_gemm(g, EPI_STORE, LA_W_BF16, st));
     return LA_OK;
   }
 
@@ -581,7 +610,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
   // directly), then a packing kernel adds them and normalises
   const int ks_o = gemm_ksplit(T, &L.o);
   g = base_gemm(&L.o, T);
-  g.apack = int4 ? s.apack : s.apack_o;  // bf16: packed by the attention merge
+  g.apack = quant ? s.apack : s.apack_o;  // bf16: packed by the attention merge
   g.asum = s.asum;
   if (ks_o > 1) {
     g.partial = s.parts;
@@ -590,26 +619,26 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.y = s.h;
     g.ldy = H;
   }
-  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
+  LA_TRY(launch_gemm(g, EPI_STORE, wf, st));
 
   // h += O partial sums; RMSNorm; gate/up + SiLU (bf16: packed straight into
   // the down operand)
   if (ev) LA_TRY(hipEventRecord(ev[1], st));
-  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+  if ((rs = pack_rows(s.h, H, T, H, L.post_norm, m->rms_eps, s.apack, s.asum, wf, s.parts,
                       ks_o > 1 ? ks_o : 0, ks_o > 1 ? s.h : nullptr, st)) != LA_OK)
     return rs;
   g = base_gemm(&L.gate_up, T);
   g.apack = s.apack;
   g.asum = s.asum;
-  if (int4) {
+  if (quant) {
     g.y = s.mlp;
     g.ldy = F;
   } else {
     g.y_apack = s.apack_m;
   }
-  LA_TRY(launch_gemm(g, EPI_SILU, int4, st));
-  if (int4)
-    if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, true, nullptr, 0, nullptr,
+  LA_TRY(launch_gemm(g, EPI_SILU, wf, st));
+  if (quant)
+    if ((rs = pack_rows(s.mlp, F, T, F, nullptr, 0.f, s.apack_m, s.asum_m, wf, nullptr, 0, nullptr,
                         st)) != LA_OK)
       return rs;
 
@@ -625,7 +654,7 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     g.y = s.h;
     g.ldy = H;
   }
-  LA_TRY(launch_gemm(g, EPI_STORE, int4, st));
+  LA_TRY(launch_gemm(g, EPI_STORE, wf, st));
   carry->pending = ks_d > 1 ? ks_d : 0;
   return LA_OK;
 }
@@ -725,7 +754,7 @@ la_status la_pack_rows(const float* x, int32_t M, int32_t K, const uint16_t* nor
                        float rms_eps, int32_t fmt, void* packed, size_t packed_bytes,
                        hipStream_t stream) {
   if (!x || !packed) return LA_ERR_ARG;
-  if (fmt != LA_W_BF16 && fmt != LA_W_INT4) return LA_ERR_ARG;
+  if (fmt != LA_W_BF16 && fmt != LA_W_INT4 && fmt != LA_W_W8A8) return LA_ERR_ARG;
   if (M < 1 || M > 512 || K < 256 || K % 256 || K > 16384) return LA_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(packed) || (norm_gain && !aligned16(norm_gain))) return LA_ERR_ARG;
   if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
@@ -733,8 +762,7 @@ la_status la_pack_rows(const float* x, int32_t M, int32_t K, const uint16_t* nor
   Carver c(packed);
   uint16_t* apack = c.take<uint16_t>(apack_elems(M, K));
   float* asum = c.take<float>((size_t)((M + 7) / 8) * (K / 128) * 16);
-  return pack_rows(x, K, M, K, norm_gain, rms_eps, apack, asum, fmt == LA_W_INT4, nullptr, 0, nullptr,
-                   stream);
+  return pack_rows(x, K, M, K, norm_gain, rms_eps, apack, asum, fmt, nullptr, 0, nullptr, stream);
 }
 
 la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, const uint16_t* bias,
@@ -755,7 +783,7 @@ la_status la_wgemm_packed(const void* packed, int32_t M, const la_weight* w, con
   g.residual = residual;
   g.y = y;
   g.ldy = epi == EPI_SILU ? w->n / 2 : w->n;
-  return hip_status(launch_gemm(g, epi, w->fmt == LA_W_INT4, stream));
+  return hip_status(launch_gemm(g, epi, w->fmt, stream));
 }
 
 size_t la_wgemm_workspace(int32_t M, const la_weight* w, int32_t epilogue) {
@@ -918,7 +946,6 @@ la_status la_lm_head_argmax_penalized(const float* h, int32_t M, const la_weight
   if (norm_gain && !(rms_eps > 0.f)) return LA_ERR_ARG;
   const size_t need = la_lm_head_argmax_workspace(M, lm);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
-  const bool int4 = lm->fmt == LA_W_INT4;
   Carver c(workspace);
   uint16_t* apack = c.take<uint16_t>(apack_elems(M, lm->k));
   float* asum = c.take<float>((size_t)((M + 7) / 8) * (lm->k / 128) * 16);
@@ -930,7 +957,7 @@ la_status la_lm_head_argmax_penalized(const float* h, int32_t M, const la_weight
   g.rep_words = rep_words;
   g.rep_rows = rep_rows;
   g.rep_theta = rep_penalty;
-  if ((st = gemm_from_rows(g, h, lm->k, norm_gain, rms_eps, apack, asum, EPI_ARGMAX, int4, stream)) != LA_OK)
+  if ((st = gemm_from_rows(g, h, lm->k, norm_gain, rms_eps, apack, asum, EPI_ARGMAX, lm->fmt, stream)) != LA_OK)
     return st;
   return hip_status(launch_argmax_reduce(amax, M, parts, nullptr, ids, top1, gap, nullptr, stream));
 }
@@ -983,7 +1010,7 @@ la_status la_pbd_layer(const la_model* m, int32_t layer, const la_kv_cache* kv, 
                       &carry, nullptr, stream)) != LA_OK)
     return st;
   if (carry.pending)
-    return pack_rows(y, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, carry.pending, y,
+    return pack_rows(y, H, T, H, nullptr, 0.f, nullptr, nullptr, LA_W_BF16, s.parts, carry.pending, y,
                      stream);
   return LA_OK;
 }
@@ -1053,14 +1080,14 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   LA_TRY(launch_prologue(p, stream));
   Carry carry;
   const la_weight* lm = m->lm_head.data ? &m->lm_head : &m->embed;
-  const bool int4 = lm->fmt == LA_W_INT4;
+  const bool quant_lm = lm->fmt != LA_W_BF16;
   for (int l = 0; l < m->n_layers; ++l) {
     // the gain after layer l: the next input norm, or the final norm when the
     // lm_head takes the packed rows directly (bf16)
     // (sampling stores the logits themselves: the final norm is applied by the
     // packing below, not folded into the lm_head's epilogue)
     const uint16_t* next_gain = l + 1 < m->n_layers ? m->layers[l + 1].in_norm
-                                                    : (int4 || sampled ? nullptr : m->final_norm);
+                                                    : (quant_lm || sampled ? nullptr : m->final_norm);
     const hipEvent_t* ev = opts && opts->block_events ? opts->block_events + 2 * l : nullptr;
     st = run_layer(m, l, kv, prefix_len, causal_rows, window_len, B, W, max_len, s, nullptr, &carry,
                    next_gain, stream, nullptr, ev);
@@ -1068,7 +1095,7 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
   }
   if (!carry.packed) {
     // h += last partial sums (written back for out_hidden); final RMSNorm; pack
-    if ((st = pack_rows(s.h, H, T, H, m->final_norm, m->rms_eps, s.apack, s.asum, int4, s.parts,
+    if ((st = pack_rows(s.h, H, T, H, m->final_norm, m->rms_eps, s.apack, s.asum, lm->fmt, s.parts,
                         carry.pending, carry.pending ? s.h : nullptr, stream)) != LA_OK)
       return st;
   }
@@ -1082,7 +1109,7 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
     g.asum = s.asum;
     g.y = smp->logits;
     g.ldy = lm->n;
-    LA_TRY(launch_gemm(g, EPI_STORE, int4, stream));
+    LA_TRY(launch_gemm(g, EPI_STORE, lm->fmt, stream));
     SampleArgs sa = sample_args(smp, smp->logits, T, lm->n, lm->n);
     if (opts->rep_bits) {
       sa.rep_bits = opts->rep_bits;
@@ -1111,7 +1138,7 @@ la_status la_pbd_step_opts(const la_model* m, const la_kv_cache* kv, const int32
     g.ss_tiles = H / 16;
     g.eps = m->rms_eps;
   }
-  LA_TRY(launch_gemm(g, EPI_ARGMAX, int4, stream));
+  LA_TRY(launch_gemm(g, EPI_ARGMAX, lm->fmt, stream));
   return hip_status(launch_argmax_reduce(s.amax, T, s.vocab_parts, s.flags, out_ids, nullptr, out_gap,
                                          nullptr, stream));
 }
@@ -1162,7 +1189,7 @@ la_status la_pbd_prefill(const la_model* m, const la_kv_cache* kv, const int32_t
     if (st != LA_OK) return st;
   }
   if (carry.pending &&
-      (st = pack_rows(s.h, H, T, H, nullptr, 0.f, nullptr, nullptr, false, s.parts, carry.pending,
+      (st = pack_rows(s.h, H, T, H, nullptr, 0.f, nullptr, nullptr, LA_W_BF16, s.parts, carry.pending,
                       s.h, stream)) != LA_OK)
     return st;
   // each sequence's last prompt row (and its flags) -> final norm, lm_head, argmax
@@ -1178,7 +1205,7 @@ la_status la_pbd_prefill(const la_model* m, const la_kv_cache* kv, const int32_t
   GemmArgs g = base_gemm(lm, B);
   g.amax = s.amax;
   if ((st = gemm_from_rows(g, s.h_last, H, m->final_norm, m->rms_eps, s.apack, s.asum, EPI_ARGMAX,
-                           lm->fmt == LA_W_INT4, stream)) != LA_OK)
+                           lm->fmt, stream)) != LA_OK)
     return st;
   return hip_status(launch_argmax_reduce(s.amax, B, s.vocab_parts, s.pre_flags, out_ids, nullptr,
                                          out_gap, nullptr, stream));
@@ -1187,19 +1214,20 @@ la_status la_pbd_prefill(const la_model* m, const la_kv_cache* kv, const int32_t
 size_t la_pack_weight_bytes(const la_weight* src, int32_t layout, int32_t scales) {
   if (!src || src->layout != LA_LAYOUT_ROWS || src->n < 1 || src->k < 128 || src->k % 128) return 0;
   if (layout != LA_LAYOUT_TILED && layout != LA_LAYOUT_TILED_GU && layout != LA_LAYOUT_TILED_QKV) return 0;
-  if (src->fmt != LA_W_BF16 && !(src->fmt == LA_W_INT4 && src->group == 128)) return 0;
+  if (src->fmt != LA_W_BF16 && src->fmt != LA_W_W8A8 && !(src->fmt == LA_W_INT4 && src->group == 128)) return 0;
   if (layout == LA_LAYOUT_TILED_GU && src->n % 16) return 0;
   if (layout == LA_LAYOUT_TILED_QKV && src->n % kHeadDim) return 0;
   const size_t n_tiles = layout == LA_LAYOUT_TILED_GU ? (size_t)(src->n / 2 + 7) / 8 : (size_t)(src->n + 15) / 16;
-  if (scales) return src->fmt == LA_W_INT4 ? n_tiles * (src->k / 128) * 16 * 2 : 0;
-  return src->fmt == LA_W_INT4 ? n_tiles * 16 * (size_t)(src->k / 2) : n_tiles * 16 * (size_t)src->k * 2;
+  if (scales) return src->fmt == LA_W_INT4 ? n_tiles * (src->k / 128) * 16 * 2 : src->fmt == LA_W_W8A8 ? (size_t)src->n * 4 : 0;
+  return src->fmt == LA_W_INT4 ? n_tiles * 16 * (size_t)(src->k / 2)
+         : src->fmt == LA_W_W8A8 ? n_tiles * 16 * (size_t)src->k : n_tiles * 16 * (size_t)src->k * 2;
 }
 
 la_status la_pack_weight(const la_weight* src, int32_t layout, void* dst, void* dst_scales,
                          hipStream_t stream) {
   if (!src || !src->data || !dst) return LA_ERR_ARG;
   if (la_pack_weight_bytes(src, layout, 0) == 0) return LA_ERR_SHAPE;
-  if (src->fmt == LA_W_INT4 && (!src->scales || !dst_scales)) return LA_ERR_ARG;
+  if (src->fmt != LA_W_BF16 && (!src->scales || !dst_scales)) return LA_ERR_ARG;
   if (!aligned16(src->data) || !aligned16(dst)) return LA_ERR_ARG;
   return hip_status(launch_pack_weight(*src, layout, dst, dst_scales, stream));
 }

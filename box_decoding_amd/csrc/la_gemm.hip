@@ -24,6 +24,8 @@
 // in flight exactly and never drains the ring.
 #include "la_gemm_common.hpp"
 
+#include <string.h>
+
 namespace la {
 
 // Rows per GEMM launch: four 8-row tiles keep the accumulators and the operand
@@ -747,6 +749,240 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- w8a8
+
+// w8a8 (the RK3588 conversion's format; read as int8 weight codes with one
+// fp32 scale per output channel, int8 activations with one scale per row):
+// the packed activations are int8 [M/16][K/64][64 lanes][16 bytes] (lane l:
+// row l % 16, k = 64 u + 16 (l / 16) .. + 15) plus fp32 row scales (in the
+// asum buffer); tiled weights are int8 [n_tiles][K/64][64 lanes][16 bytes]
+// in the same lane order, so one 16-byte load per lane is one operand of
+// v_mfma_i32_16x16x64_i8 on either side.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+constexpr int kW8Waves = 8;   // loading waves; one more runs the epilogues
+constexpr int kW8Units = 4;   // K units of 64 per stage and wave
+
+// One workgroup per row (rows M .. 16-padded become zero): v = x + the NP
+// partial sums in order (optionally written back), RMSNorm with gain
+// (optional), then s = max|v| / 127 and q = round-half-even(v / s) clamped to
+// [-127, 127] (s = 0: q = 0), every decision in fp32.  A thread takes 16
+// consecutive k.
+template <int NP>
+__global__ __launch_bounds__(1024) void k_pack_w8(PackArgs a) {
+  __shared__ float red[16];
+  const int m = blockIdx.x, t = threadIdx.x, nw = blockDim.x >> 6;
+  const int K16 = a.K >> 4, U64 = a.K >> 6;
+  const bool live = m < a.M && t < K16;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = 0.f;
+  if (live) {
+    const float* x = a.x + (size_t)m * a.ldx + t * 16;
+    float4 p[4 * (NP + 1)];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) p[h] = *(const float4*)(x + 4 * h);
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+      const float* pp = a.parts + ((size_t)min(s, a.n_parts - 1) * a.M + m) * a.K + t * 16;
+      const float on = s < a.n_parts ? 1.f : 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float4 q = *(const float4*)(pp + 4 * h);
+        p[4 * s + 4 + h] = make_float4(q.x * on, q.y * on, q.z * on, q.w * on);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float4 tt = p[h];
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        const float4 q = p[4 * s + 4 + h];
+        tt.x += q.x; tt.y += q.y; tt.z += q.z; tt.w += q.w;
+      }
+      v[4 * h] = tt.x; v[4 * h + 1] = tt.y; v[4 * h + 2] = tt.z; v[4 * h + 3] = tt.w;
+    }
+    if (a.h_out) {
+      float* ho = a.h_out + (size_t)m * a.ldx + t * 16;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) *(float4*)(ho + 4 * h) = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+    }
+  }
+  if (!a.apack) return;
+  if (a.gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += v[e] * v[e];
+    ss = warp_sum(ss);
+    if ((t & 63) == 0) red[t >> 6] = ss;
+    __syncthreads();
+    ss = 0.f;
+    for (int w = 0; w < nw; ++w) ss += red[w];  // fixed order
+    const float inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    __syncthreads();
+    if (live) {
+      const uint4 g0 = *(const uint4*)(a.gain + t * 16), g1 = *(const uint4*)(a.gain + t * 16 + 8);
+      const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = v[e] * inv * bf16_to_f32((gw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    }
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[e]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = 0.f;
+  for (int w = 0; w < nw; ++w) mx = fmaxf(mx, red[w]);
+  const float sc = mx / 127.0f;
+  if (t < K16) {
+    uint32_t w4[4] = {0u, 0u, 0u, 0u};
+    if (sc > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float q = fminf(fmaxf(__builtin_rintf(v[e] / sc), -127.f), 127.f);
+        w4[e >> 2] |= ((uint32_t)(int)q & 0xFFu) << (8 * (e & 3));
+      }
+    }
+    const int u = t >> 2, g = t & 3;
+    const size_t off = (((size_t)(m >> 4) * U64 + u) * 64 + g * 16 + (m & 15)) * 16;
+    *(uint4*)((uint8_t*)a.apack + off) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+  if (t == 0 && a.asum) a.asum[m] = sc;
+}
+
+// w8a8 GEMM for up to 16 MT rows per launch: work items are (column tile, K
+// slice); 8 loading waves split a slice's 64-k units and stream stages of
+// kW8Units units (their weight and activation fragments) D deep; int32 sums
+// meet exactly in LDS, are scaled by the row's and the column's scale into the
+// fp32 output tile, and the epilogue wave finishes the item with the same
+// epilogues as the bf16 kernel (bias, RoPE and the K/V write, SiLU, residual,
+// partial sums, running top-2).
+template <int MT, int EPI>
+__global__ __launch_bounds__((kW8Waves + 1) * 64) void k_gemm_w8(GemmArgs a) {
+  constexpr int D = MT == 1 ? 3 : 2;
+  __shared__ __align__(16) i32x4 red[kW8Waves * MT * 64];
+  __shared__ float outv[MT * 16 * 17];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int units = a.K >> 6;
+  const int ks = (int)blockIdx.x % a.ksplit;
+  const int tb = (int)blockIdx.x / a.ksplit, gt = (int)gridDim.x / a.ksplit;
+  const int s_lo = units * ks / a.ksplit, s_hi = units * (ks + 1) / a.ksplit;
+  const int s_len = s_hi - s_lo;
+  const int nb = ((s_len + kW8Waves - 1) / kW8Waves + kW8Units - 1) / kW8Units;  // stages per item
+  const int n_my = (a.n_tiles - tb + gt - 1) / gt;
+  const int total = n_my * nb;
+  if (total <= 0) return;  // uniform over the workgroup
+  const int rows = min(min(kRowsPerLaunch, a.M - a.m_base), MT * 16);
+  const int mtv = (rows + 15) >> 4;
+
+  if (wave == kW8Waves) {
+    EpiPre e;
+    if (EPI == EPI_QKV) epi_rows(a, rows, e);
+    if (EPI != EPI_STORE) epi_inv(a, rows, e);
+    Top2 t2 = {-INFINITY, -INFINITY, 0x7FFFFFFF};
+    for (int it = 0; it < n_my; ++it) {
+      epi_prefetch<EPI>(a, tb + it * gt, rows, e);
+      __syncthreads();
+      __syncthreads();
+      epilogue<EPI>(a, tb + it * gt, ks, rows, outv, e, t2);
+    }
+    if (EPI == EPI_ARGMAX) {
+      const float iv = row_inv(e, lane);
+      if (lane < rows) {
+        float* o = a.amax + ((size_t)(a.m_base + lane) * a.n_parts + blockIdx.x) * 3;
+        o[0] = t2.v1 * iv;
+        o[1] = __int_as_float(t2.i1);
+        o[2] = t2.v2 * iv;
+      }
+    }
+    return;
+  }
+
+  const int ulo = s_lo + s_len * wave / kW8Waves, uhi = s_lo + s_len * (wave + 1) / kW8Waves;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.apack, (uint32_t)((a.M + 15) >> 4) * units * 1024);
+  const int mt0 = a.m_base >> 4;
+  const float* sw = (const float*)a.wscale;
+
+  struct St {
+    u32x4 w[kW8Units];
+    u32x4 x[kW8Units][MT];
+  };
+  auto tile_of = [&](int bi) { return tb + (bi / nb) * gt; };
+  auto issue = [&](int bi, St& st) {
+    const int tile = tile_of(min(bi, total - 1));
+    const int u0 = ulo + (bi % nb) * kW8Units;
+    uint32_t wrow = 0;
+    if (a.layout == LA_LAYOUT_ROWS) wrow = (uint32_t)min(col_row<EPI>(a.N, tile, lane & 15), a.N - 1) * a.K + (lane >> 4) * 16;
+#pragma unroll
+    for (int j = 0; j < kW8Units; ++j) {
+      const int u = u0 + j;
+      const bool ok = bi < total && u < uhi;
+      const uint32_t wo = a.layout == LA_LAYOUT_ROWS ? wrow + (uint32_t)u * 64
+                                                     : (((uint32_t)tile * units + u) * 64 + lane) * 16;
+      st.w[j] = bload16<kNonTemporal>(rw, ok ? wo : kOOB);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t xo = (((uint32_t)(mt0 + mt) * units + u) * 64 + lane) * 16;
+        st.x[j][mt] = bload16<0>(ra, ok && mt < mtv ? xo : kOOB);
+      }
+    }
+  };
+  i32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (i32x4){0, 0, 0, 0};
+  auto compute = [&](const St& st) {
+#pragma unroll
+    for (int j = 0; j < kW8Units; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_i8(st.x[j][mt], st.w[j], acc[mt]);
+  };
+  // an item's int32 sums: exact across the waves, then both scales
+  auto finish_item = [&](int bi) {
+    const int tile = tile_of(bi);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      red[(wave * MT + mt) * 64 + lane] = acc[mt];
+      acc[mt] = (i32x4){0, 0, 0, 0};
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < MT * 256; idx += kW8Waves * 64) {
+      const int mt = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+      const int src = (r >> 2) * 16 + c, e = r & 3;
+      int sum = 0;
+      for (int w = 0; w < kW8Waves; ++w) sum += red[(w * MT + mt) * 64 + src][e];
+      const int ml = mt * 16 + r;
+      const float sa = ml < rows ? a.asum[a.m_base + ml] : 0.f;
+      const float sc = sw[min(col_row<EPI>(a.N, tile, c), a.N - 1)];
+      outv[ml * 17 + c] = (float)sum * sa * sc;
+    }
+    __syncthreads();
+  };
+
+  St st[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, st[j]);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int bi0 = 0;; bi0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int bi = bi0 + j;
+      issue(bi + D - 1, st[(j + D - 1) % D]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st[j]);
+      if (bi % nb == nb - 1) finish_item(bi);
+      if (bi + 1 >= total) return;  // uniform
+    }
+  }
+}
+
 // ---------------------------------------------------------------- weight packing
 
 // One thread per 16-byte entry of the tiled layout; rows past n read as zero.
@@ -755,14 +991,15 @@ __global__ __launch_bounds__(256) void k_pack_weight(la_weight src, int layout, 
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= entries) return;
   const int lane = (int)(e & 63), c = lane & 15, g = lane >> 4;
-  const bool int4 = src.fmt == LA_W_INT4;
-  const int UT = int4 ? src.k / 128 : src.k / 32;
+  const bool int4 = src.fmt == LA_W_INT4, w8 = src.fmt == LA_W_W8A8;
+  const int UT = int4 ? src.k / 128 : w8 ? src.k / 64 : src.k / 32;
   const size_t tu = e >> 6;
   const int t = (int)(tu / UT), u = (int)(tu % UT);
   const int row = layout_row(layout, src.n, t, c);
   u32x4 v = {0u, 0u, 0u, 0u};
   if (row < src.n) {
     const size_t off = int4 ? (size_t)row * (src.k / 2) + (size_t)u * 64 + g * 16
+                       : w8 ? (size_t)row * src.k + (size_t)u * 64 + g * 16
                             : ((size_t)row * src.k + (size_t)u * 32 + g * 8) * 2;
     v = *(const u32x4*)((const uint8_t*)src.data + off);
   }
@@ -776,8 +1013,13 @@ __global__ __launch_bounds__(256) void k_pack_weight(la_weight src, int layout, 
 hipError_t launch_pack_weight(const la_weight& src, int layout, void* dst, void* dst_scales,
                               hipStream_t s) {
   const int n_tiles = layout == LA_LAYOUT_TILED_GU ? (src.n / 2 + 7) / 8 : (src.n + 15) / 16;
-  const int UT = src.fmt == LA_W_INT4 ? src.k / 128 : src.k / 32;
+  const int UT = src.fmt == LA_W_INT4 ? src.k / 128 : src.fmt == LA_W_W8A8 ? src.k / 64 : src.k / 32;
   const size_t entries = (size_t)n_tiles * UT * 64;
+  if (src.fmt == LA_W_W8A8 && dst_scales) {
+    // per-channel scales stay indexed by weight row
+    const hipError_t e = hipMemcpyAsync(dst_scales, src.scales, (size_t)src.n * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, src,
                      layout, (uint8_t*)dst, (uint16_t*)dst_scales, entries);
   return hipGetLastError();
@@ -948,7 +1190,57 @@ static hipError_t launch_gemm_fmt(const GemmArgs& a, int epi, const GemmPlan& p,
   }
 }
 
-hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s) {
+// ---------------------------------------------------------------- w8a8 host side
+
+GemmPlan plan_gemm_w8(int M, int N, int K, int epi, bool allow_split) {
+  GemmPlan p;
+  memset(&p, 0, sizeof(p));
+  p.n_tiles = epi == EPI_SILU ? N / 16 : (N + 15) / 16;
+  const int units = K / 64, cus = cu_count();
+  int ks = 1;
+  if (allow_split && epi == EPI_STORE && p.n_tiles < cus) ks = std::min(8, std::max(1, cus / p.n_tiles));
+  ks = std::max(1, std::min(ks, units / kW8Waves));
+  p.ksplit = ks;
+  p.grid = std::max(1, std::min(p.n_tiles, cus / ks)) * ks;
+  p.launches = (M + kRowsPerLaunch - 1) / kRowsPerLaunch;
+  return p;
+}
+
+template <int MT, int EPI>
+static hipError_t launch_w8_one(const GemmArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_w8<MT, EPI>), dim3(grid), dim3((kW8Waves + 1) * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MT>
+static hipError_t launch_w8_epi(const GemmArgs& a, int epi, int grid, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_w8_one<MT, EPI_STORE>(a, grid, s);
+    case EPI_SILU: return launch_w8_one<MT, EPI_SILU>(a, grid, s);
+    case EPI_QKV: return launch_w8_one<MT, EPI_QKV>(a, grid, s);
+    case EPI_ARGMAX: return launch_w8_one<MT, EPI_ARGMAX>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static hipError_t launch_gemm_w8(GemmArgs a, int epi, hipStream_t s) {
+  if (a.K % 64 || !a.asum || !a.wscale) return hipErrorInvalidValue;
+  const GemmPlan p = plan_gemm_w8(a.M, a.N, a.K, epi, a.partial != nullptr);
+  a.n_tiles = p.n_tiles;
+  a.ksplit = p.ksplit;
+  a.n_parts = p.grid;
+  for (int l = 0; l < p.launches; ++l) {
+    a.m_base = l * kRowsPerLaunch;
+    const int rows = std::min(kRowsPerLaunch, a.M - a.m_base);
+    const hipError_t e = rows <= 16 ? launch_w8_epi<1>(a, epi, p.grid, s) : launch_w8_epi<2>(a, epi, p.grid, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemm(GemmArgs a, int epi, int fmt, hipStream_t s) {
+  if (fmt == LA_W_W8A8) return launch_gemm_w8(a, epi, s);
+  const bool int4 = fmt == LA_W_INT4;
   if (use_big_gemm(a.M, a.K, int4, epi)) return launch_gemm_big(a, epi, int4, s);
   const GemmPlan p = plan_gemm(a.M, a.N, a.K, int4, epi, a.partial != nullptr);
   a.n_tiles = p.n_tiles;
@@ -979,7 +1271,25 @@ static hipError_t launch_pack_np(const PackArgs& a, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NP>
+static hipError_t launch_pack_w8(const PackArgs& a, hipStream_t s) {
+  const int rows = a.apack ? ((a.M + 15) / 16) * 16 : a.M;
+  const int bd = ((a.K / 16) + 63) / 64 * 64;
+  hipLaunchKernelGGL((k_pack_w8<NP>), dim3(rows), dim3(bd), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
+  if (a.w8) {
+    // int8 rows and their scales; every row of the last 16-row tile is written
+    if (a.K % 64 || a.K / 16 > 1024) return hipErrorInvalidValue;
+    const int n = a.parts ? a.n_parts : 0;
+    if (n < 0 || n > 8) return hipErrorInvalidValue;
+    if (n == 0) return launch_pack_w8<0>(a, s);
+    if (n <= 2) return launch_pack_w8<2>(a, s);
+    if (n <= 4) return launch_pack_w8<4>(a, s);
+    return launch_pack_w8<8>(a, s);
+  }
   // every operand row of the last tile is written (rows >= M become zero)
   const int rows = a.apack ? ((a.M + 7) / 8) * 8 : a.M;
   if (a.K / 8 > 2048) return hipErrorInvalidValue;

@@ -11,9 +11,10 @@ enum GemmEpi { EPI_STORE = 0, EPI_SILU = 1, EPI_QKV = 2, EPI_ARGMAX = 3 };
 // Arguments of one small-M GEMM launch (rows m_base .. m_base+31 at most).
 struct GemmArgs {
   const uint16_t* apack;     // packed activations of all M rows
-  const float* asum;         // INT4 only: [MT][K/128][16] per-group sums of the packed rows
+  const float* asum;         // INT4: [MT][K/128][16] per-group sums of the packed rows;
+                             // w8a8: the rows' scales [M]
   const void* w;             // weight data
-  const uint16_t* wscale;    // INT4 scales
+  const uint16_t* wscale;    // INT4 scales (fp16); w8a8: per-channel fp32 scales
   uint32_t w_bytes;          // size of the weight data (buffer range)
   uint32_t s_bytes;          // size of the INT4 scales
   int layout;                // LA_LAYOUT_* of w
@@ -67,8 +68,9 @@ struct PackArgs {
   const uint16_t* gain;  // nullable: no RMSNorm
   float eps;
   uint16_t* apack;       // nullable: no packing
-  float* asum;           // INT4 only (nullable otherwise)
+  float* asum;           // INT4: group sums; w8a8: the rows' scales (nullable otherwise)
   bool int4;
+  bool w8;               // w8a8: int8 rows and per-row scales instead of bf16 hi/lo
   const float* parts;    // nullable: [n_parts][M][K] partial sums to add
   int n_parts;
   float* h_out;          // nullable: receives v (may alias x)
@@ -150,7 +152,10 @@ hipError_t launch_commit_refeed(const int32_t* out_ids, const int32_t* n_accept,
                                 int32_t* prefix_len, int32_t* causal_rows, int32_t* window_len, int B,
                                 int W, int block, int mask_id, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
-hipError_t launch_gemm(GemmArgs a, int epi, bool int4, hipStream_t s);
+// fmt: LA_W_BF16, LA_W_INT4 or LA_W_W8A8 (the weight's format; the operand was
+// packed for it)
+hipError_t launch_gemm(GemmArgs a, int epi, int fmt, hipStream_t s);
+GemmPlan plan_gemm_w8(int M, int N, int K, int epi, bool allow_split);
 hipError_t launch_argmax_reduce(const float* amax, int M, int n_tiles, const int32_t* flags,
                                 int32_t* ids, float* top1, float* gap, int32_t* err,
                                 hipStream_t s);

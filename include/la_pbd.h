@@ -51,7 +51,7 @@ typedef enum {
 } la_status;
 
 /* Weight formats. */
-enum { LA_W_BF16 = 0, LA_W_INT4 = 1 };
+enum { LA_W_BF16 = 0, LA_W_INT4 = 1, LA_W_W8A8 = 2 };
 
 /* Weight layouts.  LA_LAYOUT_ROWS is the plain row-major matrix.  The tiled
  * layouts hold the same values regrouped in tiles of 16 rows so that the
@@ -67,7 +67,10 @@ enum { LA_W_BF16 = 0, LA_W_INT4 = 1 };
  * INT4 tiled (group 128): data = uint8 [n_tiles][k/128][64][16]; entry
  *   [t][u][16g + c] holds the 32 codes of row c of tile t at columns
  *   128u + 32g .. +31 packed as in row-major storage; scales = fp16
- *   [n_tiles][k/128][16] (scale of row c of tile t, group u). */
+ *   [n_tiles][k/128][16] (scale of row c of tile t, group u).
+ * w8a8 tiled: data = int8 [n_tiles][k/64][64][16]; entry [t][u][16g + c] holds
+ *   row c of tile t at columns 64u + 16g .. +15; scales stay fp32 [n], indexed
+ *   by weight row. */
 enum { LA_LAYOUT_ROWS = 0, LA_LAYOUT_TILED = 1, LA_LAYOUT_TILED_GU = 2, LA_LAYOUT_TILED_QKV = 3 };
 
 /* A weight matrix W[n, k] (y = x . W^T).
@@ -77,6 +80,14 @@ enum { LA_LAYOUT_ROWS = 0, LA_LAYOUT_TILED = 1, LA_LAYOUT_TILED_GU = 2, LA_LAYOU
  *    low nibble and element 2i+1 in its high nibble; scales = fp16 [n][k/group];
  *    element j of row r is (q - 8) * scales[r][j / group].  group is 32 for the
  *    embedding and 128 for the linears and the lm_head.
+ *  LA_W_W8A8: the RK3588 conversion's format ("LocateAnything-3B for RK3588
+ *    (RKLLM + RKNN)", "Files"; "How it differs from the original", item 3),
+ *    read as: data = int8 [n][k] codes, scales = fp32 [n], element j of row r
+ *    is q * scales[r]; the activations entering the product are quantised per
+ *    row to int8 (s = max|x| / 127, q = round-half-even(x / s) clamped to
+ *    [-127, 127], decided in fp32) and the int32 sums are scaled by both
+ *    scales.  group ignored; k a multiple of 64.  A w8a8 model has w8a8
+ *    linears, a bf16 embedding and a w8a8 lm_head (the tied matrix's copy).
  *  layout: one of LA_LAYOUT_*, as above. */
 typedef struct {
   int32_t fmt;
@@ -183,7 +194,7 @@ la_status la_wgemm(const float* x, int32_t M, const la_weight* w, const uint16_t
 
 /* The two halves of la_wgemm, for callers that reuse one packed operand or
  * time the GEMM alone.  la_pack_rows writes x' (as above) for a weight of
- * format fmt (LA_W_BF16 / LA_W_INT4: the operand layout differs) into `packed`
+ * format fmt (LA_W_BF16 / LA_W_INT4 / LA_W_W8A8: the operand layout differs) into `packed`
  * (caller-owned device memory of la_packed_rows_bytes(M, K) bytes, 16-byte
  * aligned; x fp32 [M][K], 256 <= K <= 16384, K % 256 == 0).  la_wgemm_packed
  * runs the GEMM and epilogue of la_wgemm on such an operand; w->k must equal

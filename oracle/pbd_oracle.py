@@ -130,17 +130,21 @@ def quantize_rows_int8(x):
     return q.astype(np.int64), s
 
 
-def linear(x, w, rows=None, dtype=np.float64):
+def linear(x, w, rows=None, dtype=np.float64, quantize_acts=True):
     """x . W^T for a weight descriptor (rows: a subset of W's rows).  bf16 and
     INT4: the exactly decoded weight.  w8a8: the rows of x quantised to int8
     (quantize_rows_int8), the integer dot products summed exactly, then scaled
-    by the row's scale and the output channel's scale."""
-    if w["fmt"] != "w8a8":
+    by the row's scale and the output channel's scale; with quantize_acts
+    False the activations stay unquantised (the decoded weight times x: the
+    reference point for the format's own error)."""
+    if w["fmt"] != "w8a8" or not quantize_acts:
         return np.asarray(x, dtype=dtype) @ decode_weight(w, rows=rows, dtype=dtype).T
     q, s = quantize_rows_int8(x)
     data = w["data"] if rows is None else w["data"][rows]
     sw = w["scales"] if rows is None else w["scales"][rows]
-    acc = q @ np.asarray(data).view(np.int8).astype(np.int64).T
+    # integer products summed in float64: every partial sum is an integer of
+    # magnitude below 127 * 127 * K < 2^53, so the sum is exact in any order
+    acc = q.astype(np.float64) @ np.asarray(data).view(np.int8).astype(np.float64).T
     return acc.astype(dtype) * s.astype(dtype)[..., None] * np.asarray(sw, dtype=np.float32).astype(dtype)
 
 
@@ -255,7 +259,7 @@ def window_attention(q, k, v, dtype=np.float64, causal=False, causal_rows=0, win
 # ---------------------------------------------------------------------------
 
 def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float64, parts=None,
-                  causal=False, causal_rows=None, window_len=None, window_kv=None):
+                  causal=False, causal_rows=None, window_len=None, window_kv=None, quantize_acts=True):
     """One decoder layer on the window rows of every sequence.
 
     h: [B*W, H] hidden states (row b*W + j is window position j of sequence b).
@@ -267,7 +271,8 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
     decisions; the window's K/V are then inputs, as the prefix's are).
     Returns (h_out, k_bits, v_bits) where k_bits/v_bits [B*W, Hkv, D] are the
     bf16 K/V this layer computes for slots P_b + j (its own rounding).  ``parts`` (a dict) receives
-    intermediate values when given.
+    intermediate values when given.  quantize_acts False: w8a8 linears take
+    unquantised activations (see linear).
     """
     H = _dim(dims, "hidden")
     Hq = _dim(dims, "n_heads")
@@ -283,7 +288,7 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
     assert h.shape == (T, H)
 
     a = rmsnorm(h, bf16_to_float(lay["in_norm"], dtype), eps)
-    qkv = linear(a, lay["qkv"], dtype=dtype)
+    qkv = linear(a, lay["qkv"], dtype=dtype, quantize_acts=quantize_acts)
     if lay.get("qkv_bias") is not None:
         qkv = qkv + bf16_to_float(lay["qkv_bias"], dtype)
     q = qkv[:, :Hq * D].reshape(T, Hq, D)
@@ -310,11 +315,11 @@ def decoder_layer(h, lay, dims, cache, layer, prefix_len, window, dtype=np.float
             causal_rows=0 if causal_rows is None else int(causal_rows[b]),
             window_len=None if window_len is None else int(window_len[b]))
 
-    h1 = h + linear(o.reshape(T, Hq * D), lay["o"], dtype=dtype)
+    h1 = h + linear(o.reshape(T, Hq * D), lay["o"], dtype=dtype, quantize_acts=quantize_acts)
     a2 = rmsnorm(h1, bf16_to_float(lay["post_norm"], dtype), eps)
-    gu = linear(a2, lay["gate_up"], dtype=dtype)
+    gu = linear(a2, lay["gate_up"], dtype=dtype, quantize_acts=quantize_acts)
     m = silu(gu[:, :F]) * gu[:, F:]
-    h2 = h1 + linear(m, lay["down"], dtype=dtype)
+    h2 = h1 + linear(m, lay["down"], dtype=dtype, quantize_acts=quantize_acts)
     if parts is not None:
         parts.update(q=q, k=k, v=v, attn=o.reshape(T, Hq * D), h_mid=h1, mlp=m, qkv=qkv)
     return h2, k_bits, v_bits

@@ -926,6 +926,8 @@ def test_w8a8_linear_scales_the_integer_products():
     # a subset of output channels (the lm_head's chunks) gives the same columns
     rows = np.array([3, 7, 20])
     np.testing.assert_allclose(O.linear(x, w, rows=rows), y[:, rows], rtol=1e-15)
+    # unquantised activations: the decoded weight times x itself
+    np.testing.assert_allclose(O.linear(x, w, quantize_acts=False), x @ O.decode_weight(w).T, rtol=1e-15)
 
 
 def test_w8a8_linear_error_bound_and_exact_grid():
@@ -957,3 +959,16 @@ def test_w8a8_layer_zero_weights_is_identity():
     h = np.random.default_rng(3).standard_normal((6, 256))
     out, _, _ = O.decoder_layer(h, lay, d, cache, 0, P.numpy(), 6)
     np.testing.assert_array_equal(out, h)
+
+
+def test_w8a8_integer_sums_are_exact_at_full_width():
+    # K = 11008 with every code at +-127: float64 sums equal the int64 products
+    rng = np.random.default_rng(13)
+    K = 11008
+    qw = np.where(rng.random((4, K)) < 0.5, -127, 127).astype(np.int8)
+    w = {"fmt": "w8a8", "n": 4, "k": K, "group": 0, "data": qw, "scales": np.ones(4, np.float32)}
+    qx = np.where(rng.random((3, K)) < 0.5, -127, 127).astype(np.int64)
+    qx[:, 0] = 127  # max |x| = 127: s = 1, the codes are x itself
+    y = O.linear(qx.astype(np.float64), w)
+    exact = qx @ qw.astype(np.int64).T
+    assert np.array_equal(y, exact.astype(np.float64))
