@@ -18,10 +18,12 @@
 // logit distance to the row's maximum, held as 40-bit fixed point in 64-bit
 // integers, so every sum is exact and the result does not depend on the order
 // of the additions.  The nucleus boundary is found by radix selection over the
-// order-preserving 32-bit key of z, four bits per pass, each thread keeping 16
-// bin sums in registers; ties on the boundary key and the final draw are
-// located by per-wave contiguous scans in id order.  Every pass reads the row
-// (V fp32) again from L2.
+// order-preserving 32-bit key of z, four bits per pass, each thread keeping its
+// 16 bin sums in private LDS slots (bin-major, so the lanes of a wave hit
+// distinct banks whatever their digits: one read-modify-write per element);
+// wave b then sums bin b over the threads.  Ties on the boundary key and the
+// final draw are located by per-wave contiguous scans in id order.  Every
+// pass reads the row (V fp32) again from L2.
 #include "la_internal.hpp"
 
 namespace la {
@@ -31,6 +33,7 @@ namespace {
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
 constexpr float kFix = 1099511627776.0f;  // 2^40
+constexpr size_t kSampleLds = (size_t)16 * kSampleThreads * 8;  // private bins [16][threads] uint64
 
 __device__ __forceinline__ uint32_t philox_first_word(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                       uint32_t k0, uint32_t k1) {
@@ -88,7 +91,7 @@ __device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
 struct SampleShared {
   float fmax[kSampleWaves];
   int imax[kSampleWaves];
-  uint64_t bins[kSampleWaves][16];
+  uint64_t bins[16];
   uint64_t wsum[kSampleWaves];
   uint64_t total;
   float zmax;
@@ -105,6 +108,7 @@ struct SampleShared {
 
 __global__ __launch_bounds__(kSampleThreads) void k_sample(SampleArgs a) {
   __shared__ SampleShared sh;
+  extern __shared__ __align__(16) uint64_t pbins[];  // [16][kSampleThreads]
   const int m = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,31 +185,31 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SampleArgs a) {
   uint64_t above = 0, target = 0;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 28 - 4 * pass;
-    uint64_t h[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) h[b] = 0;
+    for (int b = 0; b < 16; ++b) pbins[b * kSampleThreads + tid] = 0;
     for (int v = tid; v < V; v += kSampleThreads) {
       const float z = zpen(v);
       const uint32_t k = zkey(z);
       if ((k & pmask) != prefix) continue;
-      const uint64_t q = qfix(z);
       const uint32_t d = (k >> shift) & 15u;
-#pragma unroll
-      for (int b = 0; b < 16; ++b) h[b] += d == (uint32_t)b ? q : 0ull;
+      pbins[d * kSampleThreads + tid] += qfix(z);
     }
+    __syncthreads();
+    {
+      // wave b: bin b over every thread (16 slots per lane, fixed order)
+      static_assert(kSampleWaves == 16, "one wave per bin");
+      uint64_t s = 0;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const uint64_t s = wave_sum_u64(h[b]);
-      if (lane == 0) sh.bins[wave][b] = s;
+      for (int i = 0; i < kSampleThreads / 64; ++i) s += pbins[wave * kSampleThreads + i * 64 + lane];
+      s = wave_sum_u64(s);
+      if (lane == 0) sh.bins[wave] = s;
     }
     __syncthreads();
     if (tid == 0) {
       uint64_t H[16], all = 0;
       for (int b = 0; b < 16; ++b) {
-        uint64_t s = 0;
-        for (int w = 0; w < kSampleWaves; ++w) s += sh.bins[w][b];
-        H[b] = s;
-        all += s;
+        H[b] = sh.bins[b];
+        all += H[b];
       }
       if (pass == 0) {
         // the nucleus must hold ceil(top_p * total) of the fixed-point mass
@@ -326,7 +330,14 @@ __global__ void k_offset_advance(uint64_t* offset) {
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_sample, dim3(a.M), dim3(kSampleThreads), 0, s, a);
+  static bool attr = false;  // the private bins need LDS beyond the static default
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_sample, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kSampleLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(k_sample, dim3(a.M), dim3(kSampleThreads), kSampleLds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.offset_dev || !(a.temperature > 0.f)) return e;
   hipLaunchKernelGGL(k_offset_advance, dim3(1), dim3(64), 0, s, const_cast<uint64_t*>(a.offset_dev));
