@@ -129,6 +129,30 @@ int qkv_ksplit(int M, const la_weight* w) {
   return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_QKV, true).ksplit;
 }
 
+// The front-half launch's attention runs for B sequences of W rows with keys
+// up to max_len: pages per run and runs per (sequence, KV head), every run of
+// every 16-column query tile beside the QKV tiles on its own compute unit (at
+// most 16 runs of at most kFrontMaxRunPages pages); false when the shape does not fit the launch
+// (at most 8 bf16 rows, hidden and heads x 128 both 2048, the 64 pack slices
+// beside the QKV tiles).
+bool front_shape(const la_model* m, int B, int W, int max_len, int* pps_out, int* runs_out) {
+  const int T = B * W, H = m->hidden, HQ = m->n_heads * m->head_dim;
+  const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+  if (T < 1 || T > 8 || H != 2048 || HQ != 2048 || m->layers[0].qkv.fmt != LA_W_BF16) return false;
+  if (attn_nqp(W, m->n_heads / m->n_kv_heads) > 64) return false;
+  const int G = cu_count(), n_qkv = NQKV / 16;
+  const int free_wgs = G - n_qkv;
+  const int units = B * m->n_kv_heads * attn_nqp(W, m->n_heads / m->n_kv_heads) / 16;  // items per run
+  if (n_qkv + kFrontPackSlices > G || H / 16 > n_qkv || free_wgs < units) return false;
+  const int max_pages = (max_len + kBlock - 1) / kBlock;
+  const int runs_max = std::min(std::min(16, free_wgs / units), 128 / units);
+  const int pps = std::max(2, (max_pages + runs_max - 1) / runs_max);
+  if (pps > kFrontMaxRunPages) return false;
+  *pps_out = pps;
+  *runs_out = (max_pages + pps - 1) / pps;
+  return true;
+}
+
 struct StepWs {
   float* h;
   float* q;
@@ -146,8 +170,12 @@ struct StepWs {
   float* part_ml;
   float* amax;
   float* parts;       // K-slice partial sums of the O and down projections
-  int32_t* sync;      // the front-half launch's flag words (zeroed by the prologue)
-  int n_sync;
+  int32_t* sync;      // the front-half launch's flag words, then its 8-byte words
+  int n_sync;         // (all zeroed by the prologue: n_sync int32 words)
+  uint64_t* ll_q;
+  uint64_t* ll_kv;
+  uint64_t* ll_ml;
+  uint64_t* ll_po;
   float* front_ss;    // the front-half launch's per-slice sums of squares
   int32_t* err;       // the step's error word (nullable)
   // prefill: the attention's view of the prompt as 16-row windows, the
@@ -209,8 +237,17 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
   const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
   const size_t qkv_parts = (size_t)qkv_ksplit(T, &m->layers[0].qkv) * T * NQKV;
   s.parts = c.take<float>(std::max((size_t)ksp * T * H, qkv_parts));
-  s.n_sync = 8 * 64 + m->n_kv_heads * 128 + aB * m->n_kv_heads * 16 + 8 * 128;
-  s.sync = c.take<int32_t>(s.n_sync);
+  const size_t sync_off = c.off;
+  s.sync = c.take<int32_t>(kFrontSyncWords);
+  int fpps, fruns;
+  if (!chunks && front_shape(m, B, W, max_len, &fpps, &fruns)) {
+    const size_t units = (size_t)B * m->n_kv_heads * fruns * s.nqp;
+    s.ll_q = c.take<uint64_t>((size_t)T * HQ);
+    s.ll_kv = c.take<uint64_t>((size_t)T * m->n_kv_heads * 2 * 64);
+    s.ll_ml = c.take<uint64_t>(units * 2);
+    s.ll_po = c.take<uint64_t>(units * kHeadDim);
+  }
+  s.n_sync = (int)((c.off - sync_off) / 4);
   s.front_ss = c.take<float>(8 * kFrontPackSlices);
   s.bytes = c.off;
   return s;
@@ -380,23 +417,14 @@ FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max
   FrontPlan f;
   const char* env = getenv("LA_PBD_FRONT");
   if (env && env[0] == '0') return f;
-  const int T = B * W, H = m->hidden, HQ = m->n_heads * m->head_dim;
-  const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
-  if (av || attn_out || T > 8 || H != 2048 || HQ != 2048 || L.qkv.fmt != LA_W_BF16) return f;
-  if (L.qkv.layout != LA_LAYOUT_TILED_QKV || L.o.layout != LA_LAYOUT_TILED || s.nqp > 64 || pending > 4) return f;
-  const int G = cu_count(), n_qkv = NQKV / 16;
-  const int free_wgs = G - n_qkv;
-  if (n_qkv + kFrontPackSlices > G || H / 16 > n_qkv || free_wgs < B * m->n_kv_heads) return f;
-  const int max_pages = (max_len + kBlock - 1) / kBlock;
-  const int runs_max = std::min(16, free_wgs / (B * m->n_kv_heads));
-  int pps = std::max(2, (max_pages + runs_max - 1) / runs_max);
-  if (pps > kFrontMaxRunPages) return f;
-  const int runs = (max_pages + pps - 1) / pps;
-  if (runs > s.max_splits) return f;
-  f.grid = G;
+  if (av || attn_out || pending > 4 || L.qkv.fmt != LA_W_BF16 || !s.ll_q) return f;
+  if (L.qkv.layout != LA_LAYOUT_TILED_QKV || L.o.layout != LA_LAYOUT_TILED) return f;
+  int pps, runs;
+  if (!front_shape(m, B, W, max_len, &pps, &runs)) return f;
+  f.grid = cu_count();
   f.pps = pps;
   f.runs = runs;
-  f.items = B * m->n_kv_heads * runs;
+  f.items = B * m->n_kv_heads * (s.nqp / 16) * runs;
   return f;
 }
 
@@ -422,7 +450,6 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     FrontArgs f;
     memset(&f, 0, sizeof(f));
     AttnArgs& at = f.at;
-    at.q = s.q;
     at.kc = (uint16_t*)kv->k + (size_t)l * le;
     at.vc = (uint16_t*)kv->v + (size_t)l * le;
     at.block_table = kv->block_table;
@@ -436,8 +463,6 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     at.cap = std::min(max_len, kv->max_blocks * kBlock);
     at.pages_per_split = fp.pps;
     at.max_splits = fp.runs;
-    at.part_o = s.part_o;
-    at.part_ml = s.part_ml;
     at.out_apack = s.apack_o;
     at.nqp = s.nqp;
     at.causal = m->window_mask == LA_MASK_CAUSAL;
@@ -472,6 +497,10 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     f.n_items = fp.items;
     f.runs = fp.runs;
     f.sync = s.sync;
+    f.ll_q = s.ll_q;
+    f.ll_kv = s.ll_kv;
+    f.ll_ml = s.ll_ml;
+    f.ll_po = s.ll_po;
     f.epoch = l + 1;
     f.err = s.err;
     LA_TRY(launch_front(f, fp.grid, st));
@@ -675,6 +704,7 @@ PrologueArgs base_prologue(const la_model* m, const la_kv_cache* kv, const int32
   p.cap = std::min(max_len, kv->max_blocks * kBlock);
   p.zero = s.sync;
   p.n_zero = s.n_sync;
+  p.zero_blocks = std::min(64, std::max(1, (int)(((size_t)s.n_sync * 4 + 32767) / 32768)));
   return p;
 }
 

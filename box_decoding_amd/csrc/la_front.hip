@@ -23,20 +23,26 @@
 //   pack slice p:   the 64 workgroups after the QKV tiles, 32 columns of K
 //                   each: the operand slice and its rows' sums of squares;
 //   attention item: workgroups from the top of the grid, one run of at most
-//                   kFrontMaxRunPages pages of one (sequence, KV head) each,
-//                   the whole run staged in LDS; once every run of the
-//                   (sequence, KV head) has stored its partial result, run r
-//                   merges slice r of the query columns.  (A workgroup may be
-//                   both a pack slice and an item: it packs while its pages
-//                   load.)
-// A step waits for its inputs on flag words in device memory: each producer
-// sets its own word to the launch's epoch (the layer index + 1; the step's
-// prologue zeroes every word), so no two producers write one word and no
-// atomic is needed; a waiter reads the whole array with one vector load per
-// poll.  Everything one workgroup hands another inside the launch is written
-// with agent-scope (cross-XCD coherent) stores, completed (s_waitcnt) before
-// the flag is set.  The pack and O-ready flags, which 160 and 128 workgroups
-// wait on, have a copy per XCD (each waiter polls the copy of its XCD).  Every
+//                   kFrontMaxRunPages pages of one (sequence, KV head) for one
+//                   16-column query tile each, the whole run staged in LDS and
+//                   its page pairs spread one per wave; once every run of the
+//                   tile has stored its partial result, run r merges a slice
+//                   of the tile's columns.  (A workgroup may be both a pack
+//                   slice and an item: it packs while its pages load.)
+// Hand-offs.  Data that a few workgroups read (q and the window's K / V for
+// the attention items, the runs' partial results for their merge) travels as
+// 8-byte words {32-bit datum, epoch}: one agent-scope (cross-XCD coherent)
+// store per word, read with agent-scope loads until every word it needs holds
+// the launch's epoch (the layer index + 1; the step's prologue zeroes the
+// words).  An aligned 8-byte access is never split, so a word is wholly old or
+// wholly new, and the consumer sees the data one memory trip after it is
+// written: no store has to complete before a flag, and no flag is read first.
+// Data that 128 or more workgroups read in full (the packed QKV operand, the
+// attention output) goes as plain data plus flag words: each producer stores
+// with agent-scope stores, waits for them to complete (s_waitcnt) and sets its
+// own int32 word to the epoch (no two producers write one word, no atomic);
+// these flag arrays have a copy per XCD (each waiter polls the copy of its
+// XCD) and a waiter reads a whole array with one vector load per poll.  Every
 // wait is bounded: a wait that runs out sets LA_DERR_SYNC in the error word and
 // goes on, so the launch always ends.
 #include "la_attn_common.hpp"
@@ -64,7 +70,8 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 constexpr int kRingBytes = kFrontMaxRunPages * kPageBytes;
 constexpr int kRedOff = kRingBytes;
 constexpr int kOutvOff = kRedOff + kFrontWaves * 64 * 16;
-constexpr int kFrontLds = kOutvOff + 8 * 17 * 4;
+constexpr int kQOff = kOutvOff + 8 * 17 * 4;                 // an attention item's q (hi, lo fragments)
+constexpr int kFrontLds = kQOff + 64 * 8 * 16;
 
 __device__ __forceinline__ int ld_flag(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -74,9 +81,6 @@ __device__ __forceinline__ void set_flag(int32_t* p, int v) {
 }
 __device__ __forceinline__ void st_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_u16(uint16_t* p, uint32_t v) {
-  __hip_atomic_store((short*)p, (short)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Stores made so far have reached the coherent level.
 __device__ __forceinline__ void stores_done() {
@@ -90,15 +94,39 @@ __device__ __forceinline__ u32x4 pack8(const uint32_t (&x)[8]) {
   return v;
 }
 
-// Flag arrays (ints): pack [kFlagCopies][64] (slice), qkv [Hkv][128] (tile
-// of the head), run [B * Hkv][16] (run), ready [kFlagCopies][128] (item).
+// Flag arrays (ints): pack [kFlagCopies][64] (slice), ready [kFlagCopies][128] (item).
 __device__ __forceinline__ int32_t* fl_pack(const FrontArgs& f, int copy) { return f.sync + copy * 64; }
-__device__ __forceinline__ int32_t* fl_qkv(const FrontArgs& f, int g) { return f.sync + kFlagCopies * 64 + g * 128; }
-__device__ __forceinline__ int32_t* fl_run(const FrontArgs& f, int b, int g) {
-  return f.sync + kFlagCopies * 64 + f.at.Hkv * 128 + (b * f.at.Hkv + g) * 16;
-}
 __device__ __forceinline__ int32_t* fl_ready(const FrontArgs& f, int copy) {
-  return f.sync + kFlagCopies * 64 + f.at.Hkv * 128 + f.at.B * f.at.Hkv * 16 + copy * 128;
+  return f.sync + kFlagCopies * 64 + copy * 128;
+}
+static_assert(kFlagCopies * (64 + 128) == kFrontSyncWords, "flag words the step carves");
+
+// One 8-byte word {datum, epoch}.
+__device__ __forceinline__ void ll_store(uint64_t* p, uint32_t d, int epoch) {
+  __hip_atomic_store(p, ((uint64_t)(uint32_t)epoch << 32) | d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Two words {d0, epoch}, {d1, epoch} as one 16-byte agent-scope store.
+__device__ __forceinline__ void ll_store2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t d0, uint32_t d1, int epoch) {
+  const u32x4 v = {d0, (uint32_t)epoch, d1, (uint32_t)epoch};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherent);
+}
+__device__ __forceinline__ u32x4 ll_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ bool ll_ok(u32x4 v, uint32_t epoch) { return v[1] == epoch && v[3] == epoch; }
+
+// End of a poll round of one wave: true once no active lane still misses a
+// word; false after a short sleep otherwise (the spin limit ends the wait with
+// LA_DERR_SYNC).
+__device__ __forceinline__ bool ll_round(const FrontArgs& f, bool ok, int& spins) {
+  if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
+  if (++spins >= kSpinLimit) {
+    // the first active lane reports
+    if (f.err && (threadIdx.x & 63) == (int)__builtin_amdgcn_readfirstlane(threadIdx.x & 63)) atomicOr(f.err, LA_DERR_SYNC);
+    return true;
+  }
+  __builtin_amdgcn_s_sleep(1);
+  return false;
 }
 
 // The whole workgroup waits until p[0 .. n) (n <= 128) all hold the epoch
@@ -216,8 +244,9 @@ __device__ QkvEpi qkv_epi_prepare(const FrontArgs& f, int t) {
   return e;
 }
 
-// QKV epilogue of tile t (wave 0): 1 / rms, bias, RoPE, q (coherent stores)
-// and the window's bf16 K/V written to the cache (coherent stores).
+// QKV epilogue of tile t (wave 0): 1 / rms, bias, RoPE; q as words for the
+// attention, the window's K and V as words for the attention and as bf16 into
+// the cache (for later steps).
 __device__ void qkv_epilogue(const FrontArgs& f, int t, const float* outv, float inv, const QkvEpi& e) {
   const AttnArgs& a = f.at;
   const int lane = threadIdx.x & 63;
@@ -233,24 +262,18 @@ __device__ void qkv_epilogue(const FrontArgs& f, int t, const float* outv, float
     x2 = y2;
   }
   if (head < a.Hq) {
-    float* q = const_cast<float*>(a.q) + (size_t)ml * a.Hq * kHeadDim;
-    st_f32(q + r1, x1);
-    st_f32(q + r2, x2);
+    uint64_t* q = f.ll_q + (size_t)ml * a.Hq * kHeadDim;
+    ll_store(q + r1, __float_as_uint(x1), f.epoch);
+    ll_store(q + r2, __float_as_uint(x2), f.epoch);
     return;
   }
+  const uint32_t b1 = f32_to_bf16_rne(x1), b2 = f32_to_bf16_rne(x2);
+  const int kv = head < a.Hq + a.Hkv ? 0 : 1, g = head - a.Hq - kv * a.Hkv;
+  ll_store(f.ll_kv + ((size_t)(ml * a.Hkv + g) * 2 + kv) * 64 + i, b1 | (b2 << 16), f.epoch);
   if (e.p1) {
-    st_u16(e.p1, f32_to_bf16_rne(x1));
-    st_u16(e.p2, f32_to_bf16_rne(x2));
+    *e.p1 = (uint16_t)b1;
+    *e.p2 = (uint16_t)b2;
   }
-}
-
-// KV head g of QKV tile t and its index among the (G + 2) * 8 tiles g's
-// attention waits for: the G query heads' tiles, then K's, then V's.
-__device__ __forceinline__ int2 tile_kv_slot(const AttnArgs& a, int t) {
-  const int head = t >> 3, sub = t & 7, G = a.Hq / a.Hkv;
-  if (head < a.Hq) return make_int2(head / G, (head % G) * 8 + sub);
-  if (head < a.Hq + a.Hkv) return make_int2(head - a.Hq, G * 8 + sub);
-  return make_int2(head - a.Hq - a.Hkv, (G + 1) * 8 + sub);
 }
 
 // h + the pending K-slice sums (slice order) at columns n of rows ml, read
@@ -350,7 +373,7 @@ __device__ void front_pack(const FrontArgs& f, int p) {
   if (lane < kFlagCopies) set_flag(fl_pack(f, lane) + p, f.epoch);
 }
 
-// The projection role of tile t up to its QKV counter: the packed operand
+// The projection role of tile t: the packed operand
 // (read coherently once every pack slice is in), the product, the epilogue.
 __device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
@@ -378,14 +401,8 @@ __device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
   __builtin_amdgcn_sched_barrier(0);  // every request in flight before the first product
   float* outv = (float*)(smem + kOutvOff);
   tile_reduce(af, wq, wave, (f32x4*)(smem + kRedOff), outv);
-  if (wave == 0) {
-    qkv_epilogue(f, t, outv, row_inv_rms(f, s0, s1), epi);
-    stores_done();
-    if (lane == 0) {
-      const int2 gs = tile_kv_slot(f.at, t);
-      set_flag(fl_qkv(f, gs.x) + gs.y, f.epoch);
-    }
-  }
+  if (wave == 0) qkv_epilogue(f, t, outv, row_inv_rms(f, s0, s1), epi);
+  __syncthreads();  // the epilogue's stores go out before the O weight loads
 }
 
 // The O role of tile t: waits for every attention item, reads the packed
@@ -414,30 +431,36 @@ __device__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits
   if (wave == 0) o_epilogue(f, t, res, gain, outv);
 }
 
-// One attention item: sequence b, KV head g, run r of a.pages_per_split
-// pages.  Pages whose keys all precede the window are copied into LDS at once;
-// the rest (keys this launch writes) after the QKV counter of g.  Waves
-// 0..NQT-1 hold query tiles.  A single-run sequence writes its normalised
-// output; otherwise every run stores its (max, sum, unnormalised O) and, once
-// all runs of (b, g) have, merges slice r of the query columns.
-template <int NQT>
-__device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigned char* ring, int slice) {
+// One attention item: sequence b, KV head g, query tile qt (query columns
+// 16 qt .. 16 qt + 15, column i being window row i / G of query head g G + i %
+// G), run r of a.pages_per_split pages.  Every page is copied into LDS at
+// once; the keys of the window rows (written by this launch) then come from
+// their K / V words, and q from its words (wave 0 polls them and hands the hi /
+// lo fragments on through LDS).  Wave w takes pairs w, w + 8, ..., and wave 0
+// combines the waves' states.  A single-run sequence writes its normalised
+// output; otherwise every run stores its (max, sum, unnormalised O) as words
+// and merges a slice of the tile's columns from every run's words.
+__device__ void front_attention(const FrontArgs& f, int b, int g, int qt, int r, unsigned char* smem, int slice) {
   const AttnArgs& a = f.at;
+  unsigned char* ring = smem;
   const int lane = threadIdx.x & 63, gl = lane >> 4, rr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.Hq / a.Hkv, NQ = a.W * G;
+  const int q0 = qt * 16;
   const int kps = a.pages_per_split * kBlock;
   const int n_keys = attn_keys(a, b);
   const int nruns = (n_keys + kps - 1) / kps;
   const int k0 = r * kps;
+  const uint32_t ep = (uint32_t)f.epoch;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out_apack, (uint32_t)(a.Hq * kHeadDim / 8) * 256);
   if (k0 >= n_keys) {
     if (slice >= 0 && threadIdx.x < 64) front_pack(f, slice);
     if (n_keys == 0 && r == 0) {
       // no key at all (a prefix the step flags as invalid): zero output
       const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int idx = threadIdx.x; idx < NQ * 16; idx += kFrontThreads) {
-        const int qi = idx >> 4, ch = idx & 15;
+      for (int idx = threadIdx.x; idx < 16 * 16; idx += kFrontThreads) {
+        const int qi = q0 + (idx >> 4), ch = idx & 15;
+        if (qi >= NQ) continue;
         const int wr = qi / G, hg = qi - wr * G;
         const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + ch * 8;
         const uint32_t off = ((uint32_t)(col >> 3) * 16 + row) * 16;
@@ -449,63 +472,93 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
   }
   const int k1 = min(n_keys, k0 + kps);
   const int npages = (k1 - k0 + kBlock - 1) / kBlock;
+  const int npairs = (npages + 1) >> 1;
   const int first = k0 / kBlock;
   int bt = a.block_table[(size_t)b * a.max_blocks + min(first + min(lane, npages - 1), a.max_blocks - 1)];
   bt = bt < 0 ? 0 : (bt >= a.num_blocks ? a.num_blocks - 1 : bt);
   const uint32_t cache_bytes = (uint32_t)a.num_blocks * a.Hkv * (kPageBytes / 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc, cache_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc, cache_bytes);
-  // page j: wave w copies 1 KB piece w (pieces 0..3 of K, 4..7 of V^T)
-  auto copy_page = [&](int j, bool coherent) {
+  // wave 0 packs its slice first (the pack's wait for its own stores would
+  // otherwise also wait for the page copies)
+  if (slice >= 0 && wave == 0) front_pack(f, slice);
+  // page j: wave w copies 1 KB piece w (pieces 0..3 of K, 4..7 of V^T); the
+  // slots of window rows are overwritten below
+  for (int j = 0; j < npages; ++j) {
     const int blk = __builtin_amdgcn_readlane(bt, j);
     const uint32_t base = ((uint32_t)blk * a.Hkv + g) * (kPageBytes / 2);
     void __attribute__((address_space(3)))* dst =
         (void __attribute__((address_space(3)))*)(ring + j * kPageBytes + wave * 1024);
-    if (coherent)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, kCoherent);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, 0);
-  };
-  // pages [0, early) hold only keys below the prefix length: written before this launch
-  const int early = min(npages, max(0, (a.prefix_len[b] - k0) / kBlock));
-  // wave 0 packs its slice first (the pack's wait for its own stores would
-  // otherwise also wait for the page copies)
-  if (slice >= 0 && wave == 0) front_pack(f, slice);
-  for (int j = 0; j < early; ++j) copy_page(j, false);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rk : rv, dst, 16, page_piece_src(wave, lane), base, 0, 0);
+  }
 
-  wait_flags(f, fl_qkv(f, g), (G + 2) * 8);  // q of g's query heads, K and V of g: 8 tiles per head
-
-  // wave (tile, group): query tile wave % NQT, pairs group, group + kGroups, ...
-  constexpr int kGroups = kFrontWaves / NQT;
-  const int tile = wave % NQT, grp = wave / NQT;
-  const bool qw = grp < kGroups;  // waves past kGroups * NQT stay idle
-  const int qi = tile * 16 + rr;
-  bf16x8 qh[4], ql[4];
-  if (qw) {
-    const int qc = qi < NQ ? qi : 0;
-    const int wr = qc / G, hg = qc - wr * G;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * a.W * a.Hq * kHeadDim) * 4);
-    const uint32_t qoff = ((uint32_t)((b * a.W + wr) * a.Hq + g * G + hg) * kHeadDim + gl * 8) * 4;
-    u32x4 xq[4][2];
+  // keys [wlo, wlo + nwin) of this run are window rows of this launch: thread
+  // t < 64 nwin takes two words (K if bit 5 of t is clear, else V) of key
+  // wlo + t / 64
+  const int P = a.prefix_len[b];
+  const int wlo = max(P, k0), nwin = max(0, k1 - wlo);
+  const bool kvt = (int)threadIdx.x < nwin * 64;
+  const int wkey = wlo + (threadIdx.x >> 6), kvh = (threadIdx.x >> 5) & 1, i2 = (threadIdx.x & 31) * 2;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.ll_kv, (uint32_t)(f.T * a.Hkv * 128) * 8);
+  const uint32_t kvoff =
+      kvt ? ((uint32_t)(((b * a.W + wkey - P) * a.Hkv + g) * 2 + kvh) * 64 + i2) * 8 : 0u;
+  // q of column q0 + rr (lane (gl, rr) of wave 0: dims 32 kb + 8 gl .. + 7)
+  const int qi = q0 + rr;
+  const int qc = qi < NQ ? qi : 0;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(f.ll_q, (uint32_t)(f.T * a.Hq * kHeadDim) * 8);
+  const uint32_t qoff =
+      ((uint32_t)((b * a.W + qc / G) * a.Hq + g * G + qc % G) * kHeadDim + gl * 8) * 8;
+  u32x4 xq[4][4], xw = {0u, 0u, 0u, 0u};
+  for (int spins = 0;;) {
+    bool ok = true;
+    if (wave == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      xq[kb][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128, 0, kCoherent));
-      xq[kb][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kb * 128 + 16, 0, kCoherent));
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) xq[kb][n] = ll_load2(rq, qoff + (kb * 32 + 2 * n) * 8);
     }
-    for (int j = early; j < npages; ++j) copy_page(j, true);
-    __builtin_amdgcn_sched_barrier(0);
+    if (kvt) xw = ll_load2(rw, kvoff);
+    if (wave == 0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) ok = ok && ll_ok(xq[kb][n], ep);
+    }
+    if (kvt) ok = ok && ll_ok(xw, ep);
+    if (ll_round(f, ok, spins)) break;
+  }
+  u32x4* qs = (u32x4*)(smem + kQOff);  // [8 fragments][64 lanes]
+  if (wave == 0) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       uint32_t hi[8], lo[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) split_hi_lo(qi < NQ ? __uint_as_float(xq[kb][e >> 2][e & 3]) : 0.f, hi[e], lo[e]);
-      qh[kb] = __builtin_bit_cast(bf16x8, pack8(hi));
-      ql[kb] = __builtin_bit_cast(bf16x8, pack8(lo));
+      for (int e = 0; e < 8; ++e)
+        split_hi_lo(qi < NQ ? __uint_as_float(xq[kb][e >> 1][(e & 1) * 2]) : 0.f, hi[e], lo[e]);
+      qs[kb * 64 + lane] = pack8(hi);
+      qs[(4 + kb) * 64 + lane] = pack8(lo);
     }
-  } else {
-    for (int j = early; j < npages; ++j) copy_page(j, true);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces of every page
+  __syncthreads();
+  if (kvt) {
+    // the window key's K (chunk c of key k sits at 16-byte slot c ^ k) or V^T
+    const int kk = wkey - k0, sl = kk & 15;
+    unsigned char* pg = ring + (kk >> 4) * kPageBytes;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t d = xw[2 * u];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int dim = i2 + u + 64 * h;
+        const uint16_t v = (uint16_t)(d >> (16 * h));
+        if (kvh == 0)
+          *(uint16_t*)(pg + sl * 256 + (((dim >> 3) ^ sl) * 16) + (dim & 7) * 2) = v;
+        else
+          *(uint16_t*)(pg + 4096 + dim * 32 + sl * 2) = v;
+      }
+    }
+  }
   __syncthreads();
 
   AttnState st;
@@ -514,25 +567,31 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int crows = a.causal_rows ? min(max(a.causal_rows[b], 0), a.W) : (a.causal ? a.W : 0);
-  const int wrow = (qi < NQ ? qi : 0) / G;
-  const int kcol = wrow < crows ? max(min(n_keys, a.prefix_len[b] + wrow + 1), min(n_keys, 1)) : n_keys;
-  if (qw) {
-    const int npairs = (npages + 1) >> 1;
-    for (int c = grp; c < npairs; c += kGroups) {
+  const int wrow = qc / G;
+  const int kcol = wrow < crows ? max(min(n_keys, P + wrow + 1), min(n_keys, 1)) : n_keys;
+  if (wave < npairs) {
+    bf16x8 qh[4], ql[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      qh[kb] = __builtin_bit_cast(bf16x8, qs[kb * 64 + lane]);
+      ql[kb] = __builtin_bit_cast(bf16x8, qs[(4 + kb) * 64 + lane]);
+    }
+    for (int c = wave; c < npairs; c += kFrontWaves) {
       PairRegs pr;
       read_pair(ring + c * kPairBytes, pr);
       const int p0 = k0 + 2 * c * kBlock;
       attn_pair(pr, k1 - p0, min(k1, kcol) - p0, qh, ql, st);
     }
   }
-  if (kGroups > 1) {
-    // group 0 takes in the other groups' states (group order), through the
-    // ring: every wave is done with the pages
+  const int nw = min(npairs, kFrontWaves);  // waves that hold a state
+  if (nw > 1) {
+    // wave 0 takes in the other waves' states (wave order), through the ring:
+    // every wave is done with the pages
     __syncthreads();
     float* gs = (float*)ring;
     constexpr int kStateFloats = 8 * 4 + 2;
-    if (qw && grp > 0) {
-      float* d = gs + ((grp - 1) * NQT + tile) * kStateFloats * 64 + lane;
+    if (wave > 0 && wave < nw) {
+      float* d = gs + (wave - 1) * kStateFloats * 64 + lane;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -541,17 +600,15 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
       d[33 * 64] = st.l;
     }
     __syncthreads();
-    if (grp == 0) {
+    if (wave == 0) {
       float M = st.m;
-#pragma unroll
-      for (int g2 = 1; g2 < kGroups; ++g2) M = fmaxf(M, gs[((g2 - 1) * NQT + tile) * kStateFloats * 64 + 32 * 64 + lane]);
+      for (int w2 = 1; w2 < nw; ++w2) M = fmaxf(M, gs[(w2 - 1) * kStateFloats * 64 + 32 * 64 + lane]);
       const float w0 = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
       st.l *= w0;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= w0;
-#pragma unroll
-      for (int g2 = 1; g2 < kGroups; ++g2) {
-        const float* sp = gs + ((g2 - 1) * NQT + tile) * kStateFloats * 64 + lane;
+      for (int w2 = 1; w2 < nw; ++w2) {
+        const float* sp = gs + (w2 - 1) * kStateFloats * 64 + lane;
         const float m2 = sp[32 * 64];
         const float w = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
         st.l += w * sp[33 * 64];
@@ -563,12 +620,11 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
       st.m = M;
     }
   }
-  const bool ow = grp == 0;  // the waves that hold the run's state
   float lsum = st.l;
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (nruns == 1) {
-    if (ow) {
+    if (wave == 0) {
       const float inv = 1.f / lsum;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -593,63 +649,84 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
     return;
   }
 
-  // partial result of this run
-  const size_t base = ((size_t)b * a.Hkv + g) * a.max_splits;
-  const uint32_t units = (uint32_t)(a.B * a.Hkv * a.max_splits * a.nqp);
-  const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, units * 8);
-  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(a.part_o, units * kHeadDim * 4);
-  if (ow) {
-    const uint32_t u = (uint32_t)((base + r) * a.nqp + qi);
-    if (gl == 0) {
-      const u32x2 ml2 = {__float_as_uint(st.m), __float_as_uint(lsum)};
-      __builtin_amdgcn_raw_buffer_store_b64(ml2, rml, u * 8, 0, kCoherent);
-    }
+  // partial result of this run as words: unit ((b, g) run, query column)
+  const uint32_t ubase = (uint32_t)((b * a.Hkv + g) * f.runs);
+  const uint32_t units = (uint32_t)(a.B * a.Hkv * f.runs * a.nqp);
+  const __amdgpu_buffer_rsrc_t rml = make_rsrc(f.ll_ml, units * 16);
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(f.ll_po, units * kHeadDim * 8);
+  if (wave == 0) {
+    const uint32_t u = (ubase + r) * a.nqp + qi;
+    if (gl == 0) ll_store2(rml, u * 16, __float_as_uint(st.m), __float_as_uint(lsum), f.epoch);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[dt]), rpo, (u * kHeadDim + dt * 16 + 4 * gl) * 4,
-                                            0, kCoherent);
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint32_t o = (u * kHeadDim + dt * 16 + 4 * gl) * 8;
+      ll_store2(rpo, o, __float_as_uint(st.acc[dt][0]), __float_as_uint(st.acc[dt][1]), f.epoch);
+      ll_store2(rpo, o + 16, __float_as_uint(st.acc[dt][2]), __float_as_uint(st.acc[dt][3]), f.epoch);
+    }
   }
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) set_flag(fl_run(f, b, g) + r, f.epoch);
-  wait_flags(f, fl_run(f, b, g), nruns);
 
-  // merge of query columns [qa, qb): thread (column, 4-dim chunk c4) combines
-  // every run in run order, normalises, packs (with its neighbouring chunk)
-  const int qa = r * NQ / nruns, qb = (r + 1) * NQ / nruns;
-  for (int idx = threadIdx.x; idx < (qb - qa) * 32; idx += kFrontThreads) {
-    const int q = qa + (idx >> 5), c4 = idx & 31;
-    float mm[kFrontMaxRuns], ll[kFrontMaxRuns];
-    f32x4 o[kFrontMaxRuns];
+  // merge of the tile's columns [qa, qb): thread (column, 4-dim chunk c4,
+  // half hf) combines runs hf * 8 .. hf * 8 + 7 in run order, the two halves
+  // meet (half 0 first), and the column is normalised and packed (with the
+  // neighbouring chunk)
+  const int qa = q0 + r * 16 / nruns, qb = min(q0 + (r + 1) * 16 / nruns, NQ);
+  for (int idx = threadIdx.x; idx < (qb - qa) * 64; idx += kFrontThreads) {
+    const int q = qa + (idx >> 6), c4 = (idx >> 1) & 31, hf = idx & 1;
+    const int s0 = hf * 8, ns = min(8, nruns - s0);  // ns <= 0: no run in this half
+    u32x4 mlw[8], o0[8], o1[8];
+    for (int spins = 0;;) {
+      bool ok = true;
+      if (ns > 0) {
 #pragma unroll
-    for (int s = 0; s < kFrontMaxRuns; ++s) {
-      const uint32_t u = (uint32_t)((base + min(s, nruns - 1)) * a.nqp + q);
-      const u32x2 ml2 = __builtin_amdgcn_raw_buffer_load_b64(rml, u * 8, 0, kCoherent);
-      mm[s] = __uint_as_float(ml2[0]);
-      ll[s] = __uint_as_float(ml2[1]);
-      o[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpo, (u * kHeadDim + 4 * c4) * 4, 0, kCoherent));
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t u = (ubase + s0 + min(s, ns - 1)) * a.nqp + q;
+          mlw[s] = ll_load2(rml, u * 16);
+          o0[s] = ll_load2(rpo, (u * kHeadDim + 4 * c4) * 8);
+          o1[s] = ll_load2(rpo, (u * kHeadDim + 4 * c4) * 8 + 16);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) ok = ok && ll_ok(mlw[s], ep) && ll_ok(o0[s], ep) && ll_ok(o1[s], ep);
+      }
+      if (ll_round(f, ok, spins)) break;
     }
-    __builtin_amdgcn_sched_barrier(0);  // every run's request in flight at once
-    float nm = -INFINITY;
+    float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kFrontMaxRuns; ++s)
-      if (s < nruns) nm = fmaxf(nm, mm[s]);
+    for (int s = 0; s < 8; ++s)
+      if (s < ns) M = fmaxf(M, __uint_as_float(mlw[s][0]));
     float den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < kFrontMaxRuns; ++s) {
-      if (s < nruns) {
-        const float w = mm[s] == -INFINITY ? 0.f : exp2f(mm[s] - nm);
-        den += w * ll[s];
-        num += w * o[s];
+    for (int s = 0; s < 8; ++s) {
+      if (s < ns) {
+        const float ms = __uint_as_float(mlw[s][0]);
+        const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        den += w * __uint_as_float(mlw[s][2]);
+        const f32x4 os = {__uint_as_float(o0[s][0]), __uint_as_float(o0[s][2]), __uint_as_float(o1[s][0]),
+                          __uint_as_float(o1[s][2])};
+        num += w * os;
       }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    float v[4] = {num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+    // the two halves (lanes idx, idx ^ 1): half 0's terms first
+    const float Mo = __shfl_xor(M, 1), deno = __shfl_xor(den, 1);
+    f32x4 numo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) numo[e] = __shfl_xor(num[e], 1);
+    const float Mt = fmaxf(M, Mo);
+    const float wa = M == -INFINITY ? 0.f : exp2f(M - Mt), wb = Mo == -INFINITY ? 0.f : exp2f(Mo - Mt);
+    const float w0 = hf == 0 ? wa : wb, w1 = hf == 0 ? wb : wa;
+    const float d0 = hf == 0 ? den : deno, d1 = hf == 0 ? deno : den;
+    const float dtot = w0 * d0 + w1 * d1;
+    const float inv = dtot > 0.f ? 1.f / dtot : 0.f;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float n0 = hf == 0 ? num[e] : numo[e], n1 = hf == 0 ? numo[e] : num[e];
+      v[e] = (w0 * n0 + w1 * n1) * inv;
+    }
     float w4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w4[e] = __shfl_xor(v[e], 1);  // the neighbouring chunk
-    if ((c4 & 1) == 0) {
+    for (int e = 0; e < 4; ++e) w4[e] = __shfl_xor(v[e], 2);  // the neighbouring chunk
+    if (hf == 0 && (c4 & 1) == 0) {
       const float xv[8] = {v[0], v[1], v[2], v[3], w4[0], w4[1], w4[2], w4[3]};
       const int wr = q / G, hg = q - wr * G;
       const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + 4 * c4;
@@ -665,7 +742,6 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int r, unsigne
 
 }  // namespace
 
-template <int NQT>
 __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
   extern __shared__ __align__(16) unsigned char smem[];
   const AttnArgs& a = f.at;
@@ -686,10 +762,12 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
     const bool has_item = item >= 0 && item < f.n_items;
     const bool has_slice = slice < kFrontPackSlices;
     if (has_item) {
-      // the host keeps these workgroups free of QKV and O tiles
-      const int per_b = a.Hkv * f.runs;
-      const int b = item / per_b, g = (item - b * per_b) / f.runs, r = item % f.runs;
-      front_attention<NQT>(f, b, g, r, smem, has_slice ? slice : -1);
+      // the host keeps these workgroups free of QKV and O tiles; item =
+      // ((b * Hkv + g) * tiles + qt) * runs + r
+      const int tiles = a.nqp / 16;
+      const int r = item % f.runs, rest = item / f.runs;
+      const int qt = rest % tiles, bg = rest / tiles;
+      front_attention(f, bg / a.Hkv, bg % a.Hkv, qt, r, smem, has_slice ? slice : -1);
       stores_done();
       __syncthreads();
       if (threadIdx.x < kFlagCopies) set_flag(fl_ready(f, threadIdx.x) + item, f.epoch);
@@ -699,30 +777,21 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
   }
 }
 
-template <int NQT>
-static hipError_t launch_front_t(const FrontArgs& f, int grid, hipStream_t s) {
-  static bool attr = false;  // allow the LDS beyond the static default once per instantiation
+hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
+  if (!f.ll_q || !f.ll_kv || !f.ll_ml || !f.ll_po) return hipErrorInvalidValue;
+  if (f.runs > kFrontMaxRuns || f.n_parts > kFrontMaxParts || f.at.pages_per_split > kFrontMaxRunPages ||
+      f.H != kFrontK || f.HQ != kFrontK || f.T > 8 || f.n_o_tiles > f.n_qkv_tiles || f.at.nqp % 16 ||
+      f.at.nqp < 16 || f.at.nqp > 64 || f.n_items != f.at.B * f.at.Hkv * (f.at.nqp / 16) * f.runs ||
+      f.n_qkv_tiles + kFrontPackSlices > grid || f.n_qkv_tiles + f.n_items > grid || f.n_items > 128 || f.epoch <= 0)
+    return hipErrorInvalidValue;
+  static bool attr = false;  // allow the LDS beyond the static default once
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_front<NQT>, hipFuncAttributeMaxDynamicSharedMemorySize, kFrontLds);
+    const hipError_t e = hipFuncSetAttribute((const void*)k_front, hipFuncAttributeMaxDynamicSharedMemorySize, kFrontLds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(k_front<NQT>, dim3(grid), dim3(kFrontThreads), kFrontLds, s, f);
+  hipLaunchKernelGGL(k_front, dim3(grid), dim3(kFrontThreads), kFrontLds, s, f);
   return hipGetLastError();
-}
-
-hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
-  if (f.runs > kFrontMaxRuns || f.n_parts > kFrontMaxParts || f.at.pages_per_split > kFrontMaxRunPages ||
-      f.H != kFrontK || f.HQ != kFrontK || f.T > 8 || f.n_o_tiles > f.n_qkv_tiles ||
-      f.n_qkv_tiles + kFrontPackSlices > grid || f.n_qkv_tiles + f.n_items > grid || f.n_items > 128 || f.epoch <= 0)
-    return hipErrorInvalidValue;
-  switch (f.at.nqp / 16) {
-    case 1: return launch_front_t<1>(f, grid, s);
-    case 2: return launch_front_t<2>(f, grid, s);
-    case 3: return launch_front_t<3>(f, grid, s);
-    case 4: return launch_front_t<4>(f, grid, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace la

@@ -115,8 +115,9 @@ struct PrologueArgs {
   const int32_t* window_len;  // [B] real window rows (nullable)
   const int32_t* block_table;
   int max_blocks, num_blocks, cap;
-  int32_t* zero;             // nullable: n_zero words cleared (the front kernel's counters)
-  int n_zero;
+  int32_t* zero;             // nullable: n_zero words cleared (the front kernel's flags and words;
+  int n_zero;                 // 16-byte aligned, n_zero a multiple of 4) by zero_blocks extra workgroups
+  int zero_blocks;
   // prefill: ids / embeds hold in_w rows per sequence (rows j >= in_w of the
   // W are padding: zero input, no error); a negative id takes its row of
   // embeds ([B][in_w][H] fp32, nullable)
@@ -220,13 +221,23 @@ struct FrontArgs {
   float* ss;                  // [T][H / 16] per-tile sums of squares of h1
   int n_qkv_tiles, n_o_tiles, n_items, runs;  // attention items = B * Hkv * runs
   int32_t* sync;              // flag words (the step's prologue zeroes them)
-  int epoch;                  // the value this launch's flags take: layer index + 1
+  // Data handed from a few producers to a few consumers inside the launch, as
+  // 8-byte words {32-bit datum (low half), epoch (high half)} (the step's
+  // prologue zeroes them):
+  uint64_t* ll_q;             // [T][HQ] q after bias and RoPE (fp32 bits)
+  uint64_t* ll_kv;            // [T][Hkv][2 (K, V)][64]: bf16 of dims i (low) and i + 64 (high)
+  uint64_t* ll_ml;            // [units][2] per run and query column: max, sum
+  uint64_t* ll_po;            // [units][128] per run and query column: unnormalised O
+  int epoch;                  // the value this launch's flags and words take: layer index + 1
   int32_t* err;               // nullable
 };
 // Pages of one attention run of the front-half launch (the whole run sits in
 // LDS), and the slices its operand packing splits K = 2048 into.
 constexpr int kFrontMaxRunPages = 12;
 constexpr int kFrontPackSlices = 64;
+// Flag words of the front-half launch: pack [8 copies][64 slices], ready [8
+// copies][128 items].
+constexpr int kFrontSyncWords = 8 * 64 + 8 * 128;
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s);
 // Compute units of the current device (256 when the query fails).
 int cu_count();

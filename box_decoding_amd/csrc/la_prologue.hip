@@ -22,8 +22,13 @@ __device__ __forceinline__ bool prologue_id_bad(const PrologueArgs& a, int id) {
 __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  if (a.zero && t == 0)
-    for (int i = tid; i < a.n_zero; i += 256) a.zero[i] = 0;
+  if (t >= a.T) {
+    // the extra workgroups clear the front-half launch's flags and words
+    const int n4 = a.n_zero / 4, nb = gridDim.x - a.T;
+    uint4* z = (uint4*)a.zero;
+    for (int i = (t - a.T) * 256 + tid; i < n4; i += nb * 256) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   int id_bad = 0;
   if (a.ids) {
     const int src = prologue_src(a, t);
@@ -136,7 +141,9 @@ hipError_t launch_prefill_views(const int32_t* prefix_len, int B, int L, int chu
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_prologue, dim3(a.T), dim3(256), 0, s, a);
+  if (a.zero && ((uintptr_t)a.zero % 16 || a.n_zero % 4 || a.zero_blocks < 1)) return hipErrorInvalidValue;
+  const int zb = a.zero ? a.zero_blocks : 0;
+  hipLaunchKernelGGL(k_prologue, dim3(a.T + zb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
