@@ -297,6 +297,24 @@ def cpu_baseline(workload_name, sample_layers, min_seconds=10.0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def step_modes(B, dm, dc, ids, Pd, max_len, ws, out_ids, out_gap, timed, steps, warmup):
+    """The step launched kernel by kernel and as a replayed HIP graph, each
+    timed over `steps` steps after `warmup` untimed ones: (faster ms/step, its
+    mode)."""
+    def eager():
+        B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, out_gap=out_gap)
+
+    for _ in range(warmup):
+        eager()
+    e_ms, _ = timed(eager, steps)
+    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
+    for _ in range(warmup):
+        graph.replay()
+    g_ms, _ = timed(graph.replay, steps)
+    del graph
+    return (e_ms, "eager") if e_ms <= g_ms else (g_ms, "graph")
+
+
 def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
     """Steps/s of the batched step (32 ragged sequences, same model) and the
     useful matrix-core rate of its gate/up GEMM (192 rows), against the dense
@@ -314,11 +332,9 @@ def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
     ws = B.Workspace(dev)
     out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
     out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
-    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
-    for _ in range(max(2, args.warmup)):
-        graph.replay()
     steps = max(5, args.steps // 3)
-    ms_step, _ = timed(graph.replay, steps)
+    ms_step, mode = step_modes(B, dm, dc, ids, Pd, max_len, ws, out_ids, out_gap, timed, steps,
+                               max(2, args.warmup))
     sbytes = step_bytes(model, d, P, w.window)
     T = w.batch * w.window
     F, H = d.inter, d.hidden
@@ -338,10 +354,10 @@ def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
     tflops = flops / (k_ms * 1e-3) / 1e12
     log(f"bench: batch 32: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; "
         f"gate_up GEMM {k_ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s useful")
-    del graph, cache, dc, ws
+    del cache, dc, ws
     torch.cuda.synchronize()
     return {"workload": w.name, "batch": w.batch, "window": w.window, "steps": steps,
-            "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "ms_per_step": round(ms_step, 4), "launch": mode, "steps_per_s": round(1000.0 / ms_step, 3),
             "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
             "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
@@ -365,17 +381,15 @@ def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
     ws = B.Workspace(dev)
     out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
     out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
-    graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
-    for _ in range(max(2, args.warmup)):
-        graph.replay()
     steps = max(5, args.steps // 3)
-    ms_step, _ = timed(graph.replay, steps)
+    ms_step, mode = step_modes(B, dm, dc, ids, Pd, max_len, ws, out_ids, out_gap, timed, steps,
+                               max(2, args.warmup))
     sbytes = step_bytes(model, d, P, w.window)
     log(f"bench: prefix 32768: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s")
-    del graph, cache, dc, ws
+    del cache, dc, ws
     torch.cuda.synchronize()
     return {"workload": w.name, "batch": w.batch, "window": w.window, "prefix": int(P.max()),
-            "steps": steps, "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "steps": steps, "ms_per_step": round(ms_step, 4), "launch": mode, "steps_per_s": round(1000.0 / ms_step, 3),
             "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4)}
 
@@ -501,11 +515,14 @@ def sampling_leg(B, synth, torch, dm, model, dev, timed, args):
     for _ in range(max(2, args.warmup)):
         graph.replay()
     steps = max(5, args.steps // 3)
-    ms_step, _ = timed(graph.replay, steps)
-    log(f"bench: sampled step, batch 1: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s")
+    g_ms, _ = timed(graph.replay, steps)
+    e_ms, _ = timed(lambda: B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, want_gap=False,
+                                       sampling=smp), steps)
+    ms_step, mode = (e_ms, "eager") if e_ms <= g_ms else (g_ms, "graph")
+    log(f"bench: sampled step, batch 1: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s ({mode})")
     del graph, cache, dc, ws
     torch.cuda.synchronize()
-    return {"workload": w.name, "selection": "temperature 0.7, top-p 0.9", "steps": steps,
+    return {"workload": w.name, "selection": "temperature 0.7, top-p 0.9", "steps": steps, "launch": mode,
             "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3)}
 
 
@@ -565,11 +582,9 @@ def int4_leg(B, synth, torch, dev, stream, timed, args, name="step_int4_b8_p1280
     ws = B.Workspace(dev)
     out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
     out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
-    graph = B.StepGraph(dm, dc, ids, Pd, int(P.max()) + w.window, out_ids, out_gap, ws=ws)
-    for _ in range(max(2, args.warmup)):
-        graph.replay()
     steps = max(5, args.steps // 3)
-    ms_step, _ = timed(graph.replay, steps)
+    ms_step, mode = step_modes(B, dm, dc, ids, Pd, int(P.max()) + w.window, ws, out_ids, out_gap, timed, steps,
+                               max(2, args.warmup))
     sbytes = step_bytes(model, d, P, w.window)
     # its dominant kernel: gate/up with the SiLU epilogue at 48 rows
     T, F, H = w.batch * w.window, d.inter, d.hidden
@@ -588,10 +603,10 @@ def int4_leg(B, synth, torch, dev, stream, timed, args, name="step_int4_b8_p1280
     gu_bytes = gate_up_bytes(model["layers"][0]["gate_up"], T, H, F)
     log(f"bench: {w.wfmt} batch {w.batch}: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; gate_up "
         f"{k_ms * 1e3:.1f} us, {gu_bytes / k_ms / 1e6:.0f} GB/s")
-    del graph, cache, dc, ws, dm, model
+    del cache, dc, ws, dm, model
     torch.cuda.synchronize()
     return {"workload": w.name, "batch": w.batch, "window": w.window, "prefix": int(P.max()), "weights": w.wfmt,
-            "steps": steps, "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3),
+            "steps": steps, "ms_per_step": round(ms_step, 4), "launch": mode, "steps_per_s": round(1000.0 / ms_step, 3),
             "windows_per_s": round(1000.0 / ms_step * w.batch, 2),
             "step_hbm_gbps": round(sbytes / ms_step / 1e6, 1),
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
@@ -615,15 +630,13 @@ def causal_leg(B, synth, torch, model, dev, timed, args):
     ws = B.Workspace(dev)
     out_ids = torch.empty((w.batch, w.window), dtype=torch.int32, device=dev)
     out_gap = torch.empty((w.batch, w.window), dtype=torch.float32, device=dev)
-    graph = B.StepGraph(dmc, dc, ids, Pd, int(P.max()) + w.window, out_ids, out_gap, ws=ws)
-    for _ in range(max(2, args.warmup)):
-        graph.replay()
     steps = max(5, args.steps // 3)
-    ms_step, _ = timed(graph.replay, steps)
-    log(f"bench: causal window, batch 1: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s")
-    del graph, cache, dc, ws
+    ms_step, mode = step_modes(B, dmc, dc, ids, Pd, int(P.max()) + w.window, ws, out_ids, out_gap, timed,
+                               steps, max(2, args.warmup))
+    log(f"bench: causal window, batch 1: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s ({mode})")
+    del cache, dc, ws
     torch.cuda.synchronize()
-    return {"workload": w.name, "window_mask": "causal", "steps": steps,
+    return {"workload": w.name, "window_mask": "causal", "steps": steps, "launch": mode,
             "ms_per_step": round(ms_step, 4), "steps_per_s": round(1000.0 / ms_step, 3)}
 
 
@@ -698,16 +711,21 @@ def main():
     def eager():
         B.pbd_step(dm, dc, ids, Pd, max_len, ws=ws, out_ids=out_ids, out_gap=out_gap)
 
+    # the step launched kernel by kernel, and the same step captured once as a
+    # HIP graph and replayed: each timed over the K steps, the faster one is
+    # the value (a graph's per-node launch costs more here than it saves)
     for _ in range(args.warmup):
         eager()
     torch.cuda.synchronize()
-    eager_ms, _ = timed(eager, max(3, args.steps // 5))
-    # the serving loop replays the step as one captured graph
+    log(f"bench: warmup done, timing {args.steps} eager steps")
+    eager_ms, eager_wall = timed(eager, args.steps)
     graph = B.StepGraph(dm, dc, ids, Pd, max_len, out_ids, out_gap, ws=ws)
     for _ in range(args.warmup):
         graph.replay()
-    log(f"bench: warmup done (eager {eager_ms:.3f} ms/step), timing {args.steps} graph replays")
-    ms_step, wall_ms = timed(graph.replay, args.steps)
+    log(f"bench: eager {eager_ms:.3f} ms/step, timing {args.steps} graph replays")
+    graph_ms, graph_wall = timed(graph.replay, args.steps)
+    launch_mode = "eager" if eager_ms <= graph_ms else "graph"
+    ms_step, wall_ms = (eager_ms, eager_wall) if launch_mode == "eager" else (graph_ms, graph_wall)
     steps_per_s = 1000.0 / ms_step
     sbytes = step_bytes(model, d, P, w.window)
     log(f"bench: {ms_step:.3f} ms/step (wall {wall_ms:.3f} ms), "
@@ -788,6 +806,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "eager_ms_per_step": round(eager_ms, 5),
+        "graph_ms_per_step": round(graph_ms, 5),
+        "launch": launch_mode,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -481,7 +481,10 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int qt, int r,
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc, cache_bytes);
   // wave 0 packs its slice first (the pack's wait for its own stores would
   // otherwise also wait for the page copies)
-  if (slice >= 0 && wave == 0) front_pack(f, slice);
+  if (slice >= 0) {
+    if (wave == 0) front_pack(f, slice);
+    __syncthreads();  // the pages wait: the pack is on the QKV tiles' path, the pages are not
+  }
   // page j: wave w copies 1 KB piece w (pieces 0..3 of K, 4..7 of V^T); the
   // slots of window rows are overwritten below
   for (int j = 0; j < npages; ++j) {
@@ -583,68 +586,56 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int qt, int r,
       attn_pair(pr, k1 - p0, min(k1, kcol) - p0, qh, ql, st);
     }
   }
+  // the waves' states meet through the ring (every wave is done with the
+  // pages): wave w then combines slice dt = w of the output dims over the
+  // states in wave order, and stores it
   const int nw = min(npairs, kFrontWaves);  // waves that hold a state
-  if (nw > 1) {
-    // wave 0 takes in the other waves' states (wave order), through the ring:
-    // every wave is done with the pages
-    __syncthreads();
-    float* gs = (float*)ring;
-    constexpr int kStateFloats = 8 * 4 + 2;
-    if (wave > 0 && wave < nw) {
-      float* d = gs + (wave - 1) * kStateFloats * 64 + lane;
+  constexpr int kStateFloats = 8 * 4 + 2;
+  float* gs = (float*)ring;
+  __syncthreads();
+  if (wave < nw) {
+    float* d = gs + wave * kStateFloats * 64 + lane;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[(dt * 4 + e) * 64] = st.acc[dt][e];
-      d[32 * 64] = st.m;
-      d[33 * 64] = st.l;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      float M = st.m;
-      for (int w2 = 1; w2 < nw; ++w2) M = fmaxf(M, gs[(w2 - 1) * kStateFloats * 64 + 32 * 64 + lane]);
-      const float w0 = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
-      st.l *= w0;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= w0;
-      for (int w2 = 1; w2 < nw; ++w2) {
-        const float* sp = gs + (w2 - 1) * kStateFloats * 64 + lane;
-        const float m2 = sp[32 * 64];
-        const float w = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
-        st.l += w * sp[33 * 64];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st.acc[dt][e] += w * sp[(dt * 4 + e) * 64];
-      }
-      st.m = M;
-    }
+      for (int e = 0; e < 4; ++e) d[(dt * 4 + e) * 64] = st.acc[dt][e];
+    d[32 * 64] = st.m;
+    d[33 * 64] = st.l;
   }
-  float lsum = st.l;
+  __syncthreads();
+  const int dt = wave;
+  float M = -INFINITY;
+  for (int w2 = 0; w2 < nw; ++w2) M = fmaxf(M, gs[w2 * kStateFloats * 64 + 32 * 64 + lane]);
+  float lw = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int w2 = 0; w2 < nw; ++w2) {
+    const float* sp = gs + w2 * kStateFloats * 64 + lane;
+    const float m2 = sp[32 * 64];
+    const float w = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
+    lw += w * sp[33 * 64];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += w * sp[(dt * 4 + e) * 64];
+  }
+  float lsum = lw;
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (nruns == 1) {
-    if (wave == 0) {
-      const float inv = 1.f / lsum;
+    const float inv = 1.f / lsum;
+    float v[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        float v[8];
+    for (int e = 0; e < 4; ++e) {
+      v[e] = acc[e] * inv;
+      v[4 + e] = __shfl_xor(v[e], 16);
+    }
+    if (qi < NQ && (gl & 1) == 0) {
+      const int wr = qi / G, hg = qi - wr * G;
+      const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + dt * 16 + 4 * gl;
+      uint32_t hi[8], lo[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = st.acc[dt][e] * inv;
-          v[4 + e] = __shfl_xor(v[e], 16);
-        }
-        if (qi < NQ && (gl & 1) == 0) {
-          const int wr = qi / G, hg = qi - wr * G;
-          const int row = b * a.W + wr, col = (g * G + hg) * kHeadDim + dt * 16 + 4 * gl;
-          uint32_t hi[8], lo[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) split_hi_lo(v[e], hi[e], lo[e]);
-          const uint32_t off = ((uint32_t)(col >> 3) * 16 + row) * 16;
-          __builtin_amdgcn_raw_buffer_store_b128(pack8(hi), ro, off, 0, kCoherent);
-          __builtin_amdgcn_raw_buffer_store_b128(pack8(lo), ro, off + 128, 0, kCoherent);
-        }
-      }
+      for (int e = 0; e < 8; ++e) split_hi_lo(v[e], hi[e], lo[e]);
+      const uint32_t off = ((uint32_t)(col >> 3) * 16 + row) * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(hi), ro, off, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(lo), ro, off + 128, 0, kCoherent);
     }
     return;
   }
@@ -654,15 +645,12 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int qt, int r,
   const uint32_t units = (uint32_t)(a.B * a.Hkv * f.runs * a.nqp);
   const __amdgpu_buffer_rsrc_t rml = make_rsrc(f.ll_ml, units * 16);
   const __amdgpu_buffer_rsrc_t rpo = make_rsrc(f.ll_po, units * kHeadDim * 8);
-  if (wave == 0) {
+  {
     const uint32_t u = (ubase + r) * a.nqp + qi;
-    if (gl == 0) ll_store2(rml, u * 16, __float_as_uint(st.m), __float_as_uint(lsum), f.epoch);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint32_t o = (u * kHeadDim + dt * 16 + 4 * gl) * 8;
-      ll_store2(rpo, o, __float_as_uint(st.acc[dt][0]), __float_as_uint(st.acc[dt][1]), f.epoch);
-      ll_store2(rpo, o + 16, __float_as_uint(st.acc[dt][2]), __float_as_uint(st.acc[dt][3]), f.epoch);
-    }
+    if (wave == 0 && gl == 0) ll_store2(rml, u * 16, __float_as_uint(M), __float_as_uint(lsum), f.epoch);
+    const uint32_t o = (u * kHeadDim + dt * 16 + 4 * gl) * 8;
+    ll_store2(rpo, o, __float_as_uint(acc[0]), __float_as_uint(acc[1]), f.epoch);
+    ll_store2(rpo, o + 16, __float_as_uint(acc[2]), __float_as_uint(acc[3]), f.epoch);
   }
 
   // merge of the tile's columns [qa, qb): thread (column, 4-dim chunk c4,
