@@ -73,9 +73,6 @@ constexpr int kOutvOff = kRedOff + kFrontWaves * 64 * 16;
 constexpr int kQOff = kOutvOff + 8 * 17 * 4;                 // an attention item's q (hi, lo fragments)
 constexpr int kFrontLds = kQOff + 64 * 8 * 16;
 
-__device__ __forceinline__ int ld_flag(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void set_flag(int32_t* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -130,15 +127,21 @@ __device__ __forceinline__ bool ll_round(const FrontArgs& f, bool ok, int& spins
 }
 
 // The whole workgroup waits until p[0 .. n) (n <= 128) all hold the epoch
-// (wave 0 polls, two words per lane at most).
+// (wave 0 polls, two words per lane at most).  One poll in flight: more polls
+// of the same lines from the same waiters make the flag land later.
 __device__ __forceinline__ void wait_flags(const FrontArgs& f, const int32_t* p, int n) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int spins = 0;
-    for (;;) {
-      const int v0 = lane < n ? ld_flag(p + lane) : f.epoch;
-      const int v1 = lane + 64 < n ? ld_flag(p + lane + 64) : f.epoch;
-      if (__builtin_amdgcn_ballot_w64(v0 != f.epoch || v1 != f.epoch) == 0) break;  // uniform
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(p, (uint32_t)n * 4);
+    const uint32_t o0 = lane < n ? (uint32_t)lane * 4 : kNoRow;
+    const uint32_t o1 = lane + 64 < n ? (uint32_t)(lane + 64) * 4 : kNoRow;
+    const uint32_t ep = (uint32_t)f.epoch;
+    for (int spins = 0;;) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // every poll is a fresh load
+      const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(r, o0, 0, kCoherent);
+      const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(r, o1, 0, kCoherent);
+      // words past n read as zero and count as set
+      if (__builtin_amdgcn_ballot_w64((lane < n && a != ep) || (lane + 64 < n && b != ep)) == 0) break;
       if (++spins >= kSpinLimit) {
         if (lane == 0 && f.err) atomicOr(f.err, LA_DERR_SYNC);
         break;
@@ -384,11 +387,12 @@ __device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
   if (wave == 0) epi = qkv_epi_prepare(f, t);
   wait_flags(f, fl_pack(f, blockIdx.x % kFlagCopies), kFrontPackSlices);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.xpack, kFrontK / 8 * 256);
+  const bool live = (lane & 7) < f.T;  // operand rows r (hi) and r + 8 (lo) of window row r
   bf16x8 af[kFrontUnits];
 #pragma unroll
   for (int i = 0; i < kFrontUnits; ++i) {
     const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
-    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kCoherent));
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? (kc * 16 + (lane & 15)) * 16 : kNoRow, 0, kCoherent));
   }
   // wave 0: this lane's 8 of the 64 sums of squares of row lane / 8
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(f.ss_part, 8 * kFrontPackSlices * 4);
@@ -419,11 +423,12 @@ __device__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits
   }
   wait_flags(f, fl_ready(f, blockIdx.x % kFlagCopies), f.n_items);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.at.out_apack, kFrontK / 8 * 256);
+  const bool live = (lane & 7) < f.T;  // operand rows r (hi) and r + 8 (lo) of window row r
   bf16x8 af[kFrontUnits];
 #pragma unroll
   for (int i = 0; i < kFrontUnits; ++i) {
     const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
-    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, (kc * 16 + (lane & 15)) * 16, 0, kCoherent));
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? (kc * 16 + (lane & 15)) * 16 : kNoRow, 0, kCoherent));
   }
   __builtin_amdgcn_sched_barrier(0);  // all 8 requests in flight before the first product
   float* outv = (float*)(smem + kOutvOff);
@@ -513,6 +518,7 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int qt, int r,
       ((uint32_t)((b * a.W + qc / G) * a.Hq + g * G + qc % G) * kHeadDim + gl * 8) * 8;
   u32x4 xq[4][4], xw = {0u, 0u, 0u, 0u};
   for (int spins = 0;;) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // every poll is a fresh load
     bool ok = true;
     if (wave == 0) {
 #pragma unroll
@@ -663,6 +669,7 @@ __device__ void front_attention(const FrontArgs& f, int b, int g, int qt, int r,
     const int s0 = hf * 8, ns = min(8, nruns - s0);  // ns <= 0: no run in this half
     u32x4 mlw[8], o0[8], o1[8];
     for (int spins = 0;;) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // every poll is a fresh load
       bool ok = true;
       if (ns > 0) {
 #pragma unroll
