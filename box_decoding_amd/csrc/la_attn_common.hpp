@@ -82,6 +82,16 @@ __device__ __forceinline__ bf16x8 cat_s16x4(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// bf16 of a and b (round to nearest even, one hardware conversion), a in the
+// low half.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
 // One pair of pages (keys p0 .. p0 + nvalid - 1 valid, nvalid >= 1) into the
 // running state; this lane's query column sees the first nsc <= nvalid of
 // them (fewer under the causal window, possibly none).
@@ -140,8 +150,7 @@ __device__ __forceinline__ void attn_pair(PairRegs& pr, int nvalid, int nsc, con
     const uint32_t b0 = __float_as_uint(p[2 * i]), b1 = __float_as_uint(p[2 * i + 1]);
     const uint32_t h0 = b0 & 0xFFFF0000u, h1 = b1 & 0xFFFF0000u;
     H[i] = (h0 >> 16) | h1;
-    L[i] = f32_to_bf16_rne(p[2 * i] - __uint_as_float(h0)) |
-           (f32_to_bf16_rne(p[2 * i + 1] - __uint_as_float(h1)) << 16);
+    L[i] = cvt_bf16x2(p[2 * i] - __uint_as_float(h0), p[2 * i + 1] - __uint_as_float(h1));
   }
   const bf16x8 ph = __builtin_bit_cast(bf16x8, H), pl = __builtin_bit_cast(bf16x8, L);
 #pragma unroll
