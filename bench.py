@@ -54,8 +54,8 @@ def gate_up_bytes(w, T, H, F):
 TRAFFIC_KERNELS = {
     "gate_up": ("k_gemm<1, false, 1, 2>", ("la_gemm.hip", "la_gemm_common.hpp", "la_common.hpp"),
                 TRAFFIC_FILE, "k_gemm<1, false, 1, 2> (gate/up + SiLU, LDS-staged ring)"),
-    "front": ("k_front<", ("la_front.hip", "la_attn_common.hpp", "la_internal.hpp", "la_common.hpp"),
-              FRONT_TRAFFIC_FILE, "k_front<3> (front half of a layer: RMSNorm, QKV, attention, O)"),
+    "front": ("la::k_front(", ("la_front.hip", "la_attn_common.hpp", "la_internal.hpp", "la_common.hpp"),
+              FRONT_TRAFFIC_FILE, "k_front (front half of a layer: RMSNorm, QKV, attention, O)"),
 }
 
 
