@@ -68,7 +68,10 @@ struct Wide {
   // stages); INT4 reads its own stage's, one K step ahead
   static constexpr bool PREFETCH = !INT4;
   static constexpr int LA = NS - 1;                   // copy lead (stages)
-  static constexpr int R = INT4 ? 3 : 4;              // weight ring entries; loop unroll
+  // weight ring entries (and loop unroll): INT4 stages are short at 48-64 rows,
+  // so the gate/up layout keeps 3 stages ahead; the lm_head's layout (more
+  // accumulators) has registers for 2
+  static constexpr int R = INT4 && LAY != 3 ? 3 : 4;
   static constexpr int DW = R - 1;                    // weight lead (stages)
   static constexpr int NCOPY = RTW * CPU / 4 / WAVES;  // 1 KB copies per wave and stage
   static constexpr int NC = NCOPY + (INT4 ? 1 : 0);
@@ -801,7 +804,8 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   const int n_cb = (p.n_tiles + item - 1) / item;
   const int cus = big_cus();
   const int units = int4 ? K / 128 : K / 32;
-  const int dw = int4 ? Wide<2, true, 2>::R : Wide<6, false>::R;  // stages per ring turn
+  const int dw = int4 ? (p.lay == 3 ? Wide<2, true, 3>::R : Wide<2, true, 2>::R)
+                      : Wide<6, false>::R;  // stages per ring turn
   // K slices (QKV always writes slice sums; STORE when the caller takes them):
   // the fewest rounds of items times the padded stages of one item, plus the
   // slice sums' write and read-back counted in stage times (a stage of 192
