@@ -153,7 +153,7 @@ __device__ __forceinline__ void load_stage(Stage<INT4, MT, U, AIN>& b, const WPt
 
 template <int MT, bool INT4, int U, bool AIN>
 __device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U, AIN>& b, const ASrc& A,
-                                              int u, int ulo, int uhi, f32x4 (&acc)[MT]) {
+                                              int u, int ulo, int uhi, f32x4 (&acc)[MT], uint32_t i4bias) {
   const int g = (threadIdx.x & 63) >> 4;
   const int ulast = uhi > ulo ? uhi - 1 : ulo;
   if (!INT4) {
@@ -168,9 +168,9 @@ __device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U, AIN>& b, 
       }
     }
   } else {
-    // Every 4-byte word expands with two masks and an OR into four bf16 pairs
-    // holding 128 + q (k0 k4 | k1 k5 | k2 k6 | k3 k7), the order the packed
-    // activations use.  Per group: acc += scale * (sum - 136 * sum_k a_k), since
+    // Every 4-byte word expands (int4_to_bf16x8) into four bf16 pairs holding
+    // 128 + q (k0 k4 | k1 k5 | k2 k6 | k3 k7), the order the packed activations
+    // use.  Per group: acc += scale * (sum - 136 * sum_k a_k), since
     // sum a_k (128 + q_k) - 136 sum a_k = sum a_k (q_k - 8).
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -181,13 +181,7 @@ __device__ __forceinline__ void compute_stage(const Stage<INT4, MT, U, AIN>& b, 
       for (int mt = 0; mt < MT; ++mt) t[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = b.w[i][j];
-        u32x4 bb;
-        bb[0] = (w & 0x000F000Fu) | 0x43004300u;
-        bb[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-        bb[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-        bb[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, bb);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, int4_to_bf16x8(b.w[i][j], i4bias));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8 af = AIN ? b.af[AIN ? (INT4 ? 4 * i + j : i) : 0][mt] : a_frag(A, mt, uu * 16 + g * 4 + j);
@@ -587,6 +581,7 @@ void k_gemm(GemmArgs a) {
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const uint32_t i4bias = INT4 ? int4_bias_reg() : 0u;
 
   // a work item's partial sums: through LDS to one output tile (outv), which
   // the epilogue wave takes after the second barrier
@@ -619,7 +614,7 @@ void k_gemm(GemmArgs a) {
       if (D > 1) issue(bi + D - 1, st[(j + D - 1) % D]);
       else issue(bi, st[0]);
       if (MT <= 2) __builtin_amdgcn_sched_barrier(0);
-      compute_stage<MT, INT4, U, AIN>(st[j], A, u_of(bi), ulo, uhi, acc);
+      compute_stage<MT, INT4, U, AIN>(st[j], A, u_of(bi), ulo, uhi, acc, i4bias);
       if (bi % nb == nb - 1) finish_item();
       if (bi + 1 >= total) return;  // uniform
     }

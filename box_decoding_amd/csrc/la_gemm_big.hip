@@ -135,16 +135,6 @@ __device__ __forceinline__ void stage_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// bf16 lanes holding 128 + q for the 8 nibbles of w (two masks and an OR each).
-__device__ __forceinline__ bf16x8 int4_as_bf16(uint32_t w) {
-  u32x4 bb;
-  bb[0] = (w & 0x000F000Fu) | 0x43004300u;
-  bb[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  bb[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  bb[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-  return __builtin_bit_cast(bf16x8, bb);
-}
-
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 // D[32x32] += A[32x16] . B[16x32]: lane l holds A row l%32 and B column l%32
@@ -375,6 +365,7 @@ void k_gemm_big(GemmArgs a) {
   // INT4: one 128-group per stage, per group
   //   acc += scale * (sum_k a_k (128 + q_k) - 136 * sum_k a_k),
   // the fragments of step j + 1 read while step j multiplies
+  const uint32_t i4bias = INT4 ? int4_bias_reg() : 0u;
   auto compute_int4 = [&](int slot, const WStage& s) {
     if constexpr (INT4) {
       const unsigned char* A = frag_base(slot);
@@ -394,7 +385,7 @@ void k_gemm_big(GemmArgs a) {
         if (j < 3) read_frags(A, j + 1, fa[(j + 1) & 1]);
         bf16x8 bv[CT];
 #pragma unroll
-        for (int t = 0; t < CT; ++t) bv[t] = int4_as_bf16(s.w[t][j]);
+        for (int t = 0; t < CT; ++t) bv[t] = __builtin_bit_cast(bf16x8, int4_to_bf16x8(s.w[t][j], i4bias));
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll

@@ -9,6 +9,26 @@ namespace la {
 // ---------------------------------------------------------------- column maps
 
 // Weight row read by operand column c (0..15) of column tile `tile`.
+// INT4 weights in the matrix cores: a dword w of 8 nibbles becomes 4 dwords of
+// two bf16 each, nibbles k and k + 4 as 128 + q (bf16 0x4300 | q), so a group's
+// products carry 128 times the activation sum, removed with the group sums.
+// The bias lives in a vector register that the compiler cannot see into (an
+// empty asm), so shift, mask and bias are one v_lshrrev and one v_and_or_b32
+// per dword (gfx9 reads at most one scalar or literal operand per vector op).
+__device__ __forceinline__ uint32_t int4_bias_reg() {
+  uint32_t b = 0x43004300u;
+  asm volatile("" : "+v"(b));
+  return b;
+}
+__device__ __forceinline__ u32x4 int4_to_bf16x8(uint32_t w, uint32_t bias) {
+  u32x4 bb;
+  bb[0] = (w & 0x000F000Fu) | bias;
+  bb[1] = ((w >> 4) & 0x000F000Fu) | bias;
+  bb[2] = ((w >> 8) & 0x000F000Fu) | bias;
+  bb[3] = ((w >> 12) & 0x000F000Fu) | bias;
+  return bb;
+}
+
 template <int EPI>
 __device__ __forceinline__ int col_row(int N, int tile, int c) {
   if (EPI == EPI_SILU) {
