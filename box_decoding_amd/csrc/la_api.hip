@@ -410,6 +410,7 @@ struct AttnView {
 // environment, a diagnostic switch) each step is a kernel of its own.
 struct FrontPlan {
   int grid = 0, pps = 0, runs = 0, items = 0;
+  bool gate_up = false;  // the launch also runs gate/up (LA_PBD_FRONT_GU=0 in the environment turns it off)
 };
 
 FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max_len, const StepWs& s,
@@ -425,6 +426,9 @@ FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max
   f.pps = pps;
   f.runs = runs;
   f.items = B * m->n_kv_heads * (s.nqp / 16) * runs;
+  const char* gu = getenv("LA_PBD_FRONT_GU");
+  f.gate_up = !(gu && gu[0] == '0') && L.gate_up.fmt == LA_W_BF16 && L.gate_up.layout == LA_LAYOUT_TILED_GU &&
+              L.gate_up.k == m->hidden && m->inter % 8 == 0;
   return f;
 }
 
@@ -496,6 +500,14 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     f.n_o_tiles = H / 16;
     f.n_items = fp.items;
     f.runs = fp.runs;
+    if (fp.gate_up) {
+      weight_storage(&L.gate_up, &wb, &sb);
+      f.wgu = L.gate_up.data;
+      f.wgu_bytes = (uint32_t)wb;
+      f.F = m->inter;
+      f.n_gu_tiles = m->inter / 8;
+      f.mpack = s.apack_m;
+    }
     f.sync = s.sync;
     f.ll_q = s.ll_q;
     f.ll_kv = s.ll_kv;
@@ -602,14 +614,16 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
       LA_TRY(launch_gemm(g, EPI_STORE, LA_W_BF16, st));
     }
     if (ev) LA_TRY(hipEventRecord(ev[1], st));
-    // gate/up + 1/rms + SiLU, packed straight into the down operand
-    g = base_gemm(&L.gate_up, T);
-    g.apack = s.apack;
-    g.ss_in = s.ss;
-    g.ss_tiles = H / 16;
-    g.eps = m->rms_eps;
-    g.y_apack = s.apack_m;
-    LA_TRY(launch_gemm(g, EPI_SILU, LA_W_BF16, st));
+    if (!fp.gate_up) {
+      // gate/up + 1/rms + SiLU, packed straight into the down operand
+      g = base_gemm(&L.gate_up, T);
+      g.apack = s.apack;
+      g.ss_in = s.ss;
+      g.ss_tiles = H / 16;
+      g.eps = m->rms_eps;
+      g.y_apack = s.apack_m;
+      LA_TRY(launch_gemm(g, EPI_SILU, LA_W_BF16, st));
+    }
     // down projection: K-slice partial sums when its plan splits K (a sliced
     // stream over every compute unit beats an unsplit one; the next input
     // packing adds them up), else h += directly with h * next_gain packed for

@@ -66,9 +66,12 @@ static_assert(kSliceK == 32, "a pack slice is 4 chunks of 8 columns");
 
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
-// LDS: the attention role's page ring, then the reduction tiles.
+// LDS: the attention role's page ring, or (once a workgroup's front roles are
+// done) its first kGuPreload gate/up weight tiles; then the reduction tiles.
+constexpr int kTileBytes = kFrontK / 32 * 1024;  // one 16-column tile of a tiled weight (K = 2048)
+constexpr int kGuPreload = 2;
 constexpr int kRingBytes = kFrontMaxRunPages * kPageBytes;
-constexpr int kRedOff = kRingBytes;
+constexpr int kRedOff = kRingBytes > kGuPreload * kTileBytes ? kRingBytes : kGuPreload * kTileBytes;
 constexpr int kOutvOff = kRedOff + kFrontWaves * 64 * 16;
 constexpr int kQOff = kOutvOff + 8 * 17 * 4;                 // an attention item's q (hi, lo fragments)
 constexpr int kFrontLds = kQOff + 64 * 8 * 16;
@@ -78,6 +81,9 @@ __device__ __forceinline__ void set_flag(int32_t* p, int v) {
 }
 __device__ __forceinline__ void st_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u16(uint16_t* p, uint32_t v) {
+  __hip_atomic_store((short*)p, (short)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Stores made so far have reached the coherent level.
 __device__ __forceinline__ void stores_done() {
@@ -91,12 +97,16 @@ __device__ __forceinline__ u32x4 pack8(const uint32_t (&x)[8]) {
   return v;
 }
 
-// Flag arrays (ints): pack [kFlagCopies][64] (slice), ready [kFlagCopies][128] (item).
+// Flag arrays (ints): pack [kFlagCopies][64] (slice), ready [kFlagCopies][128]
+// (item), O done [kFlagCopies][128] (O tile).
 __device__ __forceinline__ int32_t* fl_pack(const FrontArgs& f, int copy) { return f.sync + copy * 64; }
 __device__ __forceinline__ int32_t* fl_ready(const FrontArgs& f, int copy) {
   return f.sync + kFlagCopies * 64 + copy * 128;
 }
-static_assert(kFlagCopies * (64 + 128) == kFrontSyncWords, "flag words the step carves");
+__device__ __forceinline__ int32_t* fl_odone(const FrontArgs& f, int copy) {
+  return f.sync + kFlagCopies * (64 + 128) + copy * 128;
+}
+static_assert(kFlagCopies * (64 + 128 + 128) == kFrontSyncWords, "flag words the step carves");
 
 // One 8-byte word {datum, epoch}.
 __device__ __forceinline__ void ll_store(uint64_t* p, uint32_t d, int epoch) {
@@ -319,13 +329,23 @@ __device__ void o_epilogue(const FrontArgs& f, int t, const float (&res)[2][1 + 
     q += __shfl_xor(q, 2);
     q += __shfl_xor(q, 4);
     q += __shfl_xor(q, 8);
-    if (ok && c == 0) f.ss[(size_t)ml * (f.H / 16) + t] = q;
+    // read by the gate/up tiles of this launch when it runs them (agent-scope
+    // stores), else by the next kernel
+    if (ok && c == 0) {
+      if (f.wgu) st_f32(f.ss + (size_t)ml * (f.H / 16) + t, q);
+      else f.ss[(size_t)ml * (f.H / 16) + t] = q;
+    }
     if (ok) {
       uint32_t hb, lb;
       split_hi_lo(v * gain, hb, lb);
       const size_t base = ((size_t)(n >> 3) * 16 + ml) * 8 + (n & 7);
-      f.gpack[base] = (uint16_t)hb;
-      f.gpack[base + 64] = (uint16_t)lb;
+      if (f.wgu) {
+        st_u16(f.gpack + base, hb);
+        st_u16(f.gpack + base + 64, lb);
+      } else {
+        f.gpack[base] = (uint16_t)hb;
+        f.gpack[base + 64] = (uint16_t)lb;
+      }
     }
   }
 }
@@ -433,7 +453,114 @@ __device__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits
   __builtin_amdgcn_sched_barrier(0);  // all 8 requests in flight before the first product
   float* outv = (float*)(smem + kOutvOff);
   tile_reduce(af, wo, wave, (f32x4*)(smem + kRedOff), outv);
-  if (wave == 0) o_epilogue(f, t, res, gain, outv);
+  if (wave == 0) {
+    o_epilogue(f, t, res, gain, outv);
+    if (f.wgu) {
+      stores_done();
+      if (lane < kFlagCopies) set_flag(fl_odone(f, lane) + t, f.epoch);
+    }
+  }
+}
+
+// The first kGuPreload gate/up tiles of this workgroup (tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ...) copied into LDS in the tiled weight's byte
+// order (direct-to-LDS loads; wave w copies units 8w .. 8w + 7).  The caller's
+// roles no longer use LDS below kRedOff.
+__device__ void gu_preload(const FrontArgs& f, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.wgu, f.wgu_bytes);
+  for (int p = 0; p < kGuPreload; ++p) {
+    const int j = (int)blockIdx.x + p * (int)gridDim.x;
+    if (j >= f.n_gu_tiles) break;  // uniform
+#pragma unroll
+    for (int i = 0; i < kFrontUnits; ++i) {
+      const uint32_t u = (uint32_t)wave * kFrontUnits + i;
+      void __attribute__((address_space(3)))* dst =
+          (void __attribute__((address_space(3)))*)(smem + p * kTileBytes + u * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, (uint32_t)lane * 16, ((uint32_t)j * (kFrontK / 32) + u) * 1024,
+                                               0, kNonTemporal);
+    }
+  }
+}
+
+// Gate/up epilogue of tile j (wave 0, lane (row lane / 8, column lane % 8)):
+// silu(gate / rms) * (up / rms) as bf16 hi / lo into the down operand.
+__device__ __forceinline__ void gu_epilogue(const FrontArgs& f, int j, const float* outv, float inv) {
+  const int lane = threadIdx.x & 63, ml = lane >> 3, c = lane & 7;
+  if (ml >= f.T) return;
+  const float v = silu_f(outv[ml * 17 + c] * inv) * (outv[ml * 17 + c + 8] * inv);
+  const int n = j * 8 + c;
+  uint32_t h, l;
+  split_hi_lo(v, h, l);
+  const size_t base = ((size_t)(n >> 3) * 16 + ml) * 8 + (n & 7);
+  f.mpack[base] = (uint16_t)h;
+  f.mpack[base + 64] = (uint16_t)l;
+}
+
+// The gate/up role of every workgroup: its tiles blockIdx.x + k gridDim.x.
+// The first streamed tile's weights are requested before the wait; once every
+// O tile is done the packed post-norm operand and the rows' 1 / rms are read
+// (agent scope), the preloaded tiles multiply from LDS and the rest stream
+// through two register buffers.
+__device__ void front_gateup(const FrontArgs& f, unsigned char* smem) {
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x, j0 = blockIdx.x;
+  if (j0 >= f.n_gu_tiles) return;  // uniform
+  const int js = j0 + kGuPreload * G;  // first streamed tile
+  u32x4 wa[kFrontUnits], wb[kFrontUnits];
+  if (js < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js, wave, wa);
+  wait_flags(f, fl_odone(f, blockIdx.x % kFlagCopies), f.n_o_tiles);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.gpack, kFrontK / 8 * 256);
+  const bool live = (lane & 7) < f.T;  // operand rows r (hi) and r + 8 (lo) of window row r
+  bf16x8 af[kFrontUnits];
+#pragma unroll
+  for (int i = 0; i < kFrontUnits; ++i) {
+    const uint32_t kc = (uint32_t)(wave * kFrontUnits + i) * 4 + g4;
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? (kc * 16 + (lane & 15)) * 16 : kNoRow, 0, kCoherent));
+  }
+  // wave 0: 1 / rms of row lane / 8 from the O tiles' 128 sums of squares
+  float inv = 0.f;
+  if (wave == 0) {
+    const int ml = lane >> 3;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(f.ss, (uint32_t)f.T * (f.H / 16) * 4);
+    const uint32_t so = ml < f.T ? ((uint32_t)ml * (f.H / 16) + (lane & 7) * 16) * 4 : kNoRow;
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, so + k * 16, 0, kCoherent));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t += __uint_as_float(v[e]);
+    }
+    t += __shfl_xor(t, 1);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 4);
+    inv = 1.0f / sqrtf(t / (float)f.H + f.eps);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's preload copies (and everything before them)
+  __syncthreads();
+  float* outv = (float*)(smem + kOutvOff);
+  f32x4* red = (f32x4*)(smem + kRedOff);
+  for (int p = 0; p < kGuPreload; ++p) {
+    const int j = j0 + p * G;
+    if (j >= f.n_gu_tiles) return;  // uniform: no streamed tile either
+    u32x4 wf[kFrontUnits];
+#pragma unroll
+    for (int i = 0; i < kFrontUnits; ++i)
+      wf[i] = *(const u32x4*)(smem + p * kTileBytes + (((uint32_t)wave * kFrontUnits + i) * 64 + lane) * 16);
+    tile_reduce(af, wf, wave, red, outv);
+    if (wave == 0) gu_epilogue(f, j, outv, inv);
+  }
+  for (int j = js; j < f.n_gu_tiles; j += 2 * G) {
+    if (j + G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + G, wave, wb);
+    tile_reduce(af, wa, wave, red, outv);
+    if (wave == 0) gu_epilogue(f, j, outv, inv);
+    if (j + G >= f.n_gu_tiles) break;  // uniform
+    if (j + 2 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 2 * G, wave, wa);
+    tile_reduce(af, wb, wave, red, outv);
+    if (wave == 0) gu_epilogue(f, j + G, outv, inv);
+  }
 }
 
 // One attention item: sequence b, KV head g, query tile qt (query columns
@@ -748,10 +875,14 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
   if (w < f.n_qkv_tiles) {
     front_qkv(f, w, smem);
     if (w < f.n_o_tiles) {
-      // the O weights stream in while the attention runs
+      // the O weights stream in while the attention runs (and the first
+      // gate/up tiles into LDS after them)
       u32x4 wo[kFrontUnits];
       load_tile_weights(f.wo, f.wo_bytes, w, wave, wo);
+      if (f.wgu) gu_preload(f, smem);
       front_o(f, w, wo, smem);
+    } else if (f.wgu) {
+      gu_preload(f, smem);
     }
   } else {
     const bool has_item = item >= 0 && item < f.n_items;
@@ -764,16 +895,21 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
       const int qt = rest % tiles, bg = rest / tiles;
       front_attention(f, bg / a.Hkv, bg % a.Hkv, qt, r, smem, has_slice ? slice : -1);
       stores_done();
-      __syncthreads();
+      __syncthreads();  // every wave is also done with the page ring
       if (threadIdx.x < kFlagCopies) set_flag(fl_ready(f, threadIdx.x) + item, f.epoch);
     } else if (has_slice && wave == 0) {
       front_pack(f, slice);
     }
+    if (f.wgu) gu_preload(f, smem);
   }
+  if (f.wgu) front_gateup(f, smem);
 }
 
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
   if (!f.ll_q || !f.ll_kv || !f.ll_ml || !f.ll_po) return hipErrorInvalidValue;
+  if (f.wgu && (!f.mpack || f.F != f.n_gu_tiles * 8 || f.n_gu_tiles < 1 ||
+                (size_t)f.n_gu_tiles * kTileBytes > f.wgu_bytes))
+    return hipErrorInvalidValue;
   if (f.runs > kFrontMaxRuns || f.n_parts > kFrontMaxParts || f.at.pages_per_split > kFrontMaxRunPages ||
       f.H != kFrontK || f.HQ != kFrontK || f.T > 8 || f.n_o_tiles > f.n_qkv_tiles || f.at.nqp % 16 ||
       f.at.nqp < 16 || f.at.nqp > 64 || f.n_items != f.at.B * f.at.Hkv * (f.at.nqp / 16) * f.runs ||

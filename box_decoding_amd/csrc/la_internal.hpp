@@ -219,6 +219,13 @@ struct FrontArgs {
   const uint16_t* post_norm;
   uint16_t* gpack;            // packed gate/up operand: h1 * post_norm
   float* ss;                  // [T][H / 16] per-tile sums of squares of h1
+  // gate/up in the same launch (nullable wgu: the launch ends after O): the
+  // tiled gate/up weight, F / 8 tiles of 8 gate and 8 up columns, the packed
+  // down operand silu(gate) * up it writes (bf16 hi / lo, K = F)
+  const void* wgu;
+  uint32_t wgu_bytes;
+  int n_gu_tiles, F;
+  uint16_t* mpack;
   int n_qkv_tiles, n_o_tiles, n_items, runs;  // attention items = B * Hkv * runs
   int32_t* sync;              // flag words (the step's prologue zeroes them)
   // Data handed from a few producers to a few consumers inside the launch, as
@@ -236,8 +243,8 @@ struct FrontArgs {
 constexpr int kFrontMaxRunPages = 12;
 constexpr int kFrontPackSlices = 64;
 // Flag words of the front-half launch: pack [8 copies][64 slices], ready [8
-// copies][128 items].
-constexpr int kFrontSyncWords = 8 * 64 + 8 * 128;
+// copies][128 items], O tiles done [8 copies][128 tiles].
+constexpr int kFrontSyncWords = 8 * 64 + 8 * 128 + 8 * 128;
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s);
 // Compute units of the current device (256 when the query fails).
 int cu_count();
