@@ -499,7 +499,7 @@ __device__ __forceinline__ void gu_epilogue(const FrontArgs& f, int j, const flo
 }
 
 // The gate/up role of every workgroup: its tiles blockIdx.x + k gridDim.x.
-// The first streamed tile's weights are requested before the wait; once every
+// The first two streamed tiles' weights are requested before the wait; once every
 // O tile is done the packed post-norm operand and the rows' 1 / rms are read
 // (agent scope), the preloaded tiles multiply from LDS and the rest stream
 // through two register buffers.
@@ -511,6 +511,7 @@ __device__ void front_gateup(const FrontArgs& f, unsigned char* smem) {
   const int js = j0 + kGuPreload * G;  // first streamed tile
   u32x4 wa[kFrontUnits], wb[kFrontUnits];
   if (js < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js, wave, wa);
+  if (js + G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js + G, wave, wb);
   wait_flags(f, fl_odone(f, blockIdx.x % kFlagCopies), f.n_o_tiles);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.gpack, kFrontK / 8 * 256);
   const bool live = (lane & 7) < f.T;  // operand rows r (hi) and r + 8 (lo) of window row r
@@ -552,13 +553,14 @@ __device__ void front_gateup(const FrontArgs& f, unsigned char* smem) {
     tile_reduce(af, wf, wave, red, outv);
     if (wave == 0) gu_epilogue(f, j, outv, inv);
   }
+  // two tiles in flight: each buffer is refilled right after its product
   for (int j = js; j < f.n_gu_tiles; j += 2 * G) {
-    if (j + G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + G, wave, wb);
     tile_reduce(af, wa, wave, red, outv);
+    if (j + 2 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 2 * G, wave, wa);
     if (wave == 0) gu_epilogue(f, j, outv, inv);
     if (j + G >= f.n_gu_tiles) break;  // uniform
-    if (j + 2 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 2 * G, wave, wa);
     tile_reduce(af, wb, wave, red, outv);
+    if (j + 3 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 3 * G, wave, wb);
     if (wave == 0) gu_epilogue(f, j + G, outv, inv);
   }
 }
@@ -897,8 +899,11 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
       stores_done();
       __syncthreads();  // every wave is also done with the page ring
       if (threadIdx.x < kFlagCopies) set_flag(fl_ready(f, threadIdx.x) + item, f.epoch);
-    } else if (has_slice && wave == 0) {
-      front_pack(f, slice);
+    } else if (has_slice) {
+      if (wave == 0) front_pack(f, slice);
+      // the other waves' gate/up loads wait: in the same compute unit they
+      // would queue ahead of the pack's, which every QKV tile waits for
+      __syncthreads();
     }
     if (f.wgu) gu_preload(f, smem);
   }
