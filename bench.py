@@ -51,11 +51,18 @@ def gate_up_bytes(w, T, H, F):
 
 # The kernels with counter-based traffic: (name in the profile, sources it is
 # built from, summary file).
+BIG_SOURCES = ("la_gemm_big.hip", "la_gemm_common.hpp", "la_common.hpp")
 TRAFFIC_KERNELS = {
     "gate_up": ("k_gemm<1, false, 1, 2>", ("la_gemm.hip", "la_gemm_common.hpp", "la_common.hpp"),
                 TRAFFIC_FILE, "k_gemm<1, false, 1, 2> (gate/up + SiLU, LDS-staged ring)"),
+    "gate_up_b32": ("k_gemm_big<3, false, 1, 1>", BIG_SOURCES,
+                    os.path.join(ROOT, "profiles", "gate_up_traffic_step_b32_ragged.json"),
+                    "k_gemm_big<3, false, 1, 1> (gate/up + SiLU, 192 rows, 96-column items)"),
+    "gate_up_int4": ("k_gemm_big<2, true, 1, 3>", BIG_SOURCES,
+                     os.path.join(ROOT, "profiles", "gate_up_traffic_step_int4_b8_p1280.json"),
+                     "k_gemm_big<2, true, 1, 3> (INT4 gate/up + SiLU, 48 rows, eight waves)"),
     "front": ("la::k_front(", ("la_front.hip", "la_attn_common.hpp", "la_internal.hpp", "la_common.hpp"),
-              FRONT_TRAFFIC_FILE, "k_front (front half of a layer: RMSNorm, QKV, attention, O)"),
+              FRONT_TRAFFIC_FILE, "k_front (front half of a layer: RMSNorm, QKV, attention, O, gate/up + SiLU)"),
 }
 
 
@@ -78,6 +85,26 @@ def front_bytes(lay, dims, prefix_len, W):
     total += T * H * 4
     total += T * H * 4 + T * (H // 16) * 4 + 2 * T * H * 2
     return total
+
+
+def fused_front_bytes(lay, dims, prefix_len, W):
+    """Algorithmic bytes of the front-half launch when it also runs the gate/up
+    projection: the front half's bytes and the gate/up weights once, the
+    packed SiLU output (bf16 hi + lo of T rows) written once; the packed
+    post-norm operand and its sums of squares stay inside the launch."""
+    T = len(prefix_len) * W
+    H, F = dims.hidden, dims.inter
+    total = front_bytes(lay, dims, prefix_len, W)
+    total -= T * (H // 16) * 4 + 2 * T * H * 2
+    return total + weight_bytes(lay["gate_up"]) + T * F * 4
+
+
+def front_fuses_gate_up(w, row_major):
+    """Whether the library's front-half launch also runs gate/up: bf16 tiled
+    weights at up to 8 rows, unless LA_PBD_FRONT_GU=0 turns it off."""
+    return (w.batch * w.window <= 8 and w.wfmt == "bf16" and not row_major
+            and os.environ.get("LA_PBD_FRONT_GU", "1") != "0"
+            and os.environ.get("LA_PBD_FRONT", "1") != "0")
 
 
 def kernel_source_digest(which="gate_up"):
@@ -113,6 +140,7 @@ def pmc_summary(fetch_db, write_db):
 
 
 def pmc_summary_one(fetch_db, write_db, which):
+    """One kernel's summary; a kernel the runs did not dispatch is skipped."""
     pattern, _, out_path, label = TRAFFIC_KERNELS[which]
     import sqlite3
 
@@ -127,6 +155,8 @@ def pmc_summary_one(fetch_db, write_db, which):
     def summarize(db, counter):
         rows = per_kernel(db, counter)
         gu = [v for name, _, v in rows if pattern in name]
+        if not gu:
+            return None
         # the calibration copy is the runtime's copy kernel moving CAL_COPY_BYTES,
         # the largest such dispatch of the run
         copies = [v for name, _, v in rows if name.startswith("__amd_rocclr_copyBuffer")]
@@ -134,8 +164,11 @@ def pmc_summary_one(fetch_db, write_db, which):
         factor = CAL_COPY_BYTES / (cal * 1024.0)
         return sum(gu) / len(gu) * 1024.0 * factor, factor, len(gu), cal
 
-    f_bytes, f_factor, n_f, f_cal = summarize(fetch_db, "FETCH_SIZE")
-    w_bytes, w_factor, n_w, w_cal = summarize(write_db, "WRITE_SIZE")
+    fs, ws = summarize(fetch_db, "FETCH_SIZE"), summarize(write_db, "WRITE_SIZE")
+    if fs is None or ws is None:
+        return
+    f_bytes, f_factor, n_f, f_cal = fs
+    w_bytes, w_factor, n_w, w_cal = ws
     rec = {
         "kernel": label,
         "kernel_source_sha256_16": kernel_source_digest(which),
@@ -350,6 +383,7 @@ def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
             B.wgemm_packed(packed, T, model["layers"][r % d.n_layers]["gate_up"], silu_gate=True, out=yout)
 
     k_ms = timed(gemm, 1)[0] / reps
+    gu_bytes = gate_up_bytes(model["layers"][0]["gate_up"], T, H, F)
     flops = 2.0 * T * H * 2 * F
     tflops = flops / (k_ms * 1e-3) / 1e12
     log(f"bench: batch 32: {ms_step:.3f} ms/step, {1000.0 / ms_step:.1f} steps/s; "
@@ -364,7 +398,8 @@ def batch32_leg(B, synth, torch, dm, model, dev, stream, timed, args):
             "gate_up_gemm": {"rows": T, "launch_us": round(k_ms * 1e3, 2),
                              "useful_tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                              "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "matrix_core_frac_with_hi_lo": round(2 * tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+                             "matrix_core_frac_with_hi_lo": round(2 * tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "bytes_per_launch": gu_bytes, "traffic": measured_traffic("gate_up_b32")}}
 
 
 def probe_leg(B, synth, torch, dm, model, dev, stream, timed, args):
@@ -612,7 +647,8 @@ def int4_leg(B, synth, torch, dev, stream, timed, args, name="step_int4_b8_p1280
             "step_hbm_frac": round(sbytes / ms_step / 1e6 / HBM_PEAK_GBPS, 4),
             "gate_up_gemm": {"rows": T, "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes,
                              "gbps": round(gu_bytes / k_ms / 1e6, 1),
-                             "frac": round(gu_bytes / k_ms / 1e6 / HBM_PEAK_GBPS, 4)}}
+                             "frac": round(gu_bytes / k_ms / 1e6 / HBM_PEAK_GBPS, 4),
+                             "traffic": measured_traffic("gate_up_int4") if w.wfmt == "int4" else None}}
 
 
 def causal_leg(B, synth, torch, model, dev, timed, args):
@@ -746,10 +782,13 @@ def main():
         if r:
             block_ms.extend(bev.ms())
     front_us = sum(block_ms) / len(block_ms) * 1e3
-    fbytes = sum(front_bytes(lay, d, P, w.window) for lay in model["layers"]) / d.n_layers
+    fused = front_fuses_gate_up(w, args.row_major)
+    fb = fused_front_bytes if fused else front_bytes
+    fbytes = sum(fb(lay, d, P, w.window) for lay in model["layers"]) / d.n_layers
     front_gbps = fbytes / (front_us * 1e-6) / 1e9
     front_launch = w.batch * w.window <= 8 and w.wfmt == "bf16" and not args.row_major
-    log(f"bench: attention block (front-half launch) {front_us:.1f} us, {front_gbps:.0f} GB/s")
+    log(f"bench: attention block (front-half launch{' + gate/up' if fused else ''}) "
+        f"{front_us:.1f} us, {front_gbps:.0f} GB/s")
 
     # The weight-streaming kernel with the most bytes: the gate/up projection
     # with the SiLU epilogue (58% of a layer's weight bytes), the GEMM alone on
@@ -783,9 +822,11 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst
-    # the counters were taken on the batch-1 tiled workload's launches
+    # the counters were taken on each workload's own tiled launches
     b1 = args.workload == "step_b1_p1280" and not args.row_major
-    traffic = measured_traffic("gate_up") if b1 else None
+    gu_kernel = {"step_b1_p1280": "gate_up", "step_b32_ragged": "gate_up_b32",
+                 "step_int4_b8_p1280": "gate_up_int4"}.get(args.workload)
+    traffic = measured_traffic(gu_kernel) if gu_kernel and not args.row_major else None
     front_traffic = measured_traffic("front") if b1 else None
 
     roof_gu = {"bound": "hbm", "kernel": "gate_up GEMM + SiLU (la_wgemm_packed)",
@@ -793,7 +834,8 @@ def main():
                "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes}
     roof_front = {"bound": "hbm",
-                  "kernel": "front half of a layer, one persistent launch (k_front: RMSNorm, QKV, attention, O)",
+                  "kernel": "front half of a layer, one persistent launch (k_front: RMSNorm, QKV, attention, O"
+                            + (", gate/up + SiLU)" if fused else ")"),
                   "achieved": round(front_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": round(front_gbps / HBM_PEAK_GBPS, 4), "traffic": front_traffic,
                   "launch_us": round(front_us, 2), "bytes_per_launch": round(fbytes)}

@@ -434,16 +434,22 @@ def step_workspace_bytes(model: DeviceModel, B: int, W: int, max_len: int) -> in
 
 class BlockEvents:
     """2 * n_layers HIP events for la_step_opts.block_events: the time of each
-    layer's attention block in a step (ms() after the step has finished)."""
+    layer's attention block in a step (ms() after the step has finished, and
+    after a device synchronisation: the events are made for timing only,
+    without the system-scope fence whose cache writeback and invalidation
+    would add to the interval they bracket)."""
+
+    _DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self, n_layers: int):
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventElapsedTime.argtypes = [POINTER(c_float), c_void_p, c_void_p]
+        self._hip.hipEventCreateWithFlags.argtypes = [POINTER(c_void_p), ctypes.c_uint]
         self.n = 2 * n_layers
         self.events = (c_void_p * self.n)()
         for i in range(self.n):
             h = c_void_p()
-            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(h), self._DISABLE_SYSTEM_FENCE) != 0:
                 raise LaError("hipEventCreate failed")
             self.events[i] = h
         self.address = ctypes.addressof(self.events)

@@ -387,7 +387,9 @@ la_status la_sample_logits(const float* logits, int32_t M, int32_t V, int32_t ld
  *  - block_events: NULL, or 2 * n_layers events (created by the caller) for
  *    timing: block_events[2 l] is recorded on the stream before layer l's
  *    attention block (input RMSNorm, QKV, attention, O projection) and
- *    block_events[2 l + 1] after it. */
+ *    block_events[2 l + 1] after the launch that ends it (with bf16 tiled
+ *    weights at up to 8 rows that one launch also runs the gate/up
+ *    projection, unless LA_PBD_FRONT_GU=0). */
 typedef struct {
   const int32_t* causal_rows;
   const int32_t* window_len;
