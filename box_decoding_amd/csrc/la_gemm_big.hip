@@ -40,11 +40,14 @@ constexpr int kPfSink = 1024;  // LDS bytes the L2 prefetches land in (never rea
 // workgroups for a GEMM that cannot take K slices); 2: 4 x 2, eight waves
 // (two per SIMD, so one wave's other instructions run beside another's
 // products); 3 (INT4): 4 x 2 with 3 tiles of 16 columns per column wave
-// (items of 96 columns: more workgroups for the gate/up projection).
-constexpr int lay_row_waves(int lay) { return lay == 0 ? 2 : 4; }
+// (items of 96 columns: more workgroups for the gate/up projection); 4
+// (INT4, up to 48 rows): 2 row waves of 3 row tiles x 2 column waves of 3
+// tiles, four waves (the launch's rows fill the row tiles exactly, and each
+// expanded weight fragment feeds three products).
+constexpr int lay_row_waves(int lay) { return lay == 0 || lay == 4 ? 2 : 4; }
 constexpr int lay_col_waves(int lay) { return lay == 1 ? 1 : 2; }
 constexpr int lay_threads(int lay) { return lay_row_waves(lay) * lay_col_waves(lay) * 64; }
-constexpr int lay_waves_per_eu(int lay) { return lay >= 2 ? 2 : 1; }
+constexpr int lay_waves_per_eu(int lay) { return lay == 2 || lay == 3 ? 2 : 1; }
 
 template <int RT, bool INT4, int LAY = 0>
 struct Wide {
@@ -54,14 +57,15 @@ struct Wide {
   static constexpr int RWV = lay_row_waves(LAY), CW = lay_col_waves(LAY), WAVES = RWV * CW;
   static constexpr int RTW = RWV * RT * (INT4 ? 1 : 2);  // packed 16-row tiles of a launch
   static constexpr int NP = INT4 ? RT : 2 * RT;       // epilogue parts of 8 real rows per row wave
-  static constexpr int CT = INT4 ? (LAY == 3 ? 3 : 4) : (LAY == 1 ? 3 : 2);
+  static constexpr int CT = INT4 ? (LAY >= 3 ? 3 : 4) : (LAY == 1 ? 3 : 2);
   static constexpr int TPW = INT4 ? CT : 2 * CT;      // 16-column tiles per column wave
   static constexpr int ITEM = CW * TPW;               // 16-column tiles per work item
   static constexpr int SW = TPW * 16;                 // staged columns per wave
   static constexpr int NG = SW / 8;                   // 8-column epilogue groups per staged row
   static constexpr int CPU = INT4 ? 16 : 4;           // 256-byte chunks per packed tile and K unit
   static constexpr int FR = INT4 ? RT : 2 * RT;       // fragments per bf16 stage / INT4 K step
-  static constexpr int SUMS = INT4 ? RTW * 64 : 0;    // INT4 group sums of a slot (bytes)
+  static constexpr int SUMP = (RTW + 3) / 4;           // INT4 group-sum pieces of 256 B (4 row tiles each)
+  static constexpr int SUMS = INT4 ? SUMP * 256 : 0;  // INT4 group sums of a slot (bytes)
   static constexpr int SLOT = RTW * CPU * 256 + SUMS;
   static constexpr int NS = INT4 ? 4 : 6;             // LDS slots
   // bf16 reads the next stage's fragments during a stage (registers for two
@@ -80,8 +84,11 @@ struct Wide {
   // s (direct-to-LDS loads into a scratch kilobyte nobody reads).  Measured
   // slower at PF 8..16 (the loop is not waiting on weights: with every
   // workgroup reading the same L2-resident weights it runs no faster), so off.
+  // INT4 (the row waves of a column wave split the stage's tiles) measured
+  // slower too: gate/up at 48 rows with the exact-fit grid 29.6 against 25.6
+  // us at PF 8.
   static constexpr int PF = 0;
-  static constexpr int NPF = PF > DW ? CT : 0;       // prefetch loads per wave and stage
+  static constexpr int NPF = PF > DW ? (INT4 ? (CT + RWV - 1) / RWV : CT) : 0;  // prefetch loads per wave and stage
   // A wave waits for its own copies of the unit read next before the barrier
   // (loads complete in issue order).  The wait counts come from a replay of
   // the issue order: the prologue (L2 prefetches, DW stages of weights,
@@ -119,7 +126,8 @@ struct Wide {
   }
   static constexpr int WAIT = waits().loop;
   static constexpr int WAIT0 = waits().first;
-  static_assert(RTW % 4 == 0 && (R % 2 == 0 || !PREFETCH) && DW >= 1, "wide GEMM shape");
+  static_assert((RTW % 4 == 0 || (INT4 && RTW % 2 == 0)) && (R % 2 == 0 || !PREFETCH) && DW >= 1,
+                "wide GEMM shape");
   static_assert((RTW * CPU / 4) % WAVES == 0 && (!INT4 || LAY != 1), "wide GEMM shape");
   static_assert(WAIT >= 0 && WAIT0 >= 0 && WAIT < 64 && WAIT0 < 64, "vmcnt range");
   static_assert(NG <= 16 && SW % 8 == 0, "item shape");
@@ -214,10 +222,11 @@ void k_gemm_big(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t ras =
       make_rsrc(INT4 ? (const void*)(a.asum + (size_t)(a.m_base >> 3) * KG * 16) : a.apack,
                 INT4 ? (uint32_t)mtv * KG * 64 : 0u);
-  // INT4 group sums: RTW packed tiles x 16 floats = RTW / 4 pieces of 256 B;
+  // INT4 group sums: RTW packed tiles x 16 floats in SUMP pieces of 256 B (a
+  // last piece's tiles past RTW repeat the last tile into the slot's padding);
   // waves beyond the piece count repeat the first ones (same bytes, same place)
-  static_assert(!INT4 || RTW / 4 <= 4, "sum pieces");
-  const int sum_q = INT4 ? wave % (RTW / 4) : 0;
+  static_assert(!INT4 || C::SUMP <= 4, "sum pieces");
+  const int sum_q = INT4 ? wave % C::SUMP : 0;
   const uint32_t sum_voff =
       INT4 ? ((uint32_t)min(min(sum_q * 4 + (lane >> 4), RTW - 1), mtv - 1) * KG * 16 + (lane & 15)) * 4 : 0u;
   auto copy_stage = [&](const Pos& q) {
@@ -316,11 +325,20 @@ void k_gemm_big(GemmArgs a) {
       const int tile0 = ((cb0 + q.it * gt) * CW + cw) * TPW;
 #pragma unroll
       for (int i = 0; i < C::NPF; ++i) {
-        const int idx = rw * CT + i, T = idx >> 1, kk = idx & 1;
-        const int tile = tile0 + 2 * T;
-        const bool live = live_stage && tile < a.n_tiles;
-        const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
-        lds_copy16(rwt, w_lane + kk * kk_step, so, pf_sink);
+        if (INT4) {
+          // tiles rw, rw + RWV, ... of the column wave's CT
+          const int t = rw + C::RWV * i;
+          const int tile = tile0 + t;
+          const bool live = live_stage && t < CT && tile < a.n_tiles;
+          const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
+          lds_copy16(rwt, w_lane, so, pf_sink);
+        } else {
+          const int idx = rw * CT + i, T = idx >> 1, kk = idx & 1;
+          const int tile = tile0 + 2 * T;
+          const bool live = live_stage && tile < a.n_tiles;
+          const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
+          lds_copy16(rwt, w_lane + kk * kk_step, so, pf_sink);
+        }
       }
     }
   };
@@ -743,14 +761,15 @@ static constexpr size_t wide_smem(int epi) {
 int big_rows_per_launch(bool int4) { return int4 ? 64 : 192; }
 
 // The large-M kernel serves bf16 GEMMs of more than 32 rows and INT4 ones of
-// more than 64; from 33 to 64 INT4 rows it serves gate/up and the lm_head,
-// while the small-M kernel's two launches of 32 rows serve QKV, O and down
-// (measured at 48 rows: gate/up 36.5 against 43.6 us, the lm_head 173
-// against 268 us; O, down and QKV 8% slower here).
+// more than 32 except QKV, O and down at 49..64 rows, which the small-M
+// kernel's two launches of 32 rows serve.  Up to 48 INT4 rows every
+// projection takes one launch of the exact-fit grid (4): the INT4 step at
+// batch 8 measured 4.09 -> 4.00 ms against two small-M launches each for QKV,
+// O and down.
 bool use_big_gemm(int M, int K, bool int4, int epi) {
   (void)K;
   if (!int4) return M > 32;
-  return M > 64 || (M > 32 && (epi == EPI_SILU || epi == EPI_ARGMAX));
+  return M > 64 || (M > 32 && (M <= 48 || epi == EPI_SILU || epi == EPI_ARGMAX));
 }
 
 // Wave grid of a GEMM (see Wide).  Measured at 192 rows: 96-column items
@@ -760,8 +779,10 @@ bool use_big_gemm(int M, int K, bool int4, int epi) {
 // one wave run beside the products of the other wave on its SIMD.
 static int big_lay(int rows, bool int4, int epi) {
   // INT4 gate/up cannot take K slices: 96-column items (at 48 rows 30.7 us
-  // against 37.2 with 128-column items; the lm_head is faster with 128)
-  if (int4) return epi == EPI_SILU ? 3 : 2;
+  // against 37.2 with 128-column items; the lm_head is faster with 128); up
+  // to 48 rows the exact-fit grid (4), whose row tiles hold the rows without
+  // padding (gate/up at 48 rows 26.7 -> 24.2 us)
+  if (int4) return rows <= 48 && epi != EPI_ARGMAX ? 4 : epi == EPI_SILU ? 3 : 2;
   // 65..96 rows fill three 2 x 2 row tiles exactly, where 4 x 1 would pad to 128
   const int mt = (rows + 7) / 8;
   return epi == EPI_ARGMAX || (mt > 8 && mt <= 12) ? 0 : 1;
@@ -771,14 +792,15 @@ static int big_lay(int rows, bool int4, int epi) {
 // operand rows (64 rows in all); bf16 tiles of 32 operand rows (16 real rows).
 static int big_rt(int rows, bool int4, int lay) {
   const int mt = (rows + 7) / 8;
-  if (int4) return 2;
+  if (int4) return lay == 4 ? 3 : 2;
   if (lay == 0) return mt <= 8 ? 2 : mt <= 12 ? 3 : 6;
   return mt <= 8 ? 1 : mt <= 16 ? 2 : 3;
 }
 
 template <bool INT4, int LAY>
 static size_t big_smem(int rt, int epi) {
-  if (INT4) return LAY == 3 ? wide_smem<2, true, 3>(epi) : wide_smem<2, true, 2>(epi);
+  if (INT4) return LAY == 4 ? wide_smem<3, true, 4>(epi) : LAY == 3 ? wide_smem<2, true, 3>(epi)
+                                                                    : wide_smem<2, true, 2>(epi);
   if (LAY == 0) return rt == 2 ? wide_smem<2, false, 0>(epi) : rt == 3 ? wide_smem<3, false, 0>(epi)
                                                                      : wide_smem<6, false, 0>(epi);
   return rt == 1 ? wide_smem<1, false, 1>(epi) : rt == 2 ? wide_smem<2, false, 1>(epi)
@@ -790,12 +812,14 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   p.lay = big_lay(rows, int4, epi);
   p.rt = big_rt(rows, int4, p.lay);
   p.n_tiles = (epi == EPI_SILU) ? (N / 2) / 8 : (N + 15) / 16;
-  const int item = int4 ? (p.lay == 3 ? Wide<2, true, 3>::ITEM : Wide<2, true, 2>::ITEM)
+  const int item = int4 ? (p.lay == 4 ? Wide<3, true, 4>::ITEM : p.lay == 3 ? Wide<2, true, 3>::ITEM
+                                                                           : Wide<2, true, 2>::ITEM)
                         : p.lay == 1 ? Wide<3, false, 1>::ITEM : Wide<6, false, 0>::ITEM;
   const int n_cb = (p.n_tiles + item - 1) / item;
   const int cus = big_cus();
   const int units = int4 ? K / 128 : K / 32;
-  const int dw = int4 ? (p.lay == 3 ? Wide<2, true, 3>::R : Wide<2, true, 2>::R)
+  const int dw = int4 ? (p.lay == 4 ? Wide<3, true, 4>::R : p.lay == 3 ? Wide<2, true, 3>::R
+                                                                       : Wide<2, true, 2>::R)
                       : Wide<6, false>::R;  // stages per ring turn
   // K slices (QKV always writes slice sums; STORE when the caller takes them):
   // the fewest rounds of items times the padded stages of one item, plus the
@@ -826,7 +850,8 @@ BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_spl
   const int gt = (n_cb + per - 1) / per;
   p.grid = gt * p.ksplit;
   p.threads = lay_threads(p.lay);
-  p.smem = int4 ? (p.lay == 3 ? big_smem<true, 3>(p.rt, epi) : big_smem<true, 2>(p.rt, epi))
+  p.smem = int4 ? (p.lay == 4 ? big_smem<true, 4>(p.rt, epi)
+                   : p.lay == 3 ? big_smem<true, 3>(p.rt, epi) : big_smem<true, 2>(p.rt, epi))
                 : (p.lay == 0 ? big_smem<false, 0>(p.rt, epi) : big_smem<false, 1>(p.rt, epi));
   return p;
 }
@@ -856,7 +881,10 @@ static hipError_t launch_big_epi(const GemmArgs& a, int epi, const BigPlan& p, h
 
 static hipError_t launch_big_plan(const GemmArgs& g, int epi, bool int4, const BigPlan& p,
                                   hipStream_t s) {
-  if (int4) return p.lay == 3 ? launch_big_epi<2, true, 3>(g, epi, p, s) : launch_big_epi<2, true, 2>(g, epi, p, s);
+  if (int4) {
+    if (p.lay == 4) return launch_big_epi<3, true, 4>(g, epi, p, s);
+    return p.lay == 3 ? launch_big_epi<2, true, 3>(g, epi, p, s) : launch_big_epi<2, true, 2>(g, epi, p, s);
+  }
   if (p.lay == 0) {
     if (p.rt == 2) return launch_big_epi<2, false, 0>(g, epi, p, s);
     if (p.rt == 3) return launch_big_epi<3, false, 0>(g, epi, p, s);
