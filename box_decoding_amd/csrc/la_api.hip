@@ -107,7 +107,7 @@ la_status check_gemm_weight(const la_weight* w, int tiled) {
 int gemm_parts(int M, const la_weight* w, int epi) {
   if (w->fmt == LA_W_W8A8) return plan_gemm_w8(M, w->n, w->k, epi, false).grid;
   const bool int4 = w->fmt == LA_W_INT4;
-  if (use_big_gemm(M, w->k, int4, epi))
+  if (use_big_gemm(M, int4, epi, w->layout != LA_LAYOUT_ROWS))
     return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, epi, false).grid;
   return plan_gemm(M, w->n, w->k, int4, epi, false).grid;
 }
@@ -115,7 +115,7 @@ int gemm_parts(int M, const la_weight* w, int epi) {
 int gemm_ksplit(int M, const la_weight* w) {
   if (w->fmt == LA_W_W8A8) return plan_gemm_w8(M, w->n, w->k, EPI_STORE, true).ksplit;
   const bool int4 = w->fmt == LA_W_INT4;
-  if (use_big_gemm(M, w->k, int4, EPI_STORE))
+  if (use_big_gemm(M, int4, EPI_STORE, w->layout != LA_LAYOUT_ROWS))
     return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_STORE, true).ksplit;
   return plan_gemm(M, w->n, w->k, int4, EPI_STORE, true).ksplit;
 }
@@ -125,7 +125,7 @@ int gemm_ksplit(int M, const la_weight* w) {
 int qkv_ksplit(int M, const la_weight* w) {
   if (w->fmt == LA_W_W8A8) return 0;
   const bool int4 = w->fmt == LA_W_INT4;
-  if (!use_big_gemm(M, w->k, int4, EPI_QKV)) return 0;
+  if (!use_big_gemm(M, int4, EPI_QKV, w->layout != LA_LAYOUT_ROWS)) return 0;
   return plan_gemm_big(std::min(M, big_rows_per_launch(int4)), w->n, w->k, int4, EPI_QKV, true).ksplit;
 }
 

@@ -1236,7 +1236,7 @@ static hipError_t launch_gemm_w8(GemmArgs a, int epi, hipStream_t s) {
 hipError_t launch_gemm(GemmArgs a, int epi, int fmt, hipStream_t s) {
   if (fmt == LA_W_W8A8) return launch_gemm_w8(a, epi, s);
   const bool int4 = fmt == LA_W_INT4;
-  if (use_big_gemm(a.M, a.K, int4, epi)) return launch_gemm_big(a, epi, int4, s);
+  if (use_big_gemm(a.M, int4, epi, a.layout != LA_LAYOUT_ROWS)) return launch_gemm_big(a, epi, int4, s);
   const GemmPlan p = plan_gemm(a.M, a.N, a.K, int4, epi, a.partial != nullptr);
   a.n_tiles = p.n_tiles;
   a.ksplit = p.ksplit;

@@ -66,7 +66,11 @@ struct Wide {
   static constexpr int FR = INT4 ? RT : 2 * RT;       // fragments per bf16 stage / INT4 K step
   static constexpr int SUMP = (RTW + 3) / 4;           // INT4 group-sum pieces of 256 B (4 row tiles each)
   static constexpr int SUMS = INT4 ? SUMP * 256 : 0;  // INT4 group sums of a slot (bytes)
-  static constexpr int SLOT = RTW * CPU * 256 + SUMS;
+  // INT4 scales of the stage's item tiles (16 fp16 per tile), copied into the
+  // slot beside the sums: carried in registers through the weight ring they
+  // made the compiler wait for nearly every load at each turn of the ring
+  static constexpr int SCB = INT4 ? 256 : 0;
+  static constexpr int SLOT = RTW * CPU * 256 + SUMS + SCB;
   static constexpr int NS = INT4 ? 4 : 6;             // LDS slots
   // bf16 reads the next stage's fragments during a stage (registers for two
   // stages); INT4 reads its own stage's, one K step ahead
@@ -78,8 +82,8 @@ struct Wide {
   static constexpr int R = INT4 && LAY != 3 ? 3 : 4;
   static constexpr int DW = R - 1;                    // weight lead (stages)
   static constexpr int NCOPY = RTW * CPU / 4 / WAVES;  // 1 KB copies per wave and stage
-  static constexpr int NC = NCOPY + (INT4 ? 1 : 0);
-  static constexpr int NW = 2 * CT;                   // bf16: CT tiles x 2 K steps; INT4: + scales
+  static constexpr int NC = NCOPY + (INT4 ? 2 : 0);  // INT4: + group sums + scales
+  static constexpr int NW = INT4 ? CT : 2 * CT;       // bf16: CT tiles x 2 K steps
   // Optional L2 prefetch: the weights of stage s + PF pulled into L2 at stage
   // s (direct-to-LDS loads into a scratch kilobyte nobody reads).  Measured
   // slower at PF 8..16 (the loop is not waiting on weights: with every
@@ -131,6 +135,7 @@ struct Wide {
   static_assert((RTW * CPU / 4) % WAVES == 0 && (!INT4 || LAY != 1), "wide GEMM shape");
   static_assert(WAIT >= 0 && WAIT0 >= 0 && WAIT < 64 && WAIT0 < 64, "vmcnt range");
   static_assert(NG <= 16 && SW % 8 == 0, "item shape");
+  static_assert(!INT4 || ITEM * 8 <= 64, "one lane per scale dword of an item");
 };
 
 // The per-stage meeting point: this wave's LDS reads are complete, then the
@@ -229,6 +234,10 @@ void k_gemm_big(GemmArgs a) {
   const int sum_q = INT4 ? wave % C::SUMP : 0;
   const uint32_t sum_voff =
       INT4 ? ((uint32_t)min(min(sum_q * 4 + (lane >> 4), RTW - 1), mtv - 1) * KG * 16 + (lane & 15)) * 4 : 0u;
+  // INT4 scale copy: lane l < 8 ITEM takes dword l % 8 of item tile l / 8
+  // (tiled scales: [tile][unit][16] fp16); the other lanes read past the end
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(INT4 ? (const void*)a.wscale : a.w, INT4 ? a.s_bytes : 0u);
+  const uint32_t sc_voff = lane < 8 * ITEM ? (uint32_t)(lane >> 3) * (uint32_t)units * 32 + (lane & 7) * 4 : 0x40000000u;
   auto copy_stage = [&](const Pos& q) {
     const uint32_t u = (uint32_t)(s_lo + min(q.uu, nu - 1));
     unsigned char* dst = slot_ptr(q.slot);
@@ -239,7 +248,16 @@ void k_gemm_big(GemmArgs a) {
       const uint32_t soff = ((uint32_t)min(t, mtv - 1) * K8 + u * CPU + part * 4) * 256;
       lds_copy16(rap, lane * 16, soff, dst + (t * CPU + part * 4) * 256);
     }
-    if (INT4) lds_copy4(ras, sum_voff, u * 64, dst + RTW * CPU * 256 + sum_q * 256);
+    if (INT4) {
+      lds_copy4(ras, sum_voff, u * 64, dst + RTW * CPU * 256 + sum_q * 256);
+      // the item's tile scales for unit u (tiles past the weight read zero);
+      // a stage whose weights are dead (ring padding, past the last item)
+      // gets zero scales too, so its group correction adds nothing
+      const bool live_stage = q.it < n_my && q.uu < nu;
+      const uint32_t item_tile = (uint32_t)(cb0 + q.it * gt) * ITEM;
+      const uint32_t so = live_stage ? (item_tile * (uint32_t)units + u) * 32 : 0x7FFFFFFFu;
+      lds_copy4(rsc, sc_voff, so, dst + RTW * CPU * 256 + C::SUMS);
+    }
   };
 
   // ---- weights of the column wave's 16-column tiles tile0 .. tile0 + 3.  A
@@ -250,7 +268,6 @@ void k_gemm_big(GemmArgs a) {
   // 16*kk + 8*(l/32) .. +7 of the unit; in the 16-column tile's layout those
   // are lane (2*kk + l/32)*16 + l%16's bytes.
   const __amdgpu_buffer_rsrc_t rwt = make_rsrc(a.w, a.w_bytes);
-  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(INT4 ? (const void*)a.wscale : a.w, INT4 ? a.s_bytes : 0u);
   const bool tiled = a.layout != LA_LAYOUT_ROWS;
   const int UT = units;
   // row layout: weight row of operand column c of a tile = row_of_tile + row_of_lane
@@ -258,17 +275,15 @@ void k_gemm_big(GemmArgs a) {
                           : EPI == EPI_QKV ? (c < 8 ? c : 56 + c) : c;
   const int odd = (lane >> 4) & 1;  // bf16: second 16-column tile of the pair
   const int tile_rows = EPI == EPI_STORE || EPI == EPI_ARGMAX ? 16 : 8;  // row step of a 16-column tile
-  uint32_t w_lane, s_lane = 0;
+  uint32_t w_lane;
   if (INT4) {
     w_lane = tiled ? (uint32_t)lane * 16 : (uint32_t)row_of_lane * (a.K >> 1) + g * 16;
-    s_lane = tiled ? (uint32_t)c * 2 : (uint32_t)row_of_lane * KG * 2;
   } else {
     w_lane = tiled ? (uint32_t)((lane >> 5) * 16 + c) * 16 + (uint32_t)odd * UT * 1024
                    : ((uint32_t)(row_of_lane + odd * tile_rows) * a.K + (lane >> 5) * 8) * 2;
   }
   const uint32_t kk_step = tiled ? 512u : 32u;  // bf16: second K step of the unit
   const uint32_t ustride = tiled ? 1024u : 64u;
-  const uint32_t sstride = tiled ? 32u : 2u;
   auto tile_row = [&](int tile) {
     return EPI == EPI_SILU ? tile * 8 : EPI == EPI_QKV ? (tile >> 3) * 128 + (tile & 7) * 8 : tile * 16;
   };
@@ -276,12 +291,8 @@ void k_gemm_big(GemmArgs a) {
     if (tiled) return (uint32_t)tile * UT * 1024;
     return INT4 ? (uint32_t)tile_row(tile) * (a.K >> 1) : (uint32_t)tile_row(tile) * a.K * 2;
   };
-  auto tile_s = [&](int tile) -> uint32_t {
-    return tiled ? (uint32_t)tile * UT * 32 : (uint32_t)tile_row(tile) * KG * 2;
-  };
   struct WStage {
     u32x4 w[2 * CT / (INT4 ? 2 : 1)];  // bf16: [tile][K step]; INT4: [tile]
-    uint32_t s[INT4 ? CT : 1];         // fp16 bits; 32-bit so no wait to pack halves
   };
   WStage st[C::R];
   auto issue_w = [&](const Pos& q, WStage& d) {
@@ -296,8 +307,6 @@ void k_gemm_big(GemmArgs a) {
         // a dead load starts past the end of the buffer and reads zero
         const uint32_t so = live ? tile_w(tile) + u * ustride : 0x7FFFFFFFu;
         d.w[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwt, w_lane, so, kNonTemporal));
-        const uint32_t ss = live ? tile_s(tile) + u * sstride : 0x7FFFFFFFu;
-        d.s[INT4 ? t : 0] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_lane, ss, 0);
       }
     } else {
 #pragma unroll
@@ -412,7 +421,8 @@ void k_gemm_big(GemmArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
-        const float sc = fp16_to_f32(s.s[INT4 ? t : 0]);
+        const float sc = fp16_to_f32(*(const uint16_t*)(slot_ptr(slot) + RTW * CPU * 256 + C::SUMS +
+                                                        ((cw * TPW + t) * 16 + c) * 2));
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -766,9 +776,9 @@ int big_rows_per_launch(bool int4) { return int4 ? 64 : 192; }
 // projection takes one launch of the exact-fit grid (4): the INT4 step at
 // batch 8 measured 4.09 -> 4.00 ms against two small-M launches each for QKV,
 // O and down.
-bool use_big_gemm(int M, int K, bool int4, int epi) {
-  (void)K;
+bool use_big_gemm(int M, bool int4, int epi, bool tiled) {
   if (!int4) return M > 32;
+  if (!tiled) return false;  // INT4 scales are copied per item tile: tiled weights only
   return M > 64 || (M > 32 && (M <= 48 || epi == EPI_SILU || epi == EPI_ARGMAX));
 }
 

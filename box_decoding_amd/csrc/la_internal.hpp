@@ -174,7 +174,7 @@ struct BigPlan {
   size_t smem;
 };
 int big_rows_per_launch(bool int4);
-bool use_big_gemm(int M, int K, bool int4, int epi);
+bool use_big_gemm(int M, bool int4, int epi, bool tiled);
 BigPlan plan_gemm_big(int rows, int N, int K, bool int4, int epi, bool allow_split);
 hipError_t launch_gemm_big(GemmArgs a, int epi, bool int4, hipStream_t s);
 
