@@ -64,6 +64,11 @@ struct Wide {
   static constexpr int NG = SW / 8;                   // 8-column epilogue groups per staged row
   static constexpr int CPU = INT4 ? 16 : 4;           // 256-byte chunks per packed tile and K unit
   static constexpr int FR = INT4 ? RT : 2 * RT;       // fragments per bf16 stage / INT4 K step
+  // staged rows of an epilogue part: the INT4 exact-fit grid stages the hi
+  // and the lo operand rows apart and adds them when it reads (no cross-lane
+  // exchange); the eight-wave INT4 grids have no LDS left for that
+  static constexpr bool SPLIT_HL = INT4 && LAY == 4;
+  static constexpr int SROWS = SPLIT_HL ? 16 : 8;
   static constexpr int SUMP = (RTW + 3) / 4;           // INT4 group-sum pieces of 256 B (4 row tiles each)
   static constexpr int SUMS = INT4 ? SUMP * 256 : 0;  // INT4 group sums of a slot (bytes)
   // INT4 scales of the stage's item tiles (16 fp16 per tile), copied into the
@@ -194,10 +199,11 @@ void k_gemm_big(GemmArgs a) {
 
   constexpr int SW = C::SW;      // columns of a column wave
   constexpr int SROW = SW + 4;  // 16-byte aligned rows, column writes spread over banks
+  constexpr int SR = C::SROWS;  // staged rows per wave (INT4: the hi rows, then the lo rows)
   unsigned char* slots = smem;                                              // [NS][SLOT]
   unsigned char* pf_sink = smem + NS * SLOT;                                // [kPfSink]
-  float* stage = (float*)(pf_sink + kPfSink) + (size_t)wave * 8 * SROW;     // [8][SROW] per wave
-  float* amax_lds = (float*)(pf_sink + kPfSink) + (size_t)WAVES * 8 * SROW;
+  float* stage = (float*)(pf_sink + kPfSink) + (size_t)wave * SR * SROW;    // [SR][SROW] per wave
+  float* amax_lds = (float*)(pf_sink + kPfSink) + (size_t)WAVES * SR * SROW;
   float* my_amax = amax_lds + (size_t)wave * NP * 8 * 3;                    // ARGMAX: [NP*8][3]
   if (EPI == EPI_ARGMAX) {
     for (int i = lane; i < NP * 8; i += 64) {
@@ -437,7 +443,16 @@ void k_gemm_big(GemmArgs a) {
   // once.
   auto stage_part = [&](auto pc) {
     constexpr int P = decltype(pc)::value;
-    if constexpr (INT4) {
+    if constexpr (C::SPLIT_HL) {
+      // 16x16x32: lane l holds operand rows 4 (l / 16) + e: real row
+      // 4 ((l / 16) % 2) + e, hi for l < 32 and lo beyond (staged 8 rows on)
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stage[(4 * g + e) * SROW + t * 16 + c] = acc[P][t][e];
+        acc[P][t] = AccT{};
+      }
+    } else if constexpr (INT4) {
       // 16x16x32: lanes g < 2 hold real rows 4g + e after the xor-32 exchange
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
@@ -461,6 +476,14 @@ void k_gemm_big(GemmArgs a) {
       }
     }
   };
+  // A staged value (split staging: the row's hi and lo halves, 8 staged rows
+  // apart, added in that order)
+  auto st4 = [&](const float* p) -> f32x4 {
+    f32x4 v = *(const f32x4*)p;
+    if constexpr (C::SPLIT_HL) v += *(const f32x4*)(p + 8 * SROW);
+    return v;
+  };
+  auto st1 = [&](const float* p, int e) -> float { return C::SPLIT_HL ? p[e] + p[e + 8 * SROW] : p[e]; };
   // One lane per 8 consecutive staged columns of a row (r = lane / 8, column
   // group lane % 8, + 8 in a second pass when a wave stages 96 columns: the
   // group's 16-column tile is group / 2, its half group % 2), so the outputs
@@ -480,7 +503,7 @@ void k_gemm_big(GemmArgs a) {
         const int tile = tile0 + (grp >> 1), half = grp & 1;
         if (grp < C::NG && tile < a.n_tiles) {
           const float* src = stage + r * SROW + grp * 8;
-          const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+          const f32x4 x0 = st4(src), x1 = st4(src + 4);
           const int n0 = tile * 16 + half * 8;
           // the group's 8 bits of this row's bitmap (repetition penalty)
           const uint32_t used = row_ok ? rep_word(a, m, n0) >> (n0 & 31) : 0u;
@@ -523,7 +546,7 @@ void k_gemm_big(GemmArgs a) {
         // two halves of 4 columns: 8-byte hi and lo pieces
 #pragma unroll 1
         for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 gv = *(const f32x4*)(gsrc + 4 * hf), uv = *(const f32x4*)(gsrc + 8 + 4 * hf);
+          const f32x4 gv = st4(gsrc + 4 * hf), uv = st4(gsrc + 8 + 4 * hf);
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = silu_f(gv[e]) * uv[e];
@@ -560,10 +583,10 @@ void k_gemm_big(GemmArgs a) {
           const int n0 = EPI == EPI_QKV ? col_row<EPI_QKV>(a.N, tile, half * 8) : tile * 16 + half * 8;
           float* po = a.partial + ((size_t)ks * a.M + m) * a.N + n0;
           if (n0 + 8 <= a.N && (a.N & 3) == 0) {
-            *(f32x4*)po = *(const f32x4*)src;
-            *(f32x4*)(po + 4) = *(const f32x4*)(src + 4);
+            *(f32x4*)po = st4(src);
+            *(f32x4*)(po + 4) = st4(src + 4);
           } else {
-            for (int e = 0; e < 8 && n0 + e < a.N; ++e) po[e] = src[e];
+            for (int e = 0; e < 8 && n0 + e < a.N; ++e) po[e] = st1(src, e);
           }
         } else {
           // y = v (+ bias + residual)
@@ -572,7 +595,7 @@ void k_gemm_big(GemmArgs a) {
           for (int e = 0; e < 8; ++e) {
             const int n = n0 + e;
             if (n >= a.N) break;
-            float y = src[e];
+            float y = st1(src, e);
             if (a.bias) y += bf16_to_f32(a.bias[n]);
             if (a.residual) y += a.residual[(size_t)m * a.ldy + n];
             a.y[(size_t)m * a.ldy + n] = y;
@@ -763,7 +786,7 @@ static int big_cus() {
 template <int RT, bool INT4, int LAY>
 static constexpr size_t wide_smem(int epi) {
   using C = Wide<RT, INT4, LAY>;
-  return (size_t)C::NS * C::SLOT + kPfSink + (size_t)C::WAVES * 8 * (C::SW + 4) * 4 +
+  return (size_t)C::NS * C::SLOT + kPfSink + (size_t)C::WAVES * C::SROWS * (C::SW + 4) * 4 +
          (epi == EPI_ARGMAX ? (size_t)C::WAVES * C::NP * 8 * 3 * 4 : 0);
 }
 
