@@ -813,9 +813,10 @@ bool use_big_gemm(int M, bool int4, int epi, bool tiled) {
 static int big_lay(int rows, bool int4, int epi) {
   // INT4 gate/up cannot take K slices: 96-column items (at 48 rows 30.7 us
   // against 37.2 with 128-column items; the lm_head is faster with 128); up
-  // to 48 rows the exact-fit grid (4), whose row tiles hold the rows without
-  // padding (gate/up at 48 rows 26.7 -> 24.2 us)
-  if (int4) return rows <= 48 && epi != EPI_ARGMAX ? 4 : epi == EPI_SILU ? 3 : 2;
+  // to 48 rows every INT4 GEMM takes the exact-fit grid (4), whose row tiles
+  // hold the rows without padding (gate/up at 48 rows 26.7 -> 24.2 us; the
+  // lm_head too once its scales came through LDS: the step 3.657 -> 3.645 ms)
+  if (int4) return rows <= 48 ? 4 : epi == EPI_SILU ? 3 : 2;
   // 65..96 rows fill three 2 x 2 row tiles exactly, where 4 x 1 would pad to 128
   const int mt = (rows + 7) / 8;
   return epi == EPI_ARGMAX || (mt > 8 && mt <= 12) ? 0 : 1;
