@@ -58,9 +58,9 @@ TRAFFIC_KERNELS = {
     "gate_up_b32": ("k_gemm_big<3, false, 1, 1>", BIG_SOURCES,
                     os.path.join(ROOT, "profiles", "gate_up_traffic_step_b32_ragged.json"),
                     "k_gemm_big<3, false, 1, 1> (gate/up + SiLU, 192 rows, 96-column items)"),
-    "gate_up_int4": ("k_gemm_big<2, true, 1, 3>", BIG_SOURCES,
+    "gate_up_int4": ("k_gemm_big<3, true, 1, 4>", BIG_SOURCES,
                      os.path.join(ROOT, "profiles", "gate_up_traffic_step_int4_b8_p1280.json"),
-                     "k_gemm_big<2, true, 1, 3> (INT4 gate/up + SiLU, 48 rows, eight waves)"),
+                     "k_gemm_big<3, true, 1, 4> (INT4 gate/up + SiLU, 48 rows, exact-fit grid)"),
     "front": ("la::k_front(", ("la_front.hip", "la_attn_common.hpp", "la_internal.hpp", "la_common.hpp"),
               FRONT_TRAFFIC_FILE, "k_front (front half of a layer: RMSNorm, QKV, attention, O, gate/up + SiLU)"),
 }

@@ -364,6 +364,9 @@ void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_
   const int max_pages = (max_len + kBlock - 1) / kBlock;
   int pps = 2;
   while (pps < 64 && (long)B * Hkv * ((max_pages + pps - 1) / pps) > 640) pps *= 2;
+  // at least 8 pages per run while 128 runs remain: INT4 batch 8 at P 1280
+  // (336 runs of 4 pages) measured 4.15 -> 4.07 ms per step with runs of 8
+  while (pps < 8 && (long)B * Hkv * ((max_pages + 2 * pps - 1) / (2 * pps)) >= 128) pps *= 2;
   if (pps > max_pages) pps = max_pages;
   if (pps < 1) pps = 1;
   *pages_per_split = pps;
