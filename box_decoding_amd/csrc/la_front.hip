@@ -431,7 +431,7 @@ __device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
 
 // The O role of tile t: waits for every attention item, reads the packed
 // attention output coherently, multiplies, runs the epilogue.
-__device__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits], unsigned char* smem) {
+__device__ __forceinline__ void front_o(const FrontArgs& f, int t, const u32x4 (&wo)[kFrontUnits], unsigned char* smem) {
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float res[2][1 + kFrontMaxParts];
@@ -498,20 +498,30 @@ __device__ __forceinline__ void gu_epilogue(const FrontArgs& f, int j, const flo
   f.mpack[base + 64] = (uint16_t)l;
 }
 
+// This workgroup's gate/up tiles after the kGuPreload preloaded ones: the
+// first three are requested into the register buffers.
+__device__ __forceinline__ void gu_issue(const FrontArgs& f, int wave, u32x4 (&wa)[kFrontUnits],
+                                         u32x4 (&wb)[kFrontUnits], u32x4 (&wc)[kFrontUnits]) {
+  const int G = gridDim.x, js = (int)blockIdx.x + kGuPreload * G;
+  if (js < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js, wave, wa);
+  if (js + G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js + G, wave, wb);
+  if (js + 2 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js + 2 * G, wave, wc);
+}
+
 // The gate/up role of every workgroup: its tiles blockIdx.x + k gridDim.x.
-// The first two streamed tiles' weights are requested before the wait; once every
-// O tile is done the packed post-norm operand and the rows' 1 / rms are read
-// (agent scope), the preloaded tiles multiply from LDS and the rest stream
-// through two register buffers.
-__device__ void front_gateup(const FrontArgs& f, unsigned char* smem) {
+// Three streamed tiles' weights are requested before the wait (by gu_issue,
+// here unless the caller did it earlier); once every O tile is done the packed
+// post-norm operand and the rows' 1 / rms are read (agent scope), the
+// preloaded tiles multiply from LDS and the rest stream through the three
+// register buffers.
+__device__ __forceinline__ void front_gateup(const FrontArgs& f, unsigned char* smem, u32x4 (&wa)[kFrontUnits],
+                                             u32x4 (&wb)[kFrontUnits], u32x4 (&wc)[kFrontUnits], bool issued) {
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, j0 = blockIdx.x;
   if (j0 >= f.n_gu_tiles) return;  // uniform
   const int js = j0 + kGuPreload * G;  // first streamed tile
-  u32x4 wa[kFrontUnits], wb[kFrontUnits];
-  if (js < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js, wave, wa);
-  if (js + G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, js + G, wave, wb);
+  if (!issued) gu_issue(f, wave, wa, wb, wc);
   wait_flags(f, fl_odone(f, blockIdx.x % kFlagCopies), f.n_o_tiles);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.gpack, kFrontK / 8 * 256);
   const bool live = (lane & 7) < f.T;  // operand rows r (hi) and r + 8 (lo) of window row r
@@ -553,15 +563,19 @@ __device__ void front_gateup(const FrontArgs& f, unsigned char* smem) {
     tile_reduce(af, wf, wave, red, outv);
     if (wave == 0) gu_epilogue(f, j, outv, inv);
   }
-  // two tiles in flight: each buffer is refilled right after its product
-  for (int j = js; j < f.n_gu_tiles; j += 2 * G) {
+  // three tiles in flight: each buffer is refilled right after its product
+  for (int j = js; j < f.n_gu_tiles; j += 3 * G) {
     tile_reduce(af, wa, wave, red, outv);
-    if (j + 2 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 2 * G, wave, wa);
+    if (j + 3 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 3 * G, wave, wa);
     if (wave == 0) gu_epilogue(f, j, outv, inv);
     if (j + G >= f.n_gu_tiles) break;  // uniform
     tile_reduce(af, wb, wave, red, outv);
-    if (j + 3 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 3 * G, wave, wb);
+    if (j + 4 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 4 * G, wave, wb);
     if (wave == 0) gu_epilogue(f, j + G, outv, inv);
+    if (j + 2 * G >= f.n_gu_tiles) break;  // uniform
+    tile_reduce(af, wc, wave, red, outv);
+    if (j + 5 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 5 * G, wave, wc);
+    if (wave == 0) gu_epilogue(f, j + 2 * G, outv, inv);
   }
 }
 
@@ -877,12 +891,20 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
   if (w < f.n_qkv_tiles) {
     front_qkv(f, w, smem);
     if (w < f.n_o_tiles) {
-      // the O weights stream in while the attention runs (and the first
-      // gate/up tiles into LDS after them)
+      // the O weights stream in while the attention runs, then the first
+      // gate/up tiles into LDS and the next three into registers (so that
+      // they land before the O tile is done: requested after it, they were
+      // the tail of the launch)
       u32x4 wo[kFrontUnits];
       load_tile_weights(f.wo, f.wo_bytes, w, wave, wo);
-      if (f.wgu) gu_preload(f, smem);
+      u32x4 wa[kFrontUnits], wb[kFrontUnits], wc[kFrontUnits];
+      if (f.wgu) {
+        gu_preload(f, smem);
+        gu_issue(f, wave, wa, wb, wc);
+      }
       front_o(f, w, wo, smem);
+      if (f.wgu) front_gateup(f, smem, wa, wb, wc, true);
+      return;
     } else if (f.wgu) {
       gu_preload(f, smem);
     }
@@ -907,7 +929,8 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
     }
     if (f.wgu) gu_preload(f, smem);
   }
-  if (f.wgu) front_gateup(f, smem);
+  u32x4 wa[kFrontUnits], wb[kFrontUnits], wc[kFrontUnits];
+  if (f.wgu) front_gateup(f, smem, wa, wb, wc, false);
 }
 
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
