@@ -398,11 +398,16 @@ __device__ void front_pack(const FrontArgs& f, int p) {
 
 // The projection role of tile t: the packed operand
 // (read coherently once every pack slice is in), the product, the epilogue.
-__device__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem) {
+// An O tile's weights (tile t of O, t < n_o_tiles) are requested into wo at
+// the first cycle with the QKV weights: they arrive long before the attention
+// is done, and the gate/up loads issued after the QKV product no longer queue
+// ahead of them.
+__device__ __forceinline__ void front_qkv(const FrontArgs& f, int t, unsigned char* smem, u32x4 (&wo)[kFrontUnits]) {
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   u32x4 wq[kFrontUnits];
   load_tile_weights(f.wqkv, f.wqkv_bytes, t, wave, wq);
+  if (t < f.n_o_tiles) load_tile_weights(f.wo, f.wo_bytes, t, wave, wo);
   QkvEpi epi;
   if (wave == 0) epi = qkv_epi_prepare(f, t);
   wait_flags(f, fl_pack(f, blockIdx.x % kFlagCopies), kFrontPackSlices);
@@ -889,14 +894,13 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
   const int slice = w - f.n_qkv_tiles;
 
   if (w < f.n_qkv_tiles) {
-    front_qkv(f, w, smem);
+    u32x4 wo[kFrontUnits];
+    front_qkv(f, w, smem, wo);
     if (w < f.n_o_tiles) {
-      // the O weights stream in while the attention runs, then the first
-      // gate/up tiles into LDS and the next three into registers (so that
-      // they land before the O tile is done: requested after it, they were
-      // the tail of the launch)
-      u32x4 wo[kFrontUnits];
-      load_tile_weights(f.wo, f.wo_bytes, w, wave, wo);
+      // the O weights are in flight since the first cycle; the first gate/up
+      // tiles go into LDS and the next three into registers while the
+      // attention runs (so that they land before the O tile is done:
+      // requested after it, they were the tail of the launch)
       u32x4 wa[kFrontUnits], wb[kFrontUnits], wc[kFrontUnits];
       if (f.wgu) {
         gu_preload(f, smem);

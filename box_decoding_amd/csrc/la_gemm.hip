@@ -627,7 +627,9 @@ void k_gemm(GemmArgs a) {
 // optionally written back, then RMSNorm (optional) and the bf16 hi/lo split into
 // the packed layout (plus per-group sums for INT4 consumers).  A thread holds C
 // chunks of 8 values; every load of the row (x, partial sums, gain) is issued
-// before the first is used, so the kernel waits on memory once.
+// before the first is used, so the kernel waits on memory once.  Without the
+// norm (no row-wide sum) a row may be split over gridDim.y workgroups, each
+// taking blockDim.x * C consecutive chunks (a multiple of 16: whole groups).
 template <int NP, int C>
 __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
   __shared__ float red[16];
@@ -635,12 +637,14 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
   const int K8 = a.K >> 3;
   const int KG = a.K >> 7;
   const int bd = blockDim.x;
+  const int k0 = (int)blockIdx.y * bd * C;  // first chunk of this workgroup's part of the row
+  const int k1 = min(K8, k0 + bd * C);
   if (m >= a.M) {
     // padding rows of the last tile: zero operand rows and group sums
     if (a.apack)
-      for (int kc = threadIdx.x; kc < K8; kc += bd) apack_store_zero_chunk(a.apack, a.K, m, kc);
+      for (int kc = k0 + (int)threadIdx.x; kc < k1; kc += bd) apack_store_zero_chunk(a.apack, a.K, m, kc);
     if (a.int4 && a.asum) {
-      for (int gi = threadIdx.x; gi < KG; gi += bd) {
+      for (int gi = k0 / 16 + (int)threadIdx.x; gi < min(KG, (k1 + 15) / 16); gi += bd) {
         float* as = a.asum + ((size_t)(m >> 3) * KG + gi) * 16;
         as[m & 7] = 0.f;
         as[(m & 7) + 8] = 0.f;
@@ -653,7 +657,7 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
   const float* x = a.x + (size_t)m * a.ldx;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const int kc = min((int)threadIdx.x + j * bd, K8 - 1);  // clamped; masked below
+    const int kc = min(k0 + (int)threadIdx.x + j * bd, K8 - 1);  // clamped; masked below
     float4 p[2 * NP + 2];
     p[0] = *(const float4*)(x + kc * 8);
     p[1] = *(const float4*)(x + kc * 8 + 4);
@@ -683,8 +687,8 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const int kc = (int)threadIdx.x + j * bd;
-    if (kc < K8) {
+    const int kc = k0 + (int)threadIdx.x + j * bd;
+    if (kc < k1) {
       if (a.h_out) {
         float* ho = a.h_out + (size_t)m * a.ldx + kc * 8;
         *(float4*)ho = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
@@ -709,9 +713,9 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const int kc = (int)threadIdx.x + j * bd;
+    const int kc = k0 + (int)threadIdx.x + j * bd;
     float hs = 0.f, ls = 0.f;
-    if (kc < K8) {
+    if (kc < k1) {
       if (a.gain) {
         const uint32_t gw[4] = {gg[j].x, gg[j].y, gg[j].z, gg[j].w};
 #pragma unroll
@@ -735,7 +739,7 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
         hs += __shfl_xor(hs, o);
         ls += __shfl_xor(ls, o);
       }
-      if (kc < K8 && (kc & 15) == 0) {
+      if (kc < k1 && (kc & 15) == 0) {
         float* as = a.asum + ((size_t)(m >> 3) * KG + (kc >> 4)) * 16;
         as[m & 7] = hs;
         as[(m & 7) + 8] = ls;
@@ -1256,9 +1260,19 @@ hipError_t launch_gemm(GemmArgs a, int epi, int fmt, hipStream_t s) {
   return hipSuccess;
 }
 
+constexpr int kPackSplitChunks = 256;  // chunks of 8 values per workgroup of a split row
+
 template <int NP>
 static hipError_t launch_pack_np(const PackArgs& a, int rows, hipStream_t s) {
   const int K8 = a.K / 8;
+  if (!a.gain && K8 > kPackSplitChunks) {
+    // no row-wide sum: parts of kPackSplitChunks chunks, so that the rows of a
+    // small batch spread over many compute units (the INT4 down operand at 48
+    // rows: 48 workgroups of 88 KB each were bound by the per-CU load rate)
+    const dim3 grid(rows, (K8 + kPackSplitChunks - 1) / kPackSplitChunks);
+    hipLaunchKernelGGL((k_pack<NP, 1>), grid, dim3(kPackSplitChunks), 0, s, a);
+    return hipGetLastError();
+  }
   const int C = K8 <= 1024 ? 1 : 2;
   const int bd = ((K8 + C - 1) / C + 63) / 64 * 64;
   if (C == 1) hipLaunchKernelGGL((k_pack<NP, 1>), dim3(rows), dim3(bd), 0, s, a);
