@@ -24,6 +24,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 CAL_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic_step_b1_p1280.json")
 FRONT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "front_traffic_step_b1_p1280.json")
+FRONT_DOWN_SLICES = 4  # K slices of the down projection when the front-half launch runs it
 METRIC = "PBD window steps/sec (≈boxes/sec) at batch 1 and 32; achieved HBM GB/s vs peak"
 
 
@@ -62,7 +63,7 @@ TRAFFIC_KERNELS = {
                      os.path.join(ROOT, "profiles", "gate_up_traffic_step_int4_b8_p1280.json"),
                      "k_gemm_big<3, true, 1, 4> (INT4 gate/up + SiLU, 48 rows, exact-fit grid)"),
     "front": ("la::k_front(", ("la_front.hip", "la_attn_common.hpp", "la_internal.hpp", "la_common.hpp"),
-              FRONT_TRAFFIC_FILE, "k_front (front half of a layer: RMSNorm, QKV, attention, O, gate/up + SiLU)"),
+              FRONT_TRAFFIC_FILE, "k_front (a layer in one launch: RMSNorm, QKV, attention, O, gate/up + SiLU, down)"),
 }
 
 
@@ -97,6 +98,23 @@ def fused_front_bytes(lay, dims, prefix_len, W):
     total = front_bytes(lay, dims, prefix_len, W)
     total -= T * (H // 16) * 4 + 2 * T * H * 2
     return total + weight_bytes(lay["gate_up"]) + T * F * 4
+
+
+def fused_layer_bytes(lay, dims, prefix_len, W):
+    """Algorithmic bytes of the front-half launch when it runs the whole layer
+    (the down projection too): fused_front_bytes with the down weights read
+    once and its K-slice sums written once instead of the packed SiLU output,
+    which stays inside the launch."""
+    T = len(prefix_len) * W
+    H, F = dims.hidden, dims.inter
+    total = fused_front_bytes(lay, dims, prefix_len, W) - T * F * 4
+    return total + weight_bytes(lay["down"]) + FRONT_DOWN_SLICES * T * H * 4
+
+
+def front_fuses_down(w, row_major):
+    """Whether the front-half launch also runs the down projection (with
+    gate/up; LA_PBD_FRONT_DOWN=0 turns it off)."""
+    return front_fuses_gate_up(w, row_major) and os.environ.get("LA_PBD_FRONT_DOWN", "1") != "0"
 
 
 def front_fuses_gate_up(w, row_major):
@@ -783,11 +801,12 @@ def main():
             block_ms.extend(bev.ms())
     front_us = sum(block_ms) / len(block_ms) * 1e3
     fused = front_fuses_gate_up(w, args.row_major)
-    fb = fused_front_bytes if fused else front_bytes
+    fused_dn = front_fuses_down(w, args.row_major)
+    fb = fused_layer_bytes if fused_dn else fused_front_bytes if fused else front_bytes
     fbytes = sum(fb(lay, d, P, w.window) for lay in model["layers"]) / d.n_layers
     front_gbps = fbytes / (front_us * 1e-6) / 1e9
     front_launch = w.batch * w.window <= 8 and w.wfmt == "bf16" and not args.row_major
-    log(f"bench: attention block (front-half launch{' + gate/up' if fused else ''}) "
+    log(f"bench: attention block (front-half launch{' + gate/up' if fused else ''}{' + down' if fused_dn else ''}) "
         f"{front_us:.1f} us, {front_gbps:.0f} GB/s")
 
     # The weight-streaming kernel with the most bytes: the gate/up projection
@@ -835,7 +854,7 @@ def main():
                "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes}
     roof_front = {"bound": "hbm",
                   "kernel": "front half of a layer, one persistent launch (k_front: RMSNorm, QKV, attention, O"
-                            + (", gate/up + SiLU)" if fused else ")"),
+                            + (", gate/up + SiLU" if fused else "") + (", down)" if fused_dn else ")"),
                   "achieved": round(front_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": round(front_gbps / HBM_PEAK_GBPS, 4), "traffic": front_traffic,
                   "launch_us": round(front_us, 2), "bytes_per_launch": round(fbytes)}

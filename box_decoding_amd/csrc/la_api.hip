@@ -233,7 +233,9 @@ StepWs carve_step(const la_model* m, int B, int W, int max_len, void* ws, bool l
     s.pre_flags = c.take<int32_t>(B);
     s.h_last = c.take<float>((size_t)B * H);
   }
-  const int ksp = std::max(gemm_ksplit(T, &m->layers[0].o), gemm_ksplit(T, &m->layers[0].down));
+  // (at least the front launch's down slices)
+  const int ksp = std::max(std::max(gemm_ksplit(T, &m->layers[0].o), gemm_ksplit(T, &m->layers[0].down)),
+                           kFrontDownSlices);
   const int NQKV = (m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
   const size_t qkv_parts = (size_t)qkv_ksplit(T, &m->layers[0].qkv) * T * NQKV;
   s.parts = c.take<float>(std::max((size_t)ksp * T * H, qkv_parts));
@@ -411,6 +413,7 @@ struct AttnView {
 struct FrontPlan {
   int grid = 0, pps = 0, runs = 0, items = 0;
   bool gate_up = false;  // the launch also runs gate/up (LA_PBD_FRONT_GU=0 in the environment turns it off)
+  bool down = false;     // and the down projection (LA_PBD_FRONT_DOWN=0 turns it off)
 };
 
 FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max_len, const StepWs& s,
@@ -429,6 +432,14 @@ FrontPlan plan_front(const la_model* m, const la_layer& L, int B, int W, int max
   const char* gu = getenv("LA_PBD_FRONT_GU");
   f.gate_up = !(gu && gu[0] == '0') && L.gate_up.fmt == LA_W_BF16 && L.gate_up.layout == LA_LAYOUT_TILED_GU &&
               L.gate_up.k == m->hidden && m->inter % 8 == 0;
+  // the down projection as K-slice sums, two output tiles of one slice per
+  // workgroup: the grid must hold H / 16 x kFrontDownSlices / 2 workgroups
+  const char* dn = getenv("LA_PBD_FRONT_DOWN");
+  const int U = m->inter / 32;
+  f.down = f.gate_up && !(dn && dn[0] == '0') && L.down.fmt == LA_W_BF16 && L.down.layout == LA_LAYOUT_TILED &&
+           L.down.k == m->inter && L.down.n == m->hidden && m->inter % 32 == 0 && m->hidden % 16 == 0 &&
+           f.grid == (m->hidden / 16) * kFrontDownSlices / 2 && f.grid <= 256 &&
+           (U + kFrontDownSlices - 1) / kFrontDownSlices <= kFrontDownUnits;
   return f;
 }
 
@@ -508,6 +519,12 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
       f.n_gu_tiles = m->inter / 8;
       f.mpack = s.apack_m;
     }
+    if (fp.down) {
+      weight_storage(&L.down, &wb, &sb);
+      f.wdn = L.down.data;
+      f.wdn_bytes = (uint32_t)wb;
+      f.dparts = s.parts;
+    }
     f.sync = s.sync;
     f.ll_q = s.ll_q;
     f.ll_kv = s.ll_kv;
@@ -518,6 +535,12 @@ la_status run_layer(const la_model* m, int l, const la_kv_cache* kv, const int32
     LA_TRY(launch_front(f, fp.grid, st));
     carry->pending = 0;
     carry->packed = false;
+    if (fp.down) {
+      // the launch wrote the down projection's K-slice sums (the next pack adds them)
+      if (ev) LA_TRY(hipEventRecord(ev[1], st));
+      carry->pending = kFrontDownSlices;
+      return LA_OK;
+    }
   } else {
 
   // input operand: h (+ pending partial sums), RMSNorm, pack, unless the

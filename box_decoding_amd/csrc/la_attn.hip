@@ -363,7 +363,12 @@ __global__ __launch_bounds__(256) void k_attn_merge_cols(AttnArgs a) {
 void plan_attention(int B, int Hkv, int max_len, int* pages_per_split, int* max_splits) {
   const int max_pages = (max_len + kBlock - 1) / kBlock;
   int pps = 2;
-  while (pps < 64 && (long)B * Hkv * ((max_pages + pps - 1) / pps) > 640) pps *= 2;
+  // a single sequence has no empty runs in its grid: keep it within the 512
+  // workgroups that are resident together (two per compute unit), so that no
+  // run waits for a second round (prefix 32768: 514 runs of 8 pages, the step
+  // 2.78 ms, against 258 of 16, 2.71 ms)
+  const long lim = B == 1 ? 2L * cu_count() : 640;
+  while (pps < 64 && (long)B * Hkv * ((max_pages + pps - 1) / pps) > lim) pps *= 2;
   // at least 8 pages per run while 128 runs remain: INT4 batch 8 at P 1280
   // (336 runs of 4 pages) measured 4.15 -> 4.07 ms per step with runs of 8
   while (pps < 8 && (long)B * Hkv * ((max_pages + 2 * pps - 1) / (2 * pps)) >= 128) pps *= 2;

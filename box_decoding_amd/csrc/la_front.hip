@@ -98,7 +98,8 @@ __device__ __forceinline__ u32x4 pack8(const uint32_t (&x)[8]) {
 }
 
 // Flag arrays (ints): pack [kFlagCopies][64] (slice), ready [kFlagCopies][128]
-// (item), O done [kFlagCopies][128] (O tile).
+// (item), O done [kFlagCopies][128] (O tile), gate/up done [kFlagCopies][256]
+// (workgroup).
 __device__ __forceinline__ int32_t* fl_pack(const FrontArgs& f, int copy) { return f.sync + copy * 64; }
 __device__ __forceinline__ int32_t* fl_ready(const FrontArgs& f, int copy) {
   return f.sync + kFlagCopies * 64 + copy * 128;
@@ -106,7 +107,10 @@ __device__ __forceinline__ int32_t* fl_ready(const FrontArgs& f, int copy) {
 __device__ __forceinline__ int32_t* fl_odone(const FrontArgs& f, int copy) {
   return f.sync + kFlagCopies * (64 + 128) + copy * 128;
 }
-static_assert(kFlagCopies * (64 + 128 + 128) == kFrontSyncWords, "flag words the step carves");
+__device__ __forceinline__ int32_t* fl_gdone(const FrontArgs& f, int copy) {
+  return f.sync + kFlagCopies * (64 + 128 + 128) + copy * 256;
+}
+static_assert(kFlagCopies * (64 + 128 + 128 + 256) == kFrontSyncWords, "flag words the step carves");
 
 // One 8-byte word {datum, epoch}.
 __device__ __forceinline__ void ll_store(uint64_t* p, uint32_t d, int epoch) {
@@ -152,6 +156,35 @@ __device__ __forceinline__ void wait_flags(const FrontArgs& f, const int32_t* p,
       const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(r, o1, 0, kCoherent);
       // words past n read as zero and count as set
       if (__builtin_amdgcn_ballot_w64((lane < n && a != ep) || (lane + 64 < n && b != ep)) == 0) break;
+      if (++spins >= kSpinLimit) {
+        if (lane == 0 && f.err) atomicOr(f.err, LA_DERR_SYNC);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// wait_flags for up to 256 words (four per lane).
+__device__ __forceinline__ void wait_flags_wide(const FrontArgs& f, const int32_t* p, int n) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(p, (uint32_t)n * 4);
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = lane + 64 * k < n ? (uint32_t)(lane + 64 * k) * 4 : kNoRow;
+    const uint32_t ep = (uint32_t)f.epoch;
+    for (int spins = 0;;) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // every poll is a fresh load
+      uint32_t v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, o[k], 0, kCoherent);
+      bool miss = false;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) miss |= lane + 64 * k < n && v[k] != ep;
+      if (__builtin_amdgcn_ballot_w64(miss) == 0) break;
       if (++spins >= kSpinLimit) {
         if (lane == 0 && f.err) atomicOr(f.err, LA_DERR_SYNC);
         break;
@@ -499,8 +532,136 @@ __device__ __forceinline__ void gu_epilogue(const FrontArgs& f, int j, const flo
   uint32_t h, l;
   split_hi_lo(v, h, l);
   const size_t base = ((size_t)(n >> 3) * 16 + ml) * 8 + (n & 7);
-  f.mpack[base] = (uint16_t)h;
-  f.mpack[base + 64] = (uint16_t)l;
+  if (f.wdn) {
+    // read by this launch's down projection on other compute units
+    st_u16(f.mpack + base, h);
+    st_u16(f.mpack + base + 64, l);
+  } else {
+    f.mpack[base] = (uint16_t)h;
+    f.mpack[base + 64] = (uint16_t)l;
+  }
+}
+
+// The down projection's share of this workgroup when the launch runs it: K
+// slice s of kFrontDownSlices (units u0 .. u0 + nu - 1 of 32 k), output tiles
+// t0 and t0 + 1 (per = gridDim.x / kFrontDownSlices workgroups a slice, the
+// host makes 2 per = H / 16); wave w takes units u0 + w + 8 i.
+struct DnShare {
+  int s, t0, u0, nu, U;
+};
+__device__ __forceinline__ DnShare dn_share(const FrontArgs& f) {
+  DnShare d;
+  const int per = gridDim.x / kFrontDownSlices;
+  d.s = blockIdx.x / per;
+  d.t0 = 2 * (blockIdx.x % per);
+  d.U = f.F / 32;
+  const int spu = (d.U + kFrontDownSlices - 1) / kFrontDownSlices;
+  d.u0 = d.s * spu;
+  d.nu = min(spu, d.U - d.u0);
+  return d;
+}
+constexpr int kDnLds = 8;  // units per wave and tile staged in LDS: 2 x 8 x 8 KB = 128 KB
+constexpr int kDnReg = 3;  // further units per wave and tile in registers
+static_assert(8 * (kDnLds + kDnReg) == kFrontDownUnits, "units of one slice");
+static_assert(2 * kDnLds * kFrontWaves * 1024 <= kGuPreload * kTileBytes, "down weights in the preload LDS");
+
+// The first kDnLds units per wave of both down tiles into LDS (direct-to-LDS
+// loads; unit (tile k, i) of wave w at ((k kDnLds + i) 8 + w) KB), once the
+// preloaded gate/up tiles have been read.
+__device__ void dn_preload(const FrontArgs& f, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const DnShare d = dn_share(f);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.wdn, f.wdn_bytes);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int i = 0; i < kDnLds; ++i) {
+      const int ui = wave + 8 * i;
+      if (ui < d.nu) {  // uniform
+        void __attribute__((address_space(3)))* dst =
+            (void __attribute__((address_space(3)))*)(smem + ((k * kDnLds + i) * kFrontWaves + wave) * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, (uint32_t)lane * 16,
+                                                 ((uint32_t)(d.t0 + k) * d.U + d.u0 + ui) * 1024, 0, kNonTemporal);
+      }
+    }
+}
+
+// The rest of this wave's down units (kDnReg per tile) into registers.
+__device__ __forceinline__ void dn_issue_regs(const FrontArgs& f, int wave, u32x4 (&wd)[2 * kDnReg]) {
+  const int lane = threadIdx.x & 63;
+  const DnShare d = dn_share(f);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.wdn, f.wdn_bytes);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int i = 0; i < kDnReg; ++i) {
+      const int ui = wave + 8 * (kDnLds + i);
+      const uint32_t off = ui < d.nu ? ((((uint32_t)(d.t0 + k) * d.U + d.u0 + ui) * 64 + lane) * 16) : kNoRow;
+      wd[k * kDnReg + i] = bload16<kNonTemporal>(rw, off);
+    }
+}
+
+// The down role of every workgroup: once every workgroup's gate/up outputs
+// are in (the packed SiLU operand, agent-scope stores), its two output tiles
+// over its K slice; the waves' partial tiles meet in LDS (the same sums in the
+// same order as tile_reduce), and the K-slice sums go to dparts for the next
+// pack.
+__device__ __forceinline__ void front_down(const FrontArgs& f, unsigned char* smem, const u32x4 (&wd)[2 * kDnReg]) {
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const DnShare d = dn_share(f);
+  wait_flags_wide(f, fl_gdone(f, blockIdx.x % kFlagCopies), gridDim.x);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(f.mpack, (uint32_t)(f.F / 8) * 256);
+  const bool live = (lane & 7) < f.T;  // operand rows r (hi) and r + 8 (lo) of window row r
+  bf16x8 af[kDnLds + kDnReg];
+#pragma unroll
+  for (int i = 0; i < kDnLds + kDnReg; ++i) {
+    const int ui = wave + 8 * i;
+    const uint32_t kc = (uint32_t)(d.u0 + ui) * 4 + g4;
+    af[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ra, ui < d.nu && live ? (kc * 16 + (lane & 15)) * 16 : kNoRow, 0, kCoherent));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS copies (each wave reads only its own units)
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < kDnLds + kDnReg; ++i) {
+    if (wave + 8 * i < d.nu) {  // uniform
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const u32x4 w = i < kDnLds ? *(const u32x4*)(smem + ((k * kDnLds + i) * kFrontWaves + wave) * 1024 + lane * 16)
+                                   : wd[k * kDnReg + (i < kDnLds ? 0 : i - kDnLds)];
+        acc[k] = mfma_16x16x32(af[i], __builtin_bit_cast(bf16x8, w), acc[k]);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the LDS weights
+  f32x4* red = (f32x4*)smem;  // [tile][wave][lane]
+#pragma unroll
+  for (int k = 0; k < 2; ++k) red[(k * kFrontWaves + wave) * 64 + lane] = acc[k];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int k = threadIdx.x >> 7, o = threadIdx.x & 127, r = o >> 4, c = o & 15;
+    const int lh = (r >> 2) * 16 + c, ll = ((r + 8) >> 2) * 16 + c, e = r & 3;
+    float v = 0.f;
+    for (int w = 0; w < kFrontWaves; ++w)
+      v += red[(k * kFrontWaves + w) * 64 + lh][e] + red[(k * kFrontWaves + w) * 64 + ll][e];
+    if (r < f.T) f.dparts[((size_t)d.s * f.T + r) * f.H + (d.t0 + k) * 16 + c] = v;
+  }
+}
+
+// After this workgroup's gate/up tiles: its flag (once wave 0's stores of the
+// packed SiLU operand are out), the down weights' register part, the down role.
+__device__ __forceinline__ void front_dn_tail(const FrontArgs& f, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave == 0) {
+    stores_done();
+    if (lane < kFlagCopies) set_flag(fl_gdone(f, lane) + blockIdx.x, f.epoch);
+  }
+  u32x4 wd[2 * kDnReg];
+  dn_issue_regs(f, wave, wd);
+  front_down(f, smem, wd);
 }
 
 // This workgroup's gate/up tiles after the kGuPreload preloaded ones: the
@@ -524,7 +685,10 @@ __device__ __forceinline__ void front_gateup(const FrontArgs& f, unsigned char* 
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, j0 = blockIdx.x;
-  if (j0 >= f.n_gu_tiles) return;  // uniform
+  if (j0 >= f.n_gu_tiles) {  // uniform
+    if (f.wdn) dn_preload(f, smem);
+    return;
+  }
   const int js = j0 + kGuPreload * G;  // first streamed tile
   if (!issued) gu_issue(f, wave, wa, wb, wc);
   wait_flags(f, fl_odone(f, blockIdx.x % kFlagCopies), f.n_o_tiles);
@@ -560,7 +724,7 @@ __device__ __forceinline__ void front_gateup(const FrontArgs& f, unsigned char* 
   f32x4* red = (f32x4*)(smem + kRedOff);
   for (int p = 0; p < kGuPreload; ++p) {
     const int j = j0 + p * G;
-    if (j >= f.n_gu_tiles) return;  // uniform: no streamed tile either
+    if (j >= f.n_gu_tiles) break;  // uniform: no streamed tile either
     u32x4 wf[kFrontUnits];
 #pragma unroll
     for (int i = 0; i < kFrontUnits; ++i)
@@ -568,6 +732,8 @@ __device__ __forceinline__ void front_gateup(const FrontArgs& f, unsigned char* 
     tile_reduce(af, wf, wave, red, outv);
     if (wave == 0) gu_epilogue(f, j, outv, inv);
   }
+  // the preloaded tiles' LDS now takes the down projection's weights
+  if (f.wdn) dn_preload(f, smem);
   // three tiles in flight: each buffer is refilled right after its product
   for (int j = js; j < f.n_gu_tiles; j += 3 * G) {
     tile_reduce(af, wa, wave, red, outv);
@@ -908,6 +1074,7 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
       }
       front_o(f, w, wo, smem);
       if (f.wgu) front_gateup(f, smem, wa, wb, wc, true);
+      if (f.wdn) front_dn_tail(f, smem);
       return;
     } else if (f.wgu) {
       gu_preload(f, smem);
@@ -935,12 +1102,19 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
   }
   u32x4 wa[kFrontUnits], wb[kFrontUnits], wc[kFrontUnits];
   if (f.wgu) front_gateup(f, smem, wa, wb, wc, false);
+  if (f.wdn) front_dn_tail(f, smem);
 }
 
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
   if (!f.ll_q || !f.ll_kv || !f.ll_ml || !f.ll_po) return hipErrorInvalidValue;
   if (f.wgu && (!f.mpack || f.F != f.n_gu_tiles * 8 || f.n_gu_tiles < 1 ||
                 (size_t)f.n_gu_tiles * kTileBytes > f.wgu_bytes))
+    return hipErrorInvalidValue;
+  // the down projection: every workgroup two output tiles of one K slice, at
+  // most kFrontDownUnits units a slice, one gate/up-done flag per workgroup
+  if (f.wdn && (!f.wgu || !f.dparts || f.H % 16 || grid != (f.H / 16) * kFrontDownSlices / 2 || grid > 256 ||
+                f.F % 32 || (f.F / 32 + kFrontDownSlices - 1) / kFrontDownSlices > kFrontDownUnits ||
+                (size_t)(f.H / 16) * (f.F / 32) * 1024 > f.wdn_bytes))
     return hipErrorInvalidValue;
   if (f.runs > kFrontMaxRuns || f.n_parts > kFrontMaxParts || f.at.pages_per_split > kFrontMaxRunPages ||
       f.H != kFrontK || f.HQ != kFrontK || f.T > 8 || f.n_o_tiles > f.n_qkv_tiles || f.at.nqp % 16 ||

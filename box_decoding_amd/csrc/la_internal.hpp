@@ -226,6 +226,12 @@ struct FrontArgs {
   uint32_t wgu_bytes;
   int n_gu_tiles, F;
   uint16_t* mpack;
+  // the down projection in the same launch too (nullable wdn: a kernel of its
+  // own): the tiled down weight (H / 16 tiles of F / 32 units), its output as
+  // kFrontDownSlices K-slice sums [slice][T][H] that the next pack adds
+  const void* wdn;
+  uint32_t wdn_bytes;
+  float* dparts;
   int n_qkv_tiles, n_o_tiles, n_items, runs;  // attention items = B * Hkv * runs
   int32_t* sync;              // flag words (the step's prologue zeroes them)
   // Data handed from a few producers to a few consumers inside the launch, as
@@ -242,9 +248,15 @@ struct FrontArgs {
 // LDS), and the slices its operand packing splits K = 2048 into.
 constexpr int kFrontMaxRunPages = 12;
 constexpr int kFrontPackSlices = 64;
+// K slices of the down projection when the front-half launch runs it: each
+// workgroup takes two output tiles of one slice (grid = 2 x slices x ... =
+// H / 16 x slices / 2 workgroups), at most kFrontDownUnits units of 32 k.
+constexpr int kFrontDownSlices = 4;
+constexpr int kFrontDownUnits = 88;
 // Flag words of the front-half launch: pack [8 copies][64 slices], ready [8
-// copies][128 items], O tiles done [8 copies][128 tiles].
-constexpr int kFrontSyncWords = 8 * 64 + 8 * 128 + 8 * 128;
+// copies][128 items], O tiles done [8 copies][128 tiles], gate/up done [8
+// copies][256 workgroups].
+constexpr int kFrontSyncWords = 8 * 64 + 8 * 128 + 8 * 128 + 8 * 256;
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s);
 // Compute units of the current device (256 when the query fails).
 int cu_count();
