@@ -652,15 +652,15 @@ __device__ __forceinline__ void front_down(const FrontArgs& f, unsigned char* sm
 
 // After this workgroup's gate/up tiles: its flag (once wave 0's stores of the
 // packed SiLU operand are out), the down weights' register part, the down role.
-__device__ __forceinline__ void front_dn_tail(const FrontArgs& f, unsigned char* smem) {
+__device__ __forceinline__ void front_dn_tail(const FrontArgs& f, unsigned char* smem, u32x4 (&wd)[2 * kDnReg],
+                                              bool wd_issued) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) {
     stores_done();
     if (lane < kFlagCopies) set_flag(fl_gdone(f, lane) + blockIdx.x, f.epoch);
   }
-  u32x4 wd[2 * kDnReg];
-  dn_issue_regs(f, wave, wd);
+  if (!wd_issued) dn_issue_regs(f, wave, wd);
   front_down(f, smem, wd);
 }
 
@@ -681,7 +681,8 @@ __device__ __forceinline__ void gu_issue(const FrontArgs& f, int wave, u32x4 (&w
 // preloaded tiles multiply from LDS and the rest stream through the three
 // register buffers.
 __device__ __forceinline__ void front_gateup(const FrontArgs& f, unsigned char* smem, u32x4 (&wa)[kFrontUnits],
-                                             u32x4 (&wb)[kFrontUnits], u32x4 (&wc)[kFrontUnits], bool issued) {
+                                             u32x4 (&wb)[kFrontUnits], u32x4 (&wc)[kFrontUnits], bool issued,
+                                             u32x4 (&wd)[2 * kDnReg], bool& wd_issued) {
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, j0 = blockIdx.x;
@@ -746,6 +747,12 @@ __device__ __forceinline__ void front_gateup(const FrontArgs& f, unsigned char* 
     if (j + 2 * G >= f.n_gu_tiles) break;  // uniform
     tile_reduce(af, wc, wave, red, outv);
     if (j + 5 * G < f.n_gu_tiles) load_tile_weights(f.wgu, f.wgu_bytes, j + 5 * G, wave, wc);
+    // the down weights' register part once three buffers' tiles are done
+    // (wave 0 after its flag: its stores must not wait for these loads)
+    if (f.wdn && wave != 0 && !wd_issued) {
+      dn_issue_regs(f, wave, wd);
+      wd_issued = true;
+    }
     if (wave == 0) gu_epilogue(f, j + 2 * G, outv, inv);
   }
 }
@@ -1073,8 +1080,10 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
         gu_issue(f, wave, wa, wb, wc);
       }
       front_o(f, w, wo, smem);
-      if (f.wgu) front_gateup(f, smem, wa, wb, wc, true);
-      if (f.wdn) front_dn_tail(f, smem);
+      u32x4 wd[2 * kDnReg];
+      bool wd_issued = false;
+      if (f.wgu) front_gateup(f, smem, wa, wb, wc, true, wd, wd_issued);
+      if (f.wdn) front_dn_tail(f, smem, wd, wd_issued);
       return;
     } else if (f.wgu) {
       gu_preload(f, smem);
@@ -1101,8 +1110,10 @@ __global__ __launch_bounds__(kFrontThreads) void k_front(FrontArgs f) {
     if (f.wgu) gu_preload(f, smem);
   }
   u32x4 wa[kFrontUnits], wb[kFrontUnits], wc[kFrontUnits];
-  if (f.wgu) front_gateup(f, smem, wa, wb, wc, false);
-  if (f.wdn) front_dn_tail(f, smem);
+  u32x4 wd[2 * kDnReg];
+  bool wd_issued = false;
+  if (f.wgu) front_gateup(f, smem, wa, wb, wc, false, wd, wd_issued);
+  if (f.wdn) front_dn_tail(f, smem, wd, wd_issued);
 }
 
 hipError_t launch_front(const FrontArgs& f, int grid, hipStream_t s) {
