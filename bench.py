@@ -853,7 +853,8 @@ def main():
                "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                "launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": gu_bytes}
     roof_front = {"bound": "hbm",
-                  "kernel": "front half of a layer, one persistent launch (k_front: RMSNorm, QKV, attention, O"
+                  "kernel": ("a layer in one persistent launch" if fused_dn else "front half of a layer, one persistent launch")
+                            + " (k_front: RMSNorm, QKV, attention, O"
                             + (", gate/up + SiLU" if fused else "") + (", down)" if fused_dn else ")"),
                   "achieved": round(front_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": round(front_gbps / HBM_PEAK_GBPS, 4), "traffic": front_traffic,
