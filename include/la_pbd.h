@@ -388,8 +388,9 @@ la_status la_sample_logits(const float* logits, int32_t M, int32_t V, int32_t ld
  *    timing: block_events[2 l] is recorded on the stream before layer l's
  *    attention block (input RMSNorm, QKV, attention, O projection) and
  *    block_events[2 l + 1] after the launch that ends it (with bf16 tiled
- *    weights at up to 8 rows that one launch also runs the gate/up
- *    projection, unless LA_PBD_FRONT_GU=0). */
+ *    weights at up to 8 rows that one launch also runs the gate/up and down
+ *    projections, the whole layer, unless LA_PBD_FRONT_GU=0 or
+ *    LA_PBD_FRONT_DOWN=0 in the environment stops it earlier). */
 typedef struct {
   const int32_t* causal_rows;
   const int32_t* window_len;
